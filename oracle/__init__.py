@@ -1,0 +1,184 @@
+"""ctypes front end of the serial fp64 oracle (oracle.c).
+
+Test infrastructure only: the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product path never does.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+OK, INFEASIBLE, UNDERFLOW, BADARG = 0, 1, 2, 3
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+                               "-fno-fast-math", "-Wall", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Aut(C.Structure):
+    _fields_ = [("S", C.c_int32), ("V", C.c_int32), ("start", C.c_int32),
+                ("n_accept", C.c_int32), ("accept", C.c_void_p), ("E", C.c_int64),
+                ("src", C.c_void_p), ("dst", C.c_void_p), ("label_off", C.c_void_p),
+                ("label_tok", C.c_void_p), ("ranges", C.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        _lib = C.CDLL(build())
+        P = C.c_void_p
+        _lib.or_philox4x32_10.argtypes = [P, P, P]
+        _lib.or_uniform.argtypes = [C.c_uint64, C.c_uint32, C.c_uint32, C.c_uint32]
+        _lib.or_uniform.restype = C.c_double
+        _lib.or_edge_weights.argtypes = [P, P, C.c_int32, P]
+        _lib.or_dense_M.argtypes = [P, P, C.c_int32, P]
+        _lib.or_forward_backward.argtypes = [P, P, C.c_int32, P, P, P, P, P]
+        _lib.or_marginals.argtypes = [P, P, C.c_int32, P, P, P, P, P, C.c_int32, P, P, P,
+                                      C.c_int32, P]
+        _lib.or_sample_tree.argtypes = [P, P, P, C.c_int32, C.c_uint64, C.c_uint32, P, P]
+        _lib.or_replay_verify.argtypes = [P, P, P, C.c_int32, C.c_uint64, C.c_uint32, P, P, P]
+        _lib.or_ffbs.argtypes = [P, P, P, C.c_int32, P, P, P, P]
+        _lib.or_edge_count.argtypes = [P, C.c_int32, C.c_int32, C.c_int32]
+        _lib.or_edge_count.restype = C.c_int32
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(C.c_void_p)
+
+
+def philox4x32_10(ctr, key):
+    c = np.ascontiguousarray(ctr, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.zeros(4, np.uint32)
+    lib().or_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def uniform(seed: int, b: int, level: int, node: int) -> float:
+    return lib().or_uniform(seed, b, level, node)
+
+
+class Oracle:
+    """Oracle bound to one automaton (original state ids, raw edge list)."""
+
+    def __init__(self, aut):
+        self.aut = aut
+        self._keep = [np.ascontiguousarray(aut.accept, np.int32),
+                      np.ascontiguousarray(aut.src, np.int32),
+                      np.ascontiguousarray(aut.dst, np.int32),
+                      np.ascontiguousarray(aut.label_off, np.int64),
+                      np.ascontiguousarray(aut.label_tok, np.int32)]
+        acc, src, dst, off, tok = self._keep
+        self._s = _Aut(aut.S, aut.V, aut.start, acc.size, acc.ctypes.data, aut.E,
+                       src.ctypes.data, dst.ctypes.data, off.ctypes.data, tok.ctypes.data,
+                       1 if aut.ranges else 0)
+        self._sp = C.cast(C.pointer(self._s), C.c_void_p)
+
+    # p: fp32 [L, V] for one batch row
+    def edge_weights(self, p: np.ndarray) -> np.ndarray:
+        p = np.ascontiguousarray(p, np.float32)
+        L = p.shape[0]
+        W = np.zeros((L, self.aut.E), np.float64)
+        lib().or_edge_weights(self._sp, _ptr(p), L, _ptr(W))
+        return W
+
+    def dense_M(self, W: np.ndarray, i: int) -> np.ndarray:
+        M = np.zeros((self.aut.S, self.aut.S), np.float64)
+        lib().or_dense_M(self._sp, _ptr(np.ascontiguousarray(W)), i, _ptr(M))
+        return M
+
+    def forward_backward(self, W: np.ndarray):
+        L = W.shape[0]
+        S = self.aut.S
+        alpha = np.zeros((L + 1, S)); beta = np.zeros((L + 1, S))
+        alog = np.zeros(L + 1); blog = np.zeros(L + 1)
+        logZ = np.zeros(1)
+        st = lib().or_forward_backward(self._sp, _ptr(np.ascontiguousarray(W)), L, _ptr(alpha),
+                                       _ptr(alog), _ptr(beta), _ptr(blog), _ptr(logZ))
+        return dict(alpha=alpha, alog=alog, beta=beta, blog=blog, logZ=float(logZ[0]),
+                    status=int(st))
+
+    def marginals(self, p, fb, positions=None, tokens=None, conf_mode=0):
+        p = np.ascontiguousarray(p, np.float32)
+        L = p.shape[0]
+        pos = np.ascontiguousarray(np.arange(L) if positions is None else positions, np.int32)
+        q = np.zeros((pos.size, self.aut.V))
+        lognorm = np.zeros(pos.size)
+        conf = np.zeros(pos.size)
+        tok = None if tokens is None else np.ascontiguousarray(tokens, np.int32)
+        st = lib().or_marginals(self._sp, _ptr(p), L, _ptr(fb["alpha"]), _ptr(fb["alog"]),
+                                _ptr(fb["beta"]), _ptr(fb["blog"]), _ptr(pos), pos.size, _ptr(q),
+                                _ptr(lognorm), None if tok is None else _ptr(tok), conf_mode,
+                                _ptr(conf))
+        if st != OK:
+            raise RuntimeError(f"or_marginals status {st}")
+        return q, lognorm, conf
+
+    def sample_tree(self, p, W, seed: int, b: int):
+        p = np.ascontiguousarray(p, np.float32)
+        L = p.shape[0]
+        states = np.full(L + 1, -1, np.int32)
+        tokens = np.full(L, -1, np.int32)
+        st = lib().or_sample_tree(self._sp, _ptr(p), _ptr(np.ascontiguousarray(W)), L, seed, b,
+                                  _ptr(states), _ptr(tokens))
+        return states, tokens, int(st)
+
+    def replay(self, p, W, seed: int, b: int, states, tokens):
+        p = np.ascontiguousarray(p, np.float32)
+        L = p.shape[0]
+        rep = np.zeros(5, np.int64)
+        st = lib().or_replay_verify(self._sp, _ptr(p), _ptr(np.ascontiguousarray(W)), L, seed, b,
+                                    _ptr(np.ascontiguousarray(states, np.int32)),
+                                    _ptr(np.ascontiguousarray(tokens, np.int32)), _ptr(rep))
+        return dict(status=int(st), draws=int(rep[0]), hard=int(rep[1]), near=int(rep[2]),
+                    margin=int(rep[3]), first_hard=int(rep[4]))
+
+    def ffbs(self, p, W, fb, u):
+        p = np.ascontiguousarray(p, np.float32)
+        L = p.shape[0]
+        states = np.full(L + 1, -1, np.int32)
+        tokens = np.full(L, -1, np.int32)
+        st = lib().or_ffbs(self._sp, _ptr(p), _ptr(np.ascontiguousarray(W)), L, _ptr(fb["alpha"]),
+                           _ptr(np.ascontiguousarray(u, np.float64)), _ptr(states), _ptr(tokens))
+        return states, tokens, int(st)
+
+    def edge_count(self, a: int, v: int, b: int) -> int:
+        return int(lib().or_edge_count(self._sp, a, v, b))
+
+
+def step(aut, p: np.ndarray, seed: int, rows=None, q_positions=None, conf_mode=0):
+    """Oracle for one constrained step over the rows of p [B, L, V]: log Z,
+    tree-order samples, and marginals at q_positions (all positions if None;
+    an empty list skips them).  Returns a list of per-row dicts."""
+    orc = Oracle(aut)
+    B = p.shape[0]
+    out = []
+    for b in (range(B) if rows is None else rows):
+        W = orc.edge_weights(p[b])
+        fb = orc.forward_backward(W)
+        d = dict(b=b, W=W, fb=fb, logZ=fb["logZ"], status=fb["status"])
+        if fb["status"] == OK:
+            st, tk, s2 = orc.sample_tree(p[b], W, seed, b)
+            d.update(states=st, tokens=tk, sample_status=s2)
+            if q_positions is None or len(q_positions):
+                q, ln, conf = orc.marginals(p[b], fb, q_positions, tk, conf_mode)
+                d.update(q=q, lognorm=ln, conf=conf)
+        out.append(d)
+    return out

@@ -1,0 +1,329 @@
+"""Pins of the fp64 oracle against facts fixed independently of it:
+published Philox known-answer vectors, hand-derived closed forms, special
+automata that reduce to textbook results, an integer path-count DP, a
+library chain product, and brute-force enumeration of all V^L strings."""
+import os
+
+import numpy as np
+import pytest
+from scipy import stats
+
+import oracle
+from synth import automata as A
+from tests import bruteforce as BF
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_kv(name):
+    out = {}
+    for line in open(os.path.join(GOLD, name)):
+        if line.startswith("#") or not line.strip():
+            continue
+        k, *v = line.split()
+        out[k] = v
+    return out
+
+
+def _softmax(x):
+    x = x - x.max(axis=-1, keepdims=True)
+    e = np.exp(x)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+# ------------------------------------------------------------------ Philox
+def test_philox_known_answers():
+    for line in open(os.path.join(GOLD, "philox4x32_10_kat.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        w = [int(t, 16) for t in line.split()]
+        out = oracle.philox4x32_10(w[0:4], w[4:6])
+        assert list(out) == w[6:10]
+
+
+def test_uniform_definition():
+    seed = 0x123456789ABCDEF
+    for (b, lev, node) in [(0, 0, 0), (3, 2, 7), (1, 9, 255)]:
+        r = oracle.philox4x32_10([b, lev, node, 0], [seed & 0xffffffff, seed >> 32])
+        u = oracle.uniform(seed, b, lev, node)
+        assert u == (int(r[0]) >> 8) / 2.0 ** 24
+        assert 0.0 <= u < 1.0
+
+
+# -------------------------------------------------------------- closed forms
+def test_two_token_example_closed_form():
+    g = _read_kv("two_token_real_example.txt")
+    aut = A.two_token_real_dfa()
+    p = np.full((2, 2), 0.5, np.float32)
+    orc = oracle.Oracle(aut)
+    W = orc.edge_weights(p)
+    fb = orc.forward_backward(W)
+    assert fb["status"] == oracle.OK
+    assert np.exp(fb["logZ"]) == pytest.approx(float(g["Z"][0]), rel=1e-14)
+    q, lognorm, _ = orc.marginals(p, fb)
+    for i in range(2):
+        assert q[i, 1] == pytest.approx(float(g["q_dot"][0]), rel=1e-13)
+        assert q[i, 0] == pytest.approx(float(g["q_one"][0]), rel=1e-13)
+    np.testing.assert_allclose(lognorm, fb["logZ"], rtol=0, atol=1e-13)
+    # samples: uniform over the three accepted strings, never ".."
+    accepted = {tuple(map(int, s.split(","))) for s in g["accepted"]}
+    counts = {s: 0 for s in accepted}
+    n = 6000
+    for seed in range(n):
+        st, tk, status = orc.sample_tree(p, W, seed, 0)
+        assert status == oracle.OK
+        t = tuple(int(x) for x in tk)
+        assert t in accepted
+        counts[t] += 1
+    chi2 = sum((c - n / 3) ** 2 / (n / 3) for c in counts.values())
+    assert stats.chi2.sf(chi2, 2) > 1e-4
+
+
+def test_real_number_uniform_closed_form():
+    g = _read_kv("real_number_uniform.txt")
+    aut = A.real_number_dfa()
+    L = 6
+    p = np.full((L, 12), 1.0 / 12.0, np.float32)
+    orc = oracle.Oracle(aut)
+    W = orc.edge_weights(p)
+    fb = orc.forward_backward(W)
+    # p is fp32(1/12): the closed form holds for the fp32 value of 1/12
+    p12 = float(np.float32(1.0 / 12.0))
+    Z = int(g["count"][0]) * p12 ** L
+    assert np.exp(fb["logZ"]) == pytest.approx(Z, rel=1e-13)
+    assert float(g["Z"][0]) == pytest.approx(int(g["count"][0]) / 12.0 ** 6, rel=1e-15)
+    q, _, _ = orc.marginals(p, fb)
+    np.testing.assert_allclose(q[:, 10], float(g["q_dot"][0]), rtol=1e-12)
+    np.testing.assert_allclose(q[:, :10], float(g["q_digit"][0]), rtol=1e-12)
+    np.testing.assert_allclose(q[:, 11], float(g["q_pad"][0]), atol=0)
+
+
+def test_universal_automaton_reduces_to_unconstrained():
+    rng = np.random.default_rng(7)
+    V, L = 9, 13
+    p = _softmax(rng.normal(0, 2, (L, V))).astype(np.float32)
+    aut = A.universal_automaton(V)
+    orc = oracle.Oracle(aut)
+    W = orc.edge_weights(p)
+    fb = orc.forward_backward(W)
+    pd = p.astype(np.float64)
+    assert fb["logZ"] == pytest.approx(np.log(pd.sum(axis=1)).sum(), abs=1e-12)
+    q, _, _ = orc.marginals(p, fb)
+    np.testing.assert_allclose(q, pd / pd.sum(axis=1, keepdims=True), rtol=1e-12)
+    # token draws are plain inverse-CDF draws of p under the level K+1 keys
+    seed = 99
+    st, tk, status = orc.sample_tree(p, W, seed, 0)
+    K = int(np.ceil(np.log2(L)))
+    for i in range(L):
+        u = oracle.uniform(seed, 0, K + 1, i)
+        c = np.cumsum(pd[i])
+        assert tk[i] == int(np.flatnonzero(c > u * c[-1])[0])
+    assert (st == 0).all()
+
+
+def test_single_string_automaton():
+    rng = np.random.default_rng(3)
+    V, L = 7, 11
+    word = rng.integers(0, V, L)
+    p = _softmax(rng.normal(0, 1, (L, V))).astype(np.float32)
+    aut = A.single_string_automaton(word, V)
+    orc = oracle.Oracle(aut)
+    W = orc.edge_weights(p)
+    fb = orc.forward_backward(W)
+    assert fb["logZ"] == pytest.approx(np.log(p.astype(np.float64)[np.arange(L), word]).sum(),
+                                       abs=1e-12)
+    for seed in range(5):
+        st, tk, _ = orc.sample_tree(p, W, seed, 0)
+        np.testing.assert_array_equal(tk, word)
+        np.testing.assert_array_equal(st, np.arange(L + 1))
+
+
+def test_counting_mode_matches_integer_path_count():
+    # p == 1 everywhere: Z is the number of accepting (path, string) pairs
+    rng = np.random.default_rng(11)
+    aut = A.random_nfa(rng, 6, 5, 14, 2, 2.0)
+    L = 12
+    p = np.ones((L, aut.V), np.float32)
+    orc = oracle.Oracle(aut)
+    fb = orc.forward_backward(orc.edge_weights(p))
+    # integer DP over states: number of (string, path) pairs
+    cnt = [0] * aut.S
+    cnt[aut.start] = 1
+    for _ in range(L):
+        nxt = [0] * aut.S
+        for e in range(aut.E):
+            nxt[aut.dst[e]] += cnt[aut.src[e]] * int(aut.edge_label(e).size)
+        cnt = nxt
+    total = sum(cnt[f] for f in aut.accept)
+    assert total > 0
+    assert np.exp(fb["logZ"]) == pytest.approx(float(total), rel=1e-12)
+
+
+def test_chain_product_matches_library_multi_dot():
+    rng = np.random.default_rng(5)
+    aut = A.random_nfa(rng, 7, 6, 20, 3, 2.5)
+    L = 9
+    p = _softmax(rng.normal(0, 2, (L, aut.V))).astype(np.float32)
+    orc = oracle.Oracle(aut)
+    W = orc.edge_weights(p)
+    # dense count tensor c[a, v, b] from the raw edge list, contracted with p
+    c = np.zeros((aut.S, aut.V, aut.S))
+    for e in range(aut.E):
+        c[aut.src[e], aut.edge_label(e), aut.dst[e]] += 1.0
+    Ms = [np.einsum("avb,v->ab", c, p[i].astype(np.float64)) for i in range(L)]
+    for i in range(L):
+        np.testing.assert_allclose(orc.dense_M(W, i), Ms[i], rtol=1e-13, atol=1e-300)
+    prod = np.linalg.multi_dot(Ms)
+    Z = prod[aut.start, aut.accept].sum()
+    fb = orc.forward_backward(W)
+    assert fb["logZ"] == pytest.approx(np.log(Z), abs=1e-12)
+
+
+def test_range_sums_match_direct_summation():
+    rng = np.random.default_rng(2)
+    aut = A.tiny_range_automaton(rng, 5, 300, 12, dfa=False)
+    p = _softmax(rng.normal(0, 4, (4, aut.V))).astype(np.float32)
+    W = oracle.Oracle(aut).edge_weights(p)
+    for i in range(4):
+        for e in range(aut.E):
+            direct = sum(float(p[i, v]) for v in aut.edge_label(e))
+            assert W[i, e] == pytest.approx(direct, rel=1e-12, abs=1e-300)
+
+
+def test_forward_backward_invariant():
+    rng = np.random.default_rng(4)
+    aut = A.random_dfa(rng, 12, 40, 3, 0.4)
+    L = 30
+    p = _softmax(rng.normal(0, 3, (L, aut.V))).astype(np.float32)
+    orc = oracle.Oracle(aut)
+    fb = orc.forward_backward(orc.edge_weights(p))
+    assert fb["status"] == oracle.OK
+    for i in range(L + 1):
+        z = np.log(fb["alpha"][i] @ fb["beta"][i]) + fb["alog"][i] + fb["blog"][i]
+        assert z == pytest.approx(fb["logZ"], abs=1e-10)
+    q, lognorm, _ = orc.marginals(p, fb)
+    np.testing.assert_allclose(q.sum(axis=1), 1.0, rtol=1e-12)
+    np.testing.assert_allclose(lognorm, fb["logZ"], atol=1e-10)
+
+
+def test_infeasible_row():
+    aut = A.single_string_automaton([1, 2, 3], 5)
+    p = np.full((3, 5), 0.2, np.float32)
+    p[1] = 0.0
+    p[1, 4] = 1.0  # committed token that contradicts the only accepted string
+    orc = oracle.Oracle(aut)
+    fb = orc.forward_backward(orc.edge_weights(p))
+    assert fb["status"] == oracle.INFEASIBLE
+    assert fb["logZ"] == -np.inf
+
+
+# ------------------------------------------------------------ brute force
+def _tiny_family():
+    out = []
+    for k in range(4):
+        rng = np.random.default_rng(100 + k)
+        out.append((A.random_dfa(rng, 5, 4, 2, 0.6), 5))
+    for k in range(3):
+        rng = np.random.default_rng(200 + k)
+        aut = A.random_nfa(rng, 4, 4, 10, 2, 2.0)
+        # a parallel edge with an overlapping label: path counts > 1
+        aut = A._pack(aut.S, aut.V, aut.start, aut.accept.tolist(),
+                      [(int(aut.src[e]), int(aut.dst[e]), aut.edge_label(e)) for e in range(aut.E)]
+                      + [(int(aut.src[0]), int(aut.dst[0]), aut.edge_label(0))],
+                      dfa=False, name="tiny NFA + parallel edge")
+        out.append((aut, 5))
+    for k in range(2):
+        rng = np.random.default_rng(300 + k)
+        out.append((A.tiny_range_automaton(rng, 4, 5, 8, dfa=(k == 0)), 5))
+    out.append((A.real_number_dfa(), 4))
+    return out
+
+
+@pytest.mark.parametrize("idx", range(10))
+def test_oracle_vs_bruteforce(idx):
+    aut, L = _tiny_family()[idx]
+    rng = np.random.default_rng(500 + idx)
+    p = _softmax(rng.normal(0, 1.5, (L, aut.V))).astype(np.float32)
+    X, prob, Z, q_bf = BF.distribution(aut, p)
+    orc = oracle.Oracle(aut)
+    W = orc.edge_weights(p)
+    fb = orc.forward_backward(W)
+    if Z == 0:
+        assert fb["status"] == oracle.INFEASIBLE
+        return
+    assert fb["logZ"] == pytest.approx(np.log(Z), abs=1e-12)
+    q, _, _ = orc.marginals(p, fb)
+    np.testing.assert_allclose(q, q_bf, atol=1e-12)
+    # chi-square of the tree-order sampler and of FFBS against the exact law
+    n = 20000
+    idx_of = {tuple(x): j for j, x in enumerate(X.tolist())}
+    ctr_tree = np.zeros(X.shape[0])
+    ctr_ffbs = np.zeros(X.shape[0])
+    urng = np.random.default_rng(900 + idx)
+    for s in range(n):
+        st, tk, status = orc.sample_tree(p, W, 10_000 + s, 0)
+        assert status == oracle.OK
+        ctr_tree[idx_of[tuple(int(t) for t in tk)]] += 1
+        st2, tk2, status2 = orc.ffbs(p, W, fb, urng.random(2 * L + 1))
+        assert status2 == oracle.OK
+        ctr_ffbs[idx_of[tuple(int(t) for t in tk2)]] += 1
+    assert ctr_tree[prob == 0].sum() == 0
+    exp = prob * n
+    keep = exp >= 5
+    for ctr in (ctr_tree, ctr_ffbs):
+        obs = np.append(ctr[keep], ctr[~keep].sum())
+        ex = np.append(exp[keep], exp[~keep].sum())
+        if ex[-1] < 5:
+            obs[-2] += obs[-1]; ex[-2] += ex[-1]
+            obs, ex = obs[:-1], ex[:-1]
+        chi2 = ((obs - ex) ** 2 / ex).sum()
+        assert stats.chi2.sf(chi2, len(ex) - 1) > 1e-4
+
+
+def test_replay_accepts_own_samples_and_flags_planted_error():
+    rng = np.random.default_rng(8)
+    aut = A.random_dfa(rng, 10, 30, 3, 0.3)
+    L = 21
+    p = _softmax(rng.normal(0, 2, (L, aut.V))).astype(np.float32)
+    orc = oracle.Oracle(aut)
+    W = orc.edge_weights(p)
+    st, tk, status = orc.sample_tree(p, W, 77, 2)
+    assert status == oracle.OK
+    rep = orc.replay(p, W, 77, 2, st, tk)
+    assert rep["hard"] == 0 and rep["near"] == 0
+    assert rep["draws"] == 1 + (32 - 1) + L  # root + Lpad-1 midpoints + L tokens
+    # planted mistake: a token outside the sampled edge's label
+    bad = tk.copy()
+    lab = set()
+    for e in range(aut.E):
+        if aut.src[e] == st[4] and aut.dst[e] == st[5]:
+            lab |= set(aut.edge_label(e).tolist())
+    bad[4] = next(v for v in range(aut.V) if v not in lab)
+    rep2 = orc.replay(p, W, 77, 2, st, bad)
+    assert rep2["hard"] >= 1
+    # planted mistake: a different final state
+    bad_st = st.copy()
+    bad_st[-1] = next(s for s in range(aut.S) if s != st[-1])
+    assert orc.replay(p, W, 77, 2, bad_st, tk)["hard"] >= 1
+
+
+def test_samples_accepted_and_states_follow_delta():
+    from synth import configs
+    for k in (1, 2):
+        w = configs.make(k)
+        orc = oracle.Oracle(w.aut)
+        delta = {}
+        for e in range(w.aut.E):
+            for v in w.aut.edge_label(e):
+                delta[(int(w.aut.src[e]), int(v))] = int(w.aut.dst[e])
+        for b in range(w.B):
+            W = orc.edge_weights(w.p[b])
+            st, tk, status = orc.sample_tree(w.p[b], W, w.seed, b)
+            assert status == oracle.OK
+            s = w.aut.start
+            for i in range(w.L):
+                s = delta[(s, int(tk[i]))]
+                assert s == st[i + 1]
+            assert s in set(w.aut.accept.tolist())
+            for pos, toks in w.commits[b:b + 1]:
+                np.testing.assert_array_equal(tk[pos], toks)
