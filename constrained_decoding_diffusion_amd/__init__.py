@@ -1,0 +1,11 @@
+"""Finite-automaton-constrained sampling for one denoising step of a
+diffusion language model, on AMD MI355X (gfx950).
+
+The C ABI (include/fa.h, libfa.so) does the work; this package marshals
+arguments.  See ``_fa.step`` for one whole step.
+"""
+from ._fa import (  # noqa: F401
+    FA_CONF_NEGENT, FA_CONF_PROB, FA_DFA, FA_LABEL_RANGES, FA_NFA, FA_NO_TRIM,
+    FA_ROW_BADPROB, FA_ROW_INFEASIBLE, FA_ROW_UNDERFLOW, FaError, StepBuffers, Table,
+    build_transitions, lib, marginals, sample, span_tree, step,
+)

@@ -1,0 +1,115 @@
+// C-ABI entry points of one constrained denoising step: argument checks,
+// geometry, workspace layout, then the kernel launchers.  Nothing here
+// allocates device memory or synchronizes.
+#include <hip/hip_runtime_api.h>
+
+#include "fa_internal.h"
+
+using namespace fa;
+
+namespace {
+
+int ready(const fa_table *t)
+{
+    if (!t) return FA_EINVAL;
+    if (!t->h.dev) return FA_ESTATE;
+    return FA_OK;
+}
+
+int hip_rc(int e) { return e == 0 ? FA_OK : FA_EHIP; }
+
+// grids put (row, node) pairs in their second dimension
+bool grid_fits(const Geometry &g) { return (int64_t)g.B * g.Lpad * 2 <= 65535 && g.L < (1 << 24); }
+
+}  // namespace
+
+extern "C" int fa_table_upload(fa_table *t, void *dev_buf, size_t bytes, fa_stream_t stream)
+{
+    if (!t || !dev_buf || bytes < t->h.image.size()) return FA_EINVAL;
+    if (((uintptr_t)dev_buf & 255u) != 0) return FA_EINVAL;
+    hipError_t e = hipMemcpyAsync(dev_buf, t->h.image.data(), t->h.image.size(),
+                                  hipMemcpyHostToDevice, (hipStream_t)stream);
+    if (e != hipSuccess) return FA_EHIP;
+    t->h.dev = dev_buf;
+    t->h.dev_bytes = bytes;
+    return FA_OK;
+}
+
+extern "C" int fa_build_transitions(const fa_table *t, const float *p, int32_t B, int32_t L,
+                                    float *tree, int32_t *meta, void *ws, size_t ws_bytes,
+                                    int32_t *row_status, fa_stream_t stream)
+{
+    int rc = ready(t);
+    if (rc) return rc;
+    Geometry g;
+    if (!make_geometry(t->h, B, L, &g)) return FA_EINVAL;
+    if (!grid_fits(g)) return FA_ETOOBIG;
+    if (B == 0 || L == 0) return FA_OK;
+    WsLayout w = ws_layout(t->h, g);
+    if (!p || !tree || !meta || !row_status || !ws || ws_bytes < w.total) return FA_EINVAL;
+    return hip_rc(launch_build_transitions(t->h.device_view(), g, p, tree, meta, (uint8_t *)ws, w,
+                                           row_status, stream));
+}
+
+extern "C" int fa_span_tree(const fa_table *t, int32_t B, int32_t L, float *tree, int32_t *meta,
+                            double *logZ, int32_t *row_status, fa_stream_t stream)
+{
+    int rc = ready(t);
+    if (rc) return rc;
+    Geometry g;
+    if (!make_geometry(t->h, B, L, &g)) return FA_EINVAL;
+    if (!grid_fits(g)) return FA_ETOOBIG;
+    if (B == 0) return FA_OK;
+    if (!logZ || !row_status || (L > 0 && (!tree || !meta))) return FA_EINVAL;
+    return hip_rc(launch_span_tree(t->h.device_view(), g, tree, meta, logZ, row_status, stream));
+}
+
+extern "C" int fa_sample(const fa_table *t, const float *p, int32_t B, int32_t L, const float *tree,
+                         const int32_t *meta, uint64_t seed, int32_t *states, int32_t *tokens,
+                         void *ws, size_t ws_bytes, int32_t *row_status, fa_stream_t stream)
+{
+    int rc = ready(t);
+    if (rc) return rc;
+    Geometry g;
+    if (!make_geometry(t->h, B, L, &g)) return FA_EINVAL;
+    if (!grid_fits(g)) return FA_ETOOBIG;
+    if (B == 0) return FA_OK;
+    WsLayout w = ws_layout(t->h, g);
+    if (!states || !row_status || !ws || ws_bytes < w.total) return FA_EINVAL;
+    if (L > 0 && (!p || !tree || !meta || !tokens)) return FA_EINVAL;
+    return hip_rc(launch_sample(t->h.device_view(), g, p, tree, meta, seed, states, tokens,
+                                (uint8_t *)ws, w, row_status, stream));
+}
+
+extern "C" int fa_marginals(const fa_table *t, const float *p, int32_t B, int32_t L,
+                            const float *tree, const int32_t *meta, const double *logZ,
+                            const int32_t *tokens, int32_t conf_mode, float *q, float *conf,
+                            void *ws, size_t ws_bytes, int32_t *row_status, fa_stream_t stream)
+{
+    int rc = ready(t);
+    if (rc) return rc;
+    Geometry g;
+    if (!make_geometry(t->h, B, L, &g)) return FA_EINVAL;
+    if (!grid_fits(g)) return FA_ETOOBIG;
+    if (conf_mode != FA_CONF_PROB && conf_mode != FA_CONF_NEGENT) return FA_EINVAL;
+    if (B == 0 || L == 0) return FA_OK;
+    WsLayout w = ws_layout(t->h, g);
+    if (!p || !tree || !meta || !logZ || !conf || !row_status || !ws || ws_bytes < w.total)
+        return FA_EINVAL;
+    if (conf_mode == FA_CONF_PROB && !tokens) return FA_EINVAL;
+    return hip_rc(launch_marginals(t->h.device_view(), g, p, tree, meta, logZ, tokens, conf_mode, q,
+                                   conf, (uint8_t *)ws, w, row_status, stream));
+}
+
+extern "C" const char *fa_strerror(int code)
+{
+    switch (code) {
+    case FA_OK: return "ok";
+    case FA_EINVAL: return "invalid argument (size, id, range, pointer or workspace)";
+    case FA_ENOTDET: return "automaton flagged deterministic has two edges for one (state, token)";
+    case FA_ETOOBIG: return "size exceeds what the kernels index";
+    case FA_EHIP: return "HIP call or kernel launch failed";
+    case FA_ESTATE: return "table not uploaded";
+    default: return "unknown error";
+    }
+}

@@ -1,0 +1,138 @@
+// Internal declarations shared by the host table compiler, the C-ABI entry
+// points and the gfx950 kernels.  Not part of the public interface.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "../../include/fa.h"
+
+namespace fa {
+
+constexpr int kSpAlign = 64;       // trimmed state count padded to this
+constexpr int kNeg = -(1 << 29);   // exponent of an all-zero row/column
+constexpr int kDenseMax = 32;      // dense-label pairs share one mask word per token
+constexpr int kSelMax = 8192;      // LIST tokens gathered through a compact copy of p
+
+enum PairClass : int32_t { kList = 0, kDense = 1, kRange = 2 };
+
+// Device view of a compiled automaton.  All pointers address the caller's
+// device buffer; passed to kernels by value.
+struct DevTable {
+    int32_t S;       // kept states
+    int32_t Sp;      // padded
+    int32_t V;
+    int32_t start;   // compact
+    int32_t n_acc;
+    int32_t npairs;
+    int32_t nsel;
+    int32_t use_sel;
+    int32_t ndense;
+    int32_t nseg;
+    int32_t ncut;
+    int32_t has_cnt;
+    const int32_t *acc;        // [n_acc] ascending compact ids
+    const int32_t *orig;       // [S] compact -> original id
+    const int32_t *pair_a;     // [npairs] sorted by (a, b)
+    const int32_t *pair_b;
+    const int32_t *row_ptr;    // [S+1] pairs of source a
+    const int32_t *col_ptr;    // [S+1] into col_pairs
+    const int32_t *col_pairs;  // [npairs] pair ids sorted by (b, a)
+    const int32_t *pair_cls;   // [npairs] PairClass
+    const int32_t *pair_aux;   // dense index of a dense pair, else -1
+    const int32_t *list_off;   // [npairs+1]
+    const int32_t *list_tok;   // raw token ids
+    const int32_t *list_sel;   // index into sel_tok
+    const float *list_cnt;     // counts (nullptr when every count is 1)
+    const int32_t *sel_tok;    // [nsel] sorted unique LIST tokens
+    const int32_t *tm_off;     // [nsel+1] token-major LIST entries
+    const int32_t *tm_pair;
+    const float *tm_cnt;       // nullptr when every count is 1
+    const int32_t *dense_pair; // [ndense]
+    const uint32_t *tokmask;   // [V] bit j set: v in the label of dense pair j
+    const int32_t *seg_off;    // [npairs+1] disjoint segments of a RANGE pair
+    const int32_t *seg_lo;     // [nseg]
+    const int32_t *seg_hi;
+    const float *seg_cnt;
+    const int32_t *seg_lo_cut; // index of seg_lo in cuts
+    const int32_t *seg_hi_cut;
+    const int32_t *cuts;       // [ncut] sorted unique segment endpoints
+    const int32_t *cut_off;    // [ncut+1] segment events at each cut
+    const int32_t *cut_ev;     // 2*seg (start) or 2*seg+1 (end)
+    const int32_t *tok2sel;    // [V] index into sel_tok or -1 (nsel > 0)
+    const int32_t *tok2cut;    // [V] largest c with cuts[c] <= v, or -1 (nseg > 0)
+    const int32_t *seg_pair;   // [nseg] pair of each segment
+};
+
+// Host representation of a compiled automaton and its device image.
+struct HostTable {
+    int32_t S_orig = 0, V = 0, S = 0, Sp = 0, start = 0;
+    std::vector<int32_t> acc, orig;
+    std::vector<int32_t> pair_a, pair_b, row_ptr, col_ptr, col_pairs, pair_cls, pair_aux;
+    std::vector<int32_t> list_off, list_tok, list_sel;
+    std::vector<float> list_cnt;
+    std::vector<int32_t> sel_tok, tm_off, tm_pair;
+    std::vector<float> tm_cnt;
+    std::vector<int32_t> dense_pair;
+    std::vector<uint32_t> tokmask;
+    std::vector<int32_t> seg_off, seg_lo, seg_hi, seg_lo_cut, seg_hi_cut, cuts, cut_off, cut_ev;
+    std::vector<float> seg_cnt;
+    std::vector<int32_t> tok2sel, tok2cut, seg_pair;
+    bool has_cnt = false;
+    bool use_sel = false;
+    // device image
+    std::vector<uint8_t> image;
+    std::vector<size_t> offs;  // section offsets, in the order of DevTable pointers
+    void *dev = nullptr;
+    size_t dev_bytes = 0;
+
+    int32_t npairs() const { return (int32_t)pair_a.size(); }
+    int32_t ndense() const { return (int32_t)dense_pair.size(); }
+    int32_t nseg() const { return (int32_t)seg_lo.size(); }
+    int32_t ncut() const { return (int32_t)cuts.size(); }
+    int32_t nsel() const { return (int32_t)sel_tok.size(); }
+    bool needs_stream() const { return ndense() > 0 || nseg() > 0; }
+    DevTable device_view() const;
+};
+
+// Step geometry shared by all calls.
+struct Geometry {
+    int32_t B, L, Lpad, K, Sp;
+    size_t mat;          // floats per matrix = Sp*Sp
+    size_t tree_floats;  // B * 2*Lpad * mat
+    size_t meta_ints;    // B * 2*Lpad * 3 * Sp
+};
+
+bool make_geometry(const HostTable &t, int32_t B, int32_t L, Geometry *g);
+
+// Workspace layout (bytes from the start of ws), sized for the largest user.
+struct WsLayout {
+    size_t dval = 0, psel = 0, cutp = 0;       // emission reduce
+    size_t zc = 0;                             // sampler: compact boundary states
+    size_t va = 0, ea = 0, vb = 0, eb = 0;     // marginals: messages
+    size_t rcut = 0;                           // marginals: range weights per cut
+    size_t total = 0;
+};
+WsLayout ws_layout(const HostTable &t, const Geometry &g);
+
+// Kernel launchers (kernels.hip).  Return 0 or a hipError_t value.
+int launch_build_transitions(const DevTable &d, const Geometry &g, const float *p, float *tree,
+                             int32_t *meta, uint8_t *ws, const WsLayout &w, int32_t *status,
+                             void *stream);
+int launch_span_tree(const DevTable &d, const Geometry &g, float *tree, int32_t *meta,
+                     double *logZ, int32_t *status, void *stream);
+int launch_sample(const DevTable &d, const Geometry &g, const float *p, const float *tree,
+                  const int32_t *meta, uint64_t seed, int32_t *states, int32_t *tokens,
+                  uint8_t *ws, const WsLayout &w, int32_t *status, void *stream);
+int launch_marginals(const DevTable &d, const Geometry &g, const float *p, const float *tree,
+                     const int32_t *meta, const double *logZ, const int32_t *tokens,
+                     int32_t conf_mode, float *q, float *conf, uint8_t *ws, const WsLayout &w,
+                     int32_t *status, void *stream);
+
+}  // namespace fa
+
+struct fa_table {
+    fa::HostTable h;
+};

@@ -1,0 +1,535 @@
+// Host-side automaton compiler: validation, dead-state trimming, the
+// state-pair form of the edge chain model, the three label encodings
+// (token lists, dense token masks, token ranges), the token-major inverse
+// used by the marginals, and the device image.
+//
+// The state-pair form: a path over edges visits states, and the weight of
+// an edge path summed over the edges between two consecutive states is
+// c(a, v, b) = #{edges a->b whose label holds v}; this counts accepting edge
+// paths exactly, so strings keep the weight the chain over edges gives them
+// (paperfeed summary, "The insight: the constraint is a hidden Markov model";
+// NFA path counting, "Arbitrary schedules and NFAs").
+#include <algorithm>
+#include <cstring>
+#include <limits>
+#include <new>
+#include <numeric>
+#include <stdexcept>
+
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+struct Err {
+    int code;
+};
+
+template <class T>
+void append_section(std::vector<uint8_t> &img, std::vector<size_t> &offs, const std::vector<T> &v)
+{
+    size_t off = (img.size() + 255) & ~size_t(255);
+    img.resize(off + v.size() * sizeof(T));
+    if (!v.empty()) std::memcpy(img.data() + off, v.data(), v.size() * sizeof(T));
+    offs.push_back(off);
+}
+
+void build_image(HostTable &t)
+{
+    t.image.clear();
+    t.offs.clear();
+    append_section(t.image, t.offs, t.acc);
+    append_section(t.image, t.offs, t.orig);
+    append_section(t.image, t.offs, t.pair_a);
+    append_section(t.image, t.offs, t.pair_b);
+    append_section(t.image, t.offs, t.row_ptr);
+    append_section(t.image, t.offs, t.col_ptr);
+    append_section(t.image, t.offs, t.col_pairs);
+    append_section(t.image, t.offs, t.pair_cls);
+    append_section(t.image, t.offs, t.pair_aux);
+    append_section(t.image, t.offs, t.list_off);
+    append_section(t.image, t.offs, t.list_tok);
+    append_section(t.image, t.offs, t.list_sel);
+    append_section(t.image, t.offs, t.list_cnt);
+    append_section(t.image, t.offs, t.sel_tok);
+    append_section(t.image, t.offs, t.tm_off);
+    append_section(t.image, t.offs, t.tm_pair);
+    append_section(t.image, t.offs, t.tm_cnt);
+    append_section(t.image, t.offs, t.dense_pair);
+    append_section(t.image, t.offs, t.tokmask);
+    append_section(t.image, t.offs, t.seg_off);
+    append_section(t.image, t.offs, t.seg_lo);
+    append_section(t.image, t.offs, t.seg_hi);
+    append_section(t.image, t.offs, t.seg_cnt);
+    append_section(t.image, t.offs, t.seg_lo_cut);
+    append_section(t.image, t.offs, t.seg_hi_cut);
+    append_section(t.image, t.offs, t.cuts);
+    append_section(t.image, t.offs, t.cut_off);
+    append_section(t.image, t.offs, t.cut_ev);
+    append_section(t.image, t.offs, t.tok2sel);
+    append_section(t.image, t.offs, t.tok2cut);
+    append_section(t.image, t.offs, t.seg_pair);
+    t.image.resize((t.image.size() + 255) & ~size_t(255));
+}
+
+}  // namespace
+
+DevTable HostTable::device_view() const
+{
+    DevTable d{};
+    d.S = S;
+    d.Sp = Sp;
+    d.V = V;
+    d.start = start;
+    d.n_acc = (int32_t)acc.size();
+    d.npairs = npairs();
+    d.nsel = nsel();
+    d.use_sel = use_sel ? 1 : 0;
+    d.ndense = ndense();
+    d.nseg = nseg();
+    d.ncut = ncut();
+    d.has_cnt = has_cnt ? 1 : 0;
+    const uint8_t *b = static_cast<const uint8_t *>(dev);
+    size_t k = 0;
+    auto nxt = [&](auto *&ptr) {
+        ptr = reinterpret_cast<std::remove_reference_t<decltype(ptr)>>(b + offs[k++]);
+    };
+    nxt(d.acc); nxt(d.orig); nxt(d.pair_a); nxt(d.pair_b); nxt(d.row_ptr); nxt(d.col_ptr);
+    nxt(d.col_pairs); nxt(d.pair_cls); nxt(d.pair_aux); nxt(d.list_off); nxt(d.list_tok);
+    nxt(d.list_sel); nxt(d.list_cnt); nxt(d.sel_tok); nxt(d.tm_off); nxt(d.tm_pair);
+    nxt(d.tm_cnt); nxt(d.dense_pair); nxt(d.tokmask); nxt(d.seg_off); nxt(d.seg_lo);
+    nxt(d.seg_hi); nxt(d.seg_cnt); nxt(d.seg_lo_cut); nxt(d.seg_hi_cut); nxt(d.cuts);
+    nxt(d.cut_off); nxt(d.cut_ev); nxt(d.tok2sel); nxt(d.tok2cut); nxt(d.seg_pair);
+    if (!has_cnt) {
+        d.list_cnt = nullptr;
+        d.tm_cnt = nullptr;
+    }
+    return d;
+}
+
+bool make_geometry(const HostTable &t, int32_t B, int32_t L, Geometry *g)
+{
+    if (B < 0 || L < 0) return false;
+    int32_t Lpad = 1, K = 0;
+    while (Lpad < L) {
+        Lpad <<= 1;
+        ++K;
+    }
+    g->B = B;
+    g->L = L;
+    g->Lpad = Lpad;
+    g->K = K;
+    g->Sp = t.Sp;
+    g->mat = (size_t)t.Sp * t.Sp;
+    g->tree_floats = L > 0 ? (size_t)B * 2 * Lpad * g->mat : 0;
+    g->meta_ints = L > 0 ? (size_t)B * 2 * Lpad * 3 * t.Sp : 0;
+    return true;
+}
+
+WsLayout ws_layout(const HostTable &t, const Geometry &g)
+{
+    auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+    WsLayout w;
+    size_t BL = (size_t)g.B * g.L;
+    size_t o = 0;  // emission reduce region
+    w.dval = o; o = al(o + BL * t.ndense() * sizeof(float));
+    w.psel = o; o = al(o + (t.use_sel ? BL * t.nsel() * sizeof(float) : 0));
+    w.cutp = o; o = al(o + BL * t.ncut() * sizeof(double));
+    size_t a1 = o;
+    o = 0;  // sampler region
+    w.zc = o; o = al(o + (size_t)g.B * (g.Lpad + 1) * sizeof(int32_t));
+    size_t a3 = o;
+    o = 0;  // marginals region
+    size_t nv = (size_t)g.B * (g.Lpad + 1);
+    w.va = o; o = al(o + nv * g.Sp * sizeof(float));
+    w.vb = o; o = al(o + nv * g.Sp * sizeof(float));
+    w.ea = o; o = al(o + nv * sizeof(int32_t));
+    w.eb = o; o = al(o + nv * sizeof(int32_t));
+    w.rcut = o; o = al(o + BL * t.ncut() * sizeof(float));
+    size_t a4 = o;
+    w.total = std::max(a1, std::max(a3, a4));
+    if (w.total == 0) w.total = 256;
+    return w;
+}
+
+static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, int32_t n_accept,
+                   int64_t E, const int32_t *src, const int32_t *dst, const int64_t *label_off,
+                   const int32_t *label_tok, uint32_t flags, HostTable &t)
+{
+    const bool ranges = flags & FA_LABEL_RANGES;
+    if (S < 1 || V < 1 || start < 0 || start >= S || n_accept < 0 || E < 0) return FA_EINVAL;
+    if ((n_accept > 0 && !accept) || (E > 0 && (!src || !dst || !label_off))) return FA_EINVAL;
+    if ((flags & FA_DFA) && (flags & FA_NFA)) return FA_EINVAL;
+    if (flags & ~uint32_t(FA_DFA | FA_NFA | FA_LABEL_RANGES | FA_NO_TRIM)) return FA_EINVAL;
+    if (E > std::numeric_limits<int32_t>::max()) return FA_ETOOBIG;
+    if (E > 0 && label_off[0] != 0) return FA_EINVAL;
+    for (int32_t k = 0; k < n_accept; ++k)
+        if (accept[k] < 0 || accept[k] >= S) return FA_EINVAL;
+    if (E > 0 && label_off[E] > 0 && !label_tok) return FA_EINVAL;
+
+    // per-edge labels: sorted unique tokens, or sorted disjoint ranges
+    std::vector<std::vector<int32_t>> lab((size_t)E);
+    for (int64_t e = 0; e < E; ++e) {
+        if (src[e] < 0 || src[e] >= S || dst[e] < 0 || dst[e] >= S) return FA_EINVAL;
+        int64_t b0 = label_off[e], b1 = label_off[e + 1];
+        if (b1 < b0) return FA_EINVAL;
+        std::vector<int32_t> &L = lab[(size_t)e];
+        if (ranges) {
+            if ((b1 - b0) % 2) return FA_EINVAL;
+            std::vector<std::pair<int32_t, int32_t>> rr;
+            for (int64_t k = b0; k < b1; k += 2) {
+                int32_t lo = label_tok[k], hi = label_tok[k + 1];
+                if (lo < 0 || hi > V || lo > hi) return FA_EINVAL;
+                if (lo < hi) rr.emplace_back(lo, hi);
+            }
+            std::sort(rr.begin(), rr.end());
+            for (size_t k = 1; k < rr.size(); ++k)
+                if (rr[k].first < rr[k - 1].second) return FA_EINVAL;
+            for (auto &r : rr) {
+                L.push_back(r.first);
+                L.push_back(r.second);
+            }
+        } else {
+            L.assign(label_tok + b0, label_tok + b1);
+            for (int32_t v : L)
+                if (v < 0 || v >= V) return FA_EINVAL;
+            std::sort(L.begin(), L.end());
+            L.erase(std::unique(L.begin(), L.end()), L.end());
+        }
+    }
+    // determinism check on the whole input automaton
+    if (flags & FA_DFA) {
+        if (ranges) {
+            std::vector<std::vector<std::pair<int32_t, int32_t>>> per(S);
+            for (int64_t e = 0; e < E; ++e)
+                for (size_t k = 0; k < lab[e].size(); k += 2) per[src[e]].emplace_back(lab[e][k], lab[e][k + 1]);
+            for (auto &v : per) {
+                std::sort(v.begin(), v.end());
+                for (size_t k = 1; k < v.size(); ++k)
+                    if (v[k].first < v[k - 1].second) return FA_ENOTDET;
+            }
+        } else {
+            std::vector<uint64_t> keys;
+            for (int64_t e = 0; e < E; ++e)
+                for (int32_t v : lab[e]) keys.push_back(((uint64_t)(uint32_t)src[e] << 32) | (uint32_t)v);
+            std::sort(keys.begin(), keys.end());
+            for (size_t k = 1; k < keys.size(); ++k)
+                if (keys[k] == keys[k - 1]) return FA_ENOTDET;
+        }
+    }
+    // trimming: reachable from start and co-reachable to F over non-empty edges
+    std::vector<char> fwd(S, 0), bwd(S, 0), keep(S, 1);
+    if (!(flags & FA_NO_TRIM)) {
+        std::vector<std::vector<int32_t>> out(S), in(S);
+        for (int64_t e = 0; e < E; ++e)
+            if (!lab[e].empty()) {
+                out[src[e]].push_back(dst[e]);
+                in[dst[e]].push_back(src[e]);
+            }
+        std::vector<int32_t> st{start};
+        fwd[start] = 1;
+        while (!st.empty()) {
+            int32_t a = st.back();
+            st.pop_back();
+            for (int32_t b : out[a]) if (!fwd[b]) { fwd[b] = 1; st.push_back(b); }
+        }
+        for (int32_t k = 0; k < n_accept; ++k)
+            if (!bwd[accept[k]]) { bwd[accept[k]] = 1; st.push_back(accept[k]); }
+        while (!st.empty()) {
+            int32_t b = st.back();
+            st.pop_back();
+            for (int32_t a : in[b]) if (!bwd[a]) { bwd[a] = 1; st.push_back(a); }
+        }
+        for (int32_t s = 0; s < S; ++s) keep[s] = fwd[s] && bwd[s];
+        keep[start] = 1;
+    }
+    std::vector<int32_t> cid(S, -1);
+    t.orig.clear();
+    for (int32_t s = 0; s < S; ++s)
+        if (keep[s]) {
+            cid[s] = (int32_t)t.orig.size();
+            t.orig.push_back(s);
+        }
+    t.S_orig = S;
+    t.V = V;
+    t.S = (int32_t)t.orig.size();
+    t.Sp = (t.S + kSpAlign - 1) / kSpAlign * kSpAlign;
+    t.start = cid[start];
+    t.acc.clear();
+    for (int32_t k = 0; k < n_accept; ++k)
+        if (cid[accept[k]] >= 0) t.acc.push_back(cid[accept[k]]);
+    std::sort(t.acc.begin(), t.acc.end());
+    t.acc.erase(std::unique(t.acc.begin(), t.acc.end()), t.acc.end());
+
+    // edges between kept states, grouped by (a, b)
+    std::vector<int64_t> eids;
+    for (int64_t e = 0; e < E; ++e)
+        if (!lab[e].empty() && cid[src[e]] >= 0 && cid[dst[e]] >= 0) eids.push_back(e);
+    std::sort(eids.begin(), eids.end(), [&](int64_t x, int64_t y) {
+        int32_t ax = cid[src[x]], ay = cid[src[y]], bx = cid[dst[x]], by = cid[dst[y]];
+        return ax != ay ? ax < ay : (bx != by ? bx < by : x < y);
+    });
+    t.pair_a.clear(); t.pair_b.clear(); t.pair_cls.clear(); t.pair_aux.clear();
+    t.list_off.assign(1, 0); t.list_tok.clear(); t.list_cnt.clear();
+    t.seg_off.assign(1, 0); t.seg_lo.clear(); t.seg_hi.clear(); t.seg_cnt.clear();
+    t.has_cnt = false;
+    std::vector<int64_t> pair_size;
+    std::vector<int32_t> maxcnt;
+    for (size_t k0 = 0; k0 < eids.size();) {
+        size_t k1 = k0;
+        int32_t a = cid[src[eids[k0]]], b = cid[dst[eids[k0]]];
+        while (k1 < eids.size() && cid[src[eids[k1]]] == a && cid[dst[eids[k1]]] == b) ++k1;
+        t.pair_a.push_back(a);
+        t.pair_b.push_back(b);
+        if (ranges) {
+            // sweep the edges' ranges into disjoint segments with counts
+            std::vector<std::pair<int32_t, int32_t>> ev;  // (position, +1/-1)
+            for (size_t k = k0; k < k1; ++k) {
+                const auto &L = lab[eids[k]];
+                for (size_t r = 0; r < L.size(); r += 2) {
+                    ev.emplace_back(L[r], +1);
+                    ev.emplace_back(L[r + 1], -1);
+                }
+            }
+            std::sort(ev.begin(), ev.end());
+            int32_t depth = 0, mc = 0;
+            int64_t sz = 0;
+            for (size_t k = 0; k < ev.size();) {
+                int32_t x = ev[k].first;
+                int32_t before = depth;
+                while (k < ev.size() && ev[k].first == x) depth += ev[k++].second;
+                (void)before;
+                if (k < ev.size() && depth > 0) {
+                    int32_t y = ev[k].first;
+                    // merge with the previous segment if contiguous with equal count
+                    if (!t.seg_hi.empty() && (int64_t)t.seg_lo.size() > t.seg_off.back() &&
+                        t.seg_hi.back() == x && t.seg_cnt.back() == (float)depth)
+                        t.seg_hi.back() = y;
+                    else {
+                        t.seg_lo.push_back(x);
+                        t.seg_hi.push_back(y);
+                        t.seg_cnt.push_back((float)depth);
+                    }
+                    sz += (int64_t)(y - x) * depth;
+                    mc = std::max(mc, depth);
+                }
+            }
+            t.seg_off.push_back((int32_t)t.seg_lo.size());
+            t.list_off.push_back((int32_t)t.list_tok.size());
+            t.pair_cls.push_back(kRange);
+            pair_size.push_back(sz);
+            maxcnt.push_back(mc);
+            if (mc > 1) t.has_cnt = true;
+        } else {
+            std::vector<int32_t> all;
+            for (size_t k = k0; k < k1; ++k) all.insert(all.end(), lab[eids[k]].begin(), lab[eids[k]].end());
+            std::sort(all.begin(), all.end());
+            int32_t mc = 0;
+            for (size_t k = 0; k < all.size();) {
+                size_t k2 = k;
+                while (k2 < all.size() && all[k2] == all[k]) ++k2;
+                t.list_tok.push_back(all[k]);
+                t.list_cnt.push_back((float)(k2 - k));
+                mc = std::max(mc, (int32_t)(k2 - k));
+                k = k2;
+            }
+            if (t.list_tok.size() > (size_t)std::numeric_limits<int32_t>::max()) throw Err{FA_ETOOBIG};
+            t.list_off.push_back((int32_t)t.list_tok.size());
+            t.seg_off.push_back((int32_t)t.seg_lo.size());
+            t.pair_cls.push_back(kList);
+            pair_size.push_back((int64_t)all.size());
+            maxcnt.push_back(mc);
+            if (mc > 1) t.has_cnt = true;
+        }
+        t.pair_aux.push_back(-1);
+        k0 = k1;
+    }
+    const int32_t np = t.npairs();
+    // dense-mask class: the largest count-1 token lists
+    t.dense_pair.clear();
+    if (!ranges) {
+        int64_t dense_min = std::max<int64_t>(2048, V / 16);
+        std::vector<int32_t> cand;
+        for (int32_t q = 0; q < np; ++q)
+            if (maxcnt[q] == 1 && pair_size[q] >= dense_min) cand.push_back(q);
+        std::stable_sort(cand.begin(), cand.end(),
+                         [&](int32_t x, int32_t y) { return pair_size[x] > pair_size[y]; });
+        if ((int32_t)cand.size() > kDenseMax) cand.resize(kDenseMax);
+        std::sort(cand.begin(), cand.end());
+        for (int32_t q : cand) {
+            t.pair_cls[q] = kDense;
+            t.pair_aux[q] = (int32_t)t.dense_pair.size();
+            t.dense_pair.push_back(q);
+        }
+        // move dense pairs' tokens into the mask and out of the lists
+        t.tokmask.assign(t.ndense() ? (size_t)V : 0, 0u);
+        std::vector<int32_t> off2(1, 0), tok2;
+        std::vector<float> cnt2;
+        for (int32_t q = 0; q < np; ++q) {
+            if (t.pair_cls[q] == kDense) {
+                uint32_t bit = 1u << t.pair_aux[q];
+                for (int32_t k = t.list_off[q]; k < t.list_off[q + 1]; ++k) t.tokmask[t.list_tok[k]] |= bit;
+            } else {
+                tok2.insert(tok2.end(), t.list_tok.begin() + t.list_off[q], t.list_tok.begin() + t.list_off[q + 1]);
+                cnt2.insert(cnt2.end(), t.list_cnt.begin() + t.list_off[q], t.list_cnt.begin() + t.list_off[q + 1]);
+            }
+            off2.push_back((int32_t)tok2.size());
+        }
+        t.list_off.swap(off2);
+        t.list_tok.swap(tok2);
+        t.list_cnt.swap(cnt2);
+    } else {
+        t.tokmask.clear();
+    }
+    if (!t.has_cnt) t.list_cnt.clear();
+    // row and column orders of the pairs
+    t.row_ptr.assign(t.S + 1, 0);
+    t.col_ptr.assign(t.S + 1, 0);
+    for (int32_t q = 0; q < np; ++q) {
+        t.row_ptr[t.pair_a[q] + 1]++;
+        t.col_ptr[t.pair_b[q] + 1]++;
+    }
+    for (int32_t s = 0; s < t.S; ++s) {
+        t.row_ptr[s + 1] += t.row_ptr[s];
+        t.col_ptr[s + 1] += t.col_ptr[s];
+    }
+    t.col_pairs.resize(np);
+    std::iota(t.col_pairs.begin(), t.col_pairs.end(), 0);
+    std::stable_sort(t.col_pairs.begin(), t.col_pairs.end(), [&](int32_t x, int32_t y) {
+        return t.pair_b[x] != t.pair_b[y] ? t.pair_b[x] < t.pair_b[y] : t.pair_a[x] < t.pair_a[y];
+    });
+    // token-major inverse of the LIST pairs
+    t.sel_tok = t.list_tok;
+    std::sort(t.sel_tok.begin(), t.sel_tok.end());
+    t.sel_tok.erase(std::unique(t.sel_tok.begin(), t.sel_tok.end()), t.sel_tok.end());
+    const int32_t ns = t.nsel();
+    t.list_sel.resize(t.list_tok.size());
+    for (size_t k = 0; k < t.list_tok.size(); ++k)
+        t.list_sel[k] = (int32_t)(std::lower_bound(t.sel_tok.begin(), t.sel_tok.end(), t.list_tok[k]) - t.sel_tok.begin());
+    t.tm_off.assign(ns + 1, 0);
+    for (int32_t s : t.list_sel) t.tm_off[s + 1]++;
+    for (int32_t s = 0; s < ns; ++s) t.tm_off[s + 1] += t.tm_off[s];
+    t.tm_pair.resize(t.list_tok.size());
+    t.tm_cnt.assign(t.has_cnt ? t.list_tok.size() : 0, 1.f);
+    {
+        std::vector<int32_t> fill(t.tm_off.begin(), t.tm_off.end() - 1);
+        for (int32_t q = 0; q < np; ++q)
+            for (int32_t k = t.list_off[q]; k < t.list_off[q + 1]; ++k) {
+                int32_t pos = fill[t.list_sel[k]]++;
+                t.tm_pair[pos] = q;
+                if (t.has_cnt) t.tm_cnt[pos] = t.list_cnt[k];
+            }
+    }
+    // range cut points and events
+    t.cuts.clear();
+    for (size_t s = 0; s < t.seg_lo.size(); ++s) {
+        t.cuts.push_back(t.seg_lo[s]);
+        t.cuts.push_back(t.seg_hi[s]);
+    }
+    std::sort(t.cuts.begin(), t.cuts.end());
+    t.cuts.erase(std::unique(t.cuts.begin(), t.cuts.end()), t.cuts.end());
+    t.seg_lo_cut.resize(t.seg_lo.size());
+    t.seg_hi_cut.resize(t.seg_lo.size());
+    for (size_t s = 0; s < t.seg_lo.size(); ++s) {
+        t.seg_lo_cut[s] = (int32_t)(std::lower_bound(t.cuts.begin(), t.cuts.end(), t.seg_lo[s]) - t.cuts.begin());
+        t.seg_hi_cut[s] = (int32_t)(std::lower_bound(t.cuts.begin(), t.cuts.end(), t.seg_hi[s]) - t.cuts.begin());
+    }
+    t.cut_off.assign(t.ncut() + 1, 0);
+    for (size_t s = 0; s < t.seg_lo.size(); ++s) {
+        t.cut_off[t.seg_lo_cut[s] + 1]++;
+        t.cut_off[t.seg_hi_cut[s] + 1]++;
+    }
+    for (int32_t c = 0; c < t.ncut(); ++c) t.cut_off[c + 1] += t.cut_off[c];
+    t.cut_ev.resize(2 * t.seg_lo.size());
+    {
+        std::vector<int32_t> fill(t.cut_off.begin(), t.cut_off.end() - 1);
+        for (size_t s = 0; s < t.seg_lo.size(); ++s) {
+            t.cut_ev[fill[t.seg_lo_cut[s]]++] = (int32_t)(2 * s);
+            t.cut_ev[fill[t.seg_hi_cut[s]]++] = (int32_t)(2 * s + 1);
+        }
+    }
+    if (!t.has_cnt) t.seg_cnt.assign(t.seg_lo.size(), 1.f);
+    t.seg_pair.resize(t.seg_lo.size());
+    for (int32_t q = 0; q < np; ++q)
+        for (int32_t s = t.seg_off[q]; s < t.seg_off[q + 1]; ++s) t.seg_pair[s] = q;
+    t.tok2sel.assign(ns > 0 ? (size_t)V : 0, -1);
+    for (int32_t s = 0; s < ns; ++s) t.tok2sel[t.sel_tok[s]] = s;
+    t.tok2cut.assign(t.ncut() > 0 ? (size_t)V : 0, -1);
+    for (int32_t c = 0, v = 0; v < (t.ncut() > 0 ? V : 0); ++v) {
+        while (c < t.ncut() && t.cuts[c] <= v) ++c;
+        t.tok2cut[v] = c - 1;
+    }
+    t.use_sel = t.needs_stream() && ns > 0 && ns <= kSelMax;
+    build_image(t);
+    return FA_OK;
+}
+
+}  // namespace fa
+
+using namespace fa;
+
+extern "C" int fa_compile_table(int32_t S, int32_t V, int32_t start, const int32_t *accept,
+                                int32_t n_accept, int64_t E, const int32_t *src, const int32_t *dst,
+                                const int64_t *label_off, const int32_t *label_tok, uint32_t flags,
+                                fa_table **out, size_t *device_bytes)
+{
+    if (!out) return FA_EINVAL;
+    *out = nullptr;
+    fa_table *t = nullptr;
+    try {
+        t = new fa_table();
+        int rc = compile(S, V, start, accept, n_accept, E, src, dst, label_off, label_tok, flags, t->h);
+        if (rc != FA_OK) {
+            delete t;
+            return rc;
+        }
+    } catch (const Err &e) {
+        delete t;
+        return e.code;
+    } catch (const std::bad_alloc &) {
+        delete t;
+        return FA_ETOOBIG;
+    } catch (...) {
+        delete t;
+        return FA_EINVAL;
+    }
+    *out = t;
+    if (device_bytes) *device_bytes = t->h.image.size();
+    return FA_OK;
+}
+
+extern "C" void fa_table_destroy(fa_table *t) { delete t; }
+
+extern "C" int fa_table_info(const fa_table *t, int64_t *info, int32_t n)
+{
+    if (!t || (!info && n > 0) || n < 0) return FA_EINVAL;
+    const HostTable &h = t->h;
+    int32_t nl = 0, nd = 0, nr = 0;
+    for (int32_t c : h.pair_cls) (c == kList ? nl : c == kDense ? nd : nr)++;
+    int64_t v[15] = {h.S, h.Sp, h.start, (int64_t)h.acc.size(), h.npairs(), nl, nd, nr,
+                     (int64_t)h.list_tok.size(), h.nseg(), h.ncut(), h.nsel(), h.use_sel ? 1 : 0,
+                     h.V, h.S_orig};
+    for (int32_t k = 0; k < n && k < 15; ++k) info[k] = v[k];
+    return FA_OK;
+}
+
+extern "C" int fa_table_state_map(const fa_table *t, int32_t *orig_of)
+{
+    if (!t || !orig_of) return FA_EINVAL;
+    std::memcpy(orig_of, t->h.orig.data(), t->h.orig.size() * sizeof(int32_t));
+    return FA_OK;
+}
+
+extern "C" int fa_sizes(const fa_table *t, int32_t B, int32_t L, size_t *tree_bytes,
+                        size_t *meta_bytes, size_t *ws_bytes)
+{
+    if (!t) return FA_EINVAL;
+    Geometry g;
+    if (!make_geometry(t->h, B, L, &g)) return FA_EINVAL;
+    if ((size_t)g.Lpad * g.Sp > (size_t)1 << 40) return FA_ETOOBIG;
+    if ((int64_t)B * g.Lpad * 2 > 65535 || L >= (1 << 24)) return FA_ETOOBIG;
+    if (tree_bytes) *tree_bytes = g.tree_floats * sizeof(float);
+    if (meta_bytes) *meta_bytes = g.meta_ints * sizeof(int32_t);
+    if (ws_bytes) *ws_bytes = ws_layout(t->h, g).total;
+    return FA_OK;
+}

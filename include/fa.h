@@ -1,0 +1,237 @@
+/*
+ * fa.h - C ABI of the finite-automaton-constrained sampler for one
+ * denoising step of a diffusion language model, for AMD MI355X (gfx950).
+ *
+ * The operation, from "Constrained Decoding for Diffusion Language Models via
+ * Efficient Inference over Finite Automata" (paperfeed.app summary, sections
+ * "The insight: the constraint is a hidden Markov model" and "The scan trick:
+ * log-depth exact sampling"; papernotes.org summary, 关键设计 1-3):
+ *   given per-position token probabilities p[b][i][v] (the denoiser's
+ *   mean-field prediction) and an automaton M = (S, V, delta, s0, F), draw
+ *   x ~ prod_i p[i][x_i] * paths(x) / Z, where paths(x) is the number of
+ *   accepting paths of x (1 or 0 for a DFA), and return log Z, the sampled
+ *   boundary states z_0..z_L and tokens, the constrained per-token marginals
+ *   q[b][i][v] and the confidence score used for remasking.
+ *
+ * One step is four calls on one stream: fa_build_transitions (emission
+ * reduce into per-position transition matrices), fa_span_tree (bottom-up
+ * 2^k-span products and log Z), fa_sample (top-down midpoint draws, then
+ * parallel token draws), fa_marginals (constrained marginals and confidence).
+ *
+ * Ownership: the caller owns every device buffer and the stream.  The
+ * library owns only the host-side fa_table; it never allocates device memory
+ * and never synchronizes the stream.  Calls are asynchronous on `stream`
+ * (a hipStream_t; NULL is the default stream).  Distinct buffers may be used
+ * concurrently from different streams; one table may be shared.
+ *
+ * Errors: every call returns FA_OK or a synchronous error code; on a
+ * synchronous error nothing is launched.  Data-dependent conditions are
+ * OR-ed asynchronously into row_status[b] (FA_ROW_*); the caller clears
+ * row_status before a step.  Rows with a status bit set get states/tokens
+ * -1, q = 0, conf = -inf and logZ = -inf.  No C++ exception crosses this
+ * interface.
+ *
+ * Layout (all device arrays row-major, C order):
+ *   p      float  [B][L][V]
+ *   tree   float  [B][2*Lpad][Sp][Sp]   heap order: node 1 = root over
+ *                 [0, Lpad), node n has children 2n (left) and 2n+1 (right),
+ *                 leaves Lpad + i hold the transition matrix of position i
+ *                 (identity for i >= L).  Nodes with an odd index >= 3 are
+ *                 stored transposed, all others as is.
+ *   meta   int32  [B][2*Lpad][3][Sp]    per stored row/column power-of-two
+ *                 exponents of every node (row scale, column scale, row
+ *                 fold normalizer); the true matrix is
+ *                 diag(2^ro) P diag(2^co) in stored orientation.
+ *   states int32  [B][L+1]  original state ids z_0 = s0 .. z_L
+ *   tokens int32  [B][L]
+ *   q      float  [B][L][V]
+ *   conf   float  [B][L]
+ *   logZ   double [B]
+ * Lpad = smallest power of two >= L; Sp = trimmed state count rounded up to
+ * a multiple of 64 (padding rows and columns are zero).  Sizes come from
+ * fa_sizes().
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *fa_stream_t; /* a hipStream_t */
+typedef struct fa_table fa_table;
+
+enum {
+    FA_OK = 0,
+    FA_EINVAL = 1,  /* bad size, id, range, pointer or workspace */
+    FA_ENOTDET = 2, /* FA_DFA given but some (state, token) has two edges */
+    FA_ETOOBIG = 3, /* a size exceeds what the kernels index */
+    FA_EHIP = 4,    /* a HIP call or launch failed */
+    FA_ESTATE = 5   /* table not uploaded */
+};
+
+enum { FA_ROW_INFEASIBLE = 1, FA_ROW_UNDERFLOW = 2, FA_ROW_BADPROB = 4 };
+
+enum {
+    FA_DFA = 1,          /* check determinism */
+    FA_NFA = 2,          /* strings weighted by their number of accepting paths */
+    FA_LABEL_RANGES = 4, /* label_tok holds flat half-open [lo, hi) pairs */
+    FA_NO_TRIM = 8       /* keep states unreachable from s0 or unable to reach F */
+};
+
+enum { FA_CONF_PROB = 0, FA_CONF_NEGENT = 1 };
+
+/*
+ * fa_compile_table - validate and compile an automaton (host only).
+ * Cite: the automaton as a chain model, paperfeed summary "The insight: the
+ * constraint is a hidden Markov model"; NFAs, "Arbitrary schedules and
+ * NFAs"; papernotes 整体框架 (M = (S, V, delta, s0, F)).
+ *   S, V            state and vocabulary sizes (>= 1)
+ *   start           s0 in [0, S)
+ *   accept          n_accept accepting state ids in [0, S) (host pointer)
+ *   E, src, dst     edge list, ids in [0, S) (host pointers)
+ *   label_off       E+1 non-decreasing offsets into label_tok, label_off[0]=0
+ *   label_tok       token ids in [0, V) (a label is a set: repeats count
+ *                   once), or with FA_LABEL_RANGES flat [lo, hi) pairs with
+ *                   0 <= lo <= hi <= V, disjoint within one edge
+ *   flags           FA_DFA | FA_NFA | FA_LABEL_RANGES | FA_NO_TRIM
+ *   out             receives the handle (free with fa_table_destroy)
+ *   device_bytes    receives the size of the device image
+ * Dead states (unreachable from s0 or unable to reach F) are removed unless
+ * FA_NO_TRIM; state order is preserved, so ascending compact ids are
+ * ascending original ids.  Errors: FA_EINVAL, FA_ENOTDET, FA_ETOOBIG.
+ */
+int fa_compile_table(int32_t S, int32_t V, int32_t start, const int32_t *accept,
+                     int32_t n_accept, int64_t E, const int32_t *src, const int32_t *dst,
+                     const int64_t *label_off, const int32_t *label_tok, uint32_t flags,
+                     fa_table **out, size_t *device_bytes);
+
+/*
+ * fa_table_upload - copy the compiled image into dev_buf (device memory of at
+ * least device_bytes, 256-byte aligned, owned by the caller, which must
+ * outlive every later call with this table) with one asynchronous
+ * host-to-device copy on `stream`.  The handle keeps the host image alive.
+ * Errors: FA_EINVAL, FA_EHIP.
+ */
+int fa_table_upload(fa_table *t, void *dev_buf, size_t bytes, fa_stream_t stream);
+
+/* fa_table_destroy - free the host handle (not the caller's device buffer). */
+void fa_table_destroy(fa_table *t);
+
+/*
+ * fa_table_info - host-side facts about a compiled table.  Writes up to n of:
+ * [0] S' (kept states), [1] Sp, [2] start (compact), [3] accepting states
+ * kept, [4] pairs, [5] LIST pairs, [6] DENSE pairs, [7] RANGE pairs,
+ * [8] LIST entries, [9] range segments, [10] cut points, [11] sel tokens,
+ * [12] 1 if LIST entries index the selected-token gather, [13] V,
+ * [14] S (original).  Returns FA_OK or FA_EINVAL.
+ */
+int fa_table_info(const fa_table *t, int64_t *info, int32_t n);
+
+/*
+ * fa_table_state_map - orig_of[k] = original id of compact state k, for k in
+ * [0, S').  Host pointer of S' entries.
+ */
+int fa_table_state_map(const fa_table *t, int32_t *orig_of);
+
+/*
+ * fa_sizes - bytes of the tree, meta and workspace buffers a step with batch
+ * B and length L needs.  Any output pointer may be NULL.  The workspace may be
+ * shared by all four calls of a step on one stream.  Errors: FA_EINVAL,
+ * FA_ETOOBIG.
+ */
+int fa_sizes(const fa_table *t, int32_t B, int32_t L, size_t *tree_bytes, size_t *meta_bytes,
+             size_t *ws_bytes);
+
+/*
+ * fa_build_transitions - emission reduce: for every row b and position i,
+ * M_i[s][s'] = sum_v c(s, v, s') p[b][i][v] with c the number of edges s->s'
+ * whose label holds v; leaves i >= L are the identity.
+ * Cite: papernotes 关键设计 1 (each position's state transition matrix sums
+ * the reweighted emissions over the vocabulary); paperfeed "The insight"
+ * (a factorized model times a chain model is a chain model; the |E||V| term).
+ *   p        device [B][L][V] fp32, read only (values must be >= 0; NaN or
+ *            negative entries that are read set FA_ROW_BADPROB)
+ *   tree     device, fa_sizes bytes; leaves written
+ *   meta     device, fa_sizes bytes; leaf exponents written
+ *   ws       device workspace of ws_bytes >= fa_sizes
+ *   row_status device int32 [B], OR-ed
+ * Errors: FA_EINVAL, FA_ESTATE, FA_EHIP.
+ */
+int fa_build_transitions(const fa_table *t, const float *p, int32_t B, int32_t L, float *tree,
+                         int32_t *meta, void *ws, size_t ws_bytes, int32_t *row_status,
+                         fa_stream_t stream);
+
+/*
+ * fa_span_tree - bottom-up span products: level by level every internal node
+ * n gets P_n = P_2n P_2n+1 (log2 Lpad levels of batched fp32 matrix
+ * products), with power-of-two row and column exponents so long chains
+ * neither underflow nor overflow; then
+ * logZ[b] = ln sum_{f in F} P_1[s0][f].
+ * Cite: paperfeed "The scan trick: log-depth exact sampling" (2^k-step
+ * transitions from 2^(k-1)-step ones in log L rounds of batched matrix
+ * multiplication); papernotes 关键设计 2.
+ *   tree, meta  written by fa_build_transitions; internal nodes written
+ *   logZ        device double [B]; -inf for infeasible rows
+ *   row_status  device int32 [B]; FA_ROW_INFEASIBLE when Z = 0
+ * Errors: FA_EINVAL, FA_ESTATE, FA_EHIP.
+ */
+int fa_span_tree(const fa_table *t, int32_t B, int32_t L, float *tree, int32_t *meta,
+                 double *logZ, int32_t *row_status, fa_stream_t stream);
+
+/*
+ * fa_sample - top-down exact sampling: z_Lpad ~ P_1[s0][f] over f in F (the
+ * start state is pinned), then for every segment [l, r) with known boundary
+ * states the midpoint m = (l+r)/2 by z_m ~ P_[l,m)[z_l][z_m] P_[m,r)[z_m][z_r],
+ * level by level, then every token x_i ~ p[b][i][v] c(z_i, v, z_{i+1}) in
+ * parallel.  Each draw is an inverse CDF over ascending candidate ids (the
+ * smallest j with w_j > 0 and C_j > u T, C the inclusive prefix sum, T its
+ * total) with u = (r0 >> 8) 2^-24, r0 the first word of Philox4x32-10 keyed by
+ * seed and counter (b, level, node, 0): level 0 the root draw, levels 1..K
+ * the midpoints (node = heap index - 2^(level-1)), level K+1 the tokens
+ * (node = i).
+ * Cite: paperfeed "The scan trick" (midpoint conditional independence,
+ * top-down pass, parallel token emission); papernotes 关键设计 2.
+ *   states  device int32 [B][L+1] original ids; tokens device int32 [B][L]
+ *   ws      workspace (>= fa_sizes)
+ *   row_status FA_ROW_UNDERFLOW if a draw's weights vanish while Z > 0
+ * Errors: FA_EINVAL, FA_ESTATE, FA_EHIP.
+ */
+int fa_sample(const fa_table *t, const float *p, int32_t B, int32_t L, const float *tree,
+              const int32_t *meta, uint64_t seed, int32_t *states, int32_t *tokens, void *ws,
+              size_t ws_bytes, int32_t *row_status, fa_stream_t stream);
+
+/*
+ * fa_marginals - constrained per-token marginals and the remasking
+ * confidence: forward/backward boundary messages alpha_i, beta_i from the
+ * span tree (top-down), then
+ *   q[b][i][v] = p[b][i][v] sum_{(a, a') pairs holding v} c alpha_i[a]
+ *                beta_{i+1}[a'] / Z,
+ *   conf[b][i] = q[b][i][tokens[b][i]]   (FA_CONF_PROB), or
+ *              = sum_v q ln q            (FA_CONF_NEGENT, 0 ln 0 = 0).
+ * Cite: papernotes 关键设计 3 (constrained marginals as the confidence that
+ * decides which positions are committed); paperfeed "Two immediate bonuses"
+ * (LLaDA: highest probability, Dream: lowest entropy).
+ *   logZ    device double [B] from fa_span_tree
+ *   tokens  device int32 [B][L] (needed for FA_CONF_PROB; may be NULL for
+ *           FA_CONF_NEGENT)
+ *   q       device fp32 [B][L][V] or NULL (not written)
+ *   conf    device fp32 [B][L]
+ * Errors: FA_EINVAL, FA_ESTATE, FA_EHIP.
+ */
+int fa_marginals(const fa_table *t, const float *p, int32_t B, int32_t L, const float *tree,
+                 const int32_t *meta, const double *logZ, const int32_t *tokens,
+                 int32_t conf_mode, float *q, float *conf, void *ws, size_t ws_bytes,
+                 int32_t *row_status, fa_stream_t stream);
+
+/* fa_strerror - static description of an error code. */
+const char *fa_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

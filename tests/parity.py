@@ -1,0 +1,102 @@
+"""Shared helpers of the GPU parity tests: run one step through the C ABI
+and compare it with the fp64 oracle.
+
+Tolerances (fp32 path against the fp64 oracle):
+  log Z:      |d| <= 1e-4 * max(1, |log Z|)
+  marginals:  |d| <= 1e-4 * q_oracle + 1e-12 per entry, and sum_v |d| <= 1e-4
+              per position (the absolute floor sits far below anything a
+              draw can resolve: u has 24 bits)
+  draws:      bit-exact under shared uniforms, except NEAR draws whose
+              uniform lies within 1e-6 of a CDF boundary between the two
+              choices (oracle replay verifier)
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+
+LOGZ_RTOL = 1e-4
+Q_RTOL = 1e-4
+Q_ATOL = 1e-12
+Q_L1 = 1e-4
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(w, conf_mode=0, write_q=True, table=None):
+    import torch
+    import constrained_decoding_diffusion_amd as fa
+    tb = table or fa.Table.from_automaton(w.aut)
+    p = torch.from_numpy(w.p).cuda()
+    bufs = fa.step(tb, p, w.seed, conf_mode=conf_mode, write_q=write_q)
+    torch.cuda.synchronize()
+    out = dict(table=tb, bufs=bufs,
+               logZ=bufs.logZ.cpu().numpy(), status=bufs.status.cpu().numpy(),
+               states=bufs.states.cpu().numpy(), tokens=bufs.tokens.cpu().numpy()[:, :w.L],
+               conf=bufs.conf.cpu().numpy()[:, :w.L])
+    out["q"] = bufs.q.cpu().numpy() if (write_q and bufs.q is not None) else None
+    return out
+
+
+def leaf(w, g, b, i):
+    """GPU leaf of position i of row b as a dense M over compact states."""
+    tb = g["table"]
+    Sp, S = tb.info["Sp"], tb.info["S"]
+    Lpad = 1 << max(0, (w.L - 1).bit_length())
+    h = Lpad + i
+    tree = g["bufs"].tree.view(w.B, 2 * Lpad, Sp, Sp)
+    M = tree[b, h].cpu().numpy().astype(np.float64)
+    if h % 2 == 1 and h >= 3:
+        M = M.T
+    return M[:S, :S]
+
+
+def check_row(w, g, b, orc=None, q_positions=None, check_q=True, conf_mode=0):
+    """Compare row b of a GPU step with the oracle; returns the replay report."""
+    orc = orc or oracle.Oracle(w.aut)
+    W = orc.edge_weights(w.p[b])
+    fb = orc.forward_backward(W)
+    if fb["status"] != oracle.OK:
+        assert g["status"][b] & 1, f"row {b}: oracle infeasible, GPU status {g['status'][b]}"
+        assert g["logZ"][b] == -np.inf
+        assert (g["states"][b] == -1).all() and (g["tokens"][b] == -1).all()
+        return None
+    assert g["status"][b] == 0, f"row {b}: GPU status {g['status'][b]}"
+    lz = fb["logZ"]
+    assert abs(g["logZ"][b] - lz) <= LOGZ_RTOL * max(1.0, abs(lz)), (b, g["logZ"][b], lz)
+    rep = orc.replay(w.p[b], W, w.seed, b, g["states"][b], g["tokens"][b])
+    assert rep["status"] == oracle.OK, rep
+    assert rep["hard"] == 0, f"row {b}: replay {rep}"
+    if check_q:
+        pos = np.arange(w.L) if q_positions is None else np.asarray(q_positions)
+        q, lognorm, conf = orc.marginals(w.p[b], fb, pos, g["tokens"][b], conf_mode)
+        if g["q"] is not None:
+            qg = g["q"][b, pos].astype(np.float64)
+            err = np.abs(qg - q)
+            bad = err > Q_RTOL * q + Q_ATOL
+            assert not bad.any(), (f"row {b}: {bad.sum()} q entries out of tolerance, worst "
+                                   f"{np.max(err - Q_RTOL * q)} at {np.argwhere(bad)[:5]}")
+            assert (err.sum(axis=1) <= Q_L1).all()
+        cg = g["conf"][b, pos].astype(np.float64)
+        if conf_mode == 0:
+            np.testing.assert_allclose(cg, conf, rtol=1e-4, atol=1e-12)
+        else:
+            np.testing.assert_allclose(cg, conf, rtol=1e-4, atol=1e-6)
+    return rep
+
+
+def check_leaves(w, g, b, positions, orc=None):
+    orc = orc or oracle.Oracle(w.aut)
+    tb = g["table"]
+    orig = tb.orig
+    W = orc.edge_weights(w.p[b])
+    for i in positions:
+        M = orc.dense_M(W, i)[np.ix_(orig, orig)]
+        Mg = leaf(w, g, b, i)
+        np.testing.assert_allclose(Mg, M, rtol=1e-5, atol=1e-30)

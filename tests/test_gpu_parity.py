@@ -1,0 +1,160 @@
+"""GPU parity of one constrained step (C ABI) against the fp64 oracle on
+small seeded workloads that span several tiles and ragged tails."""
+import numpy as np
+import pytest
+
+import oracle
+from synth import automata as A
+from synth import configs
+from tests import parity as PT
+
+pytestmark = pytest.mark.gpu
+
+
+def _json_small():
+    aut = configs._draw(lambda r: A.json_like_dfa(r, S=200, V=20000, pool=256, string_size=13000),
+                        7001, 37)
+    return configs.from_automaton(aut, 3, 37, "normal4_zipf", 0, 7100, "json-like small")
+
+
+def _range_small():
+    aut = configs._draw(lambda r: A.range_dfa(r, S=150, V=5000, edges_per_state=16), 7201, 29)
+    return configs.from_automaton(aut, 2, 29, "normal4_zipf", 14, 7300, "range small")
+
+
+def _nfa_small():
+    def build(r):
+        a = A.random_nfa(r, 300, 2000, 3000, 8, 12.0)
+        # parallel edges with overlapping labels: path counts above one
+        extra = [(int(a.src[e]), int(a.dst[e]), a.edge_label(e)[: max(1, a.edge_label(e).size // 2)])
+                 for e in range(0, a.E, 7)]
+        edges = [(int(a.src[e]), int(a.dst[e]), a.edge_label(e)) for e in range(a.E)] + extra
+        return A._pack(a.S, a.V, 0, a.accept.tolist(), edges, dfa=False, name="random NFA small")
+    aut = configs._draw(build, 7401, 21)
+    return configs.from_automaton(aut, 2, 21, "normal4", 0, 7500, "nfa small")
+
+
+CASES = {
+    "real-number": lambda: configs.make(1),
+    "random-dfa": lambda: configs.make(2),
+    "json-small": _json_small,
+    "range-small": _range_small,
+    "nfa-small": _nfa_small,
+    "real-L1": lambda: configs.make(1, L=1),
+    "random-dfa-L3": lambda: configs.make(2, L=3, B=2),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_step_parity(name):
+    w = CASES[name]()
+    PT.log(f"[parity] {name}: {w.describe()}")
+    g = PT.run_gpu(w)
+    PT.log(f"[parity] {name}: gpu done, status {g['status']}")
+    orc = oracle.Oracle(w.aut)
+    near = 0
+    for b in range(w.B):
+        rep = PT.check_row(w, g, b, orc)
+        near += rep["near"] if rep else 0
+    if w.aut.S <= 400:
+        PT.check_leaves(w, g, 0, range(w.L), orc)
+    PT.log(f"[parity] {name}: ok, near draws {near}")
+
+
+@pytest.mark.parametrize("name", ["real-number", "json-small"])
+def test_negentropy_confidence(name):
+    w = CASES[name]()
+    PT.log(f"[parity-negent] {name}")
+    g = PT.run_gpu(w, conf_mode=1)
+    orc = oracle.Oracle(w.aut)
+    for b in range(w.B):
+        PT.check_row(w, g, b, orc, conf_mode=1)
+
+
+def test_confidence_without_q():
+    w = _json_small()
+    PT.log("[parity] conf without q")
+    g = PT.run_gpu(w, conf_mode=0, write_q=False)
+    g2 = PT.run_gpu(w, conf_mode=0, write_q=True)
+    np.testing.assert_array_equal(g["tokens"], g2["tokens"])
+    np.testing.assert_allclose(g["conf"], g2["conf"], rtol=1e-6)
+
+
+def test_special_automata():
+    rng = np.random.default_rng(12)
+    V, L = 300, 19
+    p = rng.normal(0, 2, (2, L, V))
+    p = np.exp(p - p.max(-1, keepdims=True))
+    p = (p / p.sum(-1, keepdims=True)).astype(np.float32)
+    for aut in (A.universal_automaton(V), A.single_string_automaton(rng.integers(0, V, L), V)):
+        w = configs.Workload(aut.name, aut, p, 2, L, 31337, [])
+        PT.log(f"[parity] {aut.name}")
+        g = PT.run_gpu(w)
+        orc = oracle.Oracle(aut)
+        for b in range(2):
+            PT.check_row(w, g, b, orc)
+
+
+def test_infeasible_row_is_flagged():
+    w = configs.make(2, B=2, L=16)
+    # row 1: a committed token no state can emit from the start state
+    aut = w.aut
+    first = set()
+    for e in range(aut.E):
+        if aut.src[e] == aut.start:
+            first |= set(aut.edge_label(e).tolist())
+    bad = next(v for v in range(aut.V) if v not in first)
+    w.p[1, 0] = 0.0
+    w.p[1, 0, bad] = 1.0
+    PT.log("[parity] infeasible row")
+    g = PT.run_gpu(w)
+    orc = oracle.Oracle(aut)
+    PT.check_row(w, g, 0, orc)
+    assert g["status"][1] & 1
+    assert g["logZ"][1] == -np.inf
+    assert (g["states"][1] == -1).all() and (g["tokens"][1] == -1).all()
+    assert (g["q"][1] == 0).all() and (g["conf"][1] == -np.inf).all()
+
+
+def test_bad_probability_is_flagged():
+    w = configs.make(2, B=2, L=8)
+    w.p[0, 3, int(w.aut.label_tok[0])] = np.nan  # a token some label holds
+    PT.log("[parity] bad probability")
+    g = PT.run_gpu(w)
+    assert g["status"][0] & 4
+    assert g["logZ"][0] == -np.inf
+    assert (g["tokens"][0] == -1).all()
+    PT.check_row(w, g, 1, oracle.Oracle(w.aut))
+
+
+def test_determinism_bitwise():
+    w = _json_small()
+    PT.log("[parity] determinism")
+    g1 = PT.run_gpu(w)
+    g2 = PT.run_gpu(w, table=g1["table"])
+    for k in ("logZ", "states", "tokens", "q", "conf"):
+        np.testing.assert_array_equal(g1[k], g2[k])
+    Sp = g1["table"].info["Sp"]
+    Lpad = 1 << (w.L - 1).bit_length()
+    # heap node 0 is unused; every other node is written by the step
+    t1 = g1["bufs"].tree.view(w.B, 2 * Lpad, Sp, Sp)[:, 1:].cpu().numpy()
+    t2 = g2["bufs"].tree.view(w.B, 2 * Lpad, Sp, Sp)[:, 1:].cpu().numpy()
+    np.testing.assert_array_equal(t1, t2)
+
+
+def test_empty_inputs():
+    import torch
+    import constrained_decoding_diffusion_amd as fa
+    w = configs.make(1)
+    tb = fa.Table.from_automaton(w.aut)
+    PT.log("[parity] empty inputs")
+    # B = 0: every call is a no-op
+    p0 = torch.zeros((0, 6, 12), dtype=torch.float32, device="cuda")
+    fa.step(tb, p0, 1)
+    # L = 0: the empty string is rejected (start state not accepting)
+    pz = torch.zeros((2, 0, 12), dtype=torch.float32, device="cuda")
+    bufs = fa.step(tb, pz, 1)
+    torch.cuda.synchronize()
+    assert (bufs.logZ.cpu().numpy() == -np.inf).all()
+    assert (bufs.status.cpu().numpy() & 1).all()
+    assert (bufs.states.cpu().numpy() == -1).all()
