@@ -3,12 +3,15 @@
 // position's transition matrix sums the mean-field-reweighted emissions over
 // the vocabulary; paperfeed "The insight": the |E||V| term).
 //
-// Two kernels:
-//  * emission_stream: one workgroup per position streams the p row once,
-//    coalesced, and produces what needs the whole row: the dense-mask pair
-//    sums, fp64 prefix sums at every range cut point, and a compact copy of
-//    p at the tokens the LIST pairs use.  Runs only for tables with dense or
-//    range pairs.
+// Up to three kernels, by label class:
+//  * emission_dense: pairs whose labels are large token sets (dense masks).
+//    Their sums form a contraction  D[j][pos] = sum_v mask[j][v] p[pos][v]
+//    with a 0/1 operand; it runs on fp32 MFMA (32 pairs x 32 positions per
+//    tile, K = tokens), V split over workgroups into fixed chunks whose
+//    partials are summed in chunk order.  The same pass copies p at the
+//    tokens that token-list pairs use (a compact gather source).
+//  * emission_ranges: one workgroup per position streams the row and keeps
+//    an fp64 running prefix sum at every range cut point.
 //  * emission_densify: one wavefront per stored leaf row evaluates the pair
 //    values of that row and writes the row (Sp floats) in 64-column chunks,
 //    zeros included, with its power-of-two row exponent.  Odd leaves are
@@ -18,136 +21,232 @@
 namespace fa {
 namespace {
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kDenseThreads = 256;
+constexpr int kSub = 256;         // tokens staged per step
+constexpr int kSubLd = kSub + 4;  // padded LDS row
+
+__global__ __launch_bounds__(kDenseThreads) void emission_dense(
+    DevTable d, const float *__restrict__ p, int L, int npos, int BLpad,
+    float *__restrict__ dpart, float *__restrict__ psel, int32_t *__restrict__ status)
+{
+    __shared__ __align__(16) float pt[kDenseTile][kSubLd];
+    __shared__ float red[4][kDenseTile * kDenseTile];
+    __shared__ int sh_sel0;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int chunk = blockIdx.x;
+    const int pos0 = blockIdx.y * kDenseTile;
+    const int v_begin = chunk * kDenseChunk;
+    const int v_end = min(d.V, v_begin + kDenseChunk);
+    const bool vec = (d.V & 3) == 0;
+    // staging map: thread t loads row (t >> 3), 32 tokens at column 32*(t&7)
+    const int srow = tid >> 3, scol = (tid & 7) * 32;
+    const bool row_ok = pos0 + srow < npos;
+    const float *prow = p + (size_t)(pos0 + srow) * d.V;
+    int bad = 0;
+    if (tid == 0) {
+        int lo = 0, hi = d.nsel;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (d.sel_tok[mid] < v_begin) lo = mid + 1;
+            else hi = mid;
+        }
+        sh_sel0 = lo;
+    }
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    float4 xr[8];
+    auto load = [&](int v0) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int v = v0 + scol + 4 * k;
+            if (row_ok && vec && v + 3 < v_end) {
+                xr[k] = *reinterpret_cast<const float4 *>(prow + v);
+            } else {
+                xr[k].x = (row_ok && v < v_end) ? prow[v] : 0.f;
+                xr[k].y = (row_ok && v + 1 < v_end) ? prow[v + 1] : 0.f;
+                xr[k].z = (row_ok && v + 2 < v_end) ? prow[v + 2] : 0.f;
+                xr[k].w = (row_ok && v + 3 < v_end) ? prow[v + 3] : 0.f;
+            }
+        }
+    };
+    load(v_begin);
+    __syncthreads();
+    int sptr = sh_sel0;
+    const int half = lane >> 5, l32 = lane & 31;
+    for (int v0 = v_begin; v0 < v_end; v0 += kSub) {
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            bad |= !(xr[k].x >= 0.f) | !(xr[k].y >= 0.f) | !(xr[k].z >= 0.f) | !(xr[k].w >= 0.f);
+            *reinterpret_cast<float4 *>(&pt[srow][scol + 4 * k]) = xr[k];
+        }
+        __syncthreads();
+        if (v0 + kSub < v_end) load(v0 + kSub);
+        // the wave's 64 tokens: lane l holds the mask word of token 64*wave + l
+        const int vt = v0 + 64 * wave + lane;
+        const uint32_t mword = vt < v_end ? d.tokmask[vt] : 0u;
+        const float *brow = &pt[l32][64 * wave + 32 * half];
+#pragma unroll 4
+        for (int t = 0; t < 32; t += 4) {
+            const float4 bq = *reinterpret_cast<const float4 *>(brow + t);
+            const uint32_t m0 = __shfl(mword, (lane & 32) + t);
+            const uint32_t m1 = __shfl(mword, (lane & 32) + t + 1);
+            const uint32_t m2 = __shfl(mword, (lane & 32) + t + 2);
+            const uint32_t m3 = __shfl(mword, (lane & 32) + t + 3);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32((float)((m0 >> l32) & 1u), bq.x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32((float)((m1 >> l32) & 1u), bq.y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32((float)((m2 >> l32) & 1u), bq.z, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32((float)((m3 >> l32) & 1u), bq.w, acc, 0, 0, 0);
+        }
+        // copy p at the token-list tokens of this step (sorted, unique)
+        if (psel) {
+            const int idx = sptr + tid;
+            const int tk = idx < d.nsel ? d.sel_tok[idx] : 0x7fffffff;
+            const bool in = tk < min(v0 + kSub, v_end);
+            if (in)
+                for (int r = 0; r < kDenseTile && pos0 + r < npos; ++r)
+                    psel[(size_t)(pos0 + r) * d.nsel + idx] = pt[r][tk - v0];
+            sptr += __syncthreads_count(in);
+        }
+    }
+    // sum the four waves' tiles in wave order
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int i = (r >> 2) * 8 + half * 4 + (r & 3);
+        red[wave][i * kDenseTile + l32] = acc[r];
+    }
+    __syncthreads();
+    float *outp = dpart + ((size_t)chunk * BLpad + pos0) * kDenseMax;
+    for (int k = tid; k < kDenseTile * kDenseTile; k += kDenseThreads) {
+        const int i = k / kDenseTile, j = k % kDenseTile;  // pair i, position j
+        const float s = ((red[0][k] + red[1][k]) + red[2][k]) + red[3][k];
+        outp[(size_t)j * kDenseMax + i] = s;
+    }
+    if (bad && row_ok) atomicOr(&status[(pos0 + srow) / L], (int)FA_ROW_BADPROB);
+}
+
 constexpr int kStreamThreads = 256;
 
-__global__ __launch_bounds__(kStreamThreads) void emission_stream(
-    DevTable d, const float *__restrict__ p, int L, float *__restrict__ dval,
-    float *__restrict__ psel, double *__restrict__ cutp, int32_t *__restrict__ status)
+// fp64 prefix sums of the row at every range cut point: cutp[pos][c] =
+// sum_{v < cuts[c]} p[pos][v]
+__global__ __launch_bounds__(kStreamThreads) void emission_ranges(
+    DevTable d, const float *__restrict__ p, int L, double *__restrict__ cutp,
+    int32_t *__restrict__ status)
 {
     const int pos = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float *row = p + (size_t)pos * d.V;
-    const int nd = d.ndense;
-    __shared__ float sh_x[kStreamThreads];
     __shared__ double sh_incl[kStreamThreads];
     __shared__ double sh_wsum[4];
-    __shared__ float sh_red[4][kDenseMax];
     __shared__ int sh_bad;
     if (tid == 0) sh_bad = 0;
-
-    float acc[kDenseMax];
-#pragma unroll
-    for (int j = 0; j < kDenseMax; ++j) acc[j] = 0.f;
     double carry = 0.0;
-    int cptr = 0, sptr = 0;
+    int cptr = 0;
     int bad = 0;
-    const bool want_sel = d.use_sel && psel;
     for (int c0 = 0; c0 < d.V; c0 += kStreamThreads) {
         const int v = c0 + tid;
         float x = 0.f;
         if (v < d.V) {
             x = row[v];
             bad |= !(x >= 0.f);
-            if (nd) {
-                uint32_t m = d.tokmask[v];
-#pragma unroll
-                for (int j = 0; j < kDenseMax; ++j)
-                    if (j < nd) acc[j] += ((m >> j) & 1u) ? x : 0.f;
-            }
         }
-        if (want_sel) sh_x[tid] = x;
-        if (d.ncut) {
-            double inc = wave_incl_scan_d((double)x, lane);
-            if (lane == 63) sh_wsum[wave] = inc;
-            __syncthreads();
-            double off = 0.0;
-            for (int w = 0; w < wave; ++w) off += sh_wsum[w];
-            sh_incl[tid] = off + inc;
-            __syncthreads();
-            // cut points inside this chunk (sorted, at most one per token)
-            const int idx = cptr + tid;
-            int c = (idx < d.ncut) ? d.cuts[idx] : 0x7fffffff;
-            bool in = c < c0 + kStreamThreads && c < d.V;
-            if (in) {
-                int k = c - c0;
-                cutp[(size_t)pos * d.ncut + idx] = carry + (k > 0 ? sh_incl[k - 1] : 0.0);
-            }
-            cptr += __syncthreads_count(in);
-            carry += sh_incl[kStreamThreads - 1];
-            __syncthreads();
-        } else if (want_sel) {
-            __syncthreads();
+        const double inc = wave_incl_scan_d((double)x, lane);
+        if (lane == 63) sh_wsum[wave] = inc;
+        __syncthreads();
+        double off = 0.0;
+        for (int w = 0; w < wave; ++w) off += sh_wsum[w];
+        sh_incl[tid] = off + inc;
+        __syncthreads();
+        // cut points inside this chunk (sorted, unique)
+        const int idx = cptr + tid;
+        const int c = (idx < d.ncut) ? d.cuts[idx] : 0x7fffffff;
+        const bool in = c < c0 + kStreamThreads && c < d.V;
+        if (in) {
+            const int k = c - c0;
+            cutp[(size_t)pos * d.ncut + idx] = carry + (k > 0 ? sh_incl[k - 1] : 0.0);
         }
-        if (want_sel) {
-            const int idx = sptr + tid;
-            int t = (idx < d.nsel) ? d.sel_tok[idx] : 0x7fffffff;
-            bool in = t < c0 + kStreamThreads;
-            if (in) psel[(size_t)pos * d.nsel + idx] = sh_x[t - c0];
-            sptr += __syncthreads_count(in);
-        }
+        cptr += __syncthreads_count(in);
+        carry += sh_incl[kStreamThreads - 1];
+        __syncthreads();
     }
     // cut points equal to V hold the row total
-    if (d.ncut)
-        for (int idx = cptr + tid; idx < d.ncut; idx += kStreamThreads)
-            cutp[(size_t)pos * d.ncut + idx] = carry;
-    if (nd) {
-#pragma unroll
-        for (int j = 0; j < kDenseMax; ++j) {
-            if (j < nd) {
-                float s = wave_sum(acc[j]);
-                if (lane == 0) sh_red[wave][j] = s;
-            }
-        }
-    }
+    for (int idx = cptr + tid; idx < d.ncut; idx += kStreamThreads)
+        cutp[(size_t)pos * d.ncut + idx] = carry;
     if (bad) atomicOr(&sh_bad, 1);
     __syncthreads();
-    if (tid < nd) {
-        float s = ((sh_red[0][tid] + sh_red[1][tid]) + sh_red[2][tid]) + sh_red[3][tid];
-        dval[(size_t)pos * nd + tid] = s;
-    }
     if (tid == 0 && sh_bad) atomicOr(&status[pos / L], (int)FA_ROW_BADPROB);
 }
 
+struct EmitSrc {
+    const float *p;
+    const float *dpart;
+    const float *psel;
+    const double *cutp;
+    int n_vchunks;
+    int BLpad;
+};
+
 // value of pair q at position pos
-__device__ inline float pair_value(const DevTable &d, int q, size_t pos, const float *p,
-                                   const float *dval, const float *psel, const double *cutp,
+__device__ inline float pair_value(const DevTable &d, int q, size_t pos, const EmitSrc &s,
                                    int &bad)
 {
     const int cls = d.pair_cls[q];
-    if (cls == kDense) return dval[pos * d.ndense + d.pair_aux[q]];
-    if (cls == kRange) {
-        double s = 0.0;
-        const double *cp = cutp + pos * d.ncut;
-        for (int k = d.seg_off[q]; k < d.seg_off[q + 1]; ++k)
-            s += (cp[d.seg_hi_cut[k]] - cp[d.seg_lo_cut[k]]) * (double)d.seg_cnt[k];
-        return (float)s;
+    if (cls == kDense) {
+        const int j = d.pair_aux[q];
+        float acc = 0.f;
+        for (int c = 0; c < s.n_vchunks; ++c)
+            acc += s.dpart[((size_t)c * s.BLpad + pos) * kDenseMax + j];
+        return acc;
     }
-    float s = 0.f;
+    if (cls == kRange) {
+        double acc = 0.0;
+        const double *cp = s.cutp + pos * d.ncut;
+        for (int k = d.seg_off[q]; k < d.seg_off[q + 1]; ++k)
+            acc += (cp[d.seg_hi_cut[k]] - cp[d.seg_lo_cut[k]]) * (double)d.seg_cnt[k];
+        return (float)acc;
+    }
+    float acc = 0.f;
     const int k0 = d.list_off[q], k1 = d.list_off[q + 1];
     if (d.use_sel) {
-        const float *src = psel + pos * d.nsel;
+        const float *src = s.psel + pos * d.nsel;
         if (d.list_cnt)
-            for (int k = k0; k < k1; ++k) s += src[d.list_sel[k]] * d.list_cnt[k];
+            for (int k = k0; k < k1; ++k) acc += src[d.list_sel[k]] * d.list_cnt[k];
         else
-            for (int k = k0; k < k1; ++k) s += src[d.list_sel[k]];
+            for (int k = k0; k < k1; ++k) acc += src[d.list_sel[k]];
     } else {
-        const float *src = p + pos * d.V;
+        const float *src = s.p + pos * d.V;
         for (int k = k0; k < k1; ++k) {
-            float x = src[d.list_tok[k]];
+            const float x = src[d.list_tok[k]];
             bad |= !(x >= 0.f);
-            s += d.list_cnt ? x * d.list_cnt[k] : x;
+            acc += d.list_cnt ? x * d.list_cnt[k] : x;
         }
     }
-    return s;
+    return acc;
+}
+
+// every (position, pair) value, flat over positions x pairs
+__global__ void emission_pairs(DevTable d, int L, size_t total, EmitSrc src,
+                               float *__restrict__ val, int32_t *__restrict__ status)
+{
+    for (size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x; k < total;
+         k += (size_t)gridDim.x * blockDim.x) {
+        const size_t pos = k / d.npairs;
+        const int q = (int)(k % d.npairs);
+        int bad = 0;
+        val[k] = pair_value(d, q, pos, src, bad);
+        if (bad) atomicOr(&status[pos / L], (int)FA_ROW_BADPROB);
+    }
 }
 
 constexpr int kRowsPerWave = 2;
 constexpr int kDensifyThreads = 256;
 
 __global__ __launch_bounds__(kDensifyThreads) void emission_densify(
-    DevTable d, StepView sv, const float *__restrict__ p, const float *__restrict__ dval,
-    const float *__restrict__ psel, const double *__restrict__ cutp, float *__restrict__ tree,
-    int32_t *__restrict__ meta, int32_t *__restrict__ status)
+    DevTable d, StepView sv, const float *__restrict__ val, float *__restrict__ tree,
+    int32_t *__restrict__ meta)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int b = blockIdx.y / sv.Lpad, i = blockIdx.y % sv.Lpad;
@@ -159,7 +258,7 @@ __global__ __launch_bounds__(kDensifyThreads) void emission_densify(
     int32_t *co = sv.meta_ptr(meta, b, h, 1);
     int32_t *rf = sv.meta_ptr(meta, b, h, 2);
     __shared__ float stage[4][64];
-    int bad = 0;
+    const float *pv = val + pos * d.npairs;
     for (int rr = 0; rr < kRowsPerWave; ++rr) {
         const int r = (blockIdx.x * 4 + wave) * kRowsPerWave + rr;
         if (r >= sv.Sp) break;
@@ -167,7 +266,7 @@ __global__ __launch_bounds__(kDensifyThreads) void emission_densify(
         int emax = kNeg;
         if (i >= sv.L) {  // identity leaf
             for (int c = lane; c < sv.Sp; c += 64) {
-                float x = (c == r && r < d.S) ? 1.f : 0.f;
+                const float x = (c == r && r < d.S) ? 1.f : 0.f;
                 out[c] = x;
                 emax = max(emax, fexp(x));
             }
@@ -179,6 +278,10 @@ __global__ __launch_bounds__(kDensifyThreads) void emission_densify(
             }
             int kp = k0;
             for (int cw = 0; cw < sv.Sp; cw += 64) {
+                if (kp >= k1) {  // no pair left in this row: zeros
+                    out[cw + lane] = 0.f;
+                    continue;
+                }
                 stage[wave][lane] = 0.f;
                 const int k = kp + lane;
                 int q = -1, col = 0x7fffffff;
@@ -188,9 +291,9 @@ __global__ __launch_bounds__(kDensifyThreads) void emission_densify(
                 }
                 const bool in = col < cw + 64;
                 wave_sync();
-                if (in) stage[wave][col - cw] = pair_value(d, q, pos, p, dval, psel, cutp, bad);
+                if (in) stage[wave][col - cw] = pv[q];
                 wave_sync();
-                float x = stage[wave][lane];
+                const float x = stage[wave][lane];
                 out[cw + lane] = x;
                 emax = max(emax, fexp(x));
                 kp += __popcll(__ballot(in));
@@ -204,7 +307,6 @@ __global__ __launch_bounds__(kDensifyThreads) void emission_densify(
             co[r] = 0;
         }
     }
-    if (bad) atomicOr(&status[b], (int)FA_ROW_BADPROB);
 }
 
 }  // namespace
@@ -214,19 +316,38 @@ int launch_build_transitions(const DevTable &d, const Geometry &g, const float *
                              void *stream)
 {
     hipStream_t st = (hipStream_t)stream;
-    float *dval = (float *)(ws + w.dval);
-    float *psel = d.use_sel ? (float *)(ws + w.psel) : nullptr;
-    double *cutp = (double *)(ws + w.cutp);
     const int npos = g.B * g.L;
-    if (d.ndense > 0 || d.nseg > 0) {
-        emission_stream<<<npos, kStreamThreads, 0, st>>>(d, p, g.L, dval, psel, cutp, status);
+    const int BLpad = (npos + kDenseTile - 1) / kDenseTile * kDenseTile;
+    EmitSrc src;
+    src.p = p;
+    src.dpart = (float *)(ws + w.dpart);
+    src.psel = d.use_sel ? (float *)(ws + w.psel) : nullptr;
+    src.cutp = (double *)(ws + w.cutp);
+    src.n_vchunks = w.n_vchunks;
+    src.BLpad = BLpad;
+    if (d.ndense > 0) {
+        dim3 grid(w.n_vchunks, BLpad / kDenseTile);
+        emission_dense<<<grid, kDenseThreads, 0, st>>>(d, p, g.L, npos, BLpad, (float *)src.dpart,
+                                                       (float *)src.psel, status);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return (int)e;
+    }
+    if (d.nseg > 0) {
+        emission_ranges<<<npos, kStreamThreads, 0, st>>>(d, p, g.L, (double *)src.cutp, status);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return (int)e;
+    }
+    float *val = (float *)(ws + w.val);
+    const size_t total = (size_t)npos * d.npairs;
+    if (total) {
+        const int blocks = (int)std::min<size_t>((total + 255) / 256, 1 << 20);
+        emission_pairs<<<blocks, 256, 0, st>>>(d, g.L, total, src, val, status);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
     }
     StepView sv = step_view(g);
     dim3 grid((g.Sp + 4 * kRowsPerWave - 1) / (4 * kRowsPerWave), g.B * g.Lpad);
-    emission_densify<<<grid, kDensifyThreads, 0, st>>>(d, sv, p, dval, psel, cutp, tree, meta,
-                                                       status);
+    emission_densify<<<grid, kDensifyThreads, 0, st>>>(d, sv, val, tree, meta);
     return (int)hipGetLastError();
 }
 

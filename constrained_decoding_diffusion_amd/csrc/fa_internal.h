@@ -14,7 +14,10 @@ namespace fa {
 constexpr int kSpAlign = 64;       // trimmed state count padded to this
 constexpr int kNeg = -(1 << 29);   // exponent of an all-zero row/column
 constexpr int kDenseMax = 32;      // dense-label pairs share one mask word per token
+constexpr int kDenseChunk = 4096;  // tokens per workgroup of the dense-mask contraction
+constexpr int kDenseTile = 32;     // positions per workgroup of the dense-mask contraction
 constexpr int kSelMax = 8192;      // LIST tokens gathered through a compact copy of p
+constexpr uint32_t kSelBit = 1u << 31;  // tokmask flag of LIST tokens (tables with < 32 dense pairs)
 
 enum PairClass : int32_t { kList = 0, kDense = 1, kRange = 2 };
 
@@ -33,6 +36,7 @@ struct DevTable {
     int32_t nseg;
     int32_t ncut;
     int32_t has_cnt;
+    int32_t selbit;  // 1: bit 31 of tokmask marks tokens that LIST pairs hold
     const int32_t *acc;        // [n_acc] ascending compact ids
     const int32_t *orig;       // [S] compact -> original id
     const int32_t *pair_a;     // [npairs] sorted by (a, b)
@@ -82,6 +86,7 @@ struct HostTable {
     std::vector<int32_t> tok2sel, tok2cut, seg_pair;
     bool has_cnt = false;
     bool use_sel = false;
+    bool selbit = false;
     // device image
     std::vector<uint8_t> image;
     std::vector<size_t> offs;  // section offsets, in the order of DevTable pointers
@@ -109,13 +114,15 @@ bool make_geometry(const HostTable &t, int32_t B, int32_t L, Geometry *g);
 
 // Workspace layout (bytes from the start of ws), sized for the largest user.
 struct WsLayout {
-    size_t dval = 0, psel = 0, cutp = 0;       // emission reduce
+    size_t dpart = 0, psel = 0, cutp = 0, val = 0;  // emission reduce
+    int32_t n_vchunks = 0;                     // dense-mask contraction: V split
     size_t zc = 0;                             // sampler: compact boundary states
     size_t va = 0, ea = 0, vb = 0, eb = 0;     // marginals: messages
     size_t rcut = 0;                           // marginals: range weights per cut
     size_t total = 0;
 };
 WsLayout ws_layout(const HostTable &t, const Geometry &g);
+
 
 // Kernel launchers (kernels.hip).  Return 0 or a hipError_t value.
 int launch_build_transitions(const DevTable &d, const Geometry &g, const float *p, float *tree,

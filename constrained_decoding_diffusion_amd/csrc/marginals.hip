@@ -38,25 +38,26 @@ __global__ void marg_init(DevTable d, StepView sv, float *__restrict__ va, int32
     }
 }
 
-constexpr int kVecThreads = 256;
+// out = in * T for the consumed stored rows of one node.  grid.x: column
+// blocks of CW columns; grid.y: (b, node, alpha|beta).  The rows are dealt
+// to the 16 wavefronts of the workgroup; their partial sums are added in
+// wavefront order.
+constexpr int kMsgThreads = 1024;
+constexpr int kMsgWaves = kMsgThreads / 64;
 
-// out = in * T for the consumed stored rows of one node; grid.y enumerates
-// (b, node, alpha|beta)
-__global__ __launch_bounds__(kVecThreads) void marg_level(DevTable d, StepView sv,
-                                                          const float *__restrict__ tree,
-                                                          const int32_t *__restrict__ meta,
-                                                          int nn, float *__restrict__ va,
-                                                          int32_t *__restrict__ ea,
-                                                          float *__restrict__ vb,
-                                                          int32_t *__restrict__ eb)
+template <int CW>
+__global__ __launch_bounds__(kMsgThreads) void marg_level(
+    DevTable d, StepView sv, const float *__restrict__ tree, const int32_t *__restrict__ meta,
+    int nn, float *__restrict__ va, int32_t *__restrict__ ea, float *__restrict__ vb,
+    int32_t *__restrict__ eb)
 {
-    extern __shared__ float gsh[];  // [Sp] normalized input weights
-    __shared__ int sh_max[4];
-    __shared__ int sh_G;
+    constexpr int PER = CW / 64;  // columns per lane: 4 or 1
+    __shared__ int sh_max[kMsgWaves];
+    __shared__ float red[kMsgWaves][CW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int y = blockIdx.y;
-    const int beta = y & 1;
-    const int bn = y >> 1;
+    const int cb = blockIdx.x, prod = blockIdx.y;
+    const int beta = prod & 1;
+    const int bn = prod >> 1;
     const int b = bn / nn, idx = bn % nn, n = nn + idx;
     const int span = sv.Lpad / nn, l = idx * span, r = l + span, m = l + span / 2;
     const int h = beta ? 2 * n + 1 : 2 * n;
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(kVecThreads) void marg_level(DevTable d, StepView s
     const int32_t *rf = sv.meta_ptr(meta, b, h, 2);
     // G = max_a e(in[a]) + ro[a] + rf[a]
     int e = kNeg;
-    for (int a = tid; a < d.S; a += kVecThreads) {
+    for (int a = tid; a < d.S; a += kMsgThreads) {
         const float x = vin[a];
         const int s = add_exp(ro[a], rf[a]);
         if (x > 0.f && s > kNeg) e = max(e, fexp(x) + s);
@@ -80,30 +81,47 @@ __global__ __launch_bounds__(kVecThreads) void marg_level(DevTable d, StepView s
     e = wave_max_i(e);
     if (lane == 0) sh_max[wave] = e;
     __syncthreads();
-    if (tid == 0) sh_G = max(max(sh_max[0], sh_max[1]), max(sh_max[2], sh_max[3]));
-    __syncthreads();
-    const int G = sh_G;
-    for (int a = tid; a < d.S; a += kVecThreads) {
-        const float x = vin[a];
-        const int s = add_exp(ro[a], rf[a]);
-        gsh[a] = (x > 0.f && s > kNeg && G > kNeg) ? scale2(mant(x), fexp(x) + s - G) : 0.f;
-    }
-    __syncthreads();
-    const int j = blockIdx.x * kVecThreads + tid;
-    if (j < sv.Sp) {
-        float acc = 0.f;
-        if (G > kNeg && j < d.S) {
-            const int coj = co[j];
-            for (int a = 0; a < d.S; ++a) {
-                const float g = gsh[a];
-                if (g == 0.f) continue;
-                const float x = P[(size_t)a * sv.Sp + j];
-                if (x != 0.f) acc += g * scale2(x, coj - rf[a]);
+    int G = kNeg;
+    for (int w = 0; w < kMsgWaves; ++w) G = max(G, sh_max[w]);
+    const int j0 = cb * CW + PER * lane;
+    const bool colok = j0 < sv.Sp && G > kNeg;
+    float acc[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+    if (colok) {
+        int cj[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) cj[k] = co[j0 + k];
+        for (int a = wave; a < d.S; a += kMsgWaves) {
+            const float x = vin[a];
+            const int s = add_exp(ro[a], rf[a]);
+            if (!(x > 0.f) || s <= kNeg) continue;
+            const float g = scale2(mant(x), fexp(x) + s - G);
+            if (g == 0.f) continue;
+            const int ra = rf[a];
+            const float *row = P + (size_t)a * sv.Sp + j0;
+            if constexpr (PER == 4) {
+                const float4 y = *reinterpret_cast<const float4 *>(row);
+                acc[0] += g * scale2(y.x, cj[0] - ra);
+                acc[1] += g * scale2(y.y, cj[1] - ra);
+                acc[2] += g * scale2(y.z, cj[2] - ra);
+                acc[3] += g * scale2(y.w, cj[3] - ra);
+            } else {
+                acc[0] += g * scale2(row[0], cj[0] - ra);
             }
         }
-        vout[j] = acc;
     }
-    if (blockIdx.x == 0 && tid == 0)
+#pragma unroll
+    for (int k = 0; k < PER; ++k) red[wave][PER * lane + k] = acc[k];
+    __syncthreads();
+    for (int c = tid; c < CW; c += kMsgThreads) {
+        const int j = cb * CW + c;
+        if (j >= sv.Sp) continue;
+        float s = 0.f;
+        for (int w = 0; w < kMsgWaves; ++w) s += red[w][c];
+        vout[j] = s;
+    }
+    if (cb == 0 && tid == 0)
         ebase[(size_t)b * (sv.Lpad + 1) + m] = (G > kNeg && ein > kNeg) ? ein + G : kNeg;
 }
 
@@ -137,6 +155,22 @@ __global__ void marg_rcut(DevTable d, StepView sv, const float *__restrict__ va,
 
 constexpr int kQThreads = 256;
 
+// LIST weight of selected token s: sum over its token-major entries
+__device__ inline float list_weight(const DevTable &d, int s, const float *al, const float *be)
+{
+    float r = 0.f;
+    for (int k = d.tm_off[s]; k < d.tm_off[s + 1]; ++k) {
+        const int qq = d.tm_pair[k];
+        const float w = al[d.pair_a[qq]] * be[d.pair_b[qq]];
+        r += d.tm_cnt ? w * d.tm_cnt[k] : w;
+    }
+    return r;
+}
+
+// One workgroup per position streams the p row once and writes the q row.
+// The dense-mask pairs' weight of a token is read from four 256-entry
+// tables indexed by the bytes of its mask word; tokens held by token-list
+// pairs carry a flag bit and add their precomputed weight.
 __global__ __launch_bounds__(kQThreads) void marg_q(DevTable d, StepView sv,
                                                     const float *__restrict__ p,
                                                     const double *__restrict__ logZ,
@@ -150,7 +184,8 @@ __global__ __launch_bounds__(kQThreads) void marg_q(DevTable d, StepView sv,
                                                     const float *__restrict__ rcut,
                                                     const int32_t *__restrict__ status)
 {
-    __shared__ float wd[kDenseMax];
+    __shared__ float lut[4][256];
+    __shared__ float rsel[kSelMax];
     __shared__ double sh_h[4];
     const int b = blockIdx.y, i = blockIdx.x;
     const size_t pos = (size_t)b * sv.L + i;
@@ -169,47 +204,102 @@ __global__ __launch_bounds__(kQThreads) void marg_q(DevTable d, StepView sv,
     const double factor = exp2((double)e1 + (double)e2 - lz * 1.4426950408889634074);
     const float *al = va + ((size_t)b * (sv.Lpad + 1) + i) * sv.Sp;
     const float *be = vb + ((size_t)b * (sv.Lpad + 1) + i + 1) * sv.Sp;
-    if (tid < d.ndense) {
-        const int qq = d.dense_pair[tid];
-        wd[tid] = al[d.pair_a[qq]] * be[d.pair_b[qq]];
-    }
-    __syncthreads();
-    const int tok = tokens ? tokens[pos] : -1;
-    int v0 = 0, v1 = d.V;
-    if (!qrow && conf_mode == FA_CONF_PROB) {  // only the sampled token is needed
-        v0 = tok < 0 ? 0 : tok;
-        v1 = tok < 0 ? 0 : tok + 1;
-    }
-    const float *rc = d.ncut ? rcut + pos * d.ncut : nullptr;
-    double hsum = 0.0;
-    for (int v = v0 + tid; v < v1; v += kQThreads) {
-        float r = 0.f;
-        if (d.ndense) {
-            const uint32_t msk = d.tokmask[v];
-#pragma unroll
-            for (int jj = 0; jj < kDenseMax; ++jj)
-                if (jj < d.ndense && ((msk >> jj) & 1u)) r += wd[jj];
+    const int nd = d.ndense, ng = (nd + 7) >> 3;
+    for (int g = 0; g < ng; ++g) {
+        float s = 0.f;
+        for (int bit = 0; bit < 8; ++bit) {
+            const int j = 8 * g + bit;
+            if (j < nd && ((tid >> bit) & 1)) {
+                const int qq = d.dense_pair[j];
+                s += al[d.pair_a[qq]] * be[d.pair_b[qq]];
+            }
         }
-        if (d.nsel) {
+        lut[g][tid] = s;
+    }
+    const bool sel_lds = d.nsel > 0 && d.nsel <= kSelMax;
+    if (sel_lds)
+        for (int s = tid; s < d.nsel; s += kQThreads) rsel[s] = list_weight(d, s, al, be);
+    __syncthreads();
+    const float *rc = d.ncut ? rcut + pos * d.ncut : nullptr;
+    const int tok = tokens ? tokens[pos] : -1;
+    auto weight_r = [&](int v, uint32_t m) -> float {
+        float r = 0.f;
+        bool sel = d.nsel > 0;
+        if (nd) {
+            r = lut[0][m & 255u];
+            if (ng > 1) r += lut[1][(m >> 8) & 255u];
+            if (ng > 2) r += lut[2][(m >> 16) & 255u];
+            if (ng > 3) r += lut[3][(m >> 24) & 255u];
+            if (d.selbit) sel = (m & kSelBit) != 0;
+        }
+        if (sel) {
             const int s = d.tok2sel[v];
-            if (s >= 0)
-                for (int k = d.tm_off[s]; k < d.tm_off[s + 1]; ++k) {
-                    const int qq = d.tm_pair[k];
-                    const float w = al[d.pair_a[qq]] * be[d.pair_b[qq]];
-                    r += d.tm_cnt ? w * d.tm_cnt[k] : w;
-                }
+            if (s >= 0) r += sel_lds ? rsel[s] : list_weight(d, s, al, be);
         }
         if (rc) {
             const int c = d.tok2cut[v];
             if (c >= 0) r += rc[c];
         }
-        const float x = prow[v];
-        const float qv = (r > 0.f && x > 0.f) ? (float)((double)x * (double)r * factor) : 0.f;
-        if (qrow) qrow[v] = qv;
-        if (v == tok && conf_mode == FA_CONF_PROB) conf[pos] = qv;
-        if (conf_mode == FA_CONF_NEGENT && qv > 0.f) hsum += (double)qv * log((double)qv);
+        return r;
+    };
+    auto qval = [&](float x, float r) -> float {
+        return (r > 0.f && x > 0.f) ? (float)((double)x * (double)r * factor) : 0.f;
+    };
+    double hsum = 0.0;
+    const bool negent = conf_mode == FA_CONF_NEGENT;
+    if (!qrow && !negent) {
+        // only the sampled token's marginal is needed
+        if (tid == 0)
+            conf[pos] = tok >= 0 ? qval(prow[tok], weight_r(tok, nd ? d.tokmask[tok] : 0u))
+                                 : -INFINITY;
+        return;
     }
-    if (conf_mode == FA_CONF_NEGENT) {
+    auto emit = [&](int v, float o) {
+        if (v == tok && !negent) conf[pos] = o;
+        if (negent && o > 0.f) hsum += (double)o * log((double)o);
+    };
+    if ((d.V & 3) == 0) {
+        constexpr int U = 4;  // float4 groups in flight per thread
+        const float4 *p4 = reinterpret_cast<const float4 *>(prow);
+        const uint4 *m4 = reinterpret_cast<const uint4 *>(d.tokmask);
+        float4 *q4 = reinterpret_cast<float4 *>(qrow);
+        const int n4 = d.V >> 2;
+        for (int k0 = tid; k0 < n4; k0 += U * kQThreads) {
+            float4 x[U];
+            uint4 mm[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int k = k0 + u * kQThreads;
+                x[u] = k < n4 ? p4[k] : make_float4(0.f, 0.f, 0.f, 0.f);
+                mm[u] = (nd && k < n4) ? m4[k] : make_uint4(0u, 0u, 0u, 0u);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int k = k0 + u * kQThreads;
+                if (k >= n4) break;
+                const int v = 4 * k;
+                float4 o;
+                o.x = qval(x[u].x, weight_r(v, mm[u].x));
+                o.y = qval(x[u].y, weight_r(v + 1, mm[u].y));
+                o.z = qval(x[u].z, weight_r(v + 2, mm[u].z));
+                o.w = qval(x[u].w, weight_r(v + 3, mm[u].w));
+                if (q4) q4[k] = o;
+                if (negent || (tok >= v && tok < v + 4)) {
+                    emit(v, o.x);
+                    emit(v + 1, o.y);
+                    emit(v + 2, o.z);
+                    emit(v + 3, o.w);
+                }
+            }
+        }
+    } else {
+        for (int v = tid; v < d.V; v += kQThreads) {
+            const float o = qval(prow[v], weight_r(v, nd ? d.tokmask[v] : 0u));
+            if (qrow) qrow[v] = o;
+            emit(v, o);
+        }
+    }
+    if (negent) {
         hsum = wave_sum_d(hsum);
         if (lane == 0) sh_h[wave] = hsum;
         __syncthreads();
@@ -234,11 +324,16 @@ int launch_marginals(const DevTable &d, const Geometry &g, const float *p, const
     marg_init<<<g.B, 256, 0, st>>>(d, sv, va, ea, vb, eb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
-    const size_t lds_vec = (size_t)g.Sp * sizeof(float);
     for (int level = 1; level <= g.K; ++level) {
         const int nn = 1 << (level - 1);
-        dim3 grid((g.Sp + kVecThreads - 1) / kVecThreads, g.B * nn * 2);
-        marg_level<<<grid, kVecThreads, lds_vec, st>>>(d, sv, tree, meta, nn, va, ea, vb, eb);
+        const int products = g.B * nn * 2;
+        if (products * ((g.Sp + 255) / 256) >= 256) {
+            dim3 grid((g.Sp + 255) / 256, products);
+            marg_level<256><<<grid, kMsgThreads, 0, st>>>(d, sv, tree, meta, nn, va, ea, vb, eb);
+        } else {
+            dim3 grid((g.Sp + 63) / 64, products);
+            marg_level<64><<<grid, kMsgThreads, 0, st>>>(d, sv, tree, meta, nn, va, ea, vb, eb);
+        }
         e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
     }

@@ -125,7 +125,44 @@ __global__ __launch_bounds__(256) void sample_level(DevTable d, StepView sv,
 }
 
 constexpr int kTokThreads = 256;
+constexpr int kTokChunksMax = 1024;
 
+// candidates of one token draw: the tokens of the pair (z_i, z_{i+1}) in
+// ascending order, weight p[i][v] times the number of edges holding v
+struct TokCands {
+    int cls, n, base, s0, s1;
+    uint32_t dbit;
+};
+
+__device__ inline float tok_weight(const DevTable &d, const TokCands &c, const float *prow, int k,
+                                   int &sg)
+{
+    if (c.cls == kList) {
+        const float x = prow[d.list_tok[c.base + k]];
+        return d.list_cnt ? x * d.list_cnt[c.base + k] : x;
+    }
+    if (c.cls == kDense) return (d.tokmask[k] & c.dbit) ? prow[k] : 0.f;
+    const int v = c.base + k;
+    while (sg < c.s1 && d.seg_hi[sg] <= v) ++sg;
+    return (sg < c.s1 && d.seg_lo[sg] <= v) ? prow[v] * d.seg_cnt[sg] : 0.f;
+}
+
+__device__ inline int seg_cursor(const DevTable &d, const TokCands &c, int k)
+{
+    if (c.cls != kRange) return 0;
+    int lo = c.s0, hi = c.s1;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (d.seg_hi[mid] <= c.base + k) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// One workgroup per position.  Pass 1 streams the candidates in chunks
+// (each thread a run of consecutive candidates, so loads are coalesced) and
+// keeps fp64 chunk sums; the chunk holding u*T is found serially; pass 2
+// rescans that chunk only.
 __global__ __launch_bounds__(kTokThreads) void sample_tokens(
     DevTable d, StepView sv, const float *__restrict__ p, uint64_t seed,
     const int32_t *__restrict__ zc, int32_t *__restrict__ tokens, int32_t *__restrict__ status)
@@ -134,9 +171,11 @@ __global__ __launch_bounds__(kTokThreads) void sample_tokens(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int32_t *z = zc + (size_t)b * (sv.Lpad + 1);
     const int a = z[i], c = z[i + 1];
-    __shared__ double sh_part[kTokThreads];
-    __shared__ double sh_wtot[4];
-    __shared__ int sh_q;
+    __shared__ double csum[kTokChunksMax];
+    __shared__ double sh_w[4];
+    __shared__ double sh_scan[kTokThreads];
+    __shared__ int sh_q, sh_chunk;
+    __shared__ double sh_base, sh_target;
     if (tid == 0) {
         int q = -1;
         if (a >= 0 && c >= 0) {
@@ -152,100 +191,137 @@ __global__ __launch_bounds__(kTokThreads) void sample_tokens(
     }
     __syncthreads();
     const int q = sh_q;
+    int32_t *out = tokens + (size_t)b * sv.L + i;
     if (q < 0) {
         if (tid == 0) {
-            tokens[(size_t)b * sv.L + i] = -1;
+            *out = -1;
             if (a >= 0 && c >= 0) atomicOr(&status[b], (int)FA_ROW_UNDERFLOW);
         }
         return;
     }
     const float *prow = p + ((size_t)b * sv.L + i) * d.V;
-    const int cls = d.pair_cls[q];
-    // candidate space [0, n) and its weights, ascending token order
-    int n, base = 0, s0 = 0, s1 = 0;
-    uint32_t dbit = 0;
-    if (cls == kList) {
-        base = d.list_off[q];
-        n = d.list_off[q + 1] - base;
-    } else if (cls == kDense) {
-        n = d.V;
-        dbit = 1u << d.pair_aux[q];
+    TokCands cd;
+    cd.cls = d.pair_cls[q];
+    cd.base = 0; cd.s0 = 0; cd.s1 = 0; cd.dbit = 0;
+    if (cd.cls == kList) {
+        cd.base = d.list_off[q];
+        cd.n = d.list_off[q + 1] - cd.base;
+    } else if (cd.cls == kDense) {
+        cd.n = d.V;
+        cd.dbit = 1u << d.pair_aux[q];
     } else {
-        s0 = d.seg_off[q];
-        s1 = d.seg_off[q + 1];
-        base = d.seg_lo[s0];
-        n = d.seg_hi[s1 - 1] - base;
+        cd.s0 = d.seg_off[q];
+        cd.s1 = d.seg_off[q + 1];
+        cd.base = d.seg_lo[cd.s0];
+        cd.n = d.seg_hi[cd.s1 - 1] - cd.base;
     }
-    const int sl = (n + kTokThreads - 1) / kTokThreads;
-    const int k0 = min(n, tid * sl), k1 = min(n, k0 + sl);
-    // segment cursor for range pairs
-    int seg = s0;
-    if (cls == kRange) {
-        int lo = s0, hi = s1;
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (d.seg_hi[mid] <= base + k0) lo = mid + 1;
-            else hi = mid;
+    // chunk = kTokThreads runs of `per` consecutive candidates (at most 64
+    // chunks for row-length candidate sets)
+    int per = 4;
+    while ((long long)per * kTokThreads * 64 < cd.n && per < 64) per *= 2;
+    while ((long long)per * kTokThreads * kTokChunksMax < cd.n) per *= 2;
+    const int chunk = per * kTokThreads;
+    const int nchunks = (cd.n + chunk - 1) / chunk;
+    const bool vec = cd.cls == kDense && (d.V & 3) == 0;
+    auto run_sum = [&](int c0) -> double {
+        const int k0 = c0 + tid * per;
+        double s = 0.0;
+        if (vec) {  // dense mask: float4 / uint4 loads, same order as the scalar walk
+            for (int k = k0; k < min(k0 + per, cd.n); k += 4) {
+                const float4 x = *reinterpret_cast<const float4 *>(prow + k);
+                const uint4 m = *reinterpret_cast<const uint4 *>(d.tokmask + k);
+                s += (double)((m.x & cd.dbit) ? x.x : 0.f);
+                s += (double)((m.y & cd.dbit) ? x.y : 0.f);
+                s += (double)((m.z & cd.dbit) ? x.z : 0.f);
+                s += (double)((m.w & cd.dbit) ? x.w : 0.f);
+            }
+            return s;
         }
-        seg = lo;
-    }
-    auto weight = [&](int k, int &sg) -> float {
-        if (cls == kList) {
-            const float x = prow[d.list_tok[base + k]];
-            return d.list_cnt ? x * d.list_cnt[base + k] : x;
-        }
-        if (cls == kDense) return (d.tokmask[k] & dbit) ? prow[k] : 0.f;
-        const int v = base + k;
-        while (sg < s1 && d.seg_hi[sg] <= v) ++sg;
-        if (sg < s1 && d.seg_lo[sg] <= v) return prow[v] * d.seg_cnt[sg];
-        return 0.f;
+        int sg = seg_cursor(d, cd, k0);
+        for (int k = k0; k < min(k0 + per, cd.n); ++k) s += (double)tok_weight(d, cd, prow, k, sg);
+        return s;
     };
-    double part = 0.0;
-    {
-        int sg = seg;
-        for (int k = k0; k < k1; ++k) part += (double)weight(k, sg);
+    for (int ch = 0; ch < nchunks; ++ch) {
+        double s = wave_sum_d(run_sum(ch * chunk));
+        if (lane == 0) sh_w[wave] = s;
+        __syncthreads();
+        if (tid == 0) csum[ch] = ((sh_w[0] + sh_w[1]) + sh_w[2]) + sh_w[3];
+        __syncthreads();
     }
-    // block inclusive scan of the thread partials (fp64)
-    const double ws = wave_incl_scan_d(part, lane);
-    if (lane == 63) sh_wtot[wave] = ws;
+    if (tid == 0) {
+        double T = 0.0;
+        for (int ch = 0; ch < nchunks; ++ch) T += csum[ch];
+        int pick = -1;
+        double base = 0.0, target = 0.0;
+        if (T > 0.0) {
+            target = (double)philox_u01(seed, (uint32_t)b, (uint32_t)(sv.K + 1), (uint32_t)i) * T;
+            double acc = 0.0, acc_last = 0.0;
+            int last = -1;
+            for (int ch = 0; ch < nchunks; ++ch) {
+                if (csum[ch] > 0.0) {
+                    last = ch;
+                    acc_last = acc;
+                    if (acc + csum[ch] > target) {
+                        pick = ch;
+                        base = acc;
+                        break;
+                    }
+                }
+                acc += csum[ch];
+            }
+            if (pick < 0) {
+                pick = last;
+                base = acc_last;
+            }
+        }
+        sh_chunk = pick;
+        sh_base = base;
+        sh_target = target;
+    }
     __syncthreads();
-    double off = 0.0;
-    for (int w = 0; w < wave; ++w) off += sh_wtot[w];
-    const double incl = off + ws;
-    sh_part[tid] = incl;
-    __syncthreads();
-    const double T = sh_part[kTokThreads - 1];
-    if (!(T > 0.0)) {
+    const int ch = sh_chunk;
+    if (ch < 0) {
         if (tid == 0) {
-            tokens[(size_t)b * sv.L + i] = -1;
+            *out = -1;
             atomicOr(&status[b], (int)FA_ROW_UNDERFLOW);
         }
         return;
     }
-    const float u = philox_u01(seed, (uint32_t)b, (uint32_t)(sv.K + 1), (uint32_t)i);
-    const double target = (double)u * T;
-    // first thread whose inclusive prefix passes the target
-    const bool cross = part > 0.0 && incl > target;
-    const uint64_t bal = __ballot(cross);
-    __shared__ int sh_first[4];
-    if (lane == 0) sh_first[wave] = bal ? (wave * 64 + __ffsll((unsigned long long)bal) - 1) : 0x7fffffff;
+    // pass 2: exclusive scan of the runs of the chosen chunk
+    const double part = run_sum(ch * chunk);
+    const double inc = wave_incl_scan_d(part, lane);
+    if (lane == 63) sh_w[wave] = inc;
     __syncthreads();
-    const int tstar = min(min(sh_first[0], sh_first[1]), min(sh_first[2], sh_first[3]));
-    int tpick = tstar;
-    if (tstar == 0x7fffffff) {
-        // rounding left no crossing: take the last thread with mass
-        __shared__ int sh_last[4];
-        const uint64_t any = __ballot(part > 0.0);
-        if (lane == 0) sh_last[wave] = any ? (wave * 64 + 63 - __clzll((unsigned long long)any)) : -1;
-        __syncthreads();
-        tpick = max(max(sh_last[0], sh_last[1]), max(sh_last[2], sh_last[3]));
+    double off = sh_base;
+    for (int w = 0; w < wave; ++w) off += sh_w[w];
+    sh_scan[tid] = off + inc;
+    __syncthreads();
+    const double target = sh_target;
+    const bool cross = part > 0.0 && off + inc > target;
+    const uint64_t bal = __ballot(cross);
+    __shared__ int sh_first[4], sh_lastw[4];
+    const uint64_t any = __ballot(part > 0.0);
+    if (lane == 0) {
+        sh_first[wave] = bal ? wave * 64 + __ffsll((unsigned long long)bal) - 1 : 0x7fffffff;
+        sh_lastw[wave] = any ? wave * 64 + 63 - __clzll((unsigned long long)any) : -1;
+    }
+    __syncthreads();
+    int tpick = min(min(sh_first[0], sh_first[1]), min(sh_first[2], sh_first[3]));
+    if (tpick == 0x7fffffff) tpick = max(max(sh_lastw[0], sh_lastw[1]), max(sh_lastw[2], sh_lastw[3]));
+    if (tpick < 0) {  // no mass left in the chunk: cannot happen for a chunk with csum > 0
+        if (tid == 0) {
+            *out = -1;
+            atomicOr(&status[b], (int)FA_ROW_UNDERFLOW);
+        }
+        return;
     }
     if (tid == tpick) {
-        double cacc = incl - part;
+        double cacc = sh_scan[tid] - part;
+        const int k0 = ch * chunk + tid * per;
+        int sg = seg_cursor(d, cd, k0);
         int last = -1, pick = -1;
-        int sg = seg;
-        for (int k = k0; k < k1; ++k) {
-            const float x = weight(k, sg);
+        for (int k = k0; k < min(k0 + per, cd.n); ++k) {
+            const float x = tok_weight(d, cd, prow, k, sg);
             cacc += (double)x;
             if (x > 0.f) {
                 last = k;
@@ -256,9 +332,7 @@ __global__ __launch_bounds__(kTokThreads) void sample_tokens(
             }
         }
         if (pick < 0) pick = last;
-        int tok = -1;
-        if (pick >= 0) tok = (cls == kList) ? d.list_tok[base + pick] : base + pick;
-        tokens[(size_t)b * sv.L + i] = tok;
+        *out = pick < 0 ? -1 : (cd.cls == kList ? d.list_tok[cd.base + pick] : cd.base + pick);
     }
 }
 

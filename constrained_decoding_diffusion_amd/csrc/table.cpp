@@ -89,6 +89,7 @@ DevTable HostTable::device_view() const
     d.nseg = nseg();
     d.ncut = ncut();
     d.has_cnt = has_cnt ? 1 : 0;
+    d.selbit = selbit ? 1 : 0;
     const uint8_t *b = static_cast<const uint8_t *>(dev);
     size_t k = 0;
     auto nxt = [&](auto *&ptr) {
@@ -132,9 +133,12 @@ WsLayout ws_layout(const HostTable &t, const Geometry &g)
     WsLayout w;
     size_t BL = (size_t)g.B * g.L;
     size_t o = 0;  // emission reduce region
-    w.dval = o; o = al(o + BL * t.ndense() * sizeof(float));
+    w.n_vchunks = t.ndense() ? (t.V + kDenseChunk - 1) / kDenseChunk : 0;
+    size_t BLpad = (BL + kDenseTile - 1) / kDenseTile * kDenseTile;
+    w.dpart = o; o = al(o + (size_t)w.n_vchunks * BLpad * kDenseMax * sizeof(float));
     w.psel = o; o = al(o + (t.use_sel ? BL * t.nsel() * sizeof(float) : 0));
     w.cutp = o; o = al(o + BL * t.ncut() * sizeof(double));
+    w.val = o; o = al(o + BL * t.npairs() * sizeof(float));
     size_t a1 = o;
     o = 0;  // sampler region
     w.zc = o; o = al(o + (size_t)g.B * (g.Lpad + 1) * sizeof(int32_t));
@@ -460,6 +464,9 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
         t.tok2cut[v] = c - 1;
     }
     t.use_sel = t.needs_stream() && ns > 0 && ns <= kSelMax;
+    t.selbit = t.ndense() > 0 && t.ndense() < 32 && ns > 0;
+    if (t.selbit)
+        for (int32_t v : t.sel_tok) t.tokmask[v] |= kSelBit;
     build_image(t);
     return FA_OK;
 }

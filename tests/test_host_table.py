@@ -1,0 +1,144 @@
+"""Host-side tests of libfa.so (no GPU): every symbol fa.h declares is
+exported, the automaton compiler validates its input, checks determinism,
+trims dead states, and sizes the step buffers."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import constrained_decoding_diffusion_amd as fa
+from constrained_decoding_diffusion_amd import _fa
+from synth import automata as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "fa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert {"fa_compile_table", "fa_build_transitions", "fa_span_tree", "fa_sample",
+            "fa_marginals"} <= set(names)
+    lib = C.CDLL(_fa.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_fa.EXPORTS)
+
+
+def _compile(S, V, start, accept, edges, flags=fa.FA_DFA):
+    src = np.array([e[0] for e in edges], np.int32)
+    dst = np.array([e[1] for e in edges], np.int32)
+    off = np.zeros(len(edges) + 1, np.int64)
+    off[1:] = np.cumsum([len(e[2]) for e in edges])
+    tok = np.concatenate([np.asarray(e[2], np.int32) for e in edges]) if edges else np.zeros(0, np.int32)
+    return fa.Table(S, V, start, accept, src, dst, off, tok, flags)
+
+
+def _code(fn):
+    with pytest.raises(fa.FaError) as ei:
+        fn()
+    return ei.value.code
+
+
+@pytest.mark.parametrize("case", [
+    dict(S=0, V=3, start=0, accept=[0], edges=[]),
+    dict(S=2, V=3, start=2, accept=[0], edges=[]),
+    dict(S=2, V=3, start=0, accept=[5], edges=[]),
+    dict(S=2, V=3, start=0, accept=[1], edges=[(0, 2, [1])]),
+    dict(S=2, V=3, start=0, accept=[1], edges=[(0, 1, [3])]),
+    dict(S=2, V=3, start=0, accept=[1], edges=[(0, 1, [-1])]),
+    dict(S=2, V=0, start=0, accept=[1], edges=[]),
+])
+def test_invalid_ids_rejected(case):
+    assert _code(lambda: _compile(**case)) == _fa.FA_EINVAL
+
+
+def test_invalid_ranges_and_flags():
+    R = fa.FA_DFA | fa.FA_LABEL_RANGES
+    assert _code(lambda: _compile(2, 10, 0, [1], [(0, 1, [5, 3])], R)) == _fa.FA_EINVAL
+    assert _code(lambda: _compile(2, 10, 0, [1], [(0, 1, [5])], R)) == _fa.FA_EINVAL
+    assert _code(lambda: _compile(2, 10, 0, [1], [(0, 1, [0, 11])], R)) == _fa.FA_EINVAL
+    assert _code(lambda: _compile(2, 10, 0, [1], [(0, 1, [0, 5, 3, 7])], R)) == _fa.FA_EINVAL
+    assert _code(lambda: _compile(2, 10, 0, [1], [(0, 1, [1])], fa.FA_DFA | fa.FA_NFA)) == _fa.FA_EINVAL
+    assert _code(lambda: _compile(2, 10, 0, [1], [(0, 1, [1])], 64)) == _fa.FA_EINVAL
+    # decreasing label offsets
+    with pytest.raises(fa.FaError):
+        fa.Table(2, 10, 0, [1], [0], [1], np.array([0, -1], np.int64), np.zeros(0, np.int32), 1)
+
+
+def test_determinism_check():
+    edges = [(0, 1, [3, 4]), (0, 2, [4, 5]), (1, 1, [0]), (2, 2, [0])]
+    assert _code(lambda: _compile(3, 6, 0, [1, 2], edges, fa.FA_DFA)) == _fa.FA_ENOTDET
+    t = _compile(3, 6, 0, [1, 2], edges, fa.FA_NFA)
+    assert t.info["pairs"] == 4
+    R = fa.FA_DFA | fa.FA_LABEL_RANGES
+    assert _code(lambda: _compile(3, 9, 0, [1], [(0, 1, [0, 5]), (0, 2, [4, 6])], R)) == _fa.FA_ENOTDET
+    assert _compile(3, 9, 0, [1], [(0, 1, [0, 4]), (0, 2, [4, 6])], R).info["range_pairs"] == 1
+
+
+def test_repeated_label_tokens_count_once():
+    t = _compile(2, 5, 0, [1], [(0, 1, [2, 2, 3]), (1, 1, [1])], fa.FA_DFA)
+    assert t.info["list_entries"] == 3
+
+
+def test_trimming_and_state_map():
+    # 0 -> 2 -> 4 (accepting); 1 unreachable; 3 dead (cannot reach 4)
+    edges = [(0, 2, [0]), (2, 4, [1]), (1, 4, [0]), (0, 3, [2]), (3, 3, [2]), (4, 4, [0])]
+    t = _compile(5, 3, 0, [4], edges)
+    assert t.info["S"] == 3 and t.info["S_orig"] == 5
+    np.testing.assert_array_equal(t.orig, [0, 2, 4])
+    assert t.info["pairs"] == 3 and t.info["n_accept"] == 1
+    t2 = _compile(5, 3, 0, [4], edges, fa.FA_DFA | fa.FA_NO_TRIM)
+    assert t2.info["S"] == 5 and t2.info["pairs"] == 6
+    # empty accepting set: only the start state survives, nothing is feasible
+    t3 = _compile(5, 3, 0, [], edges)
+    assert t3.info["S"] == 1 and t3.info["pairs"] == 0 and t3.info["n_accept"] == 0
+
+
+def test_label_classes():
+    rng = np.random.default_rng(0)
+    aut = A.json_like_dfa(rng, S=64, V=40000, pool=64, string_size=20000)
+    t = fa.Table.from_automaton(aut)
+    n_str = len(aut.meta["string_states"])
+    assert t.info["dense_pairs"] == n_str
+    assert t.info["use_sel"] == 1
+    # NFA with overlapping parallel edges: counts > 1 keep the pair a token list
+    edges = [(0, 1, np.arange(5000)), (0, 1, np.arange(4000, 9000)), (1, 1, [0])]
+    t2 = _compile(2, 10000, 0, [1], edges, fa.FA_NFA)
+    assert t2.info["dense_pairs"] == 0 and t2.info["list_entries"] == 9001 - 1 + 1
+
+
+def test_range_pairs_merge_parallel_edges():
+    R = fa.FA_NFA | fa.FA_LABEL_RANGES
+    # two parallel ranges overlapping on [4, 6): three segments, counts 1, 2, 1
+    t = _compile(2, 10, 0, [1], [(0, 1, [0, 6]), (0, 1, [4, 9]), (1, 1, [0, 10])], R)
+    assert t.info["range_pairs"] == 2
+    assert t.info["segments"] == 4
+    assert t.info["cuts"] == 5  # 0, 4, 6, 9, 10
+
+
+def test_sizes_and_limits():
+    t = fa.Table.from_automaton(A.real_number_dfa())
+    Sp = t.info["Sp"]
+    tree, meta, ws = t.sizes(3, 6)
+    assert tree == 3 * 2 * 8 * Sp * Sp * 4
+    assert meta == 3 * 2 * 8 * 3 * Sp * 4
+    assert ws > 0
+    assert t.sizes(0, 6)[0] == 0
+    with pytest.raises(fa.FaError) as ei:
+        t.sizes(40000, 6)
+    assert ei.value.code == _fa.FA_ETOOBIG
+
+
+def test_step_calls_need_an_uploaded_table():
+    t = fa.Table.from_automaton(A.real_number_dfa())
+    rc = _fa.lib().fa_build_transitions(t.handle, None, 1, 6, None, None, None, 0, None, None)
+    assert rc == _fa.FA_ESTATE
+    rc = _fa.lib().fa_span_tree(None, 1, 6, None, None, None, None, None)
+    assert rc == _fa.FA_EINVAL
