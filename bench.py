@@ -87,6 +87,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", type=int, default=3, help="preset 1..5 (default 3)")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="first run one plain device copy of 1 GiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -106,6 +108,13 @@ def main():
     tb.upload(dev)
     bufs = fa.StepBuffers(tb, w.B, w.L, want_q=True, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
+    if args.copy_calib:
+        src_buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst_buf = torch.empty_like(src_buf)
+        torch.cuda.synchronize()
+        dst_buf.copy_(src_buf)
+        torch.cuda.synchronize()
+        del src_buf, dst_buf
     torch.cuda.synchronize()
 
     def one_step(seed, ev=None):

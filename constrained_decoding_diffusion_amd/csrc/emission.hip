@@ -32,6 +32,7 @@ __global__ __launch_bounds__(kDenseThreads) void emission_dense(
     float *__restrict__ dpart, float *__restrict__ psel, int32_t *__restrict__ status)
 {
     __shared__ __align__(16) float pt[kDenseTile][kSubLd];
+    __shared__ __align__(16) uint32_t mk[kSub];
     __shared__ float red[4][kDenseTile * kDenseTile];
     __shared__ int sh_sel0;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -40,7 +41,8 @@ __global__ __launch_bounds__(kDenseThreads) void emission_dense(
     const int v_begin = chunk * kDenseChunk;
     const int v_end = min(d.V, v_begin + kDenseChunk);
     const bool vec = (d.V & 3) == 0;
-    // staging map: thread t loads row (t >> 3), 32 tokens at column 32*(t&7)
+    // staging map: thread t loads row (t >> 3), 32 tokens at column 32*(t&7);
+    // threads 0..63 also load the mask words of four tokens each
     const int srow = tid >> 3, scol = (tid & 7) * 32;
     const bool row_ok = pos0 + srow < npos;
     const float *prow = p + (size_t)(pos0 + srow) * d.V;
@@ -57,49 +59,63 @@ __global__ __launch_bounds__(kDenseThreads) void emission_dense(
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    float4 xr[8];
-    auto load = [&](int v0) {
+    struct Step {
+        float4 x[8];
+        uint4 m;
+    };
+    Step sa, sb;
+    auto load = [&](Step &st, int v0) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int v = v0 + scol + 4 * k;
             if (row_ok && vec && v + 3 < v_end) {
-                xr[k] = *reinterpret_cast<const float4 *>(prow + v);
+                st.x[k] = *reinterpret_cast<const float4 *>(prow + v);
             } else {
-                xr[k].x = (row_ok && v < v_end) ? prow[v] : 0.f;
-                xr[k].y = (row_ok && v + 1 < v_end) ? prow[v + 1] : 0.f;
-                xr[k].z = (row_ok && v + 2 < v_end) ? prow[v + 2] : 0.f;
-                xr[k].w = (row_ok && v + 3 < v_end) ? prow[v + 3] : 0.f;
+                st.x[k].x = (row_ok && v < v_end) ? prow[v] : 0.f;
+                st.x[k].y = (row_ok && v + 1 < v_end) ? prow[v + 1] : 0.f;
+                st.x[k].z = (row_ok && v + 2 < v_end) ? prow[v + 2] : 0.f;
+                st.x[k].w = (row_ok && v + 3 < v_end) ? prow[v + 3] : 0.f;
+            }
+        }
+        if (tid < kSub / 4) {
+            const int v = v0 + 4 * tid;
+            if (vec && v + 3 < v_end) {
+                st.m = *reinterpret_cast<const uint4 *>(d.tokmask + v);
+            } else {
+                st.m.x = v < v_end ? d.tokmask[v] : 0u;
+                st.m.y = v + 1 < v_end ? d.tokmask[v + 1] : 0u;
+                st.m.z = v + 2 < v_end ? d.tokmask[v + 2] : 0u;
+                st.m.w = v + 3 < v_end ? d.tokmask[v + 3] : 0u;
             }
         }
     };
-    load(v_begin);
+    load(sa, v_begin);
+    if (v_begin + kSub < v_end) load(sb, v_begin + kSub);
     __syncthreads();
     int sptr = sh_sel0;
     const int half = lane >> 5, l32 = lane & 31;
-    for (int v0 = v_begin; v0 < v_end; v0 += kSub) {
+    auto step = [&](Step &st, int v0) {
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            bad |= !(xr[k].x >= 0.f) | !(xr[k].y >= 0.f) | !(xr[k].z >= 0.f) | !(xr[k].w >= 0.f);
-            *reinterpret_cast<float4 *>(&pt[srow][scol + 4 * k]) = xr[k];
+            bad |= !(st.x[k].x >= 0.f) | !(st.x[k].y >= 0.f) | !(st.x[k].z >= 0.f) |
+                   !(st.x[k].w >= 0.f);
+            *reinterpret_cast<float4 *>(&pt[srow][scol + 4 * k]) = st.x[k];
         }
+        if (tid < kSub / 4) *reinterpret_cast<uint4 *>(&mk[4 * tid]) = st.m;
         __syncthreads();
-        if (v0 + kSub < v_end) load(v0 + kSub);
-        // the wave's 64 tokens: lane l holds the mask word of token 64*wave + l
-        const int vt = v0 + 64 * wave + lane;
-        const uint32_t mword = vt < v_end ? d.tokmask[vt] : 0u;
+        if (v0 + 2 * kSub < v_end) load(st, v0 + 2 * kSub);
+        // the wave's 64 tokens; half h covers tokens 32h .. 32h+31 of them
         const float *brow = &pt[l32][64 * wave + 32 * half];
-#pragma unroll 4
+        const uint32_t *mrow = &mk[64 * wave + 32 * half];
+#pragma unroll
         for (int t = 0; t < 32; t += 4) {
             const float4 bq = *reinterpret_cast<const float4 *>(brow + t);
-            const uint32_t m0 = __shfl(mword, (lane & 32) + t);
-            const uint32_t m1 = __shfl(mword, (lane & 32) + t + 1);
-            const uint32_t m2 = __shfl(mword, (lane & 32) + t + 2);
-            const uint32_t m3 = __shfl(mword, (lane & 32) + t + 3);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32((float)((m0 >> l32) & 1u), bq.x, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32((float)((m1 >> l32) & 1u), bq.y, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32((float)((m2 >> l32) & 1u), bq.z, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32((float)((m3 >> l32) & 1u), bq.w, acc, 0, 0, 0);
+            const uint4 mq = *reinterpret_cast<const uint4 *>(mrow + t);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32((float)((mq.x >> l32) & 1u), bq.x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32((float)((mq.y >> l32) & 1u), bq.y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32((float)((mq.z >> l32) & 1u), bq.z, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32((float)((mq.w >> l32) & 1u), bq.w, acc, 0, 0, 0);
         }
         // copy p at the token-list tokens of this step (sorted, unique)
         if (psel) {
@@ -111,6 +127,10 @@ __global__ __launch_bounds__(kDenseThreads) void emission_dense(
                     psel[(size_t)(pos0 + r) * d.nsel + idx] = pt[r][tk - v0];
             sptr += __syncthreads_count(in);
         }
+    };
+    for (int v0 = v_begin; v0 < v_end; v0 += 2 * kSub) {
+        step(sa, v0);
+        if (v0 + kSub < v_end) step(sb, v0 + kSub);
     }
     // sum the four waves' tiles in wave order
 #pragma unroll
@@ -183,6 +203,7 @@ __global__ __launch_bounds__(kStreamThreads) void emission_ranges(
 struct EmitSrc {
     const float *p;
     const float *dpart;
+    const float *dval;  // [npos][kDenseMax] chunk sums of the dense-mask pairs
     const float *psel;
     const double *cutp;
     int n_vchunks;
@@ -194,13 +215,7 @@ __device__ inline float pair_value(const DevTable &d, int q, size_t pos, const E
                                    int &bad)
 {
     const int cls = d.pair_cls[q];
-    if (cls == kDense) {
-        const int j = d.pair_aux[q];
-        float acc = 0.f;
-        for (int c = 0; c < s.n_vchunks; ++c)
-            acc += s.dpart[((size_t)c * s.BLpad + pos) * kDenseMax + j];
-        return acc;
-    }
+    if (cls == kDense) return s.dval[pos * kDenseMax + d.pair_aux[q]];
     if (cls == kRange) {
         double acc = 0.0;
         const double *cp = s.cutp + pos * d.ncut;
@@ -227,17 +242,76 @@ __device__ inline float pair_value(const DevTable &d, int q, size_t pos, const E
     return acc;
 }
 
-// every (position, pair) value, flat over positions x pairs
-__global__ void emission_pairs(DevTable d, int L, size_t total, EmitSrc src,
-                               float *__restrict__ val, int32_t *__restrict__ status)
+// dense-mask pair sums: add the V-chunk partials of one (position, pair) in
+// chunk order
+__global__ void emission_dense_reduce(int n_vchunks, int BLpad, int npos, int nd,
+                                      const float *__restrict__ dpart, float *__restrict__ dval)
 {
-    for (size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x; k < total;
-         k += (size_t)gridDim.x * blockDim.x) {
-        const size_t pos = k / d.npairs;
-        const int q = (int)(k % d.npairs);
-        int bad = 0;
-        val[k] = pair_value(d, q, pos, src, bad);
-        if (bad) atomicOr(&status[pos / L], (int)FA_ROW_BADPROB);
+    const int k = blockIdx.x * blockDim.x + threadIdx.x;
+    const int pos = k / kDenseMax, j = k % kDenseMax;
+    if (pos >= npos || j >= nd) return;
+    float acc = 0.f;
+    for (int c = 0; c < n_vchunks; ++c) acc += dpart[((size_t)c * BLpad + pos) * kDenseMax + j];
+    dval[(size_t)pos * kDenseMax + j] = acc;
+}
+
+constexpr int kPairsPerThread = 4;
+
+// every (position, pair) value: grid.x over pair groups, grid.y over positions
+__global__ void emission_pairs(DevTable d, int L, EmitSrc src, float *__restrict__ val,
+                               int32_t *__restrict__ status)
+{
+    const int q0 = (blockIdx.x * blockDim.x + threadIdx.x) * kPairsPerThread;
+    const size_t pos = blockIdx.y;
+    int bad = 0;
+#pragma unroll
+    for (int u = 0; u < kPairsPerThread; ++u) {
+        const int q = q0 + u;
+        if (q < d.npairs) val[pos * d.npairs + q] = pair_value(d, q, pos, src, bad);
+    }
+    if (bad) atomicOr(&status[pos / L], (int)FA_ROW_BADPROB);
+}
+
+// dense leaf rows through the (row, column) -> pair maps: one wavefront per
+// stored row, four columns per lane per step, float4 stores
+__global__ __launch_bounds__(256) void emission_densify_map(DevTable d, StepView sv,
+                                                            const float *__restrict__ val,
+                                                            float *__restrict__ tree,
+                                                            int32_t *__restrict__ meta)
+{
+    const int lane = threadIdx.x & 63;
+    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int b = blockIdx.y / sv.Lpad, i = blockIdx.y % sv.Lpad;
+    if (r >= sv.Sp) return;
+    const int h = sv.Lpad + i;
+    const bool tr = stored_transposed(h);
+    const size_t pos = (size_t)b * sv.L + i;
+    float *out = sv.mat_ptr(tree, b, h) + (size_t)r * sv.Sp;
+    const int32_t *map = (tr ? d.map_t : d.map_n) + (size_t)r * sv.Sp;
+    const float *pv = val + pos * d.npairs;
+    int emax = kNeg;
+    for (int c = 4 * lane; c < sv.Sp; c += 256) {
+        float4 x;
+        if (i < sv.L) {
+            const int4 m = *reinterpret_cast<const int4 *>(map + c);
+            x.x = m.x >= 0 ? pv[m.x] : 0.f;
+            x.y = m.y >= 0 ? pv[m.y] : 0.f;
+            x.z = m.z >= 0 ? pv[m.z] : 0.f;
+            x.w = m.w >= 0 ? pv[m.w] : 0.f;
+        } else {  // identity leaf
+            x.x = (c == r && r < d.S) ? 1.f : 0.f;
+            x.y = (c + 1 == r && r < d.S) ? 1.f : 0.f;
+            x.z = (c + 2 == r && r < d.S) ? 1.f : 0.f;
+            x.w = (c + 3 == r && r < d.S) ? 1.f : 0.f;
+        }
+        *reinterpret_cast<float4 *>(out + c) = x;
+        emax = max(max(emax, fexp(x.x)), max(fexp(x.y), max(fexp(x.z), fexp(x.w))));
+    }
+    emax = wave_max_i(emax);
+    if (lane == 0) {
+        sv.meta_ptr(meta, b, h, 2)[r] = emax;
+        sv.meta_ptr(meta, b, h, 0)[r] = 0;
+        sv.meta_ptr(meta, b, h, 1)[r] = 0;
     }
 }
 
@@ -325,11 +399,17 @@ int launch_build_transitions(const DevTable &d, const Geometry &g, const float *
     src.cutp = (double *)(ws + w.cutp);
     src.n_vchunks = w.n_vchunks;
     src.BLpad = BLpad;
+    src.dval = (float *)(ws + w.dval);
     if (d.ndense > 0) {
         dim3 grid(w.n_vchunks, BLpad / kDenseTile);
         emission_dense<<<grid, kDenseThreads, 0, st>>>(d, p, g.L, npos, BLpad, (float *)src.dpart,
                                                        (float *)src.psel, status);
         hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return (int)e;
+        const int n = npos * kDenseMax;
+        emission_dense_reduce<<<(n + 255) / 256, 256, 0, st>>>(w.n_vchunks, BLpad, npos, d.ndense,
+                                                               src.dpart, (float *)src.dval);
+        e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
     }
     if (d.nseg > 0) {
@@ -338,16 +418,20 @@ int launch_build_transitions(const DevTable &d, const Geometry &g, const float *
         if (e != hipSuccess) return (int)e;
     }
     float *val = (float *)(ws + w.val);
-    const size_t total = (size_t)npos * d.npairs;
-    if (total) {
-        const int blocks = (int)std::min<size_t>((total + 255) / 256, 1 << 20);
-        emission_pairs<<<blocks, 256, 0, st>>>(d, g.L, total, src, val, status);
+    if (d.npairs > 0) {
+        dim3 pgrid((d.npairs + 256 * kPairsPerThread - 1) / (256 * kPairsPerThread), npos);
+        emission_pairs<<<pgrid, 256, 0, st>>>(d, g.L, src, val, status);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
     }
     StepView sv = step_view(g);
-    dim3 grid((g.Sp + 4 * kRowsPerWave - 1) / (4 * kRowsPerWave), g.B * g.Lpad);
-    emission_densify<<<grid, kDensifyThreads, 0, st>>>(d, sv, val, tree, meta);
+    if (d.map_n) {
+        dim3 grid((g.Sp + 3) / 4, g.B * g.Lpad);
+        emission_densify_map<<<grid, 256, 0, st>>>(d, sv, val, tree, meta);
+    } else {
+        dim3 grid((g.Sp + 4 * kRowsPerWave - 1) / (4 * kRowsPerWave), g.B * g.Lpad);
+        emission_densify<<<grid, kDensifyThreads, 0, st>>>(d, sv, val, tree, meta);
+    }
     return (int)hipGetLastError();
 }
 

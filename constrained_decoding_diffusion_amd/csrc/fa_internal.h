@@ -17,6 +17,7 @@ constexpr int kDenseMax = 32;      // dense-label pairs share one mask word per 
 constexpr int kDenseChunk = 4096;  // tokens per workgroup of the dense-mask contraction
 constexpr int kDenseTile = 32;     // positions per workgroup of the dense-mask contraction
 constexpr int kSelMax = 8192;      // LIST tokens gathered through a compact copy of p
+constexpr int kMapMaxSp = 2048;   // dense (row, column) -> pair maps up to this Sp
 constexpr uint32_t kSelBit = 1u << 31;  // tokmask flag of LIST tokens (tables with < 32 dense pairs)
 
 enum PairClass : int32_t { kList = 0, kDense = 1, kRange = 2 };
@@ -68,6 +69,8 @@ struct DevTable {
     const int32_t *tok2sel;    // [V] index into sel_tok or -1 (nsel > 0)
     const int32_t *tok2cut;    // [V] largest c with cuts[c] <= v, or -1 (nseg > 0)
     const int32_t *seg_pair;   // [nseg] pair of each segment
+    const int32_t *map_n;      // [Sp][Sp] pair at (a, b) or -1 (Sp <= kMapMaxSp)
+    const int32_t *map_t;      // [Sp][Sp] pair at (b, a) (transposed storage)
 };
 
 // Host representation of a compiled automaton and its device image.
@@ -84,6 +87,7 @@ struct HostTable {
     std::vector<int32_t> seg_off, seg_lo, seg_hi, seg_lo_cut, seg_hi_cut, cuts, cut_off, cut_ev;
     std::vector<float> seg_cnt;
     std::vector<int32_t> tok2sel, tok2cut, seg_pair;
+    std::vector<int32_t> map_n, map_t;
     bool has_cnt = false;
     bool use_sel = false;
     bool selbit = false;
@@ -114,7 +118,7 @@ bool make_geometry(const HostTable &t, int32_t B, int32_t L, Geometry *g);
 
 // Workspace layout (bytes from the start of ws), sized for the largest user.
 struct WsLayout {
-    size_t dpart = 0, psel = 0, cutp = 0, val = 0;  // emission reduce
+    size_t dpart = 0, dval = 0, psel = 0, cutp = 0, val = 0;  // emission reduce
     int32_t n_vchunks = 0;                     // dense-mask contraction: V split
     size_t zc = 0;                             // sampler: compact boundary states
     size_t va = 0, ea = 0, vb = 0, eb = 0;     // marginals: messages

@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256) void sample_level(DevTable d, StepView sv,
 }
 
 constexpr int kTokThreads = 256;
-constexpr int kTokChunksMax = 1024;
+constexpr int kTokChunksMax = 256;
 
 // candidates of one token draw: the tokens of the pair (z_i, z_{i+1}) in
 // ascending order, weight p[i][v] times the number of edges holding v
@@ -172,6 +172,7 @@ __global__ __launch_bounds__(kTokThreads) void sample_tokens(
     const int32_t *z = zc + (size_t)b * (sv.Lpad + 1);
     const int a = z[i], c = z[i + 1];
     __shared__ double csum[kTokChunksMax];
+    __shared__ double wsum[kTokChunksMax][4];
     __shared__ double sh_w[4];
     __shared__ double sh_scan[kTokThreads];
     __shared__ int sh_q, sh_chunk;
@@ -241,13 +242,16 @@ __global__ __launch_bounds__(kTokThreads) void sample_tokens(
         for (int k = k0; k < min(k0 + per, cd.n); ++k) s += (double)tok_weight(d, cd, prow, k, sg);
         return s;
     };
+    // per-chunk wavefront partials, combined in wavefront order after one
+    // barrier
     for (int ch = 0; ch < nchunks; ++ch) {
-        double s = wave_sum_d(run_sum(ch * chunk));
-        if (lane == 0) sh_w[wave] = s;
-        __syncthreads();
-        if (tid == 0) csum[ch] = ((sh_w[0] + sh_w[1]) + sh_w[2]) + sh_w[3];
-        __syncthreads();
+        const double s = wave_sum_d(run_sum(ch * chunk));
+        if (lane == 0) wsum[ch][wave] = s;
     }
+    __syncthreads();
+    for (int ch = tid; ch < nchunks; ch += kTokThreads)
+        csum[ch] = ((wsum[ch][0] + wsum[ch][1]) + wsum[ch][2]) + wsum[ch][3];
+    __syncthreads();
     if (tid == 0) {
         double T = 0.0;
         for (int ch = 0; ch < nchunks; ++ch) T += csum[ch];

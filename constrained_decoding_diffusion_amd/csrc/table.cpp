@@ -69,6 +69,8 @@ void build_image(HostTable &t)
     append_section(t.image, t.offs, t.tok2sel);
     append_section(t.image, t.offs, t.tok2cut);
     append_section(t.image, t.offs, t.seg_pair);
+    append_section(t.image, t.offs, t.map_n);
+    append_section(t.image, t.offs, t.map_t);
     t.image.resize((t.image.size() + 255) & ~size_t(255));
 }
 
@@ -101,6 +103,11 @@ DevTable HostTable::device_view() const
     nxt(d.tm_cnt); nxt(d.dense_pair); nxt(d.tokmask); nxt(d.seg_off); nxt(d.seg_lo);
     nxt(d.seg_hi); nxt(d.seg_cnt); nxt(d.seg_lo_cut); nxt(d.seg_hi_cut); nxt(d.cuts);
     nxt(d.cut_off); nxt(d.cut_ev); nxt(d.tok2sel); nxt(d.tok2cut); nxt(d.seg_pair);
+    nxt(d.map_n); nxt(d.map_t);
+    if (map_n.empty()) {
+        d.map_n = nullptr;
+        d.map_t = nullptr;
+    }
     if (!has_cnt) {
         d.list_cnt = nullptr;
         d.tm_cnt = nullptr;
@@ -136,6 +143,7 @@ WsLayout ws_layout(const HostTable &t, const Geometry &g)
     w.n_vchunks = t.ndense() ? (t.V + kDenseChunk - 1) / kDenseChunk : 0;
     size_t BLpad = (BL + kDenseTile - 1) / kDenseTile * kDenseTile;
     w.dpart = o; o = al(o + (size_t)w.n_vchunks * BLpad * kDenseMax * sizeof(float));
+    w.dval = o; o = al(o + (t.ndense() ? BL * kDenseMax * sizeof(float) : 0));
     w.psel = o; o = al(o + (t.use_sel ? BL * t.nsel() * sizeof(float) : 0));
     w.cutp = o; o = al(o + BL * t.ncut() * sizeof(double));
     w.val = o; o = al(o + BL * t.npairs() * sizeof(float));
@@ -462,6 +470,16 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
     for (int32_t c = 0, v = 0; v < (t.ncut() > 0 ? V : 0); ++v) {
         while (c < t.ncut() && t.cuts[c] <= v) ++c;
         t.tok2cut[v] = c - 1;
+    }
+    t.map_n.clear();
+    t.map_t.clear();
+    if (t.Sp <= kMapMaxSp) {
+        t.map_n.assign((size_t)t.Sp * t.Sp, -1);
+        t.map_t.assign((size_t)t.Sp * t.Sp, -1);
+        for (int32_t q = 0; q < np; ++q) {
+            t.map_n[(size_t)t.pair_a[q] * t.Sp + t.pair_b[q]] = q;
+            t.map_t[(size_t)t.pair_b[q] * t.Sp + t.pair_a[q]] = q;
+        }
     }
     t.use_sel = t.needs_stream() && ns > 0 && ns <= kSelMax;
     t.selbit = t.ndense() > 0 && t.ndense() < 32 && ns > 0;

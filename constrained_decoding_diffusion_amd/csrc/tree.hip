@@ -48,12 +48,14 @@ __device__ inline void load8(const float *src, float4 &a, float4 &b)
     b = *reinterpret_cast<const float4 *>(src + 4);
 }
 
+// exact power-of-two rescale of four consumed entries; zero stays zero and
+// values more than 2^126 below the row maximum flush to zero
 __device__ inline float4 fold4(float4 x, int4 c, int rfrow)
 {
-    x.x = scale2(x.x, c.x - rfrow);
-    x.y = scale2(x.y, c.y - rfrow);
-    x.z = scale2(x.z, c.z - rfrow);
-    x.w = scale2(x.w, c.w - rfrow);
+    x.x = ldexpf(x.x, c.x - rfrow);
+    x.y = ldexpf(x.y, c.y - rfrow);
+    x.z = ldexpf(x.z, c.z - rfrow);
+    x.w = ldexpf(x.w, c.w - rfrow);
     return x;
 }
 
@@ -140,6 +142,125 @@ __global__ __launch_bounds__(kGemmThreads) void span_gemm(StepView sv, float *__
     if (blockIdx.x / tiles == 0 && tid < kTile) coD[tn + tid] = add_exp(roG[tn + tid], rfG[tn + tid]);
 }
 
+constexpr int kBig = 128;       // output tile of the large-level kernel
+constexpr int kBK2 = 32;        // K step per LDS stage
+constexpr int kLdk2 = kBK2 + 4; // padded LDS row (floats)
+constexpr int kBigThreads = 512;
+
+// 128x128 output tiles, eight wavefronts of 32x64 (1x2 MFMA 32x32x2 blocks),
+// double-buffered LDS stages of K = 32 (74 KB of LDS); the global data of
+// stage s+1 is loaded while stage s runs.  Small per-wave state keeps four
+// wavefronts per SIMD resident.  grid.x enumerates (product, tile) so that
+// the tiles of one product land on one XCD.
+__global__ __launch_bounds__(kBigThreads) void span_gemm128(StepView sv, float *__restrict__ tree,
+                                                            int32_t *__restrict__ meta, int n0,
+                                                            int nn)
+{
+    const int Sp = sv.Sp;
+    const int tiles = Sp / kBig;
+    const int per_prod = tiles * tiles;
+    const int nwork = sv.B * nn * per_prod;
+    int w = blockIdx.x;
+    const int full = nwork & ~7;
+    if (w < full) w = (w & 7) * (full >> 3) + (w >> 3);  // XCD-contiguous work order
+    const int prod = w / per_prod, tile = w % per_prod;
+    const int tm = (tile / tiles) * kBig, tn = (tile % tiles) * kBig;
+    const int b = prod / nn, n = n0 + prod % nn;
+    const bool tr = stored_transposed(n);
+    const int hF = tr ? 2 * n + 1 : 2 * n, hG = tr ? 2 * n : 2 * n + 1;
+    const float *F = sv.mat_ptr((const float *)tree, b, hF);
+    const float *G = sv.mat_ptr((const float *)tree, b, hG);
+    const int32_t *roF = sv.meta_ptr((const int32_t *)meta, b, hF, 0);
+    const int32_t *coF = sv.meta_ptr((const int32_t *)meta, b, hF, 1);
+    const int32_t *rfF = sv.meta_ptr((const int32_t *)meta, b, hF, 2);
+    const int32_t *roG = sv.meta_ptr((const int32_t *)meta, b, hG, 0);
+    const int32_t *coG = sv.meta_ptr((const int32_t *)meta, b, hG, 1);
+    const int32_t *rfG = sv.meta_ptr((const int32_t *)meta, b, hG, 2);
+    float *D = sv.mat_ptr(tree, b, n);
+    int32_t *roD = sv.meta_ptr(meta, b, n, 0);
+    int32_t *coD = sv.meta_ptr(meta, b, n, 1);
+    int32_t *rfD = sv.meta_ptr(meta, b, n, 2);
+
+    __shared__ __align__(16) float Fs[2][kBig][kLdk2];
+    __shared__ __align__(16) float Gs[2][kBig][kLdk2];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // loader: thread t stages row t>>2, k-quarter (t&3)*8 of both operands
+    const int lrow = tid >> 2, lk = (tid & 3) * 8;
+    const int rfFrow = rfF[tm + lrow], rfGrow = rfG[tn + lrow];
+    const float *Frow = F + (size_t)(tm + lrow) * Sp + lk;
+    const float *Grow = G + (size_t)(tn + lrow) * Sp + lk;
+    const int wr = (wave >> 1) * 32, wc = (wave & 1) * 64;
+    const int l32 = lane & 31, half = lane >> 5;
+
+    f32x16 acc[2];
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[y][r] = 0.f;
+
+    float4 fr[2], gr[2];
+    int4 cf[2], cg[2];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            fr[q] = *reinterpret_cast<const float4 *>(Frow + k0 + 4 * q);
+            gr[q] = *reinterpret_cast<const float4 *>(Grow + k0 + 4 * q);
+            cf[q] = *reinterpret_cast<const int4 *>(coF + k0 + lk + 4 * q);
+            cg[q] = *reinterpret_cast<const int4 *>(coG + k0 + lk + 4 * q);
+        }
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            *reinterpret_cast<float4 *>(&Fs[buf][lrow][lk + 4 * q]) = fold4(fr[q], cf[q], rfFrow);
+            *reinterpret_cast<float4 *>(&Gs[buf][lrow][lk + 4 * q]) = fold4(gr[q], cg[q], rfGrow);
+        }
+    };
+    const int nk = Sp / kBK2;
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int ks = 0; ks < nk; ++ks) {
+        const int buf = ks & 1;
+        if (ks + 1 < nk) gload((ks + 1) * kBK2);
+#pragma unroll
+        for (int t = 0; t < kBK2 / 2; t += 4) {
+            const float4 a = *reinterpret_cast<const float4 *>(&Fs[buf][wr + l32][half * (kBK2 / 2) + t]);
+            float4 c[2];
+#pragma unroll
+            for (int y = 0; y < 2; ++y)
+                c[y] = *reinterpret_cast<const float4 *>(&Gs[buf][wc + 32 * y + l32][half * (kBK2 / 2) + t]);
+#pragma unroll
+            for (int y = 0; y < 2; ++y) {
+                acc[y] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, c[y].x, acc[y], 0, 0, 0);
+                acc[y] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, c[y].y, acc[y], 0, 0, 0);
+                acc[y] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, c[y].z, acc[y], 0, 0, 0);
+                acc[y] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, c[y].w, acc[y], 0, 0, 0);
+            }
+        }
+        if (ks + 1 < nk) lstore(buf ^ 1);
+        __syncthreads();
+    }
+    // epilogue
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {
+        const int j = tn + wc + 32 * y + l32;
+        const int coDj = add_exp(roG[j], rfG[j]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int i = tm + wr + (r >> 2) * 8 + half * 4 + (r & 3);
+            const float v = acc[y][r];
+            D[(size_t)i * Sp + j] = v;
+            int e = (v > 0.f && coDj > kNeg) ? fexp(v) + coDj : kNeg;
+#pragma unroll
+            for (int o = 16; o > 0; o >>= 1) e = max(e, __shfl_xor(e, o));
+            if (l32 == 0 && e > kNeg) atomicMax(&rfD[i], e);
+        }
+    }
+    if (tn == 0 && tid < kBig) roD[tm + tid] = add_exp(roF[tm + tid], rfF[tm + tid]);
+    if (tm == 0 && tid < kBig) coD[tn + tid] = add_exp(roG[tn + tid], rfG[tn + tid]);
+}
+
 // log Z[b] = ln sum_{f in F} T_root[s0][f]
 __global__ void tree_logz(DevTable d, StepView sv, const float *__restrict__ tree,
                           const int32_t *__restrict__ meta, double *__restrict__ logZ,
@@ -207,8 +328,14 @@ int launch_span_tree(const DevTable &d, const Geometry &g, float *tree, int32_t 
     const int tiles = g.Sp / kTile;
     for (int k = 1; k <= g.K; ++k) {
         const int n0 = g.Lpad >> k, nn = n0;
-        dim3 grid(tiles * tiles, g.B * nn);
-        span_gemm<<<grid, kGemmThreads, 0, st>>>(sv, tree, meta, n0, nn);
+        const int big_tiles = g.Sp / kBig;
+        const long long big_wgs = (long long)g.B * nn * big_tiles * big_tiles;
+        if (g.Sp % kBig == 0 && big_wgs >= 512) {
+            span_gemm128<<<(unsigned)big_wgs, kBigThreads, 0, st>>>(sv, tree, meta, n0, nn);
+        } else {
+            dim3 grid(tiles * tiles, g.B * nn);
+            span_gemm<<<grid, kGemmThreads, 0, st>>>(sv, tree, meta, n0, nn);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
     }

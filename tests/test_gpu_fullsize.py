@@ -41,3 +41,18 @@ def test_random_nfa_full():
     orc = oracle.Oracle(w.aut)
     rep = PT.check_row(w, g, 0, orc, q_positions=_sampled_positions(w.L, 4, 7))
     PT.log(f"[full] nfa row 0: ok ({rep})")
+
+
+@pytest.mark.timeout(300)
+def test_range_dfa_full():
+    # the full range workload: generation of p (16 x 512 x 151,936) dominates
+    PT.log("[full] range DFA: generating inputs")
+    w = configs.make(4)
+    PT.log(f"[full] {w.describe()}")
+    g = PT.run_gpu(w)
+    PT.log(f"[full] range DFA: gpu done, status {g['status'].tolist()}")
+    assert (g["status"] == 0).all()
+    orc = oracle.Oracle(w.aut)
+    for b in (0, w.B - 1):
+        rep = PT.check_row(w, g, b, orc, q_positions=_sampled_positions(w.L, 3, 300 + b))
+        PT.log(f"[full] range DFA row {b}: ok ({rep})")
