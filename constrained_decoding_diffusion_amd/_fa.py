@@ -51,7 +51,7 @@ def lib():
     L.fa_table_state_map.argtypes = [P, P]
     L.fa_sizes.argtypes = [P, I32, I32, P, P, P]
     L.fa_build_transitions.argtypes = [P, P, I32, I32, P, P, P, SZ, P, P]
-    L.fa_span_tree.argtypes = [P, I32, I32, P, P, P, P, P]
+    L.fa_span_tree.argtypes = [P, I32, I32, P, P, P, SZ, P, P, P]
     L.fa_sample.argtypes = [P, P, I32, I32, P, P, U64, P, P, P, SZ, P, P]
     L.fa_marginals.argtypes = [P, P, I32, I32, P, P, P, P, I32, P, P, P, SZ, P, P]
     L.fa_strerror.argtypes = [C.c_int]
@@ -160,8 +160,8 @@ def build_transitions(table: Table, p, bufs: StepBuffers, stream):
 
 def span_tree(table: Table, bufs: StepBuffers, stream):
     _check("fa_span_tree", lib().fa_span_tree(
-        table.handle, bufs.B, bufs.L, _ptr(bufs.tree), _ptr(bufs.meta), _ptr(bufs.logZ),
-        _ptr(bufs.status), C.c_void_p(stream)))
+        table.handle, bufs.B, bufs.L, _ptr(bufs.tree), _ptr(bufs.meta), _ptr(bufs.ws),
+        bufs.ws.numel(), _ptr(bufs.logZ), _ptr(bufs.status), C.c_void_p(stream)))
 
 
 def sample(table: Table, p, bufs: StepBuffers, seed: int, stream):

@@ -52,7 +52,8 @@ extern "C" int fa_build_transitions(const fa_table *t, const float *p, int32_t B
 }
 
 extern "C" int fa_span_tree(const fa_table *t, int32_t B, int32_t L, float *tree, int32_t *meta,
-                            double *logZ, int32_t *row_status, fa_stream_t stream)
+                            void *ws, size_t ws_bytes, double *logZ, int32_t *row_status,
+                            fa_stream_t stream)
 {
     int rc = ready(t);
     if (rc) return rc;
@@ -60,8 +61,11 @@ extern "C" int fa_span_tree(const fa_table *t, int32_t B, int32_t L, float *tree
     if (!make_geometry(t->h, B, L, &g)) return FA_EINVAL;
     if (!grid_fits(g)) return FA_ETOOBIG;
     if (B == 0) return FA_OK;
-    if (!logZ || !row_status || (L > 0 && (!tree || !meta))) return FA_EINVAL;
-    return hip_rc(launch_span_tree(t->h.device_view(), g, tree, meta, logZ, row_status, stream));
+    if (!logZ || !row_status) return FA_EINVAL;
+    WsLayout w = ws_layout(t->h, g);
+    if (L > 0 && (!tree || !meta || !ws || ws_bytes < w.total)) return FA_EINVAL;
+    return hip_rc(launch_span_tree(t->h.device_view(), g, tree, meta, (uint8_t *)ws, w, logZ,
+                                   row_status, stream));
 }
 
 extern "C" int fa_sample(const fa_table *t, const float *p, int32_t B, int32_t L, const float *tree,

@@ -31,30 +31,32 @@ __global__ __launch_bounds__(kDenseThreads) void emission_dense(
     DevTable d, const float *__restrict__ p, int L, int npos, int BLpad,
     float *__restrict__ dpart, float *__restrict__ psel, int32_t *__restrict__ status)
 {
-    __shared__ __align__(16) float pt[kDenseTile][kSubLd];
-    __shared__ __align__(16) uint32_t mk[kSub];
-    __shared__ float red[4][kDenseTile * kDenseTile];
-    __shared__ int sh_sel0;
+    constexpr int kSteps = kDenseChunk / kSub;
+    __shared__ __align__(16) float pt[2][kDenseTile][kSubLd];
+    __shared__ __align__(16) uint32_t mk[2][kSub];
+    __shared__ int sel_at[kSteps + 1];  // first token-list index at or after each step
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int chunk = blockIdx.x;
     const int pos0 = blockIdx.y * kDenseTile;
     const int v_begin = chunk * kDenseChunk;
     const int v_end = min(d.V, v_begin + kDenseChunk);
+    const int nsteps = (v_end - v_begin + kSub - 1) / kSub;
     const bool vec = (d.V & 3) == 0;
-    // staging map: thread t loads row (t >> 3), 32 tokens at column 32*(t&7);
-    // threads 0..63 also load the mask words of four tokens each
-    const int srow = tid >> 3, scol = (tid & 7) * 32;
-    const bool row_ok = pos0 + srow < npos;
-    const float *prow = p + (size_t)(pos0 + srow) * d.V;
+    // staging map: load k of thread t is float4 number 256k + t of the
+    // 32 x 256 tile, so each wavefront reads one contiguous 1 KB row segment
+    // (row 4k + wave, column 4*lane); threads 0..63 also load the mask words
+    // of four tokens each
+    const int scol = 4 * lane;
     int bad = 0;
-    if (tid == 0) {
+    if (psel && tid <= kSteps) {
+        const int vs = v_begin + tid * kSub;
         int lo = 0, hi = d.nsel;
         while (lo < hi) {
             const int mid = (lo + hi) >> 1;
-            if (d.sel_tok[mid] < v_begin) lo = mid + 1;
+            if (d.sel_tok[mid] < vs) lo = mid + 1;
             else hi = mid;
         }
-        sh_sel0 = lo;
+        sel_at[tid] = lo;
     }
     f32x16 acc;
 #pragma unroll
@@ -67,7 +69,10 @@ __global__ __launch_bounds__(kDenseThreads) void emission_dense(
     auto load = [&](Step &st, int v0) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const int v = v0 + scol + 4 * k;
+            const int row = 4 * k + wave;
+            const bool row_ok = pos0 + row < npos;
+            const float *prow = p + (size_t)(pos0 + row) * d.V;
+            const int v = v0 + scol;
             if (row_ok && vec && v + 3 < v_end) {
                 st.x[k] = *reinterpret_cast<const float4 *>(prow + v);
             } else {
@@ -89,25 +94,25 @@ __global__ __launch_bounds__(kDenseThreads) void emission_dense(
             }
         }
     };
-    load(sa, v_begin);
-    if (v_begin + kSub < v_end) load(sb, v_begin + kSub);
-    __syncthreads();
-    int sptr = sh_sel0;
-    const int half = lane >> 5, l32 = lane & 31;
-    auto step = [&](Step &st, int v0) {
-        __syncthreads();
+    auto store = [&](const Step &st, int buf) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            bad |= !(st.x[k].x >= 0.f) | !(st.x[k].y >= 0.f) | !(st.x[k].z >= 0.f) |
-                   !(st.x[k].w >= 0.f);
-            *reinterpret_cast<float4 *>(&pt[srow][scol + 4 * k]) = st.x[k];
+            const int row = 4 * k + wave;
+            const bool b = !(st.x[k].x >= 0.f) | !(st.x[k].y >= 0.f) | !(st.x[k].z >= 0.f) |
+                           !(st.x[k].w >= 0.f);
+            if (b) bad |= 1 << k;  // remember which staged rows saw a bad value
+            *reinterpret_cast<float4 *>(&pt[buf][row][scol]) = st.x[k];
         }
-        if (tid < kSub / 4) *reinterpret_cast<uint4 *>(&mk[4 * tid]) = st.m;
-        __syncthreads();
-        if (v0 + 2 * kSub < v_end) load(st, v0 + 2 * kSub);
-        // the wave's 64 tokens; half h covers tokens 32h .. 32h+31 of them
-        const float *brow = &pt[l32][64 * wave + 32 * half];
-        const uint32_t *mrow = &mk[64 * wave + 32 * half];
+        if (tid < kSub / 4) *reinterpret_cast<uint4 *>(&mk[buf][4 * tid]) = st.m;
+    };
+    const int half = lane >> 5, l32 = lane & 31;
+    // step s: MFMAs over LDS buffer s&1, copy of the token-list tokens, then
+    // stage s+1 (registers) to the other buffer and a new load into the
+    // freed registers; one barrier per step
+    auto step = [&](int s, Step &next, int buf) {
+        const int v0 = v_begin + s * kSub;
+        const float *brow = &pt[buf][l32][64 * wave + 32 * half];
+        const uint32_t *mrow = &mk[buf][64 * wave + 32 * half];
 #pragma unroll
         for (int t = 0; t < 32; t += 4) {
             const float4 bq = *reinterpret_cast<const float4 *>(brow + t);
@@ -117,35 +122,50 @@ __global__ __launch_bounds__(kDenseThreads) void emission_dense(
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32((float)((mq.z >> l32) & 1u), bq.z, acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32((float)((mq.w >> l32) & 1u), bq.w, acc, 0, 0, 0);
         }
-        // copy p at the token-list tokens of this step (sorted, unique)
         if (psel) {
-            const int idx = sptr + tid;
-            const int tk = idx < d.nsel ? d.sel_tok[idx] : 0x7fffffff;
-            const bool in = tk < min(v0 + kSub, v_end);
-            if (in)
+            const int idx = sel_at[s] + tid;
+            if (idx < sel_at[s + 1]) {
+                const int tk = d.sel_tok[idx];
                 for (int r = 0; r < kDenseTile && pos0 + r < npos; ++r)
-                    psel[(size_t)(pos0 + r) * d.nsel + idx] = pt[r][tk - v0];
-            sptr += __syncthreads_count(in);
+                    psel[(size_t)(pos0 + r) * d.nsel + idx] = pt[buf][r][tk - v0];
+            }
         }
+        if (s + 1 < nsteps) {
+            store(next, buf ^ 1);
+            if (s + 3 < nsteps) load(next, v_begin + (s + 3) * kSub);
+        }
+        __syncthreads();
     };
-    for (int v0 = v_begin; v0 < v_end; v0 += 2 * kSub) {
-        step(sa, v0);
-        if (v0 + kSub < v_end) step(sb, v0 + kSub);
+    load(sa, v_begin);
+    if (nsteps > 1) load(sb, v_begin + kSub);
+    store(sa, 0);
+    if (nsteps > 2) load(sa, v_begin + 2 * kSub);
+    __syncthreads();
+    // stage s sits in sa (s even) or sb (s odd)
+    for (int s = 0; s < nsteps; s += 2) {
+        step(s, sb, 0);
+        if (s + 1 < nsteps) step(s + 1, sa, 1);
     }
-    // sum the four waves' tiles in wave order
+    // sum the four waves' tiles in wave order (reusing the staging LDS)
+    float *red = &pt[0][0][0];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int i = (r >> 2) * 8 + half * 4 + (r & 3);
-        red[wave][i * kDenseTile + l32] = acc[r];
+        red[wave * (kDenseTile * kDenseTile) + i * kDenseTile + l32] = acc[r];
     }
     __syncthreads();
     float *outp = dpart + ((size_t)chunk * BLpad + pos0) * kDenseMax;
     for (int k = tid; k < kDenseTile * kDenseTile; k += kDenseThreads) {
         const int i = k / kDenseTile, j = k % kDenseTile;  // pair i, position j
-        const float s = ((red[0][k] + red[1][k]) + red[2][k]) + red[3][k];
-        outp[(size_t)j * kDenseMax + i] = s;
+        const int W = kDenseTile * kDenseTile;
+        const float sum = ((red[k] + red[W + k]) + red[2 * W + k]) + red[3 * W + k];
+        outp[(size_t)j * kDenseMax + i] = sum;
     }
-    if (bad && row_ok) atomicOr(&status[(pos0 + srow) / L], (int)FA_ROW_BADPROB);
+    for (int k = 0; k < 8; ++k) {
+        const int row = 4 * k + wave;
+        if (((bad >> k) & 1) && pos0 + row < npos)
+            atomicOr(&status[(pos0 + row) / L], (int)FA_ROW_BADPROB);
+    }
 }
 
 constexpr int kStreamThreads = 256;

@@ -121,6 +121,7 @@ struct WsLayout {
     size_t dpart = 0, dval = 0, psel = 0, cutp = 0, val = 0;  // emission reduce
     int32_t n_vchunks = 0;                     // dense-mask contraction: V split
     size_t zc = 0;                             // sampler: compact boundary states
+    size_t kpart = 0;                          // span tree: split-K partial tiles
     size_t va = 0, ea = 0, vb = 0, eb = 0;     // marginals: messages
     size_t rcut = 0;                           // marginals: range weights per cut
     size_t total = 0;
@@ -133,7 +134,11 @@ int launch_build_transitions(const DevTable &d, const Geometry &g, const float *
                              int32_t *meta, uint8_t *ws, const WsLayout &w, int32_t *status,
                              void *stream);
 int launch_span_tree(const DevTable &d, const Geometry &g, float *tree, int32_t *meta,
-                     double *logZ, int32_t *status, void *stream);
+                     uint8_t *ws, const WsLayout &w, double *logZ, int32_t *status, void *stream);
+
+// Split of one tree level's products along K (upper levels with few
+// products): 1 = no split.
+int tree_ksplit(const Geometry &g, int level);
 int launch_sample(const DevTable &d, const Geometry &g, const float *p, const float *tree,
                   const int32_t *meta, uint64_t seed, int32_t *states, int32_t *tokens,
                   uint8_t *ws, const WsLayout &w, int32_t *status, void *stream);

@@ -52,6 +52,8 @@ __global__ __launch_bounds__(kMsgThreads) void marg_level(
     int32_t *__restrict__ eb)
 {
     constexpr int PER = CW / 64;  // columns per lane: 4 or 1
+    extern __shared__ float gsh[];  // [Sp] normalized input weights, then [Sp] row folds
+    int *rsh = reinterpret_cast<int *>(gsh + sv.Sp);
     __shared__ int sh_max[kMsgWaves];
     __shared__ float red[kMsgWaves][CW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -71,11 +73,13 @@ __global__ __launch_bounds__(kMsgThreads) void marg_level(
     const int32_t *ro = sv.meta_ptr(meta, b, h, 0);
     const int32_t *co = sv.meta_ptr(meta, b, h, 1);
     const int32_t *rf = sv.meta_ptr(meta, b, h, 2);
-    // G = max_a e(in[a]) + ro[a] + rf[a]
+    // G = max_a e(in[a]) + ro[a] + rf[a]; the per-row exponents go to LDS
     int e = kNeg;
     for (int a = tid; a < d.S; a += kMsgThreads) {
         const float x = vin[a];
         const int s = add_exp(ro[a], rf[a]);
+        rsh[a] = s;
+        gsh[a] = x;
         if (x > 0.f && s > kNeg) e = max(e, fexp(x) + s);
     }
     e = wave_max_i(e);
@@ -83,6 +87,15 @@ __global__ __launch_bounds__(kMsgThreads) void marg_level(
     __syncthreads();
     int G = kNeg;
     for (int w = 0; w < kMsgWaves; ++w) G = max(G, sh_max[w]);
+    // normalized input weights g[a] and the row fold rf[a] (replaces the
+    // row exponent slot)
+    for (int a = tid; a < d.S; a += kMsgThreads) {
+        const float x = gsh[a];
+        const int s = rsh[a];
+        gsh[a] = (x > 0.f && s > kNeg && G > kNeg) ? scale2(mant(x), fexp(x) + s - G) : 0.f;
+        rsh[a] = rf[a];
+    }
+    __syncthreads();
     const int j0 = cb * CW + PER * lane;
     const bool colok = j0 < sv.Sp && G > kNeg;
     float acc[PER];
@@ -92,13 +105,11 @@ __global__ __launch_bounds__(kMsgThreads) void marg_level(
         int cj[PER];
 #pragma unroll
         for (int k = 0; k < PER; ++k) cj[k] = co[j0 + k];
+#pragma unroll 4
         for (int a = wave; a < d.S; a += kMsgWaves) {
-            const float x = vin[a];
-            const int s = add_exp(ro[a], rf[a]);
-            if (!(x > 0.f) || s <= kNeg) continue;
-            const float g = scale2(mant(x), fexp(x) + s - G);
+            const float g = gsh[a];
             if (g == 0.f) continue;
-            const int ra = rf[a];
+            const int ra = rsh[a];
             const float *row = P + (size_t)a * sv.Sp + j0;
             if constexpr (PER == 4) {
                 const float4 y = *reinterpret_cast<const float4 *>(row);
@@ -168,9 +179,13 @@ __device__ inline float list_weight(const DevTable &d, int s, const float *al, c
 }
 
 // One workgroup per position streams the p row once and writes the q row.
-// The dense-mask pairs' weight of a token is read from four 256-entry
-// tables indexed by the bytes of its mask word; tokens held by token-list
-// pairs carry a flag bit and add their precomputed weight.
+// The dense-mask pairs' weight of a token is read from NG 256-entry tables
+// indexed by the bytes of its mask word; with SELBIT, tokens held by
+// token-list pairs carry a flag bit and add their precomputed weight (LIST
+// only tables look every token up instead); RANGES adds the weight of the
+// token's cut interval.  The feature set is a template so the per-token
+// path has no branches beyond the rare token-list lookups.
+template <int NG, bool SELBIT, bool LISTALL, bool RANGES>
 __global__ __launch_bounds__(kQThreads) void marg_q(DevTable d, StepView sv,
                                                     const float *__restrict__ p,
                                                     const double *__restrict__ logZ,
@@ -184,8 +199,8 @@ __global__ __launch_bounds__(kQThreads) void marg_q(DevTable d, StepView sv,
                                                     const float *__restrict__ rcut,
                                                     const int32_t *__restrict__ status)
 {
-    __shared__ float lut[4][256];
-    __shared__ float rsel[kSelMax];
+    __shared__ float lut[NG > 0 ? NG : 1][256];
+    __shared__ float rsel[(SELBIT || LISTALL) ? kSelMax : 1];
     __shared__ double sh_h[4];
     const int b = blockIdx.y, i = blockIdx.x;
     const size_t pos = (size_t)b * sv.L + i;
@@ -204,8 +219,9 @@ __global__ __launch_bounds__(kQThreads) void marg_q(DevTable d, StepView sv,
     const double factor = exp2((double)e1 + (double)e2 - lz * 1.4426950408889634074);
     const float *al = va + ((size_t)b * (sv.Lpad + 1) + i) * sv.Sp;
     const float *be = vb + ((size_t)b * (sv.Lpad + 1) + i + 1) * sv.Sp;
-    const int nd = d.ndense, ng = (nd + 7) >> 3;
-    for (int g = 0; g < ng; ++g) {
+    const int nd = d.ndense;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
         float s = 0.f;
         for (int bit = 0; bit < 8; ++bit) {
             const int j = 8 * g + bit;
@@ -217,26 +233,28 @@ __global__ __launch_bounds__(kQThreads) void marg_q(DevTable d, StepView sv,
         lut[g][tid] = s;
     }
     const bool sel_lds = d.nsel > 0 && d.nsel <= kSelMax;
-    if (sel_lds)
-        for (int s = tid; s < d.nsel; s += kQThreads) rsel[s] = list_weight(d, s, al, be);
+    if (SELBIT || LISTALL)
+        if (sel_lds)
+            for (int s = tid; s < d.nsel; s += kQThreads) rsel[s] = list_weight(d, s, al, be);
     __syncthreads();
-    const float *rc = d.ncut ? rcut + pos * d.ncut : nullptr;
+    const float *rc = RANGES ? rcut + pos * d.ncut : nullptr;
     const int tok = tokens ? tokens[pos] : -1;
+    auto list_r = [&](int v) -> float {
+        const int s = d.tok2sel[v];
+        if (s < 0) return 0.f;
+        return sel_lds ? rsel[s] : list_weight(d, s, al, be);
+    };
     auto weight_r = [&](int v, uint32_t m) -> float {
         float r = 0.f;
-        bool sel = d.nsel > 0;
-        if (nd) {
-            r = lut[0][m & 255u];
-            if (ng > 1) r += lut[1][(m >> 8) & 255u];
-            if (ng > 2) r += lut[2][(m >> 16) & 255u];
-            if (ng > 3) r += lut[3][(m >> 24) & 255u];
-            if (d.selbit) sel = (m & kSelBit) != 0;
+        if constexpr (NG > 0) r = lut[0][m & 255u];
+        if constexpr (NG > 1) r += lut[1][(m >> 8) & 255u];
+        if constexpr (NG > 2) r += lut[2][(m >> 16) & 255u];
+        if constexpr (NG > 3) r += lut[3][(m >> 24) & 255u];
+        if constexpr (SELBIT) {
+            if (m & kSelBit) r += list_r(v);
         }
-        if (sel) {
-            const int s = d.tok2sel[v];
-            if (s >= 0) r += sel_lds ? rsel[s] : list_weight(d, s, al, be);
-        }
-        if (rc) {
+        if constexpr (LISTALL) r += list_r(v);
+        if constexpr (RANGES) {
             const int c = d.tok2cut[v];
             if (c >= 0) r += rc[c];
         }
@@ -245,19 +263,17 @@ __global__ __launch_bounds__(kQThreads) void marg_q(DevTable d, StepView sv,
     auto qval = [&](float x, float r) -> float {
         return (r > 0.f && x > 0.f) ? (float)((double)x * (double)r * factor) : 0.f;
     };
-    double hsum = 0.0;
     const bool negent = conf_mode == FA_CONF_NEGENT;
     if (!qrow && !negent) {
         // only the sampled token's marginal is needed
         if (tid == 0)
-            conf[pos] = tok >= 0 ? qval(prow[tok], weight_r(tok, nd ? d.tokmask[tok] : 0u))
+            conf[pos] = tok >= 0 ? qval(prow[tok], weight_r(tok, NG > 0 || SELBIT ? d.tokmask[tok] : 0u))
                                  : -INFINITY;
         return;
     }
-    auto emit = [&](int v, float o) {
-        if (v == tok && !negent) conf[pos] = o;
-        if (negent && o > 0.f) hsum += (double)o * log((double)o);
-    };
+    double hsum = 0.0;
+    float tokq = -INFINITY;
+    bool have_tok = false;
     if ((d.V & 3) == 0) {
         constexpr int U = 4;  // float4 groups in flight per thread
         const float4 *p4 = reinterpret_cast<const float4 *>(prow);
@@ -269,34 +285,44 @@ __global__ __launch_bounds__(kQThreads) void marg_q(DevTable d, StepView sv,
             uint4 mm[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int k = k0 + u * kQThreads;
-                x[u] = k < n4 ? p4[k] : make_float4(0.f, 0.f, 0.f, 0.f);
-                mm[u] = (nd && k < n4) ? m4[k] : make_uint4(0u, 0u, 0u, 0u);
+                const int k = min(k0 + u * kQThreads, n4 - 1);
+                x[u] = p4[k];
+                if constexpr (NG > 0 || SELBIT) mm[u] = m4[k];
+                else mm[u] = make_uint4(0u, 0u, 0u, 0u);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int k = k0 + u * kQThreads;
-                if (k >= n4) break;
-                const int v = 4 * k;
+                const int v = 4 * min(k, n4 - 1);  // in-bounds tokens for the lookups
                 float4 o;
                 o.x = qval(x[u].x, weight_r(v, mm[u].x));
                 o.y = qval(x[u].y, weight_r(v + 1, mm[u].y));
                 o.z = qval(x[u].z, weight_r(v + 2, mm[u].z));
                 o.w = qval(x[u].w, weight_r(v + 3, mm[u].w));
-                if (q4) q4[k] = o;
-                if (negent || (tok >= v && tok < v + 4)) {
-                    emit(v, o.x);
-                    emit(v + 1, o.y);
-                    emit(v + 2, o.z);
-                    emit(v + 3, o.w);
+                if (k < n4) {
+                    if (q4) q4[k] = o;
+                    if (tok >= v && tok < v + 4) {
+                        have_tok = true;
+                        tokq = tok == v ? o.x : tok == v + 1 ? o.y : tok == v + 2 ? o.z : o.w;
+                    }
+                    if (negent) {
+                        if (o.x > 0.f) hsum += (double)o.x * log((double)o.x);
+                        if (o.y > 0.f) hsum += (double)o.y * log((double)o.y);
+                        if (o.z > 0.f) hsum += (double)o.z * log((double)o.z);
+                        if (o.w > 0.f) hsum += (double)o.w * log((double)o.w);
+                    }
                 }
             }
         }
     } else {
         for (int v = tid; v < d.V; v += kQThreads) {
-            const float o = qval(prow[v], weight_r(v, nd ? d.tokmask[v] : 0u));
+            const float o = qval(prow[v], weight_r(v, NG > 0 || SELBIT ? d.tokmask[v] : 0u));
             if (qrow) qrow[v] = o;
-            emit(v, o);
+            if (v == tok) {
+                have_tok = true;
+                tokq = o;
+            }
+            if (negent && o > 0.f) hsum += (double)o * log((double)o);
         }
     }
     if (negent) {
@@ -304,8 +330,9 @@ __global__ __launch_bounds__(kQThreads) void marg_q(DevTable d, StepView sv,
         if (lane == 0) sh_h[wave] = hsum;
         __syncthreads();
         if (tid == 0) conf[pos] = (float)(((sh_h[0] + sh_h[1]) + sh_h[2]) + sh_h[3]);
-    } else if (tid == 0 && tok < 0) {
-        conf[pos] = -INFINITY;
+    } else {
+        if (have_tok) conf[pos] = tokq;
+        if (tid == 0 && tok < 0) conf[pos] = -INFINITY;
     }
 }
 
@@ -324,15 +351,24 @@ int launch_marginals(const DevTable &d, const Geometry &g, const float *p, const
     marg_init<<<g.B, 256, 0, st>>>(d, sv, va, ea, vb, eb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
+    const size_t lds = (size_t)g.Sp * (sizeof(float) + sizeof(int));
+    if (lds > 48 * 1024) {  // large automata: allow the dynamic LDS the kernels need
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&marg_level<256>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return (int)e;
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&marg_level<64>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return (int)e;
+    }
     for (int level = 1; level <= g.K; ++level) {
         const int nn = 1 << (level - 1);
         const int products = g.B * nn * 2;
         if (products * ((g.Sp + 255) / 256) >= 256) {
             dim3 grid((g.Sp + 255) / 256, products);
-            marg_level<256><<<grid, kMsgThreads, 0, st>>>(d, sv, tree, meta, nn, va, ea, vb, eb);
+            marg_level<256><<<grid, kMsgThreads, lds, st>>>(d, sv, tree, meta, nn, va, ea, vb, eb);
         } else {
             dim3 grid((g.Sp + 63) / 64, products);
-            marg_level<64><<<grid, kMsgThreads, 0, st>>>(d, sv, tree, meta, nn, va, ea, vb, eb);
+            marg_level<64><<<grid, kMsgThreads, lds, st>>>(d, sv, tree, meta, nn, va, ea, vb, eb);
         }
         e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
@@ -343,8 +379,33 @@ int launch_marginals(const DevTable &d, const Geometry &g, const float *p, const
         e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
     }
-    marg_q<<<dim3(g.L, g.B), kQThreads, 0, st>>>(d, sv, p, logZ, tokens, conf_mode, q,
-                                                           conf, va, ea, vb, eb, rcut, status);
+    const dim3 qgrid(g.L, g.B);
+    const int ng = (d.ndense + 7) / 8;
+    const bool listall = d.nsel > 0 && !d.selbit;
+    const bool ranges = d.ncut > 0;
+#define FA_MARG_Q(NG, SB, LA, RG)                                                              \
+    marg_q<NG, SB, LA, RG><<<qgrid, kQThreads, 0, st>>>(d, sv, p, logZ, tokens, conf_mode, q,  \
+                                                        conf, va, ea, vb, eb, rcut, status)
+    if (ranges) {
+        if (listall) FA_MARG_Q(0, false, true, true);
+        else FA_MARG_Q(0, false, false, true);
+    } else if (ng == 0) {
+        if (listall) FA_MARG_Q(0, false, true, false);
+        else FA_MARG_Q(0, false, false, false);
+    } else if (d.selbit) {
+        if (ng == 1) FA_MARG_Q(1, true, false, false);
+        else if (ng == 2) FA_MARG_Q(2, true, false, false);
+        else if (ng == 3) FA_MARG_Q(3, true, false, false);
+        else FA_MARG_Q(4, true, false, false);
+    } else if (listall) {  // 32 dense pairs leave no flag bit for token-list tokens
+        FA_MARG_Q(4, false, true, false);
+    } else {
+        if (ng == 1) FA_MARG_Q(1, false, false, false);
+        else if (ng == 2) FA_MARG_Q(2, false, false, false);
+        else if (ng == 3) FA_MARG_Q(3, false, false, false);
+        else FA_MARG_Q(4, false, false, false);
+    }
+#undef FA_MARG_Q
     return (int)hipGetLastError();
 }
 

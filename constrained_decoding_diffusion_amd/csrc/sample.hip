@@ -51,6 +51,34 @@ __device__ inline float mant(float x)
     return frexpf(x, &e);
 }
 
+// the same inverse CDF over weights held in registers: candidate
+// 64*c + lane is w[c]
+template <int C>
+__device__ int wave_icdf_regs(const float (&w)[C], int n, float u, int lane)
+{
+    double carry = 0.0;
+    double incl[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const double s = wave_incl_scan_d((double)w[c], lane);
+        incl[c] = carry + s;
+        carry += __shfl(s, 63);
+    }
+    const double T = carry;
+    if (!(T > 0.0)) return -1;
+    const double target = (double)u * T;
+    int last = -1;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const bool pos = 64 * c + lane < n && w[c] > 0.f;
+        const uint64_t hit = __ballot(pos && incl[c] > target);
+        if (hit) return 64 * c + __ffsll((unsigned long long)hit) - 1;
+        const uint64_t any = __ballot(pos);
+        if (any) last = 64 * c + 63 - __clzll((unsigned long long)any);
+    }
+    return last;
+}
+
 // root: z_Lpad over the accepting states
 __global__ void sample_root(DevTable d, StepView sv, const float *__restrict__ tree,
                             const int32_t *__restrict__ meta, uint64_t seed,
@@ -104,20 +132,48 @@ __global__ __launch_bounds__(256) void sample_level(DevTable d, StepView sv,
         const float *PR = sv.mat_ptr(tree, b, 2 * n + 1) + (size_t)zr * sv.Sp;
         const int32_t *coL = sv.meta_ptr(meta, b, 2 * n, 1);
         const int32_t *coR = sv.meta_ptr(meta, b, 2 * n + 1, 1);
-        auto expo = [&](int k) {
-            const float a = PL[k], c = PR[k];
-            if (!(a > 0.f) || !(c > 0.f) || coL[k] <= kNeg || coR[k] <= kNeg) return kNeg;
-            return fexp(a) + coL[k] + fexp(c) + coR[k];
+        auto expo2 = [&](float a, float c, int cl, int cr) {
+            if (!(a > 0.f) || !(c > 0.f) || cl <= kNeg || cr <= kNeg) return kNeg;
+            return fexp(a) + cl + fexp(c) + cr;
         };
-        int e = kNeg;
-        for (int k = lane; k < d.S; k += 64) e = max(e, expo(k));
-        const int emax = wave_max_i(e);
-        if (emax > kNeg) {
-            const float u = philox_u01(seed, (uint32_t)b, (uint32_t)level, (uint32_t)idx);
-            j = wave_icdf(d.S, u, lane, [&](int k) {
-                const int ek = expo(k);
-                return ek > kNeg ? scale2(mant(PL[k]) * mant(PR[k]), ek - emax) : 0.f;
-            });
+        const float u = philox_u01(seed, (uint32_t)b, (uint32_t)level, (uint32_t)idx);
+        constexpr int C = 8;
+        if (d.S <= 64 * C) {
+            // every candidate's data in registers: one round of loads
+            float pa[C], pb[C];
+            int ek[C];
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                const int k = 64 * c + lane;
+                const bool ok = k < d.S;
+                pa[c] = ok ? PL[k] : 0.f;
+                pb[c] = ok ? PR[k] : 0.f;
+                ek[c] = ok ? coL[k] : kNeg;
+                const int cr = ok ? coR[k] : kNeg;
+                ek[c] = expo2(pa[c], pb[c], ek[c], cr);
+            }
+            int e = kNeg;
+#pragma unroll
+            for (int c = 0; c < C; ++c) e = max(e, ek[c]);
+            const int emax = wave_max_i(e);
+            if (emax > kNeg) {
+                float wv[C];
+#pragma unroll
+                for (int c = 0; c < C; ++c)
+                    wv[c] = ek[c] > kNeg ? scale2(mant(pa[c]) * mant(pb[c]), ek[c] - emax) : 0.f;
+                j = wave_icdf_regs(wv, d.S, u, lane);
+            }
+        } else {
+            auto expo = [&](int k) { return expo2(PL[k], PR[k], coL[k], coR[k]); };
+            int e = kNeg;
+            for (int k = lane; k < d.S; k += 64) e = max(e, expo(k));
+            const int emax = wave_max_i(e);
+            if (emax > kNeg) {
+                j = wave_icdf(d.S, u, lane, [&](int k) {
+                    const int ek = expo(k);
+                    return ek > kNeg ? scale2(mant(PL[k]) * mant(PR[k]), ek - emax) : 0.f;
+                });
+            }
         }
         if (j < 0 && lane == 0) atomicOr(&status[b], (int)FA_ROW_UNDERFLOW);
     }

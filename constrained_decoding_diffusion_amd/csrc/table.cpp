@@ -134,6 +134,21 @@ bool make_geometry(const HostTable &t, int32_t B, int32_t L, Geometry *g)
     return true;
 }
 
+int tree_ksplit(const Geometry &g, int level)
+{
+    // large levels run on the 128x128 kernel; smaller ones on 64x64 tiles,
+    // split along K (chunks of 64) only when the tiles alone would leave most
+    // of the 256 compute units idle
+    const long long nn = g.Lpad >> level;
+    const long long big = (long long)g.B * nn * (g.Sp / 128) * (g.Sp / 128);
+    if (g.Sp % 128 == 0 && big >= 512) return 1;
+    const long long small = (long long)g.B * nn * (g.Sp / 64) * (g.Sp / 64);
+    int s = 1;
+    // the split must divide the K blocks of 64 exactly
+    while ((g.Sp / 64) % (s * 2) == 0 && small * s * 2 <= 512) s *= 2;
+    return s;
+}
+
 WsLayout ws_layout(const HostTable &t, const Geometry &g)
 {
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
@@ -151,6 +166,14 @@ WsLayout ws_layout(const HostTable &t, const Geometry &g)
     o = 0;  // sampler region
     w.zc = o; o = al(o + (size_t)g.B * (g.Lpad + 1) * sizeof(int32_t));
     size_t a3 = o;
+    o = 0;  // span tree region
+    size_t kp = 0;
+    for (int level = 1; level <= g.K; ++level) {
+        const int s = tree_ksplit(g, level);
+        if (s > 1) kp = std::max(kp, (size_t)g.B * (g.Lpad >> level) * s * g.mat);
+    }
+    w.kpart = o; o = al(o + kp * sizeof(float));
+    size_t a2 = o;
     o = 0;  // marginals region
     size_t nv = (size_t)g.B * (g.Lpad + 1);
     w.va = o; o = al(o + nv * g.Sp * sizeof(float));
@@ -159,7 +182,7 @@ WsLayout ws_layout(const HostTable &t, const Geometry &g)
     w.eb = o; o = al(o + nv * sizeof(int32_t));
     w.rcut = o; o = al(o + BL * t.ncut() * sizeof(float));
     size_t a4 = o;
-    w.total = std::max(a1, std::max(a3, a4));
+    w.total = std::max(std::max(a1, a2), std::max(a3, a4));
     if (w.total == 0) w.total = 256;
     return w;
 }

@@ -59,14 +59,20 @@ __device__ inline float4 fold4(float4 x, int4 c, int rfrow)
     return x;
 }
 
-// One 64x64 output tile of D = X Y^T for node n of row b.
+// One 64x64 output tile of D = X Y^T for node n of row b, over the K range
+// of split blockIdx.x / tiles^2.  With one split the tile is final; with
+// several it is a partial sum written to `part` and added by span_reduce.
 __global__ __launch_bounds__(kGemmThreads) void span_gemm(StepView sv, float *__restrict__ tree,
                                                           int32_t *__restrict__ meta, int n0,
-                                                          int nn)
+                                                          int nn, int ksplit,
+                                                          float *__restrict__ part)
 {
     const int Sp = sv.Sp;
     const int tiles = Sp / kTile;
-    const int tm = (blockIdx.x / tiles) * kTile, tn = (blockIdx.x % tiles) * kTile;
+    const int T2 = tiles * tiles;
+    const int tile = blockIdx.x % T2, split = blockIdx.x / T2;
+    const int tm = (tile / tiles) * kTile, tn = (tile % tiles) * kTile;
+    const int kc = Sp / ksplit, k_begin = split * kc, k_end = k_begin + kc;
     const int b = blockIdx.y / nn, n = n0 + blockIdx.y % nn;
     const bool tr = stored_transposed(n);
     const int hF = tr ? 2 * n + 1 : 2 * n, hG = tr ? 2 * n : 2 * n + 1;
@@ -98,9 +104,9 @@ __global__ __launch_bounds__(kGemmThreads) void span_gemm(StepView sv, float *__
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 
     float4 f0, f1, g0, g1;
-    load8(Frow + lk, f0, f1);
-    load8(Grow + lk, g0, g1);
-    for (int k0 = 0; k0 < Sp; k0 += kBK) {
+    load8(Frow + k_begin + lk, f0, f1);
+    load8(Grow + k_begin + lk, g0, g1);
+    for (int k0 = k_begin; k0 < k_end; k0 += kBK) {
         const int4 cf0 = *reinterpret_cast<const int4 *>(coF + k0 + lk);
         const int4 cf1 = *reinterpret_cast<const int4 *>(coF + k0 + lk + 4);
         const int4 cg0 = *reinterpret_cast<const int4 *>(coG + k0 + lk);
@@ -111,7 +117,7 @@ __global__ __launch_bounds__(kGemmThreads) void span_gemm(StepView sv, float *__
         *reinterpret_cast<float4 *>(&Gs[lrow][lk]) = fold4(g0, cg0, rfGrow);
         *reinterpret_cast<float4 *>(&Gs[lrow][lk + 4]) = fold4(g1, cg1, rfGrow);
         __syncthreads();
-        if (k0 + kBK < Sp) {
+        if (k0 + kBK < k_end) {
             load8(Frow + k0 + kBK + lk, f0, f1);
             load8(Grow + k0 + kBK + lk, g0, g1);
         }
@@ -124,6 +130,15 @@ __global__ __launch_bounds__(kGemmThreads) void span_gemm(StepView sv, float *__
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, c.z, acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, c.w, acc, 0, 0, 0);
         }
+    }
+    if (ksplit > 1) {  // partial tile, row-major 64x64
+        float *pt = part + ((size_t)(blockIdx.y * ksplit + split) * T2 + tile) * (kTile * kTile);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int i = wr + (r >> 2) * 8 + half * 4 + (r & 3);
+            pt[i * kTile + wc + l32] = acc[r];
+        }
+        return;
     }
     // epilogue: store, row fold normalizer, outer scales
     const int j = tn + wc + l32;
@@ -138,8 +153,68 @@ __global__ __launch_bounds__(kGemmThreads) void span_gemm(StepView sv, float *__
         for (int o = 16; o > 0; o >>= 1) e = max(e, __shfl_xor(e, o));
         if (l32 == 0 && e > kNeg) atomicMax(&rfD[i], e);
     }
-    if (blockIdx.x % tiles == 0 && tid < kTile) roD[tm + tid] = add_exp(roF[tm + tid], rfF[tm + tid]);
-    if (blockIdx.x / tiles == 0 && tid < kTile) coD[tn + tid] = add_exp(roG[tn + tid], rfG[tn + tid]);
+    if (tn == 0 && tid < kTile) roD[tm + tid] = add_exp(roF[tm + tid], rfF[tm + tid]);
+    if (tm == 0 && tid < kTile) coD[tn + tid] = add_exp(roG[tn + tid], rfG[tn + tid]);
+}
+
+// add the K-split partial tiles in split order and finish the tile as the
+// single-split epilogue does
+__global__ __launch_bounds__(kGemmThreads) void span_reduce(StepView sv, float *__restrict__ tree,
+                                                            int32_t *__restrict__ meta, int n0,
+                                                            int nn, int ksplit,
+                                                            const float *__restrict__ part)
+{
+    const int Sp = sv.Sp;
+    const int tiles = Sp / kTile;
+    const int T2 = tiles * tiles;
+    const int tile = blockIdx.x;
+    const int tm = (tile / tiles) * kTile, tn = (tile % tiles) * kTile;
+    const int b = blockIdx.y / nn, n = n0 + blockIdx.y % nn;
+    const bool tr = stored_transposed(n);
+    const int hF = tr ? 2 * n + 1 : 2 * n, hG = tr ? 2 * n : 2 * n + 1;
+    const int32_t *roF = sv.meta_ptr((const int32_t *)meta, b, hF, 0);
+    const int32_t *rfF = sv.meta_ptr((const int32_t *)meta, b, hF, 2);
+    const int32_t *roG = sv.meta_ptr((const int32_t *)meta, b, hG, 0);
+    const int32_t *rfG = sv.meta_ptr((const int32_t *)meta, b, hG, 2);
+    float *D = sv.mat_ptr(tree, b, n);
+    int32_t *roD = sv.meta_ptr(meta, b, n, 0);
+    int32_t *coD = sv.meta_ptr(meta, b, n, 1);
+    int32_t *rfD = sv.meta_ptr(meta, b, n, 2);
+    const int tid = threadIdx.x;
+    const int i = tid >> 2, c0 = (tid & 3) * 16;  // row i, 16 columns
+    float4 acc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < ksplit; ++s) {
+        const float *pt = part + ((size_t)(blockIdx.y * ksplit + s) * T2 + tile) * (kTile * kTile) +
+                          i * kTile + c0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 y = *reinterpret_cast<const float4 *>(pt + 4 * q);
+            acc[q].x += y.x;
+            acc[q].y += y.y;
+            acc[q].z += y.z;
+            acc[q].w += y.w;
+        }
+    }
+    int e = kNeg;
+    float *drow = D + (size_t)(tm + i) * Sp + tn + c0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        *reinterpret_cast<float4 *>(drow + 4 * q) = acc[q];
+        const float v4[4] = {acc[q].x, acc[q].y, acc[q].z, acc[q].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = tn + c0 + 4 * q + u;
+            const int coDj = add_exp(roG[j], rfG[j]);
+            if (v4[u] > 0.f && coDj > kNeg) e = max(e, fexp(v4[u]) + coDj);
+        }
+    }
+    e = max(e, __shfl_xor(e, 1));
+    e = max(e, __shfl_xor(e, 2));
+    if ((tid & 3) == 0 && e > kNeg) atomicMax(&rfD[tm + i], e);
+    if (tn == 0 && tid < kTile) roD[tm + tid] = add_exp(roF[tm + tid], rfF[tm + tid]);
+    if (tm == 0 && tid < kTile) coD[tn + tid] = add_exp(roG[tn + tid], rfG[tn + tid]);
 }
 
 constexpr int kBig = 128;       // output tile of the large-level kernel
@@ -184,11 +259,14 @@ __global__ __launch_bounds__(kBigThreads) void span_gemm128(StepView sv, float *
     __shared__ __align__(16) float Fs[2][kBig][kLdk2];
     __shared__ __align__(16) float Gs[2][kBig][kLdk2];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // loader: thread t stages row t>>2, k-quarter (t&3)*8 of both operands
-    const int lrow = tid >> 2, lk = (tid & 3) * 8;
-    const int rfFrow = rfF[tm + lrow], rfGrow = rfG[tn + lrow];
+    // loader: thread t stages float4 (t & 7) of rows t>>3 and 64 + (t>>3) of
+    // both operands, so eight lanes read one full 128-byte row segment
+    const int lrow = tid >> 3, lk = (tid & 7) * 4;
+    const int rfF0 = rfF[tm + lrow], rfF1 = rfF[tm + 64 + lrow];
+    const int rfG0 = rfG[tn + lrow], rfG1 = rfG[tn + 64 + lrow];
     const float *Frow = F + (size_t)(tm + lrow) * Sp + lk;
     const float *Grow = G + (size_t)(tn + lrow) * Sp + lk;
+    const size_t half_rows = (size_t)64 * Sp;
     const int wr = (wave >> 1) * 32, wc = (wave & 1) * 64;
     const int l32 = lane & 31, half = lane >> 5;
 
@@ -199,22 +277,20 @@ __global__ __launch_bounds__(kBigThreads) void span_gemm128(StepView sv, float *
         for (int r = 0; r < 16; ++r) acc[y][r] = 0.f;
 
     float4 fr[2], gr[2];
-    int4 cf[2], cg[2];
+    int4 cf, cg;
     auto gload = [&](int k0) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            fr[q] = *reinterpret_cast<const float4 *>(Frow + k0 + 4 * q);
-            gr[q] = *reinterpret_cast<const float4 *>(Grow + k0 + 4 * q);
-            cf[q] = *reinterpret_cast<const int4 *>(coF + k0 + lk + 4 * q);
-            cg[q] = *reinterpret_cast<const int4 *>(coG + k0 + lk + 4 * q);
-        }
+        fr[0] = *reinterpret_cast<const float4 *>(Frow + k0);
+        fr[1] = *reinterpret_cast<const float4 *>(Frow + half_rows + k0);
+        gr[0] = *reinterpret_cast<const float4 *>(Grow + k0);
+        gr[1] = *reinterpret_cast<const float4 *>(Grow + half_rows + k0);
+        cf = *reinterpret_cast<const int4 *>(coF + k0 + lk);
+        cg = *reinterpret_cast<const int4 *>(coG + k0 + lk);
     };
     auto lstore = [&](int buf) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            *reinterpret_cast<float4 *>(&Fs[buf][lrow][lk + 4 * q]) = fold4(fr[q], cf[q], rfFrow);
-            *reinterpret_cast<float4 *>(&Gs[buf][lrow][lk + 4 * q]) = fold4(gr[q], cg[q], rfGrow);
-        }
+        *reinterpret_cast<float4 *>(&Fs[buf][lrow][lk]) = fold4(fr[0], cf, rfF0);
+        *reinterpret_cast<float4 *>(&Fs[buf][64 + lrow][lk]) = fold4(fr[1], cf, rfF1);
+        *reinterpret_cast<float4 *>(&Gs[buf][lrow][lk]) = fold4(gr[0], cg, rfG0);
+        *reinterpret_cast<float4 *>(&Gs[buf][64 + lrow][lk]) = fold4(gr[1], cg, rfG1);
     };
     const int nk = Sp / kBK2;
     gload(0);
@@ -310,7 +386,7 @@ __global__ void tree_logz_empty(DevTable d, int B, double *__restrict__ logZ,
 }  // namespace
 
 int launch_span_tree(const DevTable &d, const Geometry &g, float *tree, int32_t *meta,
-                     double *logZ, int32_t *status, void *stream)
+                     uint8_t *ws, const WsLayout &w, double *logZ, int32_t *status, void *stream)
 {
     hipStream_t st = (hipStream_t)stream;
     if (g.L == 0) {
@@ -330,11 +406,19 @@ int launch_span_tree(const DevTable &d, const Geometry &g, float *tree, int32_t 
         const int n0 = g.Lpad >> k, nn = n0;
         const int big_tiles = g.Sp / kBig;
         const long long big_wgs = (long long)g.B * nn * big_tiles * big_tiles;
-        if (g.Sp % kBig == 0 && big_wgs >= 512) {
+        const int ks = tree_ksplit(g, k);
+        if (ks == 1 && g.Sp % kBig == 0 && big_wgs >= 512) {
             span_gemm128<<<(unsigned)big_wgs, kBigThreads, 0, st>>>(sv, tree, meta, n0, nn);
         } else {
-            dim3 grid(tiles * tiles, g.B * nn);
-            span_gemm<<<grid, kGemmThreads, 0, st>>>(sv, tree, meta, n0, nn);
+            float *part = (float *)(ws + w.kpart);
+            dim3 grid(tiles * tiles * ks, g.B * nn);
+            span_gemm<<<grid, kGemmThreads, 0, st>>>(sv, tree, meta, n0, nn, ks, part);
+            if (ks > 1) {
+                hipError_t e = hipGetLastError();
+                if (e != hipSuccess) return (int)e;
+                dim3 rgrid(tiles * tiles, g.B * nn);
+                span_reduce<<<rgrid, kGemmThreads, 0, st>>>(sv, tree, meta, n0, nn, ks, part);
+            }
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return (int)e;

@@ -175,12 +175,16 @@ int fa_build_transitions(const fa_table *t, const float *p, int32_t B, int32_t L
  * transitions from 2^(k-1)-step ones in log L rounds of batched matrix
  * multiplication); papernotes 关键设计 2.
  *   tree, meta  written by fa_build_transitions; internal nodes written
+ *   ws          device workspace of ws_bytes >= fa_sizes (partial products
+ *               of the upper levels, whose few large products are split
+ *               along K)
  *   logZ        device double [B]; -inf for infeasible rows
  *   row_status  device int32 [B]; FA_ROW_INFEASIBLE when Z = 0
  * Errors: FA_EINVAL, FA_ESTATE, FA_EHIP.
  */
 int fa_span_tree(const fa_table *t, int32_t B, int32_t L, float *tree, int32_t *meta,
-                 double *logZ, int32_t *row_status, fa_stream_t stream);
+                 void *ws, size_t ws_bytes, double *logZ, int32_t *row_status,
+                 fa_stream_t stream);
 
 /*
  * fa_sample - top-down exact sampling: z_Lpad ~ P_1[s0][f] over f in F (the

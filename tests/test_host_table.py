@@ -140,5 +140,5 @@ def test_step_calls_need_an_uploaded_table():
     t = fa.Table.from_automaton(A.real_number_dfa())
     rc = _fa.lib().fa_build_transitions(t.handle, None, 1, 6, None, None, None, 0, None, None)
     assert rc == _fa.FA_ESTATE
-    rc = _fa.lib().fa_span_tree(None, 1, 6, None, None, None, None, None)
+    rc = _fa.lib().fa_span_tree(None, 1, 6, None, None, None, 0, None, None, None)
     assert rc == _fa.FA_EINVAL
