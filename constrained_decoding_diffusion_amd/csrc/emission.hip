@@ -7,8 +7,9 @@
 //  * emission_dense: pairs whose labels are large token sets (dense masks).
 //    Their sums form a contraction  D[j][pos] = sum_v mask[j][v] p[pos][v]
 //    with a 0/1 operand; it runs on fp32 MFMA (32 pairs x 32 positions per
-//    tile, K = tokens), V split over workgroups into fixed chunks whose
-//    partials are summed in chunk order.  The same pass copies p at the
+//    tile, K = tokens), V split over workgroups into chunks (sized so the
+//    workgroups fill whole rounds of the chip) whose partials are summed in
+//    chunk order.  The same pass copies p at the
 //    tokens that token-list pairs use (a compact gather source).
 //  * emission_ranges: one workgroup per position streams the row and keeps
 //    an fp64 running prefix sum at every range cut point.
@@ -27,28 +28,36 @@ constexpr int kDenseThreads = 256;
 constexpr int kSub = 256;         // tokens staged per step
 constexpr int kSubLd = kSub + 4;  // padded LDS row
 
+// One workgroup: 32 positions x one V chunk (a multiple of 256 tokens).
+// Tokens are staged 256 at a time through double-buffered LDS; each of the
+// four waves runs the MFMAs of 64 tokens per step into its own 32x32 tile,
+// and the four tiles are summed at the end.  Every global load of the loop
+// is unconditional (out-of-range elements read an in-range address and are
+// zeroed when stored to LDS), so the loop has a fixed number of memory
+// operations per step and the loads of step s+2 stay in flight while step s
+// computes.
+//
+// SEL selects how the tokens of token-list pairs are copied to psel:
+//   0: no copy; 1: from the staged LDS tiles into an LDS buffer, written out
+//   after the loop (at most kDenseSelLds such tokens per chunk); 2: gathered from
+//   p after the loop.
+template <bool VEC, int SEL>
 __global__ __launch_bounds__(kDenseThreads) void emission_dense(
-    DevTable d, const float *__restrict__ p, int L, int npos, int BLpad,
+    DevTable d, const float *__restrict__ p, int L, int npos, int BLpad, int vchunk,
     float *__restrict__ dpart, float *__restrict__ psel, int32_t *__restrict__ status)
 {
-    constexpr int kSteps = kDenseChunk / kSub;
     __shared__ __align__(16) float pt[2][kDenseTile][kSubLd];
     __shared__ __align__(16) uint32_t mk[2][kSub];
-    __shared__ int sel_at[kSteps + 1];  // first token-list index at or after each step
+    __shared__ int sel_at[kDenseStepsMax + 1];  // first token-list index at or after each step
+    __shared__ uint16_t sel_off[SEL == 1 ? kDenseSelLds : 1];
+    __shared__ float selv[SEL == 1 ? kDenseTile : 1][SEL == 1 ? kDenseSelLds : 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int chunk = blockIdx.x;
     const int pos0 = blockIdx.y * kDenseTile;
-    const int v_begin = chunk * kDenseChunk;
-    const int v_end = min(d.V, v_begin + kDenseChunk);
+    const int v_begin = chunk * vchunk;
+    const int v_end = min(d.V, v_begin + vchunk);
     const int nsteps = (v_end - v_begin + kSub - 1) / kSub;
-    const bool vec = (d.V & 3) == 0;
-    // staging map: load k of thread t is float4 number 256k + t of the
-    // 32 x 256 tile, so each wavefront reads one contiguous 1 KB row segment
-    // (row 4k + wave, column 4*lane); threads 0..63 also load the mask words
-    // of four tokens each
-    const int scol = 4 * lane;
-    int bad = 0;
-    if (psel && tid <= kSteps) {
+    if (SEL != 0 && tid <= nsteps) {
         const int vs = v_begin + tid * kSub;
         int lo = 0, hi = d.nsel;
         while (lo < hi) {
@@ -58,59 +67,73 @@ __global__ __launch_bounds__(kDenseThreads) void emission_dense(
         }
         sel_at[tid] = lo;
     }
+    if (SEL == 1) {
+        __syncthreads();
+        const int s0 = sel_at[0], nc = sel_at[nsteps] - s0;  // nc <= kDenseSelLds (host check)
+        if (tid < nc) sel_off[tid] = (uint16_t)(d.sel_tok[s0 + tid] - v_begin);
+    }
+    // staging map: load k of thread t is float4 number 256k + t of the
+    // 32 x 256 tile, i.e. row 4k + wave, column 4*lane, so each wavefront
+    // reads one contiguous 1 KB row segment; rows past npos read row npos-1
+    const int scol = 4 * lane;
+    const float *prow[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        prow[k] = p + (size_t)min(pos0 + 4 * k + wave, npos - 1) * d.V;
+    int bad = 0;
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
     struct Step {
         float4 x[8];
-        uint4 m;
+        uint32_t m;
     };
     Step sa, sb;
     auto load = [&](Step &st, int v0) {
+        const int v = v0 + scol;
+        if (VEC) {
+            // V % 4 == 0: v and v_end are multiples of 4
+            const int vc = v < v_end ? v : v_end - 4;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int row = 4 * k + wave;
-            const bool row_ok = pos0 + row < npos;
-            const float *prow = p + (size_t)(pos0 + row) * d.V;
-            const int v = v0 + scol;
-            if (row_ok && vec && v + 3 < v_end) {
-                st.x[k] = *reinterpret_cast<const float4 *>(prow + v);
-            } else {
-                st.x[k].x = (row_ok && v < v_end) ? prow[v] : 0.f;
-                st.x[k].y = (row_ok && v + 1 < v_end) ? prow[v + 1] : 0.f;
-                st.x[k].z = (row_ok && v + 2 < v_end) ? prow[v + 2] : 0.f;
-                st.x[k].w = (row_ok && v + 3 < v_end) ? prow[v + 3] : 0.f;
+            for (int k = 0; k < 8; ++k) st.x[k] = *reinterpret_cast<const float4 *>(prow[k] + vc);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                st.x[k].x = prow[k][min(v, v_end - 1)];
+                st.x[k].y = prow[k][min(v + 1, v_end - 1)];
+                st.x[k].z = prow[k][min(v + 2, v_end - 1)];
+                st.x[k].w = prow[k][min(v + 3, v_end - 1)];
             }
         }
-        if (tid < kSub / 4) {
-            const int v = v0 + 4 * tid;
-            if (vec && v + 3 < v_end) {
-                st.m = *reinterpret_cast<const uint4 *>(d.tokmask + v);
-            } else {
-                st.m.x = v < v_end ? d.tokmask[v] : 0u;
-                st.m.y = v + 1 < v_end ? d.tokmask[v + 1] : 0u;
-                st.m.z = v + 2 < v_end ? d.tokmask[v + 2] : 0u;
-                st.m.w = v + 3 < v_end ? d.tokmask[v + 3] : 0u;
-            }
-        }
+        st.m = d.tokmask[min(v0 + tid, v_end - 1)];
     };
-    auto store = [&](const Step &st, int buf) {
+    auto store = [&](const Step &st, int v0, int buf) {
+        const int v = v0 + scol;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const int row = 4 * k + wave;
-            const bool b = !(st.x[k].x >= 0.f) | !(st.x[k].y >= 0.f) | !(st.x[k].z >= 0.f) |
-                           !(st.x[k].w >= 0.f);
-            if (b) bad |= 1 << k;  // remember which staged rows saw a bad value
-            *reinterpret_cast<float4 *>(&pt[buf][row][scol]) = st.x[k];
+            const bool rok = pos0 + 4 * k + wave < npos;
+            float4 x;
+            x.x = (rok && v < v_end) ? st.x[k].x : 0.f;
+            x.y = (rok && v + 1 < v_end) ? st.x[k].y : 0.f;
+            x.z = (rok && v + 2 < v_end) ? st.x[k].z : 0.f;
+            x.w = (rok && v + 3 < v_end) ? st.x[k].w : 0.f;
+            const bool b = !(x.x >= 0.f) | !(x.y >= 0.f) | !(x.z >= 0.f) | !(x.w >= 0.f);
+            bad |= (int)b << k;  // which staged rows saw a negative or NaN value
+            *reinterpret_cast<float4 *>(&pt[buf][4 * k + wave][scol]) = x;
         }
-        if (tid < kSub / 4) *reinterpret_cast<uint4 *>(&mk[buf][4 * tid]) = st.m;
+        mk[buf][tid] = v0 + tid < v_end ? st.m : 0u;
     };
     const int half = lane >> 5, l32 = lane & 31;
-    // step s: MFMAs over LDS buffer s&1, copy of the token-list tokens, then
-    // stage s+1 (registers) to the other buffer and a new load into the
-    // freed registers; one barrier per step
+    // first token of stage s; stages past the chunk re-read its last stage
+    // (the values are zeroed when stored, since they lie past v_end)
+    auto vstage = [&](int s) { return v_begin + min(s, nsteps - 1) * kSub; };
+    // step s: MFMAs over LDS buffer s&1 (and the token-list copy), then
+    // stage s+1 from registers into the other buffer and issue the loads of
+    // stage s+3 into the freed registers; one barrier per step.  Loads and
+    // stores are unconditional so that every step issues the same memory
+    // operations (a conditional load makes the compiler wait for all
+    // outstanding loads at the next use of the registers).
     auto step = [&](int s, Step &next, int buf) {
-        const int v0 = v_begin + s * kSub;
         const float *brow = &pt[buf][l32][64 * wave + 32 * half];
         const uint32_t *mrow = &mk[buf][64 * wave + 32 * half];
 #pragma unroll
@@ -122,29 +145,27 @@ __global__ __launch_bounds__(kDenseThreads) void emission_dense(
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32((float)((mq.z >> l32) & 1u), bq.z, acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32((float)((mq.w >> l32) & 1u), bq.w, acc, 0, 0, 0);
         }
-        if (psel) {
-            const int idx = sel_at[s] + tid;
-            if (idx < sel_at[s + 1]) {
-                const int tk = d.sel_tok[idx];
-                for (int r = 0; r < kDenseTile && pos0 + r < npos; ++r)
-                    psel[(size_t)(pos0 + r) * d.nsel + idx] = pt[buf][r][tk - v0];
+        if (SEL == 1 && s < nsteps) {
+            const int j0 = sel_at[s] - sel_at[0], n = sel_at[s + 1] - sel_at[s];
+            for (int i = tid; i < n * kDenseTile; i += kDenseThreads) {
+                const int r = i & (kDenseTile - 1), j = j0 + (i >> 5);
+                selv[r][j] = pt[buf][r][sel_off[j] - s * kSub];
             }
         }
-        if (s + 1 < nsteps) {
-            store(next, buf ^ 1);
-            if (s + 3 < nsteps) load(next, v_begin + (s + 3) * kSub);
-        }
+        store(next, v_begin + (s + 1) * kSub, buf ^ 1);
+        load(next, vstage(s + 3));
         __syncthreads();
     };
-    load(sa, v_begin);
-    if (nsteps > 1) load(sb, v_begin + kSub);
-    store(sa, 0);
-    if (nsteps > 2) load(sa, v_begin + 2 * kSub);
+    load(sa, vstage(0));
+    load(sb, vstage(1));
+    store(sa, v_begin, 0);
+    load(sa, vstage(2));
     __syncthreads();
-    // stage s sits in sa (s even) or sb (s odd)
+    // stage s sits in sa (s even) or sb (s odd); an odd step count gets one
+    // all-zero step
     for (int s = 0; s < nsteps; s += 2) {
         step(s, sb, 0);
-        if (s + 1 < nsteps) step(s + 1, sa, 1);
+        step(s + 1, sa, 1);
     }
     // sum the four waves' tiles in wave order (reusing the staging LDS)
     float *red = &pt[0][0][0];
@@ -160,6 +181,18 @@ __global__ __launch_bounds__(kDenseThreads) void emission_dense(
         const int W = kDenseTile * kDenseTile;
         const float sum = ((red[k] + red[W + k]) + red[2 * W + k]) + red[3 * W + k];
         outp[(size_t)j * kDenseMax + i] = sum;
+    }
+    if (SEL != 0) {
+        const int s0 = sel_at[0], nc = sel_at[nsteps] - s0;
+        for (int i = tid; i < nc * kDenseTile; i += kDenseThreads) {
+            const int r = i / nc, j = i - r * nc;
+            if (pos0 + r < npos) {
+                float x;
+                if (SEL == 1) x = selv[r][j];
+                else x = p[(size_t)(pos0 + r) * d.V + d.sel_tok[s0 + j]];
+                psel[(size_t)(pos0 + r) * d.nsel + s0 + j] = x;
+            }
+        }
     }
     for (int k = 0; k < 8; ++k) {
         const int row = 4 * k + wave;
@@ -422,8 +455,22 @@ int launch_build_transitions(const DevTable &d, const Geometry &g, const float *
     src.dval = (float *)(ws + w.dval);
     if (d.ndense > 0) {
         dim3 grid(w.n_vchunks, BLpad / kDenseTile);
-        emission_dense<<<grid, kDenseThreads, 0, st>>>(d, p, g.L, npos, BLpad, (float *)src.dpart,
-                                                       (float *)src.psel, status);
+        const bool vec = (d.V & 3) == 0 && ((uintptr_t)p & 15) == 0;
+        const int sel = d.use_sel ? w.sel_mode : 0;
+#define FA_DENSE(VEC, SEL)                                                                      \
+    emission_dense<VEC, SEL><<<grid, kDenseThreads, 0, st>>>(d, p, g.L, npos, BLpad, w.vchunk, \
+                                                             (float *)src.dpart,                \
+                                                             (float *)src.psel, status)
+        if (vec) {
+            if (sel == 0) FA_DENSE(true, 0);
+            else if (sel == 1) FA_DENSE(true, 1);
+            else FA_DENSE(true, 2);
+        } else {
+            if (sel == 0) FA_DENSE(false, 0);
+            else if (sel == 1) FA_DENSE(false, 1);
+            else FA_DENSE(false, 2);
+        }
+#undef FA_DENSE
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
         const int n = npos * kDenseMax;

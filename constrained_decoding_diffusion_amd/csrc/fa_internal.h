@@ -14,7 +14,9 @@ namespace fa {
 constexpr int kSpAlign = 64;       // trimmed state count padded to this
 constexpr int kNeg = -(1 << 29);   // exponent of an all-zero row/column
 constexpr int kDenseMax = 32;      // dense-label pairs share one mask word per token
-constexpr int kDenseChunk = 4096;  // tokens per workgroup of the dense-mask contraction
+constexpr int kDenseStepsMax = 64;  // dense-mask contraction: 256-token steps per V chunk, at most
+constexpr int kDenseSlots = 512;    // workgroups of that contraction resident at once (256 CUs x 2)
+constexpr int kDenseSelLds = 64;    // token-list tokens per V chunk that its LDS buffer holds
 constexpr int kDenseTile = 32;     // positions per workgroup of the dense-mask contraction
 constexpr int kSelMax = 8192;      // LIST tokens gathered through a compact copy of p
 constexpr int kMapMaxSp = 2048;   // dense (row, column) -> pair maps up to this Sp
@@ -120,6 +122,8 @@ bool make_geometry(const HostTable &t, int32_t B, int32_t L, Geometry *g);
 struct WsLayout {
     size_t dpart = 0, dval = 0, psel = 0, cutp = 0, val = 0;  // emission reduce
     int32_t n_vchunks = 0;                     // dense-mask contraction: V split
+    int32_t vchunk = 0;                        // tokens per V chunk (multiple of 256)
+    int32_t sel_mode = 0;                      // token-list copy: 1 LDS-buffered, 2 gathered
     size_t zc = 0;                             // sampler: compact boundary states
     size_t kpart = 0;                          // span tree: split-K partial tiles
     size_t va = 0, ea = 0, vb = 0, eb = 0;     // marginals: messages

@@ -155,8 +155,37 @@ WsLayout ws_layout(const HostTable &t, const Geometry &g)
     WsLayout w;
     size_t BL = (size_t)g.B * g.L;
     size_t o = 0;  // emission reduce region
-    w.n_vchunks = t.ndense() ? (t.V + kDenseChunk - 1) / kDenseChunk : 0;
     size_t BLpad = (BL + kDenseTile - 1) / kDenseTile * kDenseTile;
+    if (t.ndense() && BL > 0) {
+        // V split of the dense-mask contraction: chunks of whole 256-token
+        // steps; the count minimises (rounds of kDenseSlots workgroups) x
+        // (steps per chunk + a fixed cost of two steps per workgroup)
+        const long long tiles = (long long)(BLpad / kDenseTile);
+        const long long steps = (t.V + 255) / 256;
+        double best = 1e300;
+        const long long nc_lo = (steps + kDenseStepsMax - 1) / kDenseStepsMax;
+        const long long nc_hi = std::max(nc_lo, std::min(steps, 64LL));
+        for (long long nc = nc_lo; nc <= nc_hi; ++nc) {
+            const long long st = (steps + nc - 1) / nc;
+            const long long n = (steps + st - 1) / st;
+            const long long rounds = (tiles * n + kDenseSlots - 1) / kDenseSlots;
+            const double cost = (double)rounds * (double)(st + 2);
+            if (cost < best) {
+                best = cost;
+                w.n_vchunks = (int32_t)n;
+                w.vchunk = (int32_t)(st * 256);
+            }
+        }
+        // token-list copy: LDS-buffered when every chunk holds few such tokens
+        int32_t most = 0;
+        for (int32_t c = 0; c < w.n_vchunks; ++c) {
+            const int32_t lo = c * w.vchunk, hi = std::min(t.V, lo + w.vchunk);
+            const int32_t n = (int32_t)(std::lower_bound(t.sel_tok.begin(), t.sel_tok.end(), hi) -
+                                        std::lower_bound(t.sel_tok.begin(), t.sel_tok.end(), lo));
+            most = std::max(most, n);
+        }
+        w.sel_mode = most <= kDenseSelLds ? 1 : 2;
+    }
     w.dpart = o; o = al(o + (size_t)w.n_vchunks * BLpad * kDenseMax * sizeof(float));
     w.dval = o; o = al(o + (t.ndense() ? BL * kDenseMax * sizeof(float) : 0));
     w.psel = o; o = al(o + (t.use_sel ? BL * t.nsel() * sizeof(float) : 0));
@@ -504,7 +533,9 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
             t.map_t[(size_t)t.pair_b[q] * t.Sp + t.pair_a[q]] = q;
         }
     }
-    t.use_sel = t.needs_stream() && ns > 0 && ns <= kSelMax;
+    // only tables with dense-mask pairs stream p through a kernel that can copy
+    // the token-list tokens (range tables hold no token lists)
+    t.use_sel = t.ndense() > 0 && ns > 0 && ns <= kSelMax;
     t.selbit = t.ndense() > 0 && t.ndense() < 32 && ns > 0;
     if (t.selbit)
         for (int32_t v : t.sel_tok) t.tokmask[v] |= kSelBit;
