@@ -73,6 +73,9 @@ struct DevTable {
     const int32_t *seg_pair;   // [nseg] pair of each segment
     const int32_t *map_n;      // [Sp][Sp] pair at (a, b) or -1 (Sp <= kMapMaxSp)
     const int32_t *map_t;      // [Sp][Sp] pair at (b, a) (transposed storage)
+    const int32_t *tm_a;       // [list entries] source state of each token-major entry
+    const int32_t *tm_b;       // [list entries] target state
+    int32_t n_tm;              // token-major LIST entries
 };
 
 // Host representation of a compiled automaton and its device image.
@@ -90,6 +93,7 @@ struct HostTable {
     std::vector<float> seg_cnt;
     std::vector<int32_t> tok2sel, tok2cut, seg_pair;
     std::vector<int32_t> map_n, map_t;
+    std::vector<int32_t> tm_a, tm_b;
     bool has_cnt = false;
     bool use_sel = false;
     bool selbit = false;
@@ -128,6 +132,8 @@ struct WsLayout {
     size_t kpart = 0;                          // span tree: split-K partial tiles
     size_t va = 0, ea = 0, vb = 0, eb = 0;     // marginals: messages
     size_t rcut = 0;                           // marginals: range weights per cut
+    size_t pw = 0;                             // marginals: per-position pair weights
+    int32_t pw_nl = 0, pw_ld = 0;              // token-list weights per row, row length
     size_t total = 0;
 };
 WsLayout ws_layout(const HostTable &t, const Geometry &g);

@@ -165,6 +165,7 @@ __global__ void marg_rcut(DevTable d, StepView sv, const float *__restrict__ va,
 }
 
 constexpr int kQThreads = 256;
+constexpr size_t kQLdsMax = 64 * 1024;  // LDS lookup tables of the streaming q writer
 
 // LIST weight of selected token s: sum over its token-major entries
 __device__ inline float list_weight(const DevTable &d, int s, const float *al, const float *be)
@@ -336,6 +337,246 @@ __global__ __launch_bounds__(kQThreads) void marg_q(DevTable d, StepView sv,
     }
 }
 
+// Per-position pair weights alpha_i[a] beta_{i+1}[a'] that the q writer
+// looks up: pw[pos][j] for dense-mask pair j (0 past ndense), then
+// pw[pos][32 + s] = the summed weight of the token-list pairs holding
+// sel_tok[s].  One workgroup per position: the weights of all token-major
+// entries are formed in parallel into LDS (chunks of kPwChunk entries), then
+// each token's entries are summed in entry order.
+constexpr int kPwThreads = 512;
+constexpr int kPwUnroll = 4;
+constexpr int kPwChunk = 8192;
+
+__global__ __launch_bounds__(kPwThreads) void marg_pairw(DevTable d, StepView sv,
+                                                         const float *__restrict__ va,
+                                                         const float *__restrict__ vb, int nl,
+                                                         int ld, float *__restrict__ pw)
+{
+    extern __shared__ float wsh[];  // [min(n_tm, kPwChunk)] entry weights | [nl] sums
+    const int pos = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int b = pos / sv.L, i = pos % sv.L;
+    const float *al = va + ((size_t)b * (sv.Lpad + 1) + i) * sv.Sp;
+    const float *be = vb + ((size_t)b * (sv.Lpad + 1) + i + 1) * sv.Sp;
+    float *out = pw + (size_t)pos * ld;
+    if (tid < kDenseMax) {
+        float w = 0.f;
+        if (tid < d.ndense) {
+            const int qq = d.dense_pair[tid];
+            w = al[d.pair_a[qq]] * be[d.pair_b[qq]];
+        }
+        out[tid] = w;
+    }
+    if (nl == 0) return;
+    const int cap = min(d.n_tm, kPwChunk);
+    float *rs = wsh + cap;
+    for (int s = tid; s < nl; s += kPwThreads) rs[s] = 0.f;
+    for (int c0 = 0; c0 < d.n_tm; c0 += kPwChunk) {
+        const int c1 = min(d.n_tm, c0 + kPwChunk);
+        __syncthreads();
+        // kPwUnroll entries per thread in flight: index loads first (clamped,
+        // unconditional), then the message gathers
+        for (int k0 = c0; k0 < c1; k0 += kPwThreads * kPwUnroll) {
+            int ka[kPwUnroll], kb[kPwUnroll];
+            float kc[kPwUnroll];
+#pragma unroll
+            for (int u = 0; u < kPwUnroll; ++u) {
+                const int k = min(k0 + u * kPwThreads + tid, c1 - 1);
+                ka[u] = d.tm_a[k];
+                kb[u] = d.tm_b[k];
+                kc[u] = d.tm_cnt ? d.tm_cnt[k] : 1.f;
+            }
+#pragma unroll
+            for (int u = 0; u < kPwUnroll; ++u) {
+                const int k = k0 + u * kPwThreads + tid;
+                const float w = al[ka[u]] * be[kb[u]];
+                if (k < c1) wsh[k - c0] = d.tm_cnt ? w * kc[u] : w;
+            }
+        }
+        __syncthreads();
+        for (int s = tid; s < nl; s += kPwThreads) {
+            const int k0 = max(d.tm_off[s], c0), k1 = min(d.tm_off[s + 1], c1);
+            float r = rs[s];
+            for (int k = k0; k < k1; ++k) r += wsh[k - c0];
+            rs[s] = r;
+        }
+    }
+    for (int s = tid; s < nl; s += kPwThreads) out[kDenseMax + s] = rs[s];
+}
+
+// Streaming q writer (V % 4 == 0, lookup tables in LDS).  One workgroup per
+// position; each thread handles U float4 groups per iteration.  Every global
+// load of the loop is unconditional (clamped index) and issued one iteration
+// ahead, and the per-token weight reads LDS only: the dense-mask lookup
+// table, the token-list weights (found by binary search over the sorted
+// token-list tokens when the mask's flag bit marks the token, or through
+// tok2sel), and the range weights at each cut.
+template <int NG, bool SELBIT, bool LISTALL, bool RANGES>
+__global__ __launch_bounds__(kQThreads) void marg_q_stream(
+    DevTable d, StepView sv, const float *__restrict__ p, const double *__restrict__ logZ,
+    const int32_t *__restrict__ tokens, int conf_mode, float *__restrict__ q,
+    float *__restrict__ conf, const int32_t *__restrict__ ea, const int32_t *__restrict__ eb,
+    const float *__restrict__ pw, int pw_ld, const float *__restrict__ rcut,
+    const int32_t *__restrict__ status)
+{
+    constexpr bool LISTS = SELBIT || LISTALL;
+    constexpr bool MASK = NG > 0 || SELBIT;
+    extern __shared__ float dyn[];  // rsel [nsel] | selk [nsel] | rcl [ncut]
+    __shared__ float lut[NG > 0 ? NG : 1][256];
+    __shared__ double sh_h[4];
+    const int b = blockIdx.y, i = blockIdx.x;
+    const size_t pos = (size_t)b * sv.L + i;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float *prow = p + pos * d.V;
+    float *qrow = q ? q + pos * d.V : nullptr;
+    const double lz = logZ[b];
+    const int e1 = ea[(size_t)b * (sv.Lpad + 1) + i], e2 = eb[(size_t)b * (sv.Lpad + 1) + i + 1];
+    const bool ok = status[b] == 0 && lz > -INFINITY && e1 > kNeg && e2 > kNeg;
+    if (!ok) {
+        if (qrow)
+            for (int v = tid; v < d.V; v += kQThreads) qrow[v] = 0.f;
+        if (tid == 0) conf[pos] = -INFINITY;
+        return;
+    }
+    const double factor = exp2((double)e1 + (double)e2 - lz * 1.4426950408889634074);
+    const float *pwr = pw + pos * pw_ld;
+    float *rsel = dyn;
+    int *selk = reinterpret_cast<int *>(dyn + (LISTS ? d.nsel : 0));
+    float *rcl = dyn + (LISTS ? d.nsel : 0) + (SELBIT ? d.nsel : 0);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        float sm = 0.f;
+        for (int bit = 0; bit < 8; ++bit)
+            if ((tid >> bit) & 1) sm += pwr[8 * g + bit];
+        lut[g][tid] = sm;
+    }
+    if (LISTS)
+        for (int k = tid; k < d.nsel; k += kQThreads) {
+            rsel[k] = pwr[kDenseMax + k];
+            if (SELBIT) selk[k] = d.sel_tok[k];
+        }
+    if (RANGES)
+        for (int c = tid; c < d.ncut; c += kQThreads) rcl[c] = rcut[pos * d.ncut + c];
+    __syncthreads();
+    const int tok = tokens ? tokens[pos] : -1;
+    auto weight_r = [&](int v, uint32_t m, int sl, int c) -> float {
+        float r = 0.f;
+        if constexpr (NG > 0) r = lut[0][m & 255u];
+        if constexpr (NG > 1) r += lut[1][(m >> 8) & 255u];
+        if constexpr (NG > 2) r += lut[2][(m >> 16) & 255u];
+        if constexpr (NG > 3) r += lut[3][(m >> 24) & 255u];
+        if constexpr (SELBIT) {
+            if (m & kSelBit) {
+                int lo = 0, hi = d.nsel - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if (selk[mid] < v) lo = mid + 1;
+                    else hi = mid;
+                }
+                r += rsel[lo];
+            }
+        }
+        if constexpr (LISTALL) {
+            if (sl >= 0) r += rsel[sl];
+        }
+        if constexpr (RANGES) {
+            if (c >= 0) r += rcl[c];
+        }
+        return r;
+    };
+    auto qval = [&](float x, float r) -> float {
+        return (r > 0.f && x > 0.f) ? (float)((double)x * (double)r * factor) : 0.f;
+    };
+    const bool negent = conf_mode == FA_CONF_NEGENT;
+    if (!qrow && !negent) {
+        // only the sampled token's marginal is needed
+        if (tid == 0) {
+            float o = -INFINITY;
+            if (tok >= 0)
+                o = qval(prow[tok], weight_r(tok, MASK ? d.tokmask[tok] : 0u,
+                                             LISTALL ? d.tok2sel[tok] : -1,
+                                             RANGES ? d.tok2cut[tok] : -1));
+            conf[pos] = o;
+        }
+        return;
+    }
+    constexpr int U = 4;
+    constexpr int kPer = U * kQThreads;  // float4 groups per iteration
+    const float4 *p4 = reinterpret_cast<const float4 *>(prow);
+    const uint4 *m4 = reinterpret_cast<const uint4 *>(d.tokmask);
+    const int4 *s4 = reinterpret_cast<const int4 *>(d.tok2sel);
+    const int4 *c4 = reinterpret_cast<const int4 *>(d.tok2cut);
+    float4 *q4 = reinterpret_cast<float4 *>(qrow);
+    const int n4 = d.V >> 2;
+    const int iters = (n4 + kPer - 1) / kPer;
+    struct Buf {
+        float4 x[U];
+        uint4 m[U];
+        int4 sl[U];
+        int4 c[U];
+    };
+    auto load = [&](Buf &bf, int it) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = min(it * kPer + u * kQThreads + tid, n4 - 1);
+            bf.x[u] = p4[k];
+            if constexpr (MASK) bf.m[u] = m4[k];
+            if constexpr (LISTALL) bf.sl[u] = s4[k];
+            if constexpr (RANGES) bf.c[u] = c4[k];
+        }
+    };
+    double hsum = 0.0;
+    float tokq = -INFINITY;
+    bool have_tok = false;
+    auto compute = [&](const Buf &bf, int it) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = it * kPer + u * kQThreads + tid;
+            const int v = 4 * min(k, n4 - 1);
+            const uint4 m = MASK ? bf.m[u] : make_uint4(0u, 0u, 0u, 0u);
+            const int4 sl = LISTALL ? bf.sl[u] : make_int4(-1, -1, -1, -1);
+            const int4 c = RANGES ? bf.c[u] : make_int4(-1, -1, -1, -1);
+            float4 o;
+            o.x = qval(bf.x[u].x, weight_r(v, m.x, sl.x, c.x));
+            o.y = qval(bf.x[u].y, weight_r(v + 1, m.y, sl.y, c.y));
+            o.z = qval(bf.x[u].z, weight_r(v + 2, m.z, sl.z, c.z));
+            o.w = qval(bf.x[u].w, weight_r(v + 3, m.w, sl.w, c.w));
+            if (k < n4) {
+                if (q4) q4[k] = o;
+                if (tok >= v && tok < v + 4) {
+                    have_tok = true;
+                    tokq = tok == v ? o.x : tok == v + 1 ? o.y : tok == v + 2 ? o.z : o.w;
+                }
+                if (negent) {
+                    if (o.x > 0.f) hsum += (double)o.x * log((double)o.x);
+                    if (o.y > 0.f) hsum += (double)o.y * log((double)o.y);
+                    if (o.z > 0.f) hsum += (double)o.z * log((double)o.z);
+                    if (o.w > 0.f) hsum += (double)o.w * log((double)o.w);
+                }
+            }
+        }
+    };
+    Buf A, Bn;
+    load(A, 0);
+    // iteration it sits in A (even) or Bn (odd); loads past the row re-read
+    // its last group and an odd count gets one empty iteration
+    for (int it = 0; it < iters; it += 2) {
+        load(Bn, it + 1);
+        compute(A, it);
+        load(A, it + 2);
+        compute(Bn, it + 1);
+    }
+    if (negent) {
+        hsum = wave_sum_d(hsum);
+        if (lane == 0) sh_h[wave] = hsum;
+        __syncthreads();
+        if (tid == 0) conf[pos] = (float)(((sh_h[0] + sh_h[1]) + sh_h[2]) + sh_h[3]);
+    } else {
+        if (have_tok) conf[pos] = tokq;
+        if (tid == 0 && tok < 0) conf[pos] = -INFINITY;
+    }
+}
+
 }  // namespace
 
 int launch_marginals(const DevTable &d, const Geometry &g, const float *p, const float *tree,
@@ -383,6 +624,57 @@ int launch_marginals(const DevTable &d, const Geometry &g, const float *p, const
     const int ng = (d.ndense + 7) / 8;
     const bool listall = d.nsel > 0 && !d.selbit;
     const bool ranges = d.ncut > 0;
+    const bool lists = d.nsel > 0;
+    // streaming path: float4 rows and every lookup table in LDS
+    const size_t qlds = (lists ? (size_t)d.nsel * (d.selbit ? 8 : 4) : 0) +
+                        (ranges ? (size_t)d.ncut * 4 : 0);
+    const bool aligned = ((uintptr_t)p & 15) == 0 && ((uintptr_t)q & 15) == 0;
+    const bool streamed = (d.V & 3) == 0 && aligned && qlds <= kQLdsMax && (!lists || w.pw_nl == d.nsel);
+    if (streamed) {
+        const int npos = g.B * g.L;
+        float *pw = (float *)(ws + w.pw);
+        const size_t plds = w.pw_nl ? ((size_t)std::min(d.n_tm, kPwChunk) + w.pw_nl) * 4 : 0;
+        if (plds > 48 * 1024) {
+            e = hipFuncSetAttribute(reinterpret_cast<const void *>(&marg_pairw),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)plds);
+            if (e != hipSuccess) return (int)e;
+        }
+        marg_pairw<<<npos, kPwThreads, plds, st>>>(d, sv, va, vb, w.pw_nl, w.pw_ld, pw);
+        e = hipGetLastError();
+        if (e != hipSuccess) return (int)e;
+#define FA_MARG_QS(NG, SB, LA, RG)                                                                \
+    do {                                                                                          \
+        auto kern = &marg_q_stream<NG, SB, LA, RG>;                                               \
+        if (qlds > 48 * 1024) {                                                                   \
+            e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),                         \
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)qlds);       \
+            if (e != hipSuccess) return (int)e;                                                   \
+        }                                                                                         \
+        kern<<<qgrid, kQThreads, qlds, st>>>(d, sv, p, logZ, tokens, conf_mode, q, conf, ea, eb, \
+                                             pw, w.pw_ld, rcut, status);                          \
+    } while (0)
+        if (ranges) {
+            if (listall) FA_MARG_QS(0, false, true, true);
+            else FA_MARG_QS(0, false, false, true);
+        } else if (ng == 0) {
+            if (listall) FA_MARG_QS(0, false, true, false);
+            else FA_MARG_QS(0, false, false, false);
+        } else if (d.selbit) {
+            if (ng == 1) FA_MARG_QS(1, true, false, false);
+            else if (ng == 2) FA_MARG_QS(2, true, false, false);
+            else if (ng == 3) FA_MARG_QS(3, true, false, false);
+            else FA_MARG_QS(4, true, false, false);
+        } else if (listall) {
+            FA_MARG_QS(4, false, true, false);
+        } else {
+            if (ng == 1) FA_MARG_QS(1, false, false, false);
+            else if (ng == 2) FA_MARG_QS(2, false, false, false);
+            else if (ng == 3) FA_MARG_QS(3, false, false, false);
+            else FA_MARG_QS(4, false, false, false);
+        }
+#undef FA_MARG_QS
+        return (int)hipGetLastError();
+    }
 #define FA_MARG_Q(NG, SB, LA, RG)                                                              \
     marg_q<NG, SB, LA, RG><<<qgrid, kQThreads, 0, st>>>(d, sv, p, logZ, tokens, conf_mode, q,  \
                                                         conf, va, ea, vb, eb, rcut, status)

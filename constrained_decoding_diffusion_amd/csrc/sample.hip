@@ -274,12 +274,19 @@ __global__ __launch_bounds__(kTokThreads) void sample_tokens(
     }
     // chunk = kTokThreads runs of `per` consecutive candidates (at most 64
     // chunks for row-length candidate sets)
+    const bool vec = cd.cls == kDense && (d.V & 3) == 0 && ((uintptr_t)prow & 15) == 0;
+    // dense rows up to kTokChunksMax chunks of 4096 tokens stream through the
+    // coalesced pass 1 below
+    const bool streamed = vec && (long long)cd.n <= (long long)kTokChunksMax * 16 * kTokThreads;
     int per = 4;
-    while ((long long)per * kTokThreads * 64 < cd.n && per < 64) per *= 2;
-    while ((long long)per * kTokThreads * kTokChunksMax < cd.n) per *= 2;
+    if (streamed) {
+        per = 16;
+    } else {
+        while ((long long)per * kTokThreads * 64 < cd.n && per < 64) per *= 2;
+        while ((long long)per * kTokThreads * kTokChunksMax < cd.n) per *= 2;
+    }
     const int chunk = per * kTokThreads;
     const int nchunks = (cd.n + chunk - 1) / chunk;
-    const bool vec = cd.cls == kDense && (d.V & 3) == 0;
     auto run_sum = [&](int c0) -> double {
         const int k0 = c0 + tid * per;
         double s = 0.0;
@@ -300,9 +307,54 @@ __global__ __launch_bounds__(kTokThreads) void sample_tokens(
     };
     // per-chunk wavefront partials, combined in wavefront order after one
     // barrier
-    for (int ch = 0; ch < nchunks; ++ch) {
-        const double s = wave_sum_d(run_sum(ch * chunk));
-        if (lane == 0) wsum[ch][wave] = s;
+    if (streamed) {
+        // chunk ch = float4 groups [1024 ch, 1024 ch + 1024): thread t takes
+        // groups 1024 ch + 256 u + t (u < 4), so each load instruction reads
+        // 1 KB contiguous per wavefront; the loads of chunk ch+1 are issued
+        // (unconditionally, clamped) before chunk ch is summed
+        const float4 *p4 = reinterpret_cast<const float4 *>(prow);
+        const uint4 *m4 = reinterpret_cast<const uint4 *>(d.tokmask);
+        const int n4 = d.V >> 2;
+        struct Buf {
+            float4 x[4];
+            uint4 m[4];
+        };
+        auto load = [&](Buf &bf, int ch) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int k = min(ch * 1024 + u * kTokThreads + tid, n4 - 1);
+                bf.x[u] = p4[k];
+                bf.m[u] = m4[k];
+            }
+        };
+        auto chunk_sum = [&](const Buf &bf, int ch) -> double {
+            double s = 0.0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (ch * 1024 + u * kTokThreads + tid < n4) {
+                    s += (double)((bf.m[u].x & cd.dbit) ? bf.x[u].x : 0.f);
+                    s += (double)((bf.m[u].y & cd.dbit) ? bf.x[u].y : 0.f);
+                    s += (double)((bf.m[u].z & cd.dbit) ? bf.x[u].z : 0.f);
+                    s += (double)((bf.m[u].w & cd.dbit) ? bf.x[u].w : 0.f);
+                }
+            }
+            return s;
+        };
+        Buf A, Bn;
+        load(A, 0);
+        for (int ch = 0; ch < nchunks; ch += 2) {
+            load(Bn, ch + 1);
+            const double s0 = wave_sum_d(chunk_sum(A, ch));
+            if (lane == 0) wsum[ch][wave] = s0;
+            load(A, ch + 2);
+            const double s1 = wave_sum_d(chunk_sum(Bn, ch + 1));
+            if (lane == 0 && ch + 1 < nchunks) wsum[ch + 1][wave] = s1;
+        }
+    } else {
+        for (int ch = 0; ch < nchunks; ++ch) {
+            const double s = wave_sum_d(run_sum(ch * chunk));
+            if (lane == 0) wsum[ch][wave] = s;
+        }
     }
     __syncthreads();
     for (int ch = tid; ch < nchunks; ch += kTokThreads)

@@ -71,6 +71,8 @@ void build_image(HostTable &t)
     append_section(t.image, t.offs, t.seg_pair);
     append_section(t.image, t.offs, t.map_n);
     append_section(t.image, t.offs, t.map_t);
+    append_section(t.image, t.offs, t.tm_a);
+    append_section(t.image, t.offs, t.tm_b);
     t.image.resize((t.image.size() + 255) & ~size_t(255));
 }
 
@@ -103,7 +105,8 @@ DevTable HostTable::device_view() const
     nxt(d.tm_cnt); nxt(d.dense_pair); nxt(d.tokmask); nxt(d.seg_off); nxt(d.seg_lo);
     nxt(d.seg_hi); nxt(d.seg_cnt); nxt(d.seg_lo_cut); nxt(d.seg_hi_cut); nxt(d.cuts);
     nxt(d.cut_off); nxt(d.cut_ev); nxt(d.tok2sel); nxt(d.tok2cut); nxt(d.seg_pair);
-    nxt(d.map_n); nxt(d.map_t);
+    nxt(d.map_n); nxt(d.map_t); nxt(d.tm_a); nxt(d.tm_b);
+    d.n_tm = (int32_t)tm_pair.size();
     if (map_n.empty()) {
         d.map_n = nullptr;
         d.map_t = nullptr;
@@ -210,6 +213,9 @@ WsLayout ws_layout(const HostTable &t, const Geometry &g)
     w.ea = o; o = al(o + nv * sizeof(int32_t));
     w.eb = o; o = al(o + nv * sizeof(int32_t));
     w.rcut = o; o = al(o + BL * t.ncut() * sizeof(float));
+    w.pw_nl = t.nsel() <= kSelMax ? t.nsel() : 0;
+    w.pw_ld = (kDenseMax + w.pw_nl + 3) & ~3;
+    w.pw = o; o = al(o + BL * (size_t)w.pw_ld * sizeof(float));
     size_t a4 = o;
     w.total = std::max(std::max(a1, a2), std::max(a3, a4));
     if (w.total == 0) w.total = 256;
@@ -483,6 +489,12 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
                 t.tm_pair[pos] = q;
                 if (t.has_cnt) t.tm_cnt[pos] = t.list_cnt[k];
             }
+    }
+    t.tm_a.resize(t.tm_pair.size());
+    t.tm_b.resize(t.tm_pair.size());
+    for (size_t k = 0; k < t.tm_pair.size(); ++k) {
+        t.tm_a[k] = t.pair_a[t.tm_pair[k]];
+        t.tm_b[k] = t.pair_b[t.tm_pair[k]];
     }
     // range cut points and events
     t.cuts.clear();
