@@ -108,19 +108,39 @@ __global__ __launch_bounds__(kDenseThreads) void emission_dense(
         st.m = d.tokmask[min(v0 + tid, v_end - 1)];
     };
     auto store = [&](const Step &st, int v0, int buf) {
-        const int v = v0 + scol;
+        float4 xs[8];
+        if (v0 + kSub <= v_end && pos0 + kDenseTile <= npos) {  // whole tile in range
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const bool rok = pos0 + 4 * k + wave < npos;
-            float4 x;
-            x.x = (rok && v < v_end) ? st.x[k].x : 0.f;
-            x.y = (rok && v + 1 < v_end) ? st.x[k].y : 0.f;
-            x.z = (rok && v + 2 < v_end) ? st.x[k].z : 0.f;
-            x.w = (rok && v + 3 < v_end) ? st.x[k].w : 0.f;
-            const bool b = !(x.x >= 0.f) | !(x.y >= 0.f) | !(x.z >= 0.f) | !(x.w >= 0.f);
-            bad |= (int)b << k;  // which staged rows saw a negative or NaN value
-            *reinterpret_cast<float4 *>(&pt[buf][4 * k + wave][scol]) = x;
+            for (int k = 0; k < 8; ++k) xs[k] = st.x[k];
+        } else {
+            const int v = v0 + scol;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const bool rok = pos0 + 4 * k + wave < npos;
+                xs[k].x = (rok && v < v_end) ? st.x[k].x : 0.f;
+                xs[k].y = (rok && v + 1 < v_end) ? st.x[k].y : 0.f;
+                xs[k].z = (rok && v + 2 < v_end) ? st.x[k].z : 0.f;
+                xs[k].w = (rok && v + 3 < v_end) ? st.x[k].w : 0.f;
+            }
         }
+        // screen: as unsigned bit patterns, every value that is not >= 0
+        // (negative, NaN) and also -0 exceeds 0x7F800000; only then take the
+        // exact test per staged row
+        uint32_t mx = 0u;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            mx = max(mx, max(max(__float_as_uint(xs[k].x), __float_as_uint(xs[k].y)),
+                             max(__float_as_uint(xs[k].z), __float_as_uint(xs[k].w))));
+        if (mx > 0x7F800000u) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const bool b = !(xs[k].x >= 0.f) | !(xs[k].y >= 0.f) | !(xs[k].z >= 0.f) |
+                               !(xs[k].w >= 0.f);
+                bad |= (int)b << k;  // which staged rows saw a negative or NaN value
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) *reinterpret_cast<float4 *>(&pt[buf][4 * k + wave][scol]) = xs[k];
         mk[buf][tid] = v0 + tid < v_end ? st.m : 0u;
     };
     const int half = lane >> 5, l32 = lane & 31;
@@ -436,6 +456,102 @@ __global__ __launch_bounds__(kDensifyThreads) void emission_densify(
     }
 }
 
+// value of pair q at position pos, with a dense-mask pair's V-chunk partials
+// added here in chunk order
+__device__ inline float pair_value_direct(const DevTable &d, int q, size_t pos, const EmitSrc &s,
+                                          int &bad)
+{
+    if (d.pair_cls[q] == kDense) {
+        const int j = d.pair_aux[q];
+        const float *dp = s.dpart + pos * kDenseMax + j;
+        const size_t cs = (size_t)s.BLpad * kDenseMax;  // chunk stride
+        float acc = 0.f;
+        int c = 0;
+        // eight partials loaded together, then added in chunk order
+        for (; c + 8 <= s.n_vchunks; c += 8) {
+            float t[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) t[u] = dp[(size_t)(c + u) * cs];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc += t[u];
+        }
+        for (; c < s.n_vchunks; ++c) acc += dp[(size_t)c * cs];
+        return acc;
+    }
+    return pair_value(d, q, pos, s, bad);
+}
+
+// Leaves from pair values in one pass.  One workgroup per group of rg
+// stored rows of one leaf (rg * Sp <= kLeafTile): the tile is cleared in
+// LDS, every pair of those rows is evaluated in parallel (they are one
+// contiguous range of the leaf entries, in pair order or in column order for
+// a transposed leaf; a one-token list pair reads its value directly) and
+// placed in the tile with its row's largest exponent, then the tile is
+// written out with float4 stores.
+constexpr int kLeafThreads = 256;
+constexpr int kLeafTile = 4096;  // floats
+
+__global__ __launch_bounds__(kLeafThreads) void emission_leaves(DevTable d, StepView sv, int rg,
+                                                                EmitSrc src, float *__restrict__ tree,
+                                                                int32_t *__restrict__ meta,
+                                                                int32_t *__restrict__ status)
+{
+    __shared__ __align__(16) float tile[kLeafTile];
+    __shared__ int remax[kLeafTile / kSpAlign];
+    const int tid = threadIdx.x;
+    const int Sp = sv.Sp;
+    const int b = blockIdx.y / sv.Lpad, i = blockIdx.y % sv.Lpad;
+    const int r0 = blockIdx.x * rg;
+    const int nr = min(rg, Sp - r0);
+    const int h = sv.Lpad + i;
+    const bool tr = stored_transposed(h);
+    const size_t pos = (size_t)b * sv.L + i;
+    float4 *tile4 = reinterpret_cast<float4 *>(tile);
+    const int n4 = nr * Sp / 4;
+    for (int k = tid; k < n4; k += kLeafThreads) tile4[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int r = tid; r < nr; r += kLeafThreads) remax[r] = kNeg;
+    __syncthreads();
+    if (i < sv.L) {
+        const int rlo = min(r0, d.S), rhi = min(r0 + nr, d.S);
+        const int k0 = tr ? d.col_ptr[rlo] : d.row_ptr[rlo];
+        const int k1 = tr ? d.col_ptr[rhi] : d.row_ptr[rhi];
+        int bad = 0;
+        const int32_t *erc = tr ? d.ent_t_rc : d.ent_n_rc;
+        const int32_t *esrc = tr ? d.ent_t_src : d.ent_n_src;
+        const float *direct = d.use_sel ? src.psel + pos * d.nsel : src.p + pos * d.V;
+        for (int k = k0 + tid; k < k1; k += kLeafThreads) {
+            const int rc = erc[k], code = esrc[k];
+            const int row = (rc >> 16) - r0, col = rc & 0xffff;
+            float v;
+            if (code >= 0) {
+                v = direct[code];
+                if (!d.use_sel) bad |= !(v >= 0.f);
+            } else {
+                v = pair_value_direct(d, -1 - code, pos, src, bad);
+            }
+            tile[row * Sp + col] = v;
+            if (v > 0.f) atomicMax(&remax[row], fexp(v));
+        }
+        if (bad) atomicOr(&status[b], (int)FA_ROW_BADPROB);
+    } else {  // identity leaf past the sequence end
+        for (int r = tid; r < nr; r += kLeafThreads)
+            if (r0 + r < d.S) {
+                tile[r * Sp + r0 + r] = 1.f;
+                remax[r] = fexp(1.f);
+            }
+    }
+    __syncthreads();
+    float4 *M4 = reinterpret_cast<float4 *>(sv.mat_ptr(tree, b, h) + (size_t)r0 * Sp);
+    for (int k = tid; k < n4; k += kLeafThreads) M4[k] = tile4[k];
+    int32_t *ro = sv.meta_ptr(meta, b, h, 0), *co = sv.meta_ptr(meta, b, h, 1);
+    int32_t *rf = sv.meta_ptr(meta, b, h, 2);
+    for (int r = tid; r < nr; r += kLeafThreads) {
+        rf[r0 + r] = remax[r];
+        ro[r0 + r] = 0;
+        co[r0 + r] = 0;
+    }
+}
+
 }  // namespace
 
 int launch_build_transitions(const DevTable &d, const Geometry &g, const float *p, float *tree,
@@ -453,6 +569,8 @@ int launch_build_transitions(const DevTable &d, const Geometry &g, const float *
     src.n_vchunks = w.n_vchunks;
     src.BLpad = BLpad;
     src.dval = (float *)(ws + w.dval);
+    // leaves straight from pair values when an LDS tile holds a row
+    const bool fused = g.Sp <= kLeafTile;  // the leaf entries exist for Sp < 65536
     if (d.ndense > 0) {
         dim3 grid(w.n_vchunks, BLpad / kDenseTile);
         const bool vec = (d.V & 3) == 0 && ((uintptr_t)p & 15) == 0;
@@ -473,16 +591,25 @@ int launch_build_transitions(const DevTable &d, const Geometry &g, const float *
 #undef FA_DENSE
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
-        const int n = npos * kDenseMax;
-        emission_dense_reduce<<<(n + 255) / 256, 256, 0, st>>>(w.n_vchunks, BLpad, npos, d.ndense,
-                                                               src.dpart, (float *)src.dval);
-        e = hipGetLastError();
-        if (e != hipSuccess) return (int)e;
+        if (!fused) {
+            const int n = npos * kDenseMax;
+            emission_dense_reduce<<<(n + 255) / 256, 256, 0, st>>>(w.n_vchunks, BLpad, npos, d.ndense,
+                                                                   src.dpart, (float *)src.dval);
+            e = hipGetLastError();
+            if (e != hipSuccess) return (int)e;
+        }
     }
     if (d.nseg > 0) {
         emission_ranges<<<npos, kStreamThreads, 0, st>>>(d, p, g.L, (double *)src.cutp, status);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
+    }
+    StepView sv = step_view(g);
+    if (fused) {
+        const int rg = kLeafTile / g.Sp;
+        dim3 grid((g.Sp + rg - 1) / rg, g.B * g.Lpad);
+        emission_leaves<<<grid, kLeafThreads, 0, st>>>(d, sv, rg, src, tree, meta, status);
+        return (int)hipGetLastError();
     }
     float *val = (float *)(ws + w.val);
     if (d.npairs > 0) {
@@ -491,7 +618,6 @@ int launch_build_transitions(const DevTable &d, const Geometry &g, const float *
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
     }
-    StepView sv = step_view(g);
     if (d.map_n) {
         dim3 grid((g.Sp + 3) / 4, g.B * g.Lpad);
         emission_densify_map<<<grid, 256, 0, st>>>(d, sv, val, tree, meta);

@@ -75,6 +75,14 @@ struct DevTable {
     const int32_t *map_t;      // [Sp][Sp] pair at (b, a) (transposed storage)
     const int32_t *tm_a;       // [list entries] source state of each token-major entry
     const int32_t *tm_b;       // [list entries] target state
+    // leaf entries, in pair order (row-major leaves) and in column order
+    // (transposed leaves): stored (row << 16 | column), and the value's
+    // source: >= 0 a direct index (psel column, or token of p without a
+    // compact copy) of a one-token count-1 list pair, else -1 - pair
+    const int32_t *ent_n_rc;
+    const int32_t *ent_n_src;
+    const int32_t *ent_t_rc;
+    const int32_t *ent_t_src;
     int32_t n_tm;              // token-major LIST entries
 };
 
@@ -94,6 +102,7 @@ struct HostTable {
     std::vector<int32_t> tok2sel, tok2cut, seg_pair;
     std::vector<int32_t> map_n, map_t;
     std::vector<int32_t> tm_a, tm_b;
+    std::vector<int32_t> ent_n_rc, ent_n_src, ent_t_rc, ent_t_src;
     bool has_cnt = false;
     bool use_sel = false;
     bool selbit = false;

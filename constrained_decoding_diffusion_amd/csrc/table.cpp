@@ -73,6 +73,10 @@ void build_image(HostTable &t)
     append_section(t.image, t.offs, t.map_t);
     append_section(t.image, t.offs, t.tm_a);
     append_section(t.image, t.offs, t.tm_b);
+    append_section(t.image, t.offs, t.ent_n_rc);
+    append_section(t.image, t.offs, t.ent_n_src);
+    append_section(t.image, t.offs, t.ent_t_rc);
+    append_section(t.image, t.offs, t.ent_t_src);
     t.image.resize((t.image.size() + 255) & ~size_t(255));
 }
 
@@ -106,6 +110,7 @@ DevTable HostTable::device_view() const
     nxt(d.seg_hi); nxt(d.seg_cnt); nxt(d.seg_lo_cut); nxt(d.seg_hi_cut); nxt(d.cuts);
     nxt(d.cut_off); nxt(d.cut_ev); nxt(d.tok2sel); nxt(d.tok2cut); nxt(d.seg_pair);
     nxt(d.map_n); nxt(d.map_t); nxt(d.tm_a); nxt(d.tm_b);
+    nxt(d.ent_n_rc); nxt(d.ent_n_src); nxt(d.ent_t_rc); nxt(d.ent_t_src);
     d.n_tm = (int32_t)tm_pair.size();
     if (map_n.empty()) {
         d.map_n = nullptr;
@@ -551,6 +556,28 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
     t.selbit = t.ndense() > 0 && t.ndense() < 32 && ns > 0;
     if (t.selbit)
         for (int32_t v : t.sel_tok) t.tokmask[v] |= kSelBit;
+    // leaf entries (stored row, column and value source) in both orders
+    t.ent_n_rc.clear(); t.ent_n_src.clear(); t.ent_t_rc.clear(); t.ent_t_src.clear();
+    if (t.Sp < 65536) {
+        auto src_code = [&](int32_t q) -> int32_t {
+            if (t.pair_cls[q] == kList && t.list_off[q + 1] - t.list_off[q] == 1) {
+                const int32_t k = t.list_off[q];
+                if (t.list_cnt.empty() || t.list_cnt[k] == 1.f)
+                    return t.use_sel ? t.list_sel[k] : t.list_tok[k];
+            }
+            return -1 - q;
+        };
+        t.ent_n_rc.resize(np); t.ent_n_src.resize(np); t.ent_t_rc.resize(np); t.ent_t_src.resize(np);
+        for (int32_t q = 0; q < np; ++q) {
+            t.ent_n_rc[q] = (t.pair_a[q] << 16) | t.pair_b[q];
+            t.ent_n_src[q] = src_code(q);
+        }
+        for (int32_t k = 0; k < np; ++k) {
+            const int32_t q = t.col_pairs[k];
+            t.ent_t_rc[k] = (t.pair_b[q] << 16) | t.pair_a[q];
+            t.ent_t_src[k] = src_code(q);
+        }
+    }
     build_image(t);
     return FA_OK;
 }

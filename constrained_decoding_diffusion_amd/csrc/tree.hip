@@ -103,24 +103,30 @@ __global__ __launch_bounds__(kGemmThreads) void span_gemm(StepView sv, float *__
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 
+    // operands and column exponents of the next K block are loaded while
+    // the current one computes; every step issues the same loads (the last
+    // re-reads the final block), and the scheduling barriers keep the fold
+    // arithmetic, which waits for the loads, out of the MFMAs
     float4 f0, f1, g0, g1;
-    load8(Frow + k_begin + lk, f0, f1);
-    load8(Grow + k_begin + lk, g0, g1);
+    int4 cf0, cf1, cg0, cg1;
+    auto gl = [&](int k0) {
+        load8(Frow + k0 + lk, f0, f1);
+        load8(Grow + k0 + lk, g0, g1);
+        cf0 = *reinterpret_cast<const int4 *>(coF + k0 + lk);
+        cf1 = *reinterpret_cast<const int4 *>(coF + k0 + lk + 4);
+        cg0 = *reinterpret_cast<const int4 *>(coG + k0 + lk);
+        cg1 = *reinterpret_cast<const int4 *>(coG + k0 + lk + 4);
+    };
+    gl(k_begin);
     for (int k0 = k_begin; k0 < k_end; k0 += kBK) {
-        const int4 cf0 = *reinterpret_cast<const int4 *>(coF + k0 + lk);
-        const int4 cf1 = *reinterpret_cast<const int4 *>(coF + k0 + lk + 4);
-        const int4 cg0 = *reinterpret_cast<const int4 *>(coG + k0 + lk);
-        const int4 cg1 = *reinterpret_cast<const int4 *>(coG + k0 + lk + 4);
         __syncthreads();
         *reinterpret_cast<float4 *>(&Fs[lrow][lk]) = fold4(f0, cf0, rfFrow);
         *reinterpret_cast<float4 *>(&Fs[lrow][lk + 4]) = fold4(f1, cf1, rfFrow);
         *reinterpret_cast<float4 *>(&Gs[lrow][lk]) = fold4(g0, cg0, rfGrow);
         *reinterpret_cast<float4 *>(&Gs[lrow][lk + 4]) = fold4(g1, cg1, rfGrow);
         __syncthreads();
-        if (k0 + kBK < k_end) {
-            load8(Frow + k0 + kBK + lk, f0, f1);
-            load8(Grow + k0 + kBK + lk, g0, g1);
-        }
+        gl(min(k0 + kBK, k_end - kBK));
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < kBK / 2; t += 4) {
             const float4 a = *reinterpret_cast<const float4 *>(&Fs[wr + l32][half * (kBK / 2) + t]);
@@ -130,6 +136,7 @@ __global__ __launch_bounds__(kGemmThreads) void span_gemm(StepView sv, float *__
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, c.z, acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, c.w, acc, 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
     }
     if (ksplit > 1) {  // partial tile, row-major 64x64
         float *pt = part + ((size_t)(blockIdx.y * ksplit + split) * T2 + tile) * (kTile * kTile);
@@ -298,7 +305,10 @@ __global__ __launch_bounds__(kBigThreads) void span_gemm128(StepView sv, float *
     __syncthreads();
     for (int ks = 0; ks < nk; ++ks) {
         const int buf = ks & 1;
-        if (ks + 1 < nk) gload((ks + 1) * kBK2);
+        // unconditional (the last step re-reads the final K block), and kept
+        // ahead of the MFMAs, with the fold arithmetic after them
+        gload(min(ks + 1, nk - 1) * kBK2);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < kBK2 / 2; t += 4) {
             const float4 a = *reinterpret_cast<const float4 *>(&Fs[buf][wr + l32][half * (kBK2 / 2) + t]);
@@ -314,7 +324,8 @@ __global__ __launch_bounds__(kBigThreads) void span_gemm128(StepView sv, float *
                 acc[y] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, c[y].w, acc[y], 0, 0, 0);
             }
         }
-        if (ks + 1 < nk) lstore(buf ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+        lstore(buf ^ 1);
         __syncthreads();
     }
     // epilogue
@@ -383,6 +394,172 @@ __global__ void tree_logz_empty(DevTable d, int B, double *__restrict__ logZ,
     if (!ok) atomicOr(&status[b], (int)FA_ROW_INFEASIBLE);
 }
 
+// Large levels with one 256x256 output tile per workgroup (one whole
+// product when Sp = 256): 8 waves of 64 x 128 (2 x 4 MFMA tiles of 32x32),
+// 128 MFMAs per wave per K step of 32, double-buffered LDS (147 KB, one
+// workgroup per CU).  Every K step issues the same loads (the last step
+// re-reads the final K block), and the loads of block ks+1 are in flight
+// while block ks computes.  Row exponents are reduced inside the workgroup: one
+// store (full rows) or atomicMax (several column tiles) per row.
+constexpr int kHuge = 256;
+constexpr int kHugeThreads = 512;
+
+__global__ __launch_bounds__(kHugeThreads) void span_gemm256(StepView sv, float *__restrict__ tree,
+                                                             int32_t *__restrict__ meta, int n0,
+                                                             int nn)
+{
+    const int Sp = sv.Sp;
+    const int tiles = Sp / kHuge;
+    const int per_prod = tiles * tiles;
+    const int nwork = sv.B * nn * per_prod;
+    int w = blockIdx.x;
+    const int full = nwork & ~7;
+    if (per_prod > 1 && w < full) w = (w & 7) * (full >> 3) + (w >> 3);  // XCD-contiguous order
+    const int prod = w / per_prod, tile = w % per_prod;
+    const int tm = (tile / tiles) * kHuge, tn = (tile % tiles) * kHuge;
+    const int b = prod / nn, n = n0 + prod % nn;
+    const bool tr = stored_transposed(n);
+    const int hF = tr ? 2 * n + 1 : 2 * n, hG = tr ? 2 * n : 2 * n + 1;
+    const float *F = sv.mat_ptr((const float *)tree, b, hF);
+    const float *G = sv.mat_ptr((const float *)tree, b, hG);
+    const int32_t *roF = sv.meta_ptr((const int32_t *)meta, b, hF, 0);
+    const int32_t *coF = sv.meta_ptr((const int32_t *)meta, b, hF, 1);
+    const int32_t *rfF = sv.meta_ptr((const int32_t *)meta, b, hF, 2);
+    const int32_t *roG = sv.meta_ptr((const int32_t *)meta, b, hG, 0);
+    const int32_t *coG = sv.meta_ptr((const int32_t *)meta, b, hG, 1);
+    const int32_t *rfG = sv.meta_ptr((const int32_t *)meta, b, hG, 2);
+    float *D = sv.mat_ptr(tree, b, n);
+    int32_t *roD = sv.meta_ptr(meta, b, n, 0);
+    int32_t *coD = sv.meta_ptr(meta, b, n, 1);
+    int32_t *rfD = sv.meta_ptr(meta, b, n, 2);
+
+    __shared__ __align__(16) float Fs[2][kHuge][kLdk2];
+    __shared__ __align__(16) float Gs[2][kHuge][kLdk2];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // loader: thread t stages float4 (t & 7) of rows (t >> 3) + 64 q, q < 4,
+    // of both operands: eight lanes read one 128-byte row segment
+    const int lrow = tid >> 3, lk = (tid & 7) * 4;
+    int rfFq[4], rfGq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        rfFq[q] = rfF[tm + lrow + 64 * q];
+        rfGq[q] = rfG[tn + lrow + 64 * q];
+    }
+    const float *Frow = F + (size_t)(tm + lrow) * Sp + lk;
+    const float *Grow = G + (size_t)(tn + lrow) * Sp + lk;
+    const size_t q_rows = (size_t)64 * Sp;
+    const int wr = (wave >> 1) * 64, wc = (wave & 1) * 128;
+    const int l32 = lane & 31, half = lane >> 5;
+
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int ry = 0; ry < 2; ++ry)
+#pragma unroll
+        for (int cy = 0; cy < 4; ++cy)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[ry][cy][r] = 0.f;
+
+    const int nk = Sp / kBK2;
+    struct Stage {
+        float4 f[4], g[4];
+        int4 cf, cg;
+    };
+    auto gload = [&](Stage &st, int ks) {
+        const int k0 = min(ks, nk - 1) * kBK2;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            st.f[q] = *reinterpret_cast<const float4 *>(Frow + q * q_rows + k0);
+            st.g[q] = *reinterpret_cast<const float4 *>(Grow + q * q_rows + k0);
+        }
+        st.cf = *reinterpret_cast<const int4 *>(coF + k0 + lk);
+        st.cg = *reinterpret_cast<const int4 *>(coG + k0 + lk);
+    };
+    auto lstore = [&](const Stage &st, int buf) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            *reinterpret_cast<float4 *>(&Fs[buf][lrow + 64 * q][lk]) = fold4(st.f[q], st.cf, rfFq[q]);
+            *reinterpret_cast<float4 *>(&Gs[buf][lrow + 64 * q][lk]) = fold4(st.g[q], st.cg, rfGq[q]);
+        }
+    };
+    auto mfmas = [&](int buf) {
+#pragma unroll
+        for (int t = 0; t < kBK2 / 2; t += 4) {
+            float4 a[2], c[4];
+#pragma unroll
+            for (int ry = 0; ry < 2; ++ry)
+                a[ry] = *reinterpret_cast<const float4 *>(&Fs[buf][wr + 32 * ry + l32][half * (kBK2 / 2) + t]);
+#pragma unroll
+            for (int cy = 0; cy < 4; ++cy)
+                c[cy] = *reinterpret_cast<const float4 *>(&Gs[buf][wc + 32 * cy + l32][half * (kBK2 / 2) + t]);
+#pragma unroll
+            for (int ry = 0; ry < 2; ++ry)
+#pragma unroll
+                for (int cy = 0; cy < 4; ++cy) {
+                    acc[ry][cy] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[ry].x, c[cy].x, acc[ry][cy], 0, 0, 0);
+                    acc[ry][cy] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[ry].y, c[cy].y, acc[ry][cy], 0, 0, 0);
+                    acc[ry][cy] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[ry].z, c[cy].z, acc[ry][cy], 0, 0, 0);
+                    acc[ry][cy] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[ry].w, c[cy].w, acc[ry][cy], 0, 0, 0);
+                }
+        }
+    };
+    Stage st;
+    gload(st, 0);
+    lstore(st, 0);
+    __syncthreads();
+    // step ks: issue the loads of K block ks+1, compute buffer ks & 1 (128
+    // MFMAs per wave cover the load latency), store block ks+1 into the other
+    // buffer.  nk = Sp / 32 is even.
+    // The scheduling barriers keep the compiler from moving the fold
+    // arithmetic of the stores (which waits for the loads) into the MFMAs.
+    for (int ks = 0; ks < nk; ks += 2) {
+        gload(st, ks + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(0);
+        __builtin_amdgcn_sched_barrier(0);
+        lstore(st, 1);
+        __syncthreads();
+        gload(st, ks + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(1);
+        __builtin_amdgcn_sched_barrier(0);
+        lstore(st, 0);
+        __syncthreads();
+    }
+    // epilogue: D, and per row the largest e(D[i][j]) + coD[j]
+    int coDj[4];
+#pragma unroll
+    for (int cy = 0; cy < 4; ++cy) {
+        const int j = tn + wc + 32 * cy + l32;
+        coDj[cy] = add_exp(roG[j], rfG[j]);
+    }
+    int *red = reinterpret_cast<int *>(&Fs[0][0][0]);  // [2][kHuge] row maxima per column half
+#pragma unroll
+    for (int ry = 0; ry < 2; ++ry) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int il = wr + 32 * ry + (r >> 2) * 8 + half * 4 + (r & 3);
+            int e = kNeg;
+#pragma unroll
+            for (int cy = 0; cy < 4; ++cy) {
+                const float v = acc[ry][cy][r];
+                D[(size_t)(tm + il) * Sp + tn + wc + 32 * cy + l32] = v;
+                if (v > 0.f && coDj[cy] > kNeg) e = max(e, fexp(v) + coDj[cy]);
+            }
+#pragma unroll
+            for (int o = 16; o > 0; o >>= 1) e = max(e, __shfl_xor(e, o));
+            if (l32 == 0) red[(wc / 128) * kHuge + il] = e;
+        }
+    }
+    __syncthreads();
+    if (tid < kHuge) {
+        const int e = max(red[tid], red[kHuge + tid]);
+        if (tiles == 1) rfD[tm + tid] = e;
+        else if (e > kNeg) atomicMax(&rfD[tm + tid], e);
+    }
+    if (tn == 0 && tid < kHuge) roD[tm + tid] = add_exp(roF[tm + tid], rfF[tm + tid]);
+    if (tm == 0 && tid >= kHuge) coD[tn + tid - kHuge] = add_exp(roG[tn + tid - kHuge], rfG[tn + tid - kHuge]);
+}
+
 }  // namespace
 
 int launch_span_tree(const DevTable &d, const Geometry &g, float *tree, int32_t *meta,
@@ -407,7 +584,11 @@ int launch_span_tree(const DevTable &d, const Geometry &g, float *tree, int32_t 
         const int big_tiles = g.Sp / kBig;
         const long long big_wgs = (long long)g.B * nn * big_tiles * big_tiles;
         const int ks = tree_ksplit(g, k);
-        if (ks == 1 && g.Sp % kBig == 0 && big_wgs >= 512) {
+        const int huge_tiles = g.Sp / kHuge;
+        const long long huge_wgs = (long long)g.B * nn * huge_tiles * huge_tiles;
+        if (ks == 1 && g.Sp % kHuge == 0 && huge_wgs >= 256) {
+            span_gemm256<<<(unsigned)huge_wgs, kHugeThreads, 0, st>>>(sv, tree, meta, n0, nn);
+        } else if (ks == 1 && g.Sp % kBig == 0 && big_wgs >= 512) {
             span_gemm128<<<(unsigned)big_wgs, kBigThreads, 0, st>>>(sv, tree, meta, n0, nn);
         } else {
             float *part = (float *)(ws + w.kpart);
