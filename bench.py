@@ -47,19 +47,60 @@ def traffic_record(kernel: str):
 
 
 def algorithmic_work(tb, B, L):
+    """Algorithmic bytes / flops per step and per launch of the measured
+    kernels (the method's own data movement and arithmetic, no re-reads)."""
     S, Sp, V = tb.info["S"], tb.info["Sp"], tb.info["V"]
     Lpad = 1 << max(0, (L - 1).bit_length())
     K = Lpad.bit_length() - 1
     table_bytes = tb.device_bytes
     p_bytes = B * L * V * 4
+    mask_bytes = V * 4
     leaves = B * Lpad * Sp * Sp * 4
     internal = B * (Lpad - 1) * Sp * Sp * 4
     return dict(
         a1_bytes=p_bytes + table_bytes + leaves,
         a2_flops=2.0 * Sp ** 3 * B * (Lpad - 1),
-        a2_launches=K,
         a4_bytes=p_bytes + p_bytes + leaves + internal + table_bytes,
+        # per launch of the kernels the library can bracket with events
+        kernels={
+            "emission_dense": dict(bound="hbm", work=p_bytes + mask_bytes, unit="GB/s",
+                                   per_unit="p read once (B*L*V*4) + token mask (V*4)"),
+            "span_gemm_level1": dict(bound="mfma", work=2.0 * Sp ** 3 * B * (Lpad // 2),
+                                     unit="TFLOP/s",
+                                     per_unit="2*Sp^3 per product, B*Lpad/2 products"),
+            "marg_q": dict(bound="hbm", work=2 * p_bytes + mask_bytes, unit="GB/s",
+                           per_unit="p read + q write (2*B*L*V*4) + token mask (V*4)"),
+        },
         S=S, Sp=Sp, V=V, Lpad=Lpad, K=K)
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch has loaded."""
+
+    def __init__(self):
+        import ctypes as C
+        self.C = C
+        self.hip = C.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [C.c_void_p]
+
+    def create(self):
+        ev = self.C.c_void_p()
+        if self.hip.hipEventCreate(self.C.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return ev.value
+
+    def elapsed_ms(self, a, b):
+        """Milliseconds between two recorded events, or None when the kernel
+        did not run (this workload has no such launch)."""
+        ms = self.C.c_float()
+        if self.hip.hipEventElapsedTime(self.C.byref(ms), self.C.c_void_p(a), self.C.c_void_p(b)) != 0:
+            return None
+        return ms.value
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(self.C.c_void_p(ev))
 
 
 def cpu_baseline(w):
@@ -80,6 +121,99 @@ def cpu_baseline(w):
                        f"serial fp64 C, {dt:.2f} s")
 
 
+# --- rocprofv3 output -> committed summaries ------------------------------
+
+# measured kernels: how to find their dispatches in rocprofv3 output
+KERNEL_MATCH = {
+    "emission_dense": lambda n: "emission_dense<" in n,
+    "span_gemm_level1": lambda n: "span_gemm" in n,   # first of the family after tree_init_rf
+    "marg_q": lambda n: "marg_q" in n,
+}
+
+
+def _select(rows, name):
+    """Dispatches of one measured kernel, in dispatch order; for the tree
+    products only the first level (the first product launch after each
+    tree_init_rf)."""
+    rows = sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
+    match = KERNEL_MATCH[name]
+    if name != "span_gemm_level1":
+        return [r for r in rows if match(r["Kernel_Name"])]
+    out, armed = [], False
+    for r in rows:
+        if "tree_init_rf" in r["Kernel_Name"]:
+            armed = True
+        elif armed and match(r["Kernel_Name"]):
+            out.append(r)
+            armed = False
+    return out
+
+
+def summarize_counters(fetch_dir, write_dir, command):
+    """profiles/traffic_<kernel>.json and profiles/counters_json_like_dfa.md
+    from one FETCH_SIZE and one WRITE_SIZE pass (each with --copy-calib)."""
+    import csv
+    rows = {}
+    for tag, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        path = os.path.join(d, "run_counter_collection.csv")
+        rows[tag] = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == tag]
+    # calibration: the 1 GiB device copy moves 2^30 bytes each way
+    calib = {}
+    for tag, rs in rows.items():
+        kib = max(float(r["Counter_Value"]) for r in rs if "copyBuffer" in r["Kernel_Name"])
+        calib[tag] = (1 << 30) / (kib * 1024.0)
+    lines = ["# HBM bytes per launch from rocprofv3 counters (json-like DFA, B=4, L=256, V=151,936)",
+             "", "Command (one pass per counter, from the repository root; the 1 GiB device copy of",
+             "`--copy-calib` calibrates each counter):", "", "```", command, "```", "",
+             f"Calibration: FETCH_SIZE x {calib['FETCH_SIZE']:.3f}, WRITE_SIZE x {calib['WRITE_SIZE']:.3f}"
+             " (bytes = counter KiB x 1024 x factor).", "",
+             "| kernel | dispatch | fetch MB | write MB | traffic MB |", "|---|---|---|---|---|"]
+    h = src_hash()
+    for name in KERNEL_MATCH:
+        mean = lambda rs: sum(float(r["Counter_Value"]) for r in rs) / len(rs)
+        fsel, wsel = _select(rows["FETCH_SIZE"], name), _select(rows["WRITE_SIZE"], name)
+        if not fsel or not wsel:
+            continue
+        kname, grid = fsel[0]["Kernel_Name"], int(fsel[0]["Grid_Size"])
+        fk, wk = mean(fsel), mean(wsel)
+        fb = fk * 1024.0 * calib["FETCH_SIZE"]
+        wb = wk * 1024.0 * calib["WRITE_SIZE"]
+        rec = dict(kernel=name, dispatch=kname[:120], grid_threads=grid, fetch_bytes=fb,
+                   write_bytes=wb, bytes_per_launch=fb + wb, src_hash=h,
+                   calibration=calib, command=command)
+        with open(os.path.join(ROOT, "profiles", f"traffic_{name}.json"), "w") as fh:
+            json.dump(rec, fh, indent=1)
+        lines.append(f"| {name} | `{kname[:60]}` grid {grid} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | "
+                     f"{(fb + wb) / 1e6:.1f} |")
+    with open(os.path.join(ROOT, "profiles", "counters_json_like_dfa.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+def summarize_trace(trace_dir, command):
+    """profiles/step_json_like_dfa_kernel_trace.md from a --kernel-trace
+    --stats run: per-kernel totals and per-launch-shape averages."""
+    import csv
+    stats = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
+    trace = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))))
+    short = lambda n: n.replace("fa::(anonymous namespace)::", "").split("(fa::")[0][:60]
+    lines = ["# Kernel trace of the constrained step (json-like DFA, B=4, L=256, V=151,936)", "",
+             "Command (from the repository root):", "", "```", command, "```", "",
+             "| kernel | calls | avg us | total ms | % |", "|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['TotalDurationNs']) / 1e6:.2f} | {float(r['Percentage']):.1f} |")
+    groups = {}
+    for r in trace:
+        k = (short(r["Kernel_Name"]), r["Grid_Size_X"], r["Grid_Size_Y"])
+        groups.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines += ["", "Per launch shape (grid in threads):", "", "| kernel | grid x | grid y | calls | avg us |",
+              "|---|---|---|---|---|"]
+    for k, v in sorted(groups.items(), key=lambda kv: -sum(kv[1]))[:30]:
+        lines.append(f"| `{k[0]}` | {k[1]} | {k[2]} | {len(v)} | {sum(v) / len(v):.1f} |")
+    with open(os.path.join(ROOT, "profiles", "step_json_like_dfa_kernel_trace.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -89,7 +223,18 @@ def main():
     ap.add_argument("--workload", type=int, default=3, help="preset 1..5 (default 3)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="first run one plain device copy of 1 GiB (counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic_*.json from two rocprofv3 --pmc passes, then exit")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="write the kernel-trace summary under profiles/ from a rocprofv3 run, then exit")
+    ap.add_argument("--command", default="", help="the command recorded in a summary")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.command)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.command)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(rows shard across GPUs with no communication; see the design notes)",
@@ -117,8 +262,17 @@ def main():
         del src_buf, dst_buf
     torch.cuda.synchronize()
 
-    def one_step(seed, ev=None):
+    # the library brackets one kernel per step with HIP events on its own
+    # stream; the timed steps rotate over the three measured kernels
+    prof_ids = [("emission_dense", fa.FA_PROF_EMISSION_DENSE),
+                ("span_gemm_level1", fa.FA_PROF_TREE_LEVEL1),
+                ("marg_q", fa.FA_PROF_MARG_Q)]
+    hev = HipEvents()
+
+    def one_step(seed, ev=None, kev=None):
         bufs.status.zero_()
+        if kev:
+            fa.profile_kernel(kev[0], kev[1], kev[2])
         if ev: ev[0].record()
         fa.build_transitions(tb, p, bufs, stream)
         if ev: ev[1].record()
@@ -133,16 +287,21 @@ def main():
         one_step(w.seed + s)
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    kevs = []
+    for s in range(args.steps):
+        name, pid = prof_ids[s % len(prof_ids)]
+        kevs.append((pid, hev.create(), hev.create(), name))
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record()
     for s in range(args.steps):
-        one_step(w.seed + args.warmup + s, evs[s])
+        one_step(w.seed + args.warmup + s, evs[s], kevs[s][:3])
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    fa.profile_kernel(fa.FA_PROF_NONE)
     total_ms = t_start.elapsed_time(t_end)
     names = ["build_transitions", "span_tree", "sample", "marginals"]
     stage_ms = {n: 0.0 for n in names}
@@ -150,6 +309,14 @@ def main():
         for k, n in enumerate(names):
             stage_ms[n] += ev[k].elapsed_time(ev[k + 1])
     stage_us = {n: 1000.0 * v / args.steps for n, v in stage_ms.items()}
+    kern_us = {}
+    for pid, a, b, name in kevs:
+        ms = hev.elapsed_ms(a, b)
+        if ms is not None:
+            kern_us.setdefault(name, []).append(1000.0 * ms)
+        hev.destroy(a)
+        hev.destroy(b)
+    kern_us = {k: sum(v) / len(v) for k, v in kern_us.items()}
     ms_per_step = total_ms / args.steps
     status = bufs.status.cpu().numpy()
 
@@ -167,25 +334,20 @@ def main():
     for n in ("build_transitions", "marginals"):
         stages[n]["frac"] = stages[n]["gbs"] / HBM_PEAK_GBS
     stages["span_tree"]["frac"] = stages["span_tree"]["tflops"] / FP32_MFMA_PEAK_TFLOPS
-    dominant = max(names, key=lambda n: stage_us[n])
-    if dominant == "span_tree":
-        # span_gemm launches: K per step; the call adds one fill and one
-        # root-reduction launch of a few microseconds
-        per_launch_us = stage_us["span_tree"] / work["a2_launches"]
-        achieved = work["a2_flops"] / (stage_us["span_tree"] * 1e6)
-        tr = traffic_record("span_gemm")
-        roof = dict(bound="mfma", kernel="span_gemm", achieved=achieved,
-                    peak=FP32_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=achieved / FP32_MFMA_PEAK_TFLOPS,
-                    traffic=(tr["bytes_per_launch"] if tr else None),
-                    avg_launch_us=per_launch_us, launches_per_step=work["a2_launches"])
-    else:
-        kern = {"build_transitions": "emission", "marginals": "marg_q", "sample": "sample"}[dominant]
-        st = stages[dominant]
-        tr = traffic_record(kern)
-        roof = dict(bound="hbm", kernel=kern, achieved=st.get("gbs", 0.0), peak=HBM_PEAK_GBS,
-                    unit="GB/s", frac=st.get("frac", 0.0),
-                    traffic=(tr["bytes_per_launch"] if tr else None))
+    kernels = {}
+    for name, us in kern_us.items():
+        kw = work["kernels"][name]
+        if kw["bound"] == "hbm":
+            achieved, peak = kw["work"] / (us * 1e3), HBM_PEAK_GBS
+        else:
+            achieved, peak = kw["work"] / (us * 1e6), FP32_MFMA_PEAK_TFLOPS
+        tr = traffic_record(name)
+        kernels[name] = dict(bound=kw["bound"], achieved=achieved, peak=peak, unit=kw["unit"],
+                             frac=achieved / peak, avg_launch_us=us, work_per_launch=kw["work"],
+                             work_basis=kw["per_unit"],
+                             traffic=(tr["bytes_per_launch"] if tr else None))
+    dominant = max(kernels, key=lambda k: kernels[k]["avg_launch_us"])
+    roof = dict(kernels[dominant], kernel=dominant)
     out = {
         "metric": METRIC,
         "value": 1000.0 / ms_per_step,
@@ -203,6 +365,7 @@ def main():
         "config": {"workload": w.describe(), "B": w.B, "L": w.L, "S": w.aut.S, "V": w.aut.V,
                    "sequence_steps_per_s": w.B * 1000.0 / ms_per_step},
         "roofline": roof,
+        "kernels": kernels,
         "stages": stages,
         "wall_s": wall,
         "row_status": status.tolist(),

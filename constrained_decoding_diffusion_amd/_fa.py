@@ -18,10 +18,11 @@ FA_OK, FA_EINVAL, FA_ENOTDET, FA_ETOOBIG, FA_EHIP, FA_ESTATE = range(6)
 FA_ROW_INFEASIBLE, FA_ROW_UNDERFLOW, FA_ROW_BADPROB = 1, 2, 4
 FA_DFA, FA_NFA, FA_LABEL_RANGES, FA_NO_TRIM = 1, 2, 4, 8
 FA_CONF_PROB, FA_CONF_NEGENT = 0, 1
+FA_PROF_NONE, FA_PROF_EMISSION_DENSE, FA_PROF_TREE_LEVEL1, FA_PROF_MARG_Q = range(4)
 
 EXPORTS = ["fa_compile_table", "fa_table_upload", "fa_table_destroy", "fa_table_info",
            "fa_table_state_map", "fa_sizes", "fa_build_transitions", "fa_span_tree", "fa_sample",
-           "fa_marginals", "fa_strerror"]
+           "fa_marginals", "fa_strerror", "fa_profile_kernel"]
 
 
 class FaError(RuntimeError):
@@ -54,6 +55,7 @@ def lib():
     L.fa_span_tree.argtypes = [P, I32, I32, P, P, P, SZ, P, P, P]
     L.fa_sample.argtypes = [P, P, I32, I32, P, P, U64, P, P, P, SZ, P, P]
     L.fa_marginals.argtypes = [P, P, I32, I32, P, P, P, P, I32, P, P, P, SZ, P, P]
+    L.fa_profile_kernel.argtypes = [I32, P, P]
     L.fa_strerror.argtypes = [C.c_int]
     L.fa_strerror.restype = C.c_char_p
     for fn in EXPORTS:
@@ -176,6 +178,13 @@ def marginals(table: Table, p, bufs: StepBuffers, conf_mode: int, stream, write_
         table.handle, _ptr(p), bufs.B, bufs.L, _ptr(bufs.tree), _ptr(bufs.meta), _ptr(bufs.logZ),
         _ptr(bufs.tokens), conf_mode, _ptr(bufs.q if write_q else None), _ptr(bufs.conf),
         _ptr(bufs.ws), bufs.ws.numel(), _ptr(bufs.status), C.c_void_p(stream)))
+
+
+def profile_kernel(which: int, start_event=None, stop_event=None):
+    """Measurement hook: bracket the launches of one kernel with two HIP
+    events (raw hipEvent_t handles as ints), FA_PROF_NONE to clear."""
+    _check("fa_profile_kernel", lib().fa_profile_kernel(which, C.c_void_p(start_event or 0),
+                                                        C.c_void_p(stop_event or 0)))
 
 
 def step(table: Table, p, seed: int, bufs: StepBuffers = None, conf_mode: int = FA_CONF_PROB,

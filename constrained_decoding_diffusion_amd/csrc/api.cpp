@@ -21,7 +21,33 @@ int hip_rc(int e) { return e == 0 ? FA_OK : FA_EHIP; }
 // grids put (row, node) pairs in their second dimension
 bool grid_fits(const Geometry &g) { return (int64_t)g.B * g.Lpad * 2 <= 65535 && g.L < (1 << 24); }
 
+struct ProfHook {
+    int which = FA_PROF_NONE;
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+ProfHook g_prof;
+
 }  // namespace
+
+namespace fa {
+
+int prof_mark(int which, bool begin, void *stream)
+{
+    if (which == FA_PROF_NONE || g_prof.which != which) return 0;
+    return (int)hipEventRecord(begin ? g_prof.start : g_prof.stop, (hipStream_t)stream);
+}
+
+}  // namespace fa
+
+extern "C" int fa_profile_kernel(int32_t which, void *start_event, void *stop_event)
+{
+    if (which < FA_PROF_NONE || which > FA_PROF_MARG_Q) return FA_EINVAL;
+    if (which != FA_PROF_NONE && (!start_event || !stop_event)) return FA_EINVAL;
+    g_prof.which = which;
+    g_prof.start = (hipEvent_t)start_event;
+    g_prof.stop = (hipEvent_t)stop_event;
+    return FA_OK;
+}
 
 extern "C" int fa_table_upload(fa_table *t, void *dev_buf, size_t bytes, fa_stream_t stream)
 {

@@ -57,16 +57,7 @@ __global__ __launch_bounds__(kDenseThreads) void emission_dense(
     const int v_begin = chunk * vchunk;
     const int v_end = min(d.V, v_begin + vchunk);
     const int nsteps = (v_end - v_begin + kSub - 1) / kSub;
-    if (SEL != 0 && tid <= nsteps) {
-        const int vs = v_begin + tid * kSub;
-        int lo = 0, hi = d.nsel;
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (d.sel_tok[mid] < vs) lo = mid + 1;
-            else hi = mid;
-        }
-        sel_at[tid] = lo;
-    }
+    if (SEL != 0 && tid <= nsteps) sel_at[tid] = d.sel_lb[v_begin / kSub + tid];
     if (SEL == 1) {
         __syncthreads();
         const int s0 = sel_at[0], nc = sel_at[nsteps] - s0;  // nc <= kDenseSelLds (host check)
@@ -487,9 +478,11 @@ __device__ inline float pair_value_direct(const DevTable &d, int q, size_t pos, 
 // contiguous range of the leaf entries, in pair order or in column order for
 // a transposed leaf; a one-token list pair reads its value directly) and
 // placed in the tile with its row's largest exponent, then the tile is
-// written out with float4 stores.
+// written out with float4 stores.  The first entries and their direct values
+// are loaded before the tile is cleared.
 constexpr int kLeafThreads = 256;
 constexpr int kLeafTile = 4096;  // floats
+constexpr int kLeafPre = 4;      // leaf entries per thread loaded ahead
 
 __global__ __launch_bounds__(kLeafThreads) void emission_leaves(DevTable d, StepView sv, int rg,
                                                                 EmitSrc src, float *__restrict__ tree,
@@ -508,20 +501,52 @@ __global__ __launch_bounds__(kLeafThreads) void emission_leaves(DevTable d, Step
     const size_t pos = (size_t)b * sv.L + i;
     float4 *tile4 = reinterpret_cast<float4 *>(tile);
     const int n4 = nr * Sp / 4;
+    const bool real = i < sv.L;
+    const int rlo = min(r0, d.S), rhi = min(r0 + nr, d.S);
+    const int k0 = real ? (tr ? d.col_ptr[rlo] : d.row_ptr[rlo]) : 0;
+    const int ne = real ? (tr ? d.col_ptr[rhi] : d.row_ptr[rhi]) - k0 : 0;
+    const int32_t *erc = (tr ? d.ent_t_rc : d.ent_n_rc) + k0;
+    const int32_t *esrc = (tr ? d.ent_t_src : d.ent_n_src) + k0;
+    const float *direct = d.use_sel ? src.psel + pos * d.nsel : src.p + pos * d.V;
+    // the first kLeafPre entries per thread, and their direct values, are
+    // loaded (clamped, unconditionally) before the tile is cleared
+    int prc[kLeafPre], pcode[kLeafPre];
+    float pval[kLeafPre];
+    if (ne > 0) {
+#pragma unroll
+        for (int u = 0; u < kLeafPre; ++u) {
+            const int k = min(tid + u * kLeafThreads, ne - 1);
+            prc[u] = erc[k];
+            pcode[u] = esrc[k];
+        }
+#pragma unroll
+        for (int u = 0; u < kLeafPre; ++u) pval[u] = direct[max(pcode[u], 0)];
+    }
     for (int k = tid; k < n4; k += kLeafThreads) tile4[k] = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int r = tid; r < nr; r += kLeafThreads) remax[r] = kNeg;
     __syncthreads();
-    if (i < sv.L) {
-        const int rlo = min(r0, d.S), rhi = min(r0 + nr, d.S);
-        const int k0 = tr ? d.col_ptr[rlo] : d.row_ptr[rlo];
-        const int k1 = tr ? d.col_ptr[rhi] : d.row_ptr[rhi];
+    if (real) {
         int bad = 0;
-        const int32_t *erc = tr ? d.ent_t_rc : d.ent_n_rc;
-        const int32_t *esrc = tr ? d.ent_t_src : d.ent_n_src;
-        const float *direct = d.use_sel ? src.psel + pos * d.nsel : src.p + pos * d.V;
-        for (int k = k0 + tid; k < k1; k += kLeafThreads) {
-            const int rc = erc[k], code = esrc[k];
+        auto place = [&](int rc, float v) {
             const int row = (rc >> 16) - r0, col = rc & 0xffff;
+            tile[row * Sp + col] = v;
+            if (v > 0.f) atomicMax(&remax[row], fexp(v));
+        };
+#pragma unroll
+        for (int u = 0; u < kLeafPre; ++u) {
+            if (tid + u * kLeafThreads < ne) {
+                float v;
+                if (pcode[u] >= 0) {
+                    v = pval[u];
+                    if (!d.use_sel) bad |= !(v >= 0.f);
+                } else {
+                    v = pair_value_direct(d, -1 - pcode[u], pos, src, bad);
+                }
+                place(prc[u], v);
+            }
+        }
+        for (int k = tid + kLeafPre * kLeafThreads; k < ne; k += kLeafThreads) {
+            const int code = esrc[k];
             float v;
             if (code >= 0) {
                 v = direct[code];
@@ -529,8 +554,7 @@ __global__ __launch_bounds__(kLeafThreads) void emission_leaves(DevTable d, Step
             } else {
                 v = pair_value_direct(d, -1 - code, pos, src, bad);
             }
-            tile[row * Sp + col] = v;
-            if (v > 0.f) atomicMax(&remax[row], fexp(v));
+            place(erc[k], v);
         }
         if (bad) atomicOr(&status[b], (int)FA_ROW_BADPROB);
     } else {  // identity leaf past the sequence end
@@ -574,6 +598,8 @@ int launch_build_transitions(const DevTable &d, const Geometry &g, const float *
     if (d.ndense > 0) {
         dim3 grid(w.n_vchunks, BLpad / kDenseTile);
         const bool vec = (d.V & 3) == 0 && ((uintptr_t)p & 15) == 0;
+        int pe = prof_mark(FA_PROF_EMISSION_DENSE, true, stream);
+        if (pe) return pe;
         const int sel = d.use_sel ? w.sel_mode : 0;
 #define FA_DENSE(VEC, SEL)                                                                      \
     emission_dense<VEC, SEL><<<grid, kDenseThreads, 0, st>>>(d, p, g.L, npos, BLpad, w.vchunk, \
@@ -591,6 +617,8 @@ int launch_build_transitions(const DevTable &d, const Geometry &g, const float *
 #undef FA_DENSE
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
+        pe = prof_mark(FA_PROF_EMISSION_DENSE, false, stream);
+        if (pe) return pe;
         if (!fused) {
             const int n = npos * kDenseMax;
             emission_dense_reduce<<<(n + 255) / 256, 256, 0, st>>>(w.n_vchunks, BLpad, npos, d.ndense,

@@ -83,6 +83,7 @@ struct DevTable {
     const int32_t *ent_n_src;
     const int32_t *ent_t_rc;
     const int32_t *ent_t_src;
+    const int32_t *sel_lb;     // [V/256 + 2] first sel_tok index at or after token 256 t
     int32_t n_tm;              // token-major LIST entries
 };
 
@@ -103,6 +104,7 @@ struct HostTable {
     std::vector<int32_t> map_n, map_t;
     std::vector<int32_t> tm_a, tm_b;
     std::vector<int32_t> ent_n_rc, ent_n_src, ent_t_rc, ent_t_src;
+    std::vector<int32_t> sel_lb;
     bool has_cnt = false;
     bool use_sel = false;
     bool selbit = false;
@@ -154,6 +156,11 @@ int launch_build_transitions(const DevTable &d, const Geometry &g, const float *
                              void *stream);
 int launch_span_tree(const DevTable &d, const Geometry &g, float *tree, int32_t *meta,
                      uint8_t *ws, const WsLayout &w, double *logZ, int32_t *status, void *stream);
+
+// Measurement hook: records the caller's start (begin) or stop event on
+// `stream` when `which` is the kernel selected by fa_profile_kernel.
+// Returns 0 or a hipError_t value.
+int prof_mark(int which, bool begin, void *stream);
 
 // Split of one tree level's products along K (upper levels with few
 // products): 1 = no split.

@@ -650,6 +650,8 @@ int launch_marginals(const DevTable &d, const Geometry &g, const float *p, const
                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)qlds);       \
             if (e != hipSuccess) return (int)e;                                                   \
         }                                                                                         \
+        e = (hipError_t)prof_mark(FA_PROF_MARG_Q, true, stream);                                  \
+        if (e != hipSuccess) return (int)e;                                                       \
         kern<<<qgrid, kQThreads, qlds, st>>>(d, sv, p, logZ, tokens, conf_mode, q, conf, ea, eb, \
                                              pw, w.pw_ld, rcut, status);                          \
     } while (0)
@@ -673,8 +675,12 @@ int launch_marginals(const DevTable &d, const Geometry &g, const float *p, const
             else FA_MARG_QS(4, false, false, false);
         }
 #undef FA_MARG_QS
-        return (int)hipGetLastError();
+        e = hipGetLastError();
+        if (e != hipSuccess) return (int)e;
+        return prof_mark(FA_PROF_MARG_Q, false, stream);
     }
+    e = (hipError_t)prof_mark(FA_PROF_MARG_Q, true, stream);
+    if (e != hipSuccess) return (int)e;
 #define FA_MARG_Q(NG, SB, LA, RG)                                                              \
     marg_q<NG, SB, LA, RG><<<qgrid, kQThreads, 0, st>>>(d, sv, p, logZ, tokens, conf_mode, q,  \
                                                         conf, va, ea, vb, eb, rcut, status)
@@ -698,7 +704,9 @@ int launch_marginals(const DevTable &d, const Geometry &g, const float *p, const
         else FA_MARG_Q(4, false, false, false);
     }
 #undef FA_MARG_Q
-    return (int)hipGetLastError();
+    e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+    return prof_mark(FA_PROF_MARG_Q, false, stream);
 }
 
 }  // namespace fa

@@ -77,6 +77,7 @@ void build_image(HostTable &t)
     append_section(t.image, t.offs, t.ent_n_src);
     append_section(t.image, t.offs, t.ent_t_rc);
     append_section(t.image, t.offs, t.ent_t_src);
+    append_section(t.image, t.offs, t.sel_lb);
     t.image.resize((t.image.size() + 255) & ~size_t(255));
 }
 
@@ -110,7 +111,7 @@ DevTable HostTable::device_view() const
     nxt(d.seg_hi); nxt(d.seg_cnt); nxt(d.seg_lo_cut); nxt(d.seg_hi_cut); nxt(d.cuts);
     nxt(d.cut_off); nxt(d.cut_ev); nxt(d.tok2sel); nxt(d.tok2cut); nxt(d.seg_pair);
     nxt(d.map_n); nxt(d.map_t); nxt(d.tm_a); nxt(d.tm_b);
-    nxt(d.ent_n_rc); nxt(d.ent_n_src); nxt(d.ent_t_rc); nxt(d.ent_t_src);
+    nxt(d.ent_n_rc); nxt(d.ent_n_src); nxt(d.ent_t_rc); nxt(d.ent_t_src); nxt(d.sel_lb);
     d.n_tm = (int32_t)tm_pair.size();
     if (map_n.empty()) {
         d.map_n = nullptr;
@@ -556,6 +557,11 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
     t.selbit = t.ndense() > 0 && t.ndense() < 32 && ns > 0;
     if (t.selbit)
         for (int32_t v : t.sel_tok) t.tokmask[v] |= kSelBit;
+    // first token-list token at or after every multiple of 256 tokens
+    t.sel_lb.resize((size_t)V / 256 + 2);
+    for (size_t k = 0; k < t.sel_lb.size(); ++k)
+        t.sel_lb[k] = (int32_t)(std::lower_bound(t.sel_tok.begin(), t.sel_tok.end(), (int64_t)k * 256) -
+                                t.sel_tok.begin());
     // leaf entries (stored row, column and value source) in both orders
     t.ent_n_rc.clear(); t.ent_n_src.clear(); t.ent_t_rc.clear(); t.ent_t_src.clear();
     if (t.Sp < 65536) {

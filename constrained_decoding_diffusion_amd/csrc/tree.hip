@@ -584,6 +584,10 @@ int launch_span_tree(const DevTable &d, const Geometry &g, float *tree, int32_t 
         const int big_tiles = g.Sp / kBig;
         const long long big_wgs = (long long)g.B * nn * big_tiles * big_tiles;
         const int ks = tree_ksplit(g, k);
+        if (k == 1) {
+            const int pe = prof_mark(FA_PROF_TREE_LEVEL1, true, stream);
+            if (pe) return pe;
+        }
         const int huge_tiles = g.Sp / kHuge;
         const long long huge_wgs = (long long)g.B * nn * huge_tiles * huge_tiles;
         if (ks == 1 && g.Sp % kHuge == 0 && huge_wgs >= 256) {
@@ -603,6 +607,10 @@ int launch_span_tree(const DevTable &d, const Geometry &g, float *tree, int32_t 
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
+        if (k == 1) {
+            const int pe = prof_mark(FA_PROF_TREE_LEVEL1, false, stream);
+            if (pe) return pe;
+        }
     }
     tree_logz<<<g.B, 64, 0, st>>>(d, sv, tree, meta, logZ, status);
     return (int)hipGetLastError();

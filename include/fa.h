@@ -234,6 +234,22 @@ int fa_marginals(const fa_table *t, const float *p, int32_t B, int32_t L, const 
 /* fa_strerror - static description of an error code. */
 const char *fa_strerror(int code);
 
+/* Measurement hook; not part of the method.
+ * fa_profile_kernel - bracket every launch of one kernel with two HIP events
+ *   owned by the caller (hipEvent_t handles passed as void *):
+ *   hipEventRecord(start) just before and hipEventRecord(stop) just after the
+ *   launch, on the stream the launch uses, until cleared with FA_PROF_NONE.
+ *   which:
+ *     FA_PROF_EMISSION_DENSE  dense-mask contraction in fa_build_transitions
+ *     FA_PROF_TREE_LEVEL1     matrix products of the first span-tree level
+ *     FA_PROF_MARG_Q          per-token marginal writer in fa_marginals
+ *   The setting is process-global and unsynchronized: set it from the thread
+ *   that issues the step calls, between calls.
+ * Errors: FA_EINVAL (unknown id, or an event missing for a kernel id).
+ */
+enum { FA_PROF_NONE = 0, FA_PROF_EMISSION_DENSE = 1, FA_PROF_TREE_LEVEL1 = 2, FA_PROF_MARG_Q = 3 };
+int fa_profile_kernel(int32_t which, void *start_event, void *stop_event);
+
 #ifdef __cplusplus
 }
 #endif

@@ -142,3 +142,15 @@ def test_step_calls_need_an_uploaded_table():
     assert rc == _fa.FA_ESTATE
     rc = _fa.lib().fa_span_tree(None, 1, 6, None, None, None, 0, None, None, None)
     assert rc == _fa.FA_EINVAL
+
+
+def test_profile_hook_arguments():
+    lib = _fa.lib()
+    assert lib.fa_profile_kernel(_fa.FA_PROF_NONE, None, None) == _fa.FA_OK
+    assert lib.fa_profile_kernel(_fa.FA_PROF_MARG_Q, None, None) == _fa.FA_EINVAL
+    assert lib.fa_profile_kernel(99, None, None) == _fa.FA_EINVAL
+    assert lib.fa_profile_kernel(-1, None, None) == _fa.FA_EINVAL
+    # a set hook with no GPU work issued is cleared again
+    fake = C.c_void_p(0x1000)
+    assert lib.fa_profile_kernel(_fa.FA_PROF_EMISSION_DENSE, fake, fake) == _fa.FA_OK
+    assert lib.fa_profile_kernel(_fa.FA_PROF_NONE, None, None) == _fa.FA_OK
