@@ -44,6 +44,7 @@ __global__ void marg_init(DevTable d, StepView sv, float *__restrict__ va, int32
 // wavefront order.
 constexpr int kMsgThreads = 1024;
 constexpr int kMsgWaves = kMsgThreads / 64;
+constexpr int kMsgU = 4;  // rows per wavefront per load group
 
 template <int CW>
 __global__ __launch_bounds__(kMsgThreads) void marg_level(
@@ -105,21 +106,45 @@ __global__ __launch_bounds__(kMsgThreads) void marg_level(
         int cj[PER];
 #pragma unroll
         for (int k = 0; k < PER; ++k) cj[k] = co[j0 + k];
-#pragma unroll 4
-        for (int a = wave; a < d.S; a += kMsgWaves) {
-            const float g = gsh[a];
-            if (g == 0.f) continue;
-            const int ra = rsh[a];
-            const float *row = P + (size_t)a * sv.Sp + j0;
-            if constexpr (PER == 4) {
-                const float4 y = *reinterpret_cast<const float4 *>(row);
-                acc[0] += g * scale2(y.x, cj[0] - ra);
-                acc[1] += g * scale2(y.y, cj[1] - ra);
-                acc[2] += g * scale2(y.z, cj[2] - ra);
-                acc[3] += g * scale2(y.w, cj[3] - ra);
-            } else {
-                acc[0] += g * scale2(row[0], cj[0] - ra);
+        // rows a = wave + 16 t of this wavefront, in groups of kMsgU whose
+        // loads are unconditional (clamped) and issued one group ahead.  A
+        // row with zero input weight adds +0: its consumed entries are at
+        // most 1 (the row fold) and an all-zero row stays zero, so every
+        // row is summed, in order, with no data-dependent branch.
+        const int na = (d.S - wave + kMsgWaves - 1) / kMsgWaves;
+        struct Grp {
+            float4 y[kMsgU];
+        };
+        auto ld = [&](Grp &gr, int t) {
+#pragma unroll
+            for (int u = 0; u < kMsgU; ++u) {
+                const int a = min(wave + (t + u) * kMsgWaves, d.S - 1);
+                const float *row = P + (size_t)a * sv.Sp + j0;
+                if constexpr (PER == 4) gr.y[u] = *reinterpret_cast<const float4 *>(row);
+                else gr.y[u].x = row[0];
             }
+        };
+        auto use = [&](const Grp &gr, int t) {
+#pragma unroll
+            for (int u = 0; u < kMsgU; ++u) {
+                const int a = min(wave + (t + u) * kMsgWaves, d.S - 1);
+                const float g = (t + u < na) ? gsh[a] : 0.f;
+                const int ra = rsh[a];
+                acc[0] += g * scale2(gr.y[u].x, cj[0] - ra);
+                if constexpr (PER == 4) {
+                    acc[1] += g * scale2(gr.y[u].y, cj[1] - ra);
+                    acc[2] += g * scale2(gr.y[u].z, cj[2] - ra);
+                    acc[3] += g * scale2(gr.y[u].w, cj[3] - ra);
+                }
+            }
+        };
+        Grp A, B;
+        ld(A, 0);
+        for (int t = 0; t < na; t += 2 * kMsgU) {
+            ld(B, t + kMsgU);
+            use(A, t);
+            ld(A, t + 2 * kMsgU);
+            use(B, t + kMsgU);
         }
     }
 #pragma unroll
