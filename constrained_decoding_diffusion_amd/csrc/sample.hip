@@ -112,72 +112,106 @@ __global__ void sample_root(DevTable d, StepView sv, const float *__restrict__ t
 
 // one midpoint level: node n = nn + idx covers [l, r); children 2n (stored as
 // is) and 2n+1 (stored transposed): both needed vectors are stored rows
-__global__ __launch_bounds__(256) void sample_level(DevTable d, StepView sv,
-                                                    const float *__restrict__ tree,
-                                                    const int32_t *__restrict__ meta,
-                                                    uint64_t seed, int level, int nn,
-                                                    int32_t *__restrict__ zc,
-                                                    int32_t *__restrict__ status)
+// midpoint draw of node n (level `level`, index idx within the level) by
+// one wavefront, given its boundary states; -1 when they are -1 or when every
+// candidate's weight vanishes (then the row is flagged)
+__device__ int draw_mid(const DevTable &d, const StepView &sv, const float *__restrict__ tree,
+                        const int32_t *__restrict__ meta, uint64_t seed, int b, int level, int idx,
+                        int n, int zl, int zr, int lane, int32_t *__restrict__ status)
 {
-    const int lane = threadIdx.x & 63;
-    const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (gw >= sv.B * nn) return;
-    const int b = gw / nn, idx = gw % nn, n = nn + idx;
-    const int span = sv.Lpad / nn, l = idx * span, r = l + span, m = l + span / 2;
-    int32_t *z = zc + (size_t)b * (sv.Lpad + 1);
-    const int zl = z[l], zr = z[r];
     int j = -1;
-    if (zl >= 0 && zr >= 0) {
-        const float *PL = sv.mat_ptr(tree, b, 2 * n) + (size_t)zl * sv.Sp;
-        const float *PR = sv.mat_ptr(tree, b, 2 * n + 1) + (size_t)zr * sv.Sp;
-        const int32_t *coL = sv.meta_ptr(meta, b, 2 * n, 1);
-        const int32_t *coR = sv.meta_ptr(meta, b, 2 * n + 1, 1);
-        auto expo2 = [&](float a, float c, int cl, int cr) {
-            if (!(a > 0.f) || !(c > 0.f) || cl <= kNeg || cr <= kNeg) return kNeg;
-            return fexp(a) + cl + fexp(c) + cr;
-        };
-        const float u = philox_u01(seed, (uint32_t)b, (uint32_t)level, (uint32_t)idx);
-        constexpr int C = 8;
-        if (d.S <= 64 * C) {
-            // every candidate's data in registers: one round of loads
-            float pa[C], pb[C];
-            int ek[C];
+    if (zl < 0 || zr < 0) return -1;
+    const float *PL = sv.mat_ptr(tree, b, 2 * n) + (size_t)zl * sv.Sp;
+    const float *PR = sv.mat_ptr(tree, b, 2 * n + 1) + (size_t)zr * sv.Sp;
+    const int32_t *coL = sv.meta_ptr(meta, b, 2 * n, 1);
+    const int32_t *coR = sv.meta_ptr(meta, b, 2 * n + 1, 1);
+    auto expo2 = [&](float a, float c, int cl, int cr) {
+        if (!(a > 0.f) || !(c > 0.f) || cl <= kNeg || cr <= kNeg) return kNeg;
+        return fexp(a) + cl + fexp(c) + cr;
+    };
+    const float u = philox_u01(seed, (uint32_t)b, (uint32_t)level, (uint32_t)idx);
+    constexpr int C = 8;
+    if (d.S <= 64 * C) {
+        // every candidate's data in registers: one round of loads
+        float pa[C], pb[C];
+        int ek[C];
 #pragma unroll
-            for (int c = 0; c < C; ++c) {
-                const int k = 64 * c + lane;
-                const bool ok = k < d.S;
-                pa[c] = ok ? PL[k] : 0.f;
-                pb[c] = ok ? PR[k] : 0.f;
-                ek[c] = ok ? coL[k] : kNeg;
-                const int cr = ok ? coR[k] : kNeg;
-                ek[c] = expo2(pa[c], pb[c], ek[c], cr);
-            }
-            int e = kNeg;
+        for (int c = 0; c < C; ++c) {
+            const int k = 64 * c + lane;
+            const bool ok = k < d.S;
+            pa[c] = ok ? PL[k] : 0.f;
+            pb[c] = ok ? PR[k] : 0.f;
+            ek[c] = ok ? coL[k] : kNeg;
+            const int cr = ok ? coR[k] : kNeg;
+            ek[c] = expo2(pa[c], pb[c], ek[c], cr);
+        }
+        int e = kNeg;
 #pragma unroll
-            for (int c = 0; c < C; ++c) e = max(e, ek[c]);
-            const int emax = wave_max_i(e);
-            if (emax > kNeg) {
-                float wv[C];
+        for (int c = 0; c < C; ++c) e = max(e, ek[c]);
+        const int emax = wave_max_i(e);
+        if (emax > kNeg) {
+            float wv[C];
 #pragma unroll
-                for (int c = 0; c < C; ++c)
-                    wv[c] = ek[c] > kNeg ? scale2(mant(pa[c]) * mant(pb[c]), ek[c] - emax) : 0.f;
-                j = wave_icdf_regs(wv, d.S, u, lane);
-            }
-        } else {
-            auto expo = [&](int k) { return expo2(PL[k], PR[k], coL[k], coR[k]); };
-            int e = kNeg;
-            for (int k = lane; k < d.S; k += 64) e = max(e, expo(k));
-            const int emax = wave_max_i(e);
-            if (emax > kNeg) {
-                j = wave_icdf(d.S, u, lane, [&](int k) {
-                    const int ek = expo(k);
-                    return ek > kNeg ? scale2(mant(PL[k]) * mant(PR[k]), ek - emax) : 0.f;
-                });
+            for (int c = 0; c < C; ++c)
+                wv[c] = ek[c] > kNeg ? scale2(mant(pa[c]) * mant(pb[c]), ek[c] - emax) : 0.f;
+            j = wave_icdf_regs(wv, d.S, u, lane);
+        }
+    } else {
+        auto expo = [&](int k) { return expo2(PL[k], PR[k], coL[k], coR[k]); };
+        int e = kNeg;
+        for (int k = lane; k < d.S; k += 64) e = max(e, expo(k));
+        const int emax = wave_max_i(e);
+        if (emax > kNeg) {
+            j = wave_icdf(d.S, u, lane, [&](int k) {
+                const int ek = expo(k);
+                return ek > kNeg ? scale2(mant(PL[k]) * mant(PR[k]), ek - emax) : 0.f;
+            });
+        }
+    }
+    if (j < 0 && lane == 0) atomicOr(&status[b], (int)FA_ROW_UNDERFLOW);
+    return j;
+}
+
+// Midpoints of `depth` (<= kSubDepth) consecutive levels from level0, one
+// subtree per workgroup: at sub-level t wavefront w < 2^t draws node w of the
+// subtree.  The subtree's boundary states stay in LDS between sub-levels
+// (slot q holds position l0 + q * span0 / 2^depth); each draw is also written
+// to zc.
+constexpr int kSubDepth = 3;
+
+__global__ __launch_bounds__(64 << (kSubDepth - 1)) void sample_levels(
+    DevTable d, StepView sv, const float *__restrict__ tree, const int32_t *__restrict__ meta,
+    uint64_t seed, int level0, int depth, int32_t *__restrict__ zc, int32_t *__restrict__ status)
+{
+    __shared__ int zs[(1 << kSubDepth) + 1];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nn0 = 1 << (level0 - 1);
+    const int b = blockIdx.x / nn0, idx0 = blockIdx.x % nn0;
+    const int span0 = sv.Lpad / nn0;
+    const int q = 1 << depth;
+    const int unit = span0 / q;
+    const int l0 = idx0 * span0;
+    int32_t *z = zc + (size_t)b * (sv.Lpad + 1);
+    if (threadIdx.x == 0) {
+        zs[0] = z[l0];
+        zs[q] = z[l0 + span0];
+    }
+    __syncthreads();
+    for (int t = 0; t < depth; ++t) {
+        if (wave < (1 << t)) {
+            const int width = q >> t;
+            const int ql = wave * width, qm = ql + width / 2;
+            const int nn = nn0 << t;
+            const int idx = (idx0 << t) + wave;
+            const int j = draw_mid(d, sv, tree, meta, seed, b, level0 + t, idx, nn + idx, zs[ql],
+                                   zs[ql + width], lane, status);
+            if (lane == 0) {
+                zs[qm] = j;
+                z[l0 + qm * unit] = j;
             }
         }
-        if (j < 0 && lane == 0) atomicOr(&status[b], (int)FA_ROW_UNDERFLOW);
+        __syncthreads();
     }
-    if (lane == 0) z[m] = j;
 }
 
 constexpr int kTokThreads = 256;
@@ -484,10 +518,11 @@ int launch_sample(const DevTable &d, const Geometry &g, const float *p, const fl
     sample_root<<<g.B, 64, 0, st>>>(d, sv, tree, meta, seed, zc, status);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
-    for (int level = 1; level <= g.K; ++level) {
-        const int nn = 1 << (level - 1);
-        const int waves = g.B * nn;
-        sample_level<<<(waves + 3) / 4, 256, 0, st>>>(d, sv, tree, meta, seed, level, nn, zc, status);
+    for (int level0 = 1; level0 <= g.K; level0 += kSubDepth) {
+        const int depth = std::min(kSubDepth, g.K - level0 + 1);
+        const int nn0 = 1 << (level0 - 1);
+        sample_levels<<<g.B * nn0, 64 << (kSubDepth - 1), 0, st>>>(d, sv, tree, meta, seed, level0,
+                                                                    depth, zc, status);
         e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
     }
