@@ -287,21 +287,31 @@ __device__ inline float pair_value(const DevTable &d, int q, size_t pos, const E
             acc += (cp[d.seg_hi_cut[k]] - cp[d.seg_lo_cut[k]]) * (double)d.seg_cnt[k];
         return (float)acc;
     }
+    // blocked sum: kListBlock terms at a time, then the block sums in order.
+    // A single running fp32 sum over a long label drops terms that fall
+    // below half an ulp of the total (a systematic loss when p decays along
+    // the label); blocks keep each addition between similar magnitudes.
+    constexpr int kListBlock = 64;
     float acc = 0.f;
     const int k0 = d.list_off[q], k1 = d.list_off[q + 1];
-    if (d.use_sel) {
-        const float *src = s.psel + pos * d.nsel;
-        if (d.list_cnt)
-            for (int k = k0; k < k1; ++k) acc += src[d.list_sel[k]] * d.list_cnt[k];
-        else
-            for (int k = k0; k < k1; ++k) acc += src[d.list_sel[k]];
-    } else {
-        const float *src = s.p + pos * d.V;
-        for (int k = k0; k < k1; ++k) {
-            const float x = src[d.list_tok[k]];
-            bad |= !(x >= 0.f);
-            acc += d.list_cnt ? x * d.list_cnt[k] : x;
+    for (int kb = k0; kb < k1; kb += kListBlock) {
+        const int ke = min(k1, kb + kListBlock);
+        float blk = 0.f;
+        if (d.use_sel) {
+            const float *src = s.psel + pos * d.nsel;
+            if (d.list_cnt)
+                for (int k = kb; k < ke; ++k) blk += src[d.list_sel[k]] * d.list_cnt[k];
+            else
+                for (int k = kb; k < ke; ++k) blk += src[d.list_sel[k]];
+        } else {
+            const float *src = s.p + pos * d.V;
+            for (int k = kb; k < ke; ++k) {
+                const float x = src[d.list_tok[k]];
+                bad |= !(x >= 0.f);
+                blk += d.list_cnt ? x * d.list_cnt[k] : x;
+            }
         }
+        acc += blk;
     }
     return acc;
 }

@@ -150,7 +150,7 @@ int tree_ksplit(const Geometry &g, int level)
     // of the 256 compute units idle
     const long long nn = g.Lpad >> level;
     const long long big = (long long)g.B * nn * (g.Sp / 128) * (g.Sp / 128);
-    if (g.Sp % 128 == 0 && big >= 512) return 1;
+    if (g.Sp % 128 == 0 && big >= 256) return 1;
     const long long small = (long long)g.B * nn * (g.Sp / 64) * (g.Sp / 64);
     int s = 1;
     // the split must divide the K blocks of 64 exactly

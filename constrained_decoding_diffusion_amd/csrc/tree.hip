@@ -592,7 +592,7 @@ int launch_span_tree(const DevTable &d, const Geometry &g, float *tree, int32_t 
         const long long huge_wgs = (long long)g.B * nn * huge_tiles * huge_tiles;
         if (ks == 1 && g.Sp % kHuge == 0 && huge_wgs >= 256) {
             span_gemm256<<<(unsigned)huge_wgs, kHugeThreads, 0, st>>>(sv, tree, meta, n0, nn);
-        } else if (ks == 1 && g.Sp % kBig == 0 && big_wgs >= 512) {
+        } else if (ks == 1 && g.Sp % kBig == 0 && big_wgs >= 256) {
             span_gemm128<<<(unsigned)big_wgs, kBigThreads, 0, st>>>(sv, tree, meta, n0, nn);
         } else {
             float *part = (float *)(ws + w.kpart);

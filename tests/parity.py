@@ -29,11 +29,11 @@ def log(msg):
     sys.stdout.flush()
 
 
-def run_gpu(w, conf_mode=0, write_q=True, table=None):
+def run_gpu(w, conf_mode=0, write_q=True, table=None, p_dev=None):
     import torch
     import constrained_decoding_diffusion_amd as fa
     tb = table or fa.Table.from_automaton(w.aut)
-    p = torch.from_numpy(w.p).cuda()
+    p = p_dev if p_dev is not None else torch.from_numpy(w.p).cuda()
     bufs = fa.step(tb, p, w.seed, conf_mode=conf_mode, write_q=write_q)
     torch.cuda.synchronize()
     out = dict(table=tb, bufs=bufs,
@@ -91,12 +91,28 @@ def check_row(w, g, b, orc=None, q_positions=None, check_q=True, conf_mode=0):
     return rep
 
 
+LEAF_RTOL = 1e-5
+LEAF_BIAS = 1e-6
+
+
 def check_leaves(w, g, b, positions, orc=None):
+    """Every leaf entry within LEAF_RTOL of the oracle's M_i, and no
+    systematic drift: the mass-weighted relative error of each leaf,
+    sum(M_gpu - M) / sum(M), averaged over the positions, stays within
+    LEAF_BIAS.  A drift compounds along the chain of products (-2e-6 per
+    position reached 1e-4 in the marginals after 16 positions), so it is
+    checked on its own."""
     orc = orc or oracle.Oracle(w.aut)
     tb = g["table"]
     orig = tb.orig
     W = orc.edge_weights(w.p[b])
+    drift = []
     for i in positions:
         M = orc.dense_M(W, i)[np.ix_(orig, orig)]
         Mg = leaf(w, g, b, i)
-        np.testing.assert_allclose(Mg, M, rtol=1e-5, atol=1e-30)
+        np.testing.assert_allclose(Mg, M, rtol=LEAF_RTOL, atol=1e-30)
+        if M.sum() > 0:
+            drift.append(float((Mg - M).sum() / M.sum()))
+    if drift:
+        bias = float(np.mean(drift))
+        assert abs(bias) <= LEAF_BIAS, f"row {b}: leaf drift {bias:.3g}"

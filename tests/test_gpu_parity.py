@@ -34,6 +34,28 @@ def _nfa_small():
     return configs.from_automaton(aut, 2, 21, "normal4", 0, 7500, "nfa small")
 
 
+def _json_odd_v():
+    # V % 4 != 0: scalar dense-mask loads, the chunked token draw and the
+    # general q writer
+    aut = configs._draw(lambda r: A.json_like_dfa(r, S=120, V=9999, pool=128, string_size=6000),
+                        7601, 23)
+    return configs.from_automaton(aut, 2, 23, "normal4_zipf", 3, 7700, "json-like odd V")
+
+
+def _json_many_list_tokens():
+    # more than 64 token-list tokens per V chunk: their copy is gathered from p
+    aut = configs._draw(lambda r: A.json_like_dfa(r, S=96, V=20000, pool=6000, max_struct=64,
+                                                  string_size=12000), 7801, 19)
+    return configs.from_automaton(aut, 3, 19, "normal4_zipf", 0, 7900, "json-like many list tokens")
+
+
+def _json_32_dense():
+    # 32 dense-mask pairs: no flag bit is left for token-list tokens
+    aut = configs._draw(lambda r: A.json_like_dfa(r, S=400, V=8000, string_frac=0.1, pool=200,
+                                                  string_size=5000), 8001, 17)
+    return configs.from_automaton(aut, 2, 17, "normal4_zipf", 2, 8100, "json-like 32 dense")
+
+
 CASES = {
     "real-number": lambda: configs.make(1),
     "random-dfa": lambda: configs.make(2),
@@ -42,6 +64,9 @@ CASES = {
     "nfa-small": _nfa_small,
     "real-L1": lambda: configs.make(1, L=1),
     "random-dfa-L3": lambda: configs.make(2, L=3, B=2),
+    "json-odd-V": _json_odd_v,
+    "json-many-list-tokens": _json_many_list_tokens,
+    "json-32-dense": _json_32_dense,
 }
 
 
@@ -158,3 +183,19 @@ def test_empty_inputs():
     assert (bufs.logZ.cpu().numpy() == -np.inf).all()
     assert (bufs.status.cpu().numpy() & 1).all()
     assert (bufs.states.cpu().numpy() == -1).all()
+
+
+def test_misaligned_probabilities():
+    """p at a 4-byte offset from a 16-byte boundary takes the scalar load
+    paths; the step still matches the oracle."""
+    import torch
+    w = _json_small()
+    PT.log("[parity] misaligned p")
+    base = torch.empty(w.p.size + 1, dtype=torch.float32, device="cuda")
+    p = base[1:].view(w.p.shape)
+    p.copy_(torch.from_numpy(w.p))
+    assert p.data_ptr() % 16 != 0
+    g = PT.run_gpu(w, p_dev=p)
+    orc = oracle.Oracle(w.aut)
+    for b in range(w.B):
+        PT.check_row(w, g, b, orc)
