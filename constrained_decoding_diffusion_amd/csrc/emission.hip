@@ -72,9 +72,12 @@ __global__ __launch_bounds__(kDenseThreads) void emission_dense(
     for (int k = 0; k < 8; ++k)
         prow[k] = p + (size_t)min(pos0 + 4 * k + wave, npos - 1) * d.V;
     int bad = 0;
-    f32x16 acc;
+    // the MFMA chain covers two steps (128 terms per output and wavefront);
+    // its sum then goes into a separate total, so a long chunk is not one
+    // running fp32 sum that drops terms far below its own ulp
+    f32x16 acc, tot;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    for (int r = 0; r < 16; ++r) acc[r] = tot[r] = 0.f;
     struct Step {
         float4 x[8];
         uint32_t m;
@@ -177,13 +180,18 @@ __global__ __launch_bounds__(kDenseThreads) void emission_dense(
     for (int s = 0; s < nsteps; s += 2) {
         step(s, sb, 0);
         step(s + 1, sa, 1);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            tot[r] += acc[r];
+            acc[r] = 0.f;
+        }
     }
     // sum the four waves' tiles in wave order (reusing the staging LDS)
     float *red = &pt[0][0][0];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int i = (r >> 2) * 8 + half * 4 + (r & 3);
-        red[wave * (kDenseTile * kDenseTile) + i * kDenseTile + l32] = acc[r];
+        red[wave * (kDenseTile * kDenseTile) + i * kDenseTile + l32] = tot[r];
     }
     __syncthreads();
     float *outp = dpart + ((size_t)chunk * BLpad + pos0) * kDenseMax;

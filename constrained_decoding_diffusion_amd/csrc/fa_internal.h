@@ -144,6 +144,7 @@ struct WsLayout {
     size_t va = 0, ea = 0, vb = 0, eb = 0;     // marginals: messages
     size_t rcut = 0;                           // marginals: range weights per cut
     size_t pw = 0;                             // marginals: per-position pair weights
+    size_t hpart = 0;                          // marginals: q ln q partial sums per row part
     int32_t pw_nl = 0, pw_ld = 0;              // token-list weights per row, row length
     size_t total = 0;
 };

@@ -191,6 +191,7 @@ __global__ void marg_rcut(DevTable d, StepView sv, const float *__restrict__ va,
 
 constexpr int kQThreads = 256;
 constexpr size_t kQLdsMax = 64 * 1024;  // LDS lookup tables of the streaming q writer
+constexpr int kQParts = 4;              // workgroups per position of the streaming q writer
 
 // LIST weight of selected token s: sum over its token-major entries
 __device__ inline float list_weight(const DevTable &d, int s, const float *al, const float *be)
@@ -429,8 +430,10 @@ __global__ __launch_bounds__(kPwThreads) void marg_pairw(DevTable d, StepView sv
     for (int s = tid; s < nl; s += kPwThreads) out[kDenseMax + s] = rs[s];
 }
 
-// Streaming q writer (V % 4 == 0, lookup tables in LDS).  One workgroup per
-// position; each thread handles U float4 groups per iteration.  Every global
+// Streaming q writer (V % 4 == 0, lookup tables in LDS).  kQParts
+// workgroups per position, consecutive in the grid, each over one
+// contiguous part of the row (adjacent workgroups stream adjacent memory);
+// each thread handles U float4 groups per iteration.  Every global
 // load of the loop is unconditional (clamped index) and issued one iteration
 // ahead, and the per-token weight reads LDS only: the dense-mask lookup
 // table, the token-list weights (found by binary search over the sorted
@@ -442,25 +445,31 @@ __global__ __launch_bounds__(kQThreads) void marg_q_stream(
     const int32_t *__restrict__ tokens, int conf_mode, float *__restrict__ q,
     float *__restrict__ conf, const int32_t *__restrict__ ea, const int32_t *__restrict__ eb,
     const float *__restrict__ pw, int pw_ld, const float *__restrict__ rcut,
-    const int32_t *__restrict__ status)
+    double *__restrict__ hpart, const int32_t *__restrict__ status)
 {
     constexpr bool LISTS = SELBIT || LISTALL;
     constexpr bool MASK = NG > 0 || SELBIT;
     extern __shared__ float dyn[];  // rsel [nsel] | selk [nsel] | rcl [ncut]
     __shared__ float lut[NG > 0 ? NG : 1][256];
     __shared__ double sh_h[4];
-    const int b = blockIdx.y, i = blockIdx.x;
+    const int b = blockIdx.y, i = blockIdx.x / kQParts, part = blockIdx.x % kQParts;
     const size_t pos = (size_t)b * sv.L + i;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float *prow = p + pos * d.V;
     float *qrow = q ? q + pos * d.V : nullptr;
+    // this part's float4 groups [k_lo, k_hi) of the row
+    const int n4 = d.V >> 2;
+    const int per = (n4 + kQParts - 1) / kQParts;
+    const int k_lo = min(n4, part * per), k_hi = min(n4, k_lo + per);
     const double lz = logZ[b];
     const int e1 = ea[(size_t)b * (sv.Lpad + 1) + i], e2 = eb[(size_t)b * (sv.Lpad + 1) + i + 1];
     const bool ok = status[b] == 0 && lz > -INFINITY && e1 > kNeg && e2 > kNeg;
+    const bool negent = conf_mode == FA_CONF_NEGENT;
     if (!ok) {
         if (qrow)
-            for (int v = tid; v < d.V; v += kQThreads) qrow[v] = 0.f;
-        if (tid == 0) conf[pos] = -INFINITY;
+            for (int v = 4 * k_lo + tid; v < 4 * k_hi; v += kQThreads) qrow[v] = 0.f;
+        if (tid == 0 && negent) hpart[pos * kQParts + part] = -INFINITY;
+        if (tid == 0 && part == 0) conf[pos] = -INFINITY;
         return;
     }
     const double factor = exp2((double)e1 + (double)e2 - lz * 1.4426950408889634074);
@@ -512,10 +521,9 @@ __global__ __launch_bounds__(kQThreads) void marg_q_stream(
     auto qval = [&](float x, float r) -> float {
         return (r > 0.f && x > 0.f) ? (float)((double)x * (double)r * factor) : 0.f;
     };
-    const bool negent = conf_mode == FA_CONF_NEGENT;
     if (!qrow && !negent) {
         // only the sampled token's marginal is needed
-        if (tid == 0) {
+        if (tid == 0 && part == 0) {
             float o = -INFINITY;
             if (tok >= 0)
                 o = qval(prow[tok], weight_r(tok, MASK ? d.tokmask[tok] : 0u,
@@ -532,8 +540,7 @@ __global__ __launch_bounds__(kQThreads) void marg_q_stream(
     const int4 *s4 = reinterpret_cast<const int4 *>(d.tok2sel);
     const int4 *c4 = reinterpret_cast<const int4 *>(d.tok2cut);
     float4 *q4 = reinterpret_cast<float4 *>(qrow);
-    const int n4 = d.V >> 2;
-    const int iters = (n4 + kPer - 1) / kPer;
+    const int iters = (k_hi - k_lo + kPer - 1) / kPer;
     struct Buf {
         float4 x[U];
         uint4 m[U];
@@ -543,7 +550,7 @@ __global__ __launch_bounds__(kQThreads) void marg_q_stream(
     auto load = [&](Buf &bf, int it) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int k = min(it * kPer + u * kQThreads + tid, n4 - 1);
+            const int k = min(k_lo + it * kPer + u * kQThreads + tid, k_hi - 1);
             bf.x[u] = p4[k];
             if constexpr (MASK) bf.m[u] = m4[k];
             if constexpr (LISTALL) bf.sl[u] = s4[k];
@@ -556,8 +563,8 @@ __global__ __launch_bounds__(kQThreads) void marg_q_stream(
     auto compute = [&](const Buf &bf, int it) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int k = it * kPer + u * kQThreads + tid;
-            const int v = 4 * min(k, n4 - 1);
+            const int k = k_lo + it * kPer + u * kQThreads + tid;
+            const int v = 4 * min(k, k_hi - 1);
             const uint4 m = MASK ? bf.m[u] : make_uint4(0u, 0u, 0u, 0u);
             const int4 sl = LISTALL ? bf.sl[u] : make_int4(-1, -1, -1, -1);
             const int4 c = RANGES ? bf.c[u] : make_int4(-1, -1, -1, -1);
@@ -566,7 +573,7 @@ __global__ __launch_bounds__(kQThreads) void marg_q_stream(
             o.y = qval(bf.x[u].y, weight_r(v + 1, m.y, sl.y, c.y));
             o.z = qval(bf.x[u].z, weight_r(v + 2, m.z, sl.z, c.z));
             o.w = qval(bf.x[u].w, weight_r(v + 3, m.w, sl.w, c.w));
-            if (k < n4) {
+            if (k < k_hi) {
                 if (q4) q4[k] = o;
                 if (tok >= v && tok < v + 4) {
                     have_tok = true;
@@ -581,25 +588,39 @@ __global__ __launch_bounds__(kQThreads) void marg_q_stream(
             }
         }
     };
-    Buf A, Bn;
-    load(A, 0);
-    // iteration it sits in A (even) or Bn (odd); loads past the row re-read
-    // its last group and an odd count gets one empty iteration
-    for (int it = 0; it < iters; it += 2) {
-        load(Bn, it + 1);
-        compute(A, it);
-        load(A, it + 2);
-        compute(Bn, it + 1);
+    if (k_hi > k_lo) {
+        Buf A, Bn;
+        load(A, 0);
+        // iteration it sits in A (even) or Bn (odd); loads past the part
+        // re-read its last group and an odd count gets one empty iteration
+        for (int it = 0; it < iters; it += 2) {
+            load(Bn, it + 1);
+            compute(A, it);
+            load(A, it + 2);
+            compute(Bn, it + 1);
+        }
     }
     if (negent) {
         hsum = wave_sum_d(hsum);
         if (lane == 0) sh_h[wave] = hsum;
         __syncthreads();
-        if (tid == 0) conf[pos] = (float)(((sh_h[0] + sh_h[1]) + sh_h[2]) + sh_h[3]);
+        if (tid == 0) hpart[pos * kQParts + part] = ((sh_h[0] + sh_h[1]) + sh_h[2]) + sh_h[3];
     } else {
         if (have_tok) conf[pos] = tokq;
-        if (tid == 0 && tok < 0) conf[pos] = -INFINITY;
+        if (tid == 0 && part == 0 && tok < 0) conf[pos] = -INFINITY;
     }
+}
+
+// NEGENT confidence of the streaming q writer: the parts' fp64 sums of
+// q ln q, added in part order (a failed row's parts hold -inf)
+__global__ void marg_negent_sum(int npos, const double *__restrict__ hpart,
+                                float *__restrict__ conf)
+{
+    const int pos = blockIdx.x * blockDim.x + threadIdx.x;
+    if (pos >= npos) return;
+    double s = 0.0;
+    for (int k = 0; k < kQParts; ++k) s += hpart[(size_t)pos * kQParts + k];
+    conf[pos] = (float)s;
 }
 
 }  // namespace
@@ -658,6 +679,8 @@ int launch_marginals(const DevTable &d, const Geometry &g, const float *p, const
     if (streamed) {
         const int npos = g.B * g.L;
         float *pw = (float *)(ws + w.pw);
+        double *hpart = (double *)(ws + w.hpart);
+        const dim3 sgrid(g.L * kQParts, g.B);
         const size_t plds = w.pw_nl ? ((size_t)std::min(d.n_tm, kPwChunk) + w.pw_nl) * 4 : 0;
         if (plds > 48 * 1024) {
             e = hipFuncSetAttribute(reinterpret_cast<const void *>(&marg_pairw),
@@ -677,8 +700,8 @@ int launch_marginals(const DevTable &d, const Geometry &g, const float *p, const
         }                                                                                         \
         e = (hipError_t)prof_mark(FA_PROF_MARG_Q, true, stream);                                  \
         if (e != hipSuccess) return (int)e;                                                       \
-        kern<<<qgrid, kQThreads, qlds, st>>>(d, sv, p, logZ, tokens, conf_mode, q, conf, ea, eb, \
-                                             pw, w.pw_ld, rcut, status);                          \
+        kern<<<sgrid, kQThreads, qlds, st>>>(d, sv, p, logZ, tokens, conf_mode, q, conf, ea, eb, \
+                                             pw, w.pw_ld, rcut, hpart, status);                   \
     } while (0)
         if (ranges) {
             if (listall) FA_MARG_QS(0, false, true, true);
@@ -702,7 +725,13 @@ int launch_marginals(const DevTable &d, const Geometry &g, const float *p, const
 #undef FA_MARG_QS
         e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
-        return prof_mark(FA_PROF_MARG_Q, false, stream);
+        const int pe = prof_mark(FA_PROF_MARG_Q, false, stream);
+        if (pe) return pe;
+        if (conf_mode == FA_CONF_NEGENT) {
+            marg_negent_sum<<<(npos + 255) / 256, 256, 0, st>>>(npos, hpart, conf);
+            e = hipGetLastError();
+        }
+        return (int)e;
     }
     e = (hipError_t)prof_mark(FA_PROF_MARG_Q, true, stream);
     if (e != hipSuccess) return (int)e;

@@ -222,6 +222,7 @@ WsLayout ws_layout(const HostTable &t, const Geometry &g)
     w.pw_nl = t.nsel() <= kSelMax ? t.nsel() : 0;
     w.pw_ld = (kDenseMax + w.pw_nl + 3) & ~3;
     w.pw = o; o = al(o + BL * (size_t)w.pw_ld * sizeof(float));
+    w.hpart = o; o = al(o + BL * 4 * sizeof(double));  // the q writer's row parts
     size_t a4 = o;
     w.total = std::max(std::max(a1, a2), std::max(a3, a4));
     if (w.total == 0) w.total = 256;
