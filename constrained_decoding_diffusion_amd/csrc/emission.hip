@@ -6,11 +6,14 @@
 // Up to three kernels, by label class:
 //  * emission_dense: pairs whose labels are large token sets (dense masks).
 //    Their sums form a contraction  D[j][pos] = sum_v mask[j][v] p[pos][v]
-//    with a 0/1 operand; it runs on fp32 MFMA (32 pairs x 32 positions per
-//    tile, K = tokens), V split over workgroups into chunks (sized so the
+//    with a 0/1 operand.  It runs on bf16 MFMA (32 pairs x 32 positions per
+//    tile, K = tokens) without rounding any term: each p value is cut into
+//    three bf16 pieces that add up to it exactly, so every product with a
+//    0/1 mask value is exact, and each short MFMA chain is added into an
+//    fp32 total.  V is split over workgroups into chunks (sized so the
 //    workgroups fill whole rounds of the chip) whose partials are summed in
-//    chunk order.  The same pass copies p at the
-//    tokens that token-list pairs use (a compact gather source).
+//    chunk order.  The same pass copies p at the tokens that token-list
+//    pairs use (a compact gather source).
 //  * emission_ranges: one workgroup per position streams the row and keeps
 //    an fp64 running prefix sum at every range cut point.
 //  * emission_densify: one wavefront per stored leaf row evaluates the pair
@@ -18,20 +21,45 @@
 //    zeros included, with its power-of-two row exponent.  Odd leaves are
 //    stored transposed, so their stored rows are the columns of M_i.
 #include "device_common.h"
+#include "pair_value.h"
 
 namespace fa {
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
+{
+    const u32x4 v = {a, b, c, d};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// the upper halves of two words, a's in the low half: two bf16 values
+__device__ inline uint32_t upper_halves(uint32_t a, uint32_t b)
+{
+    return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// 0xffffffff when bit k of w is set, else 0
+__device__ inline uint32_t bit_fill(uint32_t w, int k)
+{
+    return (uint32_t)__builtin_amdgcn_sbfe((int)w, k, 1);
+}
 
 constexpr int kDenseThreads = 256;
 constexpr int kSub = 256;         // tokens staged per step
 constexpr int kSubLd = kSub + 4;  // padded LDS row
 
 // One workgroup: 32 positions x one V chunk (a multiple of 256 tokens).
-// Tokens are staged 256 at a time through double-buffered LDS; each of the
-// four waves runs the MFMAs of 64 tokens per step into its own 32x32 tile,
-// and the four tiles are summed at the end.  Every global load of the loop
+// Tokens are staged 256 at a time through double-buffered LDS (every
+// wavefront load reads 1 KB of one row); each of the four waves runs the
+// MFMAs of 64 tokens per step into its own 32x32 tile, and the four tiles
+// are summed at the end.  A value x is cut as x = hi + mid + lo, each an
+// exact bf16: hi is the top half of x's bits, mid the top half of x - hi,
+// lo the rest (at most 8 significant bits); the three pieces share the mask
+// operand (1.0 or 0).  Every global load of the loop
 // is unconditional (out-of-range elements read an in-range address and are
 // zeroed when stored to LDS), so the loop has a fixed number of memory
 // operations per step and the loads of step s+2 stay in flight while step s
@@ -72,12 +100,9 @@ __global__ __launch_bounds__(kDenseThreads) void emission_dense(
     for (int k = 0; k < 8; ++k)
         prow[k] = p + (size_t)min(pos0 + 4 * k + wave, npos - 1) * d.V;
     int bad = 0;
-    // the MFMA chain covers two steps (128 terms per output and wavefront);
-    // its sum then goes into a separate total, so a long chunk is not one
-    // running fp32 sum that drops terms far below its own ulp
-    f32x16 acc, tot;
+    f32x16 tot, zero16;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = tot[r] = 0.f;
+    for (int r = 0; r < 16; ++r) tot[r] = zero16[r] = 0.f;
     struct Step {
         float4 x[8];
         uint32_t m;
@@ -150,15 +175,45 @@ __global__ __launch_bounds__(kDenseThreads) void emission_dense(
     auto step = [&](int s, Step &next, int buf) {
         const float *brow = &pt[buf][l32][64 * wave + 32 * half];
         const uint32_t *mrow = &mk[buf][64 * wave + 32 * half];
+        // k-slot v of this lane half is token 8q + v of its 32; the mask
+        // operand is the same for the three pieces
+        f32x16 acc;
 #pragma unroll
-        for (int t = 0; t < 32; t += 4) {
-            const float4 bq = *reinterpret_cast<const float4 *>(brow + t);
-            const uint4 mq = *reinterpret_cast<const uint4 *>(mrow + t);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32((float)((mq.x >> l32) & 1u), bq.x, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32((float)((mq.y >> l32) & 1u), bq.y, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32((float)((mq.z >> l32) & 1u), bq.z, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32((float)((mq.w >> l32) & 1u), bq.w, acc, 0, 0, 0);
+        for (int q = 0; q < 4; ++q) {
+            const float4 x0 = *reinterpret_cast<const float4 *>(brow + 8 * q);
+            const float4 x1 = *reinterpret_cast<const float4 *>(brow + 8 * q + 4);
+            const uint4 m0 = *reinterpret_cast<const uint4 *>(mrow + 8 * q);
+            const uint4 m1 = *reinterpret_cast<const uint4 *>(mrow + 8 * q + 4);
+            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            const uint32_t ms[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+            uint32_t ub[8], rb[8], lb[8];
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+                ub[v] = __float_as_uint(xs[v]);
+                const float r = xs[v] - __uint_as_float(ub[v] & 0xFFFF0000u);
+                rb[v] = __float_as_uint(r);
+                lb[v] = __float_as_uint(r - __uint_as_float(rb[v] & 0xFFFF0000u));
+            }
+            uint32_t am[4], bh[4], bm[4], bl[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                am[j] = (bit_fill(ms[2 * j], l32) & 0x3F80u) | (bit_fill(ms[2 * j + 1], l32) & 0x3F800000u);
+                bh[j] = upper_halves(ub[2 * j], ub[2 * j + 1]);
+                bm[j] = upper_halves(rb[2 * j], rb[2 * j + 1]);
+                bl[j] = upper_halves(lb[2 * j], lb[2 * j + 1]);
+            }
+            const bf16x8 A = as_bf16x8(am[0], am[1], am[2], am[3]);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, as_bf16x8(bh[0], bh[1], bh[2], bh[3]),
+                                                          q == 0 ? zero16 : acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, as_bf16x8(bm[0], bm[1], bm[2], bm[3]),
+                                                          acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, as_bf16x8(bl[0], bl[1], bl[2], bl[3]),
+                                                          acc, 0, 0, 0);
         }
+        // the step's twelve-MFMA chain goes into the total, so no long fp32
+        // chain drops terms far below its own ulp
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tot[r] += acc[r];
         if (SEL == 1 && s < nsteps) {
             const int j0 = sel_at[s] - sel_at[0], n = sel_at[s + 1] - sel_at[s];
             for (int i = tid; i < n * kDenseTile; i += kDenseThreads) {
@@ -180,11 +235,6 @@ __global__ __launch_bounds__(kDenseThreads) void emission_dense(
     for (int s = 0; s < nsteps; s += 2) {
         step(s, sb, 0);
         step(s + 1, sa, 1);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            tot[r] += acc[r];
-            acc[r] = 0.f;
-        }
     }
     // sum the four waves' tiles in wave order (reusing the staging LDS)
     float *red = &pt[0][0][0];
@@ -270,58 +320,6 @@ __global__ __launch_bounds__(kStreamThreads) void emission_ranges(
     if (bad) atomicOr(&sh_bad, 1);
     __syncthreads();
     if (tid == 0 && sh_bad) atomicOr(&status[pos / L], (int)FA_ROW_BADPROB);
-}
-
-struct EmitSrc {
-    const float *p;
-    const float *dpart;
-    const float *dval;  // [npos][kDenseMax] chunk sums of the dense-mask pairs
-    const float *psel;
-    const double *cutp;
-    int n_vchunks;
-    int BLpad;
-};
-
-// value of pair q at position pos
-__device__ inline float pair_value(const DevTable &d, int q, size_t pos, const EmitSrc &s,
-                                   int &bad)
-{
-    const int cls = d.pair_cls[q];
-    if (cls == kDense) return s.dval[pos * kDenseMax + d.pair_aux[q]];
-    if (cls == kRange) {
-        double acc = 0.0;
-        const double *cp = s.cutp + pos * d.ncut;
-        for (int k = d.seg_off[q]; k < d.seg_off[q + 1]; ++k)
-            acc += (cp[d.seg_hi_cut[k]] - cp[d.seg_lo_cut[k]]) * (double)d.seg_cnt[k];
-        return (float)acc;
-    }
-    // blocked sum: kListBlock terms at a time, then the block sums in order.
-    // A single running fp32 sum over a long label drops terms that fall
-    // below half an ulp of the total (a systematic loss when p decays along
-    // the label); blocks keep each addition between similar magnitudes.
-    constexpr int kListBlock = 64;
-    float acc = 0.f;
-    const int k0 = d.list_off[q], k1 = d.list_off[q + 1];
-    for (int kb = k0; kb < k1; kb += kListBlock) {
-        const int ke = min(k1, kb + kListBlock);
-        float blk = 0.f;
-        if (d.use_sel) {
-            const float *src = s.psel + pos * d.nsel;
-            if (d.list_cnt)
-                for (int k = kb; k < ke; ++k) blk += src[d.list_sel[k]] * d.list_cnt[k];
-            else
-                for (int k = kb; k < ke; ++k) blk += src[d.list_sel[k]];
-        } else {
-            const float *src = s.p + pos * d.V;
-            for (int k = kb; k < ke; ++k) {
-                const float x = src[d.list_tok[k]];
-                bad |= !(x >= 0.f);
-                blk += d.list_cnt ? x * d.list_cnt[k] : x;
-            }
-        }
-        acc += blk;
-    }
-    return acc;
 }
 
 // dense-mask pair sums: add the V-chunk partials of one (position, pair) in
@@ -465,41 +463,17 @@ __global__ __launch_bounds__(kDensifyThreads) void emission_densify(
     }
 }
 
-// value of pair q at position pos, with a dense-mask pair's V-chunk partials
-// added here in chunk order
-__device__ inline float pair_value_direct(const DevTable &d, int q, size_t pos, const EmitSrc &s,
-                                          int &bad)
-{
-    if (d.pair_cls[q] == kDense) {
-        const int j = d.pair_aux[q];
-        const float *dp = s.dpart + pos * kDenseMax + j;
-        const size_t cs = (size_t)s.BLpad * kDenseMax;  // chunk stride
-        float acc = 0.f;
-        int c = 0;
-        // eight partials loaded together, then added in chunk order
-        for (; c + 8 <= s.n_vchunks; c += 8) {
-            float t[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) t[u] = dp[(size_t)(c + u) * cs];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) acc += t[u];
-        }
-        for (; c < s.n_vchunks; ++c) acc += dp[(size_t)c * cs];
-        return acc;
-    }
-    return pair_value(d, q, pos, s, bad);
-}
-
 // Leaves from pair values in one pass.  One workgroup per group of rg
 // stored rows of one leaf (rg * Sp <= kLeafTile): the tile is cleared in
 // LDS, every pair of those rows is evaluated in parallel (they are one
 // contiguous range of the leaf entries, in pair order or in column order for
 // a transposed leaf; a one-token list pair reads its value directly) and
 // placed in the tile with its row's largest exponent, then the tile is
-// written out with float4 stores.  The first entries and their direct values
+// written out with float4 stores.  The value of every pair that is not one
+// token's probability is also stored for the leaf level of the marginal
+// message pass.  The first entries, their direct values and their pair ids
 // are loaded before the tile is cleared.
 constexpr int kLeafThreads = 256;
-constexpr int kLeafTile = 4096;  // floats
 constexpr int kLeafPre = 4;      // leaf entries per thread loaded ahead
 
 __global__ __launch_bounds__(kLeafThreads) void emission_leaves(DevTable d, StepView sv, int rg,
@@ -528,7 +502,7 @@ __global__ __launch_bounds__(kLeafThreads) void emission_leaves(DevTable d, Step
     const float *direct = d.use_sel ? src.psel + pos * d.nsel : src.p + pos * d.V;
     // the first kLeafPre entries per thread, and their direct values, are
     // loaded (clamped, unconditionally) before the tile is cleared
-    int prc[kLeafPre], pcode[kLeafPre];
+    int prc[kLeafPre], pcode[kLeafPre], pind[kLeafPre];
     float pval[kLeafPre];
     if (ne > 0) {
 #pragma unroll
@@ -538,7 +512,10 @@ __global__ __launch_bounds__(kLeafThreads) void emission_leaves(DevTable d, Step
             pcode[u] = esrc[k];
         }
 #pragma unroll
-        for (int u = 0; u < kLeafPre; ++u) pval[u] = direct[max(pcode[u], 0)];
+        for (int u = 0; u < kLeafPre; ++u) {
+            pval[u] = direct[max(pcode[u], 0)];
+            pind[u] = d.n_ind > 0 ? d.ind_pair[max(-1 - pcode[u], 0)] : 0;
+        }
     }
     for (int k = tid; k < n4; k += kLeafThreads) tile4[k] = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int r = tid; r < nr; r += kLeafThreads) remax[r] = kNeg;
@@ -558,7 +535,8 @@ __global__ __launch_bounds__(kLeafThreads) void emission_leaves(DevTable d, Step
                     v = pval[u];
                     if (!d.use_sel) bad |= !(v >= 0.f);
                 } else {
-                    v = pair_value_direct(d, -1 - pcode[u], pos, src, bad);
+                    v = pair_value_direct(d, pind[u], pos, src, bad);
+                    src.ndval[pos * d.n_ind + (-1 - pcode[u])] = v;
                 }
                 place(prc[u], v);
             }
@@ -570,7 +548,9 @@ __global__ __launch_bounds__(kLeafThreads) void emission_leaves(DevTable d, Step
                 v = direct[code];
                 if (!d.use_sel) bad |= !(v >= 0.f);
             } else {
-                v = pair_value_direct(d, -1 - code, pos, src, bad);
+                const int j = -1 - code;
+                v = pair_value_direct(d, d.ind_pair[j], pos, src, bad);
+                src.ndval[pos * d.n_ind + j] = v;
             }
             place(erc[k], v);
         }
@@ -603,14 +583,7 @@ int launch_build_transitions(const DevTable &d, const Geometry &g, const float *
     hipStream_t st = (hipStream_t)stream;
     const int npos = g.B * g.L;
     const int BLpad = (npos + kDenseTile - 1) / kDenseTile * kDenseTile;
-    EmitSrc src;
-    src.p = p;
-    src.dpart = (float *)(ws + w.dpart);
-    src.psel = d.use_sel ? (float *)(ws + w.psel) : nullptr;
-    src.cutp = (double *)(ws + w.cutp);
-    src.n_vchunks = w.n_vchunks;
-    src.BLpad = BLpad;
-    src.dval = (float *)(ws + w.dval);
+    const EmitSrc src = emit_src(d, g, p, ws, w);
     // leaves straight from pair values when an LDS tile holds a row
     const bool fused = g.Sp <= kLeafTile;  // the leaf entries exist for Sp < 65536
     if (d.ndense > 0) {

@@ -14,6 +14,7 @@ namespace fa {
 constexpr int kSpAlign = 64;       // trimmed state count padded to this
 constexpr int kNeg = -(1 << 29);   // exponent of an all-zero row/column
 constexpr int kDenseMax = 32;      // dense-label pairs share one mask word per token
+constexpr int kLeafTile = 4096;    // floats of the LDS tile of the one-pass leaf writer
 constexpr int kDenseStepsMax = 64;  // dense-mask contraction: 256-token steps per V chunk, at most
 constexpr int kDenseSlots = 512;    // workgroups of that contraction resident at once (256 CUs x 2)
 constexpr int kDenseSelLds = 64;    // token-list tokens per V chunk that its LDS buffer holds
@@ -78,11 +79,14 @@ struct DevTable {
     // leaf entries, in pair order (row-major leaves) and in column order
     // (transposed leaves): stored (row << 16 | column), and the value's
     // source: >= 0 a direct index (psel column, or token of p without a
-    // compact copy) of a one-token count-1 list pair, else -1 - pair
+    // compact copy) of a one-token count-1 list pair, else -1 - j for the
+    // j-th indirect pair (ind_pair[j])
     const int32_t *ent_n_rc;
     const int32_t *ent_n_src;
     const int32_t *ent_t_rc;
     const int32_t *ent_t_src;
+    const int32_t *ind_pair;   // [n_ind] pairs whose value is computed (not one direct read)
+    int32_t n_ind;
     const int32_t *sel_lb;     // [V/256 + 2] first sel_tok index at or after token 256 t
     int32_t n_tm;              // token-major LIST entries
 };
@@ -103,7 +107,7 @@ struct HostTable {
     std::vector<int32_t> tok2sel, tok2cut, seg_pair;
     std::vector<int32_t> map_n, map_t;
     std::vector<int32_t> tm_a, tm_b;
-    std::vector<int32_t> ent_n_rc, ent_n_src, ent_t_rc, ent_t_src;
+    std::vector<int32_t> ent_n_rc, ent_n_src, ent_t_rc, ent_t_src, ind_pair;
     std::vector<int32_t> sel_lb;
     bool has_cnt = false;
     bool use_sel = false;
@@ -143,6 +147,7 @@ struct WsLayout {
     size_t kpart = 0;                          // span tree: split-K partial tiles
     size_t va = 0, ea = 0, vb = 0, eb = 0;     // marginals: messages
     size_t rcut = 0;                           // marginals: range weights per cut
+    size_t ndval = 0;                          // emission: values of the indirect pairs (persist)
     size_t pw = 0;                             // marginals: per-position pair weights
     size_t hpart = 0;                          // marginals: q ln q partial sums per row part
     int32_t pw_nl = 0, pw_ld = 0;              // token-list weights per row, row length

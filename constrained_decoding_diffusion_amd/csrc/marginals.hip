@@ -10,6 +10,7 @@
 // vector's own power-of-two exponent.  Then, per position,
 //   q[i][v] = p[i][v] sum_{pairs (a,a') holding v} c alpha_i[a] beta_{i+1}[a'] / Z.
 #include "device_common.h"
+#include "pair_value.h"
 
 namespace fa {
 namespace {
@@ -623,6 +624,116 @@ __global__ void marg_negent_sum(int npos, const double *__restrict__ hpart,
     conf[pos] = (float)s;
 }
 
+// Leaf level of the message pass without reading the leaves.  Each leaf
+// holds only the automaton's pairs, whose values are recomputed from the
+// emission workspace: a one-token list pair reads p (or its compact copy),
+// every other pair the value the leaf writer stored for it, so the values are
+// bit-identical to the leaf entries.  One workgroup
+// per (leaf pair, alpha|beta): the input weights are normalized as in
+// marg_level (leaf scales: ro = co = 0, row fold rf); every thread loads its
+// (at most kLeafMsgPer) leaf entries and their values at once, and each
+// term g[in] * v * 2^-rf[in] goes to LDS in output-grouped order (column
+// order for alpha through a row-major leaf, pair order for beta through a
+// transposed one); each output state then adds its own segment in order.
+constexpr int kLeafMsgThreads = 512;
+constexpr int kLeafMsgPer = 24;  // leaf entries per thread
+constexpr int kLeafMsgMax = kLeafMsgThreads * kLeafMsgPer;
+
+__global__ __launch_bounds__(kLeafMsgThreads) void marg_leaf(
+    DevTable d, StepView sv, EmitSrc src, const int32_t *__restrict__ meta,
+    float *__restrict__ va, int32_t *__restrict__ ea, float *__restrict__ vb,
+    int32_t *__restrict__ eb)
+{
+    extern __shared__ float lsh[];  // terms [npairs] | g [S] | rf [S]
+    float *term = lsh;
+    float *gsh = lsh + d.npairs;
+    int *rsh = reinterpret_cast<int *>(gsh + d.S);
+    __shared__ int sh_max[kLeafMsgThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nn = sv.Lpad >> 1;
+    const int prod = blockIdx.x, beta = prod & 1, bn = prod >> 1;
+    const int b = bn / nn, idx = bn % nn;
+    const int l = 2 * idx, m = l + 1;
+    const int i = beta ? l + 1 : l;  // position of the leaf
+    const int h = sv.Lpad + i;
+    const int srcpos = beta ? l + 2 : l;
+    const bool real = i < sv.L;
+    const size_t pos = (size_t)b * sv.L + min(i, max(sv.L - 1, 0));
+    float *vbase = beta ? vb : va;
+    int32_t *ebase = beta ? eb : ea;
+    const float *vin = vbase + ((size_t)b * (sv.Lpad + 1) + srcpos) * sv.Sp;
+    float *vout = vbase + ((size_t)b * (sv.Lpad + 1) + m) * sv.Sp;
+    const int ein = ebase[(size_t)b * (sv.Lpad + 1) + srcpos];
+    const int32_t *rf = sv.meta_ptr(meta, b, h, 2);
+    // this thread's leaf entries and their values, all loads issued together
+    // (clamped, unconditional)
+    const int np = d.npairs;
+    const int32_t *erc = beta ? d.ent_n_rc : d.ent_t_rc;
+    const int32_t *esrc = beta ? d.ent_n_src : d.ent_t_src;
+    const float *direct = d.use_sel ? src.psel + pos * d.nsel : src.p + pos * d.V;
+    // indirect pairs read the values the leaf writer stored for them
+    const float *indv = src.ndval + pos * d.n_ind;
+    int prc[kLeafMsgPer];
+    float pval[kLeafMsgPer];
+    if (real && np > 0) {
+        int pcode[kLeafMsgPer];
+#pragma unroll
+        for (int u = 0; u < kLeafMsgPer; ++u) {
+            const int k = min(tid + u * kLeafMsgThreads, np - 1);
+            prc[u] = erc[k];
+            pcode[u] = esrc[k];
+        }
+#pragma unroll
+        for (int u = 0; u < kLeafMsgPer; ++u) {
+            const float xd = direct[max(pcode[u], 0)];
+            const float xi = indv[max(-1 - pcode[u], 0)];
+            pval[u] = pcode[u] >= 0 ? xd : xi;
+        }
+    }
+    int e = kNeg;
+    for (int a = tid; a < d.S; a += kLeafMsgThreads) {
+        const float x = vin[a];
+        const int sr = rf[a];
+        rsh[a] = sr;
+        gsh[a] = x;
+        if (x > 0.f && sr > kNeg) e = max(e, fexp(x) + sr);
+    }
+    e = wave_max_i(e);
+    if (lane == 0) sh_max[wave] = e;
+    __syncthreads();
+    int G = kNeg;
+    for (int w = 0; w < kLeafMsgThreads / 64; ++w) G = max(G, sh_max[w]);
+    for (int a = tid; a < d.S; a += kLeafMsgThreads) {
+        const float x = gsh[a];
+        const int sr = rsh[a];
+        gsh[a] = (x > 0.f && sr > kNeg && G > kNeg) ? scale2(mant(x), fexp(x) + sr - G) : 0.f;
+    }
+    __syncthreads();
+    if (!real) {  // identity leaf: v = 1 on the diagonal
+        for (int j = tid; j < sv.Sp; j += kLeafMsgThreads)
+            vout[j] = j < d.S ? gsh[j] * scale2(1.f, -rsh[j]) : 0.f;
+    } else {
+#pragma unroll
+        for (int u = 0; u < kLeafMsgPer; ++u) {
+            const int k = tid + u * kLeafMsgThreads;
+            if (k < np) {
+                const int in = prc[u] & 0xffff;
+                term[k] = gsh[in] * scale2(pval[u], -rsh[in]);
+            }
+        }
+        __syncthreads();
+        const int32_t *seg = beta ? d.row_ptr : d.col_ptr;
+        for (int j = tid; j < sv.Sp; j += kLeafMsgThreads) {
+            float acc = 0.f;
+            if (j < d.S)
+                for (int k = seg[j]; k < seg[j + 1]; ++k) acc += term[k];
+            vout[j] = G > kNeg ? acc : 0.f;
+        }
+    }
+    if (tid == 0)
+        ebase[(size_t)b * (sv.Lpad + 1) + m] = (G > kNeg && ein > kNeg) ? ein + G : kNeg;
+}
+
 }  // namespace
 
 int launch_marginals(const DevTable &d, const Geometry &g, const float *p, const float *tree,
@@ -647,9 +758,26 @@ int launch_marginals(const DevTable &d, const Geometry &g, const float *p, const
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return (int)e;
     }
+    // the leaf level straight from pair values when the leaf entries exist
+    // (Sp < 65536) and their terms fit in LDS
+    const bool sparse_leaf = g.K >= 1 && g.Sp <= kLeafTile && d.npairs <= kLeafMsgMax &&
+                             ((size_t)d.npairs + 2 * (size_t)d.S) * 4 <= 64 * 1024;
     for (int level = 1; level <= g.K; ++level) {
         const int nn = 1 << (level - 1);
         const int products = g.B * nn * 2;
+        if (level == g.K && sparse_leaf) {
+            const size_t llds = ((size_t)d.npairs + 2 * (size_t)d.S) * 4;
+            if (llds > 48 * 1024) {
+                e = hipFuncSetAttribute(reinterpret_cast<const void *>(&marg_leaf),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)llds);
+                if (e != hipSuccess) return (int)e;
+            }
+            marg_leaf<<<products, kLeafMsgThreads, llds, st>>>(d, sv, emit_src(d, g, p, ws, w), meta,
+                                                              va, ea, vb, eb);
+            e = hipGetLastError();
+            if (e != hipSuccess) return (int)e;
+            continue;
+        }
         if (products * ((g.Sp + 255) / 256) >= 256) {
             dim3 grid((g.Sp + 255) / 256, products);
             marg_level<256><<<grid, kMsgThreads, lds, st>>>(d, sv, tree, meta, nn, va, ea, vb, eb);

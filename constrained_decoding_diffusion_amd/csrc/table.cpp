@@ -78,6 +78,7 @@ void build_image(HostTable &t)
     append_section(t.image, t.offs, t.ent_t_rc);
     append_section(t.image, t.offs, t.ent_t_src);
     append_section(t.image, t.offs, t.sel_lb);
+    append_section(t.image, t.offs, t.ind_pair);
     t.image.resize((t.image.size() + 255) & ~size_t(255));
 }
 
@@ -112,6 +113,8 @@ DevTable HostTable::device_view() const
     nxt(d.cut_off); nxt(d.cut_ev); nxt(d.tok2sel); nxt(d.tok2cut); nxt(d.seg_pair);
     nxt(d.map_n); nxt(d.map_t); nxt(d.tm_a); nxt(d.tm_b);
     nxt(d.ent_n_rc); nxt(d.ent_n_src); nxt(d.ent_t_rc); nxt(d.ent_t_src); nxt(d.sel_lb);
+    nxt(d.ind_pair);
+    d.n_ind = (int32_t)ind_pair.size();
     d.n_tm = (int32_t)tm_pair.size();
     if (map_n.empty()) {
         d.map_n = nullptr;
@@ -195,16 +198,23 @@ WsLayout ws_layout(const HostTable &t, const Geometry &g)
         }
         w.sel_mode = most <= kDenseSelLds ? 1 : 2;
     }
-    w.dpart = o; o = al(o + (size_t)w.n_vchunks * BLpad * kDenseMax * sizeof(float));
-    w.dval = o; o = al(o + (t.ndense() ? BL * kDenseMax * sizeof(float) : 0));
+    // the compact token copy and the stored indirect pair values persist
+    // through the step (the leaf level of the marginal message pass reads
+    // pair values from them); every other region is a union over one call
+    const bool fused = g.Sp <= kLeafTile;  // leaves straight from pair values
     w.psel = o; o = al(o + (t.use_sel ? BL * t.nsel() * sizeof(float) : 0));
+    // one spare float: a clamped read of slot 0 stays inside even with no indirect pairs
+    w.ndval = o; o = al(o + (fused ? (BL * t.ind_pair.size() + 1) * sizeof(float) : 0));
+    const size_t a0 = o;
+    w.dpart = o; o = al(o + (size_t)w.n_vchunks * BLpad * kDenseMax * sizeof(float));
+    w.dval = o; o = al(o + (t.ndense() && !fused ? BL * kDenseMax * sizeof(float) : 0));
     w.cutp = o; o = al(o + BL * t.ncut() * sizeof(double));
-    w.val = o; o = al(o + BL * t.npairs() * sizeof(float));
+    w.val = o; o = al(o + (fused ? 0 : BL * t.npairs() * sizeof(float)));
     size_t a1 = o;
-    o = 0;  // sampler region
+    o = a0;  // sampler region
     w.zc = o; o = al(o + (size_t)g.B * (g.Lpad + 1) * sizeof(int32_t));
     size_t a3 = o;
-    o = 0;  // span tree region
+    o = a0;  // span tree region
     size_t kp = 0;
     for (int level = 1; level <= g.K; ++level) {
         const int s = tree_ksplit(g, level);
@@ -212,7 +222,7 @@ WsLayout ws_layout(const HostTable &t, const Geometry &g)
     }
     w.kpart = o; o = al(o + kp * sizeof(float));
     size_t a2 = o;
-    o = 0;  // marginals region
+    o = a0;  // marginals region
     size_t nv = (size_t)g.B * (g.Lpad + 1);
     w.va = o; o = al(o + nv * g.Sp * sizeof(float));
     w.vb = o; o = al(o + nv * g.Sp * sizeof(float));
@@ -565,14 +575,24 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
                                 t.sel_tok.begin());
     // leaf entries (stored row, column and value source) in both orders
     t.ent_n_rc.clear(); t.ent_n_src.clear(); t.ent_t_rc.clear(); t.ent_t_src.clear();
+    t.ind_pair.clear();
     if (t.Sp < 65536) {
-        auto src_code = [&](int32_t q) -> int32_t {
+        std::vector<int32_t> ind_of(np, -1);
+        for (int32_t q = 0; q < np; ++q) {
+            bool direct = false;
             if (t.pair_cls[q] == kList && t.list_off[q + 1] - t.list_off[q] == 1) {
                 const int32_t k = t.list_off[q];
-                if (t.list_cnt.empty() || t.list_cnt[k] == 1.f)
-                    return t.use_sel ? t.list_sel[k] : t.list_tok[k];
+                direct = t.list_cnt.empty() || t.list_cnt[k] == 1.f;
             }
-            return -1 - q;
+            if (!direct) {
+                ind_of[q] = (int32_t)t.ind_pair.size();
+                t.ind_pair.push_back(q);
+            }
+        }
+        auto src_code = [&](int32_t q) -> int32_t {
+            if (ind_of[q] >= 0) return -1 - ind_of[q];
+            const int32_t k = t.list_off[q];
+            return t.use_sel ? t.list_sel[k] : t.list_tok[k];
         };
         t.ent_n_rc.resize(np); t.ent_n_src.resize(np); t.ent_t_rc.resize(np); t.ent_t_src.resize(np);
         for (int32_t q = 0; q < np; ++q) {

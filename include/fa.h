@@ -139,9 +139,10 @@ int fa_table_state_map(const fa_table *t, int32_t *orig_of);
 
 /*
  * fa_sizes - bytes of the tree, meta and workspace buffers a step with batch
- * B and length L needs.  Any output pointer may be NULL.  The workspace may be
- * shared by all four calls of a step on one stream.  Errors: FA_EINVAL,
- * FA_ETOOBIG.
+ * B and length L needs.  Any output pointer may be NULL.  The four calls of
+ * one step take the same workspace, in order on one stream, and it must not
+ * be written in between: fa_marginals reads pair-value sources that
+ * fa_build_transitions leaves in it.  Errors: FA_EINVAL, FA_ETOOBIG.
  */
 int fa_sizes(const fa_table *t, int32_t B, int32_t L, size_t *tree_bytes, size_t *meta_bytes,
              size_t *ws_bytes);
@@ -157,7 +158,9 @@ int fa_sizes(const fa_table *t, int32_t B, int32_t L, size_t *tree_bytes, size_t
  *            negative entries that are read set FA_ROW_BADPROB)
  *   tree     device, fa_sizes bytes; leaves written
  *   meta     device, fa_sizes bytes; leaf exponents written
- *   ws       device workspace of ws_bytes >= fa_sizes
+ *   ws       device workspace of ws_bytes >= fa_sizes; keeps, for the step's
+ *            fa_marginals, the compact copy of p at token-list tokens and the
+ *            values of the pairs that are not a single token's probability
  *   row_status device int32 [B], OR-ed
  * Errors: FA_EINVAL, FA_ESTATE, FA_EHIP.
  */
@@ -224,6 +227,8 @@ int fa_sample(const fa_table *t, const float *p, int32_t B, int32_t L, const flo
  *           FA_CONF_NEGENT)
  *   q       device fp32 [B][L][V] or NULL (not written)
  *   conf    device fp32 [B][L]
+ *   ws      the workspace this step's fa_build_transitions wrote (the leaf
+ *           level of the messages reads pair values from it)
  * Errors: FA_EINVAL, FA_ESTATE, FA_EHIP.
  */
 int fa_marginals(const fa_table *t, const float *p, int32_t B, int32_t L, const float *tree,
