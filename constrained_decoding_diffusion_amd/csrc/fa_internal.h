@@ -87,6 +87,8 @@ struct DevTable {
     const int32_t *ent_t_src;
     const int32_t *ind_pair;   // [n_ind] pairs whose value is computed (not one direct read)
     int32_t n_ind;
+    const uint32_t *dense_bits;  // [ndense][dense_words] bit v%32 of word v/32: v in the label
+    int32_t dense_words;
     const int32_t *sel_lb;     // [V/256 + 2] first sel_tok index at or after token 256 t
     int32_t n_tm;              // token-major LIST entries
 };
@@ -108,6 +110,7 @@ struct HostTable {
     std::vector<int32_t> map_n, map_t;
     std::vector<int32_t> tm_a, tm_b;
     std::vector<int32_t> ent_n_rc, ent_n_src, ent_t_rc, ent_t_src, ind_pair;
+    std::vector<uint32_t> dense_bits;
     std::vector<int32_t> sel_lb;
     bool has_cnt = false;
     bool use_sel = false;

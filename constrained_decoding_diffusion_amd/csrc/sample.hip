@@ -344,45 +344,59 @@ __global__ __launch_bounds__(kTokThreads) void sample_tokens(
     if (streamed) {
         // chunk ch = float4 groups [1024 ch, 1024 ch + 1024): thread t takes
         // groups 1024 ch + 256 u + t (u < 4), so each load instruction reads
-        // 1 KB contiguous per wavefront; the loads of chunk ch+1 are issued
-        // (unconditionally, clamped) before chunk ch is summed
+        // 1 KB contiguous per wavefront; the label comes from the pair's own
+        // bit array (4 bits per group), and the loads of chunks ch+1 and
+        // ch+2 (unconditional, clamped) are in flight while chunk ch is summed
         const float4 *p4 = reinterpret_cast<const float4 *>(prow);
-        const uint4 *m4 = reinterpret_cast<const uint4 *>(d.tokmask);
+        const uint32_t *bits = d.dense_bits + (size_t)d.pair_aux[q] * d.dense_words;
         const int n4 = d.V >> 2;
         struct Buf {
             float4 x[4];
-            uint4 m[4];
+            uint32_t m[4];
         };
         auto load = [&](Buf &bf, int ch) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int k = min(ch * 1024 + u * kTokThreads + tid, n4 - 1);
                 bf.x[u] = p4[k];
-                bf.m[u] = m4[k];
+                bf.m[u] = bits[k >> 3];
             }
         };
         auto chunk_sum = [&](const Buf &bf, int ch) -> double {
             double s = 0.0;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                if (ch * 1024 + u * kTokThreads + tid < n4) {
-                    s += (double)((bf.m[u].x & cd.dbit) ? bf.x[u].x : 0.f);
-                    s += (double)((bf.m[u].y & cd.dbit) ? bf.x[u].y : 0.f);
-                    s += (double)((bf.m[u].z & cd.dbit) ? bf.x[u].z : 0.f);
-                    s += (double)((bf.m[u].w & cd.dbit) ? bf.x[u].w : 0.f);
+                const int k = ch * 1024 + u * kTokThreads + tid;
+                if (k < n4) {
+                    const uint32_t m = bf.m[u] >> ((k & 7) * 4);
+                    s += (double)((m & 1u) ? bf.x[u].x : 0.f);
+                    s += (double)((m & 2u) ? bf.x[u].y : 0.f);
+                    s += (double)((m & 4u) ? bf.x[u].z : 0.f);
+                    s += (double)((m & 8u) ? bf.x[u].w : 0.f);
                 }
             }
             return s;
         };
-        Buf A, Bn;
+        auto put = [&](const Buf &bf, int ch) {
+            const double s0 = wave_sum_d(chunk_sum(bf, ch));
+            if (lane == 0 && ch < nchunks) wsum[ch][wave] = s0;
+        };
+        Buf A, Bn, C;
         load(A, 0);
-        for (int ch = 0; ch < nchunks; ch += 2) {
-            load(Bn, ch + 1);
-            const double s0 = wave_sum_d(chunk_sum(A, ch));
-            if (lane == 0) wsum[ch][wave] = s0;
-            load(A, ch + 2);
-            const double s1 = wave_sum_d(chunk_sum(Bn, ch + 1));
-            if (lane == 0 && ch + 1 < nchunks) wsum[ch + 1][wave] = s1;
+        load(Bn, 1);
+        for (int ch = 0; ch < nchunks; ch += 3) {
+            load(C, ch + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            put(A, ch);
+            __builtin_amdgcn_sched_barrier(0);
+            load(A, ch + 3);
+            __builtin_amdgcn_sched_barrier(0);
+            put(Bn, ch + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            load(Bn, ch + 4);
+            __builtin_amdgcn_sched_barrier(0);
+            put(C, ch + 2);
+            __builtin_amdgcn_sched_barrier(0);
         }
     } else {
         for (int ch = 0; ch < nchunks; ++ch) {

@@ -79,6 +79,7 @@ void build_image(HostTable &t)
     append_section(t.image, t.offs, t.ent_t_src);
     append_section(t.image, t.offs, t.sel_lb);
     append_section(t.image, t.offs, t.ind_pair);
+    append_section(t.image, t.offs, t.dense_bits);
     t.image.resize((t.image.size() + 255) & ~size_t(255));
 }
 
@@ -115,6 +116,8 @@ DevTable HostTable::device_view() const
     nxt(d.ent_n_rc); nxt(d.ent_n_src); nxt(d.ent_t_rc); nxt(d.ent_t_src); nxt(d.sel_lb);
     nxt(d.ind_pair);
     d.n_ind = (int32_t)ind_pair.size();
+    nxt(d.dense_bits);
+    d.dense_words = (V + 31) / 32;
     d.n_tm = (int32_t)tm_pair.size();
     if (map_n.empty()) {
         d.map_n = nullptr;
@@ -565,6 +568,12 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
     // only tables with dense-mask pairs stream p through a kernel that can copy
     // the token-list tokens (range tables hold no token lists)
     t.use_sel = t.ndense() > 0 && ns > 0 && ns <= kSelMax;
+    // one bit array per dense pair (bit v%32 of word v/32: v in its label)
+    const int32_t nw = (V + 31) / 32;
+    t.dense_bits.assign((size_t)t.ndense() * nw, 0u);
+    for (int32_t j = 0; j < t.ndense(); ++j)
+        for (int32_t v = 0; v < V; ++v)
+            if ((t.tokmask[v] >> j) & 1u) t.dense_bits[(size_t)j * nw + v / 32] |= 1u << (v % 32);
     t.selbit = t.ndense() > 0 && t.ndense() < 32 && ns > 0;
     if (t.selbit)
         for (int32_t v : t.sel_tok) t.tokmask[v] |= kSelBit;
