@@ -352,6 +352,22 @@ __global__ void emission_pairs(DevTable d, int L, EmitSrc src, float *__restrict
     if (bad) atomicOr(&status[pos / L], (int)FA_ROW_BADPROB);
 }
 
+// values of the pairs that are not one token's probability (ind_pair), for
+// the one-pass leaf writer and the leaf level of the marginal message pass:
+// grid.x over groups of those pairs, grid.y over positions
+__global__ void emission_indirect(DevTable d, int L, EmitSrc src, int32_t *__restrict__ status)
+{
+    const int j0 = (blockIdx.x * blockDim.x + threadIdx.x) * kPairsPerThread;
+    const size_t pos = blockIdx.y;
+    int bad = 0;
+#pragma unroll
+    for (int u = 0; u < kPairsPerThread; ++u) {
+        const int j = j0 + u;
+        if (j < d.n_ind) src.ndval[pos * d.n_ind + j] = pair_value_direct(d, d.ind_pair[j], pos, src, bad);
+    }
+    if (bad) atomicOr(&status[pos / L], (int)FA_ROW_BADPROB);
+}
+
 // dense leaf rows through the (row, column) -> pair maps: one wavefront per
 // stored row, four columns per lane per step, float4 stores
 __global__ __launch_bounds__(256) void emission_densify_map(DevTable d, StepView sv,
@@ -470,9 +486,9 @@ __global__ __launch_bounds__(kDensifyThreads) void emission_densify(
 // a transposed leaf; a one-token list pair reads its value directly) and
 // placed in the tile with its row's largest exponent, then the tile is
 // written out with float4 stores.  The value of every pair that is not one
-// token's probability is also stored for the leaf level of the marginal
-// message pass.  The first entries, their direct values and their pair ids
-// are loaded before the tile is cleared.
+// token's probability comes from emission_indirect (one load, like a direct
+// value).  The first entries and their values are loaded before the tile is
+// cleared.
 constexpr int kLeafThreads = 256;
 constexpr int kLeafPre = 4;      // leaf entries per thread loaded ahead
 
@@ -502,7 +518,8 @@ __global__ __launch_bounds__(kLeafThreads) void emission_leaves(DevTable d, Step
     const float *direct = d.use_sel ? src.psel + pos * d.nsel : src.p + pos * d.V;
     // the first kLeafPre entries per thread, and their direct values, are
     // loaded (clamped, unconditionally) before the tile is cleared
-    int prc[kLeafPre], pcode[kLeafPre], pind[kLeafPre];
+    const float *indv = src.ndval + pos * d.n_ind;
+    int prc[kLeafPre], pcode[kLeafPre];
     float pval[kLeafPre];
     if (ne > 0) {
 #pragma unroll
@@ -513,8 +530,9 @@ __global__ __launch_bounds__(kLeafThreads) void emission_leaves(DevTable d, Step
         }
 #pragma unroll
         for (int u = 0; u < kLeafPre; ++u) {
-            pval[u] = direct[max(pcode[u], 0)];
-            pind[u] = d.n_ind > 0 ? d.ind_pair[max(-1 - pcode[u], 0)] : 0;
+            const float xd = direct[max(pcode[u], 0)];
+            const float xi = indv[max(-1 - pcode[u], 0)];
+            pval[u] = pcode[u] >= 0 ? xd : xi;
         }
     }
     for (int k = tid; k < n4; k += kLeafThreads) tile4[k] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -530,28 +548,15 @@ __global__ __launch_bounds__(kLeafThreads) void emission_leaves(DevTable d, Step
 #pragma unroll
         for (int u = 0; u < kLeafPre; ++u) {
             if (tid + u * kLeafThreads < ne) {
-                float v;
-                if (pcode[u] >= 0) {
-                    v = pval[u];
-                    if (!d.use_sel) bad |= !(v >= 0.f);
-                } else {
-                    v = pair_value_direct(d, pind[u], pos, src, bad);
-                    src.ndval[pos * d.n_ind + (-1 - pcode[u])] = v;
-                }
+                const float v = pval[u];
+                if (pcode[u] >= 0 && !d.use_sel) bad |= !(v >= 0.f);
                 place(prc[u], v);
             }
         }
         for (int k = tid + kLeafPre * kLeafThreads; k < ne; k += kLeafThreads) {
             const int code = esrc[k];
-            float v;
-            if (code >= 0) {
-                v = direct[code];
-                if (!d.use_sel) bad |= !(v >= 0.f);
-            } else {
-                const int j = -1 - code;
-                v = pair_value_direct(d, d.ind_pair[j], pos, src, bad);
-                src.ndval[pos * d.n_ind + j] = v;
-            }
+            const float v = code >= 0 ? direct[code] : indv[-1 - code];
+            if (code >= 0 && !d.use_sel) bad |= !(v >= 0.f);
             place(erc[k], v);
         }
         if (bad) atomicOr(&status[b], (int)FA_ROW_BADPROB);
@@ -625,6 +630,12 @@ int launch_build_transitions(const DevTable &d, const Geometry &g, const float *
     }
     StepView sv = step_view(g);
     if (fused) {
+        if (d.n_ind > 0) {
+            dim3 igrid((d.n_ind + 256 * kPairsPerThread - 1) / (256 * kPairsPerThread), npos);
+            emission_indirect<<<igrid, 256, 0, st>>>(d, g.L, src, status);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return (int)e;
+        }
         const int rg = kLeafTile / g.Sp;
         dim3 grid((g.Sp + rg - 1) / rg, g.B * g.Lpad);
         emission_leaves<<<grid, kLeafThreads, 0, st>>>(d, sv, rg, src, tree, meta, status);
