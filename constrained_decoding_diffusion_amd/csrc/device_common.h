@@ -50,6 +50,14 @@ __device__ inline int fexp(float x)
     return e;
 }
 
+// a float4 store that does not allocate in the caches (streaming output)
+__device__ inline void store_nt(float4 *dst, float4 v)
+{
+    typedef float f32x4n __attribute__((ext_vector_type(4)));
+    const f32x4n x = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(x, reinterpret_cast<f32x4n *>(dst));
+}
+
 // sum of two exponents, saturating at kNeg (an all-zero row or column)
 __device__ inline int add_exp(int a, int b)
 {
