@@ -15,6 +15,12 @@
 // with X, Y the consumed stored rows.  Odd (right-child) nodes are produced
 // transposed by swapping the operands.  No entry is lost unless it is 2^-126
 // below the maximum of its own row.
+//
+// Products are stored with non-temporal stores: a level is read next by the
+// level above (a compute-bound kernel) and later by the sampler and the
+// message pass, after the streaming kernels in between have evicted it, so
+// writing it straight to HBM while the MFMAs run keeps that write-back out
+// of the streaming kernels.
 #include "device_common.h"
 
 namespace fa {
@@ -154,7 +160,7 @@ __global__ __launch_bounds__(kGemmThreads) void span_gemm(StepView sv, float *__
     for (int r = 0; r < 16; ++r) {
         const int i = tm + wr + (r >> 2) * 8 + half * 4 + (r & 3);
         const float x = acc[r];
-        D[(size_t)i * Sp + j] = x;
+        __builtin_nontemporal_store(x, &D[(size_t)i * Sp + j]);
         int e = (x > 0.f && coDj > kNeg) ? fexp(x) + coDj : kNeg;
 #pragma unroll
         for (int o = 16; o > 0; o >>= 1) e = max(e, __shfl_xor(e, o));
@@ -337,7 +343,7 @@ __global__ __launch_bounds__(kBigThreads) void span_gemm128(StepView sv, float *
         for (int r = 0; r < 16; ++r) {
             const int i = tm + wr + (r >> 2) * 8 + half * 4 + (r & 3);
             const float v = acc[y][r];
-            D[(size_t)i * Sp + j] = v;
+            __builtin_nontemporal_store(v, &D[(size_t)i * Sp + j]);
             int e = (v > 0.f && coDj > kNeg) ? fexp(v) + coDj : kNeg;
 #pragma unroll
             for (int o = 16; o > 0; o >>= 1) e = max(e, __shfl_xor(e, o));
@@ -542,7 +548,7 @@ __global__ __launch_bounds__(kHugeThreads) void span_gemm256(StepView sv, float 
 #pragma unroll
             for (int cy = 0; cy < 4; ++cy) {
                 const float v = acc[ry][cy][r];
-                D[(size_t)(tm + il) * Sp + tn + wc + 32 * cy + l32] = v;
+                __builtin_nontemporal_store(v, &D[(size_t)(tm + il) * Sp + tn + wc + 32 * cy + l32]);
                 if (v > 0.f && coDj[cy] > kNeg) e = max(e, fexp(v) + coDj[cy]);
             }
 #pragma unroll
