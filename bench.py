@@ -189,14 +189,22 @@ def summarize_counters(fetch_dir, write_dir, command):
         fh.write("\n".join(lines) + "\n")
 
 
-def summarize_trace(trace_dir, command):
-    """profiles/step_json_like_dfa_kernel_trace.md from a --kernel-trace
+TRACE_NAMES = {
+    3: ("json_like_dfa", "json-like DFA, B=4, L=256, V=151,936"),
+    4: ("range_dfa", "range DFA, S=1024, B=16, L=512, V=151,936"),
+    5: ("random_nfa", "random NFA, S=10,000, E=100,000, B=1, L=64, V=151,936"),
+}
+
+
+def summarize_trace(trace_dir, command, workload=3):
+    """profiles/step_<workload>_kernel_trace.md from a --kernel-trace
     --stats run: per-kernel totals and per-launch-shape averages."""
     import csv
     stats = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
     trace = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))))
     short = lambda n: n.replace("fa::(anonymous namespace)::", "").split("(fa::")[0][:60]
-    lines = ["# Kernel trace of the constrained step (json-like DFA, B=4, L=256, V=151,936)", "",
+    stem, title = TRACE_NAMES[workload]
+    lines = [f"# Kernel trace of the constrained step ({title})", "",
              "Command (from the repository root):", "", "```", command, "```", "",
              "| kernel | calls | avg us | total ms | % |", "|---|---|---|---|---|"]
     for r in stats:
@@ -210,7 +218,7 @@ def summarize_trace(trace_dir, command):
               "|---|---|---|---|---|"]
     for k, v in sorted(groups.items(), key=lambda kv: -sum(kv[1]))[:30]:
         lines.append(f"| `{k[0]}` | {k[1]} | {k[2]} | {len(v)} | {sum(v) / len(v):.1f} |")
-    with open(os.path.join(ROOT, "profiles", "step_json_like_dfa_kernel_trace.md"), "w") as fh:
+    with open(os.path.join(ROOT, "profiles", f"step_{stem}_kernel_trace.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
 
@@ -233,7 +241,7 @@ def main():
         summarize_counters(*args.summarize_counters, args.command)
         return
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace, args.command)
+        summarize_trace(args.summarize_trace, args.command, args.workload)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "

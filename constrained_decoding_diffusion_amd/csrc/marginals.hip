@@ -163,30 +163,122 @@ __global__ __launch_bounds__(kMsgThreads) void marg_level(
 }
 
 // range weights per cut interval: rcut[pos][c] = sum of c*alpha*beta over
-// the segments covering [cuts[c], cuts[c+1]); fp64 sweep, exact zero when no
-// segment is active
-__global__ void marg_rcut(DevTable d, StepView sv, const float *__restrict__ va,
-                          const float *__restrict__ vb, float *__restrict__ rcut)
+// the segments covering [cuts[c], cuts[c+1]), in fp64, exactly zero where no
+// segment is active.  One workgroup per position; each thread takes a run of
+// consecutive cuts.  The active-segment count at every cut comes from a block
+// scan of the runs' count changes; the weight sum is a segmented fp64 scan
+// that restarts at zero at every cut where no segment is active (a rounding
+// residue never carries past such a cut), and a sum rounded below zero is
+// written as zero.
+constexpr int kRcutThreads = 256;
+
+// segmented sum: (x, reset) o (y, reset') = (reset' ? y : x + y, reset | reset')
+struct SegSum {
+    double x;
+    int reset;
+};
+
+__device__ inline SegSum seg_combine(SegSum a, SegSum b)
 {
-    const int pos = blockIdx.x * blockDim.x + threadIdx.x;
-    if (pos >= sv.B * sv.L) return;
+    return SegSum{b.reset ? b.x : a.x + b.x, a.reset | b.reset};
+}
+
+__global__ __launch_bounds__(kRcutThreads) void marg_rcut(DevTable d, StepView sv,
+                                                          const float *__restrict__ va,
+                                                          const float *__restrict__ vb,
+                                                          float *__restrict__ rcut, int ab_lds)
+{
+    extern __shared__ float abs_[];  // alpha [Sp] | beta [Sp] when ab_lds
+    __shared__ int sh_cnt[kRcutThreads];
+    __shared__ double sh_x[kRcutThreads];
+    __shared__ int sh_r[kRcutThreads];
+    const int pos = blockIdx.x;
+    const int tid = threadIdx.x;
     const int b = pos / sv.L, i = pos % sv.L;
-    const float *al = va + ((size_t)b * (sv.Lpad + 1) + i) * sv.Sp;
-    const float *be = vb + ((size_t)b * (sv.Lpad + 1) + i + 1) * sv.Sp;
-    double R = 0.0;
-    int active = 0;
+    const float *alg = va + ((size_t)b * (sv.Lpad + 1) + i) * sv.Sp;
+    const float *beg = vb + ((size_t)b * (sv.Lpad + 1) + i + 1) * sv.Sp;
+    const float *al = alg, *be = beg;
+    if (ab_lds) {
+        for (int a = tid; a < d.S; a += kRcutThreads) {
+            abs_[a] = alg[a];
+            abs_[sv.Sp + a] = beg[a];
+        }
+        al = abs_;
+        be = abs_ + sv.Sp;
+    }
+    const int per = (d.ncut + kRcutThreads - 1) / kRcutThreads;
+    const int c0 = min(tid * per, d.ncut), c1 = min(c0 + per, d.ncut);
+    // count changes of this run, then the active count before it
+    int dc = 0;
+    for (int k = d.cut_off[c0]; k < d.cut_off[c1]; ++k) dc += (d.cut_ev[k] & 1) ? -1 : 1;
+    sh_cnt[tid] = dc;
+    __syncthreads();
+    // exclusive scan of the count changes (Hillis-Steele over the block)
+    for (int o = 1; o < kRcutThreads; o <<= 1) {
+        const int v = tid >= o ? sh_cnt[tid - o] : 0;
+        __syncthreads();
+        sh_cnt[tid] += v;
+        __syncthreads();
+    }
+    const int act0 = sh_cnt[tid] - dc;
+    auto weight = [&](int ev) {
+        const int sg = ev >> 1;
+        const int q = d.seg_pair[sg];
+        return (double)al[d.pair_a[q]] * (double)be[d.pair_b[q]] * (double)d.seg_cnt[sg];
+    };
+    // this run's segmented sum
+    SegSum mine{0.0, 0};
+    {
+        int act = act0;
+        for (int c = c0; c < c1; ++c) {
+            for (int k = d.cut_off[c]; k < d.cut_off[c + 1]; ++k) {
+                const int ev = d.cut_ev[k];
+                const double w = weight(ev);
+                if (ev & 1) {
+                    mine.x -= w;
+                    --act;
+                } else {
+                    mine.x += w;
+                    ++act;
+                }
+            }
+            if (act == 0) mine = SegSum{0.0, 1};
+        }
+    }
+    // inclusive segmented scan over the runs, then the carry into this run
+    sh_x[tid] = mine.x;
+    sh_r[tid] = mine.reset;
+    __syncthreads();
+    for (int o = 1; o < kRcutThreads; o <<= 1) {
+        SegSum v{0.0, 0};
+        const bool has = tid >= o;
+        if (has) v = SegSum{sh_x[tid - o], sh_r[tid - o]};
+        __syncthreads();
+        if (has) {
+            const SegSum r = seg_combine(v, SegSum{sh_x[tid], sh_r[tid]});
+            sh_x[tid] = r.x;
+            sh_r[tid] = r.reset;
+        }
+        __syncthreads();
+    }
+    double R = tid > 0 ? sh_x[tid - 1] : 0.0;
+    // write the run
     float *out = rcut + (size_t)pos * d.ncut;
-    for (int c = 0; c < d.ncut; ++c) {
+    int act = act0;
+    for (int c = c0; c < c1; ++c) {
         for (int k = d.cut_off[c]; k < d.cut_off[c + 1]; ++k) {
             const int ev = d.cut_ev[k];
-            const int s = ev >> 1;
-            const int q = d.seg_pair[s];
-            const double w = (double)al[d.pair_a[q]] * (double)be[d.pair_b[q]] * (double)d.seg_cnt[s];
-            if (ev & 1) { R -= w; --active; }
-            else { R += w; ++active; }
+            const double w = weight(ev);
+            if (ev & 1) {
+                R -= w;
+                --act;
+            } else {
+                R += w;
+                ++act;
+            }
         }
-        if (active == 0 || R < 0.0) R = 0.0;
-        out[c] = (float)R;
+        if (act == 0) R = 0.0;
+        out[c] = R > 0.0 ? (float)R : 0.f;
     }
 }
 
@@ -792,7 +884,9 @@ int launch_marginals(const DevTable &d, const Geometry &g, const float *p, const
     }
     if (d.ncut) {
         const int npos = g.B * g.L;
-        marg_rcut<<<(npos + 63) / 64, 64, 0, st>>>(d, sv, va, vb, rcut);
+        const size_t ab = (size_t)2 * g.Sp * sizeof(float);
+        const int ab_lds = ab <= 48 * 1024;
+        marg_rcut<<<npos, kRcutThreads, ab_lds ? ab : 0, st>>>(d, sv, va, vb, rcut, ab_lds);
         e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
     }
