@@ -89,6 +89,9 @@ struct DevTable {
     int32_t n_ind;
     const uint32_t *dense_bits;  // [ndense][dense_words] bit v%32 of word v/32: v in the label
     int32_t dense_words;
+    const int32_t *ev_a;       // [2 nseg] per cut event (cut_ev order): the states of its pair
+    const int32_t *ev_b;
+    const float *ev_w;         // [2 nseg] its count, negative at a segment end
     const int32_t *sel_lb;     // [V/256 + 2] first sel_tok index at or after token 256 t
     int32_t n_tm;              // token-major LIST entries
 };
@@ -111,6 +114,8 @@ struct HostTable {
     std::vector<int32_t> tm_a, tm_b;
     std::vector<int32_t> ent_n_rc, ent_n_src, ent_t_rc, ent_t_src, ind_pair;
     std::vector<uint32_t> dense_bits;
+    std::vector<int32_t> ev_a, ev_b;
+    std::vector<float> ev_w;
     std::vector<int32_t> sel_lb;
     bool has_cnt = false;
     bool use_sel = false;

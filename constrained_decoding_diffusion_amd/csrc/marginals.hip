@@ -164,13 +164,16 @@ __global__ __launch_bounds__(kMsgThreads) void marg_level(
 
 // range weights per cut interval: rcut[pos][c] = sum of c*alpha*beta over
 // the segments covering [cuts[c], cuts[c+1]), in fp64, exactly zero where no
-// segment is active.  One workgroup per position; each thread takes a run of
-// consecutive cuts.  The active-segment count at every cut comes from a block
-// scan of the runs' count changes; the weight sum is a segmented fp64 scan
-// that restarts at zero at every cut where no segment is active (a rounding
-// residue never carries past such a cut), and a sum rounded below zero is
-// written as zero.
+// segment is active.  One workgroup per position walks the cuts in tiles of
+// kRcutTile: each thread takes kRcutPer consecutive cuts of the tile and
+// sums their events (one load each of the event's states and signed count;
+// alpha and beta come from LDS), a block scan of the active-segment counts
+// marks the cuts where no segment is active, and a segmented fp64 scan
+// restarts the weight sum at exactly zero there (a rounding residue never
+// carries past such a cut); a sum rounded below zero is written as zero.
 constexpr int kRcutThreads = 256;
+constexpr int kRcutPer = 8;
+constexpr int kRcutTile = kRcutThreads * kRcutPer;
 
 // segmented sum: (x, reset) o (y, reset') = (reset' ? y : x + y, reset | reset')
 struct SegSum {
@@ -192,6 +195,8 @@ __global__ __launch_bounds__(kRcutThreads) void marg_rcut(DevTable d, StepView s
     __shared__ int sh_cnt[kRcutThreads];
     __shared__ double sh_x[kRcutThreads];
     __shared__ int sh_r[kRcutThreads];
+    __shared__ int sh_act;
+    __shared__ double sh_carry;
     const int pos = blockIdx.x;
     const int tid = threadIdx.x;
     const int b = pos / sv.L, i = pos % sv.L;
@@ -206,79 +211,92 @@ __global__ __launch_bounds__(kRcutThreads) void marg_rcut(DevTable d, StepView s
         al = abs_;
         be = abs_ + sv.Sp;
     }
-    const int per = (d.ncut + kRcutThreads - 1) / kRcutThreads;
-    const int c0 = min(tid * per, d.ncut), c1 = min(c0 + per, d.ncut);
-    // count changes of this run, then the active count before it
-    int dc = 0;
-    for (int k = d.cut_off[c0]; k < d.cut_off[c1]; ++k) dc += (d.cut_ev[k] & 1) ? -1 : 1;
-    sh_cnt[tid] = dc;
-    __syncthreads();
-    // exclusive scan of the count changes (Hillis-Steele over the block)
-    for (int o = 1; o < kRcutThreads; o <<= 1) {
-        const int v = tid >= o ? sh_cnt[tid - o] : 0;
-        __syncthreads();
-        sh_cnt[tid] += v;
-        __syncthreads();
+    if (tid == 0) {
+        sh_act = 0;
+        sh_carry = 0.0;
     }
-    const int act0 = sh_cnt[tid] - dc;
-    auto weight = [&](int ev) {
-        const int sg = ev >> 1;
-        const int q = d.seg_pair[sg];
-        return (double)al[d.pair_a[q]] * (double)be[d.pair_b[q]] * (double)d.seg_cnt[sg];
-    };
-    // this run's segmented sum
-    SegSum mine{0.0, 0};
-    {
-        int act = act0;
-        for (int c = c0; c < c1; ++c) {
-            for (int k = d.cut_off[c]; k < d.cut_off[c + 1]; ++k) {
-                const int ev = d.cut_ev[k];
-                const double w = weight(ev);
-                if (ev & 1) {
-                    mine.x -= w;
-                    --act;
-                } else {
-                    mine.x += w;
-                    ++act;
-                }
-            }
-            if (act == 0) mine = SegSum{0.0, 1};
-        }
-    }
-    // inclusive segmented scan over the runs, then the carry into this run
-    sh_x[tid] = mine.x;
-    sh_r[tid] = mine.reset;
-    __syncthreads();
-    for (int o = 1; o < kRcutThreads; o <<= 1) {
-        SegSum v{0.0, 0};
-        const bool has = tid >= o;
-        if (has) v = SegSum{sh_x[tid - o], sh_r[tid - o]};
-        __syncthreads();
-        if (has) {
-            const SegSum r = seg_combine(v, SegSum{sh_x[tid], sh_r[tid]});
-            sh_x[tid] = r.x;
-            sh_r[tid] = r.reset;
-        }
-        __syncthreads();
-    }
-    double R = tid > 0 ? sh_x[tid - 1] : 0.0;
-    // write the run
     float *out = rcut + (size_t)pos * d.ncut;
-    int act = act0;
-    for (int c = c0; c < c1; ++c) {
-        for (int k = d.cut_off[c]; k < d.cut_off[c + 1]; ++k) {
-            const int ev = d.cut_ev[k];
-            const double w = weight(ev);
-            if (ev & 1) {
-                R -= w;
-                --act;
-            } else {
-                R += w;
-                ++act;
+    for (int t0 = 0; t0 < d.ncut; t0 += kRcutTile) {
+        __syncthreads();  // alpha/beta staged; the previous tile's carry is final
+        const int c0 = min(t0 + tid * kRcutPer, d.ncut), c1 = min(c0 + kRcutPer, d.ncut);
+        const int k0 = d.cut_off[c0];
+        int off[kRcutPer + 1];
+#pragma unroll
+        for (int j = 0; j <= kRcutPer; ++j) off[j] = d.cut_off[min(c0 + j, c1)];
+        // per cut: signed weight sum and count change of its events
+        double dw[kRcutPer];
+        int dc[kRcutPer];
+        int dsum = 0;
+#pragma unroll
+        for (int j = 0; j < kRcutPer; ++j) {
+            double w = 0.0;
+            int cnt = 0;
+            for (int k = off[j]; k < off[j + 1]; ++k) {
+                const float sw = d.ev_w[k];
+                w += (double)al[d.ev_a[k]] * (double)be[d.ev_b[k]] * (double)sw;
+                cnt += sw < 0.f ? -1 : 1;
+            }
+            dw[j] = w;
+            dc[j] = cnt;
+            dsum += cnt;
+        }
+        (void)k0;
+        // active count before this thread's cuts: exclusive block scan + the tile's carry-in
+        sh_cnt[tid] = dsum;
+        __syncthreads();
+        for (int o = 1; o < kRcutThreads; o <<= 1) {
+            const int v = tid >= o ? sh_cnt[tid - o] : 0;
+            __syncthreads();
+            sh_cnt[tid] += v;
+            __syncthreads();
+        }
+        const int act0 = sh_act + sh_cnt[tid] - dsum;
+        // this thread's segmented sum over its cuts
+        SegSum mine{0.0, 0};
+        {
+            int act = act0;
+#pragma unroll
+            for (int j = 0; j < kRcutPer; ++j) {
+                act += dc[j];
+                mine.x += dw[j];
+                if (c0 + j < c1 && act == 0) mine = SegSum{0.0, 1};
             }
         }
-        if (act == 0) R = 0.0;
-        out[c] = R > 0.0 ? (float)R : 0.f;
+        sh_x[tid] = mine.x;
+        sh_r[tid] = mine.reset;
+        __syncthreads();
+        for (int o = 1; o < kRcutThreads; o <<= 1) {
+            SegSum v{0.0, 0};
+            const bool has = tid >= o;
+            if (has) v = SegSum{sh_x[tid - o], sh_r[tid - o]};
+            __syncthreads();
+            if (has) {
+                const SegSum r = seg_combine(v, SegSum{sh_x[tid], sh_r[tid]});
+                sh_x[tid] = r.x;
+                sh_r[tid] = r.reset;
+            }
+            __syncthreads();
+        }
+        // carry into this thread: the previous tile's running sum combined
+        // with the runs before it in this tile
+        const SegSum before = tid > 0 ? seg_combine(SegSum{sh_carry, 0}, SegSum{sh_x[tid - 1], sh_r[tid - 1]})
+                                      : SegSum{sh_carry, 0};
+        double R = before.x;
+        int act = act0;
+#pragma unroll
+        for (int j = 0; j < kRcutPer; ++j) {
+            if (c0 + j < c1) {
+                act += dc[j];
+                R += dw[j];
+                if (act == 0) R = 0.0;
+                out[c0 + j] = R > 0.0 ? (float)R : 0.f;
+            }
+        }
+        __syncthreads();  // every thread has read sh_carry / sh_act of this tile
+        if (tid == kRcutThreads - 1) {
+            sh_carry = seg_combine(SegSum{sh_carry, 0}, SegSum{sh_x[tid], sh_r[tid]}).x;
+            sh_act = act0 + dsum;
+        }
     }
 }
 

@@ -80,6 +80,9 @@ void build_image(HostTable &t)
     append_section(t.image, t.offs, t.sel_lb);
     append_section(t.image, t.offs, t.ind_pair);
     append_section(t.image, t.offs, t.dense_bits);
+    append_section(t.image, t.offs, t.ev_a);
+    append_section(t.image, t.offs, t.ev_b);
+    append_section(t.image, t.offs, t.ev_w);
     t.image.resize((t.image.size() + 255) & ~size_t(255));
 }
 
@@ -118,6 +121,9 @@ DevTable HostTable::device_view() const
     d.n_ind = (int32_t)ind_pair.size();
     nxt(d.dense_bits);
     d.dense_words = (V + 31) / 32;
+    nxt(d.ev_a);
+    nxt(d.ev_b);
+    nxt(d.ev_w);
     d.n_tm = (int32_t)tm_pair.size();
     if (map_n.empty()) {
         d.map_n = nullptr;
@@ -548,6 +554,16 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
     t.seg_pair.resize(t.seg_lo.size());
     for (int32_t q = 0; q < np; ++q)
         for (int32_t s = t.seg_off[q]; s < t.seg_off[q + 1]; ++s) t.seg_pair[s] = q;
+    // per cut event: the states (a, b) of its pair and its count, negative at a segment end
+    t.ev_a.resize(t.cut_ev.size());
+    t.ev_b.resize(t.cut_ev.size());
+    t.ev_w.resize(t.cut_ev.size());
+    for (size_t k = 0; k < t.cut_ev.size(); ++k) {
+        const int32_t ev = t.cut_ev[k], sg = ev >> 1, q = t.seg_pair[sg];
+        t.ev_a[k] = t.pair_a[q];
+        t.ev_b[k] = t.pair_b[q];
+        t.ev_w[k] = (ev & 1) ? -t.seg_cnt[sg] : t.seg_cnt[sg];
+    }
     t.tok2sel.assign(ns > 0 ? (size_t)V : 0, -1);
     for (int32_t s = 0; s < ns; ++s) t.tok2sel[t.sel_tok[s]] = s;
     t.tok2cut.assign(t.ncut() > 0 ? (size_t)V : 0, -1);
