@@ -273,7 +273,16 @@ __global__ __launch_bounds__(kDenseThreads) void emission_dense(
 constexpr int kStreamThreads = 256;
 
 // fp64 prefix sums of the row at every range cut point: cutp[pos][c] =
-// sum_{v < cuts[c]} p[pos][v]
+// sum_{v < cuts[c]} p[pos][v].  One workgroup per position reads the row in
+// tiles of kRangeTile tokens, each thread a run of kRangePer consecutive
+// tokens (four float4 loads; the next tile's loads are in flight while one
+// is summed).  A thread sums its run in fp64, one block scan gives the runs'
+// offsets, and each thread then writes the prefix at every cut point inside
+// its run: the run's first cut index (tok2cut) and its 16 cut bits (one word
+// of cutbits) are loaded with the run, so the writes need no further loads.
+constexpr int kRangePer = 16;
+constexpr int kRangeTile = kStreamThreads * kRangePer;
+
 __global__ __launch_bounds__(kStreamThreads) void emission_ranges(
     DevTable d, const float *__restrict__ p, int L, double *__restrict__ cutp,
     int32_t *__restrict__ status)
@@ -281,42 +290,88 @@ __global__ __launch_bounds__(kStreamThreads) void emission_ranges(
     const int pos = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float *row = p + (size_t)pos * d.V;
-    __shared__ double sh_incl[kStreamThreads];
-    __shared__ double sh_wsum[4];
+    double *out = cutp + (size_t)pos * d.ncut;
+    __shared__ double sh_wsum[kStreamThreads / 64];
     __shared__ int sh_bad;
     if (tid == 0) sh_bad = 0;
-    double carry = 0.0;
-    int cptr = 0;
-    int bad = 0;
-    for (int c0 = 0; c0 < d.V; c0 += kStreamThreads) {
-        const int v = c0 + tid;
-        float x = 0.f;
-        if (v < d.V) {
-            x = row[v];
-            bad |= !(x >= 0.f);
+    const bool vec = (d.V & 3) == 0 && ((uintptr_t)row & 15) == 0;
+    struct Run {
+        float x[kRangePer];
+        int c_lo;       // first cut index at or after the run's first token
+        uint32_t cbit;  // the run's cut bits (bit k: a cut at token v0 + k)
+    };
+    const int nwords = (d.V + 31) / 32;
+    auto load = [&](Run &r, int t0) {
+        const int v0 = t0 + kRangePer * tid;
+        r.c_lo = d.tok2cut[min(max(v0 - 1, 0), d.V - 1)];
+        r.cbit = d.cutbits[min(v0 >> 5, nwords - 1)];
+        if (vec) {
+            const float4 *r4 = reinterpret_cast<const float4 *>(row);
+            const int g0 = v0 >> 2, gl = (d.V >> 2) - 1;
+#pragma unroll
+            for (int j = 0; j < kRangePer / 4; ++j) {
+                const float4 y = r4[min(g0 + j, gl)];
+                r.x[4 * j] = y.x;
+                r.x[4 * j + 1] = y.y;
+                r.x[4 * j + 2] = y.z;
+                r.x[4 * j + 3] = y.w;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kRangePer; ++j) r.x[j] = row[min(v0 + j, d.V - 1)];
         }
-        const double inc = wave_incl_scan_d((double)x, lane);
+    };
+    double carry = 0.0;
+    int bad = 0;
+    Run A, B;
+    load(A, 0);
+    auto tile = [&](const Run &r, int t0) {
+        const int v0 = t0 + kRangePer * tid;
+        // this run's values (zero past the row) and their fp64 sum
+        float xs[kRangePer];
+        double s = 0.0;
+#pragma unroll
+        for (int j = 0; j < kRangePer; ++j) {
+            xs[j] = v0 + j < d.V ? r.x[j] : 0.f;
+            bad |= !(xs[j] >= 0.f);
+            s += (double)xs[j];
+        }
+        // exclusive block scan of the run sums
+        const double inc = wave_incl_scan_d(s, lane);
         if (lane == 63) sh_wsum[wave] = inc;
         __syncthreads();
-        double off = 0.0;
-        for (int w = 0; w < wave; ++w) off += sh_wsum[w];
-        sh_incl[tid] = off + inc;
-        __syncthreads();
-        // cut points inside this chunk (sorted, unique)
-        const int idx = cptr + tid;
-        const int c = (idx < d.ncut) ? d.cuts[idx] : 0x7fffffff;
-        const bool in = c < c0 + kStreamThreads && c < d.V;
-        if (in) {
-            const int k = c - c0;
-            cutp[(size_t)pos * d.ncut + idx] = carry + (k > 0 ? sh_incl[k - 1] : 0.0);
+        double off = carry + (inc - s);
+        double tot = carry;
+        for (int w = 0; w < kStreamThreads / 64; ++w) {
+            if (w < wave) off += sh_wsum[w];
+            tot += sh_wsum[w];
         }
-        cptr += __syncthreads_count(in);
-        carry += sh_incl[kStreamThreads - 1];
-        __syncthreads();
+        __syncthreads();  // sh_wsum is rewritten by the next tile
+        // cut points inside [v0, v0 + kRangePer): consecutive indices from c
+        if (v0 < d.V) {
+            int c = v0 > 0 ? r.c_lo + 1 : 0;
+            uint32_t m = (r.cbit >> (v0 & 31)) & ((1u << kRangePer) - 1u);
+            if (v0 + kRangePer > d.V) m &= (1u << (d.V - v0)) - 1u;
+            double run = off;
+            int k = 0;
+            while (m) {
+                const int at = __ffs(m) - 1;
+                m &= m - 1u;
+                for (; k < at; ++k) run += (double)xs[k];
+                out[c++] = run;
+            }
+        }
+        carry = tot;
+    };
+    for (int t0 = 0; t0 < d.V; t0 += 2 * kRangeTile) {
+        load(B, t0 + kRangeTile);
+        tile(A, t0);
+        load(A, t0 + 2 * kRangeTile);
+        if (t0 + kRangeTile < d.V) tile(B, t0 + kRangeTile);
     }
     // cut points equal to V hold the row total
-    for (int idx = cptr + tid; idx < d.ncut; idx += kStreamThreads)
-        cutp[(size_t)pos * d.ncut + idx] = carry;
+    const int nin = d.tok2cut[d.V - 1] + 1;  // cuts below V
+    for (int idx = nin + tid; idx < d.ncut; idx += kStreamThreads) out[idx] = carry;
     if (bad) atomicOr(&sh_bad, 1);
     __syncthreads();
     if (tid == 0 && sh_bad) atomicOr(&status[pos / L], (int)FA_ROW_BADPROB);

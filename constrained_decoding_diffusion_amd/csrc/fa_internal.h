@@ -92,6 +92,7 @@ struct DevTable {
     const int32_t *ev_a;       // [2 nseg] per cut event (cut_ev order): the states of its pair
     const int32_t *ev_b;
     const float *ev_w;         // [2 nseg] its count, negative at a segment end
+    const uint32_t *cutbits;   // [(V+31)/32] bit v%32 of word v/32: a cut point at token v < V
     const int32_t *sel_lb;     // [V/256 + 2] first sel_tok index at or after token 256 t
     int32_t n_tm;              // token-major LIST entries
 };
@@ -116,6 +117,7 @@ struct HostTable {
     std::vector<uint32_t> dense_bits;
     std::vector<int32_t> ev_a, ev_b;
     std::vector<float> ev_w;
+    std::vector<uint32_t> cutbits;
     std::vector<int32_t> sel_lb;
     bool has_cnt = false;
     bool use_sel = false;

@@ -83,6 +83,7 @@ void build_image(HostTable &t)
     append_section(t.image, t.offs, t.ev_a);
     append_section(t.image, t.offs, t.ev_b);
     append_section(t.image, t.offs, t.ev_w);
+    append_section(t.image, t.offs, t.cutbits);
     t.image.resize((t.image.size() + 255) & ~size_t(255));
 }
 
@@ -124,6 +125,7 @@ DevTable HostTable::device_view() const
     nxt(d.ev_a);
     nxt(d.ev_b);
     nxt(d.ev_w);
+    nxt(d.cutbits);
     d.n_tm = (int32_t)tm_pair.size();
     if (map_n.empty()) {
         d.map_n = nullptr;
@@ -566,6 +568,10 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
     }
     t.tok2sel.assign(ns > 0 ? (size_t)V : 0, -1);
     for (int32_t s = 0; s < ns; ++s) t.tok2sel[t.sel_tok[s]] = s;
+    // bit v % 32 of word v / 32: a cut point sits at token v (cuts below V)
+    t.cutbits.assign(t.ncut() > 0 ? (size_t)(V + 31) / 32 : 0, 0u);
+    for (int32_t c = 0; c < t.ncut(); ++c)
+        if (t.cuts[c] < V) t.cutbits[t.cuts[c] / 32] |= 1u << (t.cuts[c] % 32);
     t.tok2cut.assign(t.ncut() > 0 ? (size_t)V : 0, -1);
     for (int32_t c = 0, v = 0; v < (t.ncut() > 0 ? V : 0); ++v) {
         while (c < t.ncut() && t.cuts[c] <= v) ++c;
