@@ -409,17 +409,17 @@ __global__ void emission_pairs(DevTable d, int L, EmitSrc src, float *__restrict
 
 // values of the pairs that are not one token's probability (ind_pair), for
 // the one-pass leaf writer and the leaf level of the marginal message pass:
+// one pair per thread (each value is a short chain of dependent loads),
 // grid.x over groups of those pairs, grid.y over positions
-__global__ void emission_indirect(DevTable d, int L, EmitSrc src, int32_t *__restrict__ status)
+constexpr int kIndThreads = 128;
+
+__global__ __launch_bounds__(kIndThreads) void emission_indirect(DevTable d, int L, EmitSrc src,
+                                                                int32_t *__restrict__ status)
 {
-    const int j0 = (blockIdx.x * blockDim.x + threadIdx.x) * kPairsPerThread;
+    const int j = blockIdx.x * blockDim.x + threadIdx.x;
     const size_t pos = blockIdx.y;
     int bad = 0;
-#pragma unroll
-    for (int u = 0; u < kPairsPerThread; ++u) {
-        const int j = j0 + u;
-        if (j < d.n_ind) src.ndval[pos * d.n_ind + j] = pair_value_direct(d, d.ind_pair[j], pos, src, bad);
-    }
+    if (j < d.n_ind) src.ndval[pos * d.n_ind + j] = pair_value_direct(d, d.ind_pair[j], pos, src, bad);
     if (bad) atomicOr(&status[pos / L], (int)FA_ROW_BADPROB);
 }
 
@@ -686,8 +686,8 @@ int launch_build_transitions(const DevTable &d, const Geometry &g, const float *
     StepView sv = step_view(g);
     if (fused) {
         if (d.n_ind > 0) {
-            dim3 igrid((d.n_ind + 256 * kPairsPerThread - 1) / (256 * kPairsPerThread), npos);
-            emission_indirect<<<igrid, 256, 0, st>>>(d, g.L, src, status);
+            dim3 igrid((d.n_ind + kIndThreads - 1) / kIndThreads, npos);
+            emission_indirect<<<igrid, kIndThreads, 0, st>>>(d, g.L, src, status);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return (int)e;
         }

@@ -80,11 +80,12 @@ __device__ int wave_icdf_regs(const float (&w)[C], int n, float u, int lane)
 }
 
 // root: z_Lpad over the accepting states
-__global__ void sample_root(DevTable d, StepView sv, const float *__restrict__ tree,
-                            const int32_t *__restrict__ meta, uint64_t seed,
-                            int32_t *__restrict__ zc, int32_t *__restrict__ status)
+// the root draw of row b by one wavefront: z[0] = start, z[Lpad] = the
+// drawn accepting state (-1, and the row flagged, when every weight vanishes)
+__device__ void draw_root(const DevTable &d, const StepView &sv, const float *__restrict__ tree,
+                          const int32_t *__restrict__ meta, uint64_t seed, int b, int lane,
+                          int32_t *__restrict__ zc, int32_t *__restrict__ status)
 {
-    const int b = blockIdx.x, lane = threadIdx.x;
     int32_t *z = zc + (size_t)b * (sv.Lpad + 1);
     const float *R = sv.mat_ptr(tree, b, 1) + (size_t)d.start * sv.Sp;
     const int32_t *co = sv.meta_ptr(meta, b, 1, 1);
@@ -108,6 +109,14 @@ __global__ void sample_root(DevTable d, StepView sv, const float *__restrict__ t
         z[sv.Lpad] = j >= 0 ? d.acc[j] : -1;
         if (j < 0 && status[b] == 0) atomicOr(&status[b], (int)FA_ROW_UNDERFLOW);
     }
+}
+
+// root draw alone (a tree of one leaf, Lpad = 1)
+__global__ void sample_root(DevTable d, StepView sv, const float *__restrict__ tree,
+                            const int32_t *__restrict__ meta, uint64_t seed,
+                            int32_t *__restrict__ zc, int32_t *__restrict__ status)
+{
+    draw_root(d, sv, tree, meta, seed, blockIdx.x, threadIdx.x, zc, status);
 }
 
 // one midpoint level: node n = nn + idx covers [l, r); children 2n (stored as
@@ -192,6 +201,10 @@ __global__ __launch_bounds__(64 << (kSubDepth - 1)) void sample_levels(
     const int unit = span0 / q;
     const int l0 = idx0 * span0;
     int32_t *z = zc + (size_t)b * (sv.Lpad + 1);
+    if (level0 == 1) {  // the first launch also draws the root (wavefront 0)
+        if (wave == 0) draw_root(d, sv, tree, meta, seed, b, lane, zc, status);
+        __syncthreads();
+    }
     if (threadIdx.x == 0) {
         zs[0] = z[l0];
         zs[q] = z[l0 + span0];
@@ -529,9 +542,12 @@ int launch_sample(const DevTable &d, const Geometry &g, const float *p, const fl
     }
     StepView sv = step_view(g);
     int32_t *zc = (int32_t *)(ws + w.zc);
-    sample_root<<<g.B, 64, 0, st>>>(d, sv, tree, meta, seed, zc, status);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return (int)e;
+    hipError_t e;
+    if (g.K == 0) {  // otherwise the first midpoint launch draws the root
+        sample_root<<<g.B, 64, 0, st>>>(d, sv, tree, meta, seed, zc, status);
+        e = hipGetLastError();
+        if (e != hipSuccess) return (int)e;
+    }
     for (int level0 = 1; level0 <= g.K; level0 += kSubDepth) {
         const int depth = std::min(kSubDepth, g.K - level0 + 1);
         const int nn0 = 1 << (level0 - 1);
