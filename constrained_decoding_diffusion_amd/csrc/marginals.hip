@@ -51,7 +51,7 @@ template <int CW>
 __global__ __launch_bounds__(kMsgThreads) void marg_level(
     DevTable d, StepView sv, const float *__restrict__ tree, const int32_t *__restrict__ meta,
     int nn, float *__restrict__ va, int32_t *__restrict__ ea, float *__restrict__ vb,
-    int32_t *__restrict__ eb)
+    int32_t *__restrict__ eb, int top)
 {
     constexpr int PER = CW / 64;  // columns per lane: 4 or 1
     extern __shared__ float gsh[];  // [Sp] normalized input weights, then [Sp] row folds
@@ -70,7 +70,25 @@ __global__ __launch_bounds__(kMsgThreads) void marg_level(
     int32_t *ebase = beta ? eb : ea;
     const float *vin = vbase + ((size_t)b * (sv.Lpad + 1) + src) * sv.Sp;
     float *vout = vbase + ((size_t)b * (sv.Lpad + 1) + m) * sv.Sp;
-    const int ein = ebase[(size_t)b * (sv.Lpad + 1) + src];
+    if (top) {
+        // the top level builds its input, the boundary vector alpha_0 = e_start
+        // or beta_Lpad = 1 on F (exponent 0), in LDS; column block 0 also
+        // stores it for the later passes
+        for (int a = tid; a < sv.Sp; a += kMsgThreads) gsh[a] = 0.f;
+        __syncthreads();
+        if (beta) {
+            for (int k = tid; k < d.n_acc; k += kMsgThreads) gsh[d.acc[k]] = 1.f;
+        } else if (tid == 0) {
+            gsh[d.start] = 1.f;
+        }
+        __syncthreads();
+        if (cb == 0) {
+            float *bound = vbase + ((size_t)b * (sv.Lpad + 1) + src) * sv.Sp;
+            for (int a = tid; a < sv.Sp; a += kMsgThreads) bound[a] = gsh[a];
+            if (tid == 0) ebase[(size_t)b * (sv.Lpad + 1) + src] = 0;
+        }
+    }
+    const int ein = top ? 0 : ebase[(size_t)b * (sv.Lpad + 1) + src];
     const float *P = sv.mat_ptr(tree, b, h);
     const int32_t *ro = sv.meta_ptr(meta, b, h, 0);
     const int32_t *co = sv.meta_ptr(meta, b, h, 1);
@@ -78,7 +96,7 @@ __global__ __launch_bounds__(kMsgThreads) void marg_level(
     // G = max_a e(in[a]) + ro[a] + rf[a]; the per-row exponents go to LDS
     int e = kNeg;
     for (int a = tid; a < d.S; a += kMsgThreads) {
-        const float x = vin[a];
+        const float x = top ? gsh[a] : vin[a];
         const int s = add_exp(ro[a], rf[a]);
         rsh[a] = s;
         gsh[a] = x;
@@ -858,10 +876,19 @@ int launch_marginals(const DevTable &d, const Geometry &g, const float *p, const
     float *va = (float *)(ws + w.va), *vb = (float *)(ws + w.vb);
     int32_t *ea = (int32_t *)(ws + w.ea), *eb = (int32_t *)(ws + w.eb);
     float *rcut = (float *)(ws + w.rcut);
-    marg_init<<<g.B, 256, 0, st>>>(d, sv, va, ea, vb, eb);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return (int)e;
     const size_t lds = (size_t)g.Sp * (sizeof(float) + sizeof(int));
+    // the leaf level straight from pair values when the leaf entries exist
+    // (Sp < 65536) and their terms fit in LDS
+    const bool sparse_leaf = g.K >= 1 && g.Sp <= kLeafTile && d.npairs <= kLeafMsgMax &&
+                             ((size_t)d.npairs + 2 * (size_t)d.S) * 4 <= 64 * 1024;
+    // the boundary vectors: built by the top marg_level launch, else here
+    const bool init_in_top = g.K >= 1 && !(g.K == 1 && sparse_leaf);
+    hipError_t e;
+    if (!init_in_top) {
+        marg_init<<<g.B, 256, 0, st>>>(d, sv, va, ea, vb, eb);
+        e = hipGetLastError();
+        if (e != hipSuccess) return (int)e;
+    }
     if (lds > 48 * 1024) {  // large automata: allow the dynamic LDS the kernels need
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(&marg_level<256>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -870,10 +897,6 @@ int launch_marginals(const DevTable &d, const Geometry &g, const float *p, const
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return (int)e;
     }
-    // the leaf level straight from pair values when the leaf entries exist
-    // (Sp < 65536) and their terms fit in LDS
-    const bool sparse_leaf = g.K >= 1 && g.Sp <= kLeafTile && d.npairs <= kLeafMsgMax &&
-                             ((size_t)d.npairs + 2 * (size_t)d.S) * 4 <= 64 * 1024;
     for (int level = 1; level <= g.K; ++level) {
         const int nn = 1 << (level - 1);
         const int products = g.B * nn * 2;
@@ -890,12 +913,13 @@ int launch_marginals(const DevTable &d, const Geometry &g, const float *p, const
             if (e != hipSuccess) return (int)e;
             continue;
         }
+        const int top = level == 1 && init_in_top;
         if (products * ((g.Sp + 255) / 256) >= 256) {
             dim3 grid((g.Sp + 255) / 256, products);
-            marg_level<256><<<grid, kMsgThreads, lds, st>>>(d, sv, tree, meta, nn, va, ea, vb, eb);
+            marg_level<256><<<grid, kMsgThreads, lds, st>>>(d, sv, tree, meta, nn, va, ea, vb, eb, top);
         } else {
             dim3 grid((g.Sp + 63) / 64, products);
-            marg_level<64><<<grid, kMsgThreads, lds, st>>>(d, sv, tree, meta, nn, va, ea, vb, eb);
+            marg_level<64><<<grid, kMsgThreads, lds, st>>>(d, sv, tree, meta, nn, va, ea, vb, eb, top);
         }
         e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
