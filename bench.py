@@ -229,6 +229,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", type=int, default=3, help="preset 1..5 (default 3)")
+    ap.add_argument("--separate", action="store_true",
+                    help="fa_sample then fa_marginals instead of fa_sample_marginals")
     ap.add_argument("--copy-calib", action="store_true",
                     help="first run one plain device copy of 1 GiB (counter calibration)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -277,6 +279,13 @@ def main():
                 ("marg_q", fa.FA_PROF_MARG_Q)]
     hev = HipEvents()
 
+    # sampling and marginals: one fa_sample_marginals call (default), or
+    # fa_sample then fa_marginals (--separate); the outputs are the same
+    if args.separate:
+        names = ["build_transitions", "span_tree", "sample", "marginals"]
+    else:
+        names = ["build_transitions", "span_tree", "sample_marginals"]
+
     def one_step(seed, ev=None, kev=None):
         bufs.status.zero_()
         if kev:
@@ -286,15 +295,19 @@ def main():
         if ev: ev[1].record()
         fa.span_tree(tb, bufs, stream)
         if ev: ev[2].record()
-        fa.sample(tb, p, bufs, seed, stream)
-        if ev: ev[3].record()
-        fa.marginals(tb, p, bufs, fa.FA_CONF_PROB, stream, write_q=True)
-        if ev: ev[4].record()
+        if args.separate:
+            fa.sample(tb, p, bufs, seed, stream)
+            if ev: ev[3].record()
+            fa.marginals(tb, p, bufs, fa.FA_CONF_PROB, stream, write_q=True)
+        else:
+            fa.sample_marginals(tb, p, bufs, seed, fa.FA_CONF_PROB, stream, write_q=True)
+        if ev: ev[len(names)].record()
 
     for s in range(args.warmup):
         one_step(w.seed + s)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(args.steps)]
     kevs = []
     for s in range(args.steps):
         name, pid = prof_ids[s % len(prof_ids)]
@@ -311,7 +324,6 @@ def main():
     wall = time.perf_counter() - wall0
     fa.profile_kernel(fa.FA_PROF_NONE)
     total_ms = t_start.elapsed_time(t_end)
-    names = ["build_transitions", "span_tree", "sample", "marginals"]
     stage_ms = {n: 0.0 for n in names}
     for ev in evs:
         for k, n in enumerate(names):
@@ -335,11 +347,15 @@ def main():
                                   gbs=work["a1_bytes"] / (stage_us["build_transitions"] * 1e3)),
         "span_tree": dict(us=stage_us["span_tree"], bound="mfma", algorithmic_flops=work["a2_flops"],
                           tflops=work["a2_flops"] / (stage_us["span_tree"] * 1e6)),
-        "sample": dict(us=stage_us["sample"], bound="latency"),
-        "marginals": dict(us=stage_us["marginals"], bound="hbm", algorithmic_bytes=work["a4_bytes"],
-                          gbs=work["a4_bytes"] / (stage_us["marginals"] * 1e3)),
     }
-    for n in ("build_transitions", "marginals"):
+    if args.separate:
+        stages["sample"] = dict(us=stage_us["sample"], bound="latency")
+        last = "marginals"
+    else:
+        last = "sample_marginals"
+    stages[last] = dict(us=stage_us[last], bound="hbm", algorithmic_bytes=work["a4_bytes"],
+                        gbs=work["a4_bytes"] / (stage_us[last] * 1e3))
+    for n in ("build_transitions", last):
         stages[n]["frac"] = stages[n]["gbs"] / HBM_PEAK_GBS
     stages["span_tree"]["frac"] = stages["span_tree"]["tflops"] / FP32_MFMA_PEAK_TFLOPS
     kernels = {}
@@ -371,6 +387,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.describe(), "B": w.B, "L": w.L, "S": w.aut.S, "V": w.aut.V,
+                   "calls": "separate" if args.separate else "joint",
                    "sequence_steps_per_s": w.B * 1000.0 / ms_per_step},
         "roofline": roof,
         "kernels": kernels,

@@ -22,7 +22,7 @@ FA_PROF_NONE, FA_PROF_EMISSION_DENSE, FA_PROF_TREE_LEVEL1, FA_PROF_MARG_Q = rang
 
 EXPORTS = ["fa_compile_table", "fa_table_upload", "fa_table_destroy", "fa_table_info",
            "fa_table_state_map", "fa_sizes", "fa_build_transitions", "fa_span_tree", "fa_sample",
-           "fa_marginals", "fa_strerror", "fa_profile_kernel"]
+           "fa_marginals", "fa_sample_marginals", "fa_strerror", "fa_profile_kernel"]
 
 
 class FaError(RuntimeError):
@@ -55,6 +55,7 @@ def lib():
     L.fa_span_tree.argtypes = [P, I32, I32, P, P, P, SZ, P, P, P]
     L.fa_sample.argtypes = [P, P, I32, I32, P, P, U64, P, P, P, SZ, P, P]
     L.fa_marginals.argtypes = [P, P, I32, I32, P, P, P, P, I32, P, P, P, SZ, P, P]
+    L.fa_sample_marginals.argtypes = [P, P, I32, I32, P, P, P, U64, I32, P, P, P, P, P, SZ, P, P]
     L.fa_profile_kernel.argtypes = [I32, P, P]
     L.fa_strerror.argtypes = [C.c_int]
     L.fa_strerror.restype = C.c_char_p
@@ -180,6 +181,15 @@ def marginals(table: Table, p, bufs: StepBuffers, conf_mode: int, stream, write_
         _ptr(bufs.ws), bufs.ws.numel(), _ptr(bufs.status), C.c_void_p(stream)))
 
 
+def sample_marginals(table: Table, p, bufs: StepBuffers, seed: int, conf_mode: int, stream,
+                     write_q=True):
+    _check("fa_sample_marginals", lib().fa_sample_marginals(
+        table.handle, _ptr(p), bufs.B, bufs.L, _ptr(bufs.tree), _ptr(bufs.meta), _ptr(bufs.logZ),
+        C.c_uint64(seed), conf_mode, _ptr(bufs.states), _ptr(bufs.tokens),
+        _ptr(bufs.q if write_q else None), _ptr(bufs.conf), _ptr(bufs.ws), bufs.ws.numel(),
+        _ptr(bufs.status), C.c_void_p(stream)))
+
+
 def profile_kernel(which: int, start_event=None, stop_event=None):
     """Measurement hook: bracket the launches of one kernel with two HIP
     events (raw hipEvent_t handles as ints), FA_PROF_NONE to clear."""
@@ -188,9 +198,12 @@ def profile_kernel(which: int, start_event=None, stop_event=None):
 
 
 def step(table: Table, p, seed: int, bufs: StepBuffers = None, conf_mode: int = FA_CONF_PROB,
-         write_q: bool = True):
+         write_q: bool = True, joint: bool = True):
     """One constrained denoising step on torch's current stream: emission
-    reduce, span tree, sampling, marginals.  p: cuda float32 [B, L, V]."""
+    reduce, span tree, sampling, marginals.  p: cuda float32 [B, L, V].
+    joint: sampling and marginals through fa_sample_marginals (one pass over
+    p less when the draws can share the q writer's pass); else fa_sample then
+    fa_marginals.  Both give the same outputs."""
     import torch
     B, L, V = p.shape
     if V != table.info["V"]:
@@ -205,6 +218,10 @@ def step(table: Table, p, seed: int, bufs: StepBuffers = None, conf_mode: int = 
     bufs.status.zero_()
     build_transitions(table, p, bufs, stream)
     span_tree(table, bufs, stream)
-    sample(table, p, bufs, seed, stream)
-    marginals(table, p, bufs, conf_mode, stream, write_q=write_q and bufs.q is not None)
+    wq = write_q and bufs.q is not None
+    if joint:
+        sample_marginals(table, p, bufs, seed, conf_mode, stream, write_q=wq)
+    else:
+        sample(table, p, bufs, seed, stream)
+        marginals(table, p, bufs, conf_mode, stream, write_q=wq)
     return bufs

@@ -131,6 +131,45 @@ extern "C" int fa_marginals(const fa_table *t, const float *p, int32_t B, int32_
                                    conf, (uint8_t *)ws, w, row_status, stream));
 }
 
+extern "C" int fa_sample_marginals(const fa_table *t, const float *p, int32_t B, int32_t L,
+                                   const float *tree, const int32_t *meta, const double *logZ,
+                                   uint64_t seed, int32_t conf_mode, int32_t *states,
+                                   int32_t *tokens, float *q, float *conf, void *ws,
+                                   size_t ws_bytes, int32_t *row_status, fa_stream_t stream)
+{
+    int rc = ready(t);
+    if (rc) return rc;
+    Geometry g;
+    if (!make_geometry(t->h, B, L, &g)) return FA_EINVAL;
+    if (!grid_fits(g)) return FA_ETOOBIG;
+    if (conf_mode != FA_CONF_PROB && conf_mode != FA_CONF_NEGENT) return FA_EINVAL;
+    if (B == 0) return FA_OK;
+    WsLayout w = ws_layout(t->h, g);
+    if (!states || !row_status || !ws || ws_bytes < w.total) return FA_EINVAL;
+    if (L > 0 && (!p || !tree || !meta || !logZ || !tokens || !conf)) return FA_EINVAL;
+    const DevTable d = t->h.device_view();
+    uint8_t *wb = (uint8_t *)ws;
+    if (L == 0 || !marg_joint_ok(d, g, p, q, conf_mode, w)) {
+        rc = launch_sample(d, g, p, tree, meta, seed, states, tokens, wb, w, row_status, stream);
+        if (rc || L == 0) return hip_rc(rc);
+        return hip_rc(launch_marginals(d, g, p, tree, meta, logZ, tokens, conf_mode, q, conf, wb,
+                                       w, row_status, stream));
+    }
+    // midpoints; messages; q with the draws' chunk sums; the token draws;
+    // the confidence of the drawn tokens and the rows the draws flagged
+    rc = launch_sample_states(d, g, tree, meta, seed, wb, w, row_status, stream);
+    if (!rc) rc = launch_marg_pass(d, g, p, tree, meta, wb, w, stream);
+    if (!rc)
+        rc = launch_marg_out(d, g, p, logZ, nullptr, conf_mode, q, conf, wb, w, 1, row_status,
+                             stream);
+    if (!rc)
+        rc = launch_sample_tokens(d, g, p, seed, states, tokens, wb, w, true, row_status, stream);
+    if (!rc)
+        rc = launch_marg_out(d, g, p, logZ, tokens, conf_mode, q, conf, wb, w, 2, row_status,
+                             stream);
+    return hip_rc(rc);
+}
+
 extern "C" const char *fa_strerror(int code)
 {
     switch (code) {

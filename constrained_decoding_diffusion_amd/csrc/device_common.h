@@ -97,6 +97,19 @@ __device__ inline double wave_sum_d(double x)
     return x;
 }
 
+// index of the pair (a, c) in the table's row-sorted pair list, or -1
+__device__ inline int pair_index(const DevTable &d, int a, int c)
+{
+    if (a < 0 || c < 0) return -1;
+    int lo = d.row_ptr[a], hi = d.row_ptr[a + 1];
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (d.pair_b[mid] < c) lo = mid + 1;
+        else hi = mid;
+    }
+    return (lo < d.row_ptr[a + 1] && d.pair_b[lo] == c) ? lo : -1;
+}
+
 __device__ inline int wave_max_i(int x)
 {
 #pragma unroll

@@ -22,6 +22,7 @@ constexpr int kDenseTile = 32;     // positions per workgroup of the dense-mask 
 constexpr int kSelMax = 8192;      // LIST tokens gathered through a compact copy of p
 constexpr int kMapMaxSp = 2048;   // dense (row, column) -> pair maps up to this Sp
 constexpr uint32_t kSelBit = 1u << 31;  // tokmask flag of LIST tokens (tables with < 32 dense pairs)
+constexpr int kRowChunk4 = 1024;   // float4 groups per chunk of a dense-pair token draw (4096 tokens)
 
 enum PairClass : int32_t { kList = 0, kDense = 1, kRange = 2 };
 
@@ -154,12 +155,15 @@ struct WsLayout {
     int32_t vchunk = 0;                        // tokens per V chunk (multiple of 256)
     int32_t sel_mode = 0;                      // token-list copy: 1 LDS-buffered, 2 gathered
     size_t zc = 0;                             // sampler: compact boundary states
+    size_t tpair = 0, tdbit = 0;               // sampler: per position the drawn pair, its dense bit
     size_t kpart = 0;                          // span tree: split-K partial tiles
     size_t va = 0, ea = 0, vb = 0, eb = 0;     // marginals: messages
     size_t rcut = 0;                           // marginals: range weights per cut
     size_t ndval = 0;                          // emission: values of the indirect pairs (persist)
     size_t pw = 0;                             // marginals: per-position pair weights
     size_t hpart = 0;                          // marginals: q ln q partial sums per row part
+    size_t tcs = 0, tcs_ok = 0;                // joint call: dense-pair chunk sums of the token draws
+    int32_t tcs_nch = 0;                       // chunks per row of those sums
     int32_t pw_nl = 0, pw_ld = 0;              // token-list weights per row, row length
     size_t total = 0;
 };
@@ -188,6 +192,32 @@ int launch_marginals(const DevTable &d, const Geometry &g, const float *p, const
                      const int32_t *meta, const double *logZ, const int32_t *tokens,
                      int32_t conf_mode, float *q, float *conf, uint8_t *ws, const WsLayout &w,
                      int32_t *status, void *stream);
+// The parts of the two calls above, for the joint call fa_sample_marginals.
+// States: the root and every midpoint (compact ids in ws at w.zc), and per
+// position the pair of its two boundary states (w.tpair: index or -1;
+// w.tdbit: its dense-mask bit or 0).  Tokens:
+// the token draws and the state output; `pre` non-null takes the dense-pair
+// chunk sums from ws at w.tcs where w.tcs_ok marks a position.
+int launch_sample_states(const DevTable &d, const Geometry &g, const float *tree,
+                         const int32_t *meta, uint64_t seed, uint8_t *ws, const WsLayout &w,
+                         int32_t *status, void *stream);
+int launch_sample_tokens(const DevTable &d, const Geometry &g, const float *p, uint64_t seed,
+                         int32_t *states, int32_t *tokens, uint8_t *ws, const WsLayout &w,
+                         bool pre, int32_t *status, void *stream);
+// Message pass (alpha/beta at every boundary, range weights per cut).
+int launch_marg_pass(const DevTable &d, const Geometry &g, const float *p, const float *tree,
+                     const int32_t *meta, uint8_t *ws, const WsLayout &w, void *stream);
+// The q writer and the confidence.  mode 0: the plain writer; 1: the
+// streaming writer that also sums the token draws' dense-pair chunks (the
+// boundary states in ws at w.zc; tokens unused); 2: after mode 1 and the
+// token draws: the PROB confidence of the sampled tokens, and zeros and -inf
+// for rows the draws flagged.  marg_joint_ok tells whether modes 1 and 2
+// apply.
+bool marg_joint_ok(const DevTable &d, const Geometry &g, const float *p, const float *q,
+                   int32_t conf_mode, const WsLayout &w);
+int launch_marg_out(const DevTable &d, const Geometry &g, const float *p, const double *logZ,
+                    const int32_t *tokens, int32_t conf_mode, float *q, float *conf, uint8_t *ws,
+                    const WsLayout &w, int mode, int32_t *status, void *stream);
 
 }  // namespace fa
 

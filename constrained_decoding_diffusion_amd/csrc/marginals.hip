@@ -568,16 +568,31 @@ __global__ __launch_bounds__(kPwThreads) void marg_pairw(DevTable d, StepView sv
 // table, the token-list weights (found by binary search over the sorted
 // token-list tokens when the mask's flag bit marks the token, or through
 // tok2sel), and the range weights at each cut.
-template <int NG, bool SELBIT, bool LISTALL, bool RANGES>
-__global__ __launch_bounds__(kQThreads) void marg_q_stream(
+//
+// The parts are whole chunks of kRowChunk4 float4 groups, so iteration `it`
+// of a part covers one chunk of the token sampler's streamed pass.  SAMP
+// (the joint call): tdbit holds the dense-mask bit of the pair the
+// position's token draw uses (0 when it is not a dense pair); for a dense
+// pair each wavefront also sums its masked p over each chunk, in the sampler's order
+// (u ascending, then x, y, z, w), and stores the sum in tcs, and part 0 sets
+// tcs_ok for the position (tokens is then unused: marg_conf_tok writes the
+// confidence after the draws).  The sums cost registers; the joint variants
+// are held to 128 VGPRs (four wavefronts per SIMD, a few spills), which
+// streams faster than three wavefronts per SIMD without spills.
+template <int NG, bool SELBIT, bool LISTALL, bool RANGES, bool SAMP>
+__global__ __launch_bounds__(kQThreads)
+__attribute__((amdgpu_waves_per_eu(SAMP && !LISTALL ? 4 : 1))) void marg_q_stream(
     DevTable d, StepView sv, const float *__restrict__ p, const double *__restrict__ logZ,
     const int32_t *__restrict__ tokens, int conf_mode, float *__restrict__ q,
     float *__restrict__ conf, const int32_t *__restrict__ ea, const int32_t *__restrict__ eb,
     const float *__restrict__ pw, int pw_ld, const float *__restrict__ rcut,
-    double *__restrict__ hpart, const int32_t *__restrict__ status)
+    double *__restrict__ hpart, const int32_t *__restrict__ status,
+    const uint32_t *__restrict__ tdbit, double *__restrict__ tcs, int32_t *__restrict__ tcs_ok,
+    int tcs_nch)
 {
     constexpr bool LISTS = SELBIT || LISTALL;
     constexpr bool MASK = NG > 0 || SELBIT;
+    static_assert(!SAMP || NG > 0, "the token draws' sums read the dense mask");
     extern __shared__ float dyn[];  // rsel [nsel] | selk [nsel] | rcl [ncut]
     __shared__ float lut[NG > 0 ? NG : 1][256];
     __shared__ double sh_h[4];
@@ -586,9 +601,10 @@ __global__ __launch_bounds__(kQThreads) void marg_q_stream(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float *prow = p + pos * d.V;
     float *qrow = q ? q + pos * d.V : nullptr;
-    // this part's float4 groups [k_lo, k_hi) of the row
+    // this part's float4 groups [k_lo, k_hi) of the row: whole chunks
     const int n4 = d.V >> 2;
-    const int per = (n4 + kQParts - 1) / kQParts;
+    const int nch = (n4 + kRowChunk4 - 1) / kRowChunk4;
+    const int per = (nch + kQParts - 1) / kQParts * kRowChunk4;
     const int k_lo = min(n4, part * per), k_hi = min(n4, k_lo + per);
     const double lz = logZ[b];
     const int e1 = ea[(size_t)b * (sv.Lpad + 1) + i], e2 = eb[(size_t)b * (sv.Lpad + 1) + i + 1];
@@ -599,6 +615,7 @@ __global__ __launch_bounds__(kQThreads) void marg_q_stream(
             for (int v = 4 * k_lo + tid; v < 4 * k_hi; v += kQThreads) qrow[v] = 0.f;
         if (tid == 0 && negent) hpart[pos * kQParts + part] = -INFINITY;
         if (tid == 0 && part == 0) conf[pos] = -INFINITY;
+        if (SAMP && tid == 0 && part == 0) tcs_ok[pos] = 0;
         return;
     }
     const double factor = exp2((double)e1 + (double)e2 - lz * 1.4426950408889634074);
@@ -620,6 +637,8 @@ __global__ __launch_bounds__(kQThreads) void marg_q_stream(
         }
     if (RANGES)
         for (int c = tid; c < d.ncut; c += kQThreads) rcl[c] = rcut[pos * d.ncut + c];
+    const uint32_t dbit = SAMP ? tdbit[pos] : 0u;
+    if (SAMP && tid == 0 && part == 0) tcs_ok[pos] = dbit != 0u;
     __syncthreads();
     const int tok = tokens ? tokens[pos] : -1;
     auto weight_r = [&](int v, uint32_t m, int sl, int c) -> float {
@@ -689,7 +708,10 @@ __global__ __launch_bounds__(kQThreads) void marg_q_stream(
     double hsum = 0.0;
     float tokq = -INFINITY;
     bool have_tok = false;
+    static_assert(kPer == kRowChunk4, "one chunk of the token draws per iteration");
+    double *tcs_row = SAMP ? tcs + (pos * tcs_nch + k_lo / kRowChunk4) * 4 + wave : nullptr;
     auto compute = [&](const Buf &bf, int it) {
+        double ts = 0.0;  // the token draw's chunk sum (SAMP)
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int k = k_lo + it * kPer + u * kQThreads + tid;
@@ -716,6 +738,18 @@ __global__ __launch_bounds__(kQThreads) void marg_q_stream(
                     if (o.z > 0.f) hsum += (double)o.z * log((double)o.z);
                     if (o.w > 0.f) hsum += (double)o.w * log((double)o.w);
                 }
+                if constexpr (SAMP) {
+                    ts += (double)((m.x & dbit) ? bf.x[u].x : 0.f);
+                    ts += (double)((m.y & dbit) ? bf.x[u].y : 0.f);
+                    ts += (double)((m.z & dbit) ? bf.x[u].z : 0.f);
+                    ts += (double)((m.w & dbit) ? bf.x[u].w : 0.f);
+                }
+            }
+        }
+        if constexpr (SAMP) {
+            if (dbit) {
+                const double w = wave_sum_d(ts);
+                if (lane == 0 && it < iters) tcs_row[4 * it] = w;
             }
         }
     };
@@ -752,6 +786,72 @@ __global__ void marg_negent_sum(int npos, const double *__restrict__ hpart,
     double s = 0.0;
     for (int k = 0; k < kQParts; ++k) s += hpart[(size_t)pos * kQParts + k];
     conf[pos] = (float)s;
+}
+
+// Finish of the joint call, after the token draws (streaming writer tables,
+// no ranges).  One wavefront per position.  Rows flagged since the q writer
+// ran get what the writer gives a flagged row (q = 0, conf = -inf, q ln q
+// parts -inf); otherwise, for FA_CONF_PROB, lane 0 recomputes the sampled
+// token's q from the pair weights in global memory with the additions of the
+// writer's lookup tables in the same order (per byte of the mask, its set
+// bits ascending from 0; the bytes' sums in byte order; then the token-list
+// weight), so conf equals the writer's value bit for bit.
+template <int NG, bool SELBIT, bool LISTALL>
+__global__ __launch_bounds__(64) void marg_conf_tok(
+    DevTable d, StepView sv, const float *__restrict__ p, const double *__restrict__ logZ,
+    const int32_t *__restrict__ tokens, int conf_mode, float *__restrict__ q,
+    float *__restrict__ conf, const int32_t *__restrict__ ea, const int32_t *__restrict__ eb,
+    const float *__restrict__ pw, int pw_ld, double *__restrict__ hpart,
+    const int32_t *__restrict__ status)
+{
+    const int b = blockIdx.y, i = blockIdx.x, lane = threadIdx.x;
+    const size_t pos = (size_t)b * sv.L + i;
+    const double lz = logZ[b];
+    const int e1 = ea[(size_t)b * (sv.Lpad + 1) + i], e2 = eb[(size_t)b * (sv.Lpad + 1) + i + 1];
+    const bool ok = status[b] == 0 && lz > -INFINITY && e1 > kNeg && e2 > kNeg;
+    const bool negent = conf_mode == FA_CONF_NEGENT;
+    if (!ok) {
+        if (q) {
+            float *qrow = q + pos * d.V;
+            for (int v = lane; v < d.V; v += 64) qrow[v] = 0.f;
+        }
+        if (negent && lane < kQParts) hpart[pos * kQParts + lane] = -INFINITY;
+        if (lane == 0) conf[pos] = -INFINITY;
+        return;
+    }
+    if (negent || lane != 0) return;
+    const int tok = tokens[pos];
+    float o = -INFINITY;
+    if (tok >= 0) {
+        const float *pwr = pw + pos * pw_ld;
+        const uint32_t m = (NG > 0 || SELBIT) ? d.tokmask[tok] : 0u;
+        float r = 0.f;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const uint32_t byte = (m >> (8 * g)) & 255u;
+            float sm = 0.f;
+            for (int bit = 0; bit < 8; ++bit)
+                if ((byte >> bit) & 1u) sm += pwr[8 * g + bit];
+            r = g == 0 ? sm : r + sm;
+        }
+        if (SELBIT && (m & kSelBit)) {
+            int lo = 0, hi = d.nsel - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (d.sel_tok[mid] < tok) lo = mid + 1;
+                else hi = mid;
+            }
+            r += pwr[kDenseMax + lo];
+        }
+        if (LISTALL) {
+            const int sl = d.tok2sel[tok];
+            if (sl >= 0) r += pwr[kDenseMax + sl];
+        }
+        const double factor = exp2((double)e1 + (double)e2 - lz * 1.4426950408889634074);
+        const float x = p[pos * d.V + tok];
+        o = (r > 0.f && x > 0.f) ? (float)((double)x * (double)r * factor) : 0.f;
+    }
+    conf[pos] = o;
 }
 
 // Leaf level of the message pass without reading the leaves.  Each leaf
@@ -871,6 +971,14 @@ int launch_marginals(const DevTable &d, const Geometry &g, const float *p, const
                      int32_t conf_mode, float *q, float *conf, uint8_t *ws, const WsLayout &w,
                      int32_t *status, void *stream)
 {
+    int rc = launch_marg_pass(d, g, p, tree, meta, ws, w, stream);
+    if (rc) return rc;
+    return launch_marg_out(d, g, p, logZ, tokens, conf_mode, q, conf, ws, w, 0, status, stream);
+}
+
+int launch_marg_pass(const DevTable &d, const Geometry &g, const float *p, const float *tree,
+                     const int32_t *meta, uint8_t *ws, const WsLayout &w, void *stream)
+{
     hipStream_t st = (hipStream_t)stream;
     StepView sv = step_view(g);
     float *va = (float *)(ws + w.va), *vb = (float *)(ws + w.vb);
@@ -932,33 +1040,101 @@ int launch_marginals(const DevTable &d, const Geometry &g, const float *p, const
         e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
     }
+    return 0;
+}
+
+namespace {
+
+size_t q_stream_lds(const DevTable &d)
+{
+    return (d.nsel > 0 ? (size_t)d.nsel * (d.selbit ? 8 : 4) : 0) +
+           (d.ncut > 0 ? (size_t)d.ncut * 4 : 0);
+}
+
+// streaming q writer: float4 rows and every lookup table in LDS
+bool q_streamed(const DevTable &d, const float *p, const float *q, const WsLayout &w)
+{
+    const bool aligned = ((uintptr_t)p & 15) == 0 && ((uintptr_t)q & 15) == 0;
+    return (d.V & 3) == 0 && aligned && q_stream_lds(d) <= kQLdsMax &&
+           (d.nsel == 0 || w.pw_nl == d.nsel);
+}
+
+}  // namespace
+
+bool marg_joint_ok(const DevTable &d, const Geometry &g, const float *p, const float *q,
+                   int32_t conf_mode, const WsLayout &w)
+{
+    // the token draws stream dense rows of at most kTokChunksMax chunks; the
+    // q writer streams the row only when it writes q or sums q ln q
+    return g.L > 0 && d.ndense > 0 && q_streamed(d, p, q, w) &&
+           (q != nullptr || conf_mode == FA_CONF_NEGENT) && w.tcs_nch <= 256;
+}
+
+int launch_marg_out(const DevTable &d, const Geometry &g, const float *p, const double *logZ,
+                    const int32_t *tokens, int32_t conf_mode, float *q, float *conf, uint8_t *ws,
+                    const WsLayout &w, int mode, int32_t *status, void *stream)
+{
+    hipStream_t st = (hipStream_t)stream;
+    StepView sv = step_view(g);
+    float *va = (float *)(ws + w.va), *vb = (float *)(ws + w.vb);
+    int32_t *ea = (int32_t *)(ws + w.ea), *eb = (int32_t *)(ws + w.eb);
+    float *rcut = (float *)(ws + w.rcut);
+    hipError_t e;
     const dim3 qgrid(g.L, g.B);
     const int ng = (d.ndense + 7) / 8;
     const bool listall = d.nsel > 0 && !d.selbit;
     const bool ranges = d.ncut > 0;
-    const bool lists = d.nsel > 0;
-    // streaming path: float4 rows and every lookup table in LDS
-    const size_t qlds = (lists ? (size_t)d.nsel * (d.selbit ? 8 : 4) : 0) +
-                        (ranges ? (size_t)d.ncut * 4 : 0);
-    const bool aligned = ((uintptr_t)p & 15) == 0 && ((uintptr_t)q & 15) == 0;
-    const bool streamed = (d.V & 3) == 0 && aligned && qlds <= kQLdsMax && (!lists || w.pw_nl == d.nsel);
+    const size_t qlds = q_stream_lds(d);
+    const bool streamed = q_streamed(d, p, q, w);
+    if (mode != 0 && !(streamed && ng > 0 && !ranges)) return (int)hipErrorInvalidValue;
     if (streamed) {
         const int npos = g.B * g.L;
         float *pw = (float *)(ws + w.pw);
         double *hpart = (double *)(ws + w.hpart);
+        const uint32_t *tdbit = (const uint32_t *)(ws + w.tdbit);
+        double *tcs = mode == 1 ? (double *)(ws + w.tcs) : nullptr;
+        int32_t *tcs_ok = mode == 1 ? (int32_t *)(ws + w.tcs_ok) : nullptr;
         const dim3 sgrid(g.L * kQParts, g.B);
-        const size_t plds = w.pw_nl ? ((size_t)std::min(d.n_tm, kPwChunk) + w.pw_nl) * 4 : 0;
-        if (plds > 48 * 1024) {
-            e = hipFuncSetAttribute(reinterpret_cast<const void *>(&marg_pairw),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)plds);
+        if (mode != 2) {  // the pair weights of mode 1 serve mode 2
+            const size_t plds = w.pw_nl ? ((size_t)std::min(d.n_tm, kPwChunk) + w.pw_nl) * 4 : 0;
+            if (plds > 48 * 1024) {
+                e = hipFuncSetAttribute(reinterpret_cast<const void *>(&marg_pairw),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)plds);
+                if (e != hipSuccess) return (int)e;
+            }
+            marg_pairw<<<npos, kPwThreads, plds, st>>>(d, sv, va, vb, w.pw_nl, w.pw_ld, pw);
+            e = hipGetLastError();
             if (e != hipSuccess) return (int)e;
         }
-        marg_pairw<<<npos, kPwThreads, plds, st>>>(d, sv, va, vb, w.pw_nl, w.pw_ld, pw);
-        e = hipGetLastError();
-        if (e != hipSuccess) return (int)e;
-#define FA_MARG_QS(NG, SB, LA, RG)                                                                \
+        if (mode == 2) {
+            const dim3 cgrid(g.L, g.B);
+#define FA_MARG_CT(NG, SB, LA)                                                                 \
+    marg_conf_tok<NG, SB, LA><<<cgrid, 64, 0, st>>>(d, sv, p, logZ, tokens, conf_mode, q, conf, \
+                                                    ea, eb, pw, w.pw_ld, hpart, status)
+            if (d.selbit) {
+                if (ng == 1) FA_MARG_CT(1, true, false);
+                else if (ng == 2) FA_MARG_CT(2, true, false);
+                else if (ng == 3) FA_MARG_CT(3, true, false);
+                else FA_MARG_CT(4, true, false);
+            } else if (listall) {
+                FA_MARG_CT(4, false, true);
+            } else {
+                if (ng == 1) FA_MARG_CT(1, false, false);
+                else if (ng == 2) FA_MARG_CT(2, false, false);
+                else if (ng == 3) FA_MARG_CT(3, false, false);
+                else FA_MARG_CT(4, false, false);
+            }
+#undef FA_MARG_CT
+            e = hipGetLastError();
+            if (e != hipSuccess) return (int)e;
+            if (conf_mode == FA_CONF_NEGENT)
+                marg_negent_sum<<<(npos + 255) / 256, 256, 0, st>>>(npos, hpart, conf);
+            return (int)hipGetLastError();
+        }
+        const bool samp = mode == 1;
+#define FA_MARG_QS_K(NG, SB, LA, RG, SA)                                                          \
     do {                                                                                          \
-        auto kern = &marg_q_stream<NG, SB, LA, RG>;                                               \
+        auto kern = &marg_q_stream<NG, SB, LA, RG, SA>;                                           \
         if (qlds > 48 * 1024) {                                                                   \
             e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),                         \
                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)qlds);       \
@@ -967,14 +1143,21 @@ int launch_marginals(const DevTable &d, const Geometry &g, const float *p, const
         e = (hipError_t)prof_mark(FA_PROF_MARG_Q, true, stream);                                  \
         if (e != hipSuccess) return (int)e;                                                       \
         kern<<<sgrid, kQThreads, qlds, st>>>(d, sv, p, logZ, tokens, conf_mode, q, conf, ea, eb, \
-                                             pw, w.pw_ld, rcut, hpart, status);                   \
+                                             pw, w.pw_ld, rcut, hpart, status, tdbit, tcs, tcs_ok,\
+                                             w.tcs_nch);                                          \
     } while (0)
+#define FA_MARG_QS(NG, SB, LA, RG)                                                                \
+    do {                                                                                          \
+        if (samp) FA_MARG_QS_K(NG, SB, LA, RG, true);                                             \
+        else FA_MARG_QS_K(NG, SB, LA, RG, false);                                                 \
+    } while (0)
+#define FA_MARG_QS0(NG, SB, LA, RG) FA_MARG_QS_K(NG, SB, LA, RG, false)
         if (ranges) {
-            if (listall) FA_MARG_QS(0, false, true, true);
-            else FA_MARG_QS(0, false, false, true);
+            if (listall) FA_MARG_QS0(0, false, true, true);
+            else FA_MARG_QS0(0, false, false, true);
         } else if (ng == 0) {
-            if (listall) FA_MARG_QS(0, false, true, false);
-            else FA_MARG_QS(0, false, false, false);
+            if (listall) FA_MARG_QS0(0, false, true, false);
+            else FA_MARG_QS0(0, false, false, false);
         } else if (d.selbit) {
             if (ng == 1) FA_MARG_QS(1, true, false, false);
             else if (ng == 2) FA_MARG_QS(2, true, false, false);
@@ -989,11 +1172,14 @@ int launch_marginals(const DevTable &d, const Geometry &g, const float *p, const
             else FA_MARG_QS(4, false, false, false);
         }
 #undef FA_MARG_QS
+#undef FA_MARG_QS0
+#undef FA_MARG_QS_K
         e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
         const int pe = prof_mark(FA_PROF_MARG_Q, false, stream);
         if (pe) return pe;
-        if (conf_mode == FA_CONF_NEGENT) {
+        // mode 1 leaves the confidence to mode 2
+        if (conf_mode == FA_CONF_NEGENT && mode != 1) {
             marg_negent_sum<<<(npos + 255) / 256, 256, 0, st>>>(npos, hpart, conf);
             e = hipGetLastError();
         }

@@ -111,12 +111,26 @@ __device__ void draw_root(const DevTable &d, const StepView &sv, const float *__
     }
 }
 
-// root draw alone (a tree of one leaf, Lpad = 1)
+// pair of the boundary states (a, c) of one position, for the token draw
+__device__ inline void put_pair(const DevTable &d, int a, int c, int32_t *tpair, uint32_t *tdbit)
+{
+    const int q = pair_index(d, a, c);
+    *tpair = q;
+    *tdbit = (q >= 0 && d.pair_cls[q] == kDense) ? 1u << d.pair_aux[q] : 0u;
+}
+
+// root draw alone (a tree of one leaf, Lpad = 1, L = 1)
 __global__ void sample_root(DevTable d, StepView sv, const float *__restrict__ tree,
                             const int32_t *__restrict__ meta, uint64_t seed,
-                            int32_t *__restrict__ zc, int32_t *__restrict__ status)
+                            int32_t *__restrict__ zc, int32_t *__restrict__ tpair,
+                            uint32_t *__restrict__ tdbit, int32_t *__restrict__ status)
 {
-    draw_root(d, sv, tree, meta, seed, blockIdx.x, threadIdx.x, zc, status);
+    const int b = blockIdx.x;
+    draw_root(d, sv, tree, meta, seed, b, threadIdx.x, zc, status);
+    if (threadIdx.x == 0) {
+        const int32_t *z = zc + (size_t)b * (sv.Lpad + 1);
+        put_pair(d, z[0], z[1], tpair + b, tdbit + b);
+    }
 }
 
 // one midpoint level: node n = nn + idx covers [l, r); children 2n (stored as
@@ -185,12 +199,14 @@ __device__ int draw_mid(const DevTable &d, const StepView &sv, const float *__re
 // subtree per workgroup: at sub-level t wavefront w < 2^t draws node w of the
 // subtree.  The subtree's boundary states stay in LDS between sub-levels
 // (slot q holds position l0 + q * span0 / 2^depth); each draw is also written
-// to zc.
+// to zc.  The launch that reaches the leaves also records, per position,
+// the pair its token draw uses.
 constexpr int kSubDepth = 3;
 
 __global__ __launch_bounds__(64 << (kSubDepth - 1)) void sample_levels(
     DevTable d, StepView sv, const float *__restrict__ tree, const int32_t *__restrict__ meta,
-    uint64_t seed, int level0, int depth, int32_t *__restrict__ zc, int32_t *__restrict__ status)
+    uint64_t seed, int level0, int depth, int32_t *__restrict__ zc, int32_t *__restrict__ tpair,
+    uint32_t *__restrict__ tdbit, int32_t *__restrict__ status)
 {
     __shared__ int zs[(1 << kSubDepth) + 1];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -225,10 +241,19 @@ __global__ __launch_bounds__(64 << (kSubDepth - 1)) void sample_levels(
         }
         __syncthreads();
     }
+    if (level0 + depth - 1 == sv.K) {  // unit = 1: slots are positions
+        const int t = threadIdx.x, i = l0 + t;
+        if (t < q && i < sv.L) {
+            const size_t pos = (size_t)b * sv.L + i;
+            put_pair(d, zs[t], zs[t + 1], tpair + pos, tdbit + pos);
+        }
+    }
 }
 
 constexpr int kTokThreads = 256;
 constexpr int kTokChunksMax = 256;
+// a streamed chunk: four float4 groups per thread
+static_assert(4 * kTokThreads == kRowChunk4, "dense-pair chunk layout");
 
 // candidates of one token draw: the tokens of the pair (z_i, z_{i+1}) in
 // ascending order, weight p[i][v] times the number of edges holding v
@@ -266,9 +291,17 @@ __device__ inline int seg_cursor(const DevTable &d, const TokCands &c, int k)
 // (each thread a run of consecutive candidates, so loads are coalesced) and
 // keeps fp64 chunk sums; the chunk holding u*T is found serially; pass 2
 // rescans that chunk only.
+// tpair: the pair of (z_i, z_{i+1}) per position, from the midpoint draws.
+//
+// pre (non-null): the q writer of the same step has already streamed the row
+// and left, where pre_ok[position] is set, the wavefront partials of every
+// pass-1 chunk of a dense pair (pre[(position * pre_nch + chunk) * 4 + wave],
+// summed in the same order as below), so pass 1 is skipped there.
 __global__ __launch_bounds__(kTokThreads) void sample_tokens(
     DevTable d, StepView sv, const float *__restrict__ p, uint64_t seed,
-    const int32_t *__restrict__ zc, int32_t *__restrict__ tokens, int32_t *__restrict__ status)
+    const int32_t *__restrict__ zc, const int32_t *__restrict__ tpair,
+    int32_t *__restrict__ tokens, int32_t *__restrict__ status, const double *__restrict__ pre,
+    const int32_t *__restrict__ pre_ok, int pre_nch)
 {
     const int b = blockIdx.y, i = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -278,23 +311,9 @@ __global__ __launch_bounds__(kTokThreads) void sample_tokens(
     __shared__ double wsum[kTokChunksMax][4];
     __shared__ double sh_w[4];
     __shared__ double sh_scan[kTokThreads];
-    __shared__ int sh_q, sh_chunk;
+    __shared__ int sh_chunk;
     __shared__ double sh_base, sh_target;
-    if (tid == 0) {
-        int q = -1;
-        if (a >= 0 && c >= 0) {
-            int lo = d.row_ptr[a], hi = d.row_ptr[a + 1];
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (d.pair_b[mid] < c) lo = mid + 1;
-                else hi = mid;
-            }
-            if (lo < d.row_ptr[a + 1] && d.pair_b[lo] == c) q = lo;
-        }
-        sh_q = q;
-    }
-    __syncthreads();
-    const int q = sh_q;
+    const int q = tpair[(size_t)b * sv.L + i];
     int32_t *out = tokens + (size_t)b * sv.L + i;
     if (q < 0) {
         if (tid == 0) {
@@ -354,7 +373,17 @@ __global__ __launch_bounds__(kTokThreads) void sample_tokens(
     };
     // per-chunk wavefront partials, combined in wavefront order after one
     // barrier
-    if (streamed) {
+    const size_t pos = (size_t)b * sv.L + i;
+    const bool have_pre = streamed && pre && pre_ok[pos];
+    if (have_pre) {
+        const double *pp = pre + pos * pre_nch * 4;
+        for (int ch = tid; ch < nchunks; ch += kTokThreads) {
+            wsum[ch][0] = pp[4 * ch];
+            wsum[ch][1] = pp[4 * ch + 1];
+            wsum[ch][2] = pp[4 * ch + 2];
+            wsum[ch][3] = pp[4 * ch + 3];
+        }
+    } else if (streamed) {
         // chunk ch = float4 groups [1024 ch, 1024 ch + 1024): thread t takes
         // groups 1024 ch + 256 u + t (u < 4), so each load instruction reads
         // 1 KB contiguous per wavefront; the label comes from the pair's own
@@ -370,7 +399,7 @@ __global__ __launch_bounds__(kTokThreads) void sample_tokens(
         auto load = [&](Buf &bf, int ch) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int k = min(ch * 1024 + u * kTokThreads + tid, n4 - 1);
+                const int k = min(ch * kRowChunk4 + u * kTokThreads + tid, n4 - 1);
                 bf.x[u] = p4[k];
                 bf.m[u] = bits[k >> 3];
             }
@@ -379,7 +408,7 @@ __global__ __launch_bounds__(kTokThreads) void sample_tokens(
             double s = 0.0;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int k = ch * 1024 + u * kTokThreads + tid;
+                const int k = ch * kRowChunk4 + u * kTokThreads + tid;
                 if (k < n4) {
                     const uint32_t m = bf.m[u] >> ((k & 7) * 4);
                     s += (double)((m & 1u) ? bf.x[u].x : 0.f);
@@ -540,11 +569,23 @@ int launch_sample(const DevTable &d, const Geometry &g, const float *p, const fl
         sample_empty<<<(g.B + 255) / 256, 256, 0, st>>>(d, g.B, states, status);
         return (int)hipGetLastError();
     }
+    int rc = launch_sample_states(d, g, tree, meta, seed, ws, w, status, stream);
+    if (rc) return rc;
+    return launch_sample_tokens(d, g, p, seed, states, tokens, ws, w, false, status, stream);
+}
+
+int launch_sample_states(const DevTable &d, const Geometry &g, const float *tree,
+                         const int32_t *meta, uint64_t seed, uint8_t *ws, const WsLayout &w,
+                         int32_t *status, void *stream)
+{
+    hipStream_t st = (hipStream_t)stream;
     StepView sv = step_view(g);
     int32_t *zc = (int32_t *)(ws + w.zc);
+    int32_t *tpair = (int32_t *)(ws + w.tpair);
+    uint32_t *tdbit = (uint32_t *)(ws + w.tdbit);
     hipError_t e;
     if (g.K == 0) {  // otherwise the first midpoint launch draws the root
-        sample_root<<<g.B, 64, 0, st>>>(d, sv, tree, meta, seed, zc, status);
+        sample_root<<<g.B, 64, 0, st>>>(d, sv, tree, meta, seed, zc, tpair, tdbit, status);
         e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
     }
@@ -552,12 +593,26 @@ int launch_sample(const DevTable &d, const Geometry &g, const float *p, const fl
         const int depth = std::min(kSubDepth, g.K - level0 + 1);
         const int nn0 = 1 << (level0 - 1);
         sample_levels<<<g.B * nn0, 64 << (kSubDepth - 1), 0, st>>>(d, sv, tree, meta, seed, level0,
-                                                                    depth, zc, status);
+                                                                    depth, zc, tpair, tdbit, status);
         e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
     }
-    sample_tokens<<<dim3(g.L, g.B), kTokThreads, 0, st>>>(d, sv, p, seed, zc, tokens, status);
-    e = hipGetLastError();
+    return 0;
+}
+
+int launch_sample_tokens(const DevTable &d, const Geometry &g, const float *p, uint64_t seed,
+                         int32_t *states, int32_t *tokens, uint8_t *ws, const WsLayout &w,
+                         bool pre, int32_t *status, void *stream)
+{
+    hipStream_t st = (hipStream_t)stream;
+    StepView sv = step_view(g);
+    const int32_t *zc = (const int32_t *)(ws + w.zc);
+    const double *tcs = pre ? (const double *)(ws + w.tcs) : nullptr;
+    const int32_t *tcs_ok = pre ? (const int32_t *)(ws + w.tcs_ok) : nullptr;
+    const int32_t *tpair = (const int32_t *)(ws + w.tpair);
+    sample_tokens<<<dim3(g.L, g.B), kTokThreads, 0, st>>>(d, sv, p, seed, zc, tpair, tokens, status,
+                                                           tcs, tcs_ok, w.tcs_nch);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
     sample_finalize<<<dim3((g.L + 1 + 255) / 256, g.B), 256, 0, st>>>(d, sv, zc, states, tokens,
                                                                       status);

@@ -222,9 +222,6 @@ WsLayout ws_layout(const HostTable &t, const Geometry &g)
     w.cutp = o; o = al(o + BL * t.ncut() * sizeof(double));
     w.val = o; o = al(o + (fused ? 0 : BL * t.npairs() * sizeof(float)));
     size_t a1 = o;
-    o = a0;  // sampler region
-    w.zc = o; o = al(o + (size_t)g.B * (g.Lpad + 1) * sizeof(int32_t));
-    size_t a3 = o;
     o = a0;  // span tree region
     size_t kp = 0;
     for (int level = 1; level <= g.K; ++level) {
@@ -245,7 +242,18 @@ WsLayout ws_layout(const HostTable &t, const Geometry &g)
     w.pw = o; o = al(o + BL * (size_t)w.pw_ld * sizeof(float));
     w.hpart = o; o = al(o + BL * 4 * sizeof(double));  // the q writer's row parts
     size_t a4 = o;
-    w.total = std::max(std::max(a1, a2), std::max(a3, a4));
+    // sampler region, apart from the others: the joint call keeps the drawn
+    // boundary states through the message pass, and the dense-pair chunk
+    // sums of the token draws from the q writer to the draws
+    o = al(std::max(std::max(a1, a2), a4));
+    w.zc = o; o = al(o + (size_t)g.B * (g.Lpad + 1) * sizeof(int32_t));
+    w.tpair = o; o = al(o + BL * sizeof(int32_t));
+    w.tdbit = o; o = al(o + BL * sizeof(uint32_t));
+    w.tcs_nch = (t.V / 4 + kRowChunk4 - 1) / kRowChunk4;
+    const bool joint = t.ndense() > 0 && t.V % 4 == 0;
+    w.tcs = o; o = al(o + (joint ? BL * (size_t)w.tcs_nch * 4 * sizeof(double) : 0));
+    w.tcs_ok = o; o = al(o + (joint ? BL * sizeof(int32_t) : 0));
+    w.total = o;
     if (w.total == 0) w.total = 256;
     return w;
 }

@@ -236,6 +236,27 @@ int fa_marginals(const fa_table *t, const float *p, int32_t B, int32_t L, const 
                  int32_t conf_mode, float *q, float *conf, void *ws, size_t ws_bytes,
                  int32_t *row_status, fa_stream_t stream);
 
+/*
+ * fa_sample_marginals - fa_sample followed by fa_marginals on the sampled
+ * tokens, in one call whose outputs are bit-identical to that pair of calls
+ * (states, tokens, q, conf and row_status).  When the table has dense-label
+ * pairs, V % 4 == 0, p and q are 16-byte aligned and the q writer streams
+ * rows (q non-NULL or FA_CONF_NEGENT), the token draws of positions whose
+ * sampled pair is a dense pair take their chunk sums from the q writer's pass
+ * over p instead of reading the row again (the same sums in the same order);
+ * otherwise the call runs the two calls' launches in order.
+ * Cite: as fa_sample and fa_marginals.
+ *   arguments  as in fa_sample and fa_marginals; tokens is an output here
+ *              and required in both confidence modes
+ *   ws         workspace (>= fa_sizes) this step's fa_build_transitions wrote
+ * Errors: FA_EINVAL, FA_ESTATE, FA_EHIP.
+ */
+int fa_sample_marginals(const fa_table *t, const float *p, int32_t B, int32_t L,
+                        const float *tree, const int32_t *meta, const double *logZ,
+                        uint64_t seed, int32_t conf_mode, int32_t *states, int32_t *tokens,
+                        float *q, float *conf, void *ws, size_t ws_bytes, int32_t *row_status,
+                        fa_stream_t stream);
+
 /* fa_strerror - static description of an error code. */
 const char *fa_strerror(int code);
 

@@ -29,12 +29,12 @@ def log(msg):
     sys.stdout.flush()
 
 
-def run_gpu(w, conf_mode=0, write_q=True, table=None, p_dev=None):
+def run_gpu(w, conf_mode=0, write_q=True, table=None, p_dev=None, joint=True):
     import torch
     import constrained_decoding_diffusion_amd as fa
     tb = table or fa.Table.from_automaton(w.aut)
     p = p_dev if p_dev is not None else torch.from_numpy(w.p).cuda()
-    bufs = fa.step(tb, p, w.seed, conf_mode=conf_mode, write_q=write_q)
+    bufs = fa.step(tb, p, w.seed, conf_mode=conf_mode, write_q=write_q, joint=joint)
     torch.cuda.synchronize()
     out = dict(table=tb, bufs=bufs,
                logZ=bufs.logZ.cpu().numpy(), status=bufs.status.cpu().numpy(),

@@ -152,6 +152,42 @@ def test_bad_probability_is_flagged():
     PT.check_row(w, g, 1, oracle.Oracle(w.aut))
 
 
+@pytest.mark.parametrize("name", ["real-number", "json-small", "json-32-dense", "json-odd-V",
+                                  "json-many-list-tokens", "range-small", "nfa-small"])
+@pytest.mark.parametrize("conf_mode,write_q", [(0, True), (1, True), (1, False), (0, False)])
+def test_joint_call_matches_separate_calls(name, conf_mode, write_q):
+    """fa_sample_marginals (token draws fed by the q writer's pass where it
+    applies) gives bit-for-bit what fa_sample then fa_marginals give."""
+    w = CASES[name]()
+    PT.log(f"[joint] {name} conf_mode {conf_mode} q {write_q}")
+    g1 = PT.run_gpu(w, conf_mode=conf_mode, write_q=write_q, joint=True)
+    g2 = PT.run_gpu(w, conf_mode=conf_mode, write_q=write_q, table=g1["table"], joint=False)
+    for k in ("status", "logZ", "states", "tokens", "conf") + (("q",) if write_q else ()):
+        np.testing.assert_array_equal(g1[k], g2[k], err_msg=k)
+
+
+def test_joint_call_flagged_rows():
+    """Rows flagged before the draws (infeasible, bad probability) come out of
+    the joint call exactly as out of the separate calls."""
+    w = configs.make(2, B=3, L=16)
+    aut = w.aut
+    first = set()
+    for e in range(aut.E):
+        if aut.src[e] == aut.start:
+            first |= set(aut.edge_label(e).tolist())
+    bad = next(v for v in range(aut.V) if v not in first)
+    w.p[1, 0] = 0.0
+    w.p[1, 0, bad] = 1.0
+    w.p[2, 5, int(aut.label_tok[0])] = np.nan
+    PT.log("[joint] flagged rows")
+    for conf_mode in (0, 1):
+        g1 = PT.run_gpu(w, conf_mode=conf_mode, joint=True)
+        g2 = PT.run_gpu(w, conf_mode=conf_mode, table=g1["table"], joint=False)
+        for k in ("status", "logZ", "states", "tokens", "q", "conf"):
+            np.testing.assert_array_equal(g1[k], g2[k], err_msg=k)
+        assert g1["status"][1] & 1 and g1["status"][2] & 4
+
+
 def test_determinism_bitwise():
     w = _json_small()
     PT.log("[parity] determinism")
