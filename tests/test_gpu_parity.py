@@ -188,6 +188,21 @@ def test_joint_call_flagged_rows():
         assert g1["status"][1] & 1 and g1["status"][2] & 4
 
 
+def test_joint_call_on_another_stream():
+    """The joint call ordered on a non-default stream (its midpoint draws
+    fork to the library's side stream and join back) gives what it gives on
+    the default stream."""
+    import torch
+    w = _json_small()
+    PT.log("[joint] non-default stream")
+    g1 = PT.run_gpu(w)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        g2 = PT.run_gpu(w, table=g1["table"])
+    for k in ("status", "logZ", "states", "tokens", "q", "conf"):
+        np.testing.assert_array_equal(g1[k], g2[k], err_msg=k)
+
+
 def test_determinism_bitwise():
     w = _json_small()
     PT.log("[parity] determinism")
