@@ -280,13 +280,13 @@ def main():
     hev = HipEvents()
 
     # sampling and marginals: one fa_sample_marginals call (default), or
-    # fa_sample then fa_marginals (--separate); the outputs are the same
-    if args.separate:
-        names = ["build_transitions", "span_tree", "sample", "marginals"]
-    else:
-        names = ["build_transitions", "span_tree", "sample_marginals"]
+    # fa_sample then fa_marginals (--separate); the outputs are the same, and
+    # the other form is timed too, after the headline steps
+    names_of = {True: ["build_transitions", "span_tree", "sample", "marginals"],
+                False: ["build_transitions", "span_tree", "sample_marginals"]}
+    names = names_of[args.separate]
 
-    def one_step(seed, ev=None, kev=None):
+    def one_step(seed, ev=None, kev=None, separate=args.separate):
         bufs.status.zero_()
         if kev:
             fa.profile_kernel(kev[0], kev[1], kev[2])
@@ -295,40 +295,57 @@ def main():
         if ev: ev[1].record()
         fa.span_tree(tb, bufs, stream)
         if ev: ev[2].record()
-        if args.separate:
+        if separate:
             fa.sample(tb, p, bufs, seed, stream)
             if ev: ev[3].record()
             fa.marginals(tb, p, bufs, fa.FA_CONF_PROB, stream, write_q=True)
         else:
             fa.sample_marginals(tb, p, bufs, seed, fa.FA_CONF_PROB, stream, write_q=True)
-        if ev: ev[len(names)].record()
+        if ev: ev[len(names_of[separate])].record()
+
+    def stage_split(separate):
+        """Mean µs per call over args.steps untimed steps with events
+        between the calls (the events cost about 20 us per step, so they
+        stay out of the timed steps)."""
+        nm = names_of[separate]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(nm) + 1)]
+               for _ in range(args.steps)]
+        for s in range(args.steps):
+            one_step(w.seed + args.warmup + s, evs[s], separate=separate)
+        torch.cuda.synchronize()
+        acc = {n: 0.0 for n in nm}
+        for ev in evs:
+            for k, n in enumerate(nm):
+                acc[n] += ev[k].elapsed_time(ev[k + 1])
+        return {n: 1000.0 * v / args.steps for n, v in acc.items()}
+
+    def timed(separate, kevs=None):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        c0 = time.perf_counter()
+        t0.record()
+        for s in range(args.steps):
+            one_step(w.seed + args.warmup + s, None, kevs[s][:3] if kevs else None, separate)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1), time.perf_counter() - c0
 
     for s in range(args.warmup):
         one_step(w.seed + s)
+        one_step(w.seed + s, separate=not args.separate)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-           for _ in range(args.steps)]
     kevs = []
     for s in range(args.steps):
         name, pid = prof_ids[s % len(prof_ids)]
         kevs.append((pid, hev.create(), hev.create(), name))
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record()
-    for s in range(args.steps):
-        one_step(w.seed + args.warmup + s, evs[s], kevs[s][:3])
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
+    # the timed steps carry only the library's kernel-bracketing events,
+    # which cost nothing measurable
+    total_ms, wall = timed(args.separate, kevs)
     fa.profile_kernel(fa.FA_PROF_NONE)
-    total_ms = t_start.elapsed_time(t_end)
-    stage_ms = {n: 0.0 for n in names}
-    for ev in evs:
-        for k, n in enumerate(names):
-            stage_ms[n] += ev[k].elapsed_time(ev[k + 1])
-    stage_us = {n: 1000.0 * v / args.steps for n, v in stage_ms.items()}
+    other_ms, _ = timed(not args.separate)
+    stage_us = stage_split(args.separate)
+    other_stage_us = stage_split(not args.separate)
     kern_us = {}
     for pid, a, b, name in kevs:
         ms = hev.elapsed_ms(a, b)
@@ -392,6 +409,10 @@ def main():
         "roofline": roof,
         "kernels": kernels,
         "stages": stages,
+        "other_form": {"calls": "joint" if args.separate else "separate",
+                       "us_per_step": 1000.0 * other_ms / args.steps,
+                       "steps_per_s": 1000.0 * args.steps / other_ms,
+                       "stages_us": other_stage_us},
         "wall_s": wall,
         "row_status": status.tolist(),
     }
