@@ -142,6 +142,12 @@ def test_step_calls_need_an_uploaded_table():
     assert rc == _fa.FA_ESTATE
     rc = _fa.lib().fa_span_tree(None, 1, 6, None, None, None, 0, None, None, None)
     assert rc == _fa.FA_EINVAL
+    rc = _fa.lib().fa_sample_marginals(t.handle, None, 1, 6, None, None, None, C.c_uint64(1), 0,
+                                       None, None, None, None, None, 0, None, None)
+    assert rc == _fa.FA_ESTATE
+    rc = _fa.lib().fa_sample_marginals(None, None, 1, 6, None, None, None, C.c_uint64(1), 0,
+                                       None, None, None, None, None, 0, None, None)
+    assert rc == _fa.FA_EINVAL
 
 
 def test_profile_hook_arguments():
