@@ -3,8 +3,6 @@
 // allocates device memory or synchronizes.
 #include <hip/hip_runtime_api.h>
 
-#include <mutex>
-
 #include "fa_internal.h"
 
 using namespace fa;
@@ -22,46 +20,6 @@ int hip_rc(int e) { return e == 0 ? FA_OK : FA_EHIP; }
 
 // grids put (row, node) pairs in their second dimension
 bool grid_fits(const Geometry &g) { return (int64_t)g.B * g.Lpad * 2 <= 65535 && g.L < (1 << 24); }
-
-// Side stream of fa_sample_marginals, one per device, created on first use
-// and kept until the process ends: the midpoint draws run on it while the
-// message pass runs on the caller's stream.  The mutex orders the event
-// records and waits of concurrent calls.
-struct Side {
-    hipStream_t s = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-};
-constexpr int kMaxDevices = 64;
-Side g_side[kMaxDevices];
-std::mutex g_side_mu;
-
-// the side stream of the device `stream` belongs to (call with g_side_mu held)
-int side_for(hipStream_t stream, Side **out)
-{
-    int dev = -1, cur = -1;
-    if (hipGetDevice(&cur) != hipSuccess) return (int)hipErrorInvalidDevice;
-    dev = cur;
-    if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return (int)hipErrorInvalidHandle;
-    if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
-    Side &sd = g_side[dev];
-    if (!sd.s) {
-        if (dev != cur && hipSetDevice(dev) != hipSuccess) return (int)hipErrorInvalidDevice;
-        Side n;
-        hipError_t e = hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming);
-        if (dev != cur) (void)hipSetDevice(cur);
-        if (e != hipSuccess) {
-            if (n.join) (void)hipEventDestroy(n.join);
-            if (n.fork) (void)hipEventDestroy(n.fork);
-            if (n.s) (void)hipStreamDestroy(n.s);
-            return (int)e;
-        }
-        sd = n;
-    }
-    *out = &sd;
-    return 0;
-}
 
 struct ProfHook {
     int which = FA_PROF_NONE;
@@ -197,21 +155,13 @@ extern "C" int fa_sample_marginals(const fa_table *t, const float *p, int32_t B,
         return hip_rc(launch_marginals(d, g, p, tree, meta, logZ, tokens, conf_mode, q, conf, wb,
                                        w, row_status, stream));
     }
-    // midpoints (side stream) beside the messages (caller's stream); q with
-    // the draws' chunk sums; the token draws; the confidence of the drawn
-    // tokens and the rows the draws flagged
-    {
-        std::lock_guard<std::mutex> lock(g_side_mu);
-        hipStream_t main = (hipStream_t)stream;
-        Side *sd = nullptr;
-        rc = side_for(main, &sd);
-        if (!rc) rc = (int)hipEventRecord(sd->fork, main);
-        if (!rc) rc = (int)hipStreamWaitEvent(sd->s, sd->fork, 0);
-        if (!rc) rc = launch_sample_states(d, g, tree, meta, seed, wb, w, row_status, sd->s);
-        if (!rc) rc = (int)hipEventRecord(sd->join, sd->s);
-        if (!rc) rc = launch_marg_pass(d, g, p, tree, meta, wb, w, stream);
-        if (!rc) rc = (int)hipStreamWaitEvent(main, sd->join, 0);
-    }
+    // midpoints riding on the message pass; q with the draws' chunk sums;
+    // the token draws; the confidence of the drawn tokens and the rows the
+    // draws flagged
+    rc = 0;
+    if (g.K == 0) rc = launch_sample_states(d, g, tree, meta, seed, wb, w, row_status, stream);
+    if (!rc)
+        rc = launch_marg_pass(d, g, p, tree, meta, wb, w, stream, g.K >= 1, seed, row_status);
     if (!rc)
         rc = launch_marg_out(d, g, p, logZ, nullptr, conf_mode, q, conf, wb, w, 1, row_status,
                              stream);

@@ -97,6 +97,13 @@ __device__ inline double wave_sum_d(double x)
     return x;
 }
 
+// mantissa of x in [0.5, 1) (x > 0): x = mant(x) 2^e
+__device__ inline float mant(float x)
+{
+    int e;
+    return frexpf(x, &e);
+}
+
 // index of the pair (a, c) in the table's row-sorted pair list, or -1
 __device__ inline int pair_index(const DevTable &d, int a, int c)
 {

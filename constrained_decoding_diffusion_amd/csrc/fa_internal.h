@@ -204,9 +204,12 @@ int launch_sample_states(const DevTable &d, const Geometry &g, const float *tree
 int launch_sample_tokens(const DevTable &d, const Geometry &g, const float *p, uint64_t seed,
                          int32_t *states, int32_t *tokens, uint8_t *ws, const WsLayout &w,
                          bool pre, int32_t *status, void *stream);
-// Message pass (alpha/beta at every boundary, range weights per cut).
+// Message pass (alpha/beta at every boundary, range weights per cut).  ride
+// (K >= 1): the launches of launch_sample_states (with `seed`, flagging
+// `status`) ride on its last launches as extra workgroups.
 int launch_marg_pass(const DevTable &d, const Geometry &g, const float *p, const float *tree,
-                     const int32_t *meta, uint8_t *ws, const WsLayout &w, void *stream);
+                     const int32_t *meta, uint8_t *ws, const WsLayout &w, void *stream,
+                     bool ride, uint64_t seed, int32_t *status);
 // The q writer and the confidence.  mode 0: the plain writer; 1: the
 // streaming writer that also sums the token draws' dense-pair chunks (the
 // boundary states in ws at w.zc; tokens unused); 2: after mode 1 and the

@@ -11,15 +11,10 @@
 //   q[i][v] = p[i][v] sum_{pairs (a,a') holding v} c alpha_i[a] beta_{i+1}[a'] / Z.
 #include "device_common.h"
 #include "pair_value.h"
+#include "sample_draw.h"
 
 namespace fa {
 namespace {
-
-__device__ inline float mant(float x)
-{
-    int e;
-    return frexpf(x, &e);
-}
 
 __global__ void marg_init(DevTable d, StepView sv, float *__restrict__ va, int32_t *__restrict__ ea,
                           float *__restrict__ vb, int32_t *__restrict__ eb)
@@ -47,19 +42,27 @@ constexpr int kMsgThreads = 1024;
 constexpr int kMsgWaves = kMsgThreads / 64;
 constexpr int kMsgU = 4;  // rows per wavefront per load group
 
+//
+// md: midpoint draws riding on the launch (the joint call): md.nwg
+// workgroups in the first rows of blockIdx.y, column block 0, so that they
+// are dispatched first; the products follow.
 template <int CW>
 __global__ __launch_bounds__(kMsgThreads) void marg_level(
     DevTable d, StepView sv, const float *__restrict__ tree, const int32_t *__restrict__ meta,
     int nn, float *__restrict__ va, int32_t *__restrict__ ea, float *__restrict__ vb,
-    int32_t *__restrict__ eb, int top)
+    int32_t *__restrict__ eb, int top, MidDraws md)
 {
+    if ((int)blockIdx.y < md.nwg) {
+        if (blockIdx.x == 0) mid_draws_wg(d, sv, md, (int)blockIdx.y);
+        return;
+    }
     constexpr int PER = CW / 64;  // columns per lane: 4 or 1
     extern __shared__ float gsh[];  // [Sp] normalized input weights, then [Sp] row folds
     int *rsh = reinterpret_cast<int *>(gsh + sv.Sp);
     __shared__ int sh_max[kMsgWaves];
     __shared__ float red[kMsgWaves][CW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int cb = blockIdx.x, prod = blockIdx.y;
+    const int cb = blockIdx.x, prod = (int)blockIdx.y - md.nwg;
     const int beta = prod & 1;
     const int bn = prod >> 1;
     const int b = bn / nn, idx = bn % nn, n = nn + idx;
@@ -502,18 +505,13 @@ constexpr int kPwThreads = 512;
 constexpr int kPwUnroll = 4;
 constexpr int kPwChunk = 8192;
 
-__global__ __launch_bounds__(kPwThreads) void marg_pairw(DevTable d, StepView sv,
-                                                         const float *__restrict__ va,
-                                                         const float *__restrict__ vb, int nl,
-                                                         int ld, float *__restrict__ pw)
+// The weights of one position from its two vectors (global or LDS); wsh:
+// LDS scratch of min(n_tm, kPwChunk) + nl floats.  All kPwThreads threads
+// call it.
+__device__ void pair_weights(const DevTable &d, const float *al, const float *be, int nl,
+                             float *__restrict__ out, float *wsh)
 {
-    extern __shared__ float wsh[];  // [min(n_tm, kPwChunk)] entry weights | [nl] sums
-    const int pos = blockIdx.x;
     const int tid = threadIdx.x;
-    const int b = pos / sv.L, i = pos % sv.L;
-    const float *al = va + ((size_t)b * (sv.Lpad + 1) + i) * sv.Sp;
-    const float *be = vb + ((size_t)b * (sv.Lpad + 1) + i + 1) * sv.Sp;
-    float *out = pw + (size_t)pos * ld;
     if (tid < kDenseMax) {
         float w = 0.f;
         if (tid < d.ndense) {
@@ -557,6 +555,19 @@ __global__ __launch_bounds__(kPwThreads) void marg_pairw(DevTable d, StepView sv
         }
     }
     for (int s = tid; s < nl; s += kPwThreads) out[kDenseMax + s] = rs[s];
+}
+
+__global__ __launch_bounds__(kPwThreads) void marg_pairw(DevTable d, StepView sv,
+                                                         const float *__restrict__ va,
+                                                         const float *__restrict__ vb, int nl,
+                                                         int ld, float *__restrict__ pw)
+{
+    extern __shared__ float wsh[];  // [min(n_tm, kPwChunk)] entry weights | [nl] sums
+    const int pos = blockIdx.x;
+    const int b = pos / sv.L, i = pos % sv.L;
+    const float *al = va + ((size_t)b * (sv.Lpad + 1) + i) * sv.Sp;
+    const float *be = vb + ((size_t)b * (sv.Lpad + 1) + i + 1) * sv.Sp;
+    pair_weights(d, al, be, nl, pw + (size_t)pos * ld, wsh);
 }
 
 // Streaming q writer (V % 4 == 0, lookup tables in LDS).  kQParts
@@ -869,19 +880,38 @@ constexpr int kLeafMsgThreads = 512;
 constexpr int kLeafMsgPer = 24;  // leaf entries per thread
 constexpr int kLeafMsgMax = kLeafMsgThreads * kLeafMsgPer;
 
+//
+// pw (non-null): each workgroup also writes the q writer's pair weights of
+// one position (pair_weights; marg_pairw is then not launched): the alpha
+// workgroup of leaves (l, l+1) those of position l+1 (alpha_{l+1} its own
+// output, beta_{l+2} from the level above), the beta workgroup those of
+// position l (alpha_l from the level above, beta_{l+1} its own output).
+// md: midpoint draws riding on the launch, md.nwg workgroups before the
+// products.
+static_assert(kLeafMsgThreads == kPwThreads, "the leaf workgroups run pair_weights");
+static_assert(kLeafMsgThreads >= kSubThreads && kMsgThreads >= kSubThreads,
+              "message-pass workgroups can carry a midpoint subtree");
+
 __global__ __launch_bounds__(kLeafMsgThreads) void marg_leaf(
     DevTable d, StepView sv, EmitSrc src, const int32_t *__restrict__ meta,
     float *__restrict__ va, int32_t *__restrict__ ea, float *__restrict__ vb,
-    int32_t *__restrict__ eb)
+    int32_t *__restrict__ eb, float *__restrict__ pw, int pw_nl, int pw_ld, MidDraws md)
 {
-    extern __shared__ float lsh[];  // terms [npairs] | g [S] | rf [S]
-    float *term = lsh;
-    float *gsh = lsh + d.npairs;
+    if ((int)blockIdx.x < md.nwg) {  // midpoint draws riding on the launch, dispatched first
+        mid_draws_wg(d, sv, md, (int)blockIdx.x);
+        return;
+    }
+    // [own output, Sp, with pw] | terms [npairs] | g [S] | rf [S]; after the
+    // leaf product the terms region holds pair_weights' scratch
+    extern __shared__ float lsh[];
+    float *own = lsh;
+    float *term = lsh + (pw ? sv.Sp : 0);
+    float *gsh = term + d.npairs;
     int *rsh = reinterpret_cast<int *>(gsh + d.S);
     __shared__ int sh_max[kLeafMsgThreads / 64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nn = sv.Lpad >> 1;
-    const int prod = blockIdx.x, beta = prod & 1, bn = prod >> 1;
+    const int prod = (int)blockIdx.x - md.nwg, beta = prod & 1, bn = prod >> 1;
     const int b = bn / nn, idx = bn % nn;
     const int l = 2 * idx, m = l + 1;
     const int i = beta ? l + 1 : l;  // position of the leaf
@@ -940,8 +970,11 @@ __global__ __launch_bounds__(kLeafMsgThreads) void marg_leaf(
     }
     __syncthreads();
     if (!real) {  // identity leaf: v = 1 on the diagonal
-        for (int j = tid; j < sv.Sp; j += kLeafMsgThreads)
-            vout[j] = j < d.S ? gsh[j] * scale2(1.f, -rsh[j]) : 0.f;
+        for (int j = tid; j < sv.Sp; j += kLeafMsgThreads) {
+            const float o = j < d.S ? gsh[j] * scale2(1.f, -rsh[j]) : 0.f;
+            vout[j] = o;
+            if (pw) own[j] = o;
+        }
     } else {
 #pragma unroll
         for (int u = 0; u < kLeafMsgPer; ++u) {
@@ -957,11 +990,49 @@ __global__ __launch_bounds__(kLeafMsgThreads) void marg_leaf(
             float acc = 0.f;
             if (j < d.S)
                 for (int k = seg[j]; k < seg[j + 1]; ++k) acc += term[k];
-            vout[j] = G > kNeg ? acc : 0.f;
+            const float o = G > kNeg ? acc : 0.f;
+            vout[j] = o;
+            if (pw) own[j] = o;
         }
     }
     if (tid == 0)
         ebase[(size_t)b * (sv.Lpad + 1) + m] = (G > kNeg && ein > kNeg) ? ein + G : kNeg;
+    // the weights of position l (beta) or l+1 (alpha), a real position
+    const int wpos = beta ? l : l + 1;
+    if (pw && wpos < sv.L) {
+        __syncthreads();  // own complete; the terms region is free
+        const size_t vrow = (size_t)b * (sv.Lpad + 1);
+        const float *al = beta ? va + (vrow + l) * sv.Sp : own;
+        const float *be = beta ? own : vb + (vrow + l + 2) * sv.Sp;
+        pair_weights(d, al, be, pw_nl, pw + ((size_t)b * sv.L + wpos) * pw_ld, term);
+    }
+}
+
+}  // namespace
+
+namespace {
+
+// the leaf level straight from pair values when the leaf entries exist
+// (Sp < 65536) and their terms fit in LDS
+bool sparse_leaf_ok(const DevTable &d, const Geometry &g)
+{
+    return g.K >= 1 && g.Sp <= kLeafTile && d.npairs <= kLeafMsgMax &&
+           ((size_t)d.npairs + 2 * (size_t)d.S) * 4 <= 64 * 1024;
+}
+
+// dynamic LDS of marg_leaf, with or without the pair weights
+size_t leaf_lds(const DevTable &d, const Geometry &g, const WsLayout &w, bool pw)
+{
+    const size_t leaf = (size_t)d.npairs + 2 * (size_t)d.S;
+    if (!pw) return leaf * 4;
+    const size_t pws = (size_t)std::min(d.n_tm, kPwChunk) + w.pw_nl;
+    return ((size_t)g.Sp + std::max(leaf, pws)) * 4;
+}
+
+// the leaf level writes the pair weights (and marg_pairw is not launched)
+bool leaf_writes_pw(const DevTable &d, const Geometry &g, const WsLayout &w)
+{
+    return sparse_leaf_ok(d, g) && g.L > 0 && leaf_lds(d, g, w, true) <= 64 * 1024;
 }
 
 }  // namespace
@@ -971,13 +1042,14 @@ int launch_marginals(const DevTable &d, const Geometry &g, const float *p, const
                      int32_t conf_mode, float *q, float *conf, uint8_t *ws, const WsLayout &w,
                      int32_t *status, void *stream)
 {
-    int rc = launch_marg_pass(d, g, p, tree, meta, ws, w, stream);
+    int rc = launch_marg_pass(d, g, p, tree, meta, ws, w, stream, false, 0, status);
     if (rc) return rc;
     return launch_marg_out(d, g, p, logZ, tokens, conf_mode, q, conf, ws, w, 0, status, stream);
 }
 
 int launch_marg_pass(const DevTable &d, const Geometry &g, const float *p, const float *tree,
-                     const int32_t *meta, uint8_t *ws, const WsLayout &w, void *stream)
+                     const int32_t *meta, uint8_t *ws, const WsLayout &w, void *stream,
+                     bool ride, uint64_t seed, int32_t *status)
 {
     hipStream_t st = (hipStream_t)stream;
     StepView sv = step_view(g);
@@ -985,10 +1057,7 @@ int launch_marg_pass(const DevTable &d, const Geometry &g, const float *p, const
     int32_t *ea = (int32_t *)(ws + w.ea), *eb = (int32_t *)(ws + w.eb);
     float *rcut = (float *)(ws + w.rcut);
     const size_t lds = (size_t)g.Sp * (sizeof(float) + sizeof(int));
-    // the leaf level straight from pair values when the leaf entries exist
-    // (Sp < 65536) and their terms fit in LDS
-    const bool sparse_leaf = g.K >= 1 && g.Sp <= kLeafTile && d.npairs <= kLeafMsgMax &&
-                             ((size_t)d.npairs + 2 * (size_t)d.S) * 4 <= 64 * 1024;
+    const bool sparse_leaf = sparse_leaf_ok(d, g);
     // the boundary vectors: built by the top marg_level launch, else here
     const bool init_in_top = g.K >= 1 && !(g.K == 1 && sparse_leaf);
     hipError_t e;
@@ -1005,29 +1074,49 @@ int launch_marg_pass(const DevTable &d, const Geometry &g, const float *p, const
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return (int)e;
     }
+    // the midpoint launches (kSubDepth levels each) ride on the last ones of
+    // the message pass, which take longer than they do; both depend only on
+    // the tree, and the launches of each chain stay in order
+    const int nmid = (g.K + kSubDepth - 1) / kSubDepth;
+    auto draws_for = [&](int level) {
+        MidDraws m{tree, meta, seed, 0, 0, 0, (int32_t *)(ws + w.zc), (int32_t *)(ws + w.tpair),
+                   (uint32_t *)(ws + w.tdbit), status};
+        const int j = level - (g.K - nmid + 1);
+        if (ride && j >= 0) {
+            m.level0 = 1 + j * kSubDepth;
+            m.depth = std::min(kSubDepth, g.K - m.level0 + 1);
+            m.nwg = g.B << (m.level0 - 1);
+        }
+        return m;
+    };
     for (int level = 1; level <= g.K; ++level) {
         const int nn = 1 << (level - 1);
         const int products = g.B * nn * 2;
+        const MidDraws md = draws_for(level);
         if (level == g.K && sparse_leaf) {
-            const size_t llds = ((size_t)d.npairs + 2 * (size_t)d.S) * 4;
+            const bool wpw = leaf_writes_pw(d, g, w);
+            const size_t llds = leaf_lds(d, g, w, wpw);
             if (llds > 48 * 1024) {
                 e = hipFuncSetAttribute(reinterpret_cast<const void *>(&marg_leaf),
                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)llds);
                 if (e != hipSuccess) return (int)e;
             }
-            marg_leaf<<<products, kLeafMsgThreads, llds, st>>>(d, sv, emit_src(d, g, p, ws, w), meta,
-                                                              va, ea, vb, eb);
+            float *pw = wpw ? (float *)(ws + w.pw) : nullptr;
+            marg_leaf<<<products + md.nwg, kLeafMsgThreads, llds, st>>>(
+                d, sv, emit_src(d, g, p, ws, w), meta, va, ea, vb, eb, pw, w.pw_nl, w.pw_ld, md);
             e = hipGetLastError();
             if (e != hipSuccess) return (int)e;
             continue;
         }
         const int top = level == 1 && init_in_top;
         if (products * ((g.Sp + 255) / 256) >= 256) {
-            dim3 grid((g.Sp + 255) / 256, products);
-            marg_level<256><<<grid, kMsgThreads, lds, st>>>(d, sv, tree, meta, nn, va, ea, vb, eb, top);
+            dim3 grid((g.Sp + 255) / 256, products + md.nwg);
+            marg_level<256><<<grid, kMsgThreads, lds, st>>>(d, sv, tree, meta, nn, va, ea, vb, eb, top,
+                                                            md);
         } else {
-            dim3 grid((g.Sp + 63) / 64, products);
-            marg_level<64><<<grid, kMsgThreads, lds, st>>>(d, sv, tree, meta, nn, va, ea, vb, eb, top);
+            dim3 grid((g.Sp + 63) / 64, products + md.nwg);
+            marg_level<64><<<grid, kMsgThreads, lds, st>>>(d, sv, tree, meta, nn, va, ea, vb, eb, top,
+                                                           md);
         }
         e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
@@ -1095,7 +1184,7 @@ int launch_marg_out(const DevTable &d, const Geometry &g, const float *p, const 
         double *tcs = mode == 1 ? (double *)(ws + w.tcs) : nullptr;
         int32_t *tcs_ok = mode == 1 ? (int32_t *)(ws + w.tcs_ok) : nullptr;
         const dim3 sgrid(g.L * kQParts, g.B);
-        if (mode != 2) {  // the pair weights of mode 1 serve mode 2
+        if (mode != 2 && !leaf_writes_pw(d, g, w)) {  // else the leaf level wrote them
             const size_t plds = w.pw_nl ? ((size_t)std::min(d.n_tm, kPwChunk) + w.pw_nl) * 4 : 0;
             if (plds > 48 * 1024) {
                 e = hipFuncSetAttribute(reinterpret_cast<const void *>(&marg_pairw),

@@ -245,11 +245,9 @@ int fa_marginals(const fa_table *t, const float *p, int32_t B, int32_t L, const 
  * sampled pair is a dense pair take their chunk sums from the q writer's pass
  * over p instead of reading the row again (the same sums in the same order);
  * otherwise the call runs the two calls' launches in order.  On the first
- * path the midpoint draws run on a side stream of the library (one per
- * device, created on first use and kept until the process ends; default
- * priority) while the message pass runs on `stream`; both are joined to
- * `stream` by events before the call returns, so `stream` orders everything
- * the call does, also under stream capture.
+ * path the midpoint draws, which depend only on the tree, run as extra
+ * workgroups of the message pass's last launches; everything stays on
+ * `stream`.
  * Cite: as fa_sample and fa_marginals.
  *   arguments  as in fa_sample and fa_marginals; tokens is an output here
  *              and required in both confidence modes
