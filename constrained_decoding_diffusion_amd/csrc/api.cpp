@@ -164,12 +164,13 @@ extern "C" int fa_sample_marginals(const fa_table *t, const float *p, int32_t B,
         rc = launch_marg_pass(d, g, p, tree, meta, wb, w, stream, g.K >= 1, seed, row_status);
     if (!rc)
         rc = launch_marg_out(d, g, p, logZ, nullptr, conf_mode, q, conf, wb, w, 1, row_status,
-                             stream);
+                             stream, nullptr);
     if (!rc)
-        rc = launch_sample_tokens(d, g, p, seed, states, tokens, wb, w, true, row_status, stream);
+        rc = launch_sample_tokens(d, g, p, seed, states, tokens, wb, w, true, row_status, stream,
+                                  false);
     if (!rc)
         rc = launch_marg_out(d, g, p, logZ, tokens, conf_mode, q, conf, wb, w, 2, row_status,
-                             stream);
+                             stream, states);
     return hip_rc(rc);
 }
 

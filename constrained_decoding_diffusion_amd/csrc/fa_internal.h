@@ -196,14 +196,14 @@ int launch_marginals(const DevTable &d, const Geometry &g, const float *p, const
 // States: the root and every midpoint (compact ids in ws at w.zc), and per
 // position the pair of its two boundary states (w.tpair: index or -1;
 // w.tdbit: its dense-mask bit or 0).  Tokens:
-// the token draws and the state output; `pre` non-null takes the dense-pair
+// the token draws and (finish) the state output; `pre` takes the dense-pair
 // chunk sums from ws at w.tcs where w.tcs_ok marks a position.
 int launch_sample_states(const DevTable &d, const Geometry &g, const float *tree,
                          const int32_t *meta, uint64_t seed, uint8_t *ws, const WsLayout &w,
                          int32_t *status, void *stream);
 int launch_sample_tokens(const DevTable &d, const Geometry &g, const float *p, uint64_t seed,
                          int32_t *states, int32_t *tokens, uint8_t *ws, const WsLayout &w,
-                         bool pre, int32_t *status, void *stream);
+                         bool pre, int32_t *status, void *stream, bool finish = true);
 // Message pass (alpha/beta at every boundary, range weights per cut).  ride
 // (K >= 1): the launches of launch_sample_states (with `seed`, flagging
 // `status`) ride on its last launches as extra workgroups.
@@ -213,14 +213,15 @@ int launch_marg_pass(const DevTable &d, const Geometry &g, const float *p, const
 // The q writer and the confidence.  mode 0: the plain writer; 1: the
 // streaming writer that also sums the token draws' dense-pair chunks (the
 // boundary states in ws at w.zc; tokens unused); 2: after mode 1 and the
-// token draws: the PROB confidence of the sampled tokens, and zeros and -inf
-// for rows the draws flagged.  marg_joint_ok tells whether modes 1 and 2
-// apply.
+// token draws (launched without their finish): the PROB confidence of the
+// sampled tokens, zeros and -inf for rows the draws flagged, and the states
+// output (and -1 tokens of flagged rows) the draws' finish would write.
+// marg_joint_ok tells whether modes 1 and 2 apply.
 bool marg_joint_ok(const DevTable &d, const Geometry &g, const float *p, const float *q,
                    int32_t conf_mode, const WsLayout &w);
 int launch_marg_out(const DevTable &d, const Geometry &g, const float *p, const double *logZ,
                     const int32_t *tokens, int32_t conf_mode, float *q, float *conf, uint8_t *ws,
-                    const WsLayout &w, int mode, int32_t *status, void *stream);
+                    const WsLayout &w, int mode, int32_t *status, void *stream, int32_t *states);
 
 }  // namespace fa
 

@@ -807,16 +807,26 @@ __global__ void marg_negent_sum(int npos, const double *__restrict__ hpart,
 // writer's lookup tables in the same order (per byte of the mask, its set
 // bits ascending from 0; the bytes' sums in byte order; then the token-list
 // weight), so conf equals the writer's value bit for bit.
+//
+// It also finishes the sampler's outputs as sample_finalize does: states in
+// original ids (-1 for a flagged row) and -1 tokens for a flagged row.
 template <int NG, bool SELBIT, bool LISTALL>
 __global__ __launch_bounds__(64) void marg_conf_tok(
     DevTable d, StepView sv, const float *__restrict__ p, const double *__restrict__ logZ,
-    const int32_t *__restrict__ tokens, int conf_mode, float *__restrict__ q,
+    int32_t *__restrict__ tokens, int conf_mode, float *__restrict__ q,
     float *__restrict__ conf, const int32_t *__restrict__ ea, const int32_t *__restrict__ eb,
     const float *__restrict__ pw, int pw_ld, double *__restrict__ hpart,
-    const int32_t *__restrict__ status)
+    const int32_t *__restrict__ status, const int32_t *__restrict__ zc,
+    int32_t *__restrict__ states)
 {
     const int b = blockIdx.y, i = blockIdx.x, lane = threadIdx.x;
     const size_t pos = (size_t)b * sv.L + i;
+    const bool flagged = status[b] != 0;
+    if (lane == 1 || (lane == 2 && i == sv.L - 1)) {  // states i and, for the last, L
+        const int k = lane == 1 ? i : sv.L;
+        const int zz = zc[(size_t)b * (sv.Lpad + 1) + k];
+        states[(size_t)b * (sv.L + 1) + k] = (flagged || zz < 0) ? -1 : d.orig[zz];
+    }
     const double lz = logZ[b];
     const int e1 = ea[(size_t)b * (sv.Lpad + 1) + i], e2 = eb[(size_t)b * (sv.Lpad + 1) + i + 1];
     const bool ok = status[b] == 0 && lz > -INFINITY && e1 > kNeg && e2 > kNeg;
@@ -827,7 +837,10 @@ __global__ __launch_bounds__(64) void marg_conf_tok(
             for (int v = lane; v < d.V; v += 64) qrow[v] = 0.f;
         }
         if (negent && lane < kQParts) hpart[pos * kQParts + lane] = -INFINITY;
-        if (lane == 0) conf[pos] = -INFINITY;
+        if (lane == 0) {
+            conf[pos] = -INFINITY;
+            if (flagged) tokens[pos] = -1;
+        }
         return;
     }
     if (negent || lane != 0) return;
@@ -1044,7 +1057,8 @@ int launch_marginals(const DevTable &d, const Geometry &g, const float *p, const
 {
     int rc = launch_marg_pass(d, g, p, tree, meta, ws, w, stream, false, 0, status);
     if (rc) return rc;
-    return launch_marg_out(d, g, p, logZ, tokens, conf_mode, q, conf, ws, w, 0, status, stream);
+    return launch_marg_out(d, g, p, logZ, tokens, conf_mode, q, conf, ws, w, 0, status, stream,
+                           nullptr);
 }
 
 int launch_marg_pass(const DevTable &d, const Geometry &g, const float *p, const float *tree,
@@ -1161,7 +1175,7 @@ bool marg_joint_ok(const DevTable &d, const Geometry &g, const float *p, const f
 
 int launch_marg_out(const DevTable &d, const Geometry &g, const float *p, const double *logZ,
                     const int32_t *tokens, int32_t conf_mode, float *q, float *conf, uint8_t *ws,
-                    const WsLayout &w, int mode, int32_t *status, void *stream)
+                    const WsLayout &w, int mode, int32_t *status, void *stream, int32_t *states)
 {
     hipStream_t st = (hipStream_t)stream;
     StepView sv = step_view(g);
@@ -1198,8 +1212,9 @@ int launch_marg_out(const DevTable &d, const Geometry &g, const float *p, const 
         if (mode == 2) {
             const dim3 cgrid(g.L, g.B);
 #define FA_MARG_CT(NG, SB, LA)                                                                 \
-    marg_conf_tok<NG, SB, LA><<<cgrid, 64, 0, st>>>(d, sv, p, logZ, tokens, conf_mode, q, conf, \
-                                                    ea, eb, pw, w.pw_ld, hpart, status)
+    marg_conf_tok<NG, SB, LA><<<cgrid, 64, 0, st>>>(d, sv, p, logZ, (int32_t *)tokens, conf_mode, \
+                                                    q, conf, ea, eb, pw, w.pw_ld, hpart, status, \
+                                                    (const int32_t *)(ws + w.zc), states)
             if (d.selbit) {
                 if (ng == 1) FA_MARG_CT(1, true, false);
                 else if (ng == 2) FA_MARG_CT(2, true, false);

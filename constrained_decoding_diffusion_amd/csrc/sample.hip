@@ -384,7 +384,7 @@ int launch_sample_states(const DevTable &d, const Geometry &g, const float *tree
 
 int launch_sample_tokens(const DevTable &d, const Geometry &g, const float *p, uint64_t seed,
                          int32_t *states, int32_t *tokens, uint8_t *ws, const WsLayout &w,
-                         bool pre, int32_t *status, void *stream)
+                         bool pre, int32_t *status, void *stream, bool finish)
 {
     hipStream_t st = (hipStream_t)stream;
     StepView sv = step_view(g);
@@ -395,7 +395,7 @@ int launch_sample_tokens(const DevTable &d, const Geometry &g, const float *p, u
     sample_tokens<<<dim3(g.L, g.B), kTokThreads, 0, st>>>(d, sv, p, seed, zc, tpair, tokens, status,
                                                            tcs, tcs_ok, w.tcs_nch);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return (int)e;
+    if (e != hipSuccess || !finish) return (int)e;
     sample_finalize<<<dim3((g.L + 1 + 255) / 256, g.B), 256, 0, st>>>(d, sv, zc, states, tokens,
                                                                       status);
     return (int)hipGetLastError();
