@@ -576,9 +576,9 @@ __global__ __launch_bounds__(kPwThreads) void marg_pairw(DevTable d, StepView sv
 // each thread handles U float4 groups per iteration.  Every global
 // load of the loop is unconditional (clamped index) and issued one iteration
 // ahead, and the per-token weight reads LDS only: the dense-mask lookup
-// table, the token-list weights (found by binary search over the sorted
-// token-list tokens when the mask's flag bit marks the token, or through
-// tok2sel), and the range weights at each cut.
+// table, the token-list weights (found in the token's 256-token bucket of
+// the sorted token-list tokens when the mask's flag bit marks the token, or
+// through tok2sel), and the range weights at each cut.
 //
 // The parts are whole chunks of kRowChunk4 float4 groups, so iteration `it`
 // of a part covers one chunk of the token sampler's streamed pass.  SAMP
@@ -604,7 +604,7 @@ __attribute__((amdgpu_waves_per_eu(SAMP && !LISTALL ? 4 : 1))) void marg_q_strea
     constexpr bool LISTS = SELBIT || LISTALL;
     constexpr bool MASK = NG > 0 || SELBIT;
     static_assert(!SAMP || NG > 0, "the token draws' sums read the dense mask");
-    extern __shared__ float dyn[];  // rsel [nsel] | selk [nsel] | rcl [ncut]
+    extern __shared__ float dyn[];  // rsel [nsel] | selk [nsel] | slb [V/256 + 2] | rcl [ncut]
     __shared__ float lut[NG > 0 ? NG : 1][256];
     __shared__ double sh_h[4];
     const int b = blockIdx.y, i = blockIdx.x / kQParts, part = blockIdx.x % kQParts;
@@ -633,7 +633,9 @@ __attribute__((amdgpu_waves_per_eu(SAMP && !LISTALL ? 4 : 1))) void marg_q_strea
     const float *pwr = pw + pos * pw_ld;
     float *rsel = dyn;
     int *selk = reinterpret_cast<int *>(dyn + (LISTS ? d.nsel : 0));
-    float *rcl = dyn + (LISTS ? d.nsel : 0) + (SELBIT ? d.nsel : 0);
+    const int nslb = SELBIT ? d.V / 256 + 2 : 0;
+    int *slb = selk + (SELBIT ? d.nsel : 0);
+    float *rcl = dyn + (LISTS ? d.nsel : 0) + (SELBIT ? d.nsel + nslb : 0);
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
         float sm = 0.f;
@@ -646,6 +648,8 @@ __attribute__((amdgpu_waves_per_eu(SAMP && !LISTALL ? 4 : 1))) void marg_q_strea
             rsel[k] = pwr[kDenseMax + k];
             if (SELBIT) selk[k] = d.sel_tok[k];
         }
+    if (SELBIT)
+        for (int k = tid; k < nslb; k += kQThreads) slb[k] = d.sel_lb[k];
     if (RANGES)
         for (int c = tid; c < d.ncut; c += kQThreads) rcl[c] = rcut[pos * d.ncut + c];
     const uint32_t dbit = SAMP ? tdbit[pos] : 0u;
@@ -660,13 +664,12 @@ __attribute__((amdgpu_waves_per_eu(SAMP && !LISTALL ? 4 : 1))) void marg_q_strea
         if constexpr (NG > 3) r += lut[3][(m >> 24) & 255u];
         if constexpr (SELBIT) {
             if (m & kSelBit) {
-                int lo = 0, hi = d.nsel - 1;
-                while (lo < hi) {
-                    const int mid = (lo + hi) >> 1;
-                    if (selk[mid] < v) lo = mid + 1;
-                    else hi = mid;
-                }
-                r += rsel[lo];
+                // v is a token-list token: its index is found inside its
+                // 256-token bucket (usually the first entry)
+                int lo = slb[v >> 8];
+                const int hi = slb[(v >> 8) + 1];
+                while (lo < hi && selk[lo] < v) ++lo;
+                r += rsel[min(lo, d.nsel - 1)];
             }
         }
         if constexpr (LISTALL) {
@@ -1148,9 +1151,11 @@ int launch_marg_pass(const DevTable &d, const Geometry &g, const float *p, const
 
 namespace {
 
+// rsel [nsel] | selk [nsel] and its 256-token index (selbit) | rcl [ncut]
 size_t q_stream_lds(const DevTable &d)
 {
     return (d.nsel > 0 ? (size_t)d.nsel * (d.selbit ? 8 : 4) : 0) +
+           (d.nsel > 0 && d.selbit ? ((size_t)d.V / 256 + 2) * 4 : 0) +
            (d.ncut > 0 ? (size_t)d.ncut * 4 : 0);
 }
 
