@@ -231,6 +231,8 @@ def main():
     ap.add_argument("--workload", type=int, default=3, help="preset 1..5 (default 3)")
     ap.add_argument("--separate", action="store_true",
                     help="fa_sample then fa_marginals instead of fa_sample_marginals")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the other call form and the stage split (profiling runs)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="first run one plain device copy of 1 GiB (counter calibration)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -333,7 +335,8 @@ def main():
 
     for s in range(args.warmup):
         one_step(w.seed + s)
-        one_step(w.seed + s, separate=not args.separate)
+        if not args.headline_only:
+            one_step(w.seed + s, separate=not args.separate)
     torch.cuda.synchronize()
     kevs = []
     for s in range(args.steps):
@@ -343,9 +346,12 @@ def main():
     # which cost nothing measurable
     total_ms, wall = timed(args.separate, kevs)
     fa.profile_kernel(fa.FA_PROF_NONE)
-    other_ms, _ = timed(not args.separate)
-    stage_us = stage_split(args.separate)
-    other_stage_us = stage_split(not args.separate)
+    if args.headline_only:
+        other_ms, stage_us, other_stage_us = None, None, None
+    else:
+        other_ms, _ = timed(not args.separate)
+        stage_us = stage_split(args.separate)
+        other_stage_us = stage_split(not args.separate)
     kern_us = {}
     for pid, a, b, name in kevs:
         ms = hev.elapsed_ms(a, b)
@@ -358,23 +364,25 @@ def main():
     status = bufs.status.cpu().numpy()
 
     work = algorithmic_work(tb, w.B, w.L)
-    stages = {
-        "build_transitions": dict(us=stage_us["build_transitions"], bound="hbm",
-                                  algorithmic_bytes=work["a1_bytes"],
-                                  gbs=work["a1_bytes"] / (stage_us["build_transitions"] * 1e3)),
-        "span_tree": dict(us=stage_us["span_tree"], bound="mfma", algorithmic_flops=work["a2_flops"],
-                          tflops=work["a2_flops"] / (stage_us["span_tree"] * 1e6)),
-    }
-    if args.separate:
-        stages["sample"] = dict(us=stage_us["sample"], bound="latency")
-        last = "marginals"
-    else:
-        last = "sample_marginals"
-    stages[last] = dict(us=stage_us[last], bound="hbm", algorithmic_bytes=work["a4_bytes"],
-                        gbs=work["a4_bytes"] / (stage_us[last] * 1e3))
-    for n in ("build_transitions", last):
-        stages[n]["frac"] = stages[n]["gbs"] / HBM_PEAK_GBS
-    stages["span_tree"]["frac"] = stages["span_tree"]["tflops"] / FP32_MFMA_PEAK_TFLOPS
+    stages = None
+    if stage_us is not None:
+        stages = {
+            "build_transitions": dict(us=stage_us["build_transitions"], bound="hbm",
+                                      algorithmic_bytes=work["a1_bytes"],
+                                      gbs=work["a1_bytes"] / (stage_us["build_transitions"] * 1e3)),
+            "span_tree": dict(us=stage_us["span_tree"], bound="mfma", algorithmic_flops=work["a2_flops"],
+                              tflops=work["a2_flops"] / (stage_us["span_tree"] * 1e6)),
+        }
+        if args.separate:
+            stages["sample"] = dict(us=stage_us["sample"], bound="latency")
+            last = "marginals"
+        else:
+            last = "sample_marginals"
+        stages[last] = dict(us=stage_us[last], bound="hbm", algorithmic_bytes=work["a4_bytes"],
+                            gbs=work["a4_bytes"] / (stage_us[last] * 1e3))
+        for n in ("build_transitions", last):
+            stages[n]["frac"] = stages[n]["gbs"] / HBM_PEAK_GBS
+        stages["span_tree"]["frac"] = stages["span_tree"]["tflops"] / FP32_MFMA_PEAK_TFLOPS
     kernels = {}
     for name, us in kern_us.items():
         kw = work["kernels"][name]
@@ -409,10 +417,11 @@ def main():
         "roofline": roof,
         "kernels": kernels,
         "stages": stages,
-        "other_form": {"calls": "joint" if args.separate else "separate",
-                       "us_per_step": 1000.0 * other_ms / args.steps,
-                       "steps_per_s": 1000.0 * args.steps / other_ms,
-                       "stages_us": other_stage_us},
+        "other_form": None if other_ms is None else {
+            "calls": "joint" if args.separate else "separate",
+            "us_per_step": 1000.0 * other_ms / args.steps,
+            "steps_per_s": 1000.0 * args.steps / other_ms,
+            "stages_us": other_stage_us},
         "wall_s": wall,
         "row_status": status.tolist(),
     }

@@ -1099,7 +1099,7 @@ int launch_marg_pass(const DevTable &d, const Geometry &g, const float *p, const
         MidDraws m{tree, meta, seed, 0, 0, 0, (int32_t *)(ws + w.zc), (int32_t *)(ws + w.tpair),
                    (uint32_t *)(ws + w.tdbit), status};
         const int j = level - (g.K - nmid + 1);
-        if (ride && j >= 0) {
+        if (ride && j >= 0 && j < nmid) {
             m.level0 = 1 + j * kSubDepth;
             m.depth = std::min(kSubDepth, g.K - m.level0 + 1);
             m.nwg = g.B << (m.level0 - 1);

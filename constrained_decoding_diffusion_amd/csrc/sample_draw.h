@@ -192,6 +192,8 @@ __device__ void sample_levels_wg(const DevTable &d, const StepView &sv,
                                  int32_t *__restrict__ tpair, uint32_t *__restrict__ tdbit,
                                  int32_t *__restrict__ status, int blk)
 {
+    // a launch outside the tree's levels draws nothing (uniform per workgroup)
+    if (level0 < 1 || depth < 1 || depth > kSubDepth || level0 + depth - 1 > sv.K) return;
     __shared__ int zs[(1 << kSubDepth) + 1];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nn0 = 1 << (level0 - 1);
