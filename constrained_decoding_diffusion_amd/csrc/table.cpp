@@ -359,7 +359,17 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
     t.S_orig = S;
     t.V = V;
     t.S = (int32_t)t.orig.size();
+    // padded to 64; for large automata to 256 (or 128) when that adds at
+    // most 10% to the S^3 products, so the span tree runs on the large-tile
+    // kernels (Sp a multiple of 256 or 128)
     t.Sp = (t.S + kSpAlign - 1) / kSpAlign * kSpAlign;
+    for (int32_t a : {256, 128}) {
+        const double sp = (double)((t.S + a - 1) / a * a);
+        if (t.S >= 1024 && sp * sp * sp <= 1.10 * (double)t.Sp * t.Sp * t.Sp) {
+            t.Sp = (int32_t)sp;
+            break;
+        }
+    }
     t.start = cid[start];
     t.acc.clear();
     for (int32_t k = 0; k < n_accept; ++k)
