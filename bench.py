@@ -231,6 +231,8 @@ def main():
     ap.add_argument("--workload", type=int, default=3, help="preset 1..5 (default 3)")
     ap.add_argument("--separate", action="store_true",
                     help="fa_sample then fa_marginals instead of fa_sample_marginals")
+    ap.add_argument("--gen-steps", type=int, default=16,
+                    help="denoising steps of the timed synthetic generation (0: none)")
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the other call form and the stage split (profiling runs)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -352,6 +354,27 @@ def main():
         other_ms, _ = timed(not args.separate)
         stage_us = stage_split(args.separate)
         other_stage_us = stage_split(not args.separate)
+    gen = None
+    if not args.headline_only and args.gen_steps > 0:
+        # a synthetic generation: T steps, each one constrained step and the
+        # remasking step (fa_commit), on a copy of p that ends one-hot
+        T = args.gen_steps
+        p_gen = p.clone()
+        fa.generate(tb, p_gen, T, w.seed, bufs=bufs)  # warm-up (the committed rows change the work)
+        p_gen.copy_(p)
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record()
+        _, committed = fa.generate(tb, p_gen, T, w.seed, bufs=bufs)
+        g1.record()
+        torch.cuda.synchronize()
+        gms = g0.elapsed_time(g1)
+        gen = {"T": T, "positions_per_step": f"ceil(masked / steps left), all {w.L} after {T}",
+               "ms": gms, "generations_per_s": 1000.0 / gms,
+               "all_committed": bool((committed[:, :w.L] == 1).all().item()),
+               "row_status": bufs.status.cpu().numpy().tolist()}
+        del p_gen
     kern_us = {}
     for pid, a, b, name in kevs:
         ms = hev.elapsed_ms(a, b)
@@ -417,6 +440,7 @@ def main():
         "roofline": roof,
         "kernels": kernels,
         "stages": stages,
+        "generation": gen,
         "other_form": None if other_ms is None else {
             "calls": "joint" if args.separate else "separate",
             "us_per_step": 1000.0 * other_ms / args.steps,

@@ -22,7 +22,7 @@ FA_PROF_NONE, FA_PROF_EMISSION_DENSE, FA_PROF_TREE_LEVEL1, FA_PROF_MARG_Q = rang
 
 EXPORTS = ["fa_compile_table", "fa_table_upload", "fa_table_destroy", "fa_table_info",
            "fa_table_state_map", "fa_sizes", "fa_build_transitions", "fa_span_tree", "fa_sample",
-           "fa_marginals", "fa_sample_marginals", "fa_strerror", "fa_profile_kernel"]
+           "fa_marginals", "fa_sample_marginals", "fa_commit", "fa_strerror", "fa_profile_kernel"]
 
 
 class FaError(RuntimeError):
@@ -56,6 +56,7 @@ def lib():
     L.fa_sample.argtypes = [P, P, I32, I32, P, P, U64, P, P, P, SZ, P, P]
     L.fa_marginals.argtypes = [P, P, I32, I32, P, P, P, P, I32, P, P, P, SZ, P, P]
     L.fa_sample_marginals.argtypes = [P, P, I32, I32, P, P, P, U64, I32, P, P, P, P, P, SZ, P, P]
+    L.fa_commit.argtypes = [I32, I32, I32, P, P, I32, P, P, P, P, P]
     L.fa_profile_kernel.argtypes = [I32, P, P]
     L.fa_strerror.argtypes = [C.c_int]
     L.fa_strerror.restype = C.c_char_p
@@ -188,6 +189,40 @@ def sample_marginals(table: Table, p, bufs: StepBuffers, seed: int, conf_mode: i
         C.c_uint64(seed), conf_mode, _ptr(bufs.states), _ptr(bufs.tokens),
         _ptr(bufs.q if write_q else None), _ptr(bufs.conf), _ptr(bufs.ws), bufs.ws.numel(),
         _ptr(bufs.status), C.c_void_p(stream)))
+
+
+def commit(p, bufs: StepBuffers, committed, fresh, steps_left: int, stream):
+    """The remasking step (fa_commit) on the step's confidence and tokens:
+    committed and fresh are cuda int32 [B, L]; committed rows of p become
+    one-hot."""
+    B, L, V = p.shape
+    _check("fa_commit", lib().fa_commit(
+        B, L, V, _ptr(bufs.conf), _ptr(bufs.tokens), steps_left, _ptr(committed), _ptr(fresh),
+        _ptr(p), _ptr(bufs.status), C.c_void_p(stream)))
+
+
+def generate(table: Table, p, T: int, seed: int, conf_mode: int = FA_CONF_PROB, bufs=None,
+             on_step=None):
+    """A synthetic T-step denoising generation on torch's current stream: p
+    (cuda float32 [B, L, V], updated in place) holds the model's per-position
+    probabilities; each step is one constrained step (seed + t) followed by
+    the remasking step with T - t steps left, so after T steps every position
+    is committed and p is one-hot at the generated tokens.  on_step(t, bufs,
+    committed, fresh), if given, is called after each step's commit.  Returns
+    (bufs, committed)."""
+    import torch
+    B, L, V = p.shape
+    if bufs is None:
+        bufs = StepBuffers(table, B, L, want_q=True, device=p.device)
+    committed = torch.zeros((B, max(L, 1)), dtype=torch.int32, device=p.device)
+    fresh = torch.zeros_like(committed)
+    stream = torch.cuda.current_stream(p.device).cuda_stream
+    for t in range(T):
+        step(table, p, seed + t, bufs, conf_mode=conf_mode)
+        commit(p, bufs, committed, fresh, T - t, stream)
+        if on_step is not None:
+            on_step(t, bufs, committed, fresh)
+    return bufs, committed
 
 
 def profile_kernel(which: int, start_event=None, stop_event=None):

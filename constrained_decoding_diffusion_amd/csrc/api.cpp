@@ -174,6 +174,18 @@ extern "C" int fa_sample_marginals(const fa_table *t, const float *p, int32_t B,
     return hip_rc(rc);
 }
 
+extern "C" int fa_commit(int32_t B, int32_t L, int32_t V, const float *conf,
+                         const int32_t *tokens, int32_t steps_left, int32_t *committed,
+                         int32_t *fresh, float *p, const int32_t *row_status, fa_stream_t stream)
+{
+    if (B < 0 || L < 0 || V < 1 || steps_left < 1) return FA_EINVAL;
+    if (L > kCommitMaxL || B > 65535) return FA_ETOOBIG;
+    if (B == 0 || L == 0) return FA_OK;
+    if (!conf || !tokens || !committed || !fresh || !p) return FA_EINVAL;
+    return hip_rc(launch_commit(B, L, V, conf, tokens, steps_left, committed, fresh, p, row_status,
+                                stream));
+}
+
 extern "C" const char *fa_strerror(int code)
 {
     switch (code) {

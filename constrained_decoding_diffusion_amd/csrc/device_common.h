@@ -117,6 +117,13 @@ __device__ inline int pair_index(const DevTable &d, int a, int c)
     return (lo < d.row_ptr[a + 1] && d.pair_b[lo] == c) ? lo : -1;
 }
 
+__device__ inline int wave_sum_i(int x)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
 __device__ inline int wave_max_i(int x)
 {
 #pragma unroll

@@ -223,6 +223,12 @@ int launch_marg_out(const DevTable &d, const Geometry &g, const float *p, const 
                     const int32_t *tokens, int32_t conf_mode, float *q, float *conf, uint8_t *ws,
                     const WsLayout &w, int mode, int32_t *status, void *stream, int32_t *states);
 
+// The remasking step (commit.hip).
+constexpr int kCommitMaxL = 8192;  // positions per row the selection holds in LDS
+int launch_commit(int B, int L, int V, const float *conf, const int32_t *tokens, int steps_left,
+                  int32_t *committed, int32_t *fresh, float *p, const int32_t *status,
+                  void *stream);
+
 }  // namespace fa
 
 struct fa_table {

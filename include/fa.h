@@ -260,6 +260,32 @@ int fa_sample_marginals(const fa_table *t, const float *p, int32_t B, int32_t L,
                         float *q, float *conf, void *ws, size_t ws_bytes, int32_t *row_status,
                         fa_stream_t stream);
 
+/*
+ * fa_commit - the remasking step between denoising steps: per row b, of the
+ * n positions still masked (committed[b][i] == 0 and tokens[b][i] >= 0), the
+ * k = ceil(n / steps_left) with the largest conf[b][i] (NaN counts as -inf;
+ * ties go to the lower position; steps_left == 1 commits all of them) are
+ * committed to their sampled tokens: committed[b][i] = 1, fresh[b][i] = 1,
+ * and p[b][i][.] becomes one-hot at tokens[b][i], which is how the next step
+ * sees a committed position.  Every other fresh entry is 0, and a row with
+ * row_status[b] != 0 commits nothing.
+ * Cite: papernotes 关键设计 3 (the constrained marginal as the confidence
+ * that decides which positions are committed); paperfeed "Two immediate
+ * bonuses" (LLaDA: highest probability; Dream: lowest entropy, i.e. pass the
+ * FA_CONF_NEGENT confidence).
+ *   conf        device fp32 [B][L] (fa_marginals)
+ *   tokens      device int32 [B][L] (fa_sample)
+ *   committed   device int32 [B][L], read and updated
+ *   fresh       device int32 [B][L], written
+ *   p           device fp32 [B][L][V], committed rows rewritten
+ *   row_status  device int32 [B] or NULL
+ * Errors: FA_EINVAL (negative sizes, V < 1, steps_left < 1, NULL buffers),
+ * FA_ETOOBIG (L > 8192), FA_EHIP.
+ */
+int fa_commit(int32_t B, int32_t L, int32_t V, const float *conf, const int32_t *tokens,
+              int32_t steps_left, int32_t *committed, int32_t *fresh, float *p,
+              const int32_t *row_status, fa_stream_t stream);
+
 /* fa_strerror - static description of an error code. */
 const char *fa_strerror(int code);
 

@@ -182,3 +182,29 @@ def step(aut, p: np.ndarray, seed: int, rows=None, q_positions=None, conf_mode=0
                 d.update(q=q, lognorm=ln, conf=conf)
         out.append(d)
     return out
+
+
+def commit_topk(conf, tokens, committed, status, steps_left: int):
+    """The remasking step written out (papernotes 关键设计 3: the confidence
+    of each position's sampled token decides which positions are committed).
+    Per row b with status[b] == 0: the masked positions are those with
+    committed == 0 and a sampled token (>= 0); with n of them, the first
+    k = ceil(n / steps_left) (all n when steps_left == 1) in the order of
+    decreasing confidence, ties by increasing position, NaN counted as -inf,
+    are committed.  Returns (new committed, fresh) as int32 arrays [B, L]."""
+    conf = np.asarray(conf, np.float64)
+    tokens = np.asarray(tokens)
+    committed = np.array(committed, dtype=np.int32, copy=True)
+    fresh = np.zeros_like(committed)
+    B, L = committed.shape
+    for b in range(B):
+        if status is not None and status[b] != 0:
+            continue
+        masked = [i for i in range(L) if committed[b, i] == 0 and tokens[b, i] >= 0]
+        n = len(masked)
+        k = n if steps_left <= 1 else -(-n // steps_left)
+        key = lambda i: (-(conf[b, i] if conf[b, i] == conf[b, i] else -np.inf), i)
+        for i in sorted(masked, key=key)[:k]:
+            committed[b, i] = 1
+            fresh[b, i] = 1
+    return committed, fresh

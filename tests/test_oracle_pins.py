@@ -327,3 +327,32 @@ def test_samples_accepted_and_states_follow_delta():
             assert s in set(w.aut.accept.tolist())
             for pos, toks in w.commits[b:b + 1]:
                 np.testing.assert_array_equal(tk[pos], toks)
+
+
+def test_commit_topk_worked_examples():
+    """The remasking selection on hand-worked rows: k = ceil(masked / steps
+    left), highest confidence first, ties to the lower position, NaN last,
+    positions without a token or already committed skipped, flagged rows
+    untouched, and the last step commits everything left."""
+    nan, ninf = float("nan"), float("-inf")
+    conf = np.array([[0.5, 0.9, 0.9, 0.1],      # 4 masked, k = 2: the two 0.9 (ties by position)
+                     [0.5, 0.9, 0.7, 0.1],      # position 1 committed: 3 masked, k = 2 -> 2, 0
+                     [nan, 0.2, ninf, 0.3],     # NaN counts as -inf; k = 2 -> 3, 1
+                     [0.9, 0.8, 0.7, 0.6],      # flagged row: nothing
+                     [0.1, 0.2, 0.3, 0.4]])     # position 3 has no token: 3 masked, k = 2 -> 2, 1
+    tokens = np.array([[3, 1, 4, 1], [5, 9, 2, 6], [5, 3, 5, 8], [9, 7, 9, 3], [2, 3, 8, -1]])
+    committed = np.zeros((5, 4), np.int32)
+    committed[1, 1] = 1
+    status = np.array([0, 0, 0, 4, 0])
+    new, fresh = oracle.commit_topk(conf, tokens, committed, status, steps_left=2)
+    np.testing.assert_array_equal(fresh, [[0, 1, 1, 0], [1, 0, 1, 0], [0, 1, 0, 1], [0, 0, 0, 0],
+                                          [0, 1, 1, 0]])
+    np.testing.assert_array_equal(new, fresh + committed)
+    # the last step commits every masked position with a token
+    new1, fresh1 = oracle.commit_topk(conf, tokens, committed, status, steps_left=1)
+    np.testing.assert_array_equal(fresh1, [[1, 1, 1, 1], [1, 0, 1, 1], [1, 1, 1, 1], [0, 0, 0, 0],
+                                           [1, 1, 1, 0]])
+    # NaN and -inf tie as -inf: position order decides between them
+    _, f3 = oracle.commit_topk(np.array([[nan, ninf, 0.0]]), np.array([[1, 1, 1]]),
+                               np.zeros((1, 3), np.int32), None, steps_left=2)
+    np.testing.assert_array_equal(f3, [[1, 0, 1]])
