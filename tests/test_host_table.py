@@ -150,6 +150,20 @@ def test_step_calls_need_an_uploaded_table():
     assert rc == _fa.FA_EINVAL
 
 
+def test_commit_argument_checks():
+    """fa_commit rejects bad sizes before launching anything."""
+    lib = _fa.lib()
+    call = lambda B, L, V, steps: lib.fa_commit(B, L, V, None, None, steps, None, None, None,
+                                                None, None)
+    assert call(1, 9000, 10, 1) == _fa.FA_ETOOBIG
+    assert call(1, 16, 10, 0) == _fa.FA_EINVAL
+    assert call(1, 16, 0, 1) == _fa.FA_EINVAL
+    assert call(-1, 16, 10, 1) == _fa.FA_EINVAL
+    assert call(1, 16, 10, 1) == _fa.FA_EINVAL  # buffers missing
+    assert call(0, 16, 10, 1) == _fa.FA_OK      # nothing to do
+    assert call(2, 0, 10, 1) == _fa.FA_OK
+
+
 def test_profile_hook_arguments():
     lib = _fa.lib()
     assert lib.fa_profile_kernel(_fa.FA_PROF_NONE, None, None) == _fa.FA_OK
