@@ -283,6 +283,9 @@ constexpr int kStreamThreads = 256;
 constexpr int kRangePer = 16;
 constexpr int kRangeTile = kStreamThreads * kRangePer;
 
+// VEC: float4 loads (V % 4 == 0 and p 16-byte aligned), decided on the host
+// so the loads of the pipelined loop sit on no branch.
+template <bool VEC>
 __global__ __launch_bounds__(kStreamThreads) void emission_ranges(
     DevTable d, const float *__restrict__ p, int L, double *__restrict__ cutp,
     int32_t *__restrict__ status)
@@ -294,7 +297,6 @@ __global__ __launch_bounds__(kStreamThreads) void emission_ranges(
     __shared__ double sh_wsum[kStreamThreads / 64];
     __shared__ int sh_bad;
     if (tid == 0) sh_bad = 0;
-    const bool vec = (d.V & 3) == 0 && ((uintptr_t)row & 15) == 0;
     struct Run {
         float x[kRangePer];
         int c_lo;       // first cut index at or after the run's first token
@@ -305,7 +307,7 @@ __global__ __launch_bounds__(kStreamThreads) void emission_ranges(
         const int v0 = t0 + kRangePer * tid;
         r.c_lo = d.tok2cut[min(max(v0 - 1, 0), d.V - 1)];
         r.cbit = d.cutbits[min(v0 >> 5, nwords - 1)];
-        if (vec) {
+        if constexpr (VEC) {
             const float4 *r4 = reinterpret_cast<const float4 *>(row);
             const int g0 = v0 >> 2, gl = (d.V >> 2) - 1;
 #pragma unroll
@@ -348,26 +350,30 @@ __global__ __launch_bounds__(kStreamThreads) void emission_ranges(
         }
         __syncthreads();  // sh_wsum is rewritten by the next tile
         // cut points inside [v0, v0 + kRangePer): consecutive indices from c
+        // (a cut at token v0 + j holds the sum of the tokens before it: the
+        // run's prefix, added in token order; static indices keep xs in
+        // registers)
         if (v0 < d.V) {
             int c = v0 > 0 ? r.c_lo + 1 : 0;
             uint32_t m = (r.cbit >> (v0 & 31)) & ((1u << kRangePer) - 1u);
             if (v0 + kRangePer > d.V) m &= (1u << (d.V - v0)) - 1u;
             double run = off;
-            int k = 0;
-            while (m) {
-                const int at = __ffs(m) - 1;
-                m &= m - 1u;
-                for (; k < at; ++k) run += (double)xs[k];
-                out[c++] = run;
+#pragma unroll
+            for (int j = 0; j < kRangePer; ++j) {
+                if ((m >> j) & 1u) out[c++] = run;
+                run += (double)xs[j];
             }
         }
         carry = tot;
     };
+    // both tiles of a pass unconditionally (a tile past the row adds zeros
+    // and holds no cut): a tile summed inside a branch made the compiler wait
+    // for every outstanding load there, the prefetch included
     for (int t0 = 0; t0 < d.V; t0 += 2 * kRangeTile) {
         load(B, t0 + kRangeTile);
         tile(A, t0);
         load(A, t0 + 2 * kRangeTile);
-        if (t0 + kRangeTile < d.V) tile(B, t0 + kRangeTile);
+        tile(B, t0 + kRangeTile);
     }
     // cut points equal to V hold the row total
     const int nin = d.tok2cut[d.V - 1] + 1;  // cuts below V
@@ -679,7 +685,12 @@ int launch_build_transitions(const DevTable &d, const Geometry &g, const float *
         }
     }
     if (d.nseg > 0) {
-        emission_ranges<<<npos, kStreamThreads, 0, st>>>(d, p, g.L, (double *)src.cutp, status);
+        if ((d.V & 3) == 0 && ((uintptr_t)p & 15) == 0)
+            emission_ranges<true><<<npos, kStreamThreads, 0, st>>>(d, p, g.L, (double *)src.cutp,
+                                                                   status);
+        else
+            emission_ranges<false><<<npos, kStreamThreads, 0, st>>>(d, p, g.L, (double *)src.cutp,
+                                                                    status);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
     }
