@@ -49,25 +49,27 @@ def traffic_record(kernel: str):
 def algorithmic_work(tb, B, L):
     """Algorithmic bytes / flops per step and per launch of the measured
     kernels (the method's own data movement and arithmetic, no re-reads)."""
+    # the method's own sizes: S trimmed states (the kernels' padded Sp adds
+    # work that is not counted)
     S, Sp, V = tb.info["S"], tb.info["Sp"], tb.info["V"]
     Lpad = 1 << max(0, (L - 1).bit_length())
     K = Lpad.bit_length() - 1
     table_bytes = tb.device_bytes
     p_bytes = B * L * V * 4
     mask_bytes = V * 4
-    leaves = B * Lpad * Sp * Sp * 4
-    internal = B * (Lpad - 1) * Sp * Sp * 4
+    leaves = B * Lpad * S * S * 4
+    internal = B * (Lpad - 1) * S * S * 4
     return dict(
         a1_bytes=p_bytes + table_bytes + leaves,
-        a2_flops=2.0 * Sp ** 3 * B * (Lpad - 1),
+        a2_flops=2.0 * S ** 3 * B * (Lpad - 1),
         a4_bytes=p_bytes + p_bytes + leaves + internal + table_bytes,
         # per launch of the kernels the library can bracket with events
         kernels={
             "emission_dense": dict(bound="hbm", work=p_bytes + mask_bytes, unit="GB/s",
                                    per_unit="p read once (B*L*V*4) + token mask (V*4)"),
-            "span_gemm_level1": dict(bound="mfma", work=2.0 * Sp ** 3 * B * (Lpad // 2),
+            "span_gemm_level1": dict(bound="mfma", work=2.0 * S ** 3 * B * (Lpad // 2),
                                      unit="TFLOP/s",
-                                     per_unit="2*Sp^3 per product, B*Lpad/2 products"),
+                                     per_unit="2*S^3 per product (S trimmed states), B*Lpad/2 products"),
             "marg_q": dict(bound="hbm", work=2 * p_bytes + mask_bytes, unit="GB/s",
                            per_unit="p read + q write (2*B*L*V*4) + token mask (V*4)"),
         },
