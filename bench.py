@@ -224,6 +224,42 @@ def summarize_trace(trace_dir, command, workload=3):
         fh.write("\n".join(lines) + "\n")
 
 
+def summarize_mfma(pmc_dir, command, workload=3):
+    """profiles/mfma_<workload>.md from one rocprofv3 --pmc pass of MfmaUtil
+    (MFMA busy cycles over active cycles and SIMDs) and the executed MFMA
+    operations (SQ_INSTS_VALU_MFMA_MOPS_* x 512 flops): per kernel launch shape."""
+    import csv
+    from collections import defaultdict
+    rows = list(csv.DictReader(open(os.path.join(pmc_dir, "run_counter_collection.csv"))))
+    short = lambda n: n.replace("fa::(anonymous namespace)::", "").split("(fa::")[0][:60]
+    agg = defaultdict(lambda: defaultdict(list))
+    for r in rows:
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        agg[(short(r["Kernel_Name"]), int(r["Grid_Size"]))][r["Counter_Name"]].append(
+            (float(r["Counter_Value"]), d))
+    stem, title = TRACE_NAMES[workload]
+    lines = [f"# MFMA utilization of the constrained step ({title})", "",
+             "Command (from the repository root):", "", "```", command, "```", "",
+             "MfmaUtil is rocprofv3's derived counter (summed SQ_VALU_MFMA_BUSY_CYCLES over "
+             "GRBM_GUI_ACTIVE x SIMDs); the executed flops are SQ_INSTS_VALU_MFMA_MOPS_* x 512. "
+             "Durations are under the counter pass.", "",
+             "| kernel | grid threads | launches | MfmaUtil % | fp32 MFMA GFLOP | bf16 MFMA GFLOP | avg us | "
+             "fp32 TFLOP/s |", "|---|---|---|---|---|---|---|---|"]
+    mean = lambda xs: sum(x[0] for x in xs) / len(xs) if xs else 0.0
+    for (name, grid), c in sorted(agg.items(), key=lambda kv: -mean(kv[1].get(
+            "SQ_INSTS_VALU_MFMA_MOPS_F32", [])) - mean(kv[1].get("SQ_INSTS_VALU_MFMA_MOPS_BF16", []))):
+        mu = c.get("MfmaUtil", [])
+        f32 = mean(c.get("SQ_INSTS_VALU_MFMA_MOPS_F32", [])) * 512
+        bf = mean(c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", [])) * 512
+        if not mu or (f32 == 0 and bf == 0):
+            continue
+        us = sum(x[1] for x in mu) / len(mu)
+        lines.append(f"| `{name}` | {grid} | {len(mu)} | {mean(mu):.1f} | {f32 / 1e9:.3f} | {bf / 1e9:.3f} | "
+                     f"{us:.1f} | {f32 / (us * 1e6):.1f} |")
+    with open(os.path.join(ROOT, "profiles", f"mfma_{stem}.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,6 +279,8 @@ def main():
                     help="write profiles/traffic_*.json from two rocprofv3 --pmc passes, then exit")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="write the kernel-trace summary under profiles/ from a rocprofv3 run, then exit")
+    ap.add_argument("--summarize-mfma", metavar="DIR",
+                    help="write profiles/mfma_<workload>.md from a --pmc MfmaUtil pass and exit")
     ap.add_argument("--command", default="", help="the command recorded in a summary")
     args = ap.parse_args()
     if args.summarize_counters:
@@ -251,8 +289,11 @@ def main():
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.command, args.workload)
         return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma, args.command, args.workload)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(rows shard across GPUs with no communication; see the design notes)",
               file=sys.stderr)
         sys.exit(2)
