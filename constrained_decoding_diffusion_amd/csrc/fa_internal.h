@@ -23,6 +23,8 @@ constexpr int kSelMax = 8192;      // LIST tokens gathered through a compact cop
 constexpr int kMapMaxSp = 2048;   // dense (row, column) -> pair maps up to this Sp
 constexpr uint32_t kSelBit = 1u << 31;  // tokmask flag of LIST tokens (tables with < 32 dense pairs)
 constexpr int kRowChunk4 = 1024;   // float4 groups per chunk of a dense-pair token draw (4096 tokens)
+constexpr int kQParts = 4;         // workgroups per position of the streaming q writer
+constexpr int kTokChunksMax = 256;  // chunks per candidate list of one token draw
 
 enum PairClass : int32_t { kList = 0, kDense = 1, kRange = 2 };
 

@@ -323,7 +323,6 @@ __global__ __launch_bounds__(kRcutThreads) void marg_rcut(DevTable d, StepView s
 
 constexpr int kQThreads = 256;
 constexpr size_t kQLdsMax = 64 * 1024;  // LDS lookup tables of the streaming q writer
-constexpr int kQParts = 4;              // workgroups per position of the streaming q writer
 
 // LIST weight of selected token s: sum over its token-major entries
 __device__ inline float list_weight(const DevTable &d, int s, const float *al, const float *be)
@@ -1175,7 +1174,7 @@ bool marg_joint_ok(const DevTable &d, const Geometry &g, const float *p, const f
     // the token draws stream dense rows of at most kTokChunksMax chunks; the
     // q writer streams the row only when it writes q or sums q ln q
     return g.L > 0 && d.ndense > 0 && q_streamed(d, p, q, w) &&
-           (q != nullptr || conf_mode == FA_CONF_NEGENT) && w.tcs_nch <= 256;
+           (q != nullptr || conf_mode == FA_CONF_NEGENT) && w.tcs_nch <= kTokChunksMax;
 }
 
 int launch_marg_out(const DevTable &d, const Geometry &g, const float *p, const double *logZ,

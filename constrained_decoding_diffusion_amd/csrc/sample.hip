@@ -33,7 +33,6 @@ __global__ __launch_bounds__(kSubThreads) void sample_levels(
 }
 
 constexpr int kTokThreads = 256;
-constexpr int kTokChunksMax = 256;
 // a streamed chunk: four float4 groups per thread
 static_assert(4 * kTokThreads == kRowChunk4, "dense-pair chunk layout");
 

@@ -240,7 +240,7 @@ WsLayout ws_layout(const HostTable &t, const Geometry &g)
     w.pw_nl = t.nsel() <= kSelMax ? t.nsel() : 0;
     w.pw_ld = (kDenseMax + w.pw_nl + 3) & ~3;
     w.pw = o; o = al(o + BL * (size_t)w.pw_ld * sizeof(float));
-    w.hpart = o; o = al(o + BL * 4 * sizeof(double));  // the q writer's row parts
+    w.hpart = o; o = al(o + BL * kQParts * sizeof(double));  // the q writer's row parts
     size_t a4 = o;
     // sampler region, apart from the others: the joint call keeps the drawn
     // boundary states through the message pass, and the dense-pair chunk
