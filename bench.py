@@ -267,6 +267,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", type=int, default=3, help="preset 1..5 (default 3)")
+    ap.add_argument("--first-level", choices=["auto", "sparse", "dense"], default="auto",
+                    help="form of the first span level (default: the library's choice)")
     ap.add_argument("--separate", action="store_true",
                     help="fa_sample then fa_marginals instead of fa_sample_marginals")
     ap.add_argument("--gen-steps", type=int, default=16,
@@ -303,7 +305,7 @@ def main():
     from synth import configs
 
     w = configs.make(args.workload)
-    tb = fa.Table.from_automaton(w.aut)
+    tb = fa.Table.from_automaton(w.aut, first_level=args.first_level)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     p = torch.from_numpy(w.p).to(dev)
@@ -479,6 +481,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.describe(), "B": w.B, "L": w.L, "S": w.aut.S, "V": w.aut.V,
                    "calls": "separate" if args.separate else "joint",
+                   "first_level": "sparse" if tb.info["first_sparse"] else "dense",
                    "sequence_steps_per_s": w.B * 1000.0 / ms_per_step},
         "roofline": roof,
         "kernels": kernels,

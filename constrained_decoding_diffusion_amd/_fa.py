@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libfa.so")
 FA_OK, FA_EINVAL, FA_ENOTDET, FA_ETOOBIG, FA_EHIP, FA_ESTATE = range(6)
 FA_ROW_INFEASIBLE, FA_ROW_UNDERFLOW, FA_ROW_BADPROB = 1, 2, 4
 FA_DFA, FA_NFA, FA_LABEL_RANGES, FA_NO_TRIM = 1, 2, 4, 8
+FA_FIRST_LEVEL_SPARSE, FA_FIRST_LEVEL_DENSE = 16, 32
 FA_CONF_PROB, FA_CONF_NEGENT = 0, 1
 FA_PROF_NONE, FA_PROF_EMISSION_DENSE, FA_PROF_TREE_LEVEL1, FA_PROF_MARG_Q = range(4)
 
@@ -77,7 +78,8 @@ def _np_ptr(a: np.ndarray):
 
 
 INFO_KEYS = ["S", "Sp", "start", "n_accept", "pairs", "list_pairs", "dense_pairs", "range_pairs",
-             "list_entries", "segments", "cuts", "sel_tokens", "use_sel", "V", "S_orig"]
+             "list_entries", "segments", "cuts", "sel_tokens", "use_sel", "V", "S_orig",
+             "first_sparse", "first_work"]
 
 
 class Table:
@@ -106,9 +108,13 @@ class Table:
         self.orig = orig
 
     @classmethod
-    def from_automaton(cls, aut, flags=None):
+    def from_automaton(cls, aut, flags=None, first_level="auto"):
+        """first_level: "auto" (the library's choice), "sparse" (first span
+        level from the pair values) or "dense" (dense matrix products)."""
         if flags is None:
             flags = (FA_DFA if aut.dfa else FA_NFA) | (FA_LABEL_RANGES if aut.ranges else 0)
+        flags |= {"auto": 0, "sparse": FA_FIRST_LEVEL_SPARSE,
+                  "dense": FA_FIRST_LEVEL_DENSE}[first_level]
         return cls(aut.S, aut.V, aut.start, aut.accept, aut.src, aut.dst, aut.label_off,
                    aut.label_tok, flags)
 

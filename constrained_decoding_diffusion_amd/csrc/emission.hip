@@ -556,6 +556,7 @@ constexpr int kLeafPre = 4;      // leaf entries per thread loaded ahead
 __global__ __launch_bounds__(kLeafThreads) void emission_leaves(DevTable d, StepView sv, int rg,
                                                                 EmitSrc src, float *__restrict__ tree,
                                                                 int32_t *__restrict__ meta,
+                                                                float *__restrict__ pv,
                                                                 int32_t *__restrict__ status)
 {
     __shared__ __align__(16) float tile[kLeafTile];
@@ -601,24 +602,27 @@ __global__ __launch_bounds__(kLeafThreads) void emission_leaves(DevTable d, Step
     __syncthreads();
     if (real) {
         int bad = 0;
-        auto place = [&](int rc, float v) {
+        // with pv, the raw value also goes to its pair's slot (pair order)
+        float *pvrow = pv ? pv + pos * d.npairs : nullptr;
+        auto place = [&](int k, int rc, float v) {
             const int row = (rc >> 16) - r0, col = rc & 0xffff;
             tile[row * Sp + col] = v;
             if (v > 0.f) atomicMax(&remax[row], fexp(v));
+            if (pvrow) pvrow[tr ? d.col_pairs[k0 + k] : k0 + k] = v;
         };
 #pragma unroll
         for (int u = 0; u < kLeafPre; ++u) {
             if (tid + u * kLeafThreads < ne) {
                 const float v = pval[u];
                 if (pcode[u] >= 0 && !d.use_sel) bad |= !(v >= 0.f);
-                place(prc[u], v);
+                place(tid + u * kLeafThreads, prc[u], v);
             }
         }
         for (int k = tid + kLeafPre * kLeafThreads; k < ne; k += kLeafThreads) {
             const int code = esrc[k];
             const float v = code >= 0 ? direct[code] : indv[-1 - code];
             if (code >= 0 && !d.use_sel) bad |= !(v >= 0.f);
-            place(erc[k], v);
+            place(k, erc[k], v);
         }
         if (bad) atomicOr(&status[b], (int)FA_ROW_BADPROB);
     } else {  // identity leaf past the sequence end
@@ -704,7 +708,8 @@ int launch_build_transitions(const DevTable &d, const Geometry &g, const float *
         }
         const int rg = kLeafTile / g.Sp;
         dim3 grid((g.Sp + rg - 1) / rg, g.B * g.Lpad);
-        emission_leaves<<<grid, kLeafThreads, 0, st>>>(d, sv, rg, src, tree, meta, status);
+        float *pv = d.first_sparse ? (float *)(ws + w.val) : nullptr;
+        emission_leaves<<<grid, kLeafThreads, 0, st>>>(d, sv, rg, src, tree, meta, pv, status);
         return (int)hipGetLastError();
     }
     float *val = (float *)(ws + w.val);

@@ -14,6 +14,9 @@ namespace fa {
 constexpr int kSpAlign = 64;       // trimmed state count padded to this
 constexpr int kNeg = -(1 << 29);   // exponent of an all-zero row/column
 constexpr int kDenseMax = 32;      // dense-label pairs share one mask word per token
+// the first span level is formed from the pair values when its multiply-adds
+// are at most 1/kSparseFirstRatio of the dense product's S^3
+constexpr int kSparseFirstRatio = 256;
 constexpr int kLeafTile = 4096;    // floats of the LDS tile of the one-pass leaf writer
 constexpr int kDenseStepsMax = 64;  // dense-mask contraction: 256-token steps per V chunk, at most
 constexpr int kDenseSlots = 512;    // workgroups of that contraction resident at once (256 CUs x 2)
@@ -90,6 +93,7 @@ struct DevTable {
     const int32_t *ent_t_src;
     const int32_t *ind_pair;   // [n_ind] pairs whose value is computed (not one direct read)
     int32_t n_ind;
+    int32_t first_sparse;        // 1: the first span level is formed from the pair values
     const uint32_t *dense_bits;  // [ndense][dense_words] bit v%32 of word v/32: v in the label
     int32_t dense_words;
     const int32_t *ev_a;       // [2 nseg] per cut event (cut_ev order): the states of its pair
@@ -125,6 +129,8 @@ struct HostTable {
     bool has_cnt = false;
     bool use_sel = false;
     bool selbit = false;
+    bool first_sparse = false;  // first span level by row combination over the pairs
+    int64_t first_work = 0;     // its multiply-adds per product: pairs (a, k) times pairs (k, c)
     // device image
     std::vector<uint8_t> image;
     std::vector<size_t> offs;  // section offsets, in the order of DevTable pointers

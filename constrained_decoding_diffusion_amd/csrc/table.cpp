@@ -105,6 +105,7 @@ DevTable HostTable::device_view() const
     d.ncut = ncut();
     d.has_cnt = has_cnt ? 1 : 0;
     d.selbit = selbit ? 1 : 0;
+    d.first_sparse = first_sparse ? 1 : 0;
     const uint8_t *b = static_cast<const uint8_t *>(dev);
     size_t k = 0;
     auto nxt = [&](auto *&ptr) {
@@ -220,7 +221,9 @@ WsLayout ws_layout(const HostTable &t, const Geometry &g)
     w.dpart = o; o = al(o + (size_t)w.n_vchunks * BLpad * kDenseMax * sizeof(float));
     w.dval = o; o = al(o + (t.ndense() && !fused ? BL * kDenseMax * sizeof(float) : 0));
     w.cutp = o; o = al(o + BL * t.ncut() * sizeof(double));
-    w.val = o; o = al(o + (fused ? 0 : BL * t.npairs() * sizeof(float)));
+    // pair values in pair order: the dense leaf writer's input on the large
+    // path, and the sparse first span level's operands
+    w.val = o; o = al(o + (fused && !t.first_sparse ? 0 : BL * t.npairs() * sizeof(float)));
     size_t a1 = o;
     o = a0;  // span tree region
     size_t kp = 0;
@@ -266,7 +269,10 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
     if (S < 1 || V < 1 || start < 0 || start >= S || n_accept < 0 || E < 0) return FA_EINVAL;
     if ((n_accept > 0 && !accept) || (E > 0 && (!src || !dst || !label_off))) return FA_EINVAL;
     if ((flags & FA_DFA) && (flags & FA_NFA)) return FA_EINVAL;
-    if (flags & ~uint32_t(FA_DFA | FA_NFA | FA_LABEL_RANGES | FA_NO_TRIM)) return FA_EINVAL;
+    if (flags & ~uint32_t(FA_DFA | FA_NFA | FA_LABEL_RANGES | FA_NO_TRIM | FA_FIRST_LEVEL_SPARSE |
+                          FA_FIRST_LEVEL_DENSE))
+        return FA_EINVAL;
+    if ((flags & FA_FIRST_LEVEL_SPARSE) && (flags & FA_FIRST_LEVEL_DENSE)) return FA_EINVAL;
     if (E > std::numeric_limits<int32_t>::max()) return FA_ETOOBIG;
     if (E > 0 && label_off[0] != 0) return FA_EINVAL;
     for (int32_t k = 0; k < n_accept; ++k)
@@ -654,6 +660,14 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
             t.ent_t_src[k] = src_code(q);
         }
     }
+    // first span level: the sparse form costs one multiply-add per pair
+    // (a, k) and pair (k, c) of the two leaves, the dense one S^3
+    int64_t w1 = 0;
+    for (int32_t q = 0; q < np; ++q) w1 += t.row_ptr[t.pair_b[q] + 1] - t.row_ptr[t.pair_b[q]];
+    t.first_work = w1;
+    if (flags & FA_FIRST_LEVEL_SPARSE) t.first_sparse = true;
+    else if (flags & FA_FIRST_LEVEL_DENSE) t.first_sparse = false;
+    else t.first_sparse = (double)kSparseFirstRatio * (double)w1 <= (double)t.Sp * t.Sp * t.Sp;
     build_image(t);
     return FA_OK;
 }
@@ -700,10 +714,10 @@ extern "C" int fa_table_info(const fa_table *t, int64_t *info, int32_t n)
     const HostTable &h = t->h;
     int32_t nl = 0, nd = 0, nr = 0;
     for (int32_t c : h.pair_cls) (c == kList ? nl : c == kDense ? nd : nr)++;
-    int64_t v[15] = {h.S, h.Sp, h.start, (int64_t)h.acc.size(), h.npairs(), nl, nd, nr,
+    int64_t v[17] = {h.S, h.Sp, h.start, (int64_t)h.acc.size(), h.npairs(), nl, nd, nr,
                      (int64_t)h.list_tok.size(), h.nseg(), h.ncut(), h.nsel(), h.use_sel ? 1 : 0,
-                     h.V, h.S_orig};
-    for (int32_t k = 0; k < n && k < 15; ++k) info[k] = v[k];
+                     h.V, h.S_orig, h.first_sparse ? 1 : 0, h.first_work};
+    for (int32_t k = 0; k < n && k < 17; ++k) info[k] = v[k];
     return FA_OK;
 }
 

@@ -566,6 +566,181 @@ __global__ __launch_bounds__(kHugeThreads) void span_gemm256(StepView sv, float 
     if (tm == 0 && tid >= kHuge) coD[tn + tid - kHuge] = add_exp(roG[tn + tid - kHuge], rfG[tn + tid - kHuge]);
 }
 
+
+// First level from the pair values.  A leaf holds one value per pair (a, b)
+// of the automaton, so the first level's product is a row combination: the
+// stored row s of node n is the sum over the first operand's pairs (s, k) of
+// x1 times the second operand's row k, with both operands the folded
+// entries the dense kernels consume (raw pair value times 2^-rf of its
+// stored row; identity leaves past the sequence end hold their diagonal).
+// A node stored as is walks rows (pair order, row_ptr); a transposed node
+// walks columns (col_pairs order, col_ptr), which is its stored rows.  One
+// wave builds one output row in an LDS row buffer (a window of `win`
+// columns at a time); within one k the targets are distinct pairs, and one
+// wave's LDS accesses stay in program order, so the buffer needs no atomics
+// and the sum runs in a fixed order.  With STAGED the second operand's
+// adjacency and folded values sit in LDS.
+constexpr int kSpThreads = 512;
+constexpr int kSpWaves = kSpThreads / 64;
+constexpr int kSpRows = 256;   // output rows per workgroup
+constexpr int kSpWin = 512;    // columns of a wave's row buffer
+constexpr size_t kSpLdsMax = 64 * 1024;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <bool STAGED>
+__global__ __launch_bounds__(kSpThreads) void span_sparse1(DevTable d, StepView sv,
+                                                           const float *__restrict__ val,
+                                                           float *__restrict__ tree,
+                                                           int32_t *__restrict__ meta, int win)
+{
+    extern __shared__ __align__(16) float sm[];
+    const int Sp = sv.Sp, S = d.S, np = d.npairs;
+    const int nn = sv.Lpad >> 1;
+    const int rblocks = (Sp + kSpRows - 1) / kSpRows;
+    const int prod = blockIdx.x / rblocks, r0 = (blockIdx.x % rblocks) * kSpRows;
+    const int r1 = min(r0 + kSpRows, Sp);
+    const int b = prod / nn, n = nn + prod % nn;
+    const bool tr = stored_transposed(n);
+    const int hF = tr ? 2 * n + 1 : 2 * n, hG = tr ? 2 * n : 2 * n + 1;
+    const int iF = hF - sv.Lpad, iG = hG - sv.Lpad;
+    const bool realF = iF < sv.L, realG = iG < sv.L;
+    const float *vF = val + ((size_t)b * sv.L + (realF ? iF : 0)) * np;
+    const float *vG = val + ((size_t)b * sv.L + (realG ? iG : 0)) * np;
+    const int32_t *ptr = tr ? d.col_ptr : d.row_ptr;
+    const int32_t *perm = tr ? d.col_pairs : nullptr;
+    const int32_t *far = tr ? d.pair_a : d.pair_b;
+    const int32_t *roF = sv.meta_ptr((const int32_t *)meta, b, hF, 0);
+    const int32_t *rfF = sv.meta_ptr((const int32_t *)meta, b, hF, 2);
+    const int32_t *roG = sv.meta_ptr((const int32_t *)meta, b, hG, 0);
+    const int32_t *rfG = sv.meta_ptr((const int32_t *)meta, b, hG, 2);
+    float *D = sv.mat_ptr(tree, b, n);
+    int32_t *roD = sv.meta_ptr(meta, b, n, 0);
+    int32_t *coD = sv.meta_ptr(meta, b, n, 1);
+    int32_t *rfD = sv.meta_ptr(meta, b, n, 2);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    float *buf = sm + wave * win;
+    int32_t *sptr = reinterpret_cast<int32_t *>(sm + kSpWaves * win);
+    float *sx = reinterpret_cast<float *>(sptr + ((S + 4) & ~3));
+    uint16_t *stt = reinterpret_cast<uint16_t *>(sx + np);
+    if (STAGED && realG) {
+        for (int k = tid; k <= S; k += kSpThreads) sptr[k] = ptr[k];
+        for (int e = tid; e < np; e += kSpThreads) {
+            const int q = perm ? perm[e] : e;
+            const int t = far[q];
+            sx[e] = ldexpf(vG[q], 0 - rfG[t]);
+            stt[e] = (uint16_t)t;
+        }
+        __syncthreads();
+    }
+    if (r0 == 0)
+        for (int t = tid; t < Sp; t += kSpThreads) coD[t] = add_exp(roG[t], rfG[t]);
+    for (int s = r0 + wave; s < r1; s += kSpWaves) {
+        const int rfs = rfF[s];
+        int e0 = 0, e1 = 0;
+        if (s < S) {
+            e0 = realF ? ptr[s] : 0;
+            e1 = realF ? ptr[s + 1] : 1;
+        }
+        int emax = kNeg;
+        for (int w0 = 0; w0 < Sp; w0 += win) {
+            const int wn = min(win, Sp - w0);
+            for (int c = lane * 4; c < wn; c += 256) *reinterpret_cast<f32x4 *>(&buf[c]) = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int eb = e0; eb < e1; eb += 64) {
+                const int cnt = min(64, e1 - eb);
+                // lane j: the first operand's entry eb + j of row s, its
+                // target k and the second operand's entries of row k
+                int kj = 0, loj = 0, hij = 0;
+                float xj = 0.f;
+                if (lane < cnt) {
+                    if (realF) {
+                        const int q = perm ? perm[eb + lane] : eb + lane;
+                        kj = far[q];
+                        xj = ldexpf(vF[q], 0 - rfs);
+                    } else {
+                        kj = s;
+                        xj = ldexpf(1.f, 0 - rfs);
+                    }
+                    if (realG) {
+                        loj = STAGED ? sptr[kj] : ptr[kj];
+                        hij = STAGED ? sptr[kj + 1] : ptr[kj + 1];
+                    } else {
+                        loj = 0;
+                        hij = 1;
+                    }
+                }
+                for (int j = 0; j < cnt; ++j) {
+                    const int k = __builtin_amdgcn_readlane(kj, j);
+                    const float x1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xj), j));
+                    const int lo = __builtin_amdgcn_readlane(loj, j);
+                    const int hi = __builtin_amdgcn_readlane(hij, j);
+                    for (int e = lo + lane; e < hi; e += 64) {
+                        int t;
+                        float x2;
+                        if (!realG) {
+                            t = k;
+                            x2 = ldexpf(1.f, 0 - rfG[k]);
+                        } else if (STAGED) {
+                            t = stt[e];
+                            x2 = sx[e];
+                        } else {
+                            const int q = perm ? perm[e] : e;
+                            t = far[q];
+                            x2 = ldexpf(vG[q], 0 - rfG[t]);
+                        }
+                        const int c = t - w0;
+                        if ((unsigned)c < (unsigned)wn) buf[c] = fmaf(x1, x2, buf[c]);
+                    }
+                }
+            }
+            float *Drow = D + (size_t)s * Sp + w0;
+            for (int c = lane * 4; c < wn; c += 256) {
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(&buf[c]);
+                __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(&Drow[c]));
+                const int4 ro = *reinterpret_cast<const int4 *>(roG + w0 + c);
+                const int4 rf = *reinterpret_cast<const int4 *>(rfG + w0 + c);
+                const int co[4] = {add_exp(ro.x, rf.x), add_exp(ro.y, rf.y), add_exp(ro.z, rf.z),
+                                   add_exp(ro.w, rf.w)};
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (v[u] > 0.f && co[u] > kNeg) emax = max(emax, fexp(v[u]) + co[u]);
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) emax = max(emax, __shfl_xor(emax, o));
+        if (lane == 0) {
+            rfD[s] = emax;
+            roD[s] = add_exp(roF[s], rfF[s]);
+        }
+    }
+}
+
+// LDS bytes of span_sparse1: the row buffers, and with staging the second
+// operand's row pointers, folded values and 16-bit targets
+size_t sparse1_lds(const DevTable &d, int win, bool staged)
+{
+    size_t b = (size_t)kSpWaves * win * sizeof(float);
+    if (staged)
+        b += (size_t)((d.S + 4) & ~3) * sizeof(int32_t) + (size_t)d.npairs * sizeof(float) +
+             (((size_t)d.npairs * sizeof(uint16_t) + 15) & ~size_t(15));
+    return b;
+}
+
+int launch_sparse1(const DevTable &d, const Geometry &g, StepView sv, const float *val, float *tree,
+                   int32_t *meta, hipStream_t st)
+{
+    const int win = std::min(g.Sp, kSpWin);
+    const bool staged = g.Sp <= 65536 && sparse1_lds(d, win, true) <= kSpLdsMax;
+    const size_t lds = sparse1_lds(d, win, staged);
+    const long long grid = (long long)g.B * (g.Lpad >> 1) * ((g.Sp + kSpRows - 1) / kSpRows);
+    if (grid > 0x7fffffffLL) return (int)hipErrorInvalidConfiguration;
+    if (staged)
+        span_sparse1<true><<<(unsigned)grid, kSpThreads, lds, st>>>(d, sv, val, tree, meta, win);
+    else
+        span_sparse1<false><<<(unsigned)grid, kSpThreads, lds, st>>>(d, sv, val, tree, meta, win);
+    return (int)hipGetLastError();
+}
+
 }  // namespace
 
 int launch_span_tree(const DevTable &d, const Geometry &g, float *tree, int32_t *meta,
@@ -596,7 +771,10 @@ int launch_span_tree(const DevTable &d, const Geometry &g, float *tree, int32_t 
         }
         const int huge_tiles = g.Sp / kHuge;
         const long long huge_wgs = (long long)g.B * nn * huge_tiles * huge_tiles;
-        if (ks == 1 && g.Sp % kHuge == 0 && huge_wgs >= 256) {
+        if (k == 1 && d.first_sparse) {
+            const int se = launch_sparse1(d, g, sv, (const float *)(ws + w.val), tree, meta, st);
+            if (se) return se;
+        } else if (ks == 1 && g.Sp % kHuge == 0 && huge_wgs >= 256) {
             span_gemm256<<<(unsigned)huge_wgs, kHugeThreads, 0, st>>>(sv, tree, meta, n0, nn);
         } else if (ks == 1 && g.Sp % kBig == 0 && big_wgs >= 256) {
             span_gemm128<<<(unsigned)big_wgs, kBigThreads, 0, st>>>(sv, tree, meta, n0, nn);

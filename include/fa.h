@@ -79,7 +79,9 @@ enum {
     FA_DFA = 1,          /* check determinism */
     FA_NFA = 2,          /* strings weighted by their number of accepting paths */
     FA_LABEL_RANGES = 4, /* label_tok holds flat half-open [lo, hi) pairs */
-    FA_NO_TRIM = 8       /* keep states unreachable from s0 or unable to reach F */
+    FA_NO_TRIM = 8,      /* keep states unreachable from s0 or unable to reach F */
+    FA_FIRST_LEVEL_SPARSE = 16, /* first span level from the pair values (row combination) */
+    FA_FIRST_LEVEL_DENSE = 32   /* first span level as dense matrix products */
 };
 
 enum { FA_CONF_PROB = 0, FA_CONF_NEGENT = 1 };
@@ -97,7 +99,10 @@ enum { FA_CONF_PROB = 0, FA_CONF_NEGENT = 1 };
  *   label_tok       token ids in [0, V) (a label is a set: repeats count
  *                   once), or with FA_LABEL_RANGES flat [lo, hi) pairs with
  *                   0 <= lo <= hi <= V, disjoint within one edge
- *   flags           FA_DFA | FA_NFA | FA_LABEL_RANGES | FA_NO_TRIM
+ *   flags           FA_DFA | FA_NFA | FA_LABEL_RANGES | FA_NO_TRIM, and at
+ *                   most one of FA_FIRST_LEVEL_SPARSE / FA_FIRST_LEVEL_DENSE
+ *                   (how fa_span_tree forms the first level; default: the
+ *                   sparse form when its work is at most 1/256 of S^3)
  *   out             receives the handle (free with fa_table_destroy)
  *   device_bytes    receives the size of the device image
  * Dead states (unreachable from s0 or unable to reach F) are removed unless
@@ -127,7 +132,9 @@ void fa_table_destroy(fa_table *t);
  * kept, [4] pairs, [5] LIST pairs, [6] DENSE pairs, [7] RANGE pairs,
  * [8] LIST entries, [9] range segments, [10] cut points, [11] sel tokens,
  * [12] 1 if LIST entries index the selected-token gather, [13] V,
- * [14] S (original).  Returns FA_OK or FA_EINVAL.
+ * [14] S (original), [15] 1 if fa_span_tree forms the first level from the
+ * pair values, [16] that form's multiply-adds per first-level product (the
+ * number of pairs (a, k), (k, c) sharing k).  Returns FA_OK or FA_EINVAL.
  */
 int fa_table_info(const fa_table *t, int64_t *info, int32_t n);
 
@@ -180,7 +187,13 @@ int fa_build_transitions(const fa_table *t, const float *p, int32_t B, int32_t L
  *   tree, meta  written by fa_build_transitions; internal nodes written
  *   ws          device workspace of ws_bytes >= fa_sizes (partial products
  *               of the upper levels, whose few large products are split
- *               along K)
+ *               along K).  When the table computes the first level from
+ *               the pair values (FA_FIRST_LEVEL_SPARSE, or chosen at compile
+ *               time when the products' sparse work is at most 1/256 of
+ *               the dense S^3), ws must hold what this step's
+ *               fa_build_transitions wrote; the level is then a sum over
+ *               pairs (a, k), (k, c) of the two leaves instead of a dense
+ *               product, the same fp32 folded operands in another order.
  *   logZ        device double [B]; -inf for infeasible rows
  *   row_status  device int32 [B]; FA_ROW_INFEASIBLE when Z = 0
  * Errors: FA_EINVAL, FA_ESTATE, FA_EHIP.

@@ -1,0 +1,93 @@
+"""GPU parity of the sparse first span level: the level-1 products formed
+from the pair values (row combination over pairs (a, k), (k, c)) instead of
+dense matrix products.  Every workload of the step parity suite runs with the
+sparse form forced; the whole step is checked against the fp64 oracle, and
+the level-1 nodes against the oracle's products M_2j M_2j+1."""
+import numpy as np
+import pytest
+
+import oracle
+from tests import parity as PT
+from tests.test_gpu_parity import CASES
+
+pytestmark = pytest.mark.gpu
+
+NODE_RTOL = 3e-5
+
+
+def _node(w, g, b, n):
+    """Level-1 node n of row b as the true span matrix over compact states."""
+    import torch
+    tb = g["table"]
+    Sp, S = tb.info["Sp"], tb.info["S"]
+    Lpad = 1 << max(0, (w.L - 1).bit_length())
+    tree = g["bufs"].tree.view(w.B, 2 * Lpad, Sp, Sp)
+    meta = g["bufs"].meta[: w.B * 2 * Lpad * 3 * Sp].view(w.B, 2 * Lpad, 3, Sp)
+    D = tree[b, n].cpu().numpy().astype(np.float64)
+    ro = meta[b, n, 0].cpu().numpy().astype(np.float64)
+    co = meta[b, n, 1].cpu().numpy().astype(np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        T = D * np.exp2(ro)[:, None] * np.exp2(co)[None, :]
+    T[D == 0] = 0.0
+    if n % 2 == 1 and n >= 3:
+        T = T.T
+    del torch
+    return T[:S, :S]
+
+
+def _check_level1(w, g, b, orc):
+    tb = g["table"]
+    orig = tb.orig
+    S = len(orig)
+    Lpad = 1 << max(0, (w.L - 1).bit_length())
+    if Lpad < 2:
+        return
+    W = orc.edge_weights(w.p[b])
+
+    def M(i):
+        if i >= w.L:
+            return np.eye(S)
+        return orc.dense_M(W, i)[np.ix_(orig, orig)]
+
+    for j in range(Lpad // 2):
+        want = M(2 * j) @ M(2 * j + 1)
+        got = _node(w, g, b, Lpad // 2 + j)
+        scale = want.max(axis=1, keepdims=True)
+        err = np.abs(got - want)
+        bad = err > NODE_RTOL * want + 1e-30 * scale
+        assert not bad.any(), (f"row {b} node {Lpad // 2 + j}: {bad.sum()} entries off, worst "
+                               f"rel {np.max(err / np.maximum(want, 1e-300))}")
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_sparse_first_level_parity(name):
+    import constrained_decoding_diffusion_amd as fa
+    w = CASES[name]()
+    tb = fa.Table.from_automaton(w.aut, first_level="sparse")
+    assert tb.info["first_sparse"] == 1
+    PT.log(f"[first-level] {name}: {w.describe()}, first-level work {tb.info['first_work']}")
+    g = PT.run_gpu(w, table=tb)
+    orc = oracle.Oracle(w.aut)
+    for b in range(w.B):
+        PT.check_row(w, g, b, orc)
+    _check_level1(w, g, 0, orc)
+    if w.B > 1:
+        _check_level1(w, g, w.B - 1, orc)
+    PT.log(f"[first-level] {name}: ok")
+
+
+@pytest.mark.parametrize("name", ["json-small", "random-dfa-L3", "nfa-small"])
+def test_sparse_and_dense_first_level_agree(name):
+    """Both forms of the first level give the same draws where no uniform
+    sits near a boundary, and log Z within the parity tolerance."""
+    import constrained_decoding_diffusion_amd as fa
+    w = CASES[name]()
+    gs = PT.run_gpu(w, table=fa.Table.from_automaton(w.aut, first_level="sparse"))
+    gd = PT.run_gpu(w, table=fa.Table.from_automaton(w.aut, first_level="dense"))
+    assert gd["table"].info["first_sparse"] == 0
+    np.testing.assert_allclose(gs["logZ"], gd["logZ"], rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(gs["q"], gd["q"], rtol=2e-4, atol=1e-10)
+    # a draw may differ only where its uniform lies within the fp32 noise
+    # of a boundary; the oracle replay in the parity test bounds those
+    same = (gs["tokens"] == gd["tokens"]).mean()
+    assert same > 0.99, same
