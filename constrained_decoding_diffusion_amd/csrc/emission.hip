@@ -602,27 +602,24 @@ __global__ __launch_bounds__(kLeafThreads) void emission_leaves(DevTable d, Step
     __syncthreads();
     if (real) {
         int bad = 0;
-        // with pv, the raw value also goes to its pair's slot (pair order)
-        float *pvrow = pv ? pv + pos * d.npairs : nullptr;
-        auto place = [&](int k, int rc, float v) {
+        auto place = [&](int rc, float v) {
             const int row = (rc >> 16) - r0, col = rc & 0xffff;
             tile[row * Sp + col] = v;
             if (v > 0.f) atomicMax(&remax[row], fexp(v));
-            if (pvrow) pvrow[tr ? d.col_pairs[k0 + k] : k0 + k] = v;
         };
 #pragma unroll
         for (int u = 0; u < kLeafPre; ++u) {
             if (tid + u * kLeafThreads < ne) {
                 const float v = pval[u];
                 if (pcode[u] >= 0 && !d.use_sel) bad |= !(v >= 0.f);
-                place(tid + u * kLeafThreads, prc[u], v);
+                place(prc[u], v);
             }
         }
         for (int k = tid + kLeafPre * kLeafThreads; k < ne; k += kLeafThreads) {
             const int code = esrc[k];
             const float v = code >= 0 ? direct[code] : indv[-1 - code];
             if (code >= 0 && !d.use_sel) bad |= !(v >= 0.f);
-            place(k, erc[k], v);
+            place(erc[k], v);
         }
         if (bad) atomicOr(&status[b], (int)FA_ROW_BADPROB);
     } else {  // identity leaf past the sequence end
@@ -633,6 +630,16 @@ __global__ __launch_bounds__(kLeafThreads) void emission_leaves(DevTable d, Step
             }
     }
     __syncthreads();
+    if (pv && real) {
+        // the folded entries (value times 2^-rf of its stored row) in the
+        // leaf's stored entry order, for the sparse first span level
+        float *pvrow = pv + pos * d.npairs + k0;
+        for (int k = tid; k < ne; k += kLeafThreads) {
+            const int rc = erc[k];
+            const int row = (rc >> 16) - r0, col = rc & 0xffff;
+            pvrow[k] = ldexpf(tile[row * Sp + col], 0 - remax[row]);
+        }
+    }
     float4 *M4 = reinterpret_cast<float4 *>(sv.mat_ptr(tree, b, h) + (size_t)r0 * Sp);
     for (int k = tid; k < n4; k += kLeafThreads) M4[k] = tile4[k];
     int32_t *ro = sv.meta_ptr(meta, b, h, 0), *co = sv.meta_ptr(meta, b, h, 1);
@@ -642,6 +649,25 @@ __global__ __launch_bounds__(kLeafThreads) void emission_leaves(DevTable d, Step
         ro[r0 + r] = 0;
         co[r0 + r] = 0;
     }
+}
+
+// Folded entries of every leaf for the sparse first span level, on the path
+// whose leaves are densified from pair-order values: in the leaf's stored
+// entry order (pair order, or column order for a transposed leaf), each
+// value times 2^-rf of its stored row, as the dense kernels consume it.
+__global__ void emission_fold_pairs(DevTable d, StepView sv, const float *__restrict__ val,
+                                    const int32_t *__restrict__ meta, float *__restrict__ pvf)
+{
+    const int e = blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t pos = blockIdx.y;
+    if (e >= d.npairs) return;
+    const int b = (int)(pos / sv.L), i = (int)(pos % sv.L);
+    const int h = sv.Lpad + i;
+    const bool tr = stored_transposed(h);
+    const int q = tr ? d.col_pairs[e] : e;
+    const int row = tr ? d.pair_b[q] : d.pair_a[q];
+    const int32_t *rf = sv.meta_ptr(meta, b, h, 2);
+    pvf[pos * d.npairs + e] = ldexpf(val[pos * d.npairs + q], 0 - rf[row]);
 }
 
 }  // namespace
@@ -708,7 +734,7 @@ int launch_build_transitions(const DevTable &d, const Geometry &g, const float *
         }
         const int rg = kLeafTile / g.Sp;
         dim3 grid((g.Sp + rg - 1) / rg, g.B * g.Lpad);
-        float *pv = d.first_sparse ? (float *)(ws + w.val) : nullptr;
+        float *pv = d.first_sparse ? (float *)(ws + w.pvf) : nullptr;
         emission_leaves<<<grid, kLeafThreads, 0, st>>>(d, sv, rg, src, tree, meta, pv, status);
         return (int)hipGetLastError();
     }
@@ -725,6 +751,12 @@ int launch_build_transitions(const DevTable &d, const Geometry &g, const float *
     } else {
         dim3 grid((g.Sp + 4 * kRowsPerWave - 1) / (4 * kRowsPerWave), g.B * g.Lpad);
         emission_densify<<<grid, kDensifyThreads, 0, st>>>(d, sv, val, tree, meta);
+    }
+    if (d.first_sparse && d.npairs > 0 && npos > 0) {
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return (int)e;
+        dim3 fgrid((d.npairs + 255) / 256, npos);
+        emission_fold_pairs<<<fgrid, 256, 0, st>>>(d, sv, val, meta, (float *)(ws + w.pvf));
     }
     return (int)hipGetLastError();
 }

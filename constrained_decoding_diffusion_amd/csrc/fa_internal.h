@@ -17,6 +17,11 @@ constexpr int kDenseMax = 32;      // dense-label pairs share one mask word per 
 // the first span level is formed from the pair values when its multiply-adds
 // are at most 1/kSparseFirstRatio of the dense product's S^3
 constexpr int kSparseFirstRatio = 256;
+// LDS of one workgroup of the sparse first level (gfx950: 160 KB per CU);
+// it holds the product's column exponents and the row pointers, which
+// bounds the states the sparse form takes
+constexpr size_t kSparseLdsMax = 160 * 1024;
+constexpr int kSparseFirstMaxS = 16384;
 constexpr int kLeafTile = 4096;    // floats of the LDS tile of the one-pass leaf writer
 constexpr int kDenseStepsMax = 64;  // dense-mask contraction: 256-token steps per V chunk, at most
 constexpr int kDenseSlots = 512;    // workgroups of that contraction resident at once (256 CUs x 2)
@@ -101,6 +106,7 @@ struct DevTable {
     const float *ev_w;         // [2 nseg] its count, negative at a segment end
     const uint32_t *cutbits;   // [(V+31)/32] bit v%32 of word v/32: a cut point at token v < V
     const int32_t *sel_lb;     // [V/256 + 2] first sel_tok index at or after token 256 t
+    const int32_t *pair_colpos;  // [npairs] position of each pair in col_pairs
     int32_t n_tm;              // token-major LIST entries
 };
 
@@ -126,6 +132,7 @@ struct HostTable {
     std::vector<float> ev_w;
     std::vector<uint32_t> cutbits;
     std::vector<int32_t> sel_lb;
+    std::vector<int32_t> pair_colpos;
     bool has_cnt = false;
     bool use_sel = false;
     bool selbit = false;
@@ -159,6 +166,7 @@ bool make_geometry(const HostTable &t, int32_t B, int32_t L, Geometry *g);
 // Workspace layout (bytes from the start of ws), sized for the largest user.
 struct WsLayout {
     size_t dpart = 0, dval = 0, psel = 0, cutp = 0, val = 0;  // emission reduce
+    size_t pvf = 0;                            // folded leaf pair values (sparse first level)
     int32_t n_vchunks = 0;                     // dense-mask contraction: V split
     int32_t vchunk = 0;                        // tokens per V chunk (multiple of 256)
     int32_t sel_mode = 0;                      // token-list copy: 1 LDS-buffered, 2 gathered

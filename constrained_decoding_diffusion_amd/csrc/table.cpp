@@ -84,6 +84,7 @@ void build_image(HostTable &t)
     append_section(t.image, t.offs, t.ev_b);
     append_section(t.image, t.offs, t.ev_w);
     append_section(t.image, t.offs, t.cutbits);
+    append_section(t.image, t.offs, t.pair_colpos);
     t.image.resize((t.image.size() + 255) & ~size_t(255));
 }
 
@@ -127,6 +128,7 @@ DevTable HostTable::device_view() const
     nxt(d.ev_b);
     nxt(d.ev_w);
     nxt(d.cutbits);
+    nxt(d.pair_colpos);
     d.n_tm = (int32_t)tm_pair.size();
     if (map_n.empty()) {
         d.map_n = nullptr;
@@ -221,9 +223,10 @@ WsLayout ws_layout(const HostTable &t, const Geometry &g)
     w.dpart = o; o = al(o + (size_t)w.n_vchunks * BLpad * kDenseMax * sizeof(float));
     w.dval = o; o = al(o + (t.ndense() && !fused ? BL * kDenseMax * sizeof(float) : 0));
     w.cutp = o; o = al(o + BL * t.ncut() * sizeof(double));
-    // pair values in pair order: the dense leaf writer's input on the large
-    // path, and the sparse first span level's operands
-    w.val = o; o = al(o + (fused && !t.first_sparse ? 0 : BL * t.npairs() * sizeof(float)));
+    w.val = o; o = al(o + (fused ? 0 : BL * t.npairs() * sizeof(float)));
+    // the sparse first span level's operands: folded pair values of every
+    // leaf in its stored order (pair order, or column order when transposed)
+    w.pvf = o; o = al(o + (t.first_sparse ? BL * t.npairs() * sizeof(float) : 0));
     size_t a1 = o;
     o = a0;  // span tree region
     size_t kp = 0;
@@ -520,6 +523,8 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
     std::stable_sort(t.col_pairs.begin(), t.col_pairs.end(), [&](int32_t x, int32_t y) {
         return t.pair_b[x] != t.pair_b[y] ? t.pair_b[x] < t.pair_b[y] : t.pair_a[x] < t.pair_a[y];
     });
+    t.pair_colpos.resize(np);
+    for (int32_t k = 0; k < np; ++k) t.pair_colpos[t.col_pairs[k]] = k;
     // token-major inverse of the LIST pairs
     t.sel_tok = t.list_tok;
     std::sort(t.sel_tok.begin(), t.sel_tok.end());
@@ -665,9 +670,15 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
     int64_t w1 = 0;
     for (int32_t q = 0; q < np; ++q) w1 += t.row_ptr[t.pair_b[q] + 1] - t.row_ptr[t.pair_b[q]];
     t.first_work = w1;
-    if (flags & FA_FIRST_LEVEL_SPARSE) t.first_sparse = true;
-    else if (flags & FA_FIRST_LEVEL_DENSE) t.first_sparse = false;
-    else t.first_sparse = (double)kSparseFirstRatio * (double)w1 <= (double)t.Sp * t.Sp * t.Sp;
+    if (flags & FA_FIRST_LEVEL_SPARSE) {
+        if (t.S > kSparseFirstMaxS) return FA_ETOOBIG;
+        t.first_sparse = true;
+    } else if (flags & FA_FIRST_LEVEL_DENSE) {
+        t.first_sparse = false;
+    } else {
+        t.first_sparse = t.S <= kSparseFirstMaxS &&
+                         (double)kSparseFirstRatio * (double)w1 <= (double)t.Sp * t.Sp * t.Sp;
+    }
     build_image(t);
     return FA_OK;
 }

@@ -568,34 +568,49 @@ __global__ __launch_bounds__(kHugeThreads) void span_gemm256(StepView sv, float 
 
 
 // First level from the pair values.  A leaf holds one value per pair (a, b)
-// of the automaton, so the first level's product is a row combination: the
-// stored row s of node n is the sum over the first operand's pairs (s, k) of
-// x1 times the second operand's row k, with both operands the folded
-// entries the dense kernels consume (raw pair value times 2^-rf of its
-// stored row; identity leaves past the sequence end hold their diagonal).
-// A node stored as is walks rows (pair order, row_ptr); a transposed node
-// walks columns (col_pairs order, col_ptr), which is its stored rows.  One
-// wave builds one output row in an LDS row buffer (a window of `win`
-// columns at a time); within one k the targets are distinct pairs, and one
-// wave's LDS accesses stay in program order, so the buffer needs no atomics
-// and the sum runs in a fixed order.  With STAGED the second operand's
-// adjacency and folded values sit in LDS.
+// of the automaton, so a first-level product is a row combination: stored
+// row s of node n is the sum over the first operand's pairs (s, k) of x1
+// times the second operand's row k, where both operands are the folded
+// entries the dense kernels consume (value times 2^-rf of its stored row,
+// written by the leaf writer in each leaf's stored entry order; identity
+// leaves past the sequence end hold their diagonal).  A node stored as is
+// walks rows (pair order, row_ptr); a transposed node walks columns
+// (col_pairs order, col_ptr), which are its stored rows.  Both operands use
+// the same walk, so the first operand's entry e has the second operand's
+// target array entry e as its k.
+//
+// One wave builds one output row, a window of `win` columns at a time, in
+// two LDS row buffers.  The row's work is cut into tasks of at most 32
+// items (one k, a slice of its row), numbered by a prefix sum over the
+// entries; lane group g (32 lanes) runs tasks g, g + 2, ... into buffer g,
+// one item per lane, both groups in lockstep.  Within one task the targets
+// are distinct pairs and one wave's LDS accesses stay in program order, so
+// the buffers need no atomics; the row is buffer 0 + buffer 1, each summed
+// in task order, so the result does not depend on timing.  The task two
+// steps ahead and the next item are read before the current item's buffer
+// update, and the next row's first-operand values are loaded while the
+// current row is built.  The column exponents of the product and the
+// walk's row pointers sit in LDS; with STAGED also the second operand's
+// targets and folded values.
 constexpr int kSpThreads = 512;
 constexpr int kSpWaves = kSpThreads / 64;
 constexpr int kSpRows = 256;   // output rows per workgroup
-constexpr int kSpWin = 512;    // columns of a wave's row buffer
-constexpr size_t kSpLdsMax = 64 * 1024;
+constexpr int kSpEnt = 64;     // first-operand entries per chunk (one per lane)
+constexpr int kSpTasks = 128;  // tasks per wave per pass (64 when the operand is not staged)
+constexpr int kSpTaskPad = 8;  // empty tasks after a pass's last one
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <bool STAGED>
+template <bool STAGED, bool ONEWIN>
 __global__ __launch_bounds__(kSpThreads) void span_sparse1(DevTable d, StepView sv,
-                                                           const float *__restrict__ val,
+                                                           const float *__restrict__ pvf,
                                                            float *__restrict__ tree,
-                                                           int32_t *__restrict__ meta, int win)
+                                                           int32_t *__restrict__ meta, int win,
+                                                           int tcap)
 {
     extern __shared__ __align__(16) float sm[];
     const int Sp = sv.Sp, S = d.S, np = d.npairs;
+    if (np <= 0) return;   // the launcher takes tables with pairs only
     const int nn = sv.Lpad >> 1;
     const int rblocks = (Sp + kSpRows - 1) / kSpRows;
     const int prod = blockIdx.x / rblocks, r0 = (blockIdx.x % rblocks) * kSpRows;
@@ -605,139 +620,261 @@ __global__ __launch_bounds__(kSpThreads) void span_sparse1(DevTable d, StepView 
     const int hF = tr ? 2 * n + 1 : 2 * n, hG = tr ? 2 * n : 2 * n + 1;
     const int iF = hF - sv.Lpad, iG = hG - sv.Lpad;
     const bool realF = iF < sv.L, realG = iG < sv.L;
-    const float *vF = val + ((size_t)b * sv.L + (realF ? iF : 0)) * np;
-    const float *vG = val + ((size_t)b * sv.L + (realG ? iG : 0)) * np;
-    const int32_t *ptr = tr ? d.col_ptr : d.row_ptr;
-    const int32_t *perm = tr ? d.col_pairs : nullptr;
-    const int32_t *far = tr ? d.pair_a : d.pair_b;
     const int32_t *roF = sv.meta_ptr((const int32_t *)meta, b, hF, 0);
     const int32_t *rfF = sv.meta_ptr((const int32_t *)meta, b, hF, 2);
     const int32_t *roG = sv.meta_ptr((const int32_t *)meta, b, hG, 0);
     const int32_t *rfG = sv.meta_ptr((const int32_t *)meta, b, hG, 2);
+    // both leaves' entries are in their stored order: the first operand's
+    // is its walk order; the second's is the other one
+    const float *vF = pvf + ((size_t)b * sv.L + (realF ? iF : 0)) * np;
+    const float *vG = pvf + ((size_t)b * sv.L + (realG ? iG : 0)) * np;
+    const int32_t *ptr = tr ? d.col_ptr : d.row_ptr;
+    const int32_t *far = tr ? d.pair_a : d.pair_b;
+    const int32_t *perm = tr ? d.col_pairs : d.pair_colpos;
+    const int npc = np - 1;
     float *D = sv.mat_ptr(tree, b, n);
     int32_t *roD = sv.meta_ptr(meta, b, n, 0);
     int32_t *coD = sv.meta_ptr(meta, b, n, 1);
     int32_t *rfD = sv.meta_ptr(meta, b, n, 2);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    float *buf = sm + wave * win;
-    int32_t *sptr = reinterpret_cast<int32_t *>(sm + kSpWaves * win);
+    const int grp = lane >> 5, sub = lane & 31;
+    float *bufw = sm + wave * 2 * win;           // this wave's two row buffers
+    float *bufg = bufw + grp * win;              // this lane group's buffer
+    int4 *task = reinterpret_cast<int4 *>(sm + kSpWaves * 2 * win) + wave * (tcap + kSpTaskPad);
+    int32_t *sco = reinterpret_cast<int32_t *>(sm + kSpWaves * (2 * win + 4 * (tcap + kSpTaskPad)));
+    int32_t *sptr = sco + Sp;
     float *sx = reinterpret_cast<float *>(sptr + ((S + 4) & ~3));
     uint16_t *stt = reinterpret_cast<uint16_t *>(sx + np);
-    if (STAGED && realG) {
-        for (int k = tid; k <= S; k += kSpThreads) sptr[k] = ptr[k];
-        for (int e = tid; e < np; e += kSpThreads) {
-            const int q = perm ? perm[e] : e;
-            const int t = far[q];
-            sx[e] = ldexpf(vG[q], 0 - rfG[t]);
-            stt[e] = (uint16_t)t;
+
+    // second operand entry e of the walk: target and folded value
+    auto g_entry = [&](int e, int &t, float &x2) {
+        if (STAGED) {
+            t = stt[e];
+            x2 = sx[e];
+        } else {
+            const int q = tr ? perm[e] : e;     // pair id
+            t = far[tr ? q : e];
+            x2 = vG[tr ? q : perm[e]];
         }
-        __syncthreads();
+    };
+    // item index: staged reads of an empty task's items stay inside the LDS
+    // block (unused); memory reads are clamped into the arrays
+    auto item = [&](int e) { return STAGED ? e : min(max(e, 0), npc); };
+    int w0 = 0, wn = Sp;
+    auto add = [&](int t, float x1, float x2) {
+        if (ONEWIN) {
+            bufg[t] = fmaf(x1, x2, bufg[t]);
+        } else {
+            const int c = t - w0;
+            if ((unsigned)c < (unsigned)wn) bufg[c] = fmaf(x1, x2, bufg[c]);
+        }
+    };
+    for (int t = tid; t < Sp; t += kSpThreads) {
+        const int c = add_exp(roG[t], rfG[t]);
+        sco[t] = c;
+        if (r0 == 0) coD[t] = c;
     }
-    if (r0 == 0)
-        for (int t = tid; t < Sp; t += kSpThreads) coD[t] = add_exp(roG[t], rfG[t]);
-    for (int s = r0 + wave; s < r1; s += kSpWaves) {
-        const int rfs = rfF[s];
-        int e0 = 0, e1 = 0;
-        if (s < S) {
-            e0 = realF ? ptr[s] : 0;
-            e1 = realF ? ptr[s + 1] : 1;
-        }
-        int emax = kNeg;
-        for (int w0 = 0; w0 < Sp; w0 += win) {
-            const int wn = min(win, Sp - w0);
-            for (int c = lane * 4; c < wn; c += 256) *reinterpret_cast<f32x4 *>(&buf[c]) = f32x4{0.f, 0.f, 0.f, 0.f};
-            for (int eb = e0; eb < e1; eb += 64) {
-                const int cnt = min(64, e1 - eb);
-                // lane j: the first operand's entry eb + j of row s, its
-                // target k and the second operand's entries of row k
-                int kj = 0, loj = 0, hij = 0;
-                float xj = 0.f;
-                if (lane < cnt) {
-                    if (realF) {
-                        const int q = perm ? perm[eb + lane] : eb + lane;
-                        kj = far[q];
-                        xj = ldexpf(vF[q], 0 - rfs);
-                    } else {
-                        kj = s;
-                        xj = ldexpf(1.f, 0 - rfs);
-                    }
-                    if (realG) {
-                        loj = STAGED ? sptr[kj] : ptr[kj];
-                        hij = STAGED ? sptr[kj + 1] : ptr[kj + 1];
-                    } else {
-                        loj = 0;
-                        hij = 1;
-                    }
+    for (int k = tid; k <= S; k += kSpThreads) sptr[k] = ptr[k];
+    // row exponents of the product: those of the first operand, folded
+    for (int r = r0 + tid; r < r1; r += kSpThreads) roD[r] = add_exp(roF[r], rfF[r]);
+    if (STAGED) {
+        // eight entries per thread in flight: the pair id q (col_pairs, or
+        // the column position for a transposed leaf's values), then target
+        // and value
+        constexpr int kU = 8;
+        for (int e0 = tid; e0 < np; e0 += kSpThreads * kU) {
+            int q[kU], t[kU];
+            float x[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) q[u] = perm[min(e0 + u * kSpThreads, npc)];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int e = min(e0 + u * kSpThreads, npc);
+                t[u] = far[tr ? q[u] : e];
+                x[u] = vG[q[u]];
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int e = e0 + u * kSpThreads;
+                if (e < np) {
+                    stt[e] = (uint16_t)t[u];
+                    sx[e] = realG ? x[u] : 0.f;
                 }
-                for (int j = 0; j < cnt; ++j) {
-                    const int k = __builtin_amdgcn_readlane(kj, j);
-                    const float x1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xj), j));
-                    const int lo = __builtin_amdgcn_readlane(loj, j);
-                    const int hi = __builtin_amdgcn_readlane(hij, j);
-                    for (int e = lo + lane; e < hi; e += 64) {
-                        int t;
-                        float x2;
-                        if (!realG) {
-                            t = k;
-                            x2 = ldexpf(1.f, 0 - rfG[k]);
-                        } else if (STAGED) {
-                            t = stt[e];
-                            x2 = sx[e];
-                        } else {
-                            const int q = perm ? perm[e] : e;
-                            t = far[q];
-                            x2 = ldexpf(vG[q], 0 - rfG[t]);
-                        }
-                        const int c = t - w0;
-                        if ((unsigned)c < (unsigned)wn) buf[c] = fmaf(x1, x2, buf[c]);
+            }
+        }
+    }
+    __syncthreads();
+
+    // first-operand entries of row s: [e0, e1) of the walk (identity: one
+    // entry k = s), and lane's entry e0 + lane (clamped) loaded
+    struct RowPf {
+        int e0, e1, k, rf;
+        float x;
+    };
+    auto row_pf = [&](int s) {
+        RowPf r;
+        const int sc = min(s, S - 1);
+        const bool has = s < S;
+        r.e0 = has && realF ? sptr[sc] : 0;
+        r.e1 = has ? (realF ? sptr[sc + 1] : 1) : 0;
+        const int ei = min(r.e0 + lane, npc);
+        r.x = vF[ei];
+        r.k = STAGED ? 0 : far[tr ? perm[ei] : ei];
+        r.rf = rfF[min(s, Sp - 1)];
+        return r;
+    };
+    int s = r0 + wave;
+    RowPf pf = row_pf(s);
+    for (; s < r1; s += kSpWaves) {
+        const int e0 = pf.e0, e1 = pf.e1;
+        float cx = realF ? pf.x : ldexpf(1.f, 0 - pf.rf);
+        int ck = realF ? (STAGED ? (int)stt[min(e0 + lane, npc)] : pf.k) : s;
+        pf = row_pf(s + kSpWaves);   // next row, in flight while this one is built
+        int emax = kNeg;
+        for (w0 = 0; w0 < Sp; w0 += win) {
+            wn = min(win, Sp - w0);
+            for (int c = lane * 4; c < 2 * win; c += 256)
+                *reinterpret_cast<f32x4 *>(&bufw[c]) = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int eb = e0; eb < e1; eb += kSpEnt) {
+                const int cnt = min(kSpEnt, e1 - eb);
+                if (eb != e0) {   // rows with more than 64 entries
+                    const int ei = min(eb + lane, npc);
+                    cx = vF[ei];
+                    ck = STAGED ? (int)stt[ei] : far[tr ? perm[ei] : ei];
+                }
+                if (!realG) {
+                    // identity second operand: entry k adds x1 2^-rf[k] at column k
+                    if (lane < cnt) {
+                        const int c = ck - w0;
+                        if ((unsigned)c < (unsigned)wn)
+                            bufw[c] = fmaf(cx, ldexpf(1.f, 0 - rfG[ck]), bufw[c]);
+                    }
+                    continue;
+                }
+                // tasks of this chunk: entry j has ceil(deg / 32) of them,
+                // numbered from the exclusive prefix sum pre
+                const int lo = sptr[ck];
+                const int deg = lane < cnt ? sptr[ck + 1] - lo : 0;
+                const int nt = (deg + 31) >> 5;
+                int pre, T;
+                if (!__any(nt > 1)) {   // at most one task per entry: a ballot
+                    const unsigned long long m = __ballot(nt > 0);
+                    pre = __popcll(m & ((1ull << lane) - 1ull));
+                    T = __popcll(m);
+                } else {
+                    int inc = nt;
+#pragma unroll
+                    for (int o = 1; o < 64; o <<= 1) {
+                        const int y = __shfl_up(inc, o);
+                        if (lane >= o) inc += y;
+                    }
+                    pre = inc - nt;
+                    T = __shfl(inc, 63);
+                }
+                for (int P = 0; P < T; P += tcap) {
+                    const int Tp = min(T - P, tcap);
+                    for (int u = max(pre, P); u < min(pre + nt, P + tcap); ++u) {
+                        const int q0 = lo + ((u - pre) << 5);
+                        task[u - P] = make_int4(__float_as_int(cx), q0, min(q0 + 32, lo + deg), 0);
+                    }
+                    // empty tasks (no items) after the last one: the step
+                    // loop runs whole pairs of steps and reads two ahead
+                    if (lane < kSpTaskPad) task[Tp + lane] = make_int4(0, 0, 0, 0);
+                    const int steps = (Tp + 1) >> 1;
+                    // step st runs task 2 st + grp; its item is loaded one
+                    // step ahead and the task two steps ahead
+                    int4 ta = task[grp];
+                    int4 tb = task[2 + grp];
+                    int t0;
+                    float x0;
+                    g_entry(item(ta.y + sub), t0, x0);
+                    float w0x = __int_as_float(ta.x);
+                    bool v0 = ta.y + sub < ta.z;
+                    for (int st = 0; st < steps; st += 2) {
+                        int t1;
+                        float x1v;
+                        g_entry(item(tb.y + sub), t1, x1v);
+                        const float w1x = __int_as_float(tb.x);
+                        const bool v1 = tb.y + sub < tb.z;
+                        ta = task[2 * st + 4 + grp];
+                        if (v0) add(t0, w0x, x0);
+                        g_entry(item(ta.y + sub), t0, x0);
+                        w0x = __int_as_float(ta.x);
+                        v0 = ta.y + sub < ta.z;
+                        tb = task[2 * st + 6 + grp];
+                        if (v1) add(t1, w1x, x1v);
                     }
                 }
             }
             float *Drow = D + (size_t)s * Sp + w0;
             for (int c = lane * 4; c < wn; c += 256) {
-                const f32x4 v = *reinterpret_cast<const f32x4 *>(&buf[c]);
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(&bufw[c]) +
+                                *reinterpret_cast<const f32x4 *>(&bufw[win + c]);
                 __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(&Drow[c]));
-                const int4 ro = *reinterpret_cast<const int4 *>(roG + w0 + c);
-                const int4 rf = *reinterpret_cast<const int4 *>(rfG + w0 + c);
-                const int co[4] = {add_exp(ro.x, rf.x), add_exp(ro.y, rf.y), add_exp(ro.z, rf.z),
-                                   add_exp(ro.w, rf.w)};
+                const int4 co = *reinterpret_cast<const int4 *>(&sco[w0 + c]);
+                const int cv[4] = {co.x, co.y, co.z, co.w};
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    if (v[u] > 0.f && co[u] > kNeg) emax = max(emax, fexp(v[u]) + co[u]);
+                    if (v[u] > 0.f && cv[u] > kNeg) emax = max(emax, fexp(v[u]) + cv[u]);
             }
         }
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) emax = max(emax, __shfl_xor(emax, o));
-        if (lane == 0) {
-            rfD[s] = emax;
-            roD[s] = add_exp(roF[s], rfF[s]);
-        }
+        if (lane == 0) rfD[s] = emax;
     }
 }
 
-// LDS bytes of span_sparse1: the row buffers, and with staging the second
-// operand's row pointers, folded values and 16-bit targets
-size_t sparse1_lds(const DevTable &d, int win, bool staged)
+// LDS bytes of span_sparse1: per wave two row buffers and the tasks; the
+// product's column exponents and the walk's row pointers; with staging the
+// second operand's folded values and 16-bit targets
+size_t sparse1_lds(const DevTable &d, int Sp, int win, bool staged)
 {
-    size_t b = (size_t)kSpWaves * win * sizeof(float);
+    const int tcap = staged ? kSpTasks : kSpTasks / 2;
+    size_t b = (size_t)kSpWaves * (2 * win + 4 * (tcap + kSpTaskPad)) * sizeof(float);
+    b += ((size_t)Sp + ((d.S + 4) & ~3)) * sizeof(int32_t);
     if (staged)
-        b += (size_t)((d.S + 4) & ~3) * sizeof(int32_t) + (size_t)d.npairs * sizeof(float) +
-             (((size_t)d.npairs * sizeof(uint16_t) + 15) & ~size_t(15));
+        b += (size_t)d.npairs * sizeof(float) + (((size_t)d.npairs * sizeof(uint16_t) + 15) & ~size_t(15));
     return b;
 }
 
-int launch_sparse1(const DevTable &d, const Geometry &g, StepView sv, const float *val, float *tree,
+int launch_sparse1(const DevTable &d, const Geometry &g, StepView sv, const float *pvf, float *tree,
                    int32_t *meta, hipStream_t st)
 {
-    const int win = std::min(g.Sp, kSpWin);
-    const bool staged = g.Sp <= 65536 && sparse1_lds(d, win, true) <= kSpLdsMax;
-    const size_t lds = sparse1_lds(d, win, staged);
+    // staged with the widest window that fits, else unstaged likewise
+    int win = 0;
+    bool staged = false;
+    for (bool stg : {true, false}) {
+        if (stg && g.Sp > 65536) continue;
+        for (int w : {std::min(g.Sp, 1024), std::min(g.Sp, 512), std::min(g.Sp, 256)})
+            if (sparse1_lds(d, g.Sp, w, stg) <= kSparseLdsMax) {
+                win = w;
+                staged = stg;
+                break;
+            }
+        if (win) break;
+    }
+    if (!win) return (int)hipErrorInvalidConfiguration;
+    const size_t lds = sparse1_lds(d, g.Sp, win, staged);
     const long long grid = (long long)g.B * (g.Lpad >> 1) * ((g.Sp + kSpRows - 1) / kSpRows);
     if (grid > 0x7fffffffLL) return (int)hipErrorInvalidConfiguration;
-    if (staged)
-        span_sparse1<true><<<(unsigned)grid, kSpThreads, lds, st>>>(d, sv, val, tree, meta, win);
-    else
-        span_sparse1<false><<<(unsigned)grid, kSpThreads, lds, st>>>(d, sv, val, tree, meta, win);
+    const bool one = win == g.Sp;
+    const void *fn = staged ? (one ? reinterpret_cast<const void *>(&span_sparse1<true, true>)
+                                   : reinterpret_cast<const void *>(&span_sparse1<true, false>))
+                            : (one ? reinterpret_cast<const void *>(&span_sparse1<false, true>)
+                                   : reinterpret_cast<const void *>(&span_sparse1<false, false>));
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return (int)e;
+#define FA_SPARSE1(ST, ONE) \
+    span_sparse1<ST, ONE><<<(unsigned)grid, kSpThreads, lds, st>>>(d, sv, pvf, tree, meta, win, \
+                                                                    ST ? kSpTasks : kSpTasks / 2)
+    if (staged) {
+        if (one) FA_SPARSE1(true, true);
+        else FA_SPARSE1(true, false);
+    } else {
+        if (one) FA_SPARSE1(false, true);
+        else FA_SPARSE1(false, false);
+    }
+#undef FA_SPARSE1
     return (int)hipGetLastError();
 }
 
@@ -771,8 +908,8 @@ int launch_span_tree(const DevTable &d, const Geometry &g, float *tree, int32_t 
         }
         const int huge_tiles = g.Sp / kHuge;
         const long long huge_wgs = (long long)g.B * nn * huge_tiles * huge_tiles;
-        if (k == 1 && d.first_sparse) {
-            const int se = launch_sparse1(d, g, sv, (const float *)(ws + w.val), tree, meta, st);
+        if (k == 1 && d.first_sparse && d.npairs > 0) {
+            const int se = launch_sparse1(d, g, sv, (const float *)(ws + w.pvf), tree, meta, st);
             if (se) return se;
         } else if (ks == 1 && g.Sp % kHuge == 0 && huge_wgs >= 256) {
             span_gemm256<<<(unsigned)huge_wgs, kHugeThreads, 0, st>>>(sv, tree, meta, n0, nn);
