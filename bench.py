@@ -59,17 +59,26 @@ def algorithmic_work(tb, B, L):
     mask_bytes = V * 4
     leaves = B * Lpad * S * S * 4
     internal = B * (Lpad - 1) * S * S * 4
+    sparse1 = bool(tb.info["first_sparse"])
+    npairs, w1 = tb.info["pairs"], tb.info["first_work"]
+    # first level: dense 2*S^3 per product, or the sparse form's multiply-adds
+    # (pairs (a, k), (k, c) sharing k) per product
+    level1_flops = B * (Lpad // 2) * (2.0 * w1 if sparse1 else 2.0 * S ** 3)
+    level1 = (dict(bound="hbm", work=B * (Lpad // 2) * (S * S * 4 + 2 * npairs * 4), unit="GB/s",
+                   per_unit="per product: the dense S*S output write + both leaves' pair values "
+                            "(2*pairs*4), B*Lpad/2 products")
+              if sparse1 else
+              dict(bound="mfma", work=2.0 * S ** 3 * B * (Lpad // 2), unit="TFLOP/s",
+                   per_unit="2*S^3 per product (S trimmed states), B*Lpad/2 products"))
     return dict(
         a1_bytes=p_bytes + table_bytes + leaves,
-        a2_flops=2.0 * S ** 3 * B * (Lpad - 1),
+        a2_flops=2.0 * S ** 3 * B * (Lpad // 2 - 1) + level1_flops,
         a4_bytes=p_bytes + p_bytes + leaves + internal + table_bytes,
         # per launch of the kernels the library can bracket with events
         kernels={
             "emission_dense": dict(bound="hbm", work=p_bytes + mask_bytes, unit="GB/s",
                                    per_unit="p read once (B*L*V*4) + token mask (V*4)"),
-            "span_gemm_level1": dict(bound="mfma", work=2.0 * S ** 3 * B * (Lpad // 2),
-                                     unit="TFLOP/s",
-                                     per_unit="2*S^3 per product (S trimmed states), B*Lpad/2 products"),
+            level1_name(tb): level1,
             "marg_q": dict(bound="hbm", work=2 * p_bytes + mask_bytes, unit="GB/s",
                            per_unit="p read + q write (2*B*L*V*4) + token mask (V*4)"),
         },
@@ -125,9 +134,15 @@ def cpu_baseline(w):
 
 # --- rocprofv3 output -> committed summaries ------------------------------
 
+def level1_name(tb):
+    """The first tree level's kernel: sparse row combination or dense MFMA."""
+    return "span_sparse1" if tb.info["first_sparse"] else "span_gemm_level1"
+
+
 # measured kernels: how to find their dispatches in rocprofv3 output
 KERNEL_MATCH = {
     "emission_dense": lambda n: "emission_dense<" in n,
+    "span_sparse1": lambda n: "span_sparse1" in n,
     "span_gemm_level1": lambda n: "span_gemm" in n,   # first of the family after tree_init_rf
     "marg_q": lambda n: "marg_q" in n,
 }
@@ -324,7 +339,7 @@ def main():
     # the library brackets one kernel per step with HIP events on its own
     # stream; the timed steps rotate over the three measured kernels
     prof_ids = [("emission_dense", fa.FA_PROF_EMISSION_DENSE),
-                ("span_gemm_level1", fa.FA_PROF_TREE_LEVEL1),
+                (level1_name(tb), fa.FA_PROF_TREE_LEVEL1),
                 ("marg_q", fa.FA_PROF_MARG_Q)]
     hev = HipEvents()
 

@@ -72,6 +72,29 @@ def test_invalid_ranges_and_flags():
         fa.Table(2, 10, 0, [1], [0], [1], np.array([0, -1], np.int64), np.zeros(0, np.int32), 1)
 
 
+def test_first_level_flags_and_choice():
+    """The first span level's form: forced either way, both at once
+    rejected, and the automatic choice by the work ratio (a chain of states
+    with one successor each is sparse; a complete graph is dense)."""
+    edges = [(s, s + 1, [s % 7]) for s in range(39)]
+    chain = lambda f: _compile(40, 10, 0, [39], edges, fa.FA_DFA | f)
+    assert chain(0).info["first_sparse"] == 1
+    assert chain(0).info["first_work"] == 38      # pairs (a, k), (k, c) sharing k
+    assert chain(fa.FA_FIRST_LEVEL_DENSE).info["first_sparse"] == 0
+    assert chain(fa.FA_FIRST_LEVEL_SPARSE).info["first_sparse"] == 1
+    both = fa.FA_FIRST_LEVEL_SPARSE | fa.FA_FIRST_LEVEL_DENSE
+    assert _code(lambda: chain(both)) == _fa.FA_EINVAL
+    full = [(a, b, [a * 64 + b]) for a in range(64) for b in range(64)]
+    t = _compile(64, 4096, 0, [63], full, fa.FA_DFA)
+    assert t.info["first_work"] == 64 ** 3 and t.info["first_sparse"] == 0
+    # the sparse form keeps the row pointers and column exponents in LDS,
+    # which bounds its states
+    big = [(s, s + 1, [0]) for s in range(16400)]
+    assert _code(lambda: _compile(16401, 2, 0, [16400], big,
+                                  fa.FA_DFA | fa.FA_FIRST_LEVEL_SPARSE)) == _fa.FA_ETOOBIG
+    assert _compile(16401, 2, 0, [16400], big, fa.FA_DFA).info["first_sparse"] == 0
+
+
 def test_determinism_check():
     edges = [(0, 1, [3, 4]), (0, 2, [4, 5]), (1, 1, [0]), (2, 2, [0])]
     assert _code(lambda: _compile(3, 6, 0, [1, 2], edges, fa.FA_DFA)) == _fa.FA_ENOTDET
