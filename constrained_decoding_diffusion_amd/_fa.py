@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libfa.so")
 FA_OK, FA_EINVAL, FA_ENOTDET, FA_ETOOBIG, FA_EHIP, FA_ESTATE = range(6)
 FA_ROW_INFEASIBLE, FA_ROW_UNDERFLOW, FA_ROW_BADPROB = 1, 2, 4
 FA_DFA, FA_NFA, FA_LABEL_RANGES, FA_NO_TRIM = 1, 2, 4, 8
-FA_FIRST_LEVEL_SPARSE, FA_FIRST_LEVEL_DENSE = 16, 32
+FA_FIRST_LEVEL_SPARSE, FA_FIRST_LEVEL_DENSE, FA_SECOND_LEVEL_SPARSE = 16, 32, 64
 FA_CONF_PROB, FA_CONF_NEGENT = 0, 1
 FA_PROF_NONE, FA_PROF_EMISSION_DENSE, FA_PROF_TREE_LEVEL1, FA_PROF_MARG_Q = range(4)
 
@@ -79,7 +79,7 @@ def _np_ptr(a: np.ndarray):
 
 INFO_KEYS = ["S", "Sp", "start", "n_accept", "pairs", "list_pairs", "dense_pairs", "range_pairs",
              "list_entries", "segments", "cuts", "sel_tokens", "use_sel", "V", "S_orig",
-             "first_sparse", "first_work"]
+             "first_sparse", "first_work", "second_sparse", "second_work", "pairs2"]
 
 
 class Table:
@@ -110,11 +110,13 @@ class Table:
     @classmethod
     def from_automaton(cls, aut, flags=None, first_level="auto"):
         """first_level: "auto" (the library's choice), "sparse" (first span
-        level from the pair values) or "dense" (dense matrix products)."""
+        level from the pair values), "sparse2" (also the second level, from
+        the two-step pattern) or "dense" (dense matrix products)."""
         if flags is None:
             flags = (FA_DFA if aut.dfa else FA_NFA) | (FA_LABEL_RANGES if aut.ranges else 0)
         flags |= {"auto": 0, "sparse": FA_FIRST_LEVEL_SPARSE,
-                  "dense": FA_FIRST_LEVEL_DENSE}[first_level]
+                  "dense": FA_FIRST_LEVEL_DENSE,
+                  "sparse2": FA_FIRST_LEVEL_SPARSE | FA_SECOND_LEVEL_SPARSE}[first_level]
         return cls(aut.S, aut.V, aut.start, aut.accept, aut.src, aut.dst, aut.label_off,
                    aut.label_tok, flags)
 

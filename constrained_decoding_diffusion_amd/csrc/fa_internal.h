@@ -21,7 +21,11 @@ constexpr int kSparseFirstRatio = 256;
 // it holds the product's column exponents and the row pointers, which
 // bounds the states the sparse form takes
 constexpr size_t kSparseLdsMax = 160 * 1024;
-constexpr int kSparseFirstMaxS = 16384;
+// LDS bound of the sparse levels: the row pointers and column exponents
+// (Sp + S words) next to eight waves' 1024-column row buffers and tasks
+constexpr int kSparseMaxSpS = 22000;
+constexpr int kSpWin = 1024;       // columns of a window when Sp > kSpWin
+constexpr int32_t kSparseSecondMaxPairs = 1 << 24;
 constexpr int kLeafTile = 4096;    // floats of the LDS tile of the one-pass leaf writer
 constexpr int kDenseStepsMax = 64;  // dense-mask contraction: 256-token steps per V chunk, at most
 constexpr int kDenseSlots = 512;    // workgroups of that contraction resident at once (256 CUs x 2)
@@ -99,6 +103,11 @@ struct DevTable {
     const int32_t *ind_pair;   // [n_ind] pairs whose value is computed (not one direct read)
     int32_t n_ind;
     int32_t first_sparse;        // 1: the first span level is formed from the pair values
+    int32_t second_sparse;       // 1: so is the second, from the two-step pattern
+    int32_t np2;                 // pairs of the two-step pattern
+    int32_t nwin;                // kSpWin-column windows of a row (0: one window of Sp <= kSpWin)
+    const int32_t *p2_a, *p2_b, *p2_row_ptr, *p2_col_ptr, *p2_col_pairs, *p2_colpos;
+    const int32_t *w1_n, *w1_t, *w2_n, *w2_t;
     const uint32_t *dense_bits;  // [ndense][dense_words] bit v%32 of word v/32: v in the label
     int32_t dense_words;
     const int32_t *ev_a;       // [2 nseg] per cut event (cut_ev order): the states of its pair
@@ -138,6 +147,15 @@ struct HostTable {
     bool selbit = false;
     bool first_sparse = false;  // first span level by row combination over the pairs
     int64_t first_work = 0;     // its multiply-adds per product: pairs (a, k) times pairs (k, c)
+    // two-step pattern: pairs (a, c) joined by pairs (a, k), (k, c), sorted
+    // (a, c), with the same row/column orders as the pairs (second level)
+    std::vector<int32_t> p2_a, p2_b, p2_row_ptr, p2_col_ptr, p2_col_pairs, p2_colpos;
+    bool second_sparse = false;
+    int64_t second_work = 0;    // multiply-adds per second-level product
+    // entry offsets of each state's row walk (_n) and column walk (_t) at
+    // every kSpWin-column window boundary, [S][nwin + 1]; only when Sp > kSpWin
+    std::vector<int32_t> w1_n, w1_t, w2_n, w2_t;
+    int32_t nwin = 0;
     // device image
     std::vector<uint8_t> image;
     std::vector<size_t> offs;  // section offsets, in the order of DevTable pointers
@@ -167,6 +185,7 @@ bool make_geometry(const HostTable &t, int32_t B, int32_t L, Geometry *g);
 struct WsLayout {
     size_t dpart = 0, dval = 0, psel = 0, cutp = 0, val = 0;  // emission reduce
     size_t pvf = 0;                            // folded leaf pair values (sparse first level)
+    size_t pv2 = 0;                            // first-level nodes on the two-step pattern (second level)
     int32_t n_vchunks = 0;                     // dense-mask contraction: V split
     int32_t vchunk = 0;                        // tokens per V chunk (multiple of 256)
     int32_t sel_mode = 0;                      // token-list copy: 1 LDS-buffered, 2 gathered

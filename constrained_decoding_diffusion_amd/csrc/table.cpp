@@ -85,6 +85,16 @@ void build_image(HostTable &t)
     append_section(t.image, t.offs, t.ev_w);
     append_section(t.image, t.offs, t.cutbits);
     append_section(t.image, t.offs, t.pair_colpos);
+    append_section(t.image, t.offs, t.p2_a);
+    append_section(t.image, t.offs, t.p2_b);
+    append_section(t.image, t.offs, t.p2_row_ptr);
+    append_section(t.image, t.offs, t.p2_col_ptr);
+    append_section(t.image, t.offs, t.p2_col_pairs);
+    append_section(t.image, t.offs, t.p2_colpos);
+    append_section(t.image, t.offs, t.w1_n);
+    append_section(t.image, t.offs, t.w1_t);
+    append_section(t.image, t.offs, t.w2_n);
+    append_section(t.image, t.offs, t.w2_t);
     t.image.resize((t.image.size() + 255) & ~size_t(255));
 }
 
@@ -129,6 +139,11 @@ DevTable HostTable::device_view() const
     nxt(d.ev_w);
     nxt(d.cutbits);
     nxt(d.pair_colpos);
+    nxt(d.p2_a); nxt(d.p2_b); nxt(d.p2_row_ptr); nxt(d.p2_col_ptr); nxt(d.p2_col_pairs);
+    nxt(d.p2_colpos); nxt(d.w1_n); nxt(d.w1_t); nxt(d.w2_n); nxt(d.w2_t);
+    d.second_sparse = second_sparse ? 1 : 0;
+    d.np2 = (int32_t)p2_a.size();
+    d.nwin = nwin;
     d.n_tm = (int32_t)tm_pair.size();
     if (map_n.empty()) {
         d.map_n = nullptr;
@@ -259,9 +274,74 @@ WsLayout ws_layout(const HostTable &t, const Geometry &g)
     const bool joint = t.ndense() > 0 && t.V % 4 == 0;
     w.tcs = o; o = al(o + (joint ? BL * (size_t)w.tcs_nch * 4 * sizeof(double) : 0));
     w.tcs_ok = o; o = al(o + (joint ? BL * sizeof(int32_t) : 0));
+    // first-level nodes on the two-step pattern: written by the first level,
+    // read by the second, apart from every per-call region
+    w.pv2 = o; o = al(o + (t.second_sparse ? (size_t)g.B * (g.Lpad / 2) * t.p2_a.size() * sizeof(float) : 0));
     w.total = o;
     if (w.total == 0) w.total = 256;
     return w;
+}
+
+// the two-step pattern of the pairs: (a, c) for every pairs (a, k), (k, c),
+// sorted by (a, c), with row pointers, the (c, a) order and its inverse
+static void build_two_step(HostTable &t)
+{
+    const int32_t S = t.S;
+    std::vector<int32_t> mark(S, -1), cs;
+    t.p2_row_ptr.assign(S + 1, 0);
+    for (int32_t a = 0; a < S; ++a) {
+        cs.clear();
+        for (int32_t e = t.row_ptr[a]; e < t.row_ptr[a + 1]; ++e) {
+            const int32_t k = t.pair_b[e];
+            for (int32_t e2 = t.row_ptr[k]; e2 < t.row_ptr[k + 1]; ++e2) {
+                const int32_t c = t.pair_b[e2];
+                if (mark[c] != a) {
+                    mark[c] = a;
+                    cs.push_back(c);
+                }
+            }
+        }
+        std::sort(cs.begin(), cs.end());
+        for (int32_t c : cs) {
+            t.p2_a.push_back(a);
+            t.p2_b.push_back(c);
+        }
+        t.p2_row_ptr[a + 1] = (int32_t)t.p2_a.size();
+    }
+    const int32_t n2 = (int32_t)t.p2_a.size();
+    t.p2_col_ptr.assign(S + 1, 0);
+    for (int32_t q = 0; q < n2; ++q) t.p2_col_ptr[t.p2_b[q] + 1]++;
+    for (int32_t s = 0; s < S; ++s) t.p2_col_ptr[s + 1] += t.p2_col_ptr[s];
+    t.p2_col_pairs.resize(n2);
+    std::iota(t.p2_col_pairs.begin(), t.p2_col_pairs.end(), 0);
+    std::stable_sort(t.p2_col_pairs.begin(), t.p2_col_pairs.end(), [&](int32_t x, int32_t y) {
+        return t.p2_b[x] != t.p2_b[y] ? t.p2_b[x] < t.p2_b[y] : t.p2_a[x] < t.p2_a[y];
+    });
+    t.p2_colpos.resize(n2);
+    for (int32_t k = 0; k < n2; ++k) t.p2_colpos[t.p2_col_pairs[k]] = k;
+}
+
+// for every state s and window w: the first entry of s's row walk (targets
+// ascending) and of its column walk (sources ascending) at or past column
+// w * kSpWin; [S][nwin + 1], the last the walk's end
+static void window_offsets(const HostTable &t, const std::vector<int32_t> &rp,
+                           const std::vector<int32_t> &cp, const std::vector<int32_t> &pa,
+                           const std::vector<int32_t> &pb, const std::vector<int32_t> &cpairs,
+                           std::vector<int32_t> &wn, std::vector<int32_t> &wt)
+{
+    const int32_t S = t.S, nw = t.nwin;
+    wn.assign((size_t)S * (nw + 1), 0);
+    wt.assign((size_t)S * (nw + 1), 0);
+    for (int32_t s = 0; s < S; ++s) {
+        int32_t e = rp[s], f = cp[s];
+        for (int32_t w = 0; w <= nw; ++w) {
+            const int64_t lim = (int64_t)w * kSpWin;
+            while (e < rp[s + 1] && pb[e] < lim) ++e;
+            while (f < cp[s + 1] && pa[cpairs[f]] < lim) ++f;
+            wn[(size_t)s * (nw + 1) + w] = w == nw ? rp[s + 1] : e;
+            wt[(size_t)s * (nw + 1) + w] = w == nw ? cp[s + 1] : f;
+        }
+    }
 }
 
 static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, int32_t n_accept,
@@ -273,7 +353,7 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
     if ((n_accept > 0 && !accept) || (E > 0 && (!src || !dst || !label_off))) return FA_EINVAL;
     if ((flags & FA_DFA) && (flags & FA_NFA)) return FA_EINVAL;
     if (flags & ~uint32_t(FA_DFA | FA_NFA | FA_LABEL_RANGES | FA_NO_TRIM | FA_FIRST_LEVEL_SPARSE |
-                          FA_FIRST_LEVEL_DENSE))
+                          FA_FIRST_LEVEL_DENSE | FA_SECOND_LEVEL_SPARSE))
         return FA_EINVAL;
     if ((flags & FA_FIRST_LEVEL_SPARSE) && (flags & FA_FIRST_LEVEL_DENSE)) return FA_EINVAL;
     if (E > std::numeric_limits<int32_t>::max()) return FA_ETOOBIG;
@@ -671,13 +751,45 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
     for (int32_t q = 0; q < np; ++q) w1 += t.row_ptr[t.pair_b[q] + 1] - t.row_ptr[t.pair_b[q]];
     t.first_work = w1;
     if (flags & FA_FIRST_LEVEL_SPARSE) {
-        if (t.S > kSparseFirstMaxS) return FA_ETOOBIG;
+        if (t.Sp + t.S > kSparseMaxSpS) return FA_ETOOBIG;
         t.first_sparse = true;
     } else if (flags & FA_FIRST_LEVEL_DENSE) {
         t.first_sparse = false;
     } else {
-        t.first_sparse = t.S <= kSparseFirstMaxS &&
+        t.first_sparse = t.Sp + t.S <= kSparseMaxSpS &&
                          (double)kSparseFirstRatio * (double)w1 <= (double)t.Sp * t.Sp * t.Sp;
+    }
+    t.p2_a.clear(); t.p2_b.clear(); t.p2_row_ptr.clear(); t.p2_col_ptr.clear();
+    t.p2_col_pairs.clear(); t.p2_colpos.clear();
+    t.w1_n.clear(); t.w1_t.clear(); t.w2_n.clear(); t.w2_t.clear();
+    t.second_sparse = false;
+    t.second_work = 0;
+    t.nwin = t.Sp > kSpWin ? (t.Sp + kSpWin - 1) / kSpWin : 0;
+    if (t.first_sparse) {
+        build_two_step(t);
+        int64_t w2 = 0;
+        for (size_t q = 0; q < t.p2_a.size(); ++q) w2 += t.p2_row_ptr[t.p2_b[q] + 1] - t.p2_row_ptr[t.p2_b[q]];
+        t.second_work = w2;
+        const bool fits = t.p2_a.size() <= (size_t)kSparseSecondMaxPairs;
+        if (flags & FA_SECOND_LEVEL_SPARSE) {
+            if (!fits) return FA_ETOOBIG;
+            t.second_sparse = true;
+        } else {
+            t.second_sparse = fits && !(flags & FA_FIRST_LEVEL_DENSE) &&
+                              (double)kSparseFirstRatio * (double)w2 <= (double)t.Sp * t.Sp * t.Sp;
+        }
+        if (t.nwin > 0) {
+            window_offsets(t, t.row_ptr, t.col_ptr, t.pair_a, t.pair_b, t.col_pairs, t.w1_n, t.w1_t);
+            if (t.second_sparse)
+                window_offsets(t, t.p2_row_ptr, t.p2_col_ptr, t.p2_a, t.p2_b, t.p2_col_pairs, t.w2_n,
+                               t.w2_t);
+        }
+        if (!t.second_sparse) {
+            t.p2_a.clear(); t.p2_b.clear(); t.p2_row_ptr.clear(); t.p2_col_ptr.clear();
+            t.p2_col_pairs.clear(); t.p2_colpos.clear();
+        }
+    } else if (flags & FA_SECOND_LEVEL_SPARSE) {
+        return FA_EINVAL;
     }
     build_image(t);
     return FA_OK;
@@ -725,10 +837,11 @@ extern "C" int fa_table_info(const fa_table *t, int64_t *info, int32_t n)
     const HostTable &h = t->h;
     int32_t nl = 0, nd = 0, nr = 0;
     for (int32_t c : h.pair_cls) (c == kList ? nl : c == kDense ? nd : nr)++;
-    int64_t v[17] = {h.S, h.Sp, h.start, (int64_t)h.acc.size(), h.npairs(), nl, nd, nr,
+    int64_t v[20] = {h.S, h.Sp, h.start, (int64_t)h.acc.size(), h.npairs(), nl, nd, nr,
                      (int64_t)h.list_tok.size(), h.nseg(), h.ncut(), h.nsel(), h.use_sel ? 1 : 0,
-                     h.V, h.S_orig, h.first_sparse ? 1 : 0, h.first_work};
-    for (int32_t k = 0; k < n && k < 17; ++k) info[k] = v[k];
+                     h.V, h.S_orig, h.first_sparse ? 1 : 0, h.first_work,
+                     h.second_sparse ? 1 : 0, h.second_work, (int64_t)h.p2_a.size()};
+    for (int32_t k = 0; k < n && k < 20; ++k) info[k] = v[k];
     return FA_OK;
 }
 

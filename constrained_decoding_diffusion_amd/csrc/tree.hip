@@ -567,31 +567,32 @@ __global__ __launch_bounds__(kHugeThreads) void span_gemm256(StepView sv, float 
 }
 
 
-// First level from the pair values.  A leaf holds one value per pair (a, b)
-// of the automaton, so a first-level product is a row combination: stored
-// row s of node n is the sum over the first operand's pairs (s, k) of x1
-// times the second operand's row k, where both operands are the folded
-// entries the dense kernels consume (value times 2^-rf of its stored row,
-// written by the leaf writer in each leaf's stored entry order; identity
-// leaves past the sequence end hold their diagonal).  A node stored as is
-// walks rows (pair order, row_ptr); a transposed node walks columns
-// (col_pairs order, col_ptr), which are its stored rows.  Both operands use
-// the same walk, so the first operand's entry e has the second operand's
-// target array entry e as its k.
+// Sparse levels.  A leaf holds one value per pair (a, b) of the automaton,
+// so a first-level product is a row combination: stored row s of node n is
+// the sum over the first operand's pairs (s, k) of x1 times the second
+// operand's row k, where both operands are the folded entries the dense
+// kernels consume (value times 2^(co - rf) of its stored row and column),
+// given per node in its stored entry order; identity leaves past the
+// sequence end hold their diagonal.  A node stored as is walks rows (pair
+// order, row pointers); a transposed node walks columns (column order),
+// which are its stored rows.  Both operands use the same walk, so the first
+// operand's entry e has target array entry e as its k.  The second level is
+// the same over the two-step pattern (pairs (a, c) joined through some k),
+// whose values the first level extracts from its output rows.
 //
 // One wave builds one output row, a window of `win` columns at a time, in
-// two LDS row buffers.  The row's work is cut into tasks of at most 32
-// items (one k, a slice of its row), numbered by a prefix sum over the
-// entries; lane group g (32 lanes) runs tasks g, g + 2, ... into buffer g,
-// one item per lane, both groups in lockstep.  Within one task the targets
-// are distinct pairs and one wave's LDS accesses stay in program order, so
-// the buffers need no atomics; the row is buffer 0 + buffer 1, each summed
-// in task order, so the result does not depend on timing.  The task two
-// steps ahead and the next item are read before the current item's buffer
-// update, and the next row's first-operand values are loaded while the
-// current row is built.  The column exponents of the product and the
-// walk's row pointers sit in LDS; with STAGED also the second operand's
-// targets and folded values.
+// two LDS row buffers.  The row's work in a window is cut into tasks of at
+// most 32 items (one k, a slice of its row inside the window), numbered by
+// a ballot or a prefix sum over the entries; lane group g (32 lanes) runs
+// tasks g, g + 2, ... into buffer g, one item per lane, both groups in
+// lockstep.  Within one task the targets are distinct pairs and one wave's
+// LDS accesses stay in program order, so the buffers need no atomics; the
+// row is buffer 0 + buffer 1, each summed in task order, so the result does
+// not depend on timing.  The task two steps ahead and the next item are
+// read before the current item's buffer update, and the next row's
+// first-operand values are loaded while the current row is built.  The
+// column exponents of the product and the walk's row pointers sit in LDS;
+// with STAGED also the second operand's targets and folded values.
 constexpr int kSpThreads = 512;
 constexpr int kSpWaves = kSpThreads / 64;
 constexpr int kSpRows = 256;   // output rows per workgroup
@@ -601,37 +602,63 @@ constexpr int kSpTaskPad = 8;  // empty tasks after a pass's last one
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// a pair pattern: row walk (row pointers, targets = b) and column walk
+// (column pointers, column order, targets = a), and per-window offsets of
+// both walks when rows span several windows
+struct SpPat {
+    const int32_t *row_ptr, *col_ptr, *pa, *pb, *col_pairs, *colpos, *wn, *wt;
+    int32_t np;
+};
+
+struct SpLevel {
+    SpPat in;              // the operands' pattern
+    SpPat out;             // pattern whose values are taken from the output (out.np = 0: none)
+    const float *vin;      // folded operand values, [B][vin_nodes][in.np], stored entry order
+    float *vout;           // raw output values on `out`, [B][vout_nodes][out.np]
+    int vin_nodes, vout_nodes;
+    int level, n0, nsp;    // products: nodes n0 .. n0 + nsp - 1 of every row
+    int win, tcap, nwin;
+};
+
 template <bool STAGED, bool ONEWIN>
-__global__ __launch_bounds__(kSpThreads) void span_sparse1(DevTable d, StepView sv,
-                                                           const float *__restrict__ pvf,
-                                                           float *__restrict__ tree,
-                                                           int32_t *__restrict__ meta, int win,
-                                                           int tcap)
+__global__ __launch_bounds__(kSpThreads) void span_sparse(DevTable d, StepView sv, SpLevel lv,
+                                                          float *__restrict__ tree,
+                                                          int32_t *__restrict__ meta)
 {
     extern __shared__ __align__(16) float sm[];
-    const int Sp = sv.Sp, S = d.S, np = d.npairs;
-    if (np <= 0) return;   // the launcher takes tables with pairs only
-    const int nn = sv.Lpad >> 1;
+    const int Sp = sv.Sp, S = d.S, np = lv.in.np;
+    if (np <= 0) return;   // the launcher takes patterns with pairs only
+    const int win = lv.win, tcap = lv.tcap, nwin = lv.nwin;
     const int rblocks = (Sp + kSpRows - 1) / kSpRows;
     const int prod = blockIdx.x / rblocks, r0 = (blockIdx.x % rblocks) * kSpRows;
     const int r1 = min(r0 + kSpRows, Sp);
-    const int b = prod / nn, n = nn + prod % nn;
+    const int b = prod / lv.nsp, n = lv.n0 + prod % lv.nsp;
     const bool tr = stored_transposed(n);
     const int hF = tr ? 2 * n + 1 : 2 * n, hG = tr ? 2 * n : 2 * n + 1;
-    const int iF = hF - sv.Lpad, iG = hG - sv.Lpad;
-    const bool realF = iF < sv.L, realG = iG < sv.L;
+    const int cbase = sv.Lpad >> (lv.level - 1);   // first node of the children's level
+    const int iF = hF - cbase, iG = hG - cbase;
+    // first level: leaves past the sequence end are the identity
+    const bool realF = lv.level > 1 || iF < sv.L, realG = lv.level > 1 || iG < sv.L;
     const int32_t *roF = sv.meta_ptr((const int32_t *)meta, b, hF, 0);
     const int32_t *rfF = sv.meta_ptr((const int32_t *)meta, b, hF, 2);
     const int32_t *roG = sv.meta_ptr((const int32_t *)meta, b, hG, 0);
     const int32_t *rfG = sv.meta_ptr((const int32_t *)meta, b, hG, 2);
-    // both leaves' entries are in their stored order: the first operand's
+    // both operands' entries are in their stored order: the first operand's
     // is its walk order; the second's is the other one
-    const float *vF = pvf + ((size_t)b * sv.L + (realF ? iF : 0)) * np;
-    const float *vG = pvf + ((size_t)b * sv.L + (realG ? iG : 0)) * np;
-    const int32_t *ptr = tr ? d.col_ptr : d.row_ptr;
-    const int32_t *far = tr ? d.pair_a : d.pair_b;
-    const int32_t *perm = tr ? d.col_pairs : d.pair_colpos;
+    const float *vF = lv.vin + ((size_t)b * lv.vin_nodes + (realF ? iF : 0)) * np;
+    const float *vG = lv.vin + ((size_t)b * lv.vin_nodes + (realG ? iG : 0)) * np;
+    const int32_t *ptr = tr ? lv.in.col_ptr : lv.in.row_ptr;
+    const int32_t *far = tr ? lv.in.pa : lv.in.pb;
+    const int32_t *perm = tr ? lv.in.col_pairs : lv.in.colpos;
+    const int32_t *woff = tr ? lv.in.wt : lv.in.wn;
     const int npc = np - 1;
+    // output values on the `out` pattern, in this node's stored entry order
+    const bool extract = lv.out.np > 0 && realF && realG;
+    const int32_t *optr = tr ? lv.out.col_ptr : lv.out.row_ptr;
+    const int32_t *ofar = tr ? lv.out.pa : lv.out.pb;
+    const int32_t *operm = tr ? lv.out.col_pairs : nullptr;
+    const int32_t *owoff = tr ? lv.out.wt : lv.out.wn;
+    float *vout = extract ? lv.vout + ((size_t)b * lv.vout_nodes + (n - lv.n0)) * lv.out.np : nullptr;
     float *D = sv.mat_ptr(tree, b, n);
     int32_t *roD = sv.meta_ptr(meta, b, n, 0);
     int32_t *coD = sv.meta_ptr(meta, b, n, 1);
@@ -660,7 +687,7 @@ __global__ __launch_bounds__(kSpThreads) void span_sparse1(DevTable d, StepView 
     // item index: staged reads of an empty task's items stay inside the LDS
     // block (unused); memory reads are clamped into the arrays
     auto item = [&](int e) { return STAGED ? e : min(max(e, 0), npc); };
-    int w0 = 0, wn = Sp;
+    int w0 = 0, wn = Sp, wi = 0;
     auto add = [&](int t, float x1, float x2) {
         if (ONEWIN) {
             bufg[t] = fmaf(x1, x2, bufg[t]);
@@ -678,8 +705,8 @@ __global__ __launch_bounds__(kSpThreads) void span_sparse1(DevTable d, StepView 
     // row exponents of the product: those of the first operand, folded
     for (int r = r0 + tid; r < r1; r += kSpThreads) roD[r] = add_exp(roF[r], rfF[r]);
     if (STAGED) {
-        // eight entries per thread in flight: the pair id q (col_pairs, or
-        // the column position for a transposed leaf's values), then target
+        // eight entries per thread in flight: the pair id q (column order,
+        // or the column position for values stored transposed), then target
         // and value
         constexpr int kU = 8;
         for (int e0 = tid; e0 < np; e0 += kSpThreads * kU) {
@@ -727,16 +754,18 @@ __global__ __launch_bounds__(kSpThreads) void span_sparse1(DevTable d, StepView 
     RowPf pf = row_pf(s);
     for (; s < r1; s += kSpWaves) {
         const int e0 = pf.e0, e1 = pf.e1;
-        float cx = realF ? pf.x : ldexpf(1.f, 0 - pf.rf);
-        int ck = realF ? (STAGED ? (int)stt[min(e0 + lane, npc)] : pf.k) : s;
+        const float cx0 = realF ? pf.x : ldexpf(1.f, 0 - pf.rf);
+        const int ck0 = realF ? (STAGED ? (int)stt[min(e0 + lane, npc)] : pf.k) : s;
         pf = row_pf(s + kSpWaves);   // next row, in flight while this one is built
         int emax = kNeg;
-        for (w0 = 0; w0 < Sp; w0 += win) {
+        for (w0 = 0, wi = 0; w0 < Sp; w0 += win, ++wi) {
             wn = min(win, Sp - w0);
             for (int c = lane * 4; c < 2 * win; c += 256)
                 *reinterpret_cast<f32x4 *>(&bufw[c]) = f32x4{0.f, 0.f, 0.f, 0.f};
             for (int eb = e0; eb < e1; eb += kSpEnt) {
                 const int cnt = min(kSpEnt, e1 - eb);
+                float cx = cx0;
+                int ck = ck0;
                 if (eb != e0) {   // rows with more than 64 entries
                     const int ei = min(eb + lane, npc);
                     cx = vF[ei];
@@ -751,10 +780,20 @@ __global__ __launch_bounds__(kSpThreads) void span_sparse1(DevTable d, StepView 
                     }
                     continue;
                 }
-                // tasks of this chunk: entry j has ceil(deg / 32) of them,
-                // numbered from the exclusive prefix sum pre
-                const int lo = sptr[ck];
-                const int deg = lane < cnt ? sptr[ck + 1] - lo : 0;
+                // tasks of this chunk: entry j has ceil(deg / 32) of them
+                // (deg: its items in this window), numbered from the
+                // exclusive prefix sum pre
+                // (windows without offsets walk the whole row; `add` keeps
+                // the window's targets)
+                int lo, hiw;
+                if (ONEWIN || nwin == 0) {
+                    lo = sptr[ck];
+                    hiw = sptr[ck + 1];
+                } else {
+                    lo = woff[(size_t)ck * (nwin + 1) + wi];
+                    hiw = woff[(size_t)ck * (nwin + 1) + wi + 1];
+                }
+                const int deg = lane < cnt ? hiw - lo : 0;
                 const int nt = (deg + 31) >> 5;
                 int pre, T;
                 if (!__any(nt > 1)) {   // at most one task per entry: a ballot
@@ -817,6 +856,16 @@ __global__ __launch_bounds__(kSpThreads) void span_sparse1(DevTable d, StepView 
                 for (int u = 0; u < 4; ++u)
                     if (v[u] > 0.f && cv[u] > kNeg) emax = max(emax, fexp(v[u]) + cv[u]);
             }
+            if (extract && s < S) {
+                // the row's values at the `out` pattern's targets in this window
+                const bool whole = ONEWIN || nwin == 0;
+                const int oa = whole ? optr[s] : owoff[(size_t)s * (nwin + 1) + wi];
+                const int ob = whole ? optr[s + 1] : owoff[(size_t)s * (nwin + 1) + wi + 1];
+                for (int e = oa + lane; e < ob; e += 64) {
+                    const int c = ofar[tr ? operm[e] : e] - w0;
+                    if ((unsigned)c < (unsigned)wn) vout[e] = bufw[c] + bufw[win + c];
+                }
+            }
         }
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) emax = max(emax, __shfl_xor(emax, o));
@@ -824,57 +873,121 @@ __global__ __launch_bounds__(kSpThreads) void span_sparse1(DevTable d, StepView 
     }
 }
 
-// LDS bytes of span_sparse1: per wave two row buffers and the tasks; the
+// The second level's operands: the first-level nodes' values on the
+// two-step pattern, folded in place as the dense kernels fold them (value
+// times 2^(co - rf) of its stored column and row), one position per thread.
+__global__ void sparse_fold(DevTable d, StepView sv, SpPat pat, float *__restrict__ v,
+                            const int32_t *__restrict__ meta, int nodes)
+{
+    const int e = blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= pat.np) return;
+    for (int y = blockIdx.y; y < sv.B * nodes; y += gridDim.y) {
+        const int b = y / nodes, j = y % nodes;
+        const int n = (sv.Lpad >> 1) + j;
+        const bool tr = stored_transposed(n);
+        const int q = tr ? pat.col_pairs[e] : e;
+        const int row = tr ? pat.pb[q] : pat.pa[q], col = tr ? pat.pa[q] : pat.pb[q];
+        const int32_t *co = sv.meta_ptr(meta, b, n, 1);
+        const int32_t *rf = sv.meta_ptr(meta, b, n, 2);
+        float *x = v + ((size_t)b * nodes + j) * pat.np + e;
+        *x = ldexpf(*x, co[col] - rf[row]);
+    }
+}
+
+// LDS bytes of span_sparse: per wave two row buffers and the tasks; the
 // product's column exponents and the walk's row pointers; with staging the
 // second operand's folded values and 16-bit targets
-size_t sparse1_lds(const DevTable &d, int Sp, int win, bool staged)
+size_t sparse_lds(const DevTable &d, int Sp, int np, int win, bool staged)
 {
     const int tcap = staged ? kSpTasks : kSpTasks / 2;
     size_t b = (size_t)kSpWaves * (2 * win + 4 * (tcap + kSpTaskPad)) * sizeof(float);
     b += ((size_t)Sp + ((d.S + 4) & ~3)) * sizeof(int32_t);
     if (staged)
-        b += (size_t)d.npairs * sizeof(float) + (((size_t)d.npairs * sizeof(uint16_t) + 15) & ~size_t(15));
+        b += (size_t)np * sizeof(float) + (((size_t)np * sizeof(uint16_t) + 15) & ~size_t(15));
     return b;
 }
 
-int launch_sparse1(const DevTable &d, const Geometry &g, StepView sv, const float *pvf, float *tree,
-                   int32_t *meta, hipStream_t st)
+SpPat pattern1(const DevTable &d)
 {
-    // staged with the widest window that fits, else unstaged likewise
-    int win = 0;
-    bool staged = false;
-    for (bool stg : {true, false}) {
-        if (stg && g.Sp > 65536) continue;
-        for (int w : {std::min(g.Sp, 1024), std::min(g.Sp, 512), std::min(g.Sp, 256)})
-            if (sparse1_lds(d, g.Sp, w, stg) <= kSparseLdsMax) {
+    return SpPat{d.row_ptr, d.col_ptr, d.pair_a, d.pair_b, d.col_pairs, d.pair_colpos,
+                 d.w1_n, d.w1_t, d.npairs};
+}
+
+SpPat pattern2(const DevTable &d)
+{
+    return SpPat{d.p2_row_ptr, d.p2_col_ptr, d.p2_a, d.p2_b, d.p2_col_pairs, d.p2_colpos,
+                 d.w2_n, d.w2_t, d.np2};
+}
+
+int launch_sparse(const DevTable &d, const Geometry &g, StepView sv, SpLevel lv, float *tree,
+                  int32_t *meta, hipStream_t st)
+{
+    // rows wider than kSpWin columns take kSpWin-column windows (the
+    // per-window offsets are built for them); narrower rows one window, or
+    // 512 or 256 columns (each window walking the whole row) when that lets
+    // the second operand be staged
+    int win = g.Sp > kSpWin ? kSpWin : g.Sp;
+    bool staged = g.Sp <= 65536 && sparse_lds(d, g.Sp, lv.in.np, win, true) <= kSparseLdsMax;
+    if (!staged && g.Sp <= kSpWin)
+        for (int w : {512, 256})
+            if (w < g.Sp && sparse_lds(d, g.Sp, lv.in.np, w, true) <= kSparseLdsMax) {
                 win = w;
-                staged = stg;
+                staged = true;
                 break;
             }
-        if (win) break;
-    }
-    if (!win) return (int)hipErrorInvalidConfiguration;
-    const size_t lds = sparse1_lds(d, g.Sp, win, staged);
-    const long long grid = (long long)g.B * (g.Lpad >> 1) * ((g.Sp + kSpRows - 1) / kSpRows);
+    const size_t lds = sparse_lds(d, g.Sp, lv.in.np, win, staged);
+    if (lds > kSparseLdsMax) return (int)hipErrorInvalidConfiguration;
+    lv.win = win;
+    lv.tcap = staged ? kSpTasks : kSpTasks / 2;
+    lv.nwin = g.Sp > kSpWin ? d.nwin : 0;
+    const long long grid = (long long)g.B * lv.nsp * ((g.Sp + kSpRows - 1) / kSpRows);
     if (grid > 0x7fffffffLL) return (int)hipErrorInvalidConfiguration;
+    if (grid == 0) return 0;
     const bool one = win == g.Sp;
-    const void *fn = staged ? (one ? reinterpret_cast<const void *>(&span_sparse1<true, true>)
-                                   : reinterpret_cast<const void *>(&span_sparse1<true, false>))
-                            : (one ? reinterpret_cast<const void *>(&span_sparse1<false, true>)
-                                   : reinterpret_cast<const void *>(&span_sparse1<false, false>));
+    const void *fn = staged ? (one ? reinterpret_cast<const void *>(&span_sparse<true, true>)
+                                   : reinterpret_cast<const void *>(&span_sparse<true, false>))
+                            : (one ? reinterpret_cast<const void *>(&span_sparse<false, true>)
+                                   : reinterpret_cast<const void *>(&span_sparse<false, false>));
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return (int)e;
-#define FA_SPARSE1(ST, ONE) \
-    span_sparse1<ST, ONE><<<(unsigned)grid, kSpThreads, lds, st>>>(d, sv, pvf, tree, meta, win, \
-                                                                    ST ? kSpTasks : kSpTasks / 2)
+#define FA_SPARSE(ST, ONE) span_sparse<ST, ONE><<<(unsigned)grid, kSpThreads, lds, st>>>(d, sv, lv, tree, meta)
     if (staged) {
-        if (one) FA_SPARSE1(true, true);
-        else FA_SPARSE1(true, false);
+        if (one) FA_SPARSE(true, true);
+        else FA_SPARSE(true, false);
     } else {
-        if (one) FA_SPARSE1(false, true);
-        else FA_SPARSE1(false, false);
+        if (one) FA_SPARSE(false, true);
+        else FA_SPARSE(false, false);
     }
-#undef FA_SPARSE1
+#undef FA_SPARSE
+    return (int)hipGetLastError();
+}
+
+// one tree level as dense products over nodes n0 .. n0 + nn - 1 of every row
+int launch_dense_level(const Geometry &g, StepView sv, int k, int n0, int nn, float *tree,
+                       int32_t *meta, uint8_t *ws, const WsLayout &w, hipStream_t st)
+{
+    if (nn <= 0) return 0;
+    const int tiles = g.Sp / kTile;
+    const int big_tiles = g.Sp / kBig;
+    const long long big_wgs = (long long)g.B * nn * big_tiles * big_tiles;
+    const int ks = tree_ksplit(g, k);
+    const int huge_tiles = g.Sp / kHuge;
+    const long long huge_wgs = (long long)g.B * nn * huge_tiles * huge_tiles;
+    if (ks == 1 && g.Sp % kHuge == 0 && huge_wgs >= 256) {
+        span_gemm256<<<(unsigned)huge_wgs, kHugeThreads, 0, st>>>(sv, tree, meta, n0, nn);
+    } else if (ks == 1 && g.Sp % kBig == 0 && big_wgs >= 256) {
+        span_gemm128<<<(unsigned)big_wgs, kBigThreads, 0, st>>>(sv, tree, meta, n0, nn);
+    } else {
+        float *part = (float *)(ws + w.kpart);
+        dim3 grid(tiles * tiles * ks, g.B * nn);
+        span_gemm<<<grid, kGemmThreads, 0, st>>>(sv, tree, meta, n0, nn, ks, part);
+        if (ks > 1) {
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return (int)e;
+            dim3 rgrid(tiles * tiles, g.B * nn);
+            span_reduce<<<rgrid, kGemmThreads, 0, st>>>(sv, tree, meta, n0, nn, ks, part);
+        }
+    }
     return (int)hipGetLastError();
 }
 
@@ -896,38 +1009,50 @@ int launch_span_tree(const DevTable &d, const Geometry &g, float *tree, int32_t 
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
     }
-    const int tiles = g.Sp / kTile;
+    const float *pvf = (const float *)(ws + w.pvf);
+    float *pv2 = (float *)(ws + w.pv2);
+    const bool sparse1 = d.first_sparse && d.npairs > 0;
+    // second level from the two-step pattern: its products whose four
+    // leaves are all inside the sequence (the rest, if any, dense)
+    const int nsp2 = d.second_sparse && d.np2 > 0 && sparse1 && g.K >= 2 ? g.L / 4 : 0;
     for (int k = 1; k <= g.K; ++k) {
         const int n0 = g.Lpad >> k, nn = n0;
-        const int big_tiles = g.Sp / kBig;
-        const long long big_wgs = (long long)g.B * nn * big_tiles * big_tiles;
-        const int ks = tree_ksplit(g, k);
         if (k == 1) {
             const int pe = prof_mark(FA_PROF_TREE_LEVEL1, true, stream);
             if (pe) return pe;
         }
-        const int huge_tiles = g.Sp / kHuge;
-        const long long huge_wgs = (long long)g.B * nn * huge_tiles * huge_tiles;
-        if (k == 1 && d.first_sparse && d.npairs > 0) {
-            const int se = launch_sparse1(d, g, sv, (const float *)(ws + w.pvf), tree, meta, st);
-            if (se) return se;
-        } else if (ks == 1 && g.Sp % kHuge == 0 && huge_wgs >= 256) {
-            span_gemm256<<<(unsigned)huge_wgs, kHugeThreads, 0, st>>>(sv, tree, meta, n0, nn);
-        } else if (ks == 1 && g.Sp % kBig == 0 && big_wgs >= 256) {
-            span_gemm128<<<(unsigned)big_wgs, kBigThreads, 0, st>>>(sv, tree, meta, n0, nn);
-        } else {
-            float *part = (float *)(ws + w.kpart);
-            dim3 grid(tiles * tiles * ks, g.B * nn);
-            span_gemm<<<grid, kGemmThreads, 0, st>>>(sv, tree, meta, n0, nn, ks, part);
-            if (ks > 1) {
-                hipError_t e = hipGetLastError();
-                if (e != hipSuccess) return (int)e;
-                dim3 rgrid(tiles * tiles, g.B * nn);
-                span_reduce<<<rgrid, kGemmThreads, 0, st>>>(sv, tree, meta, n0, nn, ks, part);
+        int e = 0;
+        if (k == 1 && sparse1) {
+            SpLevel lv{};
+            lv.in = pattern1(d);
+            if (nsp2 > 0) lv.out = pattern2(d);
+            lv.vin = pvf;
+            lv.vout = pv2;
+            lv.vin_nodes = g.L;
+            lv.vout_nodes = g.Lpad / 2;
+            lv.level = 1;
+            lv.n0 = n0;
+            lv.nsp = nn;
+            e = launch_sparse(d, g, sv, lv, tree, meta, st);
+            if (!e && nsp2 > 0) {
+                dim3 fgrid((d.np2 + 255) / 256, std::min(g.B * (g.Lpad / 2), 65535));
+                sparse_fold<<<fgrid, 256, 0, st>>>(d, sv, pattern2(d), pv2, meta, g.Lpad / 2);
+                e = (int)hipGetLastError();
             }
+        } else if (k == 2 && nsp2 > 0) {
+            SpLevel lv{};
+            lv.in = pattern2(d);
+            lv.vin = pv2;
+            lv.vin_nodes = g.Lpad / 2;
+            lv.level = 2;
+            lv.n0 = n0;
+            lv.nsp = nsp2;
+            e = launch_sparse(d, g, sv, lv, tree, meta, st);
+            if (!e) e = launch_dense_level(g, sv, k, n0 + nsp2, nn - nsp2, tree, meta, ws, w, st);
+        } else {
+            e = launch_dense_level(g, sv, k, n0, nn, tree, meta, ws, w, st);
         }
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return (int)e;
+        if (e) return e;
         if (k == 1) {
             const int pe = prof_mark(FA_PROF_TREE_LEVEL1, false, stream);
             if (pe) return pe;

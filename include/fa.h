@@ -81,7 +81,9 @@ enum {
     FA_LABEL_RANGES = 4, /* label_tok holds flat half-open [lo, hi) pairs */
     FA_NO_TRIM = 8,      /* keep states unreachable from s0 or unable to reach F */
     FA_FIRST_LEVEL_SPARSE = 16, /* first span level from the pair values (row combination) */
-    FA_FIRST_LEVEL_DENSE = 32   /* first span level as dense matrix products */
+    FA_FIRST_LEVEL_DENSE = 32,  /* first span level as dense matrix products */
+    FA_SECOND_LEVEL_SPARSE = 64 /* also the second level from the two-step pattern (needs the
+                                   first level sparse) */
 };
 
 enum { FA_CONF_PROB = 0, FA_CONF_NEGENT = 1 };
@@ -102,7 +104,11 @@ enum { FA_CONF_PROB = 0, FA_CONF_NEGENT = 1 };
  *   flags           FA_DFA | FA_NFA | FA_LABEL_RANGES | FA_NO_TRIM, and at
  *                   most one of FA_FIRST_LEVEL_SPARSE / FA_FIRST_LEVEL_DENSE
  *                   (how fa_span_tree forms the first level; default: the
- *                   sparse form when its work is at most 1/256 of S^3)
+ *                   sparse form when its work is at most 1/256 of S^3), and
+ *                   FA_SECOND_LEVEL_SPARSE (the second level likewise, over
+ *                   the pairs (a, c) joined through some k; default: when
+ *                   the first is sparse and its own work is at most 1/256 of
+ *                   S^3)
  *   out             receives the handle (free with fa_table_destroy)
  *   device_bytes    receives the size of the device image
  * Dead states (unreachable from s0 or unable to reach F) are removed unless
@@ -134,7 +140,9 @@ void fa_table_destroy(fa_table *t);
  * [12] 1 if LIST entries index the selected-token gather, [13] V,
  * [14] S (original), [15] 1 if fa_span_tree forms the first level from the
  * pair values, [16] that form's multiply-adds per first-level product (the
- * number of pairs (a, k), (k, c) sharing k).  Returns FA_OK or FA_EINVAL.
+ * number of pairs (a, k), (k, c) sharing k), [17] 1 if the second level is
+ * formed likewise, [18] its multiply-adds per product, [19] the pairs of the
+ * two-step pattern it uses.  Returns FA_OK or FA_EINVAL.
  */
 int fa_table_info(const fa_table *t, int64_t *info, int32_t n);
 

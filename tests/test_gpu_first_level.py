@@ -1,13 +1,16 @@
-"""GPU parity of the sparse first span level: the level-1 products formed
-from the pair values (row combination over pairs (a, k), (k, c)) instead of
-dense matrix products.  Every workload of the step parity suite runs with the
-sparse form forced; the whole step is checked against the fp64 oracle, and
-the level-1 nodes against the oracle's products M_2j M_2j+1."""
+"""GPU parity of the sparse span levels: the level-1 products formed from the
+pair values (row combination over pairs (a, k), (k, c)) instead of dense
+matrix products, and the level-2 products likewise over the two-step
+pattern.  Every workload of the step parity suite runs with the sparse forms
+forced; the whole step is checked against the fp64 oracle, and the level-1
+and level-2 nodes against the oracle's products of 2 and 4 leaves."""
 import numpy as np
 import pytest
 
 import oracle
 from tests import parity as PT
+from synth import automata as A
+from synth import configs
 from tests.test_gpu_parity import CASES
 
 pytestmark = pytest.mark.gpu
@@ -35,12 +38,13 @@ def _node(w, g, b, n):
     return T[:S, :S]
 
 
-def _check_level1(w, g, b, orc):
+def _check_level1(w, g, b, orc, level=1):
     tb = g["table"]
     orig = tb.orig
     S = len(orig)
     Lpad = 1 << max(0, (w.L - 1).bit_length())
-    if Lpad < 2:
+    span = 1 << level
+    if Lpad < span:
         return
     W = orc.edge_weights(w.p[b])
 
@@ -49,13 +53,15 @@ def _check_level1(w, g, b, orc):
             return np.eye(S)
         return orc.dense_M(W, i)[np.ix_(orig, orig)]
 
-    for j in range(Lpad // 2):
-        want = M(2 * j) @ M(2 * j + 1)
-        got = _node(w, g, b, Lpad // 2 + j)
+    for j in range(Lpad // span):
+        want = M(span * j)
+        for i in range(span * j + 1, span * j + span):
+            want = want @ M(i)
+        got = _node(w, g, b, Lpad // span + j)
         scale = want.max(axis=1, keepdims=True)
         err = np.abs(got - want)
         bad = err > NODE_RTOL * want + 1e-30 * scale
-        assert not bad.any(), (f"row {b} node {Lpad // 2 + j}: {bad.sum()} entries off, worst "
+        assert not bad.any(), (f"row {b} node {Lpad // span + j}: {bad.sum()} entries off, worst "
                                f"rel {np.max(err / np.maximum(want, 1e-300))}")
 
 
@@ -91,3 +97,30 @@ def test_sparse_and_dense_first_level_agree(name):
     # of a boundary; the oracle replay in the parity test bounds those
     same = (gs["tokens"] == gd["tokens"]).mean()
     assert same > 0.99, same
+
+
+def _nfa_wide():
+    # more than 1024 states: rows of both sparse levels span two 1024-column
+    # windows
+    aut = configs._draw(lambda r: A.random_nfa(r, 1500, 3000, 9000, 8, 12.0), 8201, 8)
+    return configs.from_automaton(aut, 1, 8, "normal4", 0, 8300, "nfa wide")
+
+
+SECOND = dict(CASES, **{"nfa-wide": _nfa_wide})
+
+
+@pytest.mark.parametrize("name", list(SECOND))
+def test_sparse_second_level_parity(name):
+    import constrained_decoding_diffusion_amd as fa
+    w = SECOND[name]()
+    tb = fa.Table.from_automaton(w.aut, first_level="sparse2")
+    assert tb.info["first_sparse"] == 1 and tb.info["second_sparse"] == 1
+    PT.log(f"[second-level] {name}: {w.describe()}, two-step pairs {tb.info['pairs2']}, "
+           f"work {tb.info['second_work']}")
+    g = PT.run_gpu(w, table=tb)
+    orc = oracle.Oracle(w.aut)
+    for b in range(w.B):
+        PT.check_row(w, g, b, orc)
+    _check_level1(w, g, 0, orc, level=1)
+    _check_level1(w, g, 0, orc, level=2)
+    PT.log(f"[second-level] {name}: ok")

@@ -66,7 +66,10 @@ def test_invalid_ranges_and_flags():
     assert _code(lambda: _compile(2, 10, 0, [1], [(0, 1, [0, 11])], R)) == _fa.FA_EINVAL
     assert _code(lambda: _compile(2, 10, 0, [1], [(0, 1, [0, 5, 3, 7])], R)) == _fa.FA_EINVAL
     assert _code(lambda: _compile(2, 10, 0, [1], [(0, 1, [1])], fa.FA_DFA | fa.FA_NFA)) == _fa.FA_EINVAL
-    assert _code(lambda: _compile(2, 10, 0, [1], [(0, 1, [1])], 64)) == _fa.FA_EINVAL
+    assert _code(lambda: _compile(2, 10, 0, [1], [(0, 1, [1])], 128)) == _fa.FA_EINVAL
+    # the sparse second level needs the sparse first level
+    assert _code(lambda: _compile(2, 10, 0, [1], [(0, 1, [1])], fa.FA_DFA | fa.FA_FIRST_LEVEL_DENSE
+                                  | fa.FA_SECOND_LEVEL_SPARSE)) == _fa.FA_EINVAL
     # decreasing label offsets
     with pytest.raises(fa.FaError):
         fa.Table(2, 10, 0, [1], [0], [1], np.array([0, -1], np.int64), np.zeros(0, np.int32), 1)
