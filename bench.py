@@ -60,19 +60,27 @@ def algorithmic_work(tb, B, L):
     leaves = B * Lpad * S * S * 4
     internal = B * (Lpad - 1) * S * S * 4
     sparse1 = bool(tb.info["first_sparse"])
+    sparse2 = sparse1 and bool(tb.info["second_sparse"]) and K >= 2
     npairs, w1 = tb.info["pairs"], tb.info["first_work"]
+    npairs2, w2 = tb.info["pairs2"], tb.info["second_work"]
     # first level: dense 2*S^3 per product, or the sparse form's multiply-adds
-    # (pairs (a, k), (k, c) sharing k) per product
+    # (pairs (a, k), (k, c) sharing k) per product; second level likewise for
+    # its L//4 products inside the sequence when it is sparse
     level1_flops = B * (Lpad // 2) * (2.0 * w1 if sparse1 else 2.0 * S ** 3)
-    level1 = (dict(bound="hbm", work=B * (Lpad // 2) * (S * S * 4 + 2 * npairs * 4), unit="GB/s",
+    nsp2 = L // 4 if sparse2 else 0
+    level2_flops = B * (nsp2 * 2.0 * w2 + (Lpad // 4 - nsp2) * 2.0 * S ** 3) if K >= 2 else 0.0
+    upper_flops = 2.0 * S ** 3 * B * max(Lpad // 4 - 1, 0)
+    out2 = npairs2 * 4 if sparse2 else 0
+    level1 = (dict(bound="hbm", work=B * (Lpad // 2) * (S * S * 4 + 2 * npairs * 4 + out2), unit="GB/s",
                    per_unit="per product: the dense S*S output write + both leaves' pair values "
-                            "(2*pairs*4), B*Lpad/2 products")
+                            "(2*pairs*4) + its values on the two-step pattern when the second "
+                            "level is sparse (pairs2*4), B*Lpad/2 products")
               if sparse1 else
               dict(bound="mfma", work=2.0 * S ** 3 * B * (Lpad // 2), unit="TFLOP/s",
                    per_unit="2*S^3 per product (S trimmed states), B*Lpad/2 products"))
     return dict(
         a1_bytes=p_bytes + table_bytes + leaves,
-        a2_flops=2.0 * S ** 3 * B * (Lpad // 2 - 1) + level1_flops,
+        a2_flops=level1_flops + level2_flops + upper_flops,
         a4_bytes=p_bytes + p_bytes + leaves + internal + table_bytes,
         # per launch of the kernels the library can bracket with events
         kernels={
