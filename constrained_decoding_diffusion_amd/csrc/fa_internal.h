@@ -108,6 +108,7 @@ struct DevTable {
     int32_t nwin;                // kSpWin-column windows of a row (0: one window of Sp <= kSpWin)
     const int32_t *p2_a, *p2_b, *p2_row_ptr, *p2_col_ptr, *p2_col_pairs, *p2_colpos;
     const int32_t *w1_n, *w1_t, *w2_n, *w2_t;
+    const int32_t *col_a, *p2_col_a;   // a of each column-order entry (column walk targets)
     const uint32_t *dense_bits;  // [ndense][dense_words] bit v%32 of word v/32: v in the label
     int32_t dense_words;
     const int32_t *ev_a;       // [2 nseg] per cut event (cut_ev order): the states of its pair
@@ -150,6 +151,7 @@ struct HostTable {
     // two-step pattern: pairs (a, c) joined by pairs (a, k), (k, c), sorted
     // (a, c), with the same row/column orders as the pairs (second level)
     std::vector<int32_t> p2_a, p2_b, p2_row_ptr, p2_col_ptr, p2_col_pairs, p2_colpos;
+    std::vector<int32_t> col_a, p2_col_a;   // column walks' targets: a of each column-order entry
     bool second_sparse = false;
     int64_t second_work = 0;    // multiply-adds per second-level product
     // entry offsets of each state's row walk (_n) and column walk (_t) at
@@ -186,6 +188,7 @@ struct WsLayout {
     size_t dpart = 0, dval = 0, psel = 0, cutp = 0, val = 0;  // emission reduce
     size_t pvf = 0;                            // folded leaf pair values (sparse first level)
     size_t pv2 = 0;                            // first-level nodes on the two-step pattern (second level)
+    size_t pv2alt = 0;                         // the same values in each node's other walk order
     int32_t n_vchunks = 0;                     // dense-mask contraction: V split
     int32_t vchunk = 0;                        // tokens per V chunk (multiple of 256)
     int32_t sel_mode = 0;                      // token-list copy: 1 LDS-buffered, 2 gathered

@@ -95,6 +95,8 @@ void build_image(HostTable &t)
     append_section(t.image, t.offs, t.w1_t);
     append_section(t.image, t.offs, t.w2_n);
     append_section(t.image, t.offs, t.w2_t);
+    append_section(t.image, t.offs, t.col_a);
+    append_section(t.image, t.offs, t.p2_col_a);
     t.image.resize((t.image.size() + 255) & ~size_t(255));
 }
 
@@ -141,6 +143,7 @@ DevTable HostTable::device_view() const
     nxt(d.pair_colpos);
     nxt(d.p2_a); nxt(d.p2_b); nxt(d.p2_row_ptr); nxt(d.p2_col_ptr); nxt(d.p2_col_pairs);
     nxt(d.p2_colpos); nxt(d.w1_n); nxt(d.w1_t); nxt(d.w2_n); nxt(d.w2_t);
+    nxt(d.col_a); nxt(d.p2_col_a);
     d.second_sparse = second_sparse ? 1 : 0;
     d.np2 = (int32_t)p2_a.size();
     d.nwin = nwin;
@@ -276,7 +279,9 @@ WsLayout ws_layout(const HostTable &t, const Geometry &g)
     w.tcs_ok = o; o = al(o + (joint ? BL * sizeof(int32_t) : 0));
     // first-level nodes on the two-step pattern: written by the first level,
     // read by the second, apart from every per-call region
-    w.pv2 = o; o = al(o + (t.second_sparse ? (size_t)g.B * (g.Lpad / 2) * t.p2_a.size() * sizeof(float) : 0));
+    const size_t n2 = t.second_sparse ? (size_t)g.B * (g.Lpad / 2) * t.p2_a.size() : 0;
+    w.pv2 = o; o = al(o + n2 * sizeof(float));
+    w.pv2alt = o; o = al(o + n2 * sizeof(float));
     w.total = o;
     if (w.total == 0) w.total = 256;
     return w;
@@ -762,6 +767,7 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
     t.p2_a.clear(); t.p2_b.clear(); t.p2_row_ptr.clear(); t.p2_col_ptr.clear();
     t.p2_col_pairs.clear(); t.p2_colpos.clear();
     t.w1_n.clear(); t.w1_t.clear(); t.w2_n.clear(); t.w2_t.clear();
+    t.col_a.clear(); t.p2_col_a.clear();
     t.second_sparse = false;
     t.second_work = 0;
     t.nwin = t.Sp > kSpWin ? (t.Sp + kSpWin - 1) / kSpWin : 0;
@@ -788,6 +794,10 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
             t.p2_a.clear(); t.p2_b.clear(); t.p2_row_ptr.clear(); t.p2_col_ptr.clear();
             t.p2_col_pairs.clear(); t.p2_colpos.clear();
         }
+        t.col_a.resize(np);
+        for (int32_t k = 0; k < np; ++k) t.col_a[k] = t.pair_a[t.col_pairs[k]];
+        t.p2_col_a.resize(t.p2_a.size());
+        for (size_t k = 0; k < t.p2_a.size(); ++k) t.p2_col_a[k] = t.p2_a[t.p2_col_pairs[k]];
     } else if (flags & FA_SECOND_LEVEL_SPARSE) {
         return FA_EINVAL;
     }

@@ -607,6 +607,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // both walks when rows span several windows
 struct SpPat {
     const int32_t *row_ptr, *col_ptr, *pa, *pb, *col_pairs, *colpos, *wn, *wt;
+    const int32_t *cola;   // a of each column-order entry
     int32_t np;
 };
 
@@ -614,6 +615,7 @@ struct SpLevel {
     SpPat in;              // the operands' pattern
     SpPat out;             // pattern whose values are taken from the output (out.np = 0: none)
     const float *vin;      // folded operand values, [B][vin_nodes][in.np], stored entry order
+    const float *valt;     // the same in each node's other walk order, or nullptr
     float *vout;           // raw output values on `out`, [B][vout_nodes][out.np]
     int vin_nodes, vout_nodes;
     int level, n0, nsp;    // products: nodes n0 .. n0 + nsp - 1 of every row
@@ -649,14 +651,16 @@ __global__ __launch_bounds__(kSpThreads) void span_sparse(DevTable d, StepView s
     const float *vG = lv.vin + ((size_t)b * lv.vin_nodes + (realG ? iG : 0)) * np;
     const int32_t *ptr = tr ? lv.in.col_ptr : lv.in.row_ptr;
     const int32_t *far = tr ? lv.in.pa : lv.in.pb;
+    const int32_t *wfar = tr ? lv.in.cola : lv.in.pb;   // target of walk entry e
     const int32_t *perm = tr ? lv.in.col_pairs : lv.in.colpos;
+    // the second operand's values in its walk order (other than its stored one)
+    const float *vGw = lv.valt ? lv.valt + ((size_t)b * lv.vin_nodes + iG) * np : nullptr;
     const int32_t *woff = tr ? lv.in.wt : lv.in.wn;
     const int npc = np - 1;
     // output values on the `out` pattern, in this node's stored entry order
     const bool extract = lv.out.np > 0 && realF && realG;
     const int32_t *optr = tr ? lv.out.col_ptr : lv.out.row_ptr;
-    const int32_t *ofar = tr ? lv.out.pa : lv.out.pb;
-    const int32_t *operm = tr ? lv.out.col_pairs : nullptr;
+    const int32_t *ofar = tr ? lv.out.cola : lv.out.pb;
     const int32_t *owoff = tr ? lv.out.wt : lv.out.wn;
     float *vout = extract ? lv.vout + ((size_t)b * lv.vout_nodes + (n - lv.n0)) * lv.out.np : nullptr;
     float *D = sv.mat_ptr(tree, b, n);
@@ -678,10 +682,12 @@ __global__ __launch_bounds__(kSpThreads) void span_sparse(DevTable d, StepView s
         if (STAGED) {
             t = stt[e];
             x2 = sx[e];
+        } else if (vGw) {
+            t = wfar[e];
+            x2 = vGw[e];
         } else {
-            const int q = tr ? perm[e] : e;     // pair id
-            t = far[tr ? q : e];
-            x2 = vG[tr ? q : perm[e]];
+            t = wfar[e];
+            x2 = vG[perm[e]];
         }
     };
     // item index: staged reads of an empty task's items stay inside the LDS
@@ -746,7 +752,7 @@ __global__ __launch_bounds__(kSpThreads) void span_sparse(DevTable d, StepView s
         r.e1 = has ? (realF ? sptr[sc + 1] : 1) : 0;
         const int ei = min(r.e0 + lane, npc);
         r.x = vF[ei];
-        r.k = STAGED ? 0 : far[tr ? perm[ei] : ei];
+        r.k = STAGED ? 0 : wfar[ei];
         r.rf = rfF[min(s, Sp - 1)];
         return r;
     };
@@ -769,7 +775,7 @@ __global__ __launch_bounds__(kSpThreads) void span_sparse(DevTable d, StepView s
                 if (eb != e0) {   // rows with more than 64 entries
                     const int ei = min(eb + lane, npc);
                     cx = vF[ei];
-                    ck = STAGED ? (int)stt[ei] : far[tr ? perm[ei] : ei];
+                    ck = STAGED ? (int)stt[ei] : wfar[ei];
                 }
                 if (!realG) {
                     // identity second operand: entry k adds x1 2^-rf[k] at column k
@@ -862,7 +868,7 @@ __global__ __launch_bounds__(kSpThreads) void span_sparse(DevTable d, StepView s
                 const int oa = whole ? optr[s] : owoff[(size_t)s * (nwin + 1) + wi];
                 const int ob = whole ? optr[s + 1] : owoff[(size_t)s * (nwin + 1) + wi + 1];
                 for (int e = oa + lane; e < ob; e += 64) {
-                    const int c = ofar[tr ? operm[e] : e] - w0;
+                    const int c = ofar[e] - w0;
                     if ((unsigned)c < (unsigned)wn) vout[e] = bufw[c] + bufw[win + c];
                 }
             }
@@ -875,9 +881,10 @@ __global__ __launch_bounds__(kSpThreads) void span_sparse(DevTable d, StepView s
 
 // The second level's operands: the first-level nodes' values on the
 // two-step pattern, folded in place as the dense kernels fold them (value
-// times 2^(co - rf) of its stored column and row), one position per thread.
+// times 2^(co - rf) of its stored column and row), and copied in the node's
+// other walk order (the order the second level reads a second operand in).
 __global__ void sparse_fold(DevTable d, StepView sv, SpPat pat, float *__restrict__ v,
-                            const int32_t *__restrict__ meta, int nodes)
+                            float *__restrict__ valt, const int32_t *__restrict__ meta, int nodes)
 {
     const int e = blockIdx.x * blockDim.x + threadIdx.x;
     if (e >= pat.np) return;
@@ -889,8 +896,11 @@ __global__ void sparse_fold(DevTable d, StepView sv, SpPat pat, float *__restric
         const int row = tr ? pat.pb[q] : pat.pa[q], col = tr ? pat.pa[q] : pat.pb[q];
         const int32_t *co = sv.meta_ptr(meta, b, n, 1);
         const int32_t *rf = sv.meta_ptr(meta, b, n, 2);
-        float *x = v + ((size_t)b * nodes + j) * pat.np + e;
-        *x = ldexpf(*x, co[col] - rf[row]);
+        const size_t base = ((size_t)b * nodes + j) * pat.np;
+        const float x = ldexpf(v[base + e], co[col] - rf[row]);
+        v[base + e] = x;
+        // the other walk order: column position of pair e, or pair q
+        valt[base + (tr ? q : pat.colpos[e])] = x;
     }
 }
 
@@ -910,13 +920,13 @@ size_t sparse_lds(const DevTable &d, int Sp, int np, int win, bool staged)
 SpPat pattern1(const DevTable &d)
 {
     return SpPat{d.row_ptr, d.col_ptr, d.pair_a, d.pair_b, d.col_pairs, d.pair_colpos,
-                 d.w1_n, d.w1_t, d.npairs};
+                 d.w1_n, d.w1_t, d.col_a, d.npairs};
 }
 
 SpPat pattern2(const DevTable &d)
 {
     return SpPat{d.p2_row_ptr, d.p2_col_ptr, d.p2_a, d.p2_b, d.p2_col_pairs, d.p2_colpos,
-                 d.w2_n, d.w2_t, d.np2};
+                 d.w2_n, d.w2_t, d.p2_col_a, d.np2};
 }
 
 int launch_sparse(const DevTable &d, const Geometry &g, StepView sv, SpLevel lv, float *tree,
@@ -1011,6 +1021,7 @@ int launch_span_tree(const DevTable &d, const Geometry &g, float *tree, int32_t 
     }
     const float *pvf = (const float *)(ws + w.pvf);
     float *pv2 = (float *)(ws + w.pv2);
+    float *pv2alt = (float *)(ws + w.pv2alt);
     const bool sparse1 = d.first_sparse && d.npairs > 0;
     // second level from the two-step pattern: its products whose four
     // leaves are all inside the sequence (the rest, if any, dense)
@@ -1036,13 +1047,14 @@ int launch_span_tree(const DevTable &d, const Geometry &g, float *tree, int32_t 
             e = launch_sparse(d, g, sv, lv, tree, meta, st);
             if (!e && nsp2 > 0) {
                 dim3 fgrid((d.np2 + 255) / 256, std::min(g.B * (g.Lpad / 2), 65535));
-                sparse_fold<<<fgrid, 256, 0, st>>>(d, sv, pattern2(d), pv2, meta, g.Lpad / 2);
+                sparse_fold<<<fgrid, 256, 0, st>>>(d, sv, pattern2(d), pv2, pv2alt, meta, g.Lpad / 2);
                 e = (int)hipGetLastError();
             }
         } else if (k == 2 && nsp2 > 0) {
             SpLevel lv{};
             lv.in = pattern2(d);
             lv.vin = pv2;
+            lv.valt = pv2alt;
             lv.vin_nodes = g.Lpad / 2;
             lv.level = 2;
             lv.n0 = n0;
