@@ -150,7 +150,7 @@ def level1_name(tb):
 # measured kernels: how to find their dispatches in rocprofv3 output
 KERNEL_MATCH = {
     "emission_dense": lambda n: "emission_dense<" in n,
-    "span_sparse1": lambda n: "span_sparse1" in n,
+    "span_sparse1": lambda n: "span_sparse<" in n,    # first level: first launch after tree_init_rf
     "span_gemm_level1": lambda n: "span_gemm" in n,   # first of the family after tree_init_rf
     "marg_q": lambda n: "marg_q" in n,
 }
@@ -159,10 +159,10 @@ KERNEL_MATCH = {
 def _select(rows, name):
     """Dispatches of one measured kernel, in dispatch order; for the tree
     products only the first level (the first product launch after each
-    tree_init_rf)."""
+    tree_init_rf, dense or sparse)."""
     rows = sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
     match = KERNEL_MATCH[name]
-    if name != "span_gemm_level1":
+    if name not in ("span_gemm_level1", "span_sparse1"):
         return [r for r in rows if match(r["Kernel_Name"])]
     out, armed = [], False
     for r in rows:
