@@ -105,7 +105,8 @@ struct DevTable {
     int32_t first_sparse;        // 1: the first span level is formed from the pair values
     int32_t second_sparse;       // 1: so is the second, from the two-step pattern
     int32_t np2;                 // pairs of the two-step pattern
-    int32_t nwin;                // kSpWin-column windows of a row (0: one window of Sp <= kSpWin)
+    int32_t nwin;                // win_cols-column windows of a row (0: one window)
+    int32_t win_cols;            // kSpWin for Sp > kSpWin, kSpWin / 2 for Sp > kSpWin / 2
     const int32_t *p2_a, *p2_b, *p2_row_ptr, *p2_col_ptr, *p2_col_pairs, *p2_colpos;
     const int32_t *w1_n, *w1_t, *w2_n, *w2_t;
     const int32_t *col_a, *p2_col_a;   // a of each column-order entry (column walk targets)
@@ -155,9 +156,9 @@ struct HostTable {
     bool second_sparse = false;
     int64_t second_work = 0;    // multiply-adds per second-level product
     // entry offsets of each state's row walk (_n) and column walk (_t) at
-    // every kSpWin-column window boundary, [S][nwin + 1]; only when Sp > kSpWin
+    // every window boundary, [S][nwin + 1]; only when Sp > kSpWin / 2
     std::vector<int32_t> w1_n, w1_t, w2_n, w2_t;
-    int32_t nwin = 0;
+    int32_t nwin = 0, win_cols = 0;   // windows of win_cols columns (0: one window)
     // device image
     std::vector<uint8_t> image;
     std::vector<size_t> offs;  // section offsets, in the order of DevTable pointers

@@ -147,6 +147,7 @@ DevTable HostTable::device_view() const
     d.second_sparse = second_sparse ? 1 : 0;
     d.np2 = (int32_t)p2_a.size();
     d.nwin = nwin;
+    d.win_cols = win_cols;
     d.n_tm = (int32_t)tm_pair.size();
     if (map_n.empty()) {
         d.map_n = nullptr;
@@ -328,7 +329,7 @@ static void build_two_step(HostTable &t)
 
 // for every state s and window w: the first entry of s's row walk (targets
 // ascending) and of its column walk (sources ascending) at or past column
-// w * kSpWin; [S][nwin + 1], the last the walk's end
+// w * win_cols; [S][nwin + 1], the last the walk's end
 static void window_offsets(const HostTable &t, const std::vector<int32_t> &rp,
                            const std::vector<int32_t> &cp, const std::vector<int32_t> &pa,
                            const std::vector<int32_t> &pb, const std::vector<int32_t> &cpairs,
@@ -340,7 +341,7 @@ static void window_offsets(const HostTable &t, const std::vector<int32_t> &rp,
     for (int32_t s = 0; s < S; ++s) {
         int32_t e = rp[s], f = cp[s];
         for (int32_t w = 0; w <= nw; ++w) {
-            const int64_t lim = (int64_t)w * kSpWin;
+            const int64_t lim = (int64_t)w * t.win_cols;
             while (e < rp[s + 1] && pb[e] < lim) ++e;
             while (f < cp[s + 1] && pa[cpairs[f]] < lim) ++f;
             wn[(size_t)s * (nw + 1) + w] = w == nw ? rp[s + 1] : e;
@@ -770,7 +771,10 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
     t.col_a.clear(); t.p2_col_a.clear();
     t.second_sparse = false;
     t.second_work = 0;
-    t.nwin = t.Sp > kSpWin ? (t.Sp + kSpWin - 1) / kSpWin : 0;
+    // windows: 1024 columns for wider rows, 512 for rows of 513..1024 (the
+    // width at which the sparse kernel can still stage an operand in LDS)
+    t.win_cols = t.Sp > kSpWin ? kSpWin : (t.Sp > kSpWin / 2 ? kSpWin / 2 : 0);
+    t.nwin = t.win_cols ? (t.Sp + t.win_cols - 1) / t.win_cols : 0;
     if (t.first_sparse) {
         build_two_step(t);
         int64_t w2 = 0;

@@ -932,24 +932,21 @@ SpPat pattern2(const DevTable &d)
 int launch_sparse(const DevTable &d, const Geometry &g, StepView sv, SpLevel lv, float *tree,
                   int32_t *meta, hipStream_t st)
 {
-    // rows wider than kSpWin columns take kSpWin-column windows (the
+    // rows wider than kSpWin / 2 columns take the table's windows (the
     // per-window offsets are built for them); narrower rows one window, or
-    // 512 or 256 columns (each window walking the whole row) when that lets
-    // the second operand be staged
-    int win = g.Sp > kSpWin ? kSpWin : g.Sp;
+    // 256 columns (each window walking the whole row) when that lets the
+    // second operand be staged
+    int win = d.nwin > 0 ? d.win_cols : g.Sp;
     bool staged = g.Sp <= 65536 && sparse_lds(d, g.Sp, lv.in.np, win, true) <= kSparseLdsMax;
-    if (!staged && g.Sp <= kSpWin)
-        for (int w : {512, 256})
-            if (w < g.Sp && sparse_lds(d, g.Sp, lv.in.np, w, true) <= kSparseLdsMax) {
-                win = w;
-                staged = true;
-                break;
-            }
+    if (!staged && d.nwin == 0 && g.Sp > 256 && sparse_lds(d, g.Sp, lv.in.np, 256, true) <= kSparseLdsMax) {
+        win = 256;
+        staged = true;
+    }
     const size_t lds = sparse_lds(d, g.Sp, lv.in.np, win, staged);
     if (lds > kSparseLdsMax) return (int)hipErrorInvalidConfiguration;
     lv.win = win;
     lv.tcap = staged ? kSpTasks : kSpTasks / 2;
-    lv.nwin = g.Sp > kSpWin ? d.nwin : 0;
+    lv.nwin = d.nwin;
     const long long grid = (long long)g.B * lv.nsp * ((g.Sp + kSpRows - 1) / kSpRows);
     if (grid > 0x7fffffffLL) return (int)hipErrorInvalidConfiguration;
     if (grid == 0) return 0;

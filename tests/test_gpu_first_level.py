@@ -106,7 +106,13 @@ def _nfa_wide():
     return configs.from_automaton(aut, 1, 8, "normal4", 0, 8300, "nfa wide")
 
 
-SECOND = dict(CASES, **{"nfa-wide": _nfa_wide})
+def _nfa_mid():
+    # 513..1024 states: rows walk two 512-column windows
+    aut = configs._draw(lambda r: A.random_nfa(r, 700, 3000, 5000, 8, 12.0), 8401, 8)
+    return configs.from_automaton(aut, 2, 8, "normal4", 0, 8500, "nfa mid")
+
+
+SECOND = dict(CASES, **{"nfa-wide": _nfa_wide, "nfa-mid": _nfa_mid})
 
 
 @pytest.mark.parametrize("name", list(SECOND))
