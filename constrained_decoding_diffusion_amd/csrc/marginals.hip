@@ -336,7 +336,11 @@ __device__ inline float list_weight(const DevTable &d, int s, const float *al, c
     return r;
 }
 
-// One workgroup per position streams the p row once and writes the q row.
+// nparts (1 or kQParts) workgroups per position each stream their share of
+// the p row once and write that part of the q row (short batches take
+// kQParts parts: a position per workgroup would leave most of the chip
+// idle); with FA_CONF_NEGENT and several parts each leaves its q ln q sum in
+// hpart for marg_negent_sum.
 // The dense-mask pairs' weight of a token is read from NG 256-entry tables
 // indexed by the bytes of its mask word; with SELBIT, tokens held by
 // token-list pairs carry a flag bit and add their precomputed weight (LIST
@@ -355,23 +359,32 @@ __global__ __launch_bounds__(kQThreads) void marg_q(DevTable d, StepView sv,
                                                     const float *__restrict__ vb,
                                                     const int32_t *__restrict__ eb,
                                                     const float *__restrict__ rcut,
+                                                    double *__restrict__ hpart, int nparts,
                                                     const int32_t *__restrict__ status)
 {
     __shared__ float lut[NG > 0 ? NG : 1][256];
     __shared__ float rsel[(SELBIT || LISTALL) ? kSelMax : 1];
     __shared__ double sh_h[4];
-    const int b = blockIdx.y, i = blockIdx.x;
+    const int b = blockIdx.y, i = blockIdx.x / nparts, part = blockIdx.x % nparts;
     const size_t pos = (size_t)b * sv.L + i;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float *prow = p + pos * d.V;
     float *qrow = q ? q + pos * d.V : nullptr;
+    // this part's tokens: a quarter of the float4 groups (or of the tokens)
+    const int n4 = d.V >> 2;
+    const int per4 = (n4 + nparts - 1) / nparts;
+    const int k_lo = min(part * per4, n4), k_hi = min(k_lo + per4, n4);
+    const int perv = (d.V + nparts - 1) / nparts;
+    const int v_lo = min(part * perv, d.V), v_hi = min(v_lo + perv, d.V);
     const double lz = logZ[b];
     const int e1 = ea[(size_t)b * (sv.Lpad + 1) + i], e2 = eb[(size_t)b * (sv.Lpad + 1) + i + 1];
     const bool ok = status[b] == 0 && lz > -INFINITY && e1 > kNeg && e2 > kNeg;
+    const bool negent = conf_mode == FA_CONF_NEGENT;
     if (!ok) {
         if (qrow)
-            for (int v = tid; v < d.V; v += kQThreads) qrow[v] = 0.f;
-        if (tid == 0) conf[pos] = -INFINITY;
+            for (int v = v_lo + tid; v < v_hi; v += kQThreads) qrow[v] = 0.f;
+        if (tid == 0 && part == 0) conf[pos] = -INFINITY;
+        if (tid == 0 && negent && nparts > 1) hpart[pos * kQParts + part] = -INFINITY;
         return;
     }
     const double factor = exp2((double)e1 + (double)e2 - lz * 1.4426950408889634074);
@@ -421,10 +434,9 @@ __global__ __launch_bounds__(kQThreads) void marg_q(DevTable d, StepView sv,
     auto qval = [&](float x, float r) -> float {
         return (r > 0.f && x > 0.f) ? (float)((double)x * (double)r * factor) : 0.f;
     };
-    const bool negent = conf_mode == FA_CONF_NEGENT;
     if (!qrow && !negent) {
         // only the sampled token's marginal is needed
-        if (tid == 0)
+        if (tid == 0 && part == 0)
             conf[pos] = tok >= 0 ? qval(prow[tok], weight_r(tok, NG > 0 || SELBIT ? d.tokmask[tok] : 0u))
                                  : -INFINITY;
         return;
@@ -437,13 +449,12 @@ __global__ __launch_bounds__(kQThreads) void marg_q(DevTable d, StepView sv,
         const float4 *p4 = reinterpret_cast<const float4 *>(prow);
         const uint4 *m4 = reinterpret_cast<const uint4 *>(d.tokmask);
         float4 *q4 = reinterpret_cast<float4 *>(qrow);
-        const int n4 = d.V >> 2;
-        for (int k0 = tid; k0 < n4; k0 += U * kQThreads) {
+        for (int k0 = k_lo + tid; k0 < k_hi; k0 += U * kQThreads) {
             float4 x[U];
             uint4 mm[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int k = min(k0 + u * kQThreads, n4 - 1);
+                const int k = min(k0 + u * kQThreads, k_hi - 1);
                 x[u] = p4[k];
                 if constexpr (NG > 0 || SELBIT) mm[u] = m4[k];
                 else mm[u] = make_uint4(0u, 0u, 0u, 0u);
@@ -451,13 +462,13 @@ __global__ __launch_bounds__(kQThreads) void marg_q(DevTable d, StepView sv,
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int k = k0 + u * kQThreads;
-                const int v = 4 * min(k, n4 - 1);  // in-bounds tokens for the lookups
+                const int v = 4 * min(k, k_hi - 1);  // in-bounds tokens for the lookups
                 float4 o;
                 o.x = qval(x[u].x, weight_r(v, mm[u].x));
                 o.y = qval(x[u].y, weight_r(v + 1, mm[u].y));
                 o.z = qval(x[u].z, weight_r(v + 2, mm[u].z));
                 o.w = qval(x[u].w, weight_r(v + 3, mm[u].w));
-                if (k < n4) {
+                if (k < k_hi) {
                     if (q4) q4[k] = o;
                     if (tok >= v && tok < v + 4) {
                         have_tok = true;
@@ -473,7 +484,7 @@ __global__ __launch_bounds__(kQThreads) void marg_q(DevTable d, StepView sv,
             }
         }
     } else {
-        for (int v = tid; v < d.V; v += kQThreads) {
+        for (int v = v_lo + tid; v < v_hi; v += kQThreads) {
             const float o = qval(prow[v], weight_r(v, NG > 0 || SELBIT ? d.tokmask[v] : 0u));
             if (qrow) qrow[v] = o;
             if (v == tok) {
@@ -487,10 +498,14 @@ __global__ __launch_bounds__(kQThreads) void marg_q(DevTable d, StepView sv,
         hsum = wave_sum_d(hsum);
         if (lane == 0) sh_h[wave] = hsum;
         __syncthreads();
-        if (tid == 0) conf[pos] = (float)(((sh_h[0] + sh_h[1]) + sh_h[2]) + sh_h[3]);
+        const double h = ((sh_h[0] + sh_h[1]) + sh_h[2]) + sh_h[3];
+        if (tid == 0) {
+            if (nparts > 1) hpart[pos * kQParts + part] = h;
+            else conf[pos] = (float)h;
+        }
     } else {
         if (have_tok) conf[pos] = tokq;
-        if (tid == 0 && tok < 0) conf[pos] = -INFINITY;
+        if (tid == 0 && part == 0 && tok < 0) conf[pos] = -INFINITY;
     }
 }
 
@@ -1187,7 +1202,9 @@ int launch_marg_out(const DevTable &d, const Geometry &g, const float *p, const 
     int32_t *ea = (int32_t *)(ws + w.ea), *eb = (int32_t *)(ws + w.eb);
     float *rcut = (float *)(ws + w.rcut);
     hipError_t e;
-    const dim3 qgrid(g.L, g.B);
+    // the generic writer: kQParts workgroups per position on short batches
+    const int qparts = g.B * g.L < 1024 ? kQParts : 1;
+    const dim3 qgrid(g.L * qparts, g.B);
     const int ng = (d.ndense + 7) / 8;
     const bool listall = d.nsel > 0 && !d.selbit;
     const bool ranges = d.ncut > 0;
@@ -1293,11 +1310,12 @@ int launch_marg_out(const DevTable &d, const Geometry &g, const float *p, const 
         }
         return (int)e;
     }
+    double *hpart = (double *)(ws + w.hpart);
     e = (hipError_t)prof_mark(FA_PROF_MARG_Q, true, stream);
     if (e != hipSuccess) return (int)e;
 #define FA_MARG_Q(NG, SB, LA, RG)                                                              \
     marg_q<NG, SB, LA, RG><<<qgrid, kQThreads, 0, st>>>(d, sv, p, logZ, tokens, conf_mode, q,  \
-                                                        conf, va, ea, vb, eb, rcut, status)
+                                                        conf, va, ea, vb, eb, rcut, hpart, qparts, status)
     if (ranges) {
         if (listall) FA_MARG_Q(0, false, true, true);
         else FA_MARG_Q(0, false, false, true);
@@ -1320,7 +1338,14 @@ int launch_marg_out(const DevTable &d, const Geometry &g, const float *p, const 
 #undef FA_MARG_Q
     e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
-    return prof_mark(FA_PROF_MARG_Q, false, stream);
+    const int pe = prof_mark(FA_PROF_MARG_Q, false, stream);
+    if (pe) return pe;
+    if (conf_mode == FA_CONF_NEGENT && qparts > 1) {
+        const int npos = g.B * g.L;
+        marg_negent_sum<<<(npos + 255) / 256, 256, 0, st>>>(npos, hpart, conf);
+        e = hipGetLastError();
+    }
+    return (int)e;
 }
 
 }  // namespace fa
