@@ -202,6 +202,10 @@ int fa_build_transitions(const fa_table *t, const float *p, int32_t B, int32_t L
  *               fa_build_transitions wrote; the level is then a sum over
  *               pairs (a, k), (k, c) of the two leaves instead of a dense
  *               product, the same fp32 folded operands in another order.
+ *               With FA_SECOND_LEVEL_SPARSE (or chosen likewise) the second
+ *               level is formed the same way over the pairs (a, c) joined
+ *               through some k, for its products whose four leaves lie
+ *               inside the sequence.
  *   logZ        device double [B]; -inf for infeasible rows
  *   row_status  device int32 [B]; FA_ROW_INFEASIBLE when Z = 0
  * Errors: FA_EINVAL, FA_ESTATE, FA_EHIP.

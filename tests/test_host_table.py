@@ -90,6 +90,12 @@ def test_first_level_flags_and_choice():
     full = [(a, b, [a * 64 + b]) for a in range(64) for b in range(64)]
     t = _compile(64, 4096, 0, [63], full, fa.FA_DFA)
     assert t.info["first_work"] == 64 ** 3 and t.info["first_sparse"] == 0
+    # the two-step pattern of a chain: pairs (s, s + 2); its work per product
+    # is one multiply-add per pair (s, s + 2) followed by (s + 2, s + 4)
+    t2 = chain(fa.FA_FIRST_LEVEL_SPARSE | fa.FA_SECOND_LEVEL_SPARSE)
+    assert t2.info["second_sparse"] == 1
+    assert t2.info["pairs2"] == 38 and t2.info["second_work"] == 36
+    assert chain(fa.FA_FIRST_LEVEL_DENSE).info["second_sparse"] == 0
     # the sparse form keeps the row pointers and column exponents in LDS,
     # which bounds its states
     big = [(s, s + 1, [0]) for s in range(16400)]
