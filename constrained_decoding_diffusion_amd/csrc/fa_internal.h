@@ -26,6 +26,7 @@ constexpr size_t kSparseLdsMax = 160 * 1024;
 constexpr int kSparseMaxSpS = 22000;
 constexpr int kSpWin = 1024;       // columns of a window when Sp > kSpWin
 constexpr int32_t kSparseSecondMaxPairs = 1 << 24;
+constexpr int32_t kSparseMaxPairs = 1 << 26;   // a sparse task packs its first item in 26 bits
 constexpr int kLeafTile = 4096;    // floats of the LDS tile of the one-pass leaf writer
 constexpr int kDenseStepsMax = 64;  // dense-mask contraction: 256-token steps per V chunk, at most
 constexpr int kDenseSlots = 512;    // workgroups of that contraction resident at once (256 CUs x 2)

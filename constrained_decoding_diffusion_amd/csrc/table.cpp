@@ -757,12 +757,12 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
     for (int32_t q = 0; q < np; ++q) w1 += t.row_ptr[t.pair_b[q] + 1] - t.row_ptr[t.pair_b[q]];
     t.first_work = w1;
     if (flags & FA_FIRST_LEVEL_SPARSE) {
-        if (t.Sp + t.S > kSparseMaxSpS) return FA_ETOOBIG;
+        if (t.Sp + t.S > kSparseMaxSpS || np >= kSparseMaxPairs) return FA_ETOOBIG;
         t.first_sparse = true;
     } else if (flags & FA_FIRST_LEVEL_DENSE) {
         t.first_sparse = false;
     } else {
-        t.first_sparse = t.Sp + t.S <= kSparseMaxSpS &&
+        t.first_sparse = t.Sp + t.S <= kSparseMaxSpS && np < kSparseMaxPairs &&
                          (double)kSparseFirstRatio * (double)w1 <= (double)t.Sp * t.Sp * t.Sp;
     }
     t.p2_a.clear(); t.p2_b.clear(); t.p2_row_ptr.clear(); t.p2_col_ptr.clear();

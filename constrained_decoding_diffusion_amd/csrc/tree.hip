@@ -671,8 +671,9 @@ __global__ __launch_bounds__(kSpThreads) void span_sparse(DevTable d, StepView s
     const int grp = lane >> 5, sub = lane & 31;
     float *bufw = sm + wave * 2 * win;           // this wave's two row buffers
     float *bufg = bufw + grp * win;              // this lane group's buffer
-    int4 *task = reinterpret_cast<int4 *>(sm + kSpWaves * 2 * win) + wave * (tcap + kSpTaskPad);
-    int32_t *sco = reinterpret_cast<int32_t *>(sm + kSpWaves * (2 * win + 4 * (tcap + kSpTaskPad)));
+    // a task: (first item | item count << 26, x1 bits)
+    int2 *task = reinterpret_cast<int2 *>(sm + kSpWaves * 2 * win) + wave * (tcap + kSpTaskPad);
+    int32_t *sco = reinterpret_cast<int32_t *>(sm + kSpWaves * (2 * win + 2 * (tcap + kSpTaskPad)));
     int32_t *sptr = sco + Sp;
     float *sx = reinterpret_cast<float *>(sptr + ((S + 4) & ~3));
     uint16_t *stt = reinterpret_cast<uint16_t *>(sx + np);
@@ -820,32 +821,34 @@ __global__ __launch_bounds__(kSpThreads) void span_sparse(DevTable d, StepView s
                     const int Tp = min(T - P, tcap);
                     for (int u = max(pre, P); u < min(pre + nt, P + tcap); ++u) {
                         const int q0 = lo + ((u - pre) << 5);
-                        task[u - P] = make_int4(__float_as_int(cx), q0, min(q0 + 32, lo + deg), 0);
+                        const int c = min(32, lo + deg - q0);
+                        task[u - P] = make_int2(q0 | (c << 26), __float_as_int(cx));
                     }
                     // empty tasks (no items) after the last one: the step
                     // loop runs whole pairs of steps and reads two ahead
-                    if (lane < kSpTaskPad) task[Tp + lane] = make_int4(0, 0, 0, 0);
+                    if (lane < kSpTaskPad) task[Tp + lane] = make_int2(0, 0);
                     const int steps = (Tp + 1) >> 1;
                     // step st runs task 2 st + grp; its item is loaded one
                     // step ahead and the task two steps ahead
-                    int4 ta = task[grp];
-                    int4 tb = task[2 + grp];
+                    constexpr int kLoMask = (1 << 26) - 1;
+                    int2 ta = task[grp];
+                    int2 tb = task[2 + grp];
                     int t0;
                     float x0;
-                    g_entry(item(ta.y + sub), t0, x0);
-                    float w0x = __int_as_float(ta.x);
-                    bool v0 = ta.y + sub < ta.z;
+                    g_entry(item((ta.x & kLoMask) + sub), t0, x0);
+                    float w0x = __int_as_float(ta.y);
+                    bool v0 = sub < (int)((unsigned)ta.x >> 26);
                     for (int st = 0; st < steps; st += 2) {
                         int t1;
                         float x1v;
-                        g_entry(item(tb.y + sub), t1, x1v);
-                        const float w1x = __int_as_float(tb.x);
-                        const bool v1 = tb.y + sub < tb.z;
+                        g_entry(item((tb.x & kLoMask) + sub), t1, x1v);
+                        const float w1x = __int_as_float(tb.y);
+                        const bool v1 = sub < (int)((unsigned)tb.x >> 26);
                         ta = task[2 * st + 4 + grp];
                         if (v0) add(t0, w0x, x0);
-                        g_entry(item(ta.y + sub), t0, x0);
-                        w0x = __int_as_float(ta.x);
-                        v0 = ta.y + sub < ta.z;
+                        g_entry(item((ta.x & kLoMask) + sub), t0, x0);
+                        w0x = __int_as_float(ta.y);
+                        v0 = sub < (int)((unsigned)ta.x >> 26);
                         tb = task[2 * st + 6 + grp];
                         if (v1) add(t1, w1x, x1v);
                     }
@@ -910,7 +913,7 @@ __global__ void sparse_fold(DevTable d, StepView sv, SpPat pat, float *__restric
 size_t sparse_lds(const DevTable &d, int Sp, int np, int win, bool staged)
 {
     const int tcap = staged ? kSpTasks : kSpTasks / 2;
-    size_t b = (size_t)kSpWaves * (2 * win + 4 * (tcap + kSpTaskPad)) * sizeof(float);
+    size_t b = (size_t)kSpWaves * (2 * win + 2 * (tcap + kSpTaskPad)) * sizeof(float);
     b += ((size_t)Sp + ((d.S + 4) & ~3)) * sizeof(int32_t);
     if (staged)
         b += (size_t)np * sizeof(float) + (((size_t)np * sizeof(uint16_t) + 15) & ~size_t(15));
