@@ -902,13 +902,14 @@ __global__ __launch_bounds__(64) void marg_conf_tok(
 // bit-identical to the leaf entries.  One workgroup
 // per (leaf pair, alpha|beta): the input weights are normalized as in
 // marg_level (leaf scales: ro = co = 0, row fold rf); every thread loads its
-// (at most kLeafMsgPer) leaf entries and their values at once, and each
+// (at most PER) leaf entries and their values at once, and each
 // term g[in] * v * 2^-rf[in] goes to LDS in output-grouped order (column
 // order for alpha through a row-major leaf, pair order for beta through a
 // transposed one); each output state then adds its own segment in order.
 constexpr int kLeafMsgThreads = 512;
-constexpr int kLeafMsgPer = 24;  // leaf entries per thread
-constexpr int kLeafMsgMax = kLeafMsgThreads * kLeafMsgPer;
+constexpr int kLeafMsgPer = 24;     // leaf entries per thread
+constexpr int kLeafMsgPerBig = 40;  // the same for tables with more pairs
+constexpr int kLeafMsgMax = kLeafMsgThreads * kLeafMsgPerBig;
 
 //
 // pw (non-null): each workgroup also writes the q writer's pair weights of
@@ -922,6 +923,7 @@ static_assert(kLeafMsgThreads == kPwThreads, "the leaf workgroups run pair_weigh
 static_assert(kLeafMsgThreads >= kSubThreads && kMsgThreads >= kSubThreads,
               "message-pass workgroups can carry a midpoint subtree");
 
+template <int PER>
 __global__ __launch_bounds__(kLeafMsgThreads) void marg_leaf(
     DevTable d, StepView sv, EmitSrc src, const int32_t *__restrict__ meta,
     float *__restrict__ va, int32_t *__restrict__ ea, float *__restrict__ vb,
@@ -963,18 +965,18 @@ __global__ __launch_bounds__(kLeafMsgThreads) void marg_leaf(
     const float *direct = d.use_sel ? src.psel + pos * d.nsel : src.p + pos * d.V;
     // indirect pairs read the values the leaf writer stored for them
     const float *indv = src.ndval + pos * d.n_ind;
-    int prc[kLeafMsgPer];
-    float pval[kLeafMsgPer];
+    int prc[PER];
+    float pval[PER];
     if (real && np > 0) {
-        int pcode[kLeafMsgPer];
+        int pcode[PER];
 #pragma unroll
-        for (int u = 0; u < kLeafMsgPer; ++u) {
+        for (int u = 0; u < PER; ++u) {
             const int k = min(tid + u * kLeafMsgThreads, np - 1);
             prc[u] = erc[k];
             pcode[u] = esrc[k];
         }
 #pragma unroll
-        for (int u = 0; u < kLeafMsgPer; ++u) {
+        for (int u = 0; u < PER; ++u) {
             const float xd = direct[max(pcode[u], 0)];
             const float xi = indv[max(-1 - pcode[u], 0)];
             pval[u] = pcode[u] >= 0 ? xd : xi;
@@ -1007,7 +1009,7 @@ __global__ __launch_bounds__(kLeafMsgThreads) void marg_leaf(
         }
     } else {
 #pragma unroll
-        for (int u = 0; u < kLeafMsgPer; ++u) {
+        for (int u = 0; u < PER; ++u) {
             const int k = tid + u * kLeafMsgThreads;
             if (k < np) {
                 const int in = prc[u] & 0xffff;
@@ -1047,7 +1049,7 @@ namespace {
 bool sparse_leaf_ok(const DevTable &d, const Geometry &g)
 {
     return g.K >= 1 && g.Sp <= kLeafTile && d.npairs <= kLeafMsgMax &&
-           ((size_t)d.npairs + 2 * (size_t)d.S) * 4 <= 64 * 1024;
+           ((size_t)d.npairs + 2 * (size_t)d.S) * 4 <= kSparseLdsMax;
 }
 
 // dynamic LDS of marg_leaf, with or without the pair weights
@@ -1062,7 +1064,7 @@ size_t leaf_lds(const DevTable &d, const Geometry &g, const WsLayout &w, bool pw
 // the leaf level writes the pair weights (and marg_pairw is not launched)
 bool leaf_writes_pw(const DevTable &d, const Geometry &g, const WsLayout &w)
 {
-    return sparse_leaf_ok(d, g) && g.L > 0 && leaf_lds(d, g, w, true) <= 64 * 1024;
+    return sparse_leaf_ok(d, g) && g.L > 0 && leaf_lds(d, g, w, true) <= kSparseLdsMax;
 }
 
 }  // namespace
@@ -1127,14 +1129,21 @@ int launch_marg_pass(const DevTable &d, const Geometry &g, const float *p, const
         if (level == g.K && sparse_leaf) {
             const bool wpw = leaf_writes_pw(d, g, w);
             const size_t llds = leaf_lds(d, g, w, wpw);
+            // entries per thread: the smaller register budget when it holds the table
+            const bool big = d.npairs > kLeafMsgThreads * kLeafMsgPer;
+            const void *fn = big ? reinterpret_cast<const void *>(&marg_leaf<kLeafMsgPerBig>)
+                                 : reinterpret_cast<const void *>(&marg_leaf<kLeafMsgPer>);
             if (llds > 48 * 1024) {
-                e = hipFuncSetAttribute(reinterpret_cast<const void *>(&marg_leaf),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)llds);
+                e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)llds);
                 if (e != hipSuccess) return (int)e;
             }
             float *pw = wpw ? (float *)(ws + w.pw) : nullptr;
-            marg_leaf<<<products + md.nwg, kLeafMsgThreads, llds, st>>>(
-                d, sv, emit_src(d, g, p, ws, w), meta, va, ea, vb, eb, pw, w.pw_nl, w.pw_ld, md);
+            if (big)
+                marg_leaf<kLeafMsgPerBig><<<products + md.nwg, kLeafMsgThreads, llds, st>>>(
+                    d, sv, emit_src(d, g, p, ws, w), meta, va, ea, vb, eb, pw, w.pw_nl, w.pw_ld, md);
+            else
+                marg_leaf<kLeafMsgPer><<<products + md.nwg, kLeafMsgThreads, llds, st>>>(
+                    d, sv, emit_src(d, g, p, ws, w), meta, va, ea, vb, eb, pw, w.pw_nl, w.pw_ld, md);
             e = hipGetLastError();
             if (e != hipSuccess) return (int)e;
             continue;
