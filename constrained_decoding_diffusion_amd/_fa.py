@@ -79,7 +79,7 @@ def _np_ptr(a: np.ndarray):
 
 INFO_KEYS = ["S", "Sp", "start", "n_accept", "pairs", "list_pairs", "dense_pairs", "range_pairs",
              "list_entries", "segments", "cuts", "sel_tokens", "use_sel", "V", "S_orig",
-             "first_sparse", "first_work", "second_sparse", "second_work", "pairs2"]
+             "first_sparse", "first_work", "second_sparse", "second_work", "pairs2", "leafless"]
 
 
 class Table:

@@ -163,6 +163,9 @@ __device__ inline double wave_incl_scan_d(double x, int lane)
 struct StepView {
     int32_t B, L, Lpad, K, Sp;
     size_t mat;
+    // folded leaf pair values when the table keeps no dense leaves (the
+    // leaf-level midpoint draws read them instead), else nullptr
+    const float *pvf = nullptr;
     __device__ size_t node(int b, int h) const { return (size_t)b * 2 * Lpad + h; }
     __device__ float *mat_ptr(float *tree, int b, int h) const { return tree + node(b, h) * mat; }
     __device__ const float *mat_ptr(const float *tree, int b, int h) const

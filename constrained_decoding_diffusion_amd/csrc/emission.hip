@@ -640,8 +640,10 @@ __global__ __launch_bounds__(kLeafThreads) void emission_leaves(DevTable d, Step
             pvrow[k] = ldexpf(tile[row * Sp + col], 0 - remax[row]);
         }
     }
-    float4 *M4 = reinterpret_cast<float4 *>(sv.mat_ptr(tree, b, h) + (size_t)r0 * Sp);
-    for (int k = tid; k < n4; k += kLeafThreads) M4[k] = tile4[k];
+    if (!d.leafless || sv.K == 0) {   // a one-leaf tree's root is the leaf
+        float4 *M4 = reinterpret_cast<float4 *>(sv.mat_ptr(tree, b, h) + (size_t)r0 * Sp);
+        for (int k = tid; k < n4; k += kLeafThreads) M4[k] = tile4[k];
+    }
     int32_t *ro = sv.meta_ptr(meta, b, h, 0), *co = sv.meta_ptr(meta, b, h, 1);
     int32_t *rf = sv.meta_ptr(meta, b, h, 2);
     for (int r = tid; r < nr; r += kLeafThreads) {

@@ -27,6 +27,7 @@ constexpr int kSparseMaxSpS = 22000;
 constexpr int kSpWin = 1024;       // columns of a window when Sp > kSpWin
 constexpr int32_t kSparseSecondMaxPairs = 1 << 24;
 constexpr int32_t kSparseMaxPairs = 1 << 26;   // a sparse task packs its first item in 26 bits
+constexpr int32_t kLeafMsgMaxPairs = 512 * 40; // pairs of the pair-value leaf level of the message pass
 constexpr int kLeafTile = 4096;    // floats of the LDS tile of the one-pass leaf writer
 constexpr int kDenseStepsMax = 64;  // dense-mask contraction: 256-token steps per V chunk, at most
 constexpr int kDenseSlots = 512;    // workgroups of that contraction resident at once (256 CUs x 2)
@@ -104,6 +105,7 @@ struct DevTable {
     const int32_t *ind_pair;   // [n_ind] pairs whose value is computed (not one direct read)
     int32_t n_ind;
     int32_t first_sparse;        // 1: the first span level is formed from the pair values
+    int32_t leafless;            // 1: no dense leaves; every leaf reader takes the pair values
     int32_t second_sparse;       // 1: so is the second, from the two-step pattern
     int32_t np2;                 // pairs of the two-step pattern
     int32_t nwin;                // win_cols-column windows of a row (0: one window)
@@ -149,6 +151,7 @@ struct HostTable {
     bool use_sel = false;
     bool selbit = false;
     bool first_sparse = false;  // first span level by row combination over the pairs
+    bool leafless = false;      // dense leaves not written (every leaf reader takes pair values)
     int64_t first_work = 0;     // its multiply-adds per product: pairs (a, k) times pairs (k, c)
     // two-step pattern: pairs (a, c) joined by pairs (a, k), (k, c), sorted
     // (a, c), with the same row/column orders as the pairs (second level)

@@ -1086,6 +1086,7 @@ int launch_marg_pass(const DevTable &d, const Geometry &g, const float *p, const
 {
     hipStream_t st = (hipStream_t)stream;
     StepView sv = step_view(g);
+    if (d.leafless && g.K >= 1) sv.pvf = (const float *)(ws + w.pvf);   // the riding leaf-level draws
     float *va = (float *)(ws + w.va), *vb = (float *)(ws + w.vb);
     int32_t *ea = (int32_t *)(ws + w.ea), *eb = (int32_t *)(ws + w.eb);
     float *rcut = (float *)(ws + w.rcut);

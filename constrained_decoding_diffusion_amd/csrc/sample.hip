@@ -361,6 +361,7 @@ int launch_sample_states(const DevTable &d, const Geometry &g, const float *tree
 {
     hipStream_t st = (hipStream_t)stream;
     StepView sv = step_view(g);
+    if (d.leafless && g.K >= 1) sv.pvf = (const float *)(ws + w.pvf);
     int32_t *zc = (int32_t *)(ws + w.zc);
     int32_t *tpair = (int32_t *)(ws + w.tpair);
     uint32_t *tdbit = (uint32_t *)(ws + w.tdbit);

@@ -112,6 +112,53 @@ __device__ inline void put_pair(const DevTable &d, int a, int c, int32_t *tpair,
     *tdbit = (q >= 0 && d.pair_cls[q] == kDense) ? 1u << d.pair_aux[q] : 0u;
 }
 
+// The midpoint draw of a first-level node on a table without dense leaves:
+// candidate k weighs L[zl][k] R[k][zr], the two leaves' pair values (folded:
+// a factor 2^-rf per leaf that is the same for every candidate) looked up in
+// map_n, or the identity past the sequence end.  The weights are formed as in
+// draw_mid from the same mantissas and exponent differences, so the draw is
+// the one the dense leaves give.
+__device__ int draw_mid_pairs(const DevTable &d, const StepView &sv, const int32_t *__restrict__ meta,
+                              uint64_t seed, int b, int level, int idx, int n, int zl, int zr,
+                              int lane, int32_t *__restrict__ status)
+{
+    const int iL = 2 * n - sv.Lpad, iR = iL + 1;
+    const float *vL = sv.pvf + ((size_t)b * sv.L + min(iL, sv.L - 1)) * d.npairs;
+    const float *vR = sv.pvf + ((size_t)b * sv.L + min(iR, sv.L - 1)) * d.npairs;
+    const bool realL = iL < sv.L, realR = iR < sv.L;
+    const int32_t *coL = sv.meta_ptr(meta, b, 2 * n, 1);
+    const int32_t *coR = sv.meta_ptr(meta, b, 2 * n + 1, 1);
+    const size_t Sp = sv.Sp;
+    auto pl = [&](int k) -> float {
+        if (!realL) return k == zl ? 1.f : 0.f;
+        const int q = d.map_n[(size_t)zl * Sp + k];
+        return q >= 0 ? vL[q] : 0.f;
+    };
+    auto pr = [&](int k) -> float {   // the right leaf's values are in column order
+        if (!realR) return k == zr ? 1.f : 0.f;
+        const int q = d.map_n[(size_t)k * Sp + zr];
+        return q >= 0 ? vR[d.pair_colpos[q]] : 0.f;
+    };
+    auto expo = [&](int k) {
+        const float a = pl(k), c = pr(k);
+        if (!(a > 0.f) || !(c > 0.f) || coL[k] <= kNeg || coR[k] <= kNeg) return kNeg;
+        return fexp(a) + coL[k] + fexp(c) + coR[k];
+    };
+    const float u = philox_u01(seed, (uint32_t)b, (uint32_t)level, (uint32_t)idx);
+    int j = -1;
+    int e = kNeg;
+    for (int k = lane; k < d.S; k += 64) e = max(e, expo(k));
+    const int emax = wave_max_i(e);
+    if (emax > kNeg) {
+        j = wave_icdf(d.S, u, lane, [&](int k) {
+            const int ek = expo(k);
+            return ek > kNeg ? scale2(mant(pl(k)) * mant(pr(k)), ek - emax) : 0.f;
+        });
+    }
+    if (j < 0 && lane == 0) atomicOr(&status[b], (int)FA_ROW_UNDERFLOW);
+    return j;
+}
+
 // one midpoint level: node n = nn + idx covers [l, r); children 2n (stored as
 // is) and 2n+1 (stored transposed): both needed vectors are stored rows
 // midpoint draw of node n (level `level`, index idx within the level) by
@@ -123,6 +170,8 @@ __device__ int draw_mid(const DevTable &d, const StepView &sv, const float *__re
 {
     int j = -1;
     if (zl < 0 || zr < 0) return -1;
+    if (sv.pvf && n >= (sv.Lpad >> 1))
+        return draw_mid_pairs(d, sv, meta, seed, b, level, idx, n, zl, zr, lane, status);
     const float *PL = sv.mat_ptr(tree, b, 2 * n) + (size_t)zl * sv.Sp;
     const float *PR = sv.mat_ptr(tree, b, 2 * n + 1) + (size_t)zr * sv.Sp;
     const int32_t *coL = sv.meta_ptr(meta, b, 2 * n, 1);

@@ -119,6 +119,7 @@ DevTable HostTable::device_view() const
     d.has_cnt = has_cnt ? 1 : 0;
     d.selbit = selbit ? 1 : 0;
     d.first_sparse = first_sparse ? 1 : 0;
+    d.leafless = leafless ? 1 : 0;
     const uint8_t *b = static_cast<const uint8_t *>(dev);
     size_t k = 0;
     auto nxt = [&](auto *&ptr) {
@@ -238,14 +239,14 @@ WsLayout ws_layout(const HostTable &t, const Geometry &g)
     w.psel = o; o = al(o + (t.use_sel ? BL * t.nsel() * sizeof(float) : 0));
     // one spare float: a clamped read of slot 0 stays inside even with no indirect pairs
     w.ndval = o; o = al(o + (fused ? (BL * t.ind_pair.size() + 1) * sizeof(float) : 0));
+    // the folded leaf pair values: read by the sparse first level, and on a
+    // leafless table by the leaf-level draws too (so kept through the step)
+    w.pvf = o; o = al(o + (t.first_sparse ? BL * t.npairs() * sizeof(float) : 0));
     const size_t a0 = o;
     w.dpart = o; o = al(o + (size_t)w.n_vchunks * BLpad * kDenseMax * sizeof(float));
     w.dval = o; o = al(o + (t.ndense() && !fused ? BL * kDenseMax * sizeof(float) : 0));
     w.cutp = o; o = al(o + BL * t.ncut() * sizeof(double));
     w.val = o; o = al(o + (fused ? 0 : BL * t.npairs() * sizeof(float)));
-    // the sparse first span level's operands: folded pair values of every
-    // leaf in its stored order (pair order, or column order when transposed)
-    w.pvf = o; o = al(o + (t.first_sparse ? BL * t.npairs() * sizeof(float) : 0));
     size_t a1 = o;
     o = a0;  // span tree region
     size_t kp = 0;
@@ -805,6 +806,12 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
     } else if (flags & FA_SECOND_LEVEL_SPARSE) {
         return FA_EINVAL;
     }
+    // no dense leaves when nothing reads them: the first level is sparse,
+    // the message pass's leaf level takes the pair values (LDS-resident
+    // pairs and vectors) and the leaf-level draws look pairs up in map_n
+    // (a one-leaf tree, whose root is the leaf, still writes it)
+    t.leafless = t.first_sparse && np > 0 && !t.map_n.empty() && t.Sp <= kLeafTile && np <= kLeafMsgMaxPairs &&
+                 ((size_t)np + 2 * (size_t)t.S) * 4 <= kSparseLdsMax;
     build_image(t);
     return FA_OK;
 }
@@ -851,11 +858,12 @@ extern "C" int fa_table_info(const fa_table *t, int64_t *info, int32_t n)
     const HostTable &h = t->h;
     int32_t nl = 0, nd = 0, nr = 0;
     for (int32_t c : h.pair_cls) (c == kList ? nl : c == kDense ? nd : nr)++;
-    int64_t v[20] = {h.S, h.Sp, h.start, (int64_t)h.acc.size(), h.npairs(), nl, nd, nr,
+    int64_t v[21] = {h.S, h.Sp, h.start, (int64_t)h.acc.size(), h.npairs(), nl, nd, nr,
                      (int64_t)h.list_tok.size(), h.nseg(), h.ncut(), h.nsel(), h.use_sel ? 1 : 0,
                      h.V, h.S_orig, h.first_sparse ? 1 : 0, h.first_work,
-                     h.second_sparse ? 1 : 0, h.second_work, (int64_t)h.p2_a.size()};
-    for (int32_t k = 0; k < n && k < 20; ++k) info[k] = v[k];
+                     h.second_sparse ? 1 : 0, h.second_work, (int64_t)h.p2_a.size(),
+                     h.leafless ? 1 : 0};
+    for (int32_t k = 0; k < n && k < 21; ++k) info[k] = v[k];
     return FA_OK;
 }
 
