@@ -142,7 +142,9 @@ void fa_table_destroy(fa_table *t);
  * pair values, [16] that form's multiply-adds per first-level product (the
  * number of pairs (a, k), (k, c) sharing k), [17] 1 if the second level is
  * formed likewise, [18] its multiply-adds per product, [19] the pairs of the
- * two-step pattern it uses.  Returns FA_OK or FA_EINVAL.
+ * two-step pattern it uses, [20] 1 if the step keeps no dense leaves (the
+ * first level is sparse, and the message pass's leaf level and the leaf-level
+ * midpoint draws read the pair values).  Returns FA_OK or FA_EINVAL.
  */
 int fa_table_info(const fa_table *t, int64_t *info, int32_t n);
 
@@ -171,7 +173,9 @@ int fa_sizes(const fa_table *t, int32_t B, int32_t L, size_t *tree_bytes, size_t
  * (a factorized model times a chain model is a chain model; the |E||V| term).
  *   p        device [B][L][V] fp32, read only (values must be >= 0; NaN or
  *            negative entries that are read set FA_ROW_BADPROB)
- *   tree     device, fa_sizes bytes; leaves written
+ *   tree     device, fa_sizes bytes; leaves written, except on a table
+ *            whose every leaf reader takes the pair values (fa_table_info
+ *            [20]; the first span level then sparse) when L > 1
  *   meta     device, fa_sizes bytes; leaf exponents written
  *   ws       device workspace of ws_bytes >= fa_sizes; keeps, for the step's
  *            fa_marginals, the compact copy of p at token-list tokens and the

@@ -96,6 +96,10 @@ def test_first_level_flags_and_choice():
     assert t2.info["second_sparse"] == 1
     assert t2.info["pairs2"] == 38 and t2.info["second_work"] == 36
     assert chain(fa.FA_FIRST_LEVEL_DENSE).info["second_sparse"] == 0
+    # no dense leaves once the first level is sparse and every leaf reader
+    # can take the pair values
+    assert chain(0).info["leafless"] == 1
+    assert chain(fa.FA_FIRST_LEVEL_DENSE).info["leafless"] == 0
     # the sparse form keeps the row pointers and column exponents in LDS,
     # which bounds its states
     big = [(s, s + 1, [0]) for s in range(16400)]
