@@ -57,7 +57,15 @@ def algorithmic_work(tb, B, L):
     table_bytes = tb.device_bytes
     p_bytes = B * L * V * 4
     mask_bytes = V * 4
-    leaves = B * Lpad * S * S * 4
+    dense_leaves = B * Lpad * S * S * 4
+    pair_values = B * L * tb.info["pairs"] * 4
+    # a leafless table writes each leaf's pair values, not the dense S*S leaf;
+    # a message pass whose leaf level takes the pair values reads those, not
+    # the dense leaves (both only when the tree has more than one leaf)
+    leafless = bool(tb.info["leafless"]) and K >= 1
+    leaf_msg_pairs = bool(tb.info["leaf_msg_pairs"]) and K >= 1
+    a1_leaves = pair_values if leafless else dense_leaves
+    a4_leaves = pair_values if leaf_msg_pairs else dense_leaves
     internal = B * (Lpad - 1) * S * S * 4
     sparse1 = bool(tb.info["first_sparse"])
     sparse2 = sparse1 and bool(tb.info["second_sparse"]) and K >= 2
@@ -79,9 +87,14 @@ def algorithmic_work(tb, B, L):
               dict(bound="mfma", work=2.0 * S ** 3 * B * (Lpad // 2), unit="TFLOP/s",
                    per_unit="2*S^3 per product (S trimmed states), B*Lpad/2 products"))
     return dict(
-        a1_bytes=p_bytes + table_bytes + leaves,
+        a1_bytes=p_bytes + table_bytes + a1_leaves,
+        a1_basis=("p read + table + " + ("each leaf's pair values written (B*L*pairs*4)" if leafless
+                                         else "dense leaves written (B*Lpad*S*S*4)")),
         a2_flops=level1_flops + level2_flops + upper_flops,
-        a4_bytes=p_bytes + p_bytes + leaves + internal + table_bytes,
+        a4_bytes=p_bytes + p_bytes + a4_leaves + internal + table_bytes,
+        a4_basis=("p read + q write + internal nodes read + table + " +
+                  ("leaf pair values read (B*L*pairs*4)" if leaf_msg_pairs
+                   else "dense leaves read (B*Lpad*S*S*4)")),
         # per launch of the kernels the library can bracket with events
         kernels={
             "emission_dense": dict(bound="hbm", work=p_bytes + mask_bytes, unit="GB/s",
@@ -459,7 +472,7 @@ def main():
     if stage_us is not None:
         stages = {
             "build_transitions": dict(us=stage_us["build_transitions"], bound="hbm",
-                                      algorithmic_bytes=work["a1_bytes"],
+                                      algorithmic_bytes=work["a1_bytes"], basis=work["a1_basis"],
                                       gbs=work["a1_bytes"] / (stage_us["build_transitions"] * 1e3)),
             "span_tree": dict(us=stage_us["span_tree"], bound="mfma", algorithmic_flops=work["a2_flops"],
                               tflops=work["a2_flops"] / (stage_us["span_tree"] * 1e6)),
@@ -470,6 +483,7 @@ def main():
         else:
             last = "sample_marginals"
         stages[last] = dict(us=stage_us[last], bound="hbm", algorithmic_bytes=work["a4_bytes"],
+                            basis=work["a4_basis"],
                             gbs=work["a4_bytes"] / (stage_us[last] * 1e3))
         for n in ("build_transitions", last):
             stages[n]["frac"] = stages[n]["gbs"] / HBM_PEAK_GBS

@@ -68,7 +68,7 @@ extern "C" int fa_build_transitions(const fa_table *t, const float *p, int32_t B
     int rc = ready(t);
     if (rc) return rc;
     Geometry g;
-    if (!make_geometry(t->h, B, L, &g)) return FA_EINVAL;
+    if (int grc = make_geometry(t->h, B, L, &g)) return grc;
     if (!grid_fits(g)) return FA_ETOOBIG;
     if (B == 0 || L == 0) return FA_OK;
     WsLayout w = ws_layout(t->h, g);
@@ -84,7 +84,7 @@ extern "C" int fa_span_tree(const fa_table *t, int32_t B, int32_t L, float *tree
     int rc = ready(t);
     if (rc) return rc;
     Geometry g;
-    if (!make_geometry(t->h, B, L, &g)) return FA_EINVAL;
+    if (int grc = make_geometry(t->h, B, L, &g)) return grc;
     if (!grid_fits(g)) return FA_ETOOBIG;
     if (B == 0) return FA_OK;
     if (!logZ || !row_status) return FA_EINVAL;
@@ -101,7 +101,7 @@ extern "C" int fa_sample(const fa_table *t, const float *p, int32_t B, int32_t L
     int rc = ready(t);
     if (rc) return rc;
     Geometry g;
-    if (!make_geometry(t->h, B, L, &g)) return FA_EINVAL;
+    if (int grc = make_geometry(t->h, B, L, &g)) return grc;
     if (!grid_fits(g)) return FA_ETOOBIG;
     if (B == 0) return FA_OK;
     WsLayout w = ws_layout(t->h, g);
@@ -119,7 +119,7 @@ extern "C" int fa_marginals(const fa_table *t, const float *p, int32_t B, int32_
     int rc = ready(t);
     if (rc) return rc;
     Geometry g;
-    if (!make_geometry(t->h, B, L, &g)) return FA_EINVAL;
+    if (int grc = make_geometry(t->h, B, L, &g)) return grc;
     if (!grid_fits(g)) return FA_ETOOBIG;
     if (conf_mode != FA_CONF_PROB && conf_mode != FA_CONF_NEGENT) return FA_EINVAL;
     if (B == 0 || L == 0) return FA_OK;
@@ -140,7 +140,7 @@ extern "C" int fa_sample_marginals(const fa_table *t, const float *p, int32_t B,
     int rc = ready(t);
     if (rc) return rc;
     Geometry g;
-    if (!make_geometry(t->h, B, L, &g)) return FA_EINVAL;
+    if (int grc = make_geometry(t->h, B, L, &g)) return grc;
     if (!grid_fits(g)) return FA_ETOOBIG;
     if (conf_mode != FA_CONF_PROB && conf_mode != FA_CONF_NEGENT) return FA_EINVAL;
     if (B == 0) return FA_OK;

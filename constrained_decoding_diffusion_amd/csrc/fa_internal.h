@@ -42,6 +42,17 @@ constexpr int kTokChunksMax = 256;  // chunks per candidate list of one token dr
 
 enum PairClass : int32_t { kList = 0, kDense = 1, kRange = 2 };
 
+// The message pass's leaf level runs from the pair values (marg_leaf) when
+// the leaf entries exist (Sp <= kLeafTile), the pairs fit its threads'
+// registers and the pairs plus two S-vectors fit in LDS.  The table compiler
+// (which drops the dense leaves of such tables) and the launcher (which then
+// must not read them) both decide with this one predicate.
+inline bool leaf_level_from_pairs(int64_t npairs, int64_t S, int64_t Sp)
+{
+    return Sp <= kLeafTile && npairs <= kLeafMsgMaxPairs &&
+           ((size_t)npairs + 2 * (size_t)S) * 4 <= kSparseLdsMax;
+}
+
 // Device view of a compiled automaton.  All pointers address the caller's
 // device buffer; passed to kernels by value.
 struct DevTable {
@@ -186,7 +197,9 @@ struct Geometry {
     size_t meta_ints;    // B * 2*Lpad * 3 * Sp
 };
 
-bool make_geometry(const HostTable &t, int32_t B, int32_t L, Geometry *g);
+// Lpad, K and buffer sizes of a step; FA_EINVAL for negative sizes,
+// FA_ETOOBIG for L >= 2^24
+int make_geometry(const HostTable &t, int32_t B, int32_t L, Geometry *g);
 
 // Workspace layout (bytes from the start of ws), sized for the largest user.
 struct WsLayout {

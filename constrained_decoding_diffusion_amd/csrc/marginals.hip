@@ -910,6 +910,8 @@ constexpr int kLeafMsgThreads = 512;
 constexpr int kLeafMsgPer = 24;     // leaf entries per thread
 constexpr int kLeafMsgPerBig = 40;  // the same for tables with more pairs
 constexpr int kLeafMsgMax = kLeafMsgThreads * kLeafMsgPerBig;
+static_assert(kLeafMsgMax == kLeafMsgMaxPairs,
+              "the table compiler's leafless decision assumes marg_leaf takes this many pairs");
 
 //
 // pw (non-null): each workgroup also writes the q writer's pair weights of
@@ -1048,8 +1050,7 @@ namespace {
 // (Sp < 65536) and their terms fit in LDS
 bool sparse_leaf_ok(const DevTable &d, const Geometry &g)
 {
-    return g.K >= 1 && g.Sp <= kLeafTile && d.npairs <= kLeafMsgMax &&
-           ((size_t)d.npairs + 2 * (size_t)d.S) * 4 <= kSparseLdsMax;
+    return g.K >= 1 && leaf_level_from_pairs(d.npairs, d.S, g.Sp);
 }
 
 // dynamic LDS of marg_leaf, with or without the pair weights
@@ -1092,6 +1093,8 @@ int launch_marg_pass(const DevTable &d, const Geometry &g, const float *p, const
     float *rcut = (float *)(ws + w.rcut);
     const size_t lds = (size_t)g.Sp * (sizeof(float) + sizeof(int));
     const bool sparse_leaf = sparse_leaf_ok(d, g);
+    // a leafless table wrote no dense leaves: its leaf level must take the pairs
+    if (d.leafless && g.K >= 1 && !sparse_leaf) return (int)hipErrorInvalidValue;
     // the boundary vectors: built by the top marg_level launch, else here
     const bool init_in_top = g.K >= 1 && !(g.K == 1 && sparse_leaf);
     hipError_t e;

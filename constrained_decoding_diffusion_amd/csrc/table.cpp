@@ -161,9 +161,12 @@ DevTable HostTable::device_view() const
     return d;
 }
 
-bool make_geometry(const HostTable &t, int32_t B, int32_t L, Geometry *g)
+int make_geometry(const HostTable &t, int32_t B, int32_t L, Geometry *g)
 {
-    if (B < 0 || L < 0) return false;
+    if (B < 0 || L < 0) return FA_EINVAL;
+    // positions index 24-bit fields of the kernels; this also keeps Lpad
+    // (below 2^24) far from int32 overflow
+    if (L >= (1 << 24)) return FA_ETOOBIG;
     int32_t Lpad = 1, K = 0;
     while (Lpad < L) {
         Lpad <<= 1;
@@ -177,7 +180,7 @@ bool make_geometry(const HostTable &t, int32_t B, int32_t L, Geometry *g)
     g->mat = (size_t)t.Sp * t.Sp;
     g->tree_floats = L > 0 ? (size_t)B * 2 * Lpad * g->mat : 0;
     g->meta_ints = L > 0 ? (size_t)B * 2 * Lpad * 3 * t.Sp : 0;
-    return true;
+    return FA_OK;
 }
 
 int tree_ksplit(const Geometry &g, int level)
@@ -810,8 +813,7 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
     // the message pass's leaf level takes the pair values (LDS-resident
     // pairs and vectors) and the leaf-level draws look pairs up in map_n
     // (a one-leaf tree, whose root is the leaf, still writes it)
-    t.leafless = t.first_sparse && np > 0 && !t.map_n.empty() && t.Sp <= kLeafTile && np <= kLeafMsgMaxPairs &&
-                 ((size_t)np + 2 * (size_t)t.S) * 4 <= kSparseLdsMax;
+    t.leafless = t.first_sparse && np > 0 && !t.map_n.empty() && leaf_level_from_pairs(np, t.S, t.Sp);
     build_image(t);
     return FA_OK;
 }
@@ -858,12 +860,14 @@ extern "C" int fa_table_info(const fa_table *t, int64_t *info, int32_t n)
     const HostTable &h = t->h;
     int32_t nl = 0, nd = 0, nr = 0;
     for (int32_t c : h.pair_cls) (c == kList ? nl : c == kDense ? nd : nr)++;
-    int64_t v[21] = {h.S, h.Sp, h.start, (int64_t)h.acc.size(), h.npairs(), nl, nd, nr,
-                     (int64_t)h.list_tok.size(), h.nseg(), h.ncut(), h.nsel(), h.use_sel ? 1 : 0,
-                     h.V, h.S_orig, h.first_sparse ? 1 : 0, h.first_work,
-                     h.second_sparse ? 1 : 0, h.second_work, (int64_t)h.p2_a.size(),
-                     h.leafless ? 1 : 0};
-    for (int32_t k = 0; k < n && k < 21; ++k) info[k] = v[k];
+    constexpr int32_t kInfo = 22;
+    int64_t v[kInfo] = {h.S, h.Sp, h.start, (int64_t)h.acc.size(), h.npairs(), nl, nd, nr,
+                        (int64_t)h.list_tok.size(), h.nseg(), h.ncut(), h.nsel(),
+                        h.use_sel ? 1 : 0, h.V, h.S_orig, h.first_sparse ? 1 : 0, h.first_work,
+                        h.second_sparse ? 1 : 0, h.second_work, (int64_t)h.p2_a.size(),
+                        h.leafless ? 1 : 0,
+                        h.npairs() > 0 && leaf_level_from_pairs(h.npairs(), h.S, h.Sp) ? 1 : 0};
+    for (int32_t k = 0; k < n && k < kInfo; ++k) info[k] = v[k];
     return FA_OK;
 }
 
@@ -879,7 +883,7 @@ extern "C" int fa_sizes(const fa_table *t, int32_t B, int32_t L, size_t *tree_by
 {
     if (!t) return FA_EINVAL;
     Geometry g;
-    if (!make_geometry(t->h, B, L, &g)) return FA_EINVAL;
+    if (int grc = make_geometry(t->h, B, L, &g)) return grc;
     if ((size_t)g.Lpad * g.Sp > (size_t)1 << 40) return FA_ETOOBIG;
     if ((int64_t)B * g.Lpad * 2 > 65535 || L >= (1 << 24)) return FA_ETOOBIG;
     if (tree_bytes) *tree_bytes = g.tree_floats * sizeof(float);

@@ -144,7 +144,9 @@ void fa_table_destroy(fa_table *t);
  * formed likewise, [18] its multiply-adds per product, [19] the pairs of the
  * two-step pattern it uses, [20] 1 if the step keeps no dense leaves (the
  * first level is sparse, and the message pass's leaf level and the leaf-level
- * midpoint draws read the pair values).  Returns FA_OK or FA_EINVAL.
+ * midpoint draws read the pair values), [21] 1 if the message pass's leaf
+ * level (L > 1) reads the pair values instead of the dense leaves.  Returns
+ * FA_OK or FA_EINVAL.
  */
 int fa_table_info(const fa_table *t, int64_t *info, int32_t n);
 

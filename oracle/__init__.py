@@ -54,6 +54,7 @@ def lib():
         _lib.or_sample_tree.argtypes = [P, P, P, C.c_int32, C.c_uint64, C.c_uint32, P, P]
         _lib.or_replay_verify.argtypes = [P, P, P, C.c_int32, C.c_uint64, C.c_uint32, P, P, P]
         _lib.or_ffbs.argtypes = [P, P, P, C.c_int32, P, P, P, P]
+        _lib.or_judge_draw.argtypes = [P, C.c_int32, C.c_double, C.c_int32, P]
         _lib.or_edge_count.argtypes = [P, C.c_int32, C.c_int32, C.c_int32]
         _lib.or_edge_count.restype = C.c_int32
     return _lib
@@ -73,6 +74,15 @@ def philox4x32_10(ctr, key):
 
 def uniform(seed: int, b: int, level: int, node: int) -> float:
     return lib().or_uniform(seed, b, level, node)
+
+
+def judge_draw(w, u: float, chosen: int):
+    """One draw judged as the replay verifier judges it: returns (the
+    oracle's choice, verdict 0 same / 1 NEAR / 2 HARD, fp32-margin flag)."""
+    w = np.ascontiguousarray(w, np.float64)
+    out = np.zeros(3, np.int32)
+    lib().or_judge_draw(_ptr(w), w.size, float(u), int(chosen), _ptr(out))
+    return int(out[0]), int(out[1]), int(out[2])
 
 
 class Oracle:

@@ -350,21 +350,25 @@ typedef struct {
     int64_t n_draws, n_hard, n_near, n_margin, first_hard;
 } or_replay_report;
 
-/* Boundary distance test between two choices j1 < j2 of a draw: the smallest
- * |C_k/T - u| over the CDF boundaries k in [j1, j2). */
+/* Boundary distance between two choices j1 < j2 of a draw: the largest
+ * |C_k/T - u| over the CDF boundaries k in [j1, j2).  Another implementation
+ * whose fp32 prefix sums moved every one of those boundaries across u picks
+ * j2 where this one picks j1 (or the reverse); that is a rounding effect
+ * only when all of them lie close to u.  A candidate of real weight between
+ * the two choices puts a boundary far from u, and the draw is then wrong. */
 static double boundary_gap(const double *w, int32_t n, double u, int32_t j1, int32_t j2)
 {
     double T = 0.0;
     for (int32_t j = 0; j < n; ++j) T += w[j];
-    double c = 0.0, best = INFINITY;
+    double c = 0.0, worst = 0.0;
     for (int32_t j = 0; j < j2 && j < n; ++j) {
         c += w[j];
         if (j >= j1) {
             double d = fabs(c / T - u);
-            if (d < best) best = d;
+            if (d > worst) worst = d;
         }
     }
-    return best;
+    return worst;
 }
 
 /* Judge one draw.  chosen = the candidate index the other implementation
@@ -391,6 +395,20 @@ static int32_t judge(const double *w, int32_t n, double u, int32_t chosen, int64
         if (rep->first_hard < 0) rep->first_hard = draw_id;
     }
     return chosen;
+}
+
+/* One draw judged on its own, for tests: weights w[0..n), uniform u, and the
+ * index another implementation chose.  out[0] = the oracle's own choice
+ * (-1 when the weights vanish), out[1] = 0 same choice, 1 NEAR, 2 HARD,
+ * out[2] = 1 when a HARD draw lies within 1e-4 of the boundaries (the
+ * fp32-margin count). */
+void or_judge_draw(const double *w, int32_t n, double u, int32_t chosen, int32_t out[3])
+{
+    or_replay_report rep = {0, 0, 0, 0, -1};
+    out[0] = icdf(w, n, u);
+    judge(w, n, u, chosen, 0, &rep);
+    out[1] = rep.n_hard ? 2 : (rep.n_near ? 1 : 0);
+    out[2] = rep.n_margin ? 1 : 0;
 }
 
 /* ------------------------------------------------- tree-order sampler
@@ -482,8 +500,9 @@ int or_sample_tree(const or_aut *A, const float *p, const double *W, int32_t L, 
 }
 
 /* [P1 "The scan trick"]: replay another implementation's draws under the same
- * uniforms; a differing choice is NEAR when a CDF boundary between the two
- * choices lies within 1e-6 of u, else HARD (also HARD: a zero-weight choice). */
+ * uniforms; a differing choice is NEAR when every CDF boundary between the
+ * two choices lies within 1e-6 of u, else HARD (also HARD: a zero-weight
+ * choice). */
 int or_replay_verify(const or_aut *A, const float *p, const double *W, int32_t L, uint64_t seed,
                      uint32_t b, const int32_t *states, const int32_t *tokens, int64_t report[5])
 {

@@ -103,9 +103,12 @@ def check_leaves(w, g, b, positions, orc=None):
     position reached 1e-4 in the marginals after 16 positions), so it is
     checked on its own."""
     tb = g["table"]
-    if tb.info["leafless"] and w.L > 1:
-        return   # no dense leaves: the first-level node checks cover the leaf values
     orc = orc or oracle.Oracle(w.aut)
+    if tb.info["leafless"] and w.L > 1:
+        # no dense leaves: their values are checked through the first-level
+        # nodes, each the product of two leaves, with the drift bound of two
+        check_span_nodes(w, g, b, orc, level=1)
+        return
     orig = tb.orig
     W = orc.edge_weights(w.p[b])
     drift = []
@@ -118,3 +121,63 @@ def check_leaves(w, g, b, positions, orc=None):
     if drift:
         bias = float(np.mean(drift))
         assert abs(bias) <= LEAF_BIAS, f"row {b}: leaf drift {bias:.3g}"
+
+
+NODE_RTOL = 3e-5
+
+
+def span_node(w, g, b, n):
+    """Tree node n of row b as the true span matrix over compact states
+    (stored values times 2^ro per row and 2^co per column, right children
+    transposed back)."""
+    tb = g["table"]
+    Sp, S = tb.info["Sp"], tb.info["S"]
+    Lpad = 1 << max(0, (w.L - 1).bit_length())
+    tree = g["bufs"].tree.view(w.B, 2 * Lpad, Sp, Sp)
+    meta = g["bufs"].meta[: w.B * 2 * Lpad * 3 * Sp].view(w.B, 2 * Lpad, 3, Sp)
+    D = tree[b, n].cpu().numpy().astype(np.float64)
+    ro = meta[b, n, 0].cpu().numpy().astype(np.float64)
+    co = meta[b, n, 1].cpu().numpy().astype(np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        T = D * np.exp2(ro)[:, None] * np.exp2(co)[None, :]
+    T[D == 0] = 0.0
+    if n % 2 == 1 and n >= 3:
+        T = T.T
+    return T[:S, :S]
+
+
+def check_span_nodes(w, g, b, orc, level=1):
+    """Every node of one tree level (spans of 2^level positions) against the
+    product of the oracle's M_i over its span: entries within NODE_RTOL, and
+    the mass-weighted relative error sum(P_gpu - P) / sum(P), averaged over
+    the nodes, within 2^level * LEAF_BIAS (each leaf may carry LEAF_BIAS)."""
+    tb = g["table"]
+    orig = tb.orig
+    S = len(orig)
+    Lpad = 1 << max(0, (w.L - 1).bit_length())
+    span = 1 << level
+    if Lpad < span:
+        return
+    W = orc.edge_weights(w.p[b])
+
+    def M(i):
+        if i >= w.L:
+            return np.eye(S)
+        return orc.dense_M(W, i)[np.ix_(orig, orig)]
+
+    drift = []
+    for j in range(Lpad // span):
+        want = M(span * j)
+        for i in range(span * j + 1, span * j + span):
+            want = want @ M(i)
+        got = span_node(w, g, b, Lpad // span + j)
+        scale = want.max(axis=1, keepdims=True)
+        err = np.abs(got - want)
+        bad = err > NODE_RTOL * want + 1e-30 * scale
+        assert not bad.any(), (f"row {b} node {Lpad // span + j}: {bad.sum()} entries off, worst "
+                               f"rel {np.max(err / np.maximum(want, 1e-300))}")
+        if span * j < w.L and want.sum() > 0:
+            drift.append(float((got - want).sum() / want.sum()))
+    if drift:
+        bias = float(np.mean(drift))
+        assert abs(bias) <= span * LEAF_BIAS, f"row {b} level {level}: drift {bias:.3g}"

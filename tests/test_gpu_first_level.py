@@ -15,54 +15,9 @@ from tests.test_gpu_parity import CASES
 
 pytestmark = pytest.mark.gpu
 
-NODE_RTOL = 3e-5
-
-
-def _node(w, g, b, n):
-    """Level-1 node n of row b as the true span matrix over compact states."""
-    import torch
-    tb = g["table"]
-    Sp, S = tb.info["Sp"], tb.info["S"]
-    Lpad = 1 << max(0, (w.L - 1).bit_length())
-    tree = g["bufs"].tree.view(w.B, 2 * Lpad, Sp, Sp)
-    meta = g["bufs"].meta[: w.B * 2 * Lpad * 3 * Sp].view(w.B, 2 * Lpad, 3, Sp)
-    D = tree[b, n].cpu().numpy().astype(np.float64)
-    ro = meta[b, n, 0].cpu().numpy().astype(np.float64)
-    co = meta[b, n, 1].cpu().numpy().astype(np.float64)
-    with np.errstate(over="ignore", invalid="ignore"):
-        T = D * np.exp2(ro)[:, None] * np.exp2(co)[None, :]
-    T[D == 0] = 0.0
-    if n % 2 == 1 and n >= 3:
-        T = T.T
-    del torch
-    return T[:S, :S]
-
 
 def _check_level1(w, g, b, orc, level=1):
-    tb = g["table"]
-    orig = tb.orig
-    S = len(orig)
-    Lpad = 1 << max(0, (w.L - 1).bit_length())
-    span = 1 << level
-    if Lpad < span:
-        return
-    W = orc.edge_weights(w.p[b])
-
-    def M(i):
-        if i >= w.L:
-            return np.eye(S)
-        return orc.dense_M(W, i)[np.ix_(orig, orig)]
-
-    for j in range(Lpad // span):
-        want = M(span * j)
-        for i in range(span * j + 1, span * j + span):
-            want = want @ M(i)
-        got = _node(w, g, b, Lpad // span + j)
-        scale = want.max(axis=1, keepdims=True)
-        err = np.abs(got - want)
-        bad = err > NODE_RTOL * want + 1e-30 * scale
-        assert not bad.any(), (f"row {b} node {Lpad // span + j}: {bad.sum()} entries off, worst "
-                               f"rel {np.max(err / np.maximum(want, 1e-300))}")
+    PT.check_span_nodes(w, g, b, orc, level=level)
 
 
 @pytest.mark.parametrize("name", list(CASES))

@@ -24,7 +24,7 @@ def test_json_like_full():
     orc = oracle.Oracle(w.aut)
     near = 0
     for b in range(w.B):
-        pos = _sampled_positions(w.L, 6, 100 + b)
+        pos = _sampled_positions(w.L, 16, 100 + b)
         rep = PT.check_row(w, g, b, orc, q_positions=pos)
         near += rep["near"]
         PT.check_leaves(w, g, b, pos[:3], orc)
@@ -33,13 +33,26 @@ def test_json_like_full():
     assert near <= 0.01 * 4 * 2 * w.L
 
 
+def test_json_like_full_negentropy():
+    """The entropy confidence at full size (q not written), checked at
+    sampled positions of every row, with every draw replayed."""
+    w = configs.make(3)
+    PT.log("[full] json-like, entropy confidence, no q")
+    g = PT.run_gpu(w, conf_mode=1, write_q=False)
+    orc = oracle.Oracle(w.aut)
+    for b in range(w.B):
+        pos = _sampled_positions(w.L, 4, 400 + b)
+        rep = PT.check_row(w, g, b, orc, q_positions=pos, conf_mode=1)
+        PT.log(f"[full] json-like negent row {b}: ok ({rep})")
+
+
 def test_random_nfa_full():
     w = configs.make(5)
     PT.log(f"[full] {w.describe()}")
     g = PT.run_gpu(w)
     PT.log(f"[full] nfa: gpu done, logZ {g['logZ']}")
     orc = oracle.Oracle(w.aut)
-    rep = PT.check_row(w, g, 0, orc, q_positions=_sampled_positions(w.L, 4, 7))
+    rep = PT.check_row(w, g, 0, orc, q_positions=_sampled_positions(w.L, 12, 7))
     PT.log(f"[full] nfa row 0: ok ({rep})")
 
 
@@ -54,5 +67,5 @@ def test_range_dfa_full():
     assert (g["status"] == 0).all()
     orc = oracle.Oracle(w.aut)
     for b in (0, w.B - 1):
-        rep = PT.check_row(w, g, b, orc, q_positions=_sampled_positions(w.L, 3, 300 + b))
+        rep = PT.check_row(w, g, b, orc, q_positions=_sampled_positions(w.L, 8, 300 + b))
         PT.log(f"[full] range DFA row {b}: ok ({rep})")

@@ -77,13 +77,17 @@ def test_step_parity(name):
     g = PT.run_gpu(w)
     PT.log(f"[parity] {name}: gpu done, status {g['status']}")
     orc = oracle.Oracle(w.aut)
-    near = 0
+    near = draws = 0
     for b in range(w.B):
         rep = PT.check_row(w, g, b, orc)
         near += rep["near"] if rep else 0
+        draws += rep["draws"] if rep else 0
     if w.aut.S <= 400:
         PT.check_leaves(w, g, 0, range(w.L), orc)
-    PT.log(f"[parity] {name}: ok, near draws {near}")
+    PT.log(f"[parity] {name}: ok, near draws {near} of {draws}")
+    # NEAR draws (u within 1e-6 of every boundary between the two choices)
+    # are exempt from bit-exactness; they must stay rare
+    assert near <= 0.01 * draws
 
 
 @pytest.mark.parametrize("name", ["real-number", "json-small"])
@@ -96,13 +100,20 @@ def test_negentropy_confidence(name):
         PT.check_row(w, g, b, orc, conf_mode=1)
 
 
-def test_confidence_without_q():
+@pytest.mark.parametrize("conf_mode", [0, 1])
+def test_confidence_without_q(conf_mode):
+    """The confidence with q not written, against the oracle's confidence
+    (and the draws against its replay), in both modes."""
     w = _json_small()
-    PT.log("[parity] conf without q")
-    g = PT.run_gpu(w, conf_mode=0, write_q=False)
-    g2 = PT.run_gpu(w, conf_mode=0, write_q=True)
+    PT.log(f"[parity] conf without q, mode {conf_mode}")
+    g = PT.run_gpu(w, conf_mode=conf_mode, write_q=False)
+    assert g["q"] is None
+    orc = oracle.Oracle(w.aut)
+    for b in range(w.B):
+        PT.check_row(w, g, b, orc, conf_mode=conf_mode)
+    g2 = PT.run_gpu(w, conf_mode=conf_mode, write_q=True, table=g["table"])
     np.testing.assert_array_equal(g["tokens"], g2["tokens"])
-    np.testing.assert_allclose(g["conf"], g2["conf"], rtol=1e-6)
+    np.testing.assert_array_equal(g["conf"], g2["conf"])
 
 
 def test_special_automata():
@@ -189,9 +200,9 @@ def test_joint_call_flagged_rows():
 
 
 def test_joint_call_on_another_stream():
-    """The joint call ordered on a non-default stream (its midpoint draws
-    fork to the library's side stream and join back) gives what it gives on
-    the default stream."""
+    """The joint call on a non-default stream (every launch of the call,
+    the midpoint draws riding on the message pass included, goes to the
+    caller's stream) gives what it gives on the default stream."""
     import torch
     w = _json_small()
     PT.log("[joint] non-default stream")

@@ -170,6 +170,17 @@ def test_sizes_and_limits():
     with pytest.raises(fa.FaError) as ei:
         t.sizes(40000, 6)
     assert ei.value.code == _fa.FA_ETOOBIG
+    # lengths at and far beyond the kernels' 24-bit position fields are
+    # rejected before any geometry is formed (no overflow of the padded length)
+    for L in (1 << 24, (1 << 30) + 1, 2 ** 31 - 1):
+        with pytest.raises(fa.FaError) as ei:
+            t.sizes(1, L)
+        assert ei.value.code == _fa.FA_ETOOBIG
+    with pytest.raises(fa.FaError) as ei:
+        t.sizes(1, -1)
+    assert ei.value.code == _fa.FA_EINVAL
+    rc = _fa.lib().fa_span_tree(t.handle, 1, 2 ** 31 - 1, None, None, None, 0, None, None, None)
+    assert rc in (_fa.FA_ETOOBIG, _fa.FA_ESTATE)
 
 
 def test_step_calls_need_an_uploaded_table():

@@ -356,3 +356,182 @@ def test_commit_topk_worked_examples():
     _, f3 = oracle.commit_topk(np.array([[nan, ninf, 0.0]]), np.array([[1, 1, 1]]),
                                np.zeros((1, 3), np.int32), None, steps_left=2)
     np.testing.assert_array_equal(f3, [[1, 0, 1]])
+
+
+# ------------------------------------------------------------- confidence
+@pytest.mark.parametrize("idx", range(10))
+def test_confidence_vs_bruteforce(idx):
+    """Both confidence scores against the brute-force law: PROB is the exact
+    q at the sampled token, NEGENT is sum_v q ln q of the exact q (0 ln 0 =
+    0), at every position of the tiny family."""
+    aut, L = _tiny_family()[idx]
+    rng = np.random.default_rng(700 + idx)
+    p = _softmax(rng.normal(0, 1.5, (L, aut.V))).astype(np.float32)
+    X, prob, Z, q_bf = BF.distribution(aut, p)
+    if Z == 0:
+        return
+    orc = oracle.Oracle(aut)
+    W = orc.edge_weights(p)
+    fb = orc.forward_backward(W)
+    for seed in (1, 2, 3):
+        _, tk, status = orc.sample_tree(p, W, seed, 0)
+        assert status == oracle.OK
+        _, _, conf = orc.marginals(p, fb, None, tk, 0)
+        np.testing.assert_allclose(conf, q_bf[np.arange(L), tk], rtol=1e-12, atol=1e-15)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        h = np.where(q_bf > 0, q_bf * np.log(q_bf), 0.0).sum(axis=1)
+    _, _, conf1 = orc.marginals(p, fb, None, None, 1)
+    np.testing.assert_allclose(conf1, h, rtol=1e-11, atol=1e-14)
+    assert (conf1 <= 0).all()
+
+
+def test_negentropy_closed_forms():
+    """sum_v q ln q at every position of the two hand-derived examples."""
+    g2 = _read_kv("two_token_real_example.txt")
+    aut = A.two_token_real_dfa()
+    p = np.full((2, 2), 0.5, np.float32)
+    orc = oracle.Oracle(aut)
+    fb = orc.forward_backward(orc.edge_weights(p))
+    _, _, conf = orc.marginals(p, fb, None, None, 1)
+    np.testing.assert_allclose(conf, float(g2["negent"][0]), rtol=1e-13)
+    g6 = _read_kv("real_number_uniform.txt")
+    aut = A.real_number_dfa()
+    p = np.full((6, 12), 1.0 / 12.0, np.float32)
+    orc = oracle.Oracle(aut)
+    fb = orc.forward_backward(orc.edge_weights(p))
+    _, _, conf = orc.marginals(p, fb, None, None, 1)
+    np.testing.assert_allclose(conf, float(g6["negent"][0]), rtol=1e-12)
+    # the PROB score of a digit / a dot at every position is its closed-form q
+    tk = np.array([3, 10, 0, 10, 9, 1], np.int32)
+    _, _, conf0 = orc.marginals(p, fb, None, tk, 0)
+    want = np.where(tk == 10, float(g6["q_dot"][0]), float(g6["q_digit"][0]))
+    np.testing.assert_allclose(conf0, want, rtol=1e-12)
+
+
+# ------------------------------------------------------ replay NEAR / HARD
+def test_judge_draw_hand_built():
+    """The verifier's split on hand-built weight vectors: a differing choice
+    is NEAR only when every CDF boundary between the two choices lies within
+    1e-6 of u; 5e-5 away is HARD and counts as fp32-margin; a zero-weight
+    choice, a choice past the candidates, or a real-weight candidate between
+    the two choices is HARD."""
+    u = 0.375
+    for d, verdict, margin in ((5e-7, 1, 0), (-5e-7, 1, 0), (5e-5, 2, 1), (-5e-5, 2, 1),
+                               (5e-3, 2, 0)):
+        # two candidates, boundary C_0 / T = u + d
+        w = np.array([u + d, 1.0 - (u + d)])
+        mine = 0 if d > 0 else 1
+        other = 1 - mine
+        assert oracle.judge_draw(w, u, mine) == (mine, 0, 0)
+        assert oracle.judge_draw(w, u, other) == (mine, verdict, margin)
+    # zero-weight candidates between the two choices share the boundary: NEAR
+    w = np.array([u + 5e-7, 0.0, 0.0, 1.0 - u - 5e-7])
+    assert oracle.judge_draw(w, u, 3) == (0, 1, 0)
+    # a zero-weight choice is HARD however close the boundary
+    assert oracle.judge_draw(w, u, 1)[1] == 2
+    assert oracle.judge_draw(w, u, 2)[1] == 2
+    # a choice past the candidate list is HARD
+    assert oracle.judge_draw(w, u, 4)[1] == 2
+    # first boundary at u + 5e-7, but a candidate of weight 0.3 lies between
+    # the two choices: the second boundary is far from u, so HARD
+    w = np.array([u + 5e-7, 0.3, 1.0 - u - 0.3 - 5e-7])
+    assert oracle.judge_draw(w, u, 0) == (0, 0, 0)
+    assert oracle.judge_draw(w, u, 2)[1] == 2
+    assert oracle.judge_draw(w, u, 1) == (0, 1, 0)
+    # vanishing weights: the oracle has no choice, any claim is HARD
+    assert oracle.judge_draw(np.zeros(3), u, 0)[0:2] == (-1, 2)
+
+
+def _u_from_philox(seed, b, level, node):
+    """u from the published Philox4x32-10 (pinned above by its known-answer
+    vectors): first output word of counter (b, level, node, 0) under the key
+    (seed low, seed high), top 24 bits scaled by 2^-24."""
+    r = oracle.philox4x32_10([b, level, node, 0], [seed & 0xFFFFFFFF, seed >> 32])
+    return (int(r[0]) >> 8) / float(1 << 24)
+
+
+def test_replay_near_and_hard_on_a_token_draw():
+    """End to end through the replay walker: the universal automaton with one
+    position (Lpad = 1, K = 0, the token stage is level 1, node 0) and p set
+    so that the boundary between tokens 0 and 2 sits just above u; the
+    middle token gets weight 0 or a real weight."""
+    aut = A.universal_automaton(3)
+    seed = 0xC0FFEE
+    u = _u_from_philox(seed, 0, 1, 0)
+    assert 0.01 < u < 0.98
+    orc = oracle.Oracle(aut)
+    states = np.zeros(2, np.int32)
+    # want = (hard, near, margin) counts of the replay
+    for d, mid, want in ((5e-7, 0.0, (0, 1, 0)), (5e-5, 0.0, (1, 0, 1)), (3e-3, 0.0, (1, 0, 0)),
+                         (5e-7, 0.2, (1, 0, 0))):
+        x = np.float32(u + d)
+        m = np.float32(mid)
+        p = np.array([[x, m, np.float32(1.0) - x - m]], np.float32)
+        W = orc.edge_weights(p)
+        st, tk, status = orc.sample_tree(p, W, seed, 0)
+        assert status == oracle.OK and tk[0] == 0
+        rep = orc.replay(p, W, seed, 0, states, np.array([2], np.int32))
+        assert (rep["hard"], rep["near"], rep["margin"]) == want, (d, mid, rep)
+        assert rep["draws"] == 2  # the root over F = {0}, then the token
+
+
+def _two_state_dfa():
+    # state 0: token 0 -> 0, token 1 -> 1;  state 1: token 2 -> 0, tokens
+    # 0 and 1 -> 1;  accepting {0, 1}
+    edges = [(0, 0, [0]), (0, 1, [1]), (1, 0, [2]), (1, 1, [0, 1])]
+    return A._pack(2, 3, 0, [0, 1], edges, name="two-state DFA")
+
+
+@pytest.mark.parametrize("L", [4, 3, 8])
+def test_tree_sampler_by_hand(L):
+    """Every draw of the tree-order sampler recomputed by hand: the
+    transition matrices from the raw edge list, span products by numpy,
+    inverse CDFs over ascending ids, and the uniforms keyed (b, level, heap
+    index - 2^(level-1)) for the midpoints, (b, 0, 0) for the final state and
+    (b, K+1, i) for the tokens."""
+    aut = _two_state_dfa()
+    rng = np.random.default_rng(41)
+    p = _softmax(rng.normal(0, 1, (L, aut.V))).astype(np.float32)
+    c = np.zeros((aut.S, aut.V, aut.S))
+    for e in range(aut.E):
+        c[aut.src[e], aut.edge_label(e), aut.dst[e]] += 1.0
+    Lpad = 1 << (L - 1).bit_length()
+    K = Lpad.bit_length() - 1
+    M = [np.einsum("avb,v->ab", c, p[i].astype(np.float64)) if i < L else np.eye(aut.S)
+         for i in range(Lpad)]
+
+    def span(l, r):
+        out = np.eye(aut.S)
+        for i in range(l, r):
+            out = out @ M[i]
+        return out
+
+    def icdf(w, u):
+        C = np.cumsum(w)
+        return int(np.flatnonzero((C > u * C[-1]) & (w > 0))[0])
+
+    orc = oracle.Oracle(aut)
+    W = orc.edge_weights(p)
+    for seed in (5, 6, 2 ** 40 + 9):
+        for b in (0, 3):
+            z = [-1] * (Lpad + 1)
+            z[0] = aut.start
+            F = sorted(aut.accept.tolist())
+            root = span(0, Lpad)[z[0]]
+            z[Lpad] = F[icdf(np.array([root[f] for f in F]), _u_from_philox(seed, b, 0, 0))]
+            for lev in range(1, K + 1):
+                width = Lpad >> (lev - 1)
+                for heap in range(1 << (lev - 1), 1 << lev):
+                    node = heap - (1 << (lev - 1))
+                    l, r = node * width, node * width + width
+                    m = (l + r) // 2
+                    w = span(l, m)[z[l]] * span(m, r)[:, z[r]]
+                    z[m] = icdf(w, _u_from_philox(seed, b, lev, node))
+            tk = []
+            for i in range(L):
+                w = p[i].astype(np.float64) * c[z[i], :, z[i + 1]]
+                tk.append(icdf(w, _u_from_philox(seed, b, K + 1, i)))
+            st, to, status = orc.sample_tree(p, W, seed, b)
+            assert status == oracle.OK
+            np.testing.assert_array_equal(st, z[:L + 1])
+            np.testing.assert_array_equal(to, tk)
