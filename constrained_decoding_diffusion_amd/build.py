@@ -14,12 +14,12 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["table.cpp", "api.cpp", "emission.hip", "tree.hip", "sample.hip", "marginals.hip",
-           "commit.hip"]
+           "commit.hip", "noalloc.hip"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", f"-I{CSRC}"]
 # packed fp32 instructions are kept out of every gfx950 code object
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-fno-gpu-rdc", "-munsafe-fp-atomics"]
+          "-fno-gpu-rdc"]
 
 
 def _obj(src: str, build_dir: str) -> str:
