@@ -10,5 +10,5 @@ from ._fa import (  # noqa: F401
     FA_PROF_EMISSION_DENSE, FA_PROF_MARG_Q, FA_PROF_NONE, FA_PROF_TREE_LEVEL1,
     FA_ROW_BADPROB, FA_ROW_INFEASIBLE, FA_ROW_UNDERFLOW, FaError, StepBuffers, Table,
     build_transitions, commit, generate, lib, marginals, profile_kernel, sample, sample_marginals,
-    span_tree, step,
+    span_tree, span_tree_noalloc, step,
 )

@@ -23,7 +23,9 @@ FA_PROF_NONE, FA_PROF_EMISSION_DENSE, FA_PROF_TREE_LEVEL1, FA_PROF_MARG_Q = rang
 
 EXPORTS = ["fa_compile_table", "fa_table_upload", "fa_table_destroy", "fa_table_info",
            "fa_table_state_map", "fa_sizes", "fa_build_transitions", "fa_span_tree", "fa_sample",
-           "fa_marginals", "fa_sample_marginals", "fa_commit", "fa_strerror", "fa_profile_kernel"]
+           "fa_marginals", "fa_sample_marginals", "fa_commit", "fa_strerror", "fa_profile_kernel",
+           "fa_span_tree_noalloc"]
+FA_SPAN_TREE_NOALLOC_MAX_BYTES = 8 << 20
 
 
 class FaError(RuntimeError):
@@ -54,6 +56,7 @@ def lib():
     L.fa_sizes.argtypes = [P, I32, I32, P, P, P]
     L.fa_build_transitions.argtypes = [P, P, I32, I32, P, P, P, SZ, P, P]
     L.fa_span_tree.argtypes = [P, I32, I32, P, P, P, SZ, P, P, P]
+    L.fa_span_tree_noalloc.argtypes = [P, I32, I32, P, P, P, P, P]
     L.fa_sample.argtypes = [P, P, I32, I32, P, P, U64, P, P, P, SZ, P, P]
     L.fa_marginals.argtypes = [P, P, I32, I32, P, P, P, P, I32, P, P, P, SZ, P, P]
     L.fa_sample_marginals.argtypes = [P, P, I32, I32, P, P, P, U64, I32, P, P, P, P, P, SZ, P, P]
@@ -175,6 +178,14 @@ def span_tree(table: Table, bufs: StepBuffers, stream):
     _check("fa_span_tree", lib().fa_span_tree(
         table.handle, bufs.B, bufs.L, _ptr(bufs.tree), _ptr(bufs.meta), _ptr(bufs.ws),
         bufs.ws.numel(), _ptr(bufs.logZ), _ptr(bufs.status), C.c_void_p(stream)))
+
+
+def span_tree_noalloc(table: Table, bufs: StepBuffers, stream):
+    """fa_span_tree_noalloc: the span tree with its scratch in the library's
+    own device array (bufs.ws is not used)."""
+    _check("fa_span_tree_noalloc", lib().fa_span_tree_noalloc(
+        table.handle, bufs.B, bufs.L, _ptr(bufs.tree), _ptr(bufs.meta), _ptr(bufs.logZ),
+        _ptr(bufs.status), C.c_void_p(stream)))
 
 
 def sample(table: Table, p, bufs: StepBuffers, seed: int, stream):

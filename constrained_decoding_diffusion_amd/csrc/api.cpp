@@ -18,9 +18,6 @@ int ready(const fa_table *t)
 
 int hip_rc(int e) { return e == 0 ? FA_OK : FA_EHIP; }
 
-// grids put (row, node) pairs in their second dimension
-bool grid_fits(const Geometry &g) { return (int64_t)g.B * g.Lpad * 2 <= 65535 && g.L < (1 << 24); }
-
 struct ProfHook {
     int which = FA_PROF_NONE;
     hipEvent_t start = nullptr, stop = nullptr;

@@ -201,6 +201,12 @@ struct Geometry {
 // FA_ETOOBIG for L >= 2^24
 int make_geometry(const HostTable &t, int32_t B, int32_t L, Geometry *g);
 
+// grids put (row, node) pairs in their second dimension
+inline bool grid_fits(const Geometry &g)
+{
+    return (int64_t)g.B * g.Lpad * 2 <= 65535 && g.L < (1 << 24);
+}
+
 // Workspace layout (bytes from the start of ws), sized for the largest user.
 struct WsLayout {
     size_t dpart = 0, dval = 0, psel = 0, cutp = 0, val = 0;  // emission reduce

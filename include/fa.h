@@ -317,6 +317,32 @@ int fa_commit(int32_t B, int32_t L, int32_t V, const float *conf, const int32_t 
               int32_t steps_left, int32_t *committed, int32_t *fresh, float *p,
               const int32_t *row_status, fa_stream_t stream);
 
+/*
+ * fa_span_tree_noalloc - fa_span_tree for callers that cannot allocate
+ * device memory: code under HIP graph capture, serving loops and harnesses
+ * that forbid hipMalloc.  The same kernels and outputs as fa_span_tree; the
+ * split-K partial tiles of the upper levels (the only scratch memory the
+ * span tree uses) live in a library-owned device array of
+ * FA_SPAN_TREE_NOALLOC_MAX_BYTES (8 MiB), one copy per GPU, held until the
+ * process ends.  A level is split along K only while rows x nodes x splits
+ * x (Sp/64)^2 <= 512, so its partial tiles never exceed 2^21 floats: every
+ * table and size fa_span_tree takes fits.  No workspace argument; the call
+ * allocates nothing.
+ *   arguments  as in fa_span_tree (tree, meta, logZ, row_status are the
+ *              caller's)
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (different streams, or different threads) race and must not be
+ * issued.  The array is fully written before it is read by each call.
+ * Errors: FA_EINVAL (also for a table whose first span level is formed from
+ * the pair values, fa_table_info [15] = 1: that level reads the workspace
+ * fa_build_transitions wrote, so such tables take fa_span_tree),
+ * FA_ETOOBIG (the step's partial tiles exceed FA_SPAN_TREE_NOALLOC_MAX_BYTES,
+ * or the grid limits of fa_span_tree), FA_ESTATE, FA_EHIP.
+ */
+#define FA_SPAN_TREE_NOALLOC_MAX_BYTES ((size_t)8 << 20)
+int fa_span_tree_noalloc(const fa_table *t, int32_t B, int32_t L, float *tree, int32_t *meta,
+                         double *logZ, int32_t *row_status, fa_stream_t stream);
+
 /* fa_strerror - static description of an error code. */
 const char *fa_strerror(int code);
 

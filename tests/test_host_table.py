@@ -221,3 +221,18 @@ def test_profile_hook_arguments():
     fake = C.c_void_p(0x1000)
     assert lib.fa_profile_kernel(_fa.FA_PROF_EMISSION_DENSE, fake, fake) == _fa.FA_OK
     assert lib.fa_profile_kernel(_fa.FA_PROF_NONE, None, None) == _fa.FA_OK
+
+
+def test_noalloc_span_tree_argument_checks():
+    """fa_span_tree_noalloc refuses, before launching anything, a table whose
+    first span level reads the emission workspace, and a table not uploaded."""
+    lib = _fa.lib()
+    aut = A.random_dfa(np.random.default_rng(3), 12, 40, 3, 0.4)
+    sparse = fa.Table.from_automaton(aut, first_level="sparse")
+    assert sparse.info["first_sparse"] == 1
+    call = lambda t, B, L: lib.fa_span_tree_noalloc(t, B, L, None, None, None, None, None)
+    assert call(sparse.handle, 1, 8) == _fa.FA_EINVAL
+    dense = fa.Table.from_automaton(aut, first_level="dense")
+    assert call(dense.handle, 1, 8) == _fa.FA_ESTATE
+    assert call(None, 1, 8) == _fa.FA_EINVAL
+    assert _fa.FA_SPAN_TREE_NOALLOC_MAX_BYTES == 8 << 20
