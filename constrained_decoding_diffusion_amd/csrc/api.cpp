@@ -18,6 +18,20 @@ int ready(const fa_table *t)
 
 int hip_rc(int e) { return e == 0 ? FA_OK : FA_EHIP; }
 
+bool conf_mode_ok(int32_t m)
+{
+    return m == FA_CONF_PROB || m == FA_CONF_NEGENT || m == FA_CONF_UNCONSTRAINED;
+}
+
+// the score whose path computes q: the unconstrained score runs the PROB path
+int32_t base_mode(int32_t m) { return m == FA_CONF_UNCONSTRAINED ? FA_CONF_PROB : m; }
+
+int sample_marginals_base(const DevTable &d, const Geometry &g, const float *p, const float *tree,
+                          const int32_t *meta, const double *logZ, uint64_t seed,
+                          int32_t conf_mode, int32_t *states, int32_t *tokens, float *q,
+                          float *conf, uint8_t *wb, const WsLayout &w, int32_t *row_status,
+                          fa_stream_t stream);
+
 struct ProfHook {
     int which = FA_PROF_NONE;
     hipEvent_t start = nullptr, stop = nullptr;
@@ -118,14 +132,19 @@ extern "C" int fa_marginals(const fa_table *t, const float *p, int32_t B, int32_
     Geometry g;
     if (int grc = make_geometry(t->h, B, L, &g)) return grc;
     if (!grid_fits(g)) return FA_ETOOBIG;
-    if (conf_mode != FA_CONF_PROB && conf_mode != FA_CONF_NEGENT) return FA_EINVAL;
+    if (!conf_mode_ok(conf_mode)) return FA_EINVAL;
     if (B == 0 || L == 0) return FA_OK;
     WsLayout w = ws_layout(t->h, g);
     if (!p || !tree || !meta || !logZ || !conf || !row_status || !ws || ws_bytes < w.total)
         return FA_EINVAL;
-    if (conf_mode == FA_CONF_PROB && !tokens) return FA_EINVAL;
-    return hip_rc(launch_marginals(t->h.device_view(), g, p, tree, meta, logZ, tokens, conf_mode, q,
-                                   conf, (uint8_t *)ws, w, row_status, stream));
+    if (conf_mode != FA_CONF_NEGENT && !tokens) return FA_EINVAL;
+    const DevTable d = t->h.device_view();
+    // the unconstrained score takes the PROB path for q, then its own conf
+    int rc2 = launch_marginals(d, g, p, tree, meta, logZ, tokens, base_mode(conf_mode), q, conf,
+                               (uint8_t *)ws, w, row_status, stream);
+    if (!rc2 && conf_mode == FA_CONF_UNCONSTRAINED)
+        rc2 = launch_conf_unconstrained(d, g, p, tokens, row_status, conf, stream);
+    return hip_rc(rc2);
 }
 
 extern "C" int fa_sample_marginals(const fa_table *t, const float *p, int32_t B, int32_t L,
@@ -139,18 +158,36 @@ extern "C" int fa_sample_marginals(const fa_table *t, const float *p, int32_t B,
     Geometry g;
     if (int grc = make_geometry(t->h, B, L, &g)) return grc;
     if (!grid_fits(g)) return FA_ETOOBIG;
-    if (conf_mode != FA_CONF_PROB && conf_mode != FA_CONF_NEGENT) return FA_EINVAL;
+    if (!conf_mode_ok(conf_mode)) return FA_EINVAL;
     if (B == 0) return FA_OK;
     WsLayout w = ws_layout(t->h, g);
     if (!states || !row_status || !ws || ws_bytes < w.total) return FA_EINVAL;
     if (L > 0 && (!p || !tree || !meta || !logZ || !tokens || !conf)) return FA_EINVAL;
     const DevTable d = t->h.device_view();
-    uint8_t *wb = (uint8_t *)ws;
+    rc = sample_marginals_base(d, g, p, tree, meta, logZ, seed, base_mode(conf_mode), states,
+                               tokens, q, conf, (uint8_t *)ws, w, row_status, stream);
+    if (!rc && L > 0 && conf_mode == FA_CONF_UNCONSTRAINED)
+        rc = launch_conf_unconstrained(d, g, p, tokens, row_status, conf, stream);
+    return hip_rc(rc);
+}
+
+namespace {
+
+// fa_sample_marginals for the PROB and NEGENT scores; returns 0 or a
+// hipError_t value
+int sample_marginals_base(const DevTable &d, const Geometry &g, const float *p, const float *tree,
+                          const int32_t *meta, const double *logZ, uint64_t seed,
+                          int32_t conf_mode, int32_t *states, int32_t *tokens, float *q,
+                          float *conf, uint8_t *wb, const WsLayout &w, int32_t *row_status,
+                          fa_stream_t stream)
+{
+    const int32_t L = g.L;
+    int rc;
     if (L == 0 || !marg_joint_ok(d, g, p, q, conf_mode, w)) {
         rc = launch_sample(d, g, p, tree, meta, seed, states, tokens, wb, w, row_status, stream);
-        if (rc || L == 0) return hip_rc(rc);
-        return hip_rc(launch_marginals(d, g, p, tree, meta, logZ, tokens, conf_mode, q, conf, wb,
-                                       w, row_status, stream));
+        if (rc || L == 0) return rc;
+        return launch_marginals(d, g, p, tree, meta, logZ, tokens, conf_mode, q, conf, wb, w,
+                                row_status, stream);
     }
     // midpoints riding on the message pass; q with the draws' chunk sums;
     // the token draws; the confidence of the drawn tokens and the rows the
@@ -168,8 +205,10 @@ extern "C" int fa_sample_marginals(const fa_table *t, const float *p, int32_t B,
     if (!rc)
         rc = launch_marg_out(d, g, p, logZ, tokens, conf_mode, q, conf, wb, w, 2, row_status,
                              stream, states);
-    return hip_rc(rc);
+    return rc;
 }
+
+}  // namespace
 
 extern "C" int fa_commit(int32_t B, int32_t L, int32_t V, const float *conf,
                          const int32_t *tokens, int32_t steps_left, int32_t *committed,

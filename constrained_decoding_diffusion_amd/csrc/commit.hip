@@ -13,29 +13,41 @@ namespace {
 
 constexpr int kCommitThreads = 256;
 
-// One workgroup per row.  Masked positions (not committed, a sampled token)
-// and their confidence (NaN read as -inf) go to LDS; each masked position's
-// rank is the number of masked positions with a larger confidence, or an
-// equal one and a lower index, and it is committed when its rank is below k.
-// A flagged row commits nothing.
+// One workgroup per row.  Each position gets a 64-bit key: for a masked
+// position (not committed, a sampled token) the confidence mapped to an
+// order-preserving integer and complemented (so larger confidence sorts
+// first; NaN is read as -inf) above the position (so ties go to the lower
+// position), for any other position all ones.  The keys are sorted in LDS
+// by a bitonic network over the next power of two >= L (O(L log^2 L)), and
+// the first k keys name the committed positions.  A flagged row commits
+// nothing.
+__device__ inline uint32_t ordered_bits(float c)
+{
+    const uint32_t u = __float_as_uint(c == c ? c : -INFINITY);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // ascending as c ascends
+}
+
 __global__ __launch_bounds__(kCommitThreads) void commit_select(
-    int L, const float *__restrict__ conf, const int32_t *__restrict__ tokens, int steps_left,
-    int32_t *__restrict__ committed, int32_t *__restrict__ fresh,
+    int L, int Lp2, const float *__restrict__ conf, const int32_t *__restrict__ tokens,
+    int steps_left, int32_t *__restrict__ committed, int32_t *__restrict__ fresh,
     const int32_t *__restrict__ status)
 {
-    extern __shared__ float cs[];  // [L] confidence | [L] masked flags
-    int *mk = reinterpret_cast<int *>(cs + L);
+    extern __shared__ unsigned long long keys[];  // [Lp2] keys | [L] selected flags
+    int *sel = reinterpret_cast<int *>(keys + Lp2);
     __shared__ int sh_n[kCommitThreads / 64];
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t row = (size_t)b * L;
     const bool flagged = status && status[b] != 0;
     int n = 0;
-    for (int i = tid; i < L; i += kCommitThreads) {
-        const bool m = !flagged && committed[row + i] == 0 && tokens[row + i] >= 0;
-        const float c = conf[row + i];
-        cs[i] = c == c ? c : -INFINITY;
-        mk[i] = m;
-        n += m;
+    for (int i = tid; i < Lp2; i += kCommitThreads) {
+        unsigned long long key = ~0ull;
+        if (i < L) {
+            const bool m = !flagged && committed[row + i] == 0 && tokens[row + i] >= 0;
+            if (m) key = ((unsigned long long)(~ordered_bits(conf[row + i])) << 32) | (uint32_t)i;
+            n += m;
+            sel[i] = 0;
+        }
+        keys[i] = key;
     }
     n = wave_sum_i(n);
     if (lane == 0) sh_n[wave] = n;
@@ -43,15 +55,27 @@ __global__ __launch_bounds__(kCommitThreads) void commit_select(
     n = 0;
     for (int w = 0; w < kCommitThreads / 64; ++w) n += sh_n[w];
     const int k = steps_left <= 1 ? n : (n + steps_left - 1) / steps_left;
-    for (int i = tid; i < L; i += kCommitThreads) {
-        int take = 0;
-        if (mk[i]) {
-            const float ci = cs[i];
-            int rank = 0;
-            for (int j = 0; j < L; ++j)
-                rank += mk[j] && (cs[j] > ci || (cs[j] == ci && j < i));
-            take = rank < k;
+    // bitonic sort, ascending: stage (size, stride); each thread takes the
+    // pairs (i, i ^ stride) with i < i ^ stride
+    for (int size = 2; size <= Lp2; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int t = tid; t < Lp2 / 2; t += kCommitThreads) {
+                const int i = 2 * t - (t & (stride - 1));  // bit `stride` of i clear
+                const int j = i + stride;
+                const bool up = (i & size) == 0;
+                const unsigned long long a = keys[i], c = keys[j];
+                if ((a > c) == up) {
+                    keys[i] = c;
+                    keys[j] = a;
+                }
+            }
+            __syncthreads();
         }
+    }
+    for (int r = tid; r < k; r += kCommitThreads) sel[(int)(keys[r] & 0xffffffffu)] = 1;
+    __syncthreads();
+    for (int i = tid; i < L; i += kCommitThreads) {
+        const int take = sel[i];
         fresh[row + i] = take;
         if (take) committed[row + i] = 1;
     }
@@ -85,15 +109,17 @@ int launch_commit(int B, int L, int V, const float *conf, const int32_t *tokens,
                   void *stream)
 {
     hipStream_t st = (hipStream_t)stream;
-    const size_t lds = (size_t)L * (sizeof(float) + sizeof(int));
+    int Lp2 = 1;
+    while (Lp2 < L) Lp2 <<= 1;
+    const size_t lds = (size_t)Lp2 * sizeof(unsigned long long) + (size_t)L * sizeof(int);
     hipError_t e;
     if (lds > 48 * 1024) {
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(&commit_select),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return (int)e;
     }
-    commit_select<<<B, kCommitThreads, lds, st>>>(L, conf, tokens, steps_left, committed, fresh,
-                                                  status);
+    commit_select<<<B, kCommitThreads, lds, st>>>(L, Lp2, conf, tokens, steps_left, committed,
+                                                  fresh, status);
     e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
     commit_onehot<<<dim3(L, B), kCommitThreads, 0, st>>>(L, V, fresh, tokens, p);

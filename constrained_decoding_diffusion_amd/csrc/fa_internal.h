@@ -247,6 +247,10 @@ int prof_mark(int which, bool begin, void *stream);
 // Split of one tree level's products along K (upper levels with few
 // products): 1 = no split.
 int tree_ksplit(const Geometry &g, int level);
+// conf = p at the sampled token (FA_CONF_UNCONSTRAINED), after the PROB path
+int launch_conf_unconstrained(const DevTable &d, const Geometry &g, const float *p,
+                              const int32_t *tokens, const int32_t *status, float *conf,
+                              void *stream);
 int launch_sample(const DevTable &d, const Geometry &g, const float *p, const float *tree,
                   const int32_t *meta, uint64_t seed, int32_t *states, int32_t *tokens,
                   uint8_t *ws, const WsLayout &w, int32_t *status, void *stream);

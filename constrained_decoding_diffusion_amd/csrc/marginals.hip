@@ -1196,6 +1196,34 @@ bool q_streamed(const DevTable &d, const float *p, const float *q, const WsLayou
 
 }  // namespace
 
+namespace {
+
+// the unconstrained score: the denoiser's probability of the sampled token,
+// -inf on flagged rows (as the constrained score gives them)
+__global__ void conf_unconstrained(const float *__restrict__ p, int V, int L, long long npos,
+                                   const int32_t *__restrict__ tokens,
+                                   const int32_t *__restrict__ status, float *__restrict__ conf)
+{
+    const long long pos = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (pos >= npos) return;
+    const int b = (int)(pos / L);
+    const int tok = tokens[pos];
+    conf[pos] = (status[b] == 0 && tok >= 0 && tok < V) ? p[pos * V + tok] : -INFINITY;
+}
+
+}  // namespace
+
+int launch_conf_unconstrained(const DevTable &d, const Geometry &g, const float *p,
+                              const int32_t *tokens, const int32_t *status, float *conf,
+                              void *stream)
+{
+    const long long npos = (long long)g.B * g.L;
+    if (npos == 0) return 0;
+    conf_unconstrained<<<(unsigned)((npos + 255) / 256), 256, 0, (hipStream_t)stream>>>(
+        p, d.V, g.L, npos, tokens, status, conf);
+    return (int)hipGetLastError();
+}
+
 bool marg_joint_ok(const DevTable &d, const Geometry &g, const float *p, const float *q,
                    int32_t conf_mode, const WsLayout &w)
 {

@@ -86,7 +86,7 @@ enum {
                                    first level sparse) */
 };
 
-enum { FA_CONF_PROB = 0, FA_CONF_NEGENT = 1 };
+enum { FA_CONF_PROB = 0, FA_CONF_NEGENT = 1, FA_CONF_UNCONSTRAINED = 2 };
 
 /*
  * fa_compile_table - validate and compile an automaton (host only).
@@ -249,13 +249,17 @@ int fa_sample(const fa_table *t, const float *p, int32_t B, int32_t L, const flo
  *   q[b][i][v] = p[b][i][v] sum_{(a, a') pairs holding v} c alpha_i[a]
  *                beta_{i+1}[a'] / Z,
  *   conf[b][i] = q[b][i][tokens[b][i]]   (FA_CONF_PROB), or
- *              = sum_v q ln q            (FA_CONF_NEGENT, 0 ln 0 = 0).
+ *              = sum_v q ln q            (FA_CONF_NEGENT, 0 ln 0 = 0), or
+ *              = p[b][i][tokens[b][i]]   (FA_CONF_UNCONSTRAINED: the
+ *                denoiser's own probability of the sampled token, the
+ *                score the constrained marginal is compared with;
+ *                papernotes 消融实验).
  * Cite: papernotes 关键设计 3 (constrained marginals as the confidence that
  * decides which positions are committed); paperfeed "Two immediate bonuses"
  * (LLaDA: highest probability, Dream: lowest entropy).
  *   logZ    device double [B] from fa_span_tree
- *   tokens  device int32 [B][L] (needed for FA_CONF_PROB; may be NULL for
- *           FA_CONF_NEGENT)
+ *   tokens  device int32 [B][L] (needed for FA_CONF_PROB and
+ *           FA_CONF_UNCONSTRAINED; may be NULL for FA_CONF_NEGENT)
  *   q       device fp32 [B][L][V] or NULL (not written)
  *   conf    device fp32 [B][L]
  *   ws      the workspace this step's fa_build_transitions wrote (the leaf

@@ -209,7 +209,9 @@ int or_forward_backward(const or_aut *A, const double *W, int32_t L,
  * positions listed in pos[0..npos); q is [npos][V].  lognorm[k] receives
  * ln(normalizer) + alog_i + blog_{i+1}, which equals log Z in exact
  * arithmetic.  conf (optional): mode 0 = q at tokens[i] (the sampled
- * token's constrained probability), mode 1 = sum_v q ln q (0 ln 0 = 0). */
+ * token's constrained probability), mode 1 = sum_v q ln q (0 ln 0 = 0),
+ * mode 2 = p at tokens[i] (the unconstrained probability of the sampled
+ * token, the comparison score of [P2 消融实验]). */
 int or_marginals(const or_aut *A, const float *p, int32_t L, const double *alpha,
                  const double *alog, const double *beta, const double *blog,
                  const int32_t *pos, int32_t npos, double *q, double *lognorm,
@@ -244,6 +246,9 @@ int or_marginals(const or_aut *A, const float *p, int32_t L, const double *alpha
         if (conf) {
             if (conf_mode == 0) {
                 conf[k] = (tokens && nrm > 0.0) ? qk[tokens[i]] : -INFINITY;
+            } else if (conf_mode == 2) {
+                conf[k] = (tokens && nrm > 0.0 && tokens[i] >= 0) ? (double)row[tokens[i]]
+                                                                  : -INFINITY;
             } else {
                 double h = 0.0;
                 for (int32_t v = 0; v < V; ++v) if (qk[v] > 0.0) h += qk[v] * log(qk[v]);

@@ -86,6 +86,8 @@ def check_row(w, g, b, orc=None, q_positions=None, check_q=True, conf_mode=0):
         cg = g["conf"][b, pos].astype(np.float64)
         if conf_mode == 0:
             np.testing.assert_allclose(cg, conf, rtol=1e-4, atol=1e-12)
+        elif conf_mode == 2:   # p at the sampled token: a copy of an fp32 value
+            np.testing.assert_array_equal(cg, conf)
         else:
             np.testing.assert_allclose(cg, conf, rtol=1e-4, atol=1e-6)
     return rep

@@ -17,11 +17,14 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("V", [1000, 999])
 @pytest.mark.parametrize("steps_left", [3, 1])
-def test_commit_matches_definition(V, steps_left):
+@pytest.mark.parametrize("L", [300, 8192])
+def test_commit_matches_definition(V, steps_left, L):
+    """300: more positions than threads per workgroup, a ragged power of
+    two for the sort; 8192: the longest row the selection takes."""
     import torch
     import constrained_decoding_diffusion_amd as fa
-    rng = np.random.default_rng(100 + V + steps_left)
-    B, L = 3, 300  # more positions than threads per workgroup
+    rng = np.random.default_rng(100 + V + steps_left + L)
+    B = 3
     conf = np.round(rng.random((B, L)), 1).astype(np.float32)  # many ties
     conf[0, :5] = -np.inf
     conf[1, 7] = np.nan
@@ -30,7 +33,7 @@ def test_commit_matches_definition(V, steps_left):
     committed = (rng.random((B, L)) < 0.3).astype(np.int32)
     status = np.array([0, 0, 0], np.int32)
     p = rng.random((B, L, V)).astype(np.float32)
-    PT.log(f"[commit] V={V} steps_left={steps_left}")
+    PT.log(f"[commit] V={V} steps_left={steps_left} L={L}")
     for flagged in (False, True):
         st = status.copy()
         if flagged:
@@ -89,7 +92,8 @@ def _loop(w, T, conf_mode):
 
 
 @pytest.mark.parametrize("name,T,conf_mode", [("json-small", 6, 0), ("random-dfa", 8, 0),
-                                               ("real-number", 3, 1)])
+                                               ("real-number", 3, 1), ("random-dfa", 8, 2),
+                                               ("json-small", 4, 2)])
 def test_generation_loop(name, T, conf_mode):
     import torch
     import constrained_decoding_diffusion_amd as fa

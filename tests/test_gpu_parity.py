@@ -116,6 +116,24 @@ def test_confidence_without_q(conf_mode):
     np.testing.assert_array_equal(g["conf"], g2["conf"])
 
 
+@pytest.mark.parametrize("name", ["json-small", "random-dfa", "range-small", "nfa-small"])
+@pytest.mark.parametrize("joint", [True, False])
+def test_unconstrained_confidence(name, joint):
+    """FA_CONF_UNCONSTRAINED: conf is p at the sampled token (bit for bit),
+    -inf on flagged rows; draws, log Z and q are those of the PROB call."""
+    w = CASES[name]()
+    PT.log(f"[parity-mf] {name} joint {joint}")
+    g = PT.run_gpu(w, conf_mode=2, joint=joint)
+    orc = oracle.Oracle(w.aut)
+    for b in range(w.B):
+        PT.check_row(w, g, b, orc, conf_mode=2)
+    rows = np.arange(w.B)[:, None]
+    np.testing.assert_array_equal(g["conf"], w.p[rows, np.arange(w.L)[None, :], g["tokens"]])
+    g0 = PT.run_gpu(w, conf_mode=0, joint=joint, table=g["table"])
+    for k in ("status", "logZ", "states", "tokens", "q"):
+        np.testing.assert_array_equal(g[k], g0[k], err_msg=k)
+
+
 def test_special_automata():
     rng = np.random.default_rng(12)
     V, L = 300, 19

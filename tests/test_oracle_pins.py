@@ -406,6 +406,9 @@ def test_negentropy_closed_forms():
     _, _, conf0 = orc.marginals(p, fb, None, tk, 0)
     want = np.where(tk == 10, float(g6["q_dot"][0]), float(g6["q_digit"][0]))
     np.testing.assert_allclose(conf0, want, rtol=1e-12)
+    # the unconstrained score ignores the automaton: fp32(1/12) for any token
+    _, _, conf2 = orc.marginals(p, fb, None, tk, 2)
+    np.testing.assert_array_equal(conf2, float(np.float32(1.0 / 12.0)))
 
 
 # ------------------------------------------------------ replay NEAR / HARD
