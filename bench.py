@@ -135,22 +135,200 @@ class HipEvents:
         self.hip.hipEventDestroy(self.C.c_void_p(ev))
 
 
-def cpu_baseline(w):
+def cpu_info():
+    """CPU model (from /proc/cpuinfo), logical CPUs, and the CPUs this
+    process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
+    return model, os.cpu_count(), affinity
+
+
+def cpu_baseline(w, reps=3):
     """The serial fp64 oracle, single thread, on one full step of the same
     workload (all B rows): emission weights, forward-backward, tree-order
-    sampling and marginals at every position."""
+    sampling and marginals at every position.  Median of `reps` runs."""
     import oracle
     orc = oracle.Oracle(w.aut)
-    t0 = time.perf_counter()
-    for b in range(w.B):
-        W = orc.edge_weights(w.p[b])
-        fb = orc.forward_backward(W)
-        st, tk, _ = orc.sample_tree(w.p[b], W, w.seed, b)
-        orc.marginals(w.p[b], fb, None, tk, 0)
-    dt = time.perf_counter() - t0
+    runs = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        for b in range(w.B):
+            W = orc.edge_weights(w.p[b])
+            fb = orc.forward_backward(W)
+            st, tk, _ = orc.sample_tree(w.p[b], W, w.seed, b)
+            orc.marginals(w.p[b], fb, None, tk, 0)
+        runs.append(time.perf_counter() - t0)
+    dt = sorted(runs)[len(runs) // 2]
+    model, nproc, affinity = cpu_info()
     return dict(value=1.0 / dt, unit="steps/s", cores=1, kind="oracle",
+                cpu_model=model, nproc=nproc, affinity_cpus=affinity,
+                runs_s=runs,
                 sample=f"one full step (all {w.B} rows, every position) of the same workload, "
-                       f"serial fp64 C, {dt:.2f} s")
+                       f"serial fp64 C on one thread, median of {reps} runs: {dt:.2f} s")
+
+
+def ceilings(torch, fa, dev, p, reps=7):
+    """Bandwidth ceilings measured in the same run with HIP events, median
+    of `reps` each: the library's plain read and copy kernels
+    (fa_probe_bandwidth) over p and over a 1 GiB buffer, best over a few
+    grid sizes; and torch's own device copy of 1 GiB for reference."""
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def med(fn):
+        ts = []
+        for _ in range(reps + 1):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1000.0)
+        ts = sorted(ts[1:])
+        return ts[len(ts) // 2]
+
+    def rec(us, nbytes, how):
+        gbs = nbytes / (us * 1e3)
+        return dict(us=us, bytes=nbytes, gbs=gbs, frac=gbs / HBM_PEAK_GBS, how=how)
+
+    grids = (1024, 2048, 4096, 8192)
+    part = torch.empty(max(grids), dtype=torch.float32, device=dev)
+    pb = p.numel() * 4
+    best = min((med(lambda g=g: fa.probe_bandwidth(fa.FA_PROBE_READ, p, part, pb, g, stream)), g)
+               for g in grids)
+    out = {"read_p": rec(best[0], pb, f"plain read kernel over p, {best[1]} workgroups")}
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    best = min((med(lambda g=g: fa.probe_bandwidth(fa.FA_PROBE_READ, src, part, 1 << 30, g, stream)), g)
+               for g in grids)
+    out["read_1GiB"] = rec(best[0], 1 << 30, f"plain read kernel, 1 GiB, {best[1]} workgroups")
+    best = min((med(lambda g=g: fa.probe_bandwidth(fa.FA_PROBE_COPY, src, dst, 1 << 30, g, stream)), g)
+               for g in grids)
+    out["copy_1GiB"] = rec(best[0], 2 << 30, f"plain copy kernel, 1 GiB each way, streaming stores, "
+                                             f"{best[1]} workgroups")
+    out["torch_copy_1GiB"] = rec(med(lambda: dst.copy_(src)), 2 << 30, "torch copy_ of 1 GiB")
+    del src, dst, part
+    return out
+
+
+def stage_fracs(work, stage_us, separate):
+    """Per-stage µs with the algorithmic rate and fraction of peak."""
+    st = {
+        "build_transitions": dict(us=stage_us["build_transitions"], bound="hbm",
+                                  algorithmic_bytes=work["a1_bytes"], basis=work["a1_basis"],
+                                  gbs=work["a1_bytes"] / (stage_us["build_transitions"] * 1e3)),
+        "span_tree": dict(us=stage_us["span_tree"], bound="mfma", algorithmic_flops=work["a2_flops"],
+                          tflops=work["a2_flops"] / (stage_us["span_tree"] * 1e6)),
+    }
+    if separate:
+        st["sample"] = dict(us=stage_us["sample"], bound="latency")
+        last = "marginals"
+    else:
+        last = "sample_marginals"
+    st[last] = dict(us=stage_us[last], bound="hbm", algorithmic_bytes=work["a4_bytes"],
+                    basis=work["a4_basis"], gbs=work["a4_bytes"] / (stage_us[last] * 1e3))
+    for n in ("build_transitions", last):
+        st[n]["frac"] = st[n]["gbs"] / HBM_PEAK_GBS
+    st["span_tree"]["frac"] = st["span_tree"]["tflops"] / FP32_MFMA_PEAK_TFLOPS
+    return st
+
+
+def time_workload(torch, fa, configs, k, steps, warmup, dev, device_p=False):
+    """µs per step of preset k (joint call form): `steps` steps bracketed by
+    two events, then as many with events between the calls for the stage
+    split."""
+    t_prep = time.perf_counter()
+    w = configs.make(k, device=dev if device_p else None)
+    tb = fa.Table.from_automaton(w.aut)
+    tb.upload(dev)
+    p = w.p if device_p else torch.from_numpy(w.p).to(dev)
+    bufs = fa.StepBuffers(tb, w.B, w.L, want_q=True, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    prep_s = time.perf_counter() - t_prep
+    names = ["build_transitions", "span_tree", "sample_marginals"]
+
+    def step(seed, ev=None):
+        bufs.status.zero_()
+        if ev: ev[0].record()
+        fa.build_transitions(tb, p, bufs, stream)
+        if ev: ev[1].record()
+        fa.span_tree(tb, bufs, stream)
+        if ev: ev[2].record()
+        fa.sample_marginals(tb, p, bufs, seed, fa.FA_CONF_PROB, stream, write_q=True)
+        if ev: ev[3].record()
+
+    for s in range(warmup):
+        step(w.seed + s)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for s in range(steps):
+        step(w.seed + warmup + s)
+    t1.record()
+    torch.cuda.synchronize()
+    us = 1000.0 * t0.elapsed_time(t1) / steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for s in range(steps):
+        step(w.seed + warmup + s, evs[s])
+    torch.cuda.synchronize()
+    stage_us = {n: 1000.0 * sum(ev[j].elapsed_time(ev[j + 1]) for ev in evs) / steps
+                for j, n in enumerate(names)}
+    work = algorithmic_work(tb, w.B, w.L)
+    status = bufs.status.cpu().numpy().tolist()
+    out = dict(workload=w.describe(), B=w.B, L=w.L, S=tb.info["S"], Sp=tb.info["Sp"], V=w.aut.V,
+               steps=steps, warmup=warmup, us_per_step=us, steps_per_s=1e6 / us,
+               sequence_steps_per_s=w.B * 1e6 / us,
+               first_level="sparse" if tb.info["first_sparse"] else "dense",
+               second_level="sparse" if tb.info["second_sparse"] else "dense",
+               leafless=bool(tb.info["leafless"]),
+               p_drawn="on the device (same distribution, torch generator)" if device_p
+               else "on the host (numpy PCG64)",
+               stages=stage_fracs(work, stage_us, False), row_status=status,
+               host_prep_s=prep_s)
+    del bufs, p, tb, w
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def generation_sweep(torch, fa, tb, p, seed, bufs, Ts):
+    """Synthetic generations of T denoising steps (one constrained step and
+    one remasking step each) with the constrained score (Mar) and the
+    unconstrained one (Mf), each on a fresh copy of p, timed after one
+    untimed run of the same T."""
+    out = []
+    for mode, label in ((fa.FA_CONF_PROB, "Mar"), (fa.FA_CONF_UNCONSTRAINED, "Mf")):
+        for T in Ts:
+            p_gen = p.clone()
+            fa.generate(tb, p_gen, T, seed, conf_mode=mode, bufs=bufs)
+            p_gen.copy_(p)
+            torch.cuda.synchronize()
+            g0 = torch.cuda.Event(enable_timing=True)
+            g1 = torch.cuda.Event(enable_timing=True)
+            g0.record()
+            _, committed = fa.generate(tb, p_gen, T, seed, conf_mode=mode, bufs=bufs)
+            g1.record()
+            torch.cuda.synchronize()
+            ms = g0.elapsed_time(g1)
+            out.append({"score": label, "T": T, "ms": ms, "ms_per_denoising_step": ms / T,
+                        "generations_per_s": 1000.0 / ms,
+                        "all_committed": bool((committed == 1).all().item()),
+                        "row_status": bufs.status.cpu().numpy().tolist()})
+            del p_gen
+    return out
 
 
 # --- rocprofv3 output -> committed summaries ------------------------------
@@ -307,8 +485,11 @@ def main():
                     help="form of the first span level (default: the library's choice)")
     ap.add_argument("--separate", action="store_true",
                     help="fa_sample then fa_marginals instead of fa_sample_marginals")
-    ap.add_argument("--gen-steps", type=int, default=16,
-                    help="denoising steps of the timed synthetic generation (0: none)")
+    ap.add_argument("--gen-steps", default="16,64,256",
+                    help="denoising steps T of the timed synthetic generations, comma separated, "
+                         "each with the constrained and the unconstrained score (empty: none)")
+    ap.add_argument("--other-configs", default="2,4,5",
+                    help="other presets timed after the headline (joint calls; empty: none)")
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the other call form and the stage split (profiling runs)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -332,8 +513,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
-              "(rows shard across GPUs with no communication; see the design notes)",
-              file=sys.stderr)
+              "(batch rows would shard across GPUs with no communication)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -436,26 +616,10 @@ def main():
         stage_us = stage_split(args.separate)
         other_stage_us = stage_split(not args.separate)
     gen = None
-    if not args.headline_only and args.gen_steps > 0:
-        # a synthetic generation: T steps, each one constrained step and the
-        # remasking step (fa_commit), on a copy of p that ends one-hot
-        T = args.gen_steps
-        p_gen = p.clone()
-        fa.generate(tb, p_gen, T, w.seed, bufs=bufs)  # warm-up (the committed rows change the work)
-        p_gen.copy_(p)
-        torch.cuda.synchronize()
-        g0 = torch.cuda.Event(enable_timing=True)
-        g1 = torch.cuda.Event(enable_timing=True)
-        g0.record()
-        _, committed = fa.generate(tb, p_gen, T, w.seed, bufs=bufs)
-        g1.record()
-        torch.cuda.synchronize()
-        gms = g0.elapsed_time(g1)
-        gen = {"T": T, "positions_per_step": f"ceil(masked / steps left), all {w.L} after {T}",
-               "ms": gms, "generations_per_s": 1000.0 / gms,
-               "all_committed": bool((committed[:, :w.L] == 1).all().item()),
-               "row_status": bufs.status.cpu().numpy().tolist()}
-        del p_gen
+    if not args.headline_only and args.gen_steps:
+        Ts = [int(t) for t in args.gen_steps.split(",") if int(t) > 0]
+        gen = {"positions_per_step": f"ceil(masked / steps left), all {w.L} after T",
+               "runs": generation_sweep(torch, fa, tb, p, w.seed, bufs, Ts)}
     kern_us = {}
     for pid, a, b, name in kevs:
         ms = hev.elapsed_ms(a, b)
@@ -468,26 +632,7 @@ def main():
     status = bufs.status.cpu().numpy()
 
     work = algorithmic_work(tb, w.B, w.L)
-    stages = None
-    if stage_us is not None:
-        stages = {
-            "build_transitions": dict(us=stage_us["build_transitions"], bound="hbm",
-                                      algorithmic_bytes=work["a1_bytes"], basis=work["a1_basis"],
-                                      gbs=work["a1_bytes"] / (stage_us["build_transitions"] * 1e3)),
-            "span_tree": dict(us=stage_us["span_tree"], bound="mfma", algorithmic_flops=work["a2_flops"],
-                              tflops=work["a2_flops"] / (stage_us["span_tree"] * 1e6)),
-        }
-        if args.separate:
-            stages["sample"] = dict(us=stage_us["sample"], bound="latency")
-            last = "marginals"
-        else:
-            last = "sample_marginals"
-        stages[last] = dict(us=stage_us[last], bound="hbm", algorithmic_bytes=work["a4_bytes"],
-                            basis=work["a4_basis"],
-                            gbs=work["a4_bytes"] / (stage_us[last] * 1e3))
-        for n in ("build_transitions", last):
-            stages[n]["frac"] = stages[n]["gbs"] / HBM_PEAK_GBS
-        stages["span_tree"]["frac"] = stages["span_tree"]["tflops"] / FP32_MFMA_PEAK_TFLOPS
+    stages = None if stage_us is None else stage_fracs(work, stage_us, args.separate)
     kernels = {}
     for name, us in kern_us.items():
         kw = work["kernels"][name]
@@ -532,6 +677,21 @@ def main():
         "wall_s": wall,
         "row_status": status.tolist(),
     }
+    if not args.headline_only:
+        out["ceiling"] = ceilings(torch, fa, dev, p)
+    del bufs, p
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.headline_only and args.other_configs:
+        others = {}
+        for k in [int(x) for x in args.other_configs.split(",")]:
+            if k == args.workload:
+                continue
+            # the large presets take fewer steps; the batch DFA draws p on the device
+            n = args.steps if k <= 3 else 5
+            others[f"preset{k}"] = time_workload(torch, fa, configs, k, n, 3 if k > 3 else args.warmup,
+                                                 dev, device_p=(k == 4))
+        out["configs"] = others
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

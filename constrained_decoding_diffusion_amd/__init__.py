@@ -7,8 +7,9 @@ arguments.  See ``_fa.step`` for one whole step.
 from ._fa import (  # noqa: F401
     FA_CONF_NEGENT, FA_CONF_PROB, FA_CONF_UNCONSTRAINED, FA_DFA, FA_FIRST_LEVEL_DENSE, FA_FIRST_LEVEL_SPARSE, FA_SECOND_LEVEL_SPARSE,
     FA_LABEL_RANGES, FA_NFA, FA_NO_TRIM,
+    FA_PROBE_COPY, FA_PROBE_READ,
     FA_PROF_EMISSION_DENSE, FA_PROF_MARG_Q, FA_PROF_NONE, FA_PROF_TREE_LEVEL1,
     FA_ROW_BADPROB, FA_ROW_INFEASIBLE, FA_ROW_UNDERFLOW, FaError, StepBuffers, Table,
-    build_transitions, commit, generate, lib, marginals, profile_kernel, sample, sample_marginals,
+    build_transitions, commit, generate, lib, marginals, probe_bandwidth, profile_kernel, sample, sample_marginals,
     span_tree, span_tree_noalloc, step,
 )

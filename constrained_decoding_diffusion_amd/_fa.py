@@ -20,11 +20,12 @@ FA_DFA, FA_NFA, FA_LABEL_RANGES, FA_NO_TRIM = 1, 2, 4, 8
 FA_FIRST_LEVEL_SPARSE, FA_FIRST_LEVEL_DENSE, FA_SECOND_LEVEL_SPARSE = 16, 32, 64
 FA_CONF_PROB, FA_CONF_NEGENT, FA_CONF_UNCONSTRAINED = 0, 1, 2
 FA_PROF_NONE, FA_PROF_EMISSION_DENSE, FA_PROF_TREE_LEVEL1, FA_PROF_MARG_Q = range(4)
+FA_PROBE_READ, FA_PROBE_COPY = 0, 1
 
 EXPORTS = ["fa_compile_table", "fa_table_upload", "fa_table_destroy", "fa_table_info",
            "fa_table_state_map", "fa_sizes", "fa_build_transitions", "fa_span_tree", "fa_sample",
            "fa_marginals", "fa_sample_marginals", "fa_commit", "fa_strerror", "fa_profile_kernel",
-           "fa_span_tree_noalloc"]
+           "fa_span_tree_noalloc", "fa_probe_bandwidth"]
 FA_SPAN_TREE_NOALLOC_MAX_BYTES = 8 << 20
 
 
@@ -62,6 +63,7 @@ def lib():
     L.fa_sample_marginals.argtypes = [P, P, I32, I32, P, P, P, U64, I32, P, P, P, P, P, SZ, P, P]
     L.fa_commit.argtypes = [I32, I32, I32, P, P, I32, P, P, P, P, P]
     L.fa_profile_kernel.argtypes = [I32, P, P]
+    L.fa_probe_bandwidth.argtypes = [I32, P, P, SZ, I32, P]
     L.fa_strerror.argtypes = [C.c_int]
     L.fa_strerror.restype = C.c_char_p
     for fn in EXPORTS:
@@ -243,6 +245,13 @@ def generate(table: Table, p, T: int, seed: int, conf_mode: int = FA_CONF_PROB, 
         if on_step is not None:
             on_step(t, bufs, committed, fresh)
     return bufs, committed
+
+
+def probe_bandwidth(mode: int, src, dst, nbytes: int, blocks: int, stream):
+    """Measurement hook: one plain read (FA_PROBE_READ) or copy
+    (FA_PROBE_COPY) kernel over nbytes of the cuda tensors src/dst."""
+    _check("fa_probe_bandwidth", lib().fa_probe_bandwidth(mode, _ptr(src), _ptr(dst), nbytes,
+                                                          blocks, C.c_void_p(stream)))
 
 
 def profile_kernel(which: int, start_event=None, stop_event=None):

@@ -36,7 +36,7 @@ struct ProfHook {
     int which = FA_PROF_NONE;
     hipEvent_t start = nullptr, stop = nullptr;
 };
-ProfHook g_prof;
+thread_local ProfHook g_prof;
 
 }  // namespace
 

@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kDenseThreads) void emission_dense(
             // V % 4 == 0: v and v_end are multiples of 4
             const int vc = v < v_end ? v : v_end - 4;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) st.x[k] = *reinterpret_cast<const float4 *>(prow[k] + vc);
+            for (int k = 0; k < 8; ++k) st.x[k] = load_nt(prow[k] + vc);
         } else {
 #pragma unroll
             for (int k = 0; k < 8; ++k) {

@@ -446,7 +446,6 @@ __global__ __launch_bounds__(kQThreads) void marg_q(DevTable d, StepView sv,
     bool have_tok = false;
     if ((d.V & 3) == 0) {
         constexpr int U = 4;  // float4 groups in flight per thread
-        const float4 *p4 = reinterpret_cast<const float4 *>(prow);
         const uint4 *m4 = reinterpret_cast<const uint4 *>(d.tokmask);
         float4 *q4 = reinterpret_cast<float4 *>(qrow);
         for (int k0 = k_lo + tid; k0 < k_hi; k0 += U * kQThreads) {
@@ -455,7 +454,7 @@ __global__ __launch_bounds__(kQThreads) void marg_q(DevTable d, StepView sv,
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int k = min(k0 + u * kQThreads, k_hi - 1);
-                x[u] = p4[k];
+                x[u] = load_nt(prow + 4 * (size_t)k);
                 if constexpr (NG > 0 || SELBIT) mm[u] = m4[k];
                 else mm[u] = make_uint4(0u, 0u, 0u, 0u);
             }
@@ -711,7 +710,6 @@ __attribute__((amdgpu_waves_per_eu(SAMP && !LISTALL ? 4 : 1))) void marg_q_strea
     }
     constexpr int U = 4;
     constexpr int kPer = U * kQThreads;  // float4 groups per iteration
-    const float4 *p4 = reinterpret_cast<const float4 *>(prow);
     const uint4 *m4 = reinterpret_cast<const uint4 *>(d.tokmask);
     const int4 *s4 = reinterpret_cast<const int4 *>(d.tok2sel);
     const int4 *c4 = reinterpret_cast<const int4 *>(d.tok2cut);
@@ -727,7 +725,7 @@ __attribute__((amdgpu_waves_per_eu(SAMP && !LISTALL ? 4 : 1))) void marg_q_strea
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int k = min(k_lo + it * kPer + u * kQThreads + tid, k_hi - 1);
-            bf.x[u] = p4[k];
+            bf.x[u] = load_nt(prow + 4 * (size_t)k);
             if constexpr (MASK) bf.m[u] = m4[k];
             if constexpr (LISTALL) bf.sl[u] = s4[k];
             if constexpr (RANGES) bf.c[u] = c4[k];

@@ -359,12 +359,27 @@ const char *fa_strerror(int code);
  *     FA_PROF_EMISSION_DENSE  dense-mask contraction in fa_build_transitions
  *     FA_PROF_TREE_LEVEL1     matrix products of the first span-tree level
  *     FA_PROF_MARG_Q          per-token marginal writer in fa_marginals
- *   The setting is process-global and unsynchronized: set it from the thread
- *   that issues the step calls, between calls.
+ *   The setting belongs to the calling thread (thread-local): it brackets
+ *   the launches of the step calls that thread issues.
  * Errors: FA_EINVAL (unknown id, or an event missing for a kernel id).
  */
 enum { FA_PROF_NONE = 0, FA_PROF_EMISSION_DENSE = 1, FA_PROF_TREE_LEVEL1 = 2, FA_PROF_MARG_Q = 3 };
 int fa_profile_kernel(int32_t which, void *start_event, void *stop_event);
+
+/* Measurement hook; not part of the method.
+ * fa_probe_bandwidth - one plain streaming kernel on `stream`, whose rate is
+ *   an achievable HBM ceiling for the step's kernels: `blocks` workgroups
+ *   of 256 threads, each over its own contiguous chunk, eight non-temporal
+ *   float4 loads in flight per thread (non-temporal stores for the copy).
+ *     FA_PROBE_READ  every byte of src read once; dst receives one float per
+ *                    workgroup (at least blocks * 4 bytes)
+ *     FA_PROBE_COPY  dst = src (bytes each), streaming stores
+ *   src, dst device pointers, 16-byte aligned; bytes a multiple of 16.
+ * Errors: FA_EINVAL (mode, alignment, size, blocks outside 1..2^20), FA_EHIP.
+ */
+enum { FA_PROBE_READ = 0, FA_PROBE_COPY = 1 };
+int fa_probe_bandwidth(int32_t mode, const void *src, void *dst, size_t bytes, int32_t blocks,
+                       fa_stream_t stream);
 
 #ifdef __cplusplus
 }

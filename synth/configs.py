@@ -13,7 +13,7 @@ from dataclasses import dataclass
 import numpy as np
 
 from . import automata as A
-from .probs import make_probs
+from .probs import make_probs, make_probs_device
 
 
 @dataclass
@@ -44,8 +44,10 @@ def _draw(builder, seed, L, tries=16):
     raise RuntimeError("no feasible automaton")
 
 
-def make(k: int, *, B=None, L=None, S=None, V=None, E=None) -> Workload:
-    """Preset k in 1..5, optionally shrunk."""
+def make(k: int, *, B=None, L=None, S=None, V=None, E=None, device=None) -> Workload:
+    """Preset k in 1..5, optionally shrunk.  With a device, p is drawn there
+    (make_probs_device: the same distribution, other numbers) and the
+    workload's p is a cuda tensor instead of a numpy array."""
     if k == 1:
         B, L = B or 1, L or 6
         aut = A.real_number_dfa()
@@ -75,7 +77,10 @@ def make(k: int, *, B=None, L=None, S=None, V=None, E=None) -> Workload:
         name = "random NFA"
     else:
         raise ValueError(k)
-    p, commits = make_probs(aut, B, L, kind, n_commit, 2000 + k, 3000 + k)
+    if device is None:
+        p, commits = make_probs(aut, B, L, kind, n_commit, 2000 + k, 3000 + k)
+    else:
+        p, commits = make_probs_device(aut, B, L, kind, n_commit, 2000 + k, 3000 + k, device)
     return Workload(name=name, aut=aut, p=p, B=B, L=L, seed=4000 + k, commits=commits)
 
 

@@ -57,3 +57,45 @@ def make_probs(aut: Automaton, B: int, L: int, kind: str, n_commit: int,
             p[b, pos, w[pos]] = 1.0
             commits.append((pos, w[pos]))
     return p, commits
+
+
+def make_probs_device(aut: Automaton, B: int, L: int, kind: str, n_commit: int,
+                      seed_logits: int, seed_commit: int, device):
+    """The same distribution as make_probs, drawn on the device (torch's
+    generator there, so not the same numbers): fp64 logits, fp64 softmax,
+    cast to fp32, then the committed positions one-hot on the tokens of an
+    accepted witness string (chosen on the host exactly as make_probs does).
+    For workloads whose p is too large to draw and copy from the host
+    quickly.  Returns (p cuda fp32 [B, L, V], commits)."""
+    import torch
+    V = aut.V
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed_logits)
+    p = torch.empty((B, L, V), dtype=torch.float32, device=device)
+    bias = None
+    if kind == "normal4_zipf":
+        bias = -1.1 * torch.log(torch.arange(V, dtype=torch.float64, device=device) + 1.0)
+    for b in range(B):
+        if kind in ("normal2", "normal4", "normal4_zipf"):
+            sd = 2.0 if kind == "normal2" else 4.0
+            x = torch.randn((L, V), dtype=torch.float64, device=device, generator=gen) * sd
+            if bias is not None:
+                x += bias
+        elif kind == "uniform":
+            x = torch.zeros((L, V), dtype=torch.float64, device=device)
+        else:
+            raise ValueError(kind)
+        p[b] = torch.softmax(x, dim=-1).to(torch.float32)
+    commits = []
+    if n_commit > 0:
+        crng = np.random.Generator(np.random.PCG64(seed_commit))
+        for b in range(B):
+            w = witness(aut, L, crng)
+            if w is None:
+                raise ValueError("automaton accepts no string of length L")
+            pos = np.sort(crng.choice(L, size=min(n_commit, L), replace=False))
+            pt = torch.from_numpy(pos).to(device)
+            p[b, pt] = 0.0
+            p[b, pt, torch.from_numpy(w[pos]).to(device)] = 1.0
+            commits.append((pos, w[pos]))
+    return p, commits

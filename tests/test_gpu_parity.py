@@ -279,3 +279,19 @@ def test_misaligned_probabilities():
     orc = oracle.Oracle(w.aut)
     for b in range(w.B):
         PT.check_row(w, g, b, orc)
+
+
+def test_probe_bandwidth_hook():
+    """The measurement hook's copy reproduces its source and its read pass
+    sums every element once (partial sums per workgroup)."""
+    import torch
+    import constrained_decoding_diffusion_amd as fa
+    stream = torch.cuda.current_stream().cuda_stream
+    src = torch.arange(1 << 20, dtype=torch.float32, device="cuda") % 97
+    dst = torch.zeros_like(src)
+    fa.probe_bandwidth(fa.FA_PROBE_COPY, src, dst, src.numel() * 4, 1024, stream)
+    part = torch.zeros(1024, dtype=torch.float32, device="cuda")
+    fa.probe_bandwidth(fa.FA_PROBE_READ, src, part, src.numel() * 4, 1024, stream)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
+    assert abs(float(part.double().sum()) - float(src.double().sum())) <= 1e-6 * float(src.double().sum())
