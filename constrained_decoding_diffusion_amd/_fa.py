@@ -25,7 +25,7 @@ FA_PROBE_READ, FA_PROBE_COPY = 0, 1
 EXPORTS = ["fa_compile_table", "fa_table_upload", "fa_table_destroy", "fa_table_info",
            "fa_table_state_map", "fa_sizes", "fa_build_transitions", "fa_span_tree", "fa_sample",
            "fa_marginals", "fa_sample_marginals", "fa_commit", "fa_strerror", "fa_profile_kernel",
-           "fa_span_tree_noalloc", "fa_probe_bandwidth"]
+           "fa_span_tree_noalloc", "fa_probe_bandwidth", "fa_map_sizes", "fa_map_decode"]
 FA_SPAN_TREE_NOALLOC_MAX_BYTES = 8 << 20
 
 
@@ -64,6 +64,8 @@ def lib():
     L.fa_commit.argtypes = [I32, I32, I32, P, P, I32, P, P, P, P, P]
     L.fa_profile_kernel.argtypes = [I32, P, P]
     L.fa_probe_bandwidth.argtypes = [I32, P, P, SZ, I32, P]
+    L.fa_map_sizes.argtypes = [P, I32, I32, P, P]
+    L.fa_map_decode.argtypes = [P, P, I32, I32, P, P, SZ, P, P, P, P, P]
     L.fa_strerror.argtypes = [C.c_int]
     L.fa_strerror.restype = C.c_char_p
     for fn in EXPORTS:
@@ -245,6 +247,45 @@ def generate(table: Table, p, T: int, seed: int, conf_mode: int = FA_CONF_PROB, 
         if on_step is not None:
             on_step(t, bufs, committed, fresh)
     return bufs, committed
+
+
+class MapBuffers:
+    """Device buffers of MAP decoding (batch B, length L)."""
+
+    def __init__(self, table: Table, B: int, L: int, device="cuda"):
+        import torch
+        t, w = C.c_size_t(), C.c_size_t()
+        _check("fa_map_sizes", lib().fa_map_sizes(table.handle, B, L, C.byref(t), C.byref(w)))
+        self.B, self.L = B, L
+        self.tree = torch.empty(max(t.value // 8, 1), dtype=torch.float64, device=device)
+        self.ws = torch.empty(max(w.value, 256), dtype=torch.uint8, device=device)
+        self.logmax = torch.empty(B, dtype=torch.float64, device=device)
+        self.status = torch.zeros(B, dtype=torch.int32, device=device)
+        self.states = torch.empty((B, L + 1), dtype=torch.int32, device=device)
+        self.tokens = torch.empty((B, max(L, 1)), dtype=torch.int32, device=device)
+
+
+def map_decode(table: Table, p, bufs: "MapBuffers" = None):
+    """Greedy constrained decoding (fa_map_decode) on torch's current stream:
+    p cuda float32 [B, L, V].  Returns the buffers (logmax, states, tokens,
+    status)."""
+    import torch
+    B, L, V = p.shape
+    if V != table.info["V"]:
+        raise ValueError(f"p has V={V}, table has V={table.info['V']}")
+    if not p.is_cuda or p.dtype != torch.float32 or not p.is_contiguous():
+        raise ValueError("p must be a contiguous cuda float32 tensor")
+    if table.buf is None:
+        table.upload(p.device)
+    if bufs is None:
+        bufs = MapBuffers(table, B, L, device=p.device)
+    stream = torch.cuda.current_stream(p.device).cuda_stream
+    bufs.status.zero_()
+    _check("fa_map_decode", lib().fa_map_decode(
+        table.handle, _ptr(p), B, L, _ptr(bufs.tree), _ptr(bufs.ws), bufs.ws.numel(),
+        _ptr(bufs.logmax), _ptr(bufs.states), _ptr(bufs.tokens), _ptr(bufs.status),
+        C.c_void_p(stream)))
+    return bufs
 
 
 def probe_bandwidth(mode: int, src, dst, nbytes: int, blocks: int, stream):

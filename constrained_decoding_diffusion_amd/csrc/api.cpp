@@ -210,6 +210,38 @@ int sample_marginals_base(const DevTable &d, const Geometry &g, const float *p, 
 
 }  // namespace
 
+extern "C" int fa_map_sizes(const fa_table *t, int32_t B, int32_t L, size_t *tree_bytes,
+                            size_t *ws_bytes)
+{
+    if (!t) return FA_EINVAL;
+    if (t->h.nseg() > 0) return FA_EINVAL;  // range labels: no range-maximum structure
+    Geometry g;
+    if (int grc = make_geometry(t->h, B, L, &g)) return grc;
+    if (!grid_fits(g)) return FA_ETOOBIG;
+    if (tree_bytes) *tree_bytes = g.tree_floats * sizeof(double);
+    if (ws_bytes) *ws_bytes = map_ws_layout(t->h, g).total;
+    return FA_OK;
+}
+
+extern "C" int fa_map_decode(const fa_table *t, const float *p, int32_t B, int32_t L,
+                             double *tree, void *ws, size_t ws_bytes, double *logmax,
+                             int32_t *states, int32_t *tokens, int32_t *row_status,
+                             fa_stream_t stream)
+{
+    if (t && t->h.nseg() > 0) return FA_EINVAL;
+    int rc = ready(t);
+    if (rc) return rc;
+    Geometry g;
+    if (int grc = make_geometry(t->h, B, L, &g)) return grc;
+    if (!grid_fits(g)) return FA_ETOOBIG;
+    if (B == 0) return FA_OK;
+    MapWs w = map_ws_layout(t->h, g);
+    if (!logmax || !states || !row_status) return FA_EINVAL;
+    if (L > 0 && (!p || !tree || !tokens || !ws || ws_bytes < w.total)) return FA_EINVAL;
+    return hip_rc(launch_map_decode(t->h.device_view(), g, p, tree, (uint8_t *)ws, w, logmax,
+                                    states, tokens, row_status, stream));
+}
+
 extern "C" int fa_commit(int32_t B, int32_t L, int32_t V, const float *conf,
                          const int32_t *tokens, int32_t steps_left, int32_t *committed,
                          int32_t *fresh, float *p, const int32_t *row_status, fa_stream_t stream)

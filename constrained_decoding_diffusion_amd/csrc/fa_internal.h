@@ -247,6 +247,18 @@ int prof_mark(int which, bool begin, void *stream);
 // Split of one tree level's products along K (upper levels with few
 // products): 1 = no split.
 int tree_ksplit(const Geometry &g, int level);
+// MAP decoding (map.hip): workspace regions and the launcher
+struct MapWs {
+    size_t pmax = 0;   // [B*L][npairs] fp32 pair maxima
+    size_t zc = 0;     // [B][Lpad+1] int32 compact boundary states
+    size_t kpart = 0;  // fp64 split-K partial tiles
+    size_t total = 0;
+};
+MapWs map_ws_layout(const HostTable &t, const Geometry &g);
+int launch_map_decode(const DevTable &d, const Geometry &g, const float *p, double *tree,
+                      uint8_t *ws, const MapWs &w, double *logmax, int32_t *states,
+                      int32_t *tokens, int32_t *status, void *stream);
+
 // conf = p at the sampled token (FA_CONF_UNCONSTRAINED), after the PROB path
 int launch_conf_unconstrained(const DevTable &d, const Geometry &g, const float *p,
                               const int32_t *tokens, const int32_t *status, float *conf,

@@ -1,0 +1,472 @@
+// MAP (greedy, temperature 0) constrained decoding through a max-times span
+// tree: the most probable accepted string argmax_x prod_i p[i][x_i] over x in
+// C (paperfeed summary "The evidence": greedy decoding beside sampling; "Why
+// constrained decoding breaks for diffusion LMs": MAP inference over a DFA by
+// dynamic programming).  The scan of "The scan trick" with max in place of
+// sum: 2^k-span max-times products level by level, then top-down midpoint
+// decisions and per-position token decisions.
+//
+// Numbers: natural logs in fp64 (max-plus), log 0 = -inf.  A max-times
+// product is then max_k (x + y): one add and one max per term, no rounding
+// beyond the fp64 adds, so the decisions equal those of an fp64 reference
+// except where two candidates tie to fp64 rounding.  Every decision takes the
+// smallest id among equal values.  Max-times is not a ring, so the products
+// run on the vector ALUs, not on MFMA.
+//
+// Layout: tree fp64 [B][2 Lpad][Sp][Sp] in heap order like the sum tree,
+// right children (odd nodes >= 3) stored transposed, so a product is
+// D[i][j] = max_k X[i][k] + Y[j][k] over two row-major stored operands and a
+// midpoint reads one stored row of each child.
+#include "device_common.h"
+
+namespace fa {
+namespace {
+
+constexpr int kMapThreads = 256;
+constexpr int kMapRows = 8;     // stored rows per workgroup of the leaf writer
+constexpr int kMT = 64;         // output tile of the product kernel
+constexpr int kMK = 16;         // K step staged in LDS
+constexpr int kMapSplitTarget = 2048;  // product workgroups wanted per level
+
+__device__ inline double lg(float x) { return x > 0.f ? log((double)x) : -INFINITY; }
+
+__device__ inline double *node_ptr(double *tree, int Sp, int Lpad, int b, int h)
+{
+    return tree + ((size_t)b * 2 * Lpad + h) * (size_t)Sp * Sp;
+}
+
+// ---------------------------------------------------------- pair maxima
+// One workgroup per position.  Dense-mask pairs: every thread keeps, per
+// dense pair, the largest bit pattern of p over its tokens in that pair's
+// label (non-negative floats order as their bits), and the workgroup takes
+// the maximum.  Token-list pairs: one thread per pair over its sorted
+// tokens.  A NaN or negative p at a labelled token flags the row.
+template <int NG>  // dense pairs rounded up to whole bytes of the mask (0..4)
+__global__ __launch_bounds__(kMapThreads) void map_pairmax(DevTable d, const float *__restrict__ p,
+                                                           int L, float *__restrict__ pmax,
+                                                           int32_t *__restrict__ status)
+{
+    const int pos = blockIdx.x;
+    const int b = pos / L;
+    const float *row = p + (size_t)pos * d.V;
+    float *out = pmax + (size_t)pos * d.npairs;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int bad = 0;
+    if constexpr (NG > 0) {
+        constexpr int NB = 8 * NG;
+        __shared__ uint32_t sh[kMapThreads / 64][NB];
+        uint32_t mx[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) mx[j] = 0u;
+        for (int v = tid; v < d.V; v += kMapThreads) {
+            const uint32_t m = d.tokmask[v] & ((NB == 32) ? 0xFFFFFFFFu : ((1u << NB) - 1u));
+            const float x = row[v];
+            if (m) bad |= !(x >= 0.f);
+            const uint32_t xb = x >= 0.f ? __float_as_uint(x) : 0u;
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const uint32_t sel = (uint32_t)((int32_t)(m << (31 - j)) >> 31);  // bit j: all ones
+                mx[j] = max(mx[j], xb & sel);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            uint32_t x = mx[j];
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o));
+            if (lane == 0) sh[wave][j] = x;
+        }
+        __syncthreads();
+        if (tid < d.ndense) {
+            uint32_t x = sh[0][tid];
+            for (int w = 1; w < kMapThreads / 64; ++w) x = max(x, sh[w][tid]);
+            out[d.dense_pair[tid]] = __uint_as_float(x);
+        }
+    }
+    for (int q = tid; q < d.npairs; q += kMapThreads) {
+        if (d.pair_cls[q] != kList) continue;
+        float m = 0.f;
+        for (int k = d.list_off[q]; k < d.list_off[q + 1]; ++k) {
+            const float x = row[d.list_tok[k]];
+            bad |= !(x >= 0.f);
+            if (x > m) m = x;
+        }
+        out[q] = m;
+    }
+    if (bad) atomicOr(&status[b], (int)FA_ROW_BADPROB);
+}
+
+// ---------------------------------------------------------- log leaves
+// One workgroup per (leaf, kMapRows stored rows): each stored row is built in
+// LDS (-inf, then the log pair maxima of that row, or 0 on the diagonal of an
+// identity leaf past the sequence end) and written out whole.
+__global__ __launch_bounds__(kMapThreads) void map_leaves(DevTable d, int L, int Lpad,
+                                                          const float *__restrict__ pmax,
+                                                          double *__restrict__ tree)
+{
+    extern __shared__ double rowbuf[];  // [Sp]
+    const int Sp = d.Sp;
+    const int b = blockIdx.y / Lpad, i = blockIdx.y % Lpad;
+    const int h = Lpad + i;
+    const bool tr = stored_transposed(h);
+    double *M = node_ptr(tree, Sp, Lpad, b, h);
+    const float *pm = pmax + ((size_t)b * L + i) * d.npairs;
+    const int tid = threadIdx.x;
+    for (int r = blockIdx.x * kMapRows; r < min(Sp, (int)(blockIdx.x + 1) * kMapRows); ++r) {
+        for (int c = tid; c < Sp; c += kMapThreads) rowbuf[c] = -INFINITY;
+        __syncthreads();
+        if (r < d.S) {
+            if (i >= L) {
+                if (tid == 0) rowbuf[r] = 0.0;
+            } else if (!tr) {
+                for (int k = d.row_ptr[r] + tid; k < d.row_ptr[r + 1]; k += kMapThreads)
+                    rowbuf[d.pair_b[k]] = lg(pm[k]);
+            } else {
+                for (int k = d.col_ptr[r] + tid; k < d.col_ptr[r + 1]; k += kMapThreads) {
+                    const int q = d.col_pairs[k];
+                    rowbuf[d.pair_a[q]] = lg(pm[q]);
+                }
+            }
+        }
+        __syncthreads();
+        for (int c = tid; c < Sp; c += kMapThreads) M[(size_t)r * Sp + c] = rowbuf[c];
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------ max-plus products
+// One wavefront per 64 x 64 output tile of D = X (max,+) Y^T over one K
+// range (a split); each lane owns an 8 x 8 block of the tile.  Operand tiles
+// of 64 rows x kMK are staged in LDS k-major, so a lane reads its eight rows
+// of X and eight rows of Y at one k as two contiguous runs.
+__global__ __launch_bounds__(64) void map_gemm(int Sp, int Lpad, double *__restrict__ tree, int n0,
+                                               int nn, int ksplit, double *__restrict__ part)
+{
+    __shared__ __align__(16) double Xs[kMK][kMT];
+    __shared__ __align__(16) double Ys[kMK][kMT];
+    const int tiles = Sp / kMT, T2 = tiles * tiles;
+    const int tile = blockIdx.x % T2, split = blockIdx.x / T2;
+    const int tm = (tile / tiles) * kMT, tn = (tile % tiles) * kMT;
+    const int b = blockIdx.y / nn, n = n0 + blockIdx.y % nn;
+    const bool tr = stored_transposed(n);
+    const int hF = tr ? 2 * n + 1 : 2 * n, hG = tr ? 2 * n : 2 * n + 1;
+    const double *X = node_ptr(tree, Sp, Lpad, b, hF);
+    const double *Y = node_ptr(tree, Sp, Lpad, b, hG);
+    const int lane = threadIdx.x;
+    const int r0 = (lane >> 3) * 8, c0 = (lane & 7) * 8;
+    const int kc = Sp / ksplit, k_begin = split * kc, k_end = k_begin + kc;
+    double acc[8][8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[r][c] = -INFINITY;
+    const double *xrow = X + (size_t)(tm + lane) * Sp;
+    const double *yrow = Y + (size_t)(tn + lane) * Sp;
+    for (int k0 = k_begin; k0 < k_end; k0 += kMK) {
+        double2 xv[kMK / 2], yv[kMK / 2];
+#pragma unroll
+        for (int q = 0; q < kMK / 2; ++q) {
+            xv[q] = *reinterpret_cast<const double2 *>(xrow + k0 + 2 * q);
+            yv[q] = *reinterpret_cast<const double2 *>(yrow + k0 + 2 * q);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < kMK / 2; ++q) {
+            Xs[2 * q][lane] = xv[q].x;
+            Xs[2 * q + 1][lane] = xv[q].y;
+            Ys[2 * q][lane] = yv[q].x;
+            Ys[2 * q + 1][lane] = yv[q].y;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kMK; ++k) {
+            double a[8], c[8];
+#pragma unroll
+            for (int r = 0; r < 8; r += 2) {
+                const double2 t = *reinterpret_cast<const double2 *>(&Xs[k][r0 + r]);
+                a[r] = t.x;
+                a[r + 1] = t.y;
+                const double2 u = *reinterpret_cast<const double2 *>(&Ys[k][c0 + r]);
+                c[r] = u.x;
+                c[r + 1] = u.y;
+            }
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+#pragma unroll
+                for (int cc = 0; cc < 8; ++cc) acc[r][cc] = fmax(acc[r][cc], a[r] + c[cc]);
+        }
+    }
+    double *D = ksplit > 1 ? part + ((size_t)(blockIdx.y * ksplit + split) * T2 + tile) * (kMT * kMT)
+                           : node_ptr(tree, Sp, Lpad, b, n) + (size_t)tm * Sp + tn;
+    const int ld = ksplit > 1 ? kMT : Sp;
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int cc = 0; cc < 8; cc += 2)
+            *reinterpret_cast<double2 *>(D + (size_t)(r0 + r) * ld + c0 + cc) =
+                make_double2(acc[r][cc], acc[r][cc + 1]);
+}
+
+// the maximum of the K-split partial tiles, into the node
+__global__ __launch_bounds__(kMapThreads) void map_reduce(int Sp, int Lpad, double *__restrict__ tree,
+                                                          int n0, int nn, int ksplit,
+                                                          const double *__restrict__ part)
+{
+    const int tiles = Sp / kMT, T2 = tiles * tiles;
+    const int tile = blockIdx.x;
+    const int tm = (tile / tiles) * kMT, tn = (tile % tiles) * kMT;
+    const int b = blockIdx.y / nn, n = n0 + blockIdx.y % nn;
+    double *D = node_ptr(tree, Sp, Lpad, b, n);
+    for (int e = threadIdx.x; e < kMT * kMT; e += kMapThreads) {
+        double m = -INFINITY;
+        for (int s = 0; s < ksplit; ++s)
+            m = fmax(m, part[((size_t)(blockIdx.y * ksplit + s) * T2 + tile) * (kMT * kMT) + e]);
+        D[(size_t)(tm + e / kMT) * Sp + tn + e % kMT] = m;
+    }
+}
+
+// -------------------------------------------------------- top-down decode
+// (value, id) of the better of two candidates: the larger value, the smaller
+// id among equal values
+__device__ inline void better(double &v, int &k, double v2, int k2)
+{
+    if (v2 > v || (v2 == v && k2 >= 0 && (k < 0 || k2 < k))) {
+        v = v2;
+        k = k2;
+    }
+}
+
+__device__ inline void wave_argmax(double &v, int &k)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const double v2 = __shfl_xor(v, o);
+        const int k2 = __shfl_xor(k, o);
+        better(v, k, v2, k2);
+    }
+}
+
+// Per row: log-max = max over accepting f of root[s0][f]; the final boundary
+// state is the best f (smallest among equal values).  One wavefront per row.
+__global__ __launch_bounds__(64) void map_root(DevTable d, int Lpad, const double *__restrict__ tree,
+                                               double *__restrict__ logmax, int32_t *__restrict__ zc,
+                                               int32_t *__restrict__ status)
+{
+    const int b = blockIdx.x, lane = threadIdx.x;
+    const double *R = node_ptr(const_cast<double *>(tree), d.Sp, Lpad, b, 1) + (size_t)d.start * d.Sp;
+    double v = -INFINITY;
+    int k = -1;
+    for (int a = lane; a < d.n_acc; a += 64) better(v, k, R[d.acc[a]], d.acc[a]);
+    wave_argmax(v, k);
+    const bool ok = status[b] == 0 && v > -INFINITY;
+    for (int j = 1 + lane; j < Lpad; j += 64) zc[(size_t)b * (Lpad + 1) + j] = -1;
+    if (lane == 0) {
+        zc[(size_t)b * (Lpad + 1)] = ok ? d.start : -1;
+        zc[(size_t)b * (Lpad + 1) + Lpad] = ok ? k : -1;
+        logmax[b] = ok ? v : -INFINITY;
+        if (status[b] == 0 && !(v > -INFINITY)) atomicOr(&status[b], (int)FA_ROW_INFEASIBLE);
+    }
+}
+
+// One level of midpoints: node n of level `lev` (segment [l, r), midpoint m)
+// takes the z_m maximizing left[z_l][z_m] + right[z_m][z_r]: stored row z_l of
+// the left child and stored row z_r of the (transposed) right child.  One
+// wavefront per node.
+__global__ __launch_bounds__(64) void map_mid(DevTable d, int Lpad, int lev,
+                                              const double *__restrict__ tree,
+                                              int32_t *__restrict__ zc, int32_t *__restrict__ status)
+{
+    const int nn = 1 << (lev - 1);
+    const int b = blockIdx.x / nn, j = blockIdx.x % nn;
+    const int n = nn + j;
+    const int span = Lpad >> (lev - 1);
+    const int l = j * span, r = l + span, m = l + span / 2;
+    int32_t *z = zc + (size_t)b * (Lpad + 1);
+    const int zl = z[l], zr = z[r];
+    if (zl < 0 || zr < 0) return;  // a flagged row: its states stay -1
+    const double *Lrow = node_ptr(const_cast<double *>(tree), d.Sp, Lpad, b, 2 * n) + (size_t)zl * d.Sp;
+    const double *Rrow = node_ptr(const_cast<double *>(tree), d.Sp, Lpad, b, 2 * n + 1) + (size_t)zr * d.Sp;
+    double v = -INFINITY;
+    int k = -1;
+    for (int c = threadIdx.x; c < d.S; c += 64) better(v, k, Lrow[c] + Rrow[c], c);
+    wave_argmax(v, k);
+    if (threadIdx.x == 0) {
+        z[m] = v > -INFINITY ? k : -1;
+        if (!(v > -INFINITY)) atomicOr(&status[b], (int)FA_ROW_UNDERFLOW);
+    }
+}
+
+// The most probable token of each position's edge (z_i, z_{i+1}): over the
+// pair's token list, or over the row with the dense pair's bit array;
+// smallest token among equal probabilities.  One workgroup per position.
+__global__ __launch_bounds__(kMapThreads) void map_tokens(DevTable d, int L, int Lpad,
+                                                          const float *__restrict__ p,
+                                                          const int32_t *__restrict__ zc,
+                                                          int32_t *__restrict__ tokens,
+                                                          int32_t *__restrict__ status)
+{
+    const int b = blockIdx.y, i = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int32_t *z = zc + (size_t)b * (Lpad + 1);
+    const int a = z[i], c = z[i + 1];
+    const int q = (a >= 0 && c >= 0) ? pair_index(d, a, c) : -1;
+    const float *row = p + ((size_t)b * L + i) * d.V;
+    double v = -INFINITY;  // value as fp64 of the fp32 p: the order is the same
+    int k = -1;
+    if (q >= 0) {
+        if (d.pair_cls[q] == kDense) {
+            const uint32_t *bits = d.dense_bits + (size_t)d.pair_aux[q] * d.dense_words;
+            for (int t = tid; t < d.V; t += kMapThreads)
+                if ((bits[t >> 5] >> (t & 31)) & 1u) {
+                    const float x = row[t];
+                    if (x > 0.f) better(v, k, (double)x, t);
+                }
+        } else {
+            for (int e = d.list_off[q] + tid; e < d.list_off[q + 1]; e += kMapThreads) {
+                const int t = d.list_tok[e];
+                const float x = row[t];
+                if (x > 0.f) better(v, k, (double)x, t);
+            }
+        }
+    }
+    wave_argmax(v, k);
+    __shared__ double sv[kMapThreads / 64];
+    __shared__ int sk[kMapThreads / 64];
+    if (lane == 0) {
+        sv[wave] = v;
+        sk[wave] = k;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        v = sv[0];
+        k = sk[0];
+        for (int w = 1; w < kMapThreads / 64; ++w) better(v, k, sv[w], sk[w]);
+        tokens[(size_t)b * L + i] = k;
+        if (a >= 0 && c >= 0 && k < 0) atomicOr(&status[b], (int)FA_ROW_UNDERFLOW);
+    }
+}
+
+// states in original ids; a flagged row gets -1 states and tokens
+__global__ void map_finalize(DevTable d, int L, int Lpad, const int32_t *__restrict__ zc,
+                             int32_t *__restrict__ states, int32_t *__restrict__ tokens,
+                             const int32_t *__restrict__ status)
+{
+    const int b = blockIdx.y;
+    const int k = blockIdx.x * blockDim.x + threadIdx.x;
+    if (k > L) return;
+    const bool flagged = status[b] != 0;
+    const int zz = zc[(size_t)b * (Lpad + 1) + k];
+    states[(size_t)b * (L + 1) + k] = (flagged || zz < 0) ? -1 : d.orig[zz];
+    if (k < L && flagged) tokens[(size_t)b * L + k] = -1;
+}
+
+// L = 0: the empty string, accepted when the start state is accepting
+__global__ void map_empty(DevTable d, int B, double *__restrict__ logmax,
+                          int32_t *__restrict__ states, int32_t *__restrict__ status)
+{
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= B) return;
+    bool acc = false;
+    for (int a = 0; a < d.n_acc; ++a) acc |= d.acc[a] == d.start;
+    const bool ok = acc && status[b] == 0;
+    logmax[b] = ok ? 0.0 : -INFINITY;
+    states[b] = ok ? d.orig[d.start] : -1;
+    if (!acc) atomicOr(&status[b], (int)FA_ROW_INFEASIBLE);
+}
+
+// K split of one product level: the largest power of two dividing the K
+// blocks that keeps at most kMapSplitTarget workgroups
+int map_ksplit(const Geometry &g, int level)
+{
+    const long long tiles = (long long)g.B * (g.Lpad >> level) * (g.Sp / kMT) * (g.Sp / kMT);
+    int s = 1;
+    while ((g.Sp / kMK) % (2 * s) == 0 && tiles * s * 2 <= kMapSplitTarget) s *= 2;
+    return s;
+}
+
+}  // namespace
+
+MapWs map_ws_layout(const HostTable &t, const Geometry &g)
+{
+    auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+    MapWs w;
+    size_t o = 0;
+    w.pmax = o; o = al(o + (size_t)g.B * g.L * t.npairs() * sizeof(float));
+    w.zc = o; o = al(o + (size_t)g.B * (g.Lpad + 1) * sizeof(int32_t));
+    size_t kp = 0;
+    if (g.Sp % kMT == 0)
+        for (int level = 1; level <= g.K; ++level) {
+            const int s = map_ksplit(g, level);
+            if (s > 1) kp = std::max(kp, (size_t)g.B * (g.Lpad >> level) * s * g.mat);
+        }
+    w.kpart = o; o = al(o + kp * sizeof(double));
+    w.total = o ? o : 256;
+    return w;
+}
+
+int launch_map_decode(const DevTable &d, const Geometry &g, const float *p, double *tree,
+                      uint8_t *ws, const MapWs &w, double *logmax, int32_t *states,
+                      int32_t *tokens, int32_t *status, void *stream)
+{
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e;
+    if (g.L == 0) {
+        map_empty<<<(g.B + 255) / 256, 256, 0, st>>>(d, g.B, logmax, states, status);
+        return (int)hipGetLastError();
+    }
+    float *pmax = (float *)(ws + w.pmax);
+    int32_t *zc = (int32_t *)(ws + w.zc);
+    double *part = (double *)(ws + w.kpart);
+    const int npos = g.B * g.L;
+    const int ng = (d.ndense + 7) / 8;
+#define FA_MAP_PM(NG) map_pairmax<NG><<<npos, kMapThreads, 0, st>>>(d, p, g.L, pmax, status)
+    if (ng == 0) FA_MAP_PM(0);
+    else if (ng == 1) FA_MAP_PM(1);
+    else if (ng == 2) FA_MAP_PM(2);
+    else if (ng == 3) FA_MAP_PM(3);
+    else FA_MAP_PM(4);
+#undef FA_MAP_PM
+    e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+    const size_t llds = (size_t)g.Sp * sizeof(double);
+    if (llds > 48 * 1024) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&map_leaves),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)llds);
+        if (e != hipSuccess) return (int)e;
+    }
+    map_leaves<<<dim3((g.Sp + kMapRows - 1) / kMapRows, g.B * g.Lpad), kMapThreads, llds, st>>>(
+        d, g.L, g.Lpad, pmax, tree);
+    e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+    const int tiles = g.Sp / kMT;
+    for (int k = 1; k <= g.K; ++k) {
+        const int n0 = g.Lpad >> k, nn = n0;
+        const int ks = map_ksplit(g, k);
+        map_gemm<<<dim3(tiles * tiles * ks, g.B * nn), 64, 0, st>>>(g.Sp, g.Lpad, tree, n0, nn, ks,
+                                                                      part);
+        e = hipGetLastError();
+        if (e != hipSuccess) return (int)e;
+        if (ks > 1) {
+            map_reduce<<<dim3(tiles * tiles, g.B * nn), kMapThreads, 0, st>>>(g.Sp, g.Lpad, tree, n0,
+                                                                               nn, ks, part);
+            e = hipGetLastError();
+            if (e != hipSuccess) return (int)e;
+        }
+    }
+    map_root<<<g.B, 64, 0, st>>>(d, g.Lpad, tree, logmax, zc, status);
+    e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+    for (int lev = 1; lev <= g.K; ++lev) {
+        map_mid<<<g.B << (lev - 1), 64, 0, st>>>(d, g.Lpad, lev, tree, zc, status);
+        e = hipGetLastError();
+        if (e != hipSuccess) return (int)e;
+    }
+    map_tokens<<<dim3(g.L, g.B), kMapThreads, 0, st>>>(d, g.L, g.Lpad, p, zc, tokens, status);
+    e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+    map_finalize<<<dim3((g.L + 1 + 255) / 256, g.B), 256, 0, st>>>(d, g.L, g.Lpad, zc, states,
+                                                                    tokens, status);
+    return (int)hipGetLastError();
+}
+
+}  // namespace fa

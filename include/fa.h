@@ -296,6 +296,47 @@ int fa_sample_marginals(const fa_table *t, const float *p, int32_t B, int32_t L,
                         fa_stream_t stream);
 
 /*
+ * fa_map_sizes - bytes of the fp64 tree and of the workspace fa_map_decode
+ * needs for batch B and length L.  Errors: FA_EINVAL (also for a table with
+ * range labels, which MAP decoding does not take), FA_ETOOBIG.
+ */
+int fa_map_sizes(const fa_table *t, int32_t B, int32_t L, size_t *tree_bytes, size_t *ws_bytes);
+
+/*
+ * fa_map_decode - greedy (temperature 0) constrained decoding: for every row
+ * the most probable accepted string, argmax_x prod_i p[b][i][x_i] over the
+ * strings the automaton accepts (an NFA string counts once, whatever its
+ * number of accepting paths: every path of one string has the same
+ * product), and ln of its probability.
+ * Cite: paperfeed summary "The evidence" (greedy decoding beside sampling)
+ * and "Why constrained decoding breaks for diffusion LMs" (MAP inference
+ * over an automaton by dynamic programming); the tree of "The scan trick:
+ * log-depth exact sampling" with max in place of sum.
+ * Method: per position the max-times transition matrix
+ * Mmax_i[a][b] = max over v with c(a, v, b) > 0 of p[b][i][v]; 2^k-span
+ * max-times products level by level in fp64 logs; the final boundary state
+ * maximizing root[s0][f] over f in F; top-down, every midpoint z_m
+ * maximizing P[l,m)[z_l][z_m] + P[m,r)[z_m][z_r]; every token the most
+ * probable one of its edge (z_i, z_{i+1}).  Each decision takes the smallest
+ * id (state, token) among equal values.
+ *   p        device [B][L][V] fp32 (>= 0; NaN or negative p at a labelled
+ *            token sets FA_ROW_BADPROB)
+ *   tree     device fp64, fa_map_sizes bytes ([B][2*Lpad][Sp][Sp] heap
+ *            order, right children transposed, natural logs)
+ *   ws       device workspace of ws_bytes >= fa_map_sizes
+ *   logmax   device double [B]: ln of the best string's probability, -inf
+ *            (and FA_ROW_INFEASIBLE) when no accepted string has p > 0
+ *   states   device int32 [B][L+1] original ids; tokens device int32 [B][L]
+ *            (-1 on flagged rows)
+ *   row_status device int32 [B], OR-ed
+ * Errors: FA_EINVAL (also for tables with range labels), FA_ETOOBIG,
+ * FA_ESTATE, FA_EHIP.
+ */
+int fa_map_decode(const fa_table *t, const float *p, int32_t B, int32_t L, double *tree,
+                  void *ws, size_t ws_bytes, double *logmax, int32_t *states, int32_t *tokens,
+                  int32_t *row_status, fa_stream_t stream);
+
+/*
  * fa_commit - the remasking step between denoising steps: per row b, of the
  * n positions still masked (committed[b][i] == 0 and tokens[b][i] >= 0), the
  * k = ceil(n / steps_left) with the largest conf[b][i] (NaN counts as -inf;

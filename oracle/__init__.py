@@ -55,6 +55,10 @@ def lib():
         _lib.or_replay_verify.argtypes = [P, P, P, C.c_int32, C.c_uint64, C.c_uint32, P, P, P]
         _lib.or_ffbs.argtypes = [P, P, P, C.c_int32, P, P, P, P]
         _lib.or_judge_draw.argtypes = [P, C.c_int32, C.c_double, C.c_int32, P]
+        _lib.or_map_weights.argtypes = [P, P, C.c_int32, P]
+        _lib.or_viterbi.argtypes = [P, P, C.c_int32, P]
+        _lib.or_map_tree.argtypes = [P, P, P, C.c_int32, P, P, P]
+        _lib.or_map_verify.argtypes = [P, P, P, C.c_int32, P, P, P]
         _lib.or_edge_count.argtypes = [P, C.c_int32, C.c_int32, C.c_int32]
         _lib.or_edge_count.restype = C.c_int32
     return _lib
@@ -168,6 +172,42 @@ class Oracle:
         st = lib().or_ffbs(self._sp, _ptr(p), _ptr(np.ascontiguousarray(W)), L, _ptr(fb["alpha"]),
                            _ptr(np.ascontiguousarray(u, np.float64)), _ptr(states), _ptr(tokens))
         return states, tokens, int(st)
+
+    # ---- MAP (greedy) decoding
+    def map_weights(self, p: np.ndarray) -> np.ndarray:
+        """Wm[i, e] = max of p[i, v] over the label of edge e (0 if empty)."""
+        p = np.ascontiguousarray(p, np.float32)
+        L = p.shape[0]
+        Wm = np.zeros((L, self.aut.E), np.float64)
+        lib().or_map_weights(self._sp, _ptr(p), L, _ptr(Wm))
+        return Wm
+
+    def viterbi(self, Wm) -> tuple:
+        """Serial Viterbi: (log-max, status)."""
+        out = np.zeros(1)
+        st = lib().or_viterbi(self._sp, _ptr(np.ascontiguousarray(Wm)), Wm.shape[0], _ptr(out))
+        return float(out[0]), int(st)
+
+    def map_tree(self, p, Wm):
+        """Tree-order MAP decoding: (states [L+1], tokens [L], log-max, status)."""
+        p = np.ascontiguousarray(p, np.float32)
+        L = p.shape[0]
+        states = np.full(L + 1, -1, np.int32)
+        tokens = np.full(L, -1, np.int32)
+        lm = np.zeros(1)
+        st = lib().or_map_tree(self._sp, _ptr(p), _ptr(np.ascontiguousarray(Wm)), L,
+                               _ptr(states), _ptr(tokens), _ptr(lm))
+        return states, tokens, float(lm[0]), int(st)
+
+    def map_verify(self, p, Wm, states, tokens):
+        p = np.ascontiguousarray(p, np.float32)
+        L = p.shape[0]
+        rep = np.zeros(5, np.int64)
+        st = lib().or_map_verify(self._sp, _ptr(p), _ptr(np.ascontiguousarray(Wm)), L,
+                                 _ptr(np.ascontiguousarray(states, np.int32)),
+                                 _ptr(np.ascontiguousarray(tokens, np.int32)), _ptr(rep))
+        return dict(status=int(st), decisions=int(rep[0]), hard=int(rep[1]), near=int(rep[2]),
+                    first_hard=int(rep[4]))
 
     def edge_count(self, a: int, v: int, b: int) -> int:
         return int(lib().or_edge_count(self._sp, a, v, b))

@@ -557,3 +557,247 @@ int32_t or_edge_count(const or_aut *A, int32_t a, int32_t v, int32_t b)
 {
     return edge_count(A, a, v, b);
 }
+
+/* ======================================================= MAP decoding
+ * Greedy (temperature 0) constrained decoding: the most probable accepted
+ * string, argmax_x prod_i p[i][x_i] over x in C (paperfeed summary, "The
+ * evidence": greedy decoding next to sampling; "Why constrained decoding
+ * breaks for diffusion LMs": MAP inference over DFAs by dynamic
+ * programming).  Readings: an NFA string counts once however many accepting
+ * paths it has (every path of a string has the same product, so the maximum
+ * over (string, path) pairs is the maximum over accepted strings); all
+ * values are natural logs in fp64, log 0 = -inf.
+ *
+ * Max-times weights: Wm[i*E + e] = max_{v in label(e)} p[i][v] (0 for an
+ * empty label). */
+int or_map_weights(const or_aut *A, const float *p, int32_t L, double *Wm)
+{
+    for (int32_t i = 0; i < L; ++i) {
+        const float *row = p + (size_t)i * A->V;
+        for (int64_t e = 0; e < A->E; ++e) {
+            double m = 0.0;
+            if (A->ranges) {
+                for (int64_t k = A->label_off[e]; k + 1 < A->label_off[e + 1]; k += 2)
+                    for (int32_t v = A->label_tok[k]; v < A->label_tok[k + 1]; ++v)
+                        if ((double)row[v] > m) m = (double)row[v];
+            } else {
+                for (int64_t k = A->label_off[e]; k < A->label_off[e + 1]; ++k)
+                    if ((double)row[A->label_tok[k]] > m) m = (double)row[A->label_tok[k]];
+            }
+            Wm[(size_t)i * A->E + e] = m;
+        }
+    }
+    return OR_OK;
+}
+
+static double lg(double x) { return x > 0.0 ? log(x) : -INFINITY; }
+
+/* one max-plus step forward: vout[b] = max over edges a->b of vin[a] + ln Wm */
+static void map_forward(const or_aut *A, const double *Wm, int32_t L, int32_t i,
+                        const double *vin, double *vout)
+{
+    if (i >= L) { memcpy(vout, vin, sizeof(double) * A->S); return; }
+    for (int32_t k = 0; k < A->S; ++k) vout[k] = -INFINITY;
+    for (int64_t e = 0; e < A->E; ++e) {
+        double t = vin[A->src[e]] + lg(Wm[(size_t)i * A->E + e]);
+        if (t > vout[A->dst[e]]) vout[A->dst[e]] = t;
+    }
+}
+
+/* one max-plus step backward: vout[a] = max over edges a->b of ln Wm + vin[b] */
+static void map_backward(const or_aut *A, const double *Wm, int32_t L, int32_t i,
+                         const double *vin, double *vout)
+{
+    if (i >= L) { memcpy(vout, vin, sizeof(double) * A->S); return; }
+    for (int32_t k = 0; k < A->S; ++k) vout[k] = -INFINITY;
+    for (int64_t e = 0; e < A->E; ++e) {
+        double t = lg(Wm[(size_t)i * A->E + e]) + vin[A->dst[e]];
+        if (t > vout[A->src[e]]) vout[A->src[e]] = t;
+    }
+}
+
+/* Serial Viterbi: delta_0 = ln e_{s0}, delta_{i+1} = delta_i (max,+) ln M_i,
+ * log-max = max_{f in F} delta_L[f] (-inf: no accepted string has positive
+ * weight). */
+int or_viterbi(const or_aut *A, const double *Wm, int32_t L, double *logmax)
+{
+    double *a = (double *)malloc(sizeof(double) * A->S), *b = (double *)malloc(sizeof(double) * A->S);
+    if (!a || !b) { free(a); free(b); return OR_BADARG; }
+    for (int32_t k = 0; k < A->S; ++k) a[k] = -INFINITY;
+    a[A->start] = 0.0;
+    for (int32_t i = 0; i < L; ++i) {
+        map_forward(A, Wm, L, i, a, b);
+        memcpy(a, b, sizeof(double) * A->S);
+    }
+    double m = -INFINITY;
+    for (int32_t k = 0; k < A->n_accept; ++k) if (a[A->accept[k]] > m) m = a[A->accept[k]];
+    *logmax = m;
+    free(a); free(b);
+    return m == -INFINITY ? OR_INFEASIBLE : OR_OK;
+}
+
+/* max-plus span row e_{a} M_l ... M_{m-1} and column M_m ... M_{r-1} e_{b} */
+static void map_span_row(const or_aut *A, const double *Wm, int32_t L, int32_t a, int32_t l,
+                         int32_t m, double *v, double *tmp)
+{
+    for (int32_t k = 0; k < A->S; ++k) v[k] = -INFINITY;
+    v[a] = 0.0;
+    for (int32_t i = l; i < m; ++i) {
+        map_forward(A, Wm, L, i, v, tmp);
+        memcpy(v, tmp, sizeof(double) * A->S);
+    }
+}
+
+static void map_span_col(const or_aut *A, const double *Wm, int32_t L, int32_t b, int32_t m,
+                         int32_t r, double *v, double *tmp)
+{
+    for (int32_t k = 0; k < A->S; ++k) v[k] = -INFINITY;
+    v[b] = 0.0;
+    for (int32_t i = r - 1; i >= m; --i) {
+        map_backward(A, Wm, L, i, v, tmp);
+        memcpy(v, tmp, sizeof(double) * A->S);
+    }
+}
+
+/* argmax with the smallest index among equal maxima; -1 when all are -inf */
+static int32_t argmax_first(const double *w, int32_t n)
+{
+    int32_t best = -1;
+    for (int32_t j = 0; j < n; ++j)
+        if (w[j] > -INFINITY && (best < 0 || w[j] > w[best])) best = j;
+    return best;
+}
+
+/* the MAP token of position i between states a and b: argmax_v p[i][v] over
+ * v with c(a, v, b) > 0, smallest v among equal values; -1 if none has p > 0 */
+static int32_t map_token(const or_aut *A, const float *row, int32_t a, int32_t b, double *w)
+{
+    token_weights(A, row, a, b, w);   /* p[i][v] c(a, v, b) */
+    int32_t best = -1;
+    for (int32_t v = 0; v < A->V; ++v)
+        if (w[v] > 0.0 && (best < 0 || (double)row[v] > (double)row[best])) best = v;
+    return best;
+}
+
+/* Judge of one MAP decision: the other implementation chose `chosen`;
+ * NEAR when its value equals the best up to fp64 rounding of the sums
+ * (|best - value| <= 1e-9 max(1, |best|)), else HARD. */
+static int32_t map_judge(const double *w, int32_t n, int32_t chosen, int64_t id,
+                         or_replay_report *rep)
+{
+    int32_t mine = argmax_first(w, n);
+    if (rep) rep->n_draws++;
+    if (chosen < 0 || !rep) return mine;
+    if (chosen == mine) return chosen;
+    if (chosen >= n || mine < 0 || !(w[chosen] > -INFINITY) ||
+        !(fabs(w[mine] - w[chosen]) <= 1e-9 * fmax(1.0, fabs(w[mine])))) {
+        rep->n_hard++;
+        if (rep->first_hard < 0) rep->first_hard = id;
+    } else {
+        rep->n_near++;
+    }
+    return chosen;
+}
+
+/* Tree-order MAP decoding [P1 "The scan trick", with max in place of sum]:
+ * the final boundary state over F, then for every segment [l, r) with known
+ * boundary states the midpoint m = (l+r)/2 maximizing
+ * P_{l->m}[z_l][z_m] + P_{m->r}[z_m][z_r] (max-plus span products as vector
+ * chains), level by level, then every token as the most probable token of
+ * its edge; smallest id among equal values at every decision.  With z_in /
+ * x_in (another implementation's states, original ids, and tokens) it
+ * replays their decisions and judges each one instead. */
+static int map_walk(const or_aut *A, const float *p, const double *Wm, int32_t L,
+                    const int32_t *z_in, const int32_t *x_in, int32_t *z_out, int32_t *x_out,
+                    double *logmax, or_replay_report *rep)
+{
+    const int32_t S = A->S;
+    int32_t Lpad;
+    int32_t K = ilog2_pad(L, &Lpad);
+    int32_t *z = (int32_t *)malloc(sizeof(int32_t) * ((size_t)Lpad + 1));
+    double *row = (double *)malloc(sizeof(double) * S);
+    double *col = (double *)malloc(sizeof(double) * S);
+    double *tmp = (double *)malloc(sizeof(double) * S);
+    double *w = (double *)malloc(sizeof(double) * (S > A->V ? S : A->V));
+    int32_t *acc = (int32_t *)malloc(sizeof(int32_t) * (A->n_accept > 0 ? A->n_accept : 1));
+    int status = OR_OK;
+    if (!z || !row || !col || !tmp || !w || !acc) { status = OR_BADARG; goto done; }
+    for (int32_t k = 0; k <= Lpad; ++k) z[k] = -1;
+    z[0] = A->start;
+    memcpy(acc, A->accept, sizeof(int32_t) * A->n_accept);
+    for (int32_t a1 = 1; a1 < A->n_accept; ++a1)
+        for (int32_t a2 = a1; a2 > 0 && acc[a2 - 1] > acc[a2]; --a2) {
+            int32_t t = acc[a2]; acc[a2] = acc[a2 - 1]; acc[a2 - 1] = t;
+        }
+    map_span_row(A, Wm, L, A->start, 0, Lpad, row, tmp);
+    for (int32_t k = 0; k < A->n_accept; ++k) w[k] = row[acc[k]];
+    {
+        int32_t j0 = argmax_first(w, A->n_accept);
+        if (logmax) *logmax = j0 >= 0 ? w[j0] : -INFINITY;
+        int32_t chosen = -1;
+        if (z_in) {
+            chosen = A->n_accept;  /* not accepting: judged hard */
+            for (int32_t k = 0; k < A->n_accept; ++k) if (acc[k] == z_in[L]) chosen = k;
+        }
+        int32_t j = map_judge(w, A->n_accept, chosen, 0, rep);
+        if (j0 < 0) { status = OR_INFEASIBLE; goto done; }
+        z[Lpad] = j < A->n_accept ? acc[j] : z_in[L];
+    }
+    for (int32_t lev = 1; lev <= K; ++lev) {
+        int32_t span = Lpad >> (lev - 1), nn = 1 << (lev - 1);
+        for (int32_t node = 0; node < nn; ++node) {
+            int32_t l = node * span, r = l + span, m = l + span / 2;
+            if (z[l] < 0 || z[r] < 0) { status = OR_UNDERFLOW; goto done; }
+            map_span_row(A, Wm, L, z[l], l, m, row, tmp);
+            map_span_col(A, Wm, L, z[r], m, r, col, tmp);
+            for (int32_t j = 0; j < S; ++j) w[j] = row[j] + col[j];
+            int32_t chosen = z_in ? ((m <= L) ? z_in[m] : z_in[L]) : -1;
+            int32_t j = map_judge(w, S, chosen, ((int64_t)lev << 32) | node, rep);
+            if (j < 0) { status = OR_UNDERFLOW; goto done; }
+            z[m] = j;
+        }
+    }
+    for (int32_t i = 0; i < L; ++i) {
+        const float *prow = p + (size_t)i * A->V;
+        int32_t t = map_token(A, prow, z[i], z[i + 1], w);
+        if (t < 0) { status = OR_UNDERFLOW; goto done; }
+        if (x_in && rep) {
+            rep->n_draws++;
+            /* tokens compare fp32 values exactly: only equal values may differ */
+            int32_t o = x_in[i];
+            int ok = o == t || (o >= 0 && o < A->V && edge_count(A, z[i], o, z[i + 1]) > 0 &&
+                                prow[o] == prow[t]);
+            if (!ok) {
+                rep->n_hard++;
+                if (rep->first_hard < 0) rep->first_hard = ((int64_t)(K + 1) << 32) | i;
+            } else if (o != t) {
+                rep->n_near++;
+            }
+        }
+        if (x_out) x_out[i] = t;
+    }
+    if (z_out) for (int32_t k = 0; k <= L; ++k) z_out[k] = z[k];
+done:
+    free(z); free(row); free(col); free(tmp); free(w); free(acc);
+    return status;
+}
+
+int or_map_tree(const or_aut *A, const float *p, const double *Wm, int32_t L, int32_t *states,
+                int32_t *tokens, double *logmax)
+{
+    return map_walk(A, p, Wm, L, NULL, NULL, states, tokens, logmax, NULL);
+}
+
+/* Replay another implementation's MAP decisions (states original ids
+ * [L+1], tokens [L]); report as or_replay_verify: draws = decisions,
+ * hard, near (equal up to fp64 rounding, or equal p for a token), 0, first
+ * hard decision. */
+int or_map_verify(const or_aut *A, const float *p, const double *Wm, int32_t L,
+                  const int32_t *states, const int32_t *tokens, int64_t report[5])
+{
+    or_replay_report rep = {0, 0, 0, 0, -1};
+    int st = map_walk(A, p, Wm, L, states, tokens, NULL, NULL, NULL, &rep);
+    report[0] = rep.n_draws; report[1] = rep.n_hard; report[2] = rep.n_near;
+    report[3] = rep.n_margin; report[4] = rep.first_hard;
+    return st;
+}

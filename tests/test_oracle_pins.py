@@ -538,3 +538,117 @@ def test_tree_sampler_by_hand(L):
             assert status == oracle.OK
             np.testing.assert_array_equal(st, z[:L + 1])
             np.testing.assert_array_equal(to, tk)
+
+
+# --------------------------------------------------------- MAP decoding
+@pytest.mark.parametrize("idx", range(10))
+def test_map_vs_bruteforce(idx):
+    """The most probable accepted string of the tiny family by enumeration:
+    log-max from the serial Viterbi and from the tree, and the tree's string
+    equal to the enumerated argmax (unique for these continuous p), its
+    states a path of that string through the automaton."""
+    aut, L = _tiny_family()[idx]
+    rng = np.random.default_rng(1500 + idx)
+    p = _softmax(rng.normal(0, 1.5, (L, aut.V))).astype(np.float32)
+    X = BF.all_strings(aut.V, L)
+    paths = BF.path_counts(aut, X)
+    logp = np.zeros(X.shape[0])
+    for i in range(L):
+        logp += np.log(p[i, X[:, i]].astype(np.float64))
+    orc = oracle.Oracle(aut)
+    Wm = orc.map_weights(p)
+    lv, st_v = orc.viterbi(Wm)
+    states, tokens, lt, st_t = orc.map_tree(p, Wm)
+    if not (paths > 0).any():
+        assert st_v == oracle.INFEASIBLE and st_t == oracle.INFEASIBLE
+        return
+    acc = np.flatnonzero(paths > 0)
+    order = acc[np.argsort(-logp[acc])]
+    assert logp[order[0]] - logp[order[1]] > 1e-9  # a unique maximum
+    assert lv == pytest.approx(logp[order[0]], abs=1e-12)
+    assert lt == pytest.approx(logp[order[0]], abs=1e-12)
+    np.testing.assert_array_equal(tokens, X[order[0]])
+    # the states are an accepting path of the tokens
+    assert states[0] == aut.start and states[-1] in set(aut.accept.tolist())
+    for i in range(L):
+        assert orc.edge_count(int(states[i]), int(tokens[i]), int(states[i + 1])) > 0
+
+
+def test_map_viterbi_matches_tree_on_larger_automata():
+    for k, (aut, L) in enumerate([(A.random_dfa(np.random.default_rng(31), 20, 60, 3, 0.3), 37),
+                                  (A.random_nfa(np.random.default_rng(32), 25, 50, 120, 4, 6.0), 29)]):
+        p = _softmax(np.random.default_rng(33 + k).normal(0, 3, (L, aut.V))).astype(np.float32)
+        orc = oracle.Oracle(aut)
+        Wm = orc.map_weights(p)
+        lv, st = orc.viterbi(Wm)
+        states, tokens, lt, st2 = orc.map_tree(p, Wm)
+        assert st == st2 == oracle.OK
+        assert lt == pytest.approx(lv, abs=1e-9)
+        # the decoded string's own log-probability is the maximum
+        assert np.log(p[np.arange(L), tokens].astype(np.float64)).sum() == pytest.approx(lv, abs=1e-9)
+        rep = orc.map_verify(p, Wm, states, tokens)
+        assert rep["hard"] == 0 and rep["near"] == 0
+        assert rep["decisions"] == 1 + ((1 << (L - 1).bit_length()) - 1) + L
+
+
+def test_map_special_automata():
+    rng = np.random.default_rng(34)
+    V, L = 9, 13
+    p = _softmax(rng.normal(0, 2, (L, V))).astype(np.float32)
+    p[3, 2] = p[3, 5] = p[3].max() + np.float32(0.1)   # an exact tie: the smaller id wins
+    orc = oracle.Oracle(A.universal_automaton(V))
+    states, tokens, lm, st = orc.map_tree(p, orc.map_weights(p))
+    np.testing.assert_array_equal(tokens, np.argmax(p, axis=1))
+    assert tokens[3] == 2
+    assert lm == pytest.approx(np.log(p.max(axis=1).astype(np.float64)).sum(), abs=1e-12)
+    word = rng.integers(0, V, L)
+    orc = oracle.Oracle(A.single_string_automaton(word, V))
+    states, tokens, lm, st = orc.map_tree(p, orc.map_weights(p))
+    np.testing.assert_array_equal(tokens, word)
+    np.testing.assert_array_equal(states, np.arange(L + 1))
+    assert lm == pytest.approx(np.log(p[np.arange(L), word].astype(np.float64)).sum(), abs=1e-12)
+
+
+def test_map_tie_rule_by_hand():
+    g = _read_kv("map_two_token_tie.txt")
+    aut = A.two_token_real_dfa()
+    p = np.full((2, 2), 0.5, np.float32)
+    orc = oracle.Oracle(aut)
+    states, tokens, lm, st = orc.map_tree(p, orc.map_weights(p))
+    np.testing.assert_array_equal(states, [int(x) for x in g["states"]])
+    np.testing.assert_array_equal(tokens, [int(x) for x in g["tokens"]])
+    assert lm == pytest.approx(float(g["logmax"][0]), abs=1e-15)
+
+
+def test_map_verify_flags_planted_mistakes():
+    rng = np.random.default_rng(35)
+    aut = A.random_dfa(rng, 10, 30, 3, 0.4)
+    L = 21
+    p = _softmax(rng.normal(0, 2, (L, aut.V))).astype(np.float32)
+    orc = oracle.Oracle(aut)
+    Wm = orc.map_weights(p)
+    states, tokens, lm, st = orc.map_tree(p, Wm)
+    assert st == oracle.OK
+    assert orc.map_verify(p, Wm, states, tokens)["hard"] == 0
+    # a token of the same edge with a lower probability: HARD
+    lab = [v for v in range(aut.V) if orc.edge_count(int(states[4]), v, int(states[5])) > 0]
+    worse = [v for v in lab if p[4, v] < p[4, tokens[4]]]
+    if worse:
+        bad = tokens.copy()
+        bad[4] = worse[0]
+        assert orc.map_verify(p, Wm, states, bad)["hard"] == 1
+    # an equally probable token of the same edge: NEAR, not HARD
+    if len(lab) > 1:
+        other = next(v for v in lab if v != tokens[4])
+        p2 = p.copy()
+        p2[4, other] = p2[4, tokens[4]]
+        Wm2 = orc.map_weights(p2)
+        s2, t2, _, _ = orc.map_tree(p2, Wm2)
+        alt = t2.copy()
+        alt[4] = other if t2[4] != other else tokens[4]
+        r = orc.map_verify(p2, Wm2, s2, alt)
+        assert r["hard"] == 0 and r["near"] == 1
+    # a different, non-optimal final state: HARD
+    bad_st = states.copy()
+    bad_st[-1] = next(f for f in aut.accept.tolist() if f != states[-1]) if aut.accept.size > 1 else 0
+    assert orc.map_verify(p, Wm, bad_st, tokens)["hard"] >= 1
