@@ -21,6 +21,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
+# vector ALU issue: 256 CUs x 64 lanes x 2.4 GHz (fp64 and unpacked fp32 alike)
+VALU_FP64_LANE_OPS = 256 * 64 * 2.4e9
 METRIC = "constrained denoising steps/sec + per-step µs (L=256, V=151,936); HBM/MFMA % peak"
 CSRC = os.path.join(ROOT, "constrained_decoding_diffusion_amd", "csrc")
 
@@ -301,6 +303,36 @@ def time_workload(torch, fa, configs, k, steps, warmup, dev, device_p=False):
     del bufs, p, tb, w
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
+    return out
+
+
+def time_map(torch, fa, tb, p, steps, warmup):
+    """Greedy (MAP) decoding of the whole batch, µs per call (fa_map_decode),
+    with the max-plus tree's work: one add and one max per term, B (Lpad - 1)
+    S^3 terms, against the vector ALUs' fp64 issue rate."""
+    bufs = fa.map_decode(tb, p)
+    for _ in range(warmup):
+        fa.map_decode(tb, p, bufs)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fa.map_decode(tb, p, bufs)
+    b.record()
+    torch.cuda.synchronize()
+    us = 1000.0 * a.elapsed_time(b) / steps
+    B, L, _ = p.shape
+    S = tb.info["S"]
+    Lpad = 1 << max(0, (L - 1).bit_length())
+    terms = float(B) * (Lpad - 1) * S ** 3
+    out = dict(us_per_call=us, calls_per_s=1e6 / us, steps=steps,
+               row_status=bufs.status.cpu().numpy().tolist(),
+               logmax=bufs.logmax.cpu().numpy().tolist(),
+               tree_terms=terms,
+               tree_work_basis="B*(Lpad-1)*S^3 max-plus terms (one fp64 add + one max each)",
+               valu_peak_terms_per_s=VALU_FP64_LANE_OPS / 2)
+    del bufs
     return out
 
 
@@ -679,6 +711,8 @@ def main():
     }
     if not args.headline_only:
         out["ceiling"] = ceilings(torch, fa, dev, p)
+        if not tb.info["segments"]:
+            out["map_decode"] = time_map(torch, fa, tb, p, args.steps, args.warmup)
     del bufs, p
     torch.cuda.synchronize()
     torch.cuda.empty_cache()

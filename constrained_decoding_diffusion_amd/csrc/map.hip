@@ -27,6 +27,7 @@ constexpr int kMapRows = 8;     // stored rows per workgroup of the leaf writer
 constexpr int kMT = 64;         // output tile of the product kernel
 constexpr int kMK = 16;         // K step staged in LDS
 constexpr int kMapSplitTarget = 2048;  // product workgroups wanted per level
+constexpr int kMapSelLds = 4096;       // selected tokens the pair-maximum kernel stages in LDS
 
 __device__ inline double lg(float x) { return x > 0.f ? log((double)x) : -INFINITY; }
 
@@ -36,12 +37,14 @@ __device__ inline double *node_ptr(double *tree, int Sp, int Lpad, int b, int h)
 }
 
 // ---------------------------------------------------------- pair maxima
-// One workgroup per position.  Dense-mask pairs: every thread keeps, per
-// dense pair, the largest bit pattern of p over its tokens in that pair's
-// label (non-negative floats order as their bits), and the workgroup takes
-// the maximum.  Token-list pairs: one thread per pair over its sorted
-// tokens.  A NaN or negative p at a labelled token flags the row.
-template <int NG>  // dense pairs rounded up to whole bytes of the mask (0..4)
+// One workgroup per position.  Dense-mask pairs: maxima of p bit patterns
+// (non-negative floats order as their bits) per byte value of the mask, then
+// per pair over the byte values holding its bit.  Token-list pairs: one
+// thread per pair over its sorted tokens.  A NaN or negative p at a
+// labelled token flags the row.
+// NG: dense pairs rounded up to whole bytes of the mask (0..4); VEC4: V % 4
+// == 0 and p 16-byte aligned (float4 loads)
+template <int NG, bool VEC4>
 __global__ __launch_bounds__(kMapThreads) void map_pairmax(DevTable d, const float *__restrict__ p,
                                                            int L, float *__restrict__ pmax,
                                                            int32_t *__restrict__ status)
@@ -53,41 +56,60 @@ __global__ __launch_bounds__(kMapThreads) void map_pairmax(DevTable d, const flo
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int bad = 0;
     if constexpr (NG > 0) {
+        // tokens grouped by their mask byte: T[g][y] is the largest p bit
+        // pattern over the tokens whose byte g of the mask is y (one LDS
+        // atomic max per byte and token); dense pair 8g + t is then the
+        // largest T[g][y] over the bytes y with bit t set
         constexpr int NB = 8 * NG;
-        __shared__ uint32_t sh[kMapThreads / 64][NB];
-        uint32_t mx[NB];
-#pragma unroll
-        for (int j = 0; j < NB; ++j) mx[j] = 0u;
-        for (int v = tid; v < d.V; v += kMapThreads) {
-            const uint32_t m = d.tokmask[v] & ((NB == 32) ? 0xFFFFFFFFu : ((1u << NB) - 1u));
-            const float x = row[v];
-            if (m) bad |= !(x >= 0.f);
+        constexpr uint32_t kBits = (NB == 32) ? 0xFFFFFFFFu : ((1u << NB) - 1u);
+        __shared__ uint32_t T[NG][256];
+        for (int e = tid; e < NG * 256; e += kMapThreads) T[e >> 8][e & 255] = 0u;
+        __syncthreads();
+        auto one = [&](float x, uint32_t m) {
+            m &= kBits;
+            bad |= (m != 0u) & !(x >= 0.f);
             const uint32_t xb = x >= 0.f ? __float_as_uint(x) : 0u;
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                const uint32_t sel = (uint32_t)((int32_t)(m << (31 - j)) >> 31);  // bit j: all ones
-                mx[j] = max(mx[j], xb & sel);
+            for (int g = 0; g < NG; ++g) {
+                const uint32_t y = (m >> (8 * g)) & 255u;
+                if (y) atomicMax(&T[g][y], xb);
             }
-        }
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            uint32_t x = mx[j];
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o));
-            if (lane == 0) sh[wave][j] = x;
+        };
+        if (VEC4) {
+            const int n4 = d.V >> 2;
+            for (int g = tid; g < n4; g += kMapThreads) {
+                const float4 x4 = load_nt(row + 4 * (size_t)g);
+                const uint4 m4 = reinterpret_cast<const uint4 *>(d.tokmask)[g];
+                one(x4.x, m4.x);
+                one(x4.y, m4.y);
+                one(x4.z, m4.z);
+                one(x4.w, m4.w);
+            }
+        } else {
+            for (int v = tid; v < d.V; v += kMapThreads) one(row[v], d.tokmask[v]);
         }
         __syncthreads();
-        if (tid < d.ndense) {
-            uint32_t x = sh[0][tid];
-            for (int w = 1; w < kMapThreads / 64; ++w) x = max(x, sh[w][tid]);
-            out[d.dense_pair[tid]] = __uint_as_float(x);
+        for (int j = tid; j < d.ndense; j += kMapThreads) {
+            const int g = j >> 3, t = j & 7;
+            uint32_t x = 0u;
+            for (int y = 1; y < 256; ++y)
+                if ((y >> t) & 1) x = max(x, T[g][y]);
+            out[d.dense_pair[j]] = __uint_as_float(x);
         }
+    }
+    // token lists read p at the table's selected tokens: staged in LDS once
+    // when they fit, else gathered from the row
+    __shared__ float psel[kMapSelLds];
+    const bool staged = d.use_sel && d.nsel <= kMapSelLds;
+    if (staged) {
+        for (int k = tid; k < d.nsel; k += kMapThreads) psel[k] = row[d.sel_tok[k]];
+        __syncthreads();
     }
     for (int q = tid; q < d.npairs; q += kMapThreads) {
         if (d.pair_cls[q] != kList) continue;
         float m = 0.f;
         for (int k = d.list_off[q]; k < d.list_off[q + 1]; ++k) {
-            const float x = row[d.list_tok[k]];
+            const float x = staged ? psel[d.list_sel[k]] : row[d.list_tok[k]];
             bad |= !(x >= 0.f);
             if (x > m) m = x;
         }
@@ -213,16 +235,16 @@ __global__ __launch_bounds__(kMapThreads) void map_reduce(int Sp, int Lpad, doub
                                                           const double *__restrict__ part)
 {
     const int tiles = Sp / kMT, T2 = tiles * tiles;
-    const int tile = blockIdx.x;
+    constexpr int kChunks = kMT * kMT / kMapThreads;  // workgroups per tile
+    const int tile = blockIdx.x / kChunks;
+    const int e = (blockIdx.x % kChunks) * kMapThreads + threadIdx.x;
     const int tm = (tile / tiles) * kMT, tn = (tile % tiles) * kMT;
     const int b = blockIdx.y / nn, n = n0 + blockIdx.y % nn;
     double *D = node_ptr(tree, Sp, Lpad, b, n);
-    for (int e = threadIdx.x; e < kMT * kMT; e += kMapThreads) {
-        double m = -INFINITY;
-        for (int s = 0; s < ksplit; ++s)
-            m = fmax(m, part[((size_t)(blockIdx.y * ksplit + s) * T2 + tile) * (kMT * kMT) + e]);
-        D[(size_t)(tm + e / kMT) * Sp + tn + e % kMT] = m;
-    }
+    double m = -INFINITY;
+    for (int s = 0; s < ksplit; ++s)
+        m = fmax(m, part[((size_t)(blockIdx.y * ksplit + s) * T2 + tile) * (kMT * kMT) + e]);
+    D[(size_t)(tm + e / kMT) * Sp + tn + e % kMT] = m;
 }
 
 // -------------------------------------------------------- top-down decode
@@ -316,11 +338,34 @@ __global__ __launch_bounds__(kMapThreads) void map_tokens(DevTable d, int L, int
     if (q >= 0) {
         if (d.pair_cls[q] == kDense) {
             const uint32_t *bits = d.dense_bits + (size_t)d.pair_aux[q] * d.dense_words;
-            for (int t = tid; t < d.V; t += kMapThreads)
-                if ((bits[t >> 5] >> (t & 31)) & 1u) {
-                    const float x = row[t];
-                    if (x > 0.f) better(v, k, (double)x, t);
+            if ((d.V & 3) == 0 && ((uintptr_t)row & 15) == 0) {
+                // four tokens per thread and step, two steps in flight; each
+                // thread's tokens ascend, so a strict > keeps its first maximum
+                const int n4 = d.V >> 2;
+                for (int g0 = tid; g0 < n4; g0 += 2 * kMapThreads) {
+                    const int g1 = min(g0 + kMapThreads, n4 - 1);
+                    const float4 xa = load_nt(row + 4 * (size_t)g0);
+                    const float4 xb = load_nt(row + 4 * (size_t)g1);
+                    const uint32_t wa = bits[g0 >> 3] >> ((g0 & 7) * 4);
+                    const uint32_t wb = bits[g1 >> 3] >> ((g1 & 7) * 4);
+                    const float va[4] = {xa.x, xa.y, xa.z, xa.w};
+                    const float vb[4] = {xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (((wa >> u) & 1u) && va[u] > 0.f) better(v, k, (double)va[u], 4 * g0 + u);
+                    if (g0 + kMapThreads < n4) {
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            if (((wb >> u) & 1u) && vb[u] > 0.f) better(v, k, (double)vb[u], 4 * g1 + u);
+                    }
                 }
+            } else {
+                for (int t = tid; t < d.V; t += kMapThreads)
+                    if ((bits[t >> 5] >> (t & 31)) & 1u) {
+                        const float x = row[t];
+                        if (x > 0.f) better(v, k, (double)x, t);
+                    }
+            }
         } else {
             for (int e = d.list_off[q] + tid; e < d.list_off[q + 1]; e += kMapThreads) {
                 const int t = d.list_tok[e];
@@ -419,12 +464,20 @@ int launch_map_decode(const DevTable &d, const Geometry &g, const float *p, doub
     double *part = (double *)(ws + w.kpart);
     const int npos = g.B * g.L;
     const int ng = (d.ndense + 7) / 8;
-#define FA_MAP_PM(NG) map_pairmax<NG><<<npos, kMapThreads, 0, st>>>(d, p, g.L, pmax, status)
-    if (ng == 0) FA_MAP_PM(0);
-    else if (ng == 1) FA_MAP_PM(1);
-    else if (ng == 2) FA_MAP_PM(2);
-    else if (ng == 3) FA_MAP_PM(3);
-    else FA_MAP_PM(4);
+    const bool vec4 = (d.V & 3) == 0 && ((uintptr_t)p & 15) == 0;
+#define FA_MAP_PM(NG, V4) map_pairmax<NG, V4><<<npos, kMapThreads, 0, st>>>(d, p, g.L, pmax, status)
+    if (ng == 0) FA_MAP_PM(0, false);
+    else if (vec4) {
+        if (ng == 1) FA_MAP_PM(1, true);
+        else if (ng == 2) FA_MAP_PM(2, true);
+        else if (ng == 3) FA_MAP_PM(3, true);
+        else FA_MAP_PM(4, true);
+    } else {
+        if (ng == 1) FA_MAP_PM(1, false);
+        else if (ng == 2) FA_MAP_PM(2, false);
+        else if (ng == 3) FA_MAP_PM(3, false);
+        else FA_MAP_PM(4, false);
+    }
 #undef FA_MAP_PM
     e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
@@ -447,8 +500,8 @@ int launch_map_decode(const DevTable &d, const Geometry &g, const float *p, doub
         e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
         if (ks > 1) {
-            map_reduce<<<dim3(tiles * tiles, g.B * nn), kMapThreads, 0, st>>>(g.Sp, g.Lpad, tree, n0,
-                                                                               nn, ks, part);
+            map_reduce<<<dim3(tiles * tiles * (kMT * kMT / kMapThreads), g.B * nn), kMapThreads, 0,
+                         st>>>(g.Sp, g.Lpad, tree, n0, nn, ks, part);
             e = hipGetLastError();
             if (e != hipSuccess) return (int)e;
         }
