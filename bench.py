@@ -290,6 +290,8 @@ def time_workload(torch, fa, configs, k, steps, warmup, dev, device_p=False):
                 for j, n in enumerate(names)}
     work = algorithmic_work(tb, w.B, w.L)
     status = bufs.status.cpu().numpy().tolist()
+    del bufs
+    chain = time_chain_vs_tree(torch, fa, tb, p, w.seed, min(steps, 5), 1)
     out = dict(workload=w.describe(), B=w.B, L=w.L, S=tb.info["S"], Sp=tb.info["Sp"], V=w.aut.V,
                steps=steps, warmup=warmup, us_per_step=us, steps_per_s=1e6 / us,
                sequence_steps_per_s=w.B * 1e6 / us,
@@ -299,10 +301,54 @@ def time_workload(torch, fa, configs, k, steps, warmup, dev, device_p=False):
                p_drawn="on the device (same distribution, torch generator)" if device_p
                else "on the host (numpy PCG64)",
                stages=stage_fracs(work, stage_us, False), row_status=status,
-               host_prep_s=prep_s)
-    del bufs, p, tb, w
+               chain_vs_tree=chain, host_prep_s=prep_s)
+    del p, tb, w
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
+    return out
+
+
+def time_chain_vs_tree(torch, fa, tb, p, seed, steps, warmup):
+    """The pages' central trade on this GPU: the sampling half of a step
+    (emission reduce, then the draws and log Z) through the log-depth tree
+    (fa_span_tree + fa_sample) and through the serial chain
+    (fa_chain_sample: L dependent forward launches, then backward sampling).
+    µs per step each; None when the table keeps no dense leaves."""
+    if tb.info["leafless"]:
+        return None
+    B, L, _ = p.shape
+    bufs = fa.StepBuffers(tb, B, L, want_q=False, device=p.device)
+    stream = torch.cuda.current_stream(p.device).cuda_stream
+
+    def tree_step(s):
+        bufs.status.zero_()
+        fa.build_transitions(tb, p, bufs, stream)
+        fa.span_tree(tb, bufs, stream)
+        fa.sample(tb, p, bufs, s, stream)
+
+    def chain_step(s):
+        bufs.status.zero_()
+        fa.build_transitions(tb, p, bufs, stream)
+        fa.chain_sample(tb, p, bufs, s, stream)
+
+    out = {}
+    for name, fn in (("tree", tree_step), ("chain", chain_step)):
+        for s in range(warmup):
+            fn(seed + s)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for s in range(steps):
+            fn(seed + warmup + s)
+        b.record()
+        torch.cuda.synchronize()
+        out[name + "_us"] = 1000.0 * a.elapsed_time(b) / steps
+    out["chain_over_tree"] = out["chain_us"] / out["tree_us"]
+    out["what"] = ("emission reduce + (span tree + top-down sampler) vs emission reduce + "
+                   "(serial forward filter, L launches, + backward sampler); both draw tokens")
+    out["row_status"] = bufs.status.cpu().numpy().tolist()
+    del bufs
     return out
 
 
@@ -713,6 +759,7 @@ def main():
         out["ceiling"] = ceilings(torch, fa, dev, p)
         if not tb.info["segments"]:
             out["map_decode"] = time_map(torch, fa, tb, p, args.steps, args.warmup)
+        out["chain_vs_tree"] = time_chain_vs_tree(torch, fa, tb, p, w.seed, args.steps, args.warmup)
     del bufs, p
     torch.cuda.synchronize()
     torch.cuda.empty_cache()

@@ -25,7 +25,8 @@ FA_PROBE_READ, FA_PROBE_COPY = 0, 1
 EXPORTS = ["fa_compile_table", "fa_table_upload", "fa_table_destroy", "fa_table_info",
            "fa_table_state_map", "fa_sizes", "fa_build_transitions", "fa_span_tree", "fa_sample",
            "fa_marginals", "fa_sample_marginals", "fa_commit", "fa_strerror", "fa_profile_kernel",
-           "fa_span_tree_noalloc", "fa_probe_bandwidth", "fa_map_sizes", "fa_map_decode"]
+           "fa_span_tree_noalloc", "fa_probe_bandwidth", "fa_map_sizes", "fa_map_decode",
+           "fa_chain_sample"]
 FA_SPAN_TREE_NOALLOC_MAX_BYTES = 8 << 20
 
 
@@ -65,6 +66,7 @@ def lib():
     L.fa_profile_kernel.argtypes = [I32, P, P]
     L.fa_probe_bandwidth.argtypes = [I32, P, P, SZ, I32, P]
     L.fa_map_sizes.argtypes = [P, I32, I32, P, P]
+    L.fa_chain_sample.argtypes = [P, P, I32, I32, P, U64, P, P, P, P, SZ, P, P]
     L.fa_map_decode.argtypes = [P, P, I32, I32, P, P, SZ, P, P, P, P, P]
     L.fa_strerror.argtypes = [C.c_int]
     L.fa_strerror.restype = C.c_char_p
@@ -247,6 +249,31 @@ def generate(table: Table, p, T: int, seed: int, conf_mode: int = FA_CONF_PROB, 
         if on_step is not None:
             on_step(t, bufs, committed, fresh)
     return bufs, committed
+
+
+def chain_sample(table: Table, p, bufs: StepBuffers, seed: int, stream):
+    """fa_chain_sample: the serial chain sampler on the leaves in bufs.tree
+    (after build_transitions); writes bufs.logZ, states, tokens."""
+    _check("fa_chain_sample", lib().fa_chain_sample(
+        table.handle, _ptr(p), bufs.B, bufs.L, _ptr(bufs.tree), C.c_uint64(seed), _ptr(bufs.logZ),
+        _ptr(bufs.states), _ptr(bufs.tokens), _ptr(bufs.ws), bufs.ws.numel(), _ptr(bufs.status),
+        C.c_void_p(stream)))
+
+
+def chain_step(table: Table, p, seed: int, bufs: StepBuffers = None):
+    """The emission reduce and the chain sampler on torch's current stream
+    (the serial baseline of step()'s sampling half)."""
+    import torch
+    B, L, V = p.shape
+    if table.buf is None:
+        table.upload(p.device)
+    if bufs is None:
+        bufs = StepBuffers(table, B, L, want_q=False, device=p.device)
+    stream = torch.cuda.current_stream(p.device).cuda_stream
+    bufs.status.zero_()
+    build_transitions(table, p, bufs, stream)
+    chain_sample(table, p, bufs, seed, stream)
+    return bufs
 
 
 class MapBuffers:

@@ -14,7 +14,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["table.cpp", "api.cpp", "emission.hip", "tree.hip", "sample.hip", "marginals.hip",
-           "commit.hip", "noalloc.hip", "probe.hip", "map.hip"]
+           "commit.hip", "noalloc.hip", "probe.hip", "map.hip",
+           "chain.hip"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", f"-I{CSRC}"]
 # packed fp32 instructions are kept out of every gfx950 code object

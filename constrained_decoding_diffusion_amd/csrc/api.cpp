@@ -210,6 +210,26 @@ int sample_marginals_base(const DevTable &d, const Geometry &g, const float *p, 
 
 }  // namespace
 
+extern "C" int fa_chain_sample(const fa_table *t, const float *p, int32_t B, int32_t L,
+                               const float *tree, uint64_t seed, double *logZ, int32_t *states,
+                               int32_t *tokens, void *ws, size_t ws_bytes, int32_t *row_status,
+                               fa_stream_t stream)
+{
+    int rc = ready(t);
+    if (rc) return rc;
+    Geometry g;
+    if (int grc = make_geometry(t->h, B, L, &g)) return grc;
+    if (!grid_fits(g)) return FA_ETOOBIG;
+    // the chain reads every position's dense matrix
+    if (t->h.leafless && L > 1) return FA_EINVAL;
+    if (B == 0) return FA_OK;
+    WsLayout w = ws_layout(t->h, g);
+    if (!logZ || !states || !row_status || !ws || ws_bytes < w.total) return FA_EINVAL;
+    if (L > 0 && (!p || !tree || !tokens)) return FA_EINVAL;
+    return hip_rc(launch_chain_sample(t->h.device_view(), g, p, tree, seed, logZ, states, tokens,
+                                      (uint8_t *)ws, w, row_status, stream));
+}
+
 extern "C" int fa_map_sizes(const fa_table *t, int32_t B, int32_t L, size_t *tree_bytes,
                             size_t *ws_bytes)
 {

@@ -247,6 +247,12 @@ int prof_mark(int which, bool begin, void *stream);
 // Split of one tree level's products along K (upper levels with few
 // products): 1 = no split.
 int tree_ksplit(const Geometry &g, int level);
+// the serial chain sampler (chain.hip): forward filtering over the positions,
+// backward sampling, the token draws of the tree sampler
+int launch_chain_sample(const DevTable &d, const Geometry &g, const float *p, const float *tree,
+                        uint64_t seed, double *logZ, int32_t *states, int32_t *tokens,
+                        uint8_t *ws, const WsLayout &w, int32_t *status, void *stream);
+
 // MAP decoding (map.hip): workspace regions and the launcher
 struct MapWs {
     size_t pmax = 0;   // [B*L][npairs] fp32 pair maxima

@@ -296,6 +296,28 @@ int fa_sample_marginals(const fa_table *t, const float *p, int32_t B, int32_t L,
                         fa_stream_t stream);
 
 /*
+ * fa_chain_sample - the serial chain sampler, the baseline the span tree
+ * replaces: forward filtering over the positions (L dependent steps, one
+ * launch each: a_{i+1} = (a_i 2^-e_i) M_i with e_i the exponent of max a_i,
+ * a_0 = e_{s0}), log Z = ln 2 sum e_i + ln sum_{f in F} a_L[f], then backward
+ * sampling z_L ~ a_L[f] over f in F and z_i ~ a_i[a] M_i[a][z_{i+1}] for
+ * i = L-1 .. 0, then the tokens as fa_sample draws them.  Uniforms: the state
+ * draw of z_i keyed (b, K+2, i), token i (b, K+1, i), K = log2 Lpad.  The
+ * same posterior as fa_sample, other draws.
+ * Cite: paperfeed summary "The scan trick: log-depth exact sampling" (the
+ * serial forward-backward pass with L dependent steps); papernotes 消融实验
+ * (the chain's latency against the tree's).
+ *   tree     the leaves fa_build_transitions wrote (read only; a table that
+ *            keeps no dense leaves, fa_table_info [20], is refused when L > 1)
+ *   logZ     device double [B]; states [B][L+1] original ids; tokens [B][L]
+ *   ws       the step's workspace (>= fa_sizes)
+ * Errors: FA_EINVAL, FA_ETOOBIG, FA_ESTATE, FA_EHIP.
+ */
+int fa_chain_sample(const fa_table *t, const float *p, int32_t B, int32_t L, const float *tree,
+                    uint64_t seed, double *logZ, int32_t *states, int32_t *tokens, void *ws,
+                    size_t ws_bytes, int32_t *row_status, fa_stream_t stream);
+
+/*
  * fa_map_sizes - bytes of the fp64 tree and of the workspace fa_map_decode
  * needs for batch B and length L.  Errors: FA_EINVAL (also for a table with
  * range labels, which MAP decoding does not take), FA_ETOOBIG.

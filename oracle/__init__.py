@@ -55,6 +55,7 @@ def lib():
         _lib.or_replay_verify.argtypes = [P, P, P, C.c_int32, C.c_uint64, C.c_uint32, P, P, P]
         _lib.or_ffbs.argtypes = [P, P, P, C.c_int32, P, P, P, P]
         _lib.or_judge_draw.argtypes = [P, C.c_int32, C.c_double, C.c_int32, P]
+        _lib.or_ffbs_verify.argtypes = [P, P, P, C.c_int32, P, C.c_uint64, C.c_uint32, P, P, P]
         _lib.or_map_weights.argtypes = [P, P, C.c_int32, P]
         _lib.or_viterbi.argtypes = [P, P, C.c_int32, P]
         _lib.or_map_tree.argtypes = [P, P, P, C.c_int32, P, P, P]
@@ -172,6 +173,31 @@ class Oracle:
         st = lib().or_ffbs(self._sp, _ptr(p), _ptr(np.ascontiguousarray(W)), L, _ptr(fb["alpha"]),
                            _ptr(np.ascontiguousarray(u, np.float64)), _ptr(states), _ptr(tokens))
         return states, tokens, int(st)
+
+    # ---- the serial chain sampler (forward filtering, backward sampling)
+    @staticmethod
+    def chain_uniforms(seed: int, b: int, L: int):
+        """The uniforms of the chain sampler's draws in the order or_ffbs
+        takes them: z_L, z_{L-1} .. z_0 at level K+2 (node = state index),
+        then the tokens at level K+1 (node = position)."""
+        K = (1 << max(0, (L - 1).bit_length())).bit_length() - 1
+        u = [uniform(seed, b, K + 2, L)] + [uniform(seed, b, K + 2, i) for i in range(L - 1, -1, -1)]
+        return np.array(u + [uniform(seed, b, K + 1, i) for i in range(L)], np.float64)
+
+    def chain_sample(self, p, W, fb, seed: int, b: int):
+        """FFBS with the chain sampler's keyed uniforms: (states, tokens, status)."""
+        return self.ffbs(p, W, fb, self.chain_uniforms(seed, b, np.asarray(p).shape[0]))
+
+    def chain_verify(self, p, W, fb, seed: int, b: int, states, tokens):
+        p = np.ascontiguousarray(p, np.float32)
+        L = p.shape[0]
+        rep = np.zeros(5, np.int64)
+        st = lib().or_ffbs_verify(self._sp, _ptr(p), _ptr(np.ascontiguousarray(W)), L,
+                                  _ptr(fb["alpha"]), seed, b,
+                                  _ptr(np.ascontiguousarray(states, np.int32)),
+                                  _ptr(np.ascontiguousarray(tokens, np.int32)), _ptr(rep))
+        return dict(status=int(st), draws=int(rep[0]), hard=int(rep[1]), near=int(rep[2]),
+                    margin=int(rep[3]), first_hard=int(rep[4]))
 
     # ---- MAP (greedy) decoding
     def map_weights(self, p: np.ndarray) -> np.ndarray:

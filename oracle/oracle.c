@@ -801,3 +801,52 @@ int or_map_verify(const or_aut *A, const float *p, const double *Wm, int32_t L,
     report[3] = rep.n_margin; report[4] = rep.first_hard;
     return st;
 }
+
+/* ===================================================== chain (FFBS) replay
+ * The serial chain baseline of [P1 "The scan trick"] (forward filtering over
+ * the positions, then backward sampling): z_L ~ alpha_L[f] over f in F,
+ * then z_i ~ alpha_i[a] M_i[a][z_{i+1}] for i = L-1 .. 0, then every token
+ * as in the tree sampler.  Uniforms keyed like the tree sampler's with
+ * level K+2 and node i for the draw of z_i, and level K+1, node i for token
+ * i (K = log2 Lpad).  Replays another implementation's states (original
+ * ids, [L+1]) and tokens [L], each draw conditioned on that implementation's
+ * later state and judged as in or_replay_verify; alpha from
+ * or_forward_backward.  report as or_replay_verify. */
+int or_ffbs_verify(const or_aut *A, const float *p, const double *W, int32_t L,
+                   const double *alpha, uint64_t seed, uint32_t b, const int32_t *states,
+                   const int32_t *tokens, int64_t report[5])
+{
+    const int32_t S = A->S;
+    int32_t Lpad;
+    int32_t K = ilog2_pad(L, &Lpad);
+    or_replay_report rep = {0, 0, 0, 0, -1};
+    double *w = (double *)malloc(sizeof(double) * (S > A->V ? S : A->V));
+    if (!w) return OR_BADARG;
+    int status = OR_OK;
+    memset(w, 0, sizeof(double) * S);
+    for (int32_t k = 0; k < A->n_accept; ++k) w[A->accept[k]] = alpha[(size_t)L * S + A->accept[k]];
+    int32_t z = judge(w, S, or_uniform(seed, b, (uint32_t)(K + 2), (uint32_t)L),
+                      states[L] >= 0 && states[L] < S ? states[L] : S, ((int64_t)(K + 2) << 32) | L,
+                      &rep);
+    for (int32_t i = L - 1; i >= 0 && status == OR_OK; --i) {
+        if (z < 0 || z >= S) { status = OR_UNDERFLOW; break; }
+        memset(w, 0, sizeof(double) * S);
+        for (int64_t e = 0; e < A->E; ++e)
+            if (A->dst[e] == z) w[A->src[e]] += alpha[(size_t)i * S + A->src[e]] * W[(size_t)i * A->E + e];
+        z = judge(w, S, or_uniform(seed, b, (uint32_t)(K + 2), (uint32_t)i),
+                  states[i] >= 0 && states[i] < S ? states[i] : S, ((int64_t)(K + 2) << 32) | i, &rep);
+    }
+    for (int32_t i = 0; i < L && status == OR_OK; ++i) {
+        if (states[i] < 0 || states[i] >= S || states[i + 1] < 0 || states[i + 1] >= S) {
+            status = OR_UNDERFLOW;
+            break;
+        }
+        token_weights(A, p + (size_t)i * A->V, states[i], states[i + 1], w);
+        judge(w, A->V, or_uniform(seed, b, (uint32_t)(K + 1), (uint32_t)i), tokens[i],
+              ((int64_t)(K + 1) << 32) | i, &rep);
+    }
+    report[0] = rep.n_draws; report[1] = rep.n_hard; report[2] = rep.n_near;
+    report[3] = rep.n_margin; report[4] = rep.first_hard;
+    free(w);
+    return status;
+}

@@ -652,3 +652,40 @@ def test_map_verify_flags_planted_mistakes():
     bad_st = states.copy()
     bad_st[-1] = next(f for f in aut.accept.tolist() if f != states[-1]) if aut.accept.size > 1 else 0
     assert orc.map_verify(p, Wm, bad_st, tokens)["hard"] >= 1
+
+
+# ------------------------------------------------- chain (FFBS) replay
+def test_chain_verify_accepts_own_draws_and_flags_planted_mistakes():
+    """The chain sampler (FFBS with keyed uniforms) replayed by its verifier:
+    its own draws pass; a state that cannot precede the next one, a token
+    outside its edge's label, and a different final state are HARD.  (FFBS
+    itself is pinned against enumeration by the chi-square test above.)"""
+    rng = np.random.default_rng(36)
+    aut = A.random_dfa(rng, 10, 30, 3, 0.3)
+    L = 21
+    p = _softmax(rng.normal(0, 2, (L, aut.V))).astype(np.float32)
+    orc = oracle.Oracle(aut)
+    W = orc.edge_weights(p)
+    fb = orc.forward_backward(W)
+    seed = 4242
+    st, tk, status = orc.chain_sample(p, W, fb, seed, 1)
+    assert status == oracle.OK
+    rep = orc.chain_verify(p, W, fb, seed, 1, st, tk)
+    assert rep["status"] == oracle.OK and rep["hard"] == 0 and rep["near"] == 0
+    assert rep["draws"] == (L + 1) + L
+    # a token outside the label of its edge
+    bad = tk.copy()
+    lab = {v for v in range(aut.V) if orc.edge_count(int(st[6]), v, int(st[7])) > 0}
+    bad[6] = next(v for v in range(aut.V) if v not in lab)
+    assert orc.chain_verify(p, W, fb, seed, 1, st, bad)["hard"] >= 1
+    # a state with no edge into the next state
+    bst = st.copy()
+    preds = {int(aut.src[e]) for e in range(aut.E) if aut.dst[e] == st[9]}
+    bst[8] = next(s for s in range(aut.S) if s not in preds)
+    assert orc.chain_verify(p, W, fb, seed, 1, bst, tk)["hard"] >= 1
+    # another final state
+    fst = st.copy()
+    fst[-1] = next(f for f in aut.accept.tolist() if f != st[-1]) if aut.accept.size > 1 else 0
+    assert orc.chain_verify(p, W, fb, seed, 1, fst, tk)["hard"] >= 1
+    # the keyed chain sample is accepted and pins z_0 = s0
+    assert st[0] == aut.start and st[-1] in set(aut.accept.tolist())
