@@ -751,9 +751,11 @@ __attribute__((amdgpu_waves_per_eu(SAMP && !LISTALL ? 4 : 1))) void marg_q_strea
             o.z = qval(bf.x[u].z, weight_r(v + 2, m.z, sl.z, c.z));
             o.w = qval(bf.x[u].w, weight_r(v + 3, m.w, sl.w, c.w));
             if (k < k_hi) {
-                // non-temporal: q is not read again in the step, so its lines
-                // go to HBM now instead of draining during the next kernel
-                if (q4) store_nt(q4 + k, o);
+                // plain stores: with p read non-temporally here and in the
+                // emission reduce, streaming q through the caches measured
+                // 22 us faster per launch (14 us per step) than non-temporal
+                // stores
+                if (q4) q4[k] = o;
                 if (tok >= v && tok < v + 4) {
                     have_tok = true;
                     tokq = tok == v ? o.x : tok == v + 1 ? o.y : tok == v + 2 ? o.z : o.w;
