@@ -3,6 +3,8 @@
 // allocates device memory or synchronizes.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
+
 #include "fa_internal.h"
 
 using namespace fa;
@@ -72,20 +74,52 @@ extern "C" int fa_table_upload(fa_table *t, void *dev_buf, size_t bytes, fa_stre
     return FA_OK;
 }
 
+namespace {
+
+// a row offset of a caller buffer (null stays null)
+template <class T>
+T *rows(T *ptr, size_t per_row, int32_t b0)
+{
+    return ptr ? ptr + per_row * (size_t)b0 : ptr;
+}
+
+// runs fn(b0, geometry of the chunk, workspace of the chunk) for every row
+// chunk of a step, in order; stops at the first failure
+template <class Fn>
+int each_chunk(const HostTable &h, int32_t B, int32_t L, const StepChunks &ck, uint8_t *ws, Fn fn)
+{
+    for (int32_t k = 0; k < ck.count; ++k) {
+        const int32_t b0 = k * ck.rows;
+        Geometry gc;
+        make_geometry(h, std::min(ck.rows, B - b0), L, &gc);
+        gc.b0 = b0;
+        if (int rc = fn(b0, gc, ws ? ws + (size_t)k * ck.slot : ws)) return rc;
+    }
+    return 0;
+}
+
+size_t ws_need(const StepChunks &ck) { return (size_t)ck.count * ck.slot; }
+
+}  // namespace
+
 extern "C" int fa_build_transitions(const fa_table *t, const float *p, int32_t B, int32_t L,
                                     float *tree, int32_t *meta, void *ws, size_t ws_bytes,
                                     int32_t *row_status, fa_stream_t stream)
 {
     int rc = ready(t);
     if (rc) return rc;
-    Geometry g;
-    if (int grc = make_geometry(t->h, B, L, &g)) return grc;
-    if (!grid_fits(g)) return FA_ETOOBIG;
+    StepChunks ck;
+    if (int grc = plan_chunks(t->h, B, L, false, &ck)) return grc;
     if (B == 0 || L == 0) return FA_OK;
-    WsLayout w = ws_layout(t->h, g);
-    if (!p || !tree || !meta || !row_status || !ws || ws_bytes < w.total) return FA_EINVAL;
-    return hip_rc(launch_build_transitions(t->h.device_view(), g, p, tree, meta, (uint8_t *)ws, w,
-                                           row_status, stream));
+    if (!p || !tree || !meta || !row_status || !ws || ws_bytes < ws_need(ck)) return FA_EINVAL;
+    const DevTable d = t->h.device_view();
+    return hip_rc(each_chunk(t->h, B, L, ck, (uint8_t *)ws, [&](int32_t b0, const Geometry &g,
+                                                                 uint8_t *wsc) {
+        return launch_build_transitions(d, g, rows(p, (size_t)L * d.V, b0),
+                                        rows(tree, 2 * (size_t)g.Lpad * g.mat, b0),
+                                        rows(meta, 6 * (size_t)g.Lpad * g.Sp, b0), wsc,
+                                        ws_layout(t->h, g), rows(row_status, 1, b0), stream);
+    }));
 }
 
 extern "C" int fa_span_tree(const fa_table *t, int32_t B, int32_t L, float *tree, int32_t *meta,
@@ -94,15 +128,18 @@ extern "C" int fa_span_tree(const fa_table *t, int32_t B, int32_t L, float *tree
 {
     int rc = ready(t);
     if (rc) return rc;
-    Geometry g;
-    if (int grc = make_geometry(t->h, B, L, &g)) return grc;
-    if (!grid_fits(g)) return FA_ETOOBIG;
+    StepChunks ck;
+    if (int grc = plan_chunks(t->h, B, L, false, &ck)) return grc;
     if (B == 0) return FA_OK;
     if (!logZ || !row_status) return FA_EINVAL;
-    WsLayout w = ws_layout(t->h, g);
-    if (L > 0 && (!tree || !meta || !ws || ws_bytes < w.total)) return FA_EINVAL;
-    return hip_rc(launch_span_tree(t->h.device_view(), g, tree, meta, (uint8_t *)ws, w, logZ,
-                                   row_status, stream));
+    if (L > 0 && (!tree || !meta || !ws || ws_bytes < ws_need(ck))) return FA_EINVAL;
+    const DevTable d = t->h.device_view();
+    return hip_rc(each_chunk(t->h, B, L, ck, (uint8_t *)ws, [&](int32_t b0, const Geometry &g,
+                                                                 uint8_t *wsc) {
+        return launch_span_tree(d, g, rows(tree, 2 * (size_t)g.Lpad * g.mat, b0),
+                                rows(meta, 6 * (size_t)g.Lpad * g.Sp, b0), wsc, ws_layout(t->h, g),
+                                rows(logZ, 1, b0), rows(row_status, 1, b0), stream);
+    }));
 }
 
 extern "C" int fa_sample(const fa_table *t, const float *p, int32_t B, int32_t L, const float *tree,
@@ -111,15 +148,21 @@ extern "C" int fa_sample(const fa_table *t, const float *p, int32_t B, int32_t L
 {
     int rc = ready(t);
     if (rc) return rc;
-    Geometry g;
-    if (int grc = make_geometry(t->h, B, L, &g)) return grc;
-    if (!grid_fits(g)) return FA_ETOOBIG;
+    StepChunks ck;
+    if (int grc = plan_chunks(t->h, B, L, false, &ck)) return grc;
     if (B == 0) return FA_OK;
-    WsLayout w = ws_layout(t->h, g);
-    if (!states || !row_status || !ws || ws_bytes < w.total) return FA_EINVAL;
+    if (!states || !row_status || !ws || ws_bytes < ws_need(ck)) return FA_EINVAL;
     if (L > 0 && (!p || !tree || !meta || !tokens)) return FA_EINVAL;
-    return hip_rc(launch_sample(t->h.device_view(), g, p, tree, meta, seed, states, tokens,
-                                (uint8_t *)ws, w, row_status, stream));
+    const DevTable d = t->h.device_view();
+    return hip_rc(each_chunk(t->h, B, L, ck, (uint8_t *)ws, [&](int32_t b0, const Geometry &g,
+                                                                 uint8_t *wsc) {
+        // a chunk's row b draws with the keys of batch row b0 + b
+        return launch_sample(d, g, rows(p, (size_t)L * d.V, b0),
+                             rows(tree, 2 * (size_t)g.Lpad * g.mat, b0),
+                             rows(meta, 6 * (size_t)g.Lpad * g.Sp, b0), seed,
+                             rows(states, (size_t)L + 1, b0), rows(tokens, (size_t)L, b0), wsc,
+                             ws_layout(t->h, g), rows(row_status, 1, b0), stream);
+    }));
 }
 
 extern "C" int fa_marginals(const fa_table *t, const float *p, int32_t B, int32_t L,
@@ -129,22 +172,29 @@ extern "C" int fa_marginals(const fa_table *t, const float *p, int32_t B, int32_
 {
     int rc = ready(t);
     if (rc) return rc;
-    Geometry g;
-    if (int grc = make_geometry(t->h, B, L, &g)) return grc;
-    if (!grid_fits(g)) return FA_ETOOBIG;
+    StepChunks ck;
+    if (int grc = plan_chunks(t->h, B, L, false, &ck)) return grc;
     if (!conf_mode_ok(conf_mode)) return FA_EINVAL;
     if (B == 0 || L == 0) return FA_OK;
-    WsLayout w = ws_layout(t->h, g);
-    if (!p || !tree || !meta || !logZ || !conf || !row_status || !ws || ws_bytes < w.total)
+    if (!p || !tree || !meta || !logZ || !conf || !row_status || !ws || ws_bytes < ws_need(ck))
         return FA_EINVAL;
     if (conf_mode != FA_CONF_NEGENT && !tokens) return FA_EINVAL;
     const DevTable d = t->h.device_view();
-    // the unconstrained score takes the PROB path for q, then its own conf
-    int rc2 = launch_marginals(d, g, p, tree, meta, logZ, tokens, base_mode(conf_mode), q, conf,
-                               (uint8_t *)ws, w, row_status, stream);
-    if (!rc2 && conf_mode == FA_CONF_UNCONSTRAINED)
-        rc2 = launch_conf_unconstrained(d, g, p, tokens, row_status, conf, stream);
-    return hip_rc(rc2);
+    return hip_rc(each_chunk(t->h, B, L, ck, (uint8_t *)ws, [&](int32_t b0, const Geometry &g,
+                                                                 uint8_t *wsc) {
+        const float *pc = rows(p, (size_t)L * d.V, b0);
+        const int32_t *tc = rows(tokens, (size_t)L, b0);
+        float *cc = rows(conf, (size_t)L, b0);
+        int32_t *sc = rows(row_status, 1, b0);
+        // the unconstrained score takes the PROB path for q, then its own conf
+        int r = launch_marginals(d, g, pc, rows(tree, 2 * (size_t)g.Lpad * g.mat, b0),
+                                 rows(meta, 6 * (size_t)g.Lpad * g.Sp, b0), rows(logZ, 1, b0), tc,
+                                 base_mode(conf_mode), rows(q, (size_t)L * d.V, b0), cc, wsc,
+                                 ws_layout(t->h, g), sc, stream);
+        if (!r && conf_mode == FA_CONF_UNCONSTRAINED)
+            r = launch_conf_unconstrained(d, g, pc, tc, sc, cc, stream);
+        return r;
+    }));
 }
 
 extern "C" int fa_sample_marginals(const fa_table *t, const float *p, int32_t B, int32_t L,
@@ -155,20 +205,28 @@ extern "C" int fa_sample_marginals(const fa_table *t, const float *p, int32_t B,
 {
     int rc = ready(t);
     if (rc) return rc;
-    Geometry g;
-    if (int grc = make_geometry(t->h, B, L, &g)) return grc;
-    if (!grid_fits(g)) return FA_ETOOBIG;
+    StepChunks ck;
+    if (int grc = plan_chunks(t->h, B, L, false, &ck)) return grc;
     if (!conf_mode_ok(conf_mode)) return FA_EINVAL;
     if (B == 0) return FA_OK;
-    WsLayout w = ws_layout(t->h, g);
-    if (!states || !row_status || !ws || ws_bytes < w.total) return FA_EINVAL;
+    if (!states || !row_status || !ws || ws_bytes < ws_need(ck)) return FA_EINVAL;
     if (L > 0 && (!p || !tree || !meta || !logZ || !tokens || !conf)) return FA_EINVAL;
     const DevTable d = t->h.device_view();
-    rc = sample_marginals_base(d, g, p, tree, meta, logZ, seed, base_mode(conf_mode), states,
-                               tokens, q, conf, (uint8_t *)ws, w, row_status, stream);
-    if (!rc && L > 0 && conf_mode == FA_CONF_UNCONSTRAINED)
-        rc = launch_conf_unconstrained(d, g, p, tokens, row_status, conf, stream);
-    return hip_rc(rc);
+    return hip_rc(each_chunk(t->h, B, L, ck, (uint8_t *)ws, [&](int32_t b0, const Geometry &g,
+                                                                 uint8_t *wsc) {
+        const float *pc = rows(p, (size_t)L * d.V, b0);
+        int32_t *tc = rows(tokens, (size_t)L, b0);
+        float *cc = rows(conf, (size_t)L, b0);
+        int32_t *sc = rows(row_status, 1, b0);
+        int r = sample_marginals_base(d, g, pc, rows(tree, 2 * (size_t)g.Lpad * g.mat, b0),
+                                      rows(meta, 6 * (size_t)g.Lpad * g.Sp, b0), rows(logZ, 1, b0),
+                                      seed, base_mode(conf_mode), rows(states, (size_t)L + 1, b0), tc,
+                                      rows(q, (size_t)L * d.V, b0), cc, wsc, ws_layout(t->h, g), sc,
+                                      stream);
+        if (!r && L > 0 && conf_mode == FA_CONF_UNCONSTRAINED)
+            r = launch_conf_unconstrained(d, g, pc, tc, sc, cc, stream);
+        return r;
+    }));
 }
 
 namespace {
@@ -217,17 +275,22 @@ extern "C" int fa_chain_sample(const fa_table *t, const float *p, int32_t B, int
 {
     int rc = ready(t);
     if (rc) return rc;
-    Geometry g;
-    if (int grc = make_geometry(t->h, B, L, &g)) return grc;
-    if (!grid_fits(g)) return FA_ETOOBIG;
+    StepChunks ck;
+    if (int grc = plan_chunks(t->h, B, L, false, &ck)) return grc;
     // the chain reads every position's dense matrix
     if (t->h.leafless && L > 1) return FA_EINVAL;
     if (B == 0) return FA_OK;
-    WsLayout w = ws_layout(t->h, g);
-    if (!logZ || !states || !row_status || !ws || ws_bytes < w.total) return FA_EINVAL;
+    if (!logZ || !states || !row_status || !ws || ws_bytes < ws_need(ck)) return FA_EINVAL;
     if (L > 0 && (!p || !tree || !tokens)) return FA_EINVAL;
-    return hip_rc(launch_chain_sample(t->h.device_view(), g, p, tree, seed, logZ, states, tokens,
-                                      (uint8_t *)ws, w, row_status, stream));
+    const DevTable d = t->h.device_view();
+    return hip_rc(each_chunk(t->h, B, L, ck, (uint8_t *)ws, [&](int32_t b0, const Geometry &g,
+                                                                 uint8_t *wsc) {
+        return launch_chain_sample(d, g, rows(p, (size_t)L * d.V, b0),
+                                   rows(tree, 2 * (size_t)g.Lpad * g.mat, b0), seed,
+                                   rows(logZ, 1, b0), rows(states, (size_t)L + 1, b0),
+                                   rows(tokens, (size_t)L, b0), wsc, ws_layout(t->h, g),
+                                   rows(row_status, 1, b0), stream);
+    }));
 }
 
 extern "C" int fa_map_sizes(const fa_table *t, int32_t B, int32_t L, size_t *tree_bytes,
@@ -237,9 +300,10 @@ extern "C" int fa_map_sizes(const fa_table *t, int32_t B, int32_t L, size_t *tre
     if (t->h.nseg() > 0) return FA_EINVAL;  // range labels: no range-maximum structure
     Geometry g;
     if (int grc = make_geometry(t->h, B, L, &g)) return grc;
-    if (!grid_fits(g)) return FA_ETOOBIG;
+    StepChunks ck;
+    if (int rc = plan_chunks(t->h, B, L, true, &ck)) return rc;
     if (tree_bytes) *tree_bytes = g.tree_floats * sizeof(double);
-    if (ws_bytes) *ws_bytes = map_ws_layout(t->h, g).total;
+    if (ws_bytes) *ws_bytes = std::max<size_t>(ws_need(ck), 256);
     return FA_OK;
 }
 
@@ -251,15 +315,20 @@ extern "C" int fa_map_decode(const fa_table *t, const float *p, int32_t B, int32
     if (t && t->h.nseg() > 0) return FA_EINVAL;
     int rc = ready(t);
     if (rc) return rc;
-    Geometry g;
-    if (int grc = make_geometry(t->h, B, L, &g)) return grc;
-    if (!grid_fits(g)) return FA_ETOOBIG;
+    StepChunks ck;
+    if (int grc = plan_chunks(t->h, B, L, true, &ck)) return grc;
     if (B == 0) return FA_OK;
-    MapWs w = map_ws_layout(t->h, g);
     if (!logmax || !states || !row_status) return FA_EINVAL;
-    if (L > 0 && (!p || !tree || !tokens || !ws || ws_bytes < w.total)) return FA_EINVAL;
-    return hip_rc(launch_map_decode(t->h.device_view(), g, p, tree, (uint8_t *)ws, w, logmax,
-                                    states, tokens, row_status, stream));
+    if (L > 0 && (!p || !tree || !tokens || !ws || ws_bytes < ws_need(ck))) return FA_EINVAL;
+    const DevTable d = t->h.device_view();
+    return hip_rc(each_chunk(t->h, B, L, ck, (uint8_t *)ws, [&](int32_t b0, const Geometry &g,
+                                                                 uint8_t *wsc) {
+        return launch_map_decode(d, g, rows(p, (size_t)L * d.V, b0),
+                                 rows(tree, 2 * (size_t)g.Lpad * g.mat, b0), wsc,
+                                 map_ws_layout(t->h, g), rows(logmax, 1, b0),
+                                 rows(states, (size_t)L + 1, b0), rows(tokens, (size_t)L, b0),
+                                 rows(row_status, 1, b0), stream);
+    }));
 }
 
 extern "C" int fa_commit(int32_t B, int32_t L, int32_t V, const float *conf,

@@ -149,7 +149,7 @@ __global__ __launch_bounds__(64) void chain_backward(DevTable d, StepView sv,
     }
     if (status[b] != 0) return;
     const float *aL = va + ((size_t)b * (sv.Lpad + 1) + L) * Sp;
-    int j = wave_icdf(d.n_acc, philox_u01(seed, (uint32_t)b, lev, (uint32_t)L), lane,
+    int j = wave_icdf(d.n_acc, philox_u01(seed, (uint32_t)(sv.b0 + b), lev, (uint32_t)L), lane,
                       [&](int k) { return aL[d.acc[k]]; });
     int zn = j >= 0 ? d.acc[j] : -1;
     if (lane == 0) z[L] = zn;
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(64) void chain_backward(DevTable d, StepView sv,
         const int h = sv.Lpad + i;
         const float *M = sv.mat_ptr(tree, b, h);
         const bool tr = stored_transposed(h);
-        const int zi = wave_icdf(d.S, philox_u01(seed, (uint32_t)b, lev, (uint32_t)i), lane, [&](int a) {
+        const int zi = wave_icdf(d.S, philox_u01(seed, (uint32_t)(sv.b0 + b), lev, (uint32_t)i), lane, [&](int a) {
             const float m = tr ? M[(size_t)zn * Sp + a] : M[(size_t)a * Sp + zn];
             return ai[a] * m;
         });

@@ -172,6 +172,7 @@ __device__ inline double wave_incl_scan_d(double x, int lane)
 // -------------------------------------------------------------- indexing
 struct StepView {
     int32_t B, L, Lpad, K, Sp;
+    int32_t b0;  // batch row of this launch's row 0: draws are keyed by b0 + b
     size_t mat;
     // folded leaf pair values when the table keeps no dense leaves (the
     // leaf-level midpoint draws read them instead), else nullptr
@@ -197,6 +198,7 @@ inline StepView step_view(const Geometry &g)
 {
     StepView s;
     s.B = g.B;
+    s.b0 = g.b0;
     s.L = g.L;
     s.Lpad = g.Lpad;
     s.K = g.K;

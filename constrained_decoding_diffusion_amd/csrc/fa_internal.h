@@ -192,6 +192,7 @@ struct HostTable {
 // Step geometry shared by all calls.
 struct Geometry {
     int32_t B, L, Lpad, K, Sp;
+    int32_t b0;          // batch row of the chunk's row 0 (the draws' keys use b0 + b)
     size_t mat;          // floats per matrix = Sp*Sp
     size_t tree_floats;  // B * 2*Lpad * mat
     size_t meta_ints;    // B * 2*Lpad * 3 * Sp
@@ -201,11 +202,20 @@ struct Geometry {
 // FA_ETOOBIG for L >= 2^24
 int make_geometry(const HostTable &t, int32_t B, int32_t L, Geometry *g);
 
-// grids put (row, node) pairs in their second dimension
-inline bool grid_fits(const Geometry &g)
-{
-    return (int64_t)g.B * g.Lpad * 2 <= 65535 && g.L < (1 << 24);
-}
+// Rows per launch: the step kernels put (row, node) pairs in a grid
+// dimension of at most 65535, so a batch runs in chunks of at most
+// 32767 / Lpad rows, one after the other on the caller's stream, each chunk
+// with its own workspace slot.  The chunking depends on B and L only, so
+// every call of a step finds its chunk's workspace where the previous call
+// left it.
+struct StepChunks {
+    int32_t rows = 0;   // rows per full chunk
+    int32_t count = 0;  // chunks
+    size_t slot = 0;    // workspace bytes per chunk: the larger of a full and the last chunk
+};
+// map: slots sized for MAP decoding instead of the sampling step.
+// FA_ETOOBIG when even one row does not fit (2 Lpad > 65535).
+int plan_chunks(const HostTable &t, int32_t B, int32_t L, bool map, StepChunks *c);
 
 // Workspace layout (bytes from the start of ws), sized for the largest user.
 struct WsLayout {

@@ -6,6 +6,7 @@
 // buffer is the caller's, as in fa_span_tree, and the kernels are the same.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "fa_internal.h"
@@ -54,27 +55,38 @@ extern "C" int fa_span_tree_noalloc(const fa_table *t, int32_t B, int32_t L, flo
     // fa_build_transitions left in the caller's workspace: fa_span_tree only
     if (t->h.first_sparse) return FA_EINVAL;
     if (!t->h.dev) return FA_ESTATE;
-    Geometry g;
-    if (int grc = make_geometry(t->h, B, L, &g)) return grc;
-    if (!grid_fits(g)) return FA_ETOOBIG;
+    StepChunks ck;
+    if (int grc = plan_chunks(t->h, B, L, false, &ck)) return grc;
     if (B == 0) return FA_OK;
     if (!logZ || !row_status) return FA_EINVAL;
     if (L > 0 && (!tree || !meta)) return FA_EINVAL;
     // the partial tiles go to offset 0 of the scratch array; nothing else of
     // the workspace is touched on a table with a dense first level.  The
     // split rule bounds them by 2^21 floats (see fa.h); the check guards
-    // that bound should the rule change.
-    size_t kp = 0;
-    for (int level = 1; level <= g.K; ++level) {
-        const int s = tree_ksplit(g, level);
-        if (s > 1) kp = std::max(kp, (size_t)g.B * (g.Lpad >> level) * s * g.mat * sizeof(float));
-    }
-    if (kp > kScratchBytes) return FA_ETOOBIG;
+    // that bound should the rule change.  Row chunks run in turn on the
+    // stream and reuse the array.
     uint8_t *ptr = nullptr;
-    if (int rc = scratch_of_current_device(&ptr)) return rc;
-    WsLayout ws{};
-    ws.kpart = 0;
-    const int rc = launch_span_tree(t->h.device_view(), g, tree, meta, ptr, ws, logZ, row_status,
-                                    stream);
-    return rc == 0 ? FA_OK : FA_EHIP;
+    const DevTable d = t->h.device_view();
+    for (int32_t k = 0; k < ck.count; ++k) {
+        const int32_t b0 = k * ck.rows;
+        Geometry g;
+        make_geometry(t->h, std::min(ck.rows, B - b0), L, &g);
+        g.b0 = b0;
+        size_t kp = 0;
+        for (int level = 1; level <= g.K; ++level) {
+            const int s = tree_ksplit(g, level);
+            if (s > 1) kp = std::max(kp, (size_t)g.B * (g.Lpad >> level) * s * g.mat * sizeof(float));
+        }
+        if (kp > kScratchBytes) return FA_ETOOBIG;
+        if (!ptr)
+            if (int rc = scratch_of_current_device(&ptr)) return rc;
+        WsLayout ws{};
+        ws.kpart = 0;
+        const size_t mrow = 2 * (size_t)g.Lpad;
+        const int rc = launch_span_tree(d, g, tree ? tree + mrow * g.mat * b0 : tree,
+                                        meta ? meta + mrow * 3 * g.Sp * b0 : meta, ptr, ws,
+                                        logZ + b0, row_status + b0, stream);
+        if (rc) return FA_EHIP;
+    }
+    return FA_OK;
 }

@@ -237,7 +237,7 @@ __global__ __launch_bounds__(kTokThreads) void sample_tokens(
         int pick = -1;
         double base = 0.0, target = 0.0;
         if (T > 0.0) {
-            target = (double)philox_u01(seed, (uint32_t)b, (uint32_t)(sv.K + 1), (uint32_t)i) * T;
+            target = (double)philox_u01(seed, (uint32_t)(sv.b0 + b), (uint32_t)(sv.K + 1), (uint32_t)i) * T;
             double acc = 0.0, acc_last = 0.0;
             int last = -1;
             for (int ch = 0; ch < nchunks; ++ch) {

@@ -90,7 +90,7 @@ __device__ void draw_root(const DevTable &d, const StepView &sv, const float *__
     const int m = wave_max_i(e);
     int j = -1;
     if (status[b] == 0 && m > kNeg) {
-        const float u = philox_u01(seed, (uint32_t)b, 0u, 0u);
+        const float u = philox_u01(seed, (uint32_t)(sv.b0 + b), 0u, 0u);
         j = wave_icdf(d.n_acc, u, lane, [&](int k) {
             const int f = d.acc[k];
             const float x = R[f];
@@ -144,7 +144,7 @@ __device__ int draw_mid_pairs(const DevTable &d, const StepView &sv, const int32
         if (!(a > 0.f) || !(c > 0.f) || coL[k] <= kNeg || coR[k] <= kNeg) return kNeg;
         return fexp(a) + coL[k] + fexp(c) + coR[k];
     };
-    const float u = philox_u01(seed, (uint32_t)b, (uint32_t)level, (uint32_t)idx);
+    const float u = philox_u01(seed, (uint32_t)(sv.b0 + b), (uint32_t)level, (uint32_t)idx);
     int j = -1;
     int e = kNeg;
     for (int k = lane; k < d.S; k += 64) e = max(e, expo(k));
@@ -180,7 +180,7 @@ __device__ int draw_mid(const DevTable &d, const StepView &sv, const float *__re
         if (!(a > 0.f) || !(c > 0.f) || cl <= kNeg || cr <= kNeg) return kNeg;
         return fexp(a) + cl + fexp(c) + cr;
     };
-    const float u = philox_u01(seed, (uint32_t)b, (uint32_t)level, (uint32_t)idx);
+    const float u = philox_u01(seed, (uint32_t)(sv.b0 + b), (uint32_t)level, (uint32_t)idx);
     constexpr int C = 8;
     if (d.S <= 64 * C) {
         // every candidate's data in registers: one round of loads

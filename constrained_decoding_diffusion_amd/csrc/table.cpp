@@ -173,6 +173,7 @@ int make_geometry(const HostTable &t, int32_t B, int32_t L, Geometry *g)
         ++K;
     }
     g->B = B;
+    g->b0 = 0;
     g->L = L;
     g->Lpad = Lpad;
     g->K = K;
@@ -180,6 +181,25 @@ int make_geometry(const HostTable &t, int32_t B, int32_t L, Geometry *g)
     g->mat = (size_t)t.Sp * t.Sp;
     g->tree_floats = L > 0 ? (size_t)B * 2 * Lpad * g->mat : 0;
     g->meta_ints = L > 0 ? (size_t)B * 2 * Lpad * 3 * t.Sp : 0;
+    return FA_OK;
+}
+
+int plan_chunks(const HostTable &t, int32_t B, int32_t L, bool map, StepChunks *c)
+{
+    Geometry g;
+    if (int rc = make_geometry(t, B, L, &g)) return rc;
+    if ((int64_t)g.Lpad * 2 > 65535) return FA_ETOOBIG;
+    c->rows = std::max<int32_t>(1, std::min<int32_t>(std::max<int32_t>(B, 1), 32767 / g.Lpad));
+    c->count = B == 0 ? 0 : (B + c->rows - 1) / c->rows;
+    const int32_t last = B - (c->count - 1) * c->rows;
+    size_t slot = 0;
+    for (int32_t nb : {c->rows, last}) {
+        if (nb <= 0) continue;
+        Geometry gc;
+        make_geometry(t, nb, L, &gc);
+        slot = std::max(slot, map ? map_ws_layout(t, gc).total : ws_layout(t, gc).total);
+    }
+    c->slot = (slot + 255) & ~size_t(255);
     return FA_OK;
 }
 
@@ -885,9 +905,10 @@ extern "C" int fa_sizes(const fa_table *t, int32_t B, int32_t L, size_t *tree_by
     Geometry g;
     if (int grc = make_geometry(t->h, B, L, &g)) return grc;
     if ((size_t)g.Lpad * g.Sp > (size_t)1 << 40) return FA_ETOOBIG;
-    if ((int64_t)B * g.Lpad * 2 > 65535 || L >= (1 << 24)) return FA_ETOOBIG;
+    StepChunks ck;
+    if (int rc = plan_chunks(t->h, B, L, false, &ck)) return rc;
     if (tree_bytes) *tree_bytes = g.tree_floats * sizeof(float);
     if (meta_bytes) *meta_bytes = g.meta_ints * sizeof(int32_t);
-    if (ws_bytes) *ws_bytes = ws_layout(t->h, g).total;
+    if (ws_bytes) *ws_bytes = std::max<size_t>((size_t)ck.count * ck.slot, 256);
     return FA_OK;
 }

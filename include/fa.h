@@ -161,7 +161,11 @@ int fa_table_state_map(const fa_table *t, int32_t *orig_of);
  * B and length L needs.  Any output pointer may be NULL.  The four calls of
  * one step take the same workspace, in order on one stream, and it must not
  * be written in between: fa_marginals reads pair-value sources that
- * fa_build_transitions leaves in it.  Errors: FA_EINVAL, FA_ETOOBIG.
+ * fa_build_transitions leaves in it.  Any B is taken: the step calls run a
+ * batch in chunks of at most 32767 / Lpad rows, one after the other on the
+ * stream, each chunk with its own slot of the workspace (the draws keyed by
+ * the row's index in the whole batch, so chunking changes no result).
+ * Errors: FA_EINVAL, FA_ETOOBIG (L >= 2^24, or 2 Lpad > 65535).
  */
 int fa_sizes(const fa_table *t, int32_t B, int32_t L, size_t *tree_bytes, size_t *meta_bytes,
              size_t *ws_bytes);

@@ -167,8 +167,16 @@ def test_sizes_and_limits():
     assert meta == 3 * 2 * 8 * 3 * Sp * 4
     assert ws > 0
     assert t.sizes(0, 6)[0] == 0
+    # a batch beyond one launch's grid runs in row chunks, each with its own
+    # workspace slot: 40000 rows of Lpad 8 take 10 chunks of 4095 rows
+    tb1, mb1, wb1 = t.sizes(4095, 6)
+    tbn, mbn, wbn = t.sizes(40000, 6)
+    assert tbn == 40000 * 2 * 8 * Sp * Sp * 4 and mbn == 40000 * 2 * 8 * 3 * Sp * 4
+    assert wbn >= 10 * wb1
+    # one row must fit: 2 Lpad <= 65535
+    t.sizes(1, 16384)
     with pytest.raises(fa.FaError) as ei:
-        t.sizes(40000, 6)
+        t.sizes(1, 16385)
     assert ei.value.code == _fa.FA_ETOOBIG
     # lengths at and far beyond the kernels' 24-bit position fields are
     # rejected before any geometry is formed (no overflow of the padded length)
