@@ -22,6 +22,8 @@
 // writing it straight to HBM while the MFMAs run keeps that write-back out
 // of the streaming kernels.
 #include "device_common.h"
+#include <algorithm>
+#include <atomic>
 
 namespace fa {
 namespace {
@@ -400,15 +402,25 @@ __global__ void tree_logz_empty(DevTable d, int B, double *__restrict__ logZ,
     if (!ok) atomicOr(&status[b], (int)FA_ROW_INFEASIBLE);
 }
 
-// Large levels with one 256x256 output tile per workgroup (one whole
-// product when Sp = 256): 8 waves of 64 x 128 (2 x 4 MFMA tiles of 32x32),
-// 128 MFMAs per wave per K step of 32, double-buffered LDS (147 KB, one
-// workgroup per CU).  Every K step issues the same loads (the last step
-// re-reads the final K block), and the loads of block ks+1 are in flight
-// while block ks computes.  Row exponents are reduced inside the workgroup: one
-// store (full rows) or atomicMax (several column tiles) per row.
+// Large levels with 256x256 output tiles (one whole product when Sp = 256),
+// one persistent workgroup per CU walking tiles v = blockIdx.x + k gridDim.x:
+// 8 waves of 64 x 128 (2 x 4 MFMA tiles of 32x32), 128 MFMAs per wave per K
+// step of 32, double-buffered LDS (147 KB).  The
+// loads of block ks+1 are in flight while block ks computes; during the last
+// K step of a tile they fetch block 0 of the workgroup's next tile (or
+// re-read block 0 of the current one when there is none), so the next tile
+// starts from a filled buffer while the current one is stored.  Row
+// exponents are reduced inside the workgroup through the free LDS buffer:
+// one store (full rows) or atomicMax (several column tiles) per row.
 constexpr int kHuge = 256;
 constexpr int kHugeThreads = 512;
+
+// the operand side of one 256x256 tile: stored rows tm.. of F, tn.. of G
+struct HugeSrc {
+    const float *F, *G;
+    const int32_t *coF, *coG, *rfF, *rfG;
+    int tm, tn;
+};
 
 __global__ __launch_bounds__(kHugeThreads) void span_gemm256(StepView sv, float *__restrict__ tree,
                                                              int32_t *__restrict__ meta, int n0,
@@ -418,26 +430,33 @@ __global__ __launch_bounds__(kHugeThreads) void span_gemm256(StepView sv, float 
     const int tiles = Sp / kHuge;
     const int per_prod = tiles * tiles;
     const int nwork = sv.B * nn * per_prod;
-    int w = blockIdx.x;
     const int full = nwork & ~7;
-    if (per_prod > 1 && w < full) w = (w & 7) * (full >> 3) + (w >> 3);  // XCD-contiguous order
-    const int prod = w / per_prod, tile = w % per_prod;
-    const int tm = (tile / tiles) * kHuge, tn = (tile % tiles) * kHuge;
-    const int b = prod / nn, n = n0 + prod % nn;
-    const bool tr = stored_transposed(n);
-    const int hF = tr ? 2 * n + 1 : 2 * n, hG = tr ? 2 * n : 2 * n + 1;
-    const float *F = sv.mat_ptr((const float *)tree, b, hF);
-    const float *G = sv.mat_ptr((const float *)tree, b, hG);
-    const int32_t *roF = sv.meta_ptr((const int32_t *)meta, b, hF, 0);
-    const int32_t *coF = sv.meta_ptr((const int32_t *)meta, b, hF, 1);
-    const int32_t *rfF = sv.meta_ptr((const int32_t *)meta, b, hF, 2);
-    const int32_t *roG = sv.meta_ptr((const int32_t *)meta, b, hG, 0);
-    const int32_t *coG = sv.meta_ptr((const int32_t *)meta, b, hG, 1);
-    const int32_t *rfG = sv.meta_ptr((const int32_t *)meta, b, hG, 2);
-    float *D = sv.mat_ptr(tree, b, n);
-    int32_t *roD = sv.meta_ptr(meta, b, n, 0);
-    int32_t *coD = sv.meta_ptr(meta, b, n, 1);
-    int32_t *rfD = sv.meta_ptr(meta, b, n, 2);
+    // with several tiles per product, the tiles that run on one XCD (every
+    // eighth workgroup) are consecutive ones, which share operand rows in L2
+    auto work = [&](int v) { return (per_prod > 1 && v < full) ? (v & 7) * (full >> 3) + (v >> 3) : v; };
+    auto node_of = [&](int w, int &b, int &n, int &tm, int &tn) {
+        const int prod = w / per_prod, tile = w % per_prod;
+        tm = (tile / tiles) * kHuge;
+        tn = (tile % tiles) * kHuge;
+        b = prod / nn;
+        n = n0 + prod % nn;
+    };
+    auto src_of = [&](int v) {
+        int b, n, tm, tn;
+        node_of(work(v), b, n, tm, tn);
+        const bool tr = stored_transposed(n);
+        const int hF = tr ? 2 * n + 1 : 2 * n, hG = tr ? 2 * n : 2 * n + 1;
+        HugeSrc s;
+        s.F = sv.mat_ptr((const float *)tree, b, hF);
+        s.G = sv.mat_ptr((const float *)tree, b, hG);
+        s.coF = sv.meta_ptr((const int32_t *)meta, b, hF, 1);
+        s.coG = sv.meta_ptr((const int32_t *)meta, b, hG, 1);
+        s.rfF = sv.meta_ptr((const int32_t *)meta, b, hF, 2);
+        s.rfG = sv.meta_ptr((const int32_t *)meta, b, hG, 2);
+        s.tm = tm;
+        s.tn = tn;
+        return s;
+    };
 
     __shared__ __align__(16) float Fs[2][kHuge][kLdk2];
     __shared__ __align__(16) float Gs[2][kHuge][kLdk2];
@@ -445,48 +464,44 @@ __global__ __launch_bounds__(kHugeThreads) void span_gemm256(StepView sv, float 
     // loader: thread t stages float4 (t & 7) of rows (t >> 3) + 64 q, q < 4,
     // of both operands: eight lanes read one 128-byte row segment
     const int lrow = tid >> 3, lk = (tid & 7) * 4;
-    int rfFq[4], rfGq[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        rfFq[q] = rfF[tm + lrow + 64 * q];
-        rfGq[q] = rfG[tn + lrow + 64 * q];
-    }
-    const float *Frow = F + (size_t)(tm + lrow) * Sp + lk;
-    const float *Grow = G + (size_t)(tn + lrow) * Sp + lk;
     const size_t q_rows = (size_t)64 * Sp;
     const int wr = (wave >> 1) * 64, wc = (wave & 1) * 128;
     const int l32 = lane & 31, half = lane >> 5;
-
-    f32x16 acc[2][4];
-#pragma unroll
-    for (int ry = 0; ry < 2; ++ry)
-#pragma unroll
-        for (int cy = 0; cy < 4; ++cy)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[ry][cy][r] = 0.f;
-
     const int nk = Sp / kBK2;
+
     struct Stage {
         float4 f[4], g[4];
         int4 cf, cg;
+        int rf[4], rg[4];
     };
-    auto gload = [&](Stage &st, int ks) {
-        const int k0 = min(ks, nk - 1) * kBK2;
+    // the rows' exponents come with block 0 of a tile and stay for its other blocks
+    auto gload = [&](Stage &st, const HugeSrc &s, int ks, bool rows) {
+        const int k0 = ks * kBK2;
+        const float *Fr = s.F + (size_t)(s.tm + lrow) * Sp + lk + k0;
+        const float *Gr = s.G + (size_t)(s.tn + lrow) * Sp + lk + k0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            st.f[q] = *reinterpret_cast<const float4 *>(Frow + q * q_rows + k0);
-            st.g[q] = *reinterpret_cast<const float4 *>(Grow + q * q_rows + k0);
+            st.f[q] = *reinterpret_cast<const float4 *>(Fr + q * q_rows);
+            st.g[q] = *reinterpret_cast<const float4 *>(Gr + q * q_rows);
         }
-        st.cf = *reinterpret_cast<const int4 *>(coF + k0 + lk);
-        st.cg = *reinterpret_cast<const int4 *>(coG + k0 + lk);
+        st.cf = *reinterpret_cast<const int4 *>(s.coF + k0 + lk);
+        st.cg = *reinterpret_cast<const int4 *>(s.coG + k0 + lk);
+        if (rows) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                st.rf[q] = s.rfF[s.tm + lrow + 64 * q];
+                st.rg[q] = s.rfG[s.tn + lrow + 64 * q];
+            }
+        }
     };
     auto lstore = [&](const Stage &st, int buf) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            *reinterpret_cast<float4 *>(&Fs[buf][lrow + 64 * q][lk]) = fold4(st.f[q], st.cf, rfFq[q]);
-            *reinterpret_cast<float4 *>(&Gs[buf][lrow + 64 * q][lk]) = fold4(st.g[q], st.cg, rfGq[q]);
+            *reinterpret_cast<float4 *>(&Fs[buf][lrow + 64 * q][lk]) = fold4(st.f[q], st.cf, st.rf[q]);
+            *reinterpret_cast<float4 *>(&Gs[buf][lrow + 64 * q][lk]) = fold4(st.g[q], st.cg, st.rg[q]);
         }
     };
+    f32x16 acc[2][4];
     auto mfmas = [&](int buf) {
 #pragma unroll
         for (int t = 0; t < kBK2 / 2; t += 4) {
@@ -508,62 +523,123 @@ __global__ __launch_bounds__(kHugeThreads) void span_gemm256(StepView sv, float 
                 }
         }
     };
+
+    int v = blockIdx.x;
+    if (v >= nwork) return;
+    HugeSrc cur = src_of(v);
     Stage st;
-    gload(st, 0);
+    gload(st, cur, 0, true);
     lstore(st, 0);
     __syncthreads();
-    // step ks: issue the loads of K block ks+1, compute buffer ks & 1 (128
-    // MFMAs per wave cover the load latency), store block ks+1 into the other
-    // buffer.  nk = Sp / 32 is even.
-    // The scheduling barriers keep the compiler from moving the fold
-    // arithmetic of the stores (which waits for the loads) into the MFMAs.
-    for (int ks = 0; ks < nk; ks += 2) {
-        gload(st, ks + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(0);
-        __builtin_amdgcn_sched_barrier(0);
-        lstore(st, 1);
+    for (;;) {
+        const int vn = v + (int)gridDim.x;
+        const bool more = vn < nwork;
+        const HugeSrc nxt = more ? src_of(vn) : cur;
+#pragma unroll
+        for (int ry = 0; ry < 2; ++ry)
+#pragma unroll
+            for (int cy = 0; cy < 4; ++cy)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[ry][cy][r] = 0.f;
+        // step ks: issue the loads of K block ks+1 (of the next tile after
+        // the last block), compute buffer ks & 1 (128 MFMAs per wave cover
+        // the load latency), store that block into the other buffer.
+        // nk = Sp / 32 is even.  The scheduling barriers keep the compiler
+        // from moving the fold arithmetic of the stores (which waits for
+        // the loads) into the MFMAs.
+        for (int ks = 0; ks < nk; ks += 2) {
+            gload(st, cur, ks + 1, false);
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(0);
+            __builtin_amdgcn_sched_barrier(0);
+            lstore(st, 1);
+            __syncthreads();
+            const bool last = ks + 2 == nk;
+            gload(st, last ? nxt : cur, last ? 0 : ks + 2, last);
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(1);
+            __builtin_amdgcn_sched_barrier(0);
+            lstore(st, 0);
+            __syncthreads();
+        }
+        // epilogue: D, and per row the largest e(D[i][j]) + coD[j]
+        int b, n, tm, tn;
+        node_of(work(v), b, n, tm, tn);
+        const bool tr = stored_transposed(n);
+        const int hF = tr ? 2 * n + 1 : 2 * n, hG = tr ? 2 * n : 2 * n + 1;
+        const int32_t *roF = sv.meta_ptr((const int32_t *)meta, b, hF, 0);
+        const int32_t *roG = sv.meta_ptr((const int32_t *)meta, b, hG, 0);
+        float *D = sv.mat_ptr(tree, b, n);
+        // this lane's first row and column in the tile; the empty asm keeps
+        // the addresses derived from them out of the tile loop (where they
+        // would stay live through the MFMAs)
+        int row0 = wr + half * 4, col0 = wc + l32;
+        asm volatile("" : "+v"(row0), "+v"(col0));
+        // every exponent the epilogue needs is loaded first, so that one
+        // load latency covers them all and the stores of D go out meanwhile
+        int coDj[4];
+#pragma unroll
+        for (int cy = 0; cy < 4; ++cy) {
+            const int j = tn + col0 + 32 * cy;
+            coDj[cy] = add_exp(roG[j], cur.rfG[j]);
+        }
+        int outer = kNeg;  // roD[tm + tid] (tid < 256) or coD[tn + tid - 256]
+        if (tid < kHuge) {
+            if (tn == 0) outer = add_exp(roF[tm + tid], cur.rfF[tm + tid]);
+        } else if (tm == 0) {
+            outer = add_exp(roG[tn + tid - kHuge], cur.rfG[tn + tid - kHuge]);
+        }
+#pragma unroll
+        for (int ry = 0; ry < 2; ++ry)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+#pragma unroll
+                for (int cy = 0; cy < 4; ++cy)
+                    __builtin_nontemporal_store(acc[ry][cy][r],
+                                                &D[(size_t)(tm + row0 + 32 * ry + (r >> 2) * 8 + (r & 3)) * Sp +
+                                                   tn + col0 + 32 * cy]);
+        // per row the maximum over this lane's four columns, into buffer 1
+        // (free until the next tile's first store into it): E[il][l32] of
+        // the wave's column half, rows padded to kLdk2 entries
+        int *E = reinterpret_cast<int *>(wc == 0 ? &Fs[1][0][0] : &Gs[1][0][0]);
+#pragma unroll
+        for (int ry = 0; ry < 2; ++ry) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                int e = kNeg;
+#pragma unroll
+                for (int cy = 0; cy < 4; ++cy) {
+                    const float x = acc[ry][cy][r];
+                    int ex;
+                    frexpf(x, &ex);
+                    const bool ok = (x > 0.f) & (coDj[cy] > kNeg);
+                    e = max(e, ok ? ex + coDj[cy] : kNeg);
+                }
+                E[(row0 + 32 * ry + (r >> 2) * 8 + (r & 3)) * kLdk2 + l32] = e;
+            }
+        }
         __syncthreads();
-        gload(st, ks + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(1);
-        __builtin_amdgcn_sched_barrier(0);
-        lstore(st, 0);
-        __syncthreads();
-    }
-    // epilogue: D, and per row the largest e(D[i][j]) + coD[j]
-    int coDj[4];
-#pragma unroll
-    for (int cy = 0; cy < 4; ++cy) {
-        const int j = tn + wc + 32 * cy + l32;
-        coDj[cy] = add_exp(roG[j], rfG[j]);
-    }
-    int *red = reinterpret_cast<int *>(&Fs[0][0][0]);  // [2][kHuge] row maxima per column half
-#pragma unroll
-    for (int ry = 0; ry < 2; ++ry) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int il = wr + 32 * ry + (r >> 2) * 8 + half * 4 + (r & 3);
+        if (tid < kHuge) {
+            const int4 *e0 = reinterpret_cast<const int4 *>(&Fs[1][tid][0]);
+            const int4 *e1 = reinterpret_cast<const int4 *>(&Gs[1][tid][0]);
             int e = kNeg;
 #pragma unroll
-            for (int cy = 0; cy < 4; ++cy) {
-                const float v = acc[ry][cy][r];
-                __builtin_nontemporal_store(v, &D[(size_t)(tm + il) * Sp + tn + wc + 32 * cy + l32]);
-                if (v > 0.f && coDj[cy] > kNeg) e = max(e, fexp(v) + coDj[cy]);
+            for (int k = 0; k < 8; ++k) {
+                const int4 x = e0[k], y = e1[k];
+                e = max(e, max(max(max(x.x, x.y), max(x.z, x.w)), max(max(y.x, y.y), max(y.z, y.w))));
             }
-#pragma unroll
-            for (int o = 16; o > 0; o >>= 1) e = max(e, __shfl_xor(e, o));
-            if (l32 == 0) red[(wc / 128) * kHuge + il] = e;
+            int32_t *rfD = sv.meta_ptr(meta, b, n, 2);
+            if (tiles == 1) rfD[tm + tid] = e;
+            else if (e > kNeg) atomicMax(&rfD[tm + tid], e);
+            if (tn == 0) sv.meta_ptr(meta, b, n, 0)[tm + tid] = outer;
+        } else if (tm == 0) {
+            sv.meta_ptr(meta, b, n, 1)[tn + tid - kHuge] = outer;
         }
+        if (!more) break;
+        __syncthreads();  // buffer 1 is read above and written by the next tile
+        v = vn;
+        cur = nxt;
     }
-    __syncthreads();
-    if (tid < kHuge) {
-        const int e = max(red[tid], red[kHuge + tid]);
-        if (tiles == 1) rfD[tm + tid] = e;
-        else if (e > kNeg) atomicMax(&rfD[tm + tid], e);
-    }
-    if (tn == 0 && tid < kHuge) roD[tm + tid] = add_exp(roF[tm + tid], rfF[tm + tid]);
-    if (tm == 0 && tid >= kHuge) coD[tn + tid - kHuge] = add_exp(roG[tn + tid - kHuge], rfG[tn + tid - kHuge]);
 }
 
 
@@ -972,6 +1048,22 @@ int launch_sparse(const DevTable &d, const Geometry &g, StepView sv, SpLevel lv,
     return (int)hipGetLastError();
 }
 
+// compute units of the current device (the persistent grid size), queried
+// once per device; any grid size gives the same result
+int device_cus()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 // one tree level as dense products over nodes n0 .. n0 + nn - 1 of every row
 int launch_dense_level(const Geometry &g, StepView sv, int k, int n0, int nn, float *tree,
                        int32_t *meta, uint8_t *ws, const WsLayout &w, hipStream_t st)
@@ -984,7 +1076,8 @@ int launch_dense_level(const Geometry &g, StepView sv, int k, int n0, int nn, fl
     const int huge_tiles = g.Sp / kHuge;
     const long long huge_wgs = (long long)g.B * nn * huge_tiles * huge_tiles;
     if (ks == 1 && g.Sp % kHuge == 0 && huge_wgs >= 256) {
-        span_gemm256<<<(unsigned)huge_wgs, kHugeThreads, 0, st>>>(sv, tree, meta, n0, nn);
+        const unsigned grid = (unsigned)std::min<long long>(huge_wgs, device_cus());
+        span_gemm256<<<grid, kHugeThreads, 0, st>>>(sv, tree, meta, n0, nn);
     } else if (ks == 1 && g.Sp % kBig == 0 && big_wgs >= 256) {
         span_gemm128<<<(unsigned)big_wgs, kBigThreads, 0, st>>>(sv, tree, meta, n0, nn);
     } else {
