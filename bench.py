@@ -443,6 +443,26 @@ def _select(rows, name):
     return out
 
 
+def tree_levels(rows):
+    """Dispatch id -> "L<k>" for the span tree's launches (level k of the
+    step: the k-th product launch after tree_init_rf; a split-K reduce
+    takes its product's level), so that levels of one launch shape stay
+    apart in the summaries."""
+    out, level = {}, None
+    for r in sorted(rows, key=lambda r: int(r["Dispatch_Id"])):
+        n = r["Kernel_Name"]
+        if "tree_init_rf" in n:
+            level = 0
+        elif level is not None and ("span_gemm" in n or "span_sparse<" in n):
+            level += 1
+            out[r["Dispatch_Id"]] = f"L{level}"
+        elif level is not None and "span_reduce" in n:
+            out[r["Dispatch_Id"]] = f"L{level}"
+        elif "tree_logz" in n:
+            level = None
+    return out
+
+
 def summarize_counters(fetch_dir, write_dir, command):
     """profiles/traffic_<kernel>.json and profiles/counters_json_like_dfa.md
     from one FETCH_SIZE and one WRITE_SIZE pass (each with --copy-calib)."""
@@ -505,13 +525,14 @@ def summarize_trace(trace_dir, command, workload=3):
         lines.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['TotalDurationNs']) / 1e6:.2f} | {float(r['Percentage']):.1f} |")
     groups = {}
+    lv = tree_levels(trace)
     for r in trace:
-        k = (short(r["Kernel_Name"]), r["Grid_Size_X"], r["Grid_Size_Y"])
+        k = (short(r["Kernel_Name"]), lv.get(r["Dispatch_Id"], ""), r["Grid_Size_X"], r["Grid_Size_Y"])
         groups.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    lines += ["", "Per launch shape (grid in threads):", "", "| kernel | grid x | grid y | calls | avg us |",
-              "|---|---|---|---|---|"]
+    lines += ["", "Per launch shape (grid in threads; tree level of the step for the span tree's launches):", "",
+              "| kernel | level | grid x | grid y | calls | avg us |", "|---|---|---|---|---|---|"]
     for k, v in sorted(groups.items(), key=lambda kv: -sum(kv[1]))[:30]:
-        lines.append(f"| `{k[0]}` | {k[1]} | {k[2]} | {len(v)} | {sum(v) / len(v):.1f} |")
+        lines.append(f"| `{k[0]}` | {k[1]} | {k[2]} | {k[3]} | {len(v)} | {sum(v) / len(v):.1f} |")
     with open(os.path.join(ROOT, "profiles", f"step_{stem}_kernel_trace.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
@@ -525,9 +546,10 @@ def summarize_mfma(pmc_dir, command, workload=3):
     rows = list(csv.DictReader(open(os.path.join(pmc_dir, "run_counter_collection.csv"))))
     short = lambda n: n.replace("fa::(anonymous namespace)::", "").split("(fa::")[0][:60]
     agg = defaultdict(lambda: defaultdict(list))
+    lv = tree_levels({r["Dispatch_Id"]: r for r in rows}.values())
     for r in rows:
         d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-        agg[(short(r["Kernel_Name"]), int(r["Grid_Size"]))][r["Counter_Name"]].append(
+        agg[(short(r["Kernel_Name"]), int(r["Grid_Size"]), lv.get(r["Dispatch_Id"], ""))][r["Counter_Name"]].append(
             (float(r["Counter_Value"]), d))
     stem, title = TRACE_NAMES[workload]
     lines = [f"# MFMA utilization of the constrained step ({title})", "",
@@ -535,10 +557,10 @@ def summarize_mfma(pmc_dir, command, workload=3):
              "MfmaUtil is rocprofv3's derived counter (summed SQ_VALU_MFMA_BUSY_CYCLES over "
              "GRBM_GUI_ACTIVE x SIMDs); the executed flops are SQ_INSTS_VALU_MFMA_MOPS_* x 512. "
              "Durations are under the counter pass.", "",
-             "| kernel | grid threads | launches | MfmaUtil % | fp32 MFMA GFLOP | bf16 MFMA GFLOP | avg us | "
-             "fp32 TFLOP/s |", "|---|---|---|---|---|---|---|---|"]
+             "| kernel | level | grid threads | launches | MfmaUtil % | fp32 MFMA GFLOP | bf16 MFMA GFLOP | avg us | "
+             "fp32 TFLOP/s |", "|---|---|---|---|---|---|---|---|---|"]
     mean = lambda xs: sum(x[0] for x in xs) / len(xs) if xs else 0.0
-    for (name, grid), c in sorted(agg.items(), key=lambda kv: -mean(kv[1].get(
+    for (name, grid, level), c in sorted(agg.items(), key=lambda kv: -mean(kv[1].get(
             "SQ_INSTS_VALU_MFMA_MOPS_F32", [])) - mean(kv[1].get("SQ_INSTS_VALU_MFMA_MOPS_BF16", []))):
         mu = c.get("MfmaUtil", [])
         f32 = mean(c.get("SQ_INSTS_VALU_MFMA_MOPS_F32", [])) * 512
@@ -546,7 +568,7 @@ def summarize_mfma(pmc_dir, command, workload=3):
         if not mu or (f32 == 0 and bf == 0):
             continue
         us = sum(x[1] for x in mu) / len(mu)
-        lines.append(f"| `{name}` | {grid} | {len(mu)} | {mean(mu):.1f} | {f32 / 1e9:.3f} | {bf / 1e9:.3f} | "
+        lines.append(f"| `{name}` | {level} | {grid} | {len(mu)} | {mean(mu):.1f} | {f32 / 1e9:.3f} | {bf / 1e9:.3f} | "
                      f"{us:.1f} | {f32 / (us * 1e6):.1f} |")
     with open(os.path.join(ROOT, "profiles", f"mfma_{stem}.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")

@@ -62,7 +62,7 @@ extern "C" int fa_span_tree_noalloc(const fa_table *t, int32_t B, int32_t L, flo
     if (L > 0 && (!tree || !meta)) return FA_EINVAL;
     // the partial tiles go to offset 0 of the scratch array; nothing else of
     // the workspace is touched on a table with a dense first level.  The
-    // split rule bounds them by 2^21 floats (see fa.h); the check guards
+    // split rule bounds them by 2^20 floats (see fa.h); the check guards
     // that bound should the rule change.  Row chunks run in turn on the
     // stream and reuse the array.
     uint8_t *ptr = nullptr;

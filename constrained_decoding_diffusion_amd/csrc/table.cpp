@@ -206,15 +206,17 @@ int plan_chunks(const HostTable &t, int32_t B, int32_t L, bool map, StepChunks *
 int tree_ksplit(const Geometry &g, int level)
 {
     // large levels run on the 128x128 kernel; smaller ones on 64x64 tiles,
-    // split along K (chunks of 64) only when the tiles alone would leave most
-    // of the 256 compute units idle
+    // split along K only while the tiles with their splits still fit the
+    // 256 compute units once and every split keeps a K range of at least
+    // 256: the reduce is a launch of its own (about as long as 8 K blocks of
+    // 32), so shorter splits cost more than they save
     const long long nn = g.Lpad >> level;
     const long long big = (long long)g.B * nn * (g.Sp / 128) * (g.Sp / 128);
     if (g.Sp % 128 == 0 && big >= 256) return 1;
     const long long small = (long long)g.B * nn * (g.Sp / 64) * (g.Sp / 64);
     int s = 1;
     // the split must divide the K blocks of 64 exactly
-    while ((g.Sp / 64) % (s * 2) == 0 && small * s * 2 <= 512) s *= 2;
+    while ((g.Sp / 64) % (s * 2) == 0 && small * s * 2 <= 256 && g.Sp / (s * 2) >= 256) s *= 2;
     return s;
 }
 

@@ -67,9 +67,46 @@ __device__ inline float4 fold4(float4 x, int4 c, int rfrow)
     return x;
 }
 
+// The largest exponent e(D[i][j]) + coD[j] of each row of an output tile,
+// reduced through LDS instead of lane shuffles: every lane has written its
+// maximum over its own columns of row i to E[i * ld + slot] (one slot per
+// lane and column group), and after a barrier thread t < rows reads row t's
+// `slots` entries (a multiple of 4; ld too) and folds it into rfD, which
+// holds kNeg or another tile's maximum of the row.
+__device__ inline void rowmax_from_lds(const int *E, int ld, int slots, int rows, int32_t *rfD)
+{
+    const int t = threadIdx.x;
+    if (t < rows) {
+        const int4 *r4 = reinterpret_cast<const int4 *>(E + t * ld);
+        int e = kNeg;
+        for (int k = 0; k < slots / 4; ++k) {
+            const int4 x = r4[k];
+            e = max(e, max(max(x.x, x.y), max(x.z, x.w)));
+        }
+        if (e > kNeg) atomicMax(&rfD[t], e);
+    }
+}
+
+// this lane's exponent of x scaled by 2^c: kNeg unless both are present
+__device__ inline int scaled_exp(float x, int c)
+{
+    int ex;
+    frexpf(x, &ex);
+    return (x > 0.f) & (c > kNeg) ? ex + c : kNeg;
+}
+
 // One 64x64 output tile of D = X Y^T for node n of row b, over the K range
 // of split blockIdx.x / tiles^2.  With one split the tile is final; with
 // several it is a partial sum written to `part` and added by span_reduce.
+// The levels that take this kernel hold few products, so a tile's K loop,
+// not the chip's throughput, sets its time: each thread keeps DEPTH K
+// blocks of loads in flight (a ring in registers; DEPTH divides the split's
+// K blocks, which come in pairs, so every step of the loop is the same and
+// the loads stay in flight across its iterations) and the LDS is
+// double-buffered, one barrier per K block.  A deeper ring (4) measured
+// slower: its registers cost more than the extra loads in flight gain.
+constexpr int DEPTH = 2;
+
 __global__ __launch_bounds__(kGemmThreads) void span_gemm(StepView sv, float *__restrict__ tree,
                                                           int32_t *__restrict__ meta, int n0,
                                                           int nn, int ksplit,
@@ -80,7 +117,8 @@ __global__ __launch_bounds__(kGemmThreads) void span_gemm(StepView sv, float *__
     const int T2 = tiles * tiles;
     const int tile = blockIdx.x % T2, split = blockIdx.x / T2;
     const int tm = (tile / tiles) * kTile, tn = (tile % tiles) * kTile;
-    const int kc = Sp / ksplit, k_begin = split * kc, k_end = k_begin + kc;
+    const int kc = Sp / ksplit, k_begin = split * kc;
+    const int nb = kc / kBK;  // K blocks of this split
     const int b = blockIdx.y / nn, n = n0 + blockIdx.y % nn;
     const bool tr = stored_transposed(n);
     const int hF = tr ? 2 * n + 1 : 2 * n, hG = tr ? 2 * n : 2 * n + 1;
@@ -97,13 +135,17 @@ __global__ __launch_bounds__(kGemmThreads) void span_gemm(StepView sv, float *__
     int32_t *coD = sv.meta_ptr(meta, b, n, 1);
     int32_t *rfD = sv.meta_ptr(meta, b, n, 2);
 
-    __shared__ __align__(16) float Fs[kTile][kLdk];
-    __shared__ __align__(16) float Gs[kTile][kLdk];
+    __shared__ __align__(16) float Fs[2][kTile][kLdk];
+    __shared__ __align__(16) float Gs[2][kTile][kLdk];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int lrow = tid >> 2, lk = (tid & 3) * 8;
-    const int rfFrow = rfF[tm + lrow], rfGrow = rfG[tn + lrow];
-    const float *Frow = F + (size_t)(tm + lrow) * Sp;
-    const float *Grow = G + (size_t)(tn + lrow) * Sp;
+    // loader: thread t stages float4 (t & 7) of rows (t >> 3) and (t >> 3) + 32
+    // of both operands (the four entries share their column exponents)
+    const int lrow = tid >> 3, lk = (tid & 7) * 4;
+    const int rfF0 = rfF[tm + lrow], rfF1 = rfF[tm + lrow + 32];
+    const int rfG0 = rfG[tn + lrow], rfG1 = rfG[tn + lrow + 32];
+    const float *Frow = F + (size_t)(tm + lrow) * Sp + k_begin + lk;
+    const float *Grow = G + (size_t)(tn + lrow) * Sp + k_begin + lk;
+    const size_t r32 = (size_t)32 * Sp;
     const int wr = (wave >> 1) * 32, wc = (wave & 1) * 32;
     const int l32 = lane & 31, half = lane >> 5;
 
@@ -111,40 +153,56 @@ __global__ __launch_bounds__(kGemmThreads) void span_gemm(StepView sv, float *__
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 
-    // operands and column exponents of the next K block are loaded while
-    // the current one computes; every step issues the same loads (the last
-    // re-reads the final block), and the scheduling barriers keep the fold
-    // arithmetic, which waits for the loads, out of the MFMAs
-    float4 f0, f1, g0, g1;
-    int4 cf0, cf1, cg0, cg1;
-    auto gl = [&](int k0) {
-        load8(Frow + k0 + lk, f0, f1);
-        load8(Grow + k0 + lk, g0, g1);
-        cf0 = *reinterpret_cast<const int4 *>(coF + k0 + lk);
-        cf1 = *reinterpret_cast<const int4 *>(coF + k0 + lk + 4);
-        cg0 = *reinterpret_cast<const int4 *>(coG + k0 + lk);
-        cg1 = *reinterpret_cast<const int4 *>(coG + k0 + lk + 4);
+    struct Blk {
+        float4 f0, f1, g0, g1;
+        int4 cf, cg;
     };
-    gl(k_begin);
-    for (int k0 = k_begin; k0 < k_end; k0 += kBK) {
-        __syncthreads();
-        *reinterpret_cast<float4 *>(&Fs[lrow][lk]) = fold4(f0, cf0, rfFrow);
-        *reinterpret_cast<float4 *>(&Fs[lrow][lk + 4]) = fold4(f1, cf1, rfFrow);
-        *reinterpret_cast<float4 *>(&Gs[lrow][lk]) = fold4(g0, cg0, rfGrow);
-        *reinterpret_cast<float4 *>(&Gs[lrow][lk + 4]) = fold4(g1, cg1, rfGrow);
-        __syncthreads();
-        gl(min(k0 + kBK, k_end - kBK));
-        __builtin_amdgcn_sched_barrier(0);
+    // block bi of the split (past the last one it re-reads the last, so that
+    // every step issues the same loads)
+    auto gl = [&](Blk &x, int bi) {
+        const int k0 = min(bi, nb - 1) * kBK;
+        x.f0 = *reinterpret_cast<const float4 *>(Frow + k0);
+        x.f1 = *reinterpret_cast<const float4 *>(Frow + r32 + k0);
+        x.g0 = *reinterpret_cast<const float4 *>(Grow + k0);
+        x.g1 = *reinterpret_cast<const float4 *>(Grow + r32 + k0);
+        x.cf = *reinterpret_cast<const int4 *>(coF + k_begin + k0 + lk);
+        x.cg = *reinterpret_cast<const int4 *>(coG + k_begin + k0 + lk);
+    };
+    auto ls = [&](const Blk &x, int buf) {
+        *reinterpret_cast<float4 *>(&Fs[buf][lrow][lk]) = fold4(x.f0, x.cf, rfF0);
+        *reinterpret_cast<float4 *>(&Fs[buf][lrow + 32][lk]) = fold4(x.f1, x.cf, rfF1);
+        *reinterpret_cast<float4 *>(&Gs[buf][lrow][lk]) = fold4(x.g0, x.cg, rfG0);
+        *reinterpret_cast<float4 *>(&Gs[buf][lrow + 32][lk]) = fold4(x.g1, x.cg, rfG1);
+    };
+    auto mm = [&](int buf) {
 #pragma unroll
         for (int t = 0; t < kBK / 2; t += 4) {
-            const float4 a = *reinterpret_cast<const float4 *>(&Fs[wr + l32][half * (kBK / 2) + t]);
-            const float4 c = *reinterpret_cast<const float4 *>(&Gs[wc + l32][half * (kBK / 2) + t]);
+            const float4 a = *reinterpret_cast<const float4 *>(&Fs[buf][wr + l32][half * (kBK / 2) + t]);
+            const float4 c = *reinterpret_cast<const float4 *>(&Gs[buf][wc + l32][half * (kBK / 2) + t]);
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, c.x, acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, c.y, acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, c.z, acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, c.w, acc, 0, 0, 0);
         }
-        __builtin_amdgcn_sched_barrier(0);
+    };
+    // block bi sits in ring[bi % DEPTH] until it is stored to LDS buffer
+    // bi & 1; the slot is then refilled with block bi + DEPTH
+    Blk ring[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) gl(ring[d], d);
+    ls(ring[0], 0);
+    gl(ring[0], DEPTH);
+    __syncthreads();
+    for (int bi = 0; bi < nb; bi += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            __builtin_amdgcn_sched_barrier(0);
+            mm(d & 1);
+            __builtin_amdgcn_sched_barrier(0);
+            ls(ring[(d + 1) % DEPTH], (d + 1) & 1);
+            gl(ring[(d + 1) % DEPTH], bi + d + 1 + DEPTH);
+            __syncthreads();
+        }
     }
     if (ksplit > 1) {  // partial tile, row-major 64x64
         float *pt = part + ((size_t)(blockIdx.y * ksplit + split) * T2 + tile) * (kTile * kTile);
@@ -155,21 +213,25 @@ __global__ __launch_bounds__(kGemmThreads) void span_gemm(StepView sv, float *__
         }
         return;
     }
-    // epilogue: store, row fold normalizer, outer scales
+    // epilogue: store, row fold normalizer (row maxima through the LDS of
+    // the operand buffers, free after the loop's last barrier), outer scales
     const int j = tn + wc + l32;
     const int coDj = add_exp(roG[j], rfG[j]);
+    int *E = reinterpret_cast<int *>(&Fs[0][0][0]);  // [kTile][2 * 32 + 4]
+    constexpr int ldE = 2 * 32 + 4;
+    static_assert(kTile * ldE <= 2 * kTile * kLdk, "row-maximum exchange fits the operand buffers");
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const int i = tm + wr + (r >> 2) * 8 + half * 4 + (r & 3);
+        const int il = wr + (r >> 2) * 8 + half * 4 + (r & 3);
         const float x = acc[r];
-        __builtin_nontemporal_store(x, &D[(size_t)i * Sp + j]);
-        int e = (x > 0.f && coDj > kNeg) ? fexp(x) + coDj : kNeg;
-#pragma unroll
-        for (int o = 16; o > 0; o >>= 1) e = max(e, __shfl_xor(e, o));
-        if (l32 == 0 && e > kNeg) atomicMax(&rfD[i], e);
+        __builtin_nontemporal_store(x, &D[(size_t)(tm + il) * Sp + j]);
+        E[il * ldE + (wc >> 5) * 32 + l32] = scaled_exp(x, coDj);
     }
+    __syncthreads();
+    rowmax_from_lds(E, ldE, 64, kTile, rfD + tm);
     if (tn == 0 && tid < kTile) roD[tm + tid] = add_exp(roF[tm + tid], rfF[tm + tid]);
-    if (tm == 0 && tid < kTile) coD[tn + tid] = add_exp(roG[tn + tid], rfG[tn + tid]);
+    if (tm == 0 && tid >= kTile && tid < 2 * kTile)
+        coD[tn + tid - kTile] = add_exp(roG[tn + tid - kTile], rfG[tn + tid - kTile]);
 }
 
 // add the K-split partial tiles in split order and finish the tile as the
@@ -336,24 +398,34 @@ __global__ __launch_bounds__(kBigThreads) void span_gemm128(StepView sv, float *
         lstore(buf ^ 1);
         __syncthreads();
     }
-    // epilogue
+    // epilogue: D, then the row maxima through the LDS of the operand
+    // buffers (free after the loop's last barrier)
+    int coDj[2];
 #pragma unroll
     for (int y = 0; y < 2; ++y) {
         const int j = tn + wc + 32 * y + l32;
-        const int coDj = add_exp(roG[j], rfG[j]);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int i = tm + wr + (r >> 2) * 8 + half * 4 + (r & 3);
-            const float v = acc[y][r];
-            __builtin_nontemporal_store(v, &D[(size_t)i * Sp + j]);
-            int e = (v > 0.f && coDj > kNeg) ? fexp(v) + coDj : kNeg;
-#pragma unroll
-            for (int o = 16; o > 0; o >>= 1) e = max(e, __shfl_xor(e, o));
-            if (l32 == 0 && e > kNeg) atomicMax(&rfD[i], e);
-        }
+        coDj[y] = add_exp(roG[j], rfG[j]);
     }
+    int *E = reinterpret_cast<int *>(&Fs[0][0][0]);  // [kBig][2 * 32 + 4]
+    constexpr int ldE = 2 * 32 + 4;
+    static_assert(kBig * ldE <= 2 * kBig * kLdk2, "row-maximum exchange fits the operand buffers");
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int il = wr + (r >> 2) * 8 + half * 4 + (r & 3);
+        int e = kNeg;
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+            const float v = acc[y][r];
+            __builtin_nontemporal_store(v, &D[(size_t)(tm + il) * Sp + tn + wc + 32 * y + l32]);
+            e = max(e, scaled_exp(v, coDj[y]));
+        }
+        E[il * ldE + (wc >> 6) * 32 + l32] = e;
+    }
+    __syncthreads();
+    rowmax_from_lds(E, ldE, 64, kBig, rfD + tm);
     if (tn == 0 && tid < kBig) roD[tm + tid] = add_exp(roF[tm + tid], rfF[tm + tid]);
-    if (tm == 0 && tid < kBig) coD[tn + tid] = add_exp(roG[tn + tid], rfG[tn + tid]);
+    if (tm == 0 && tid >= kBig && tid < 2 * kBig)
+        coD[tn + tid - kBig] = add_exp(roG[tn + tid - kBig], rfG[tn + tid - kBig]);
 }
 
 // log Z[b] = ln sum_{f in F} T_root[s0][f]

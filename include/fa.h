@@ -396,7 +396,7 @@ int fa_commit(int32_t B, int32_t L, int32_t V, const float *conf, const int32_t 
  * span tree uses) live in a library-owned device array of
  * FA_SPAN_TREE_NOALLOC_MAX_BYTES (8 MiB), one copy per GPU, held until the
  * process ends.  A level is split along K only while rows x nodes x splits
- * x (Sp/64)^2 <= 512, so its partial tiles never exceed 2^21 floats: every
+ * x (Sp/64)^2 <= 256, so its partial tiles never exceed 2^20 floats: every
  * table and size fa_span_tree takes fits.  No workspace argument; the call
  * allocates nothing.
  *   arguments  as in fa_span_tree (tree, meta, logZ, row_status are the

@@ -56,6 +56,14 @@ def _json_32_dense():
     return configs.from_automaton(aut, 2, 17, "normal4_zipf", 2, 8100, "json-like 32 dense")
 
 
+def _json_split_k():
+    # Sp = 512 and one row: the top tree levels' few tiles are split along K
+    # and added by the reduce kernel
+    aut = configs._draw(lambda r: A.json_like_dfa(r, S=480, V=20000, pool=256, string_size=13000),
+                        7001, 37)
+    return configs.from_automaton(aut, 1, 37, "normal4_zipf", 0, 8200, "json-like split K")
+
+
 CASES = {
     "real-number": lambda: configs.make(1),
     "random-dfa": lambda: configs.make(2),
@@ -67,6 +75,7 @@ CASES = {
     "json-odd-V": _json_odd_v,
     "json-many-list-tokens": _json_many_list_tokens,
     "json-32-dense": _json_32_dense,
+    "json-split-K": _json_split_k,
 }
 
 

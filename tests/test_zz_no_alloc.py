@@ -22,7 +22,7 @@ def _splits_k(Sp, B, Lpad):
         big = B * nn * (Sp // 128) ** 2
         if not (Sp % 128 == 0 and big >= 256):
             small = B * nn * (Sp // 64) ** 2
-            any_split |= (Sp // 64) % 2 == 0 and small * 2 <= 512
+            any_split |= (Sp // 64) % 2 == 0 and small * 2 <= 256 and Sp // 2 >= 256
         lvl += 1
     return any_split
 
@@ -61,12 +61,13 @@ def _compare(tb, w):
 
 def test_noalloc_span_tree_matches_workspace_form():
     import constrained_decoding_diffusion_amd as fa
-    aut = configs._draw(lambda r: A.json_like_dfa(r, S=200, V=20000, pool=256, string_size=13000),
+    # Sp = 512 and one row: the top levels' few tiles split along K
+    aut = configs._draw(lambda r: A.json_like_dfa(r, S=480, V=20000, pool=256, string_size=13000),
                         7001, 37)
     tb = fa.Table.from_automaton(aut, first_level="dense")
-    assert tb.info["first_sparse"] == 0
-    w1 = configs.from_automaton(aut, 3, 37, "normal4_zipf", 0, 7100, "json-like small")
-    w2 = configs.from_automaton(aut, 2, 19, "normal4_zipf", 0, 7150, "json-like smaller")
+    assert tb.info["first_sparse"] == 0 and tb.info["Sp"] == 512
+    w1 = configs.from_automaton(aut, 1, 37, "normal4_zipf", 0, 7100, "json-like small")
+    w2 = configs.from_automaton(aut, 1, 19, "normal4_zipf", 0, 7150, "json-like smaller")
     for w in (w1, w2):
         Lpad = 1 << (w.L - 1).bit_length()
         assert _splits_k(tb.info["Sp"], w.B, Lpad)
