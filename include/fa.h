@@ -28,8 +28,9 @@
  * synchronous error nothing is launched.  Data-dependent conditions are
  * OR-ed asynchronously into row_status[b] (FA_ROW_*); the caller clears
  * row_status before a step.  Rows with a status bit set get states/tokens
- * -1, q = 0, conf = -inf and logZ = -inf.  No C++ exception crosses this
- * interface.
+ * -1, q = 0 and conf = -inf; logZ = -inf for the rows fa_build_transitions
+ * or fa_span_tree flag (a row that only fa_sample flags keeps the log Z of
+ * its tree).  No C++ exception crosses this interface.
  *
  * Layout (all device arrays row-major, C order):
  *   p      float  [B][L][V]

@@ -179,6 +179,50 @@ def test_infeasible_row_is_flagged():
     assert (g["q"][1] == 0).all() and (g["conf"][1] == -np.inf).all()
 
 
+@pytest.mark.parametrize("joint", [True, False])
+def test_underflow_is_flagged(joint):
+    """A draw whose candidates all weigh zero while log Z is finite, forced
+    from the host: after the span tree, row 1's left child of the root is
+    cleared, so the first midpoint draw of that row finds no weight.  The row
+    is flagged FA_ROW_UNDERFLOW and gets the flagged outputs; log Z keeps the
+    value the tree gave; the other rows match an untouched step bit for bit."""
+    import torch
+    import constrained_decoding_diffusion_amd as fa
+    w = _json_small()
+    tb = fa.Table.from_automaton(w.aut)
+    PT.log(f"[parity] underflow, joint {joint}")
+    ref = PT.run_gpu(w, table=tb, joint=joint)
+    dev = torch.device("cuda")
+    p = torch.from_numpy(w.p).to(dev)
+    bufs = fa.StepBuffers(tb, w.B, w.L, device=dev)
+    st = torch.cuda.current_stream(dev).cuda_stream
+    bufs.status.zero_()
+    fa.build_transitions(tb, p, bufs, st)
+    fa.span_tree(tb, bufs, st)
+    Lpad = 1 << (w.L - 1).bit_length()
+    Sp = tb.info["Sp"]
+    bufs.tree.view(w.B, 2 * Lpad, Sp, Sp)[1, 2].zero_()
+    if joint:
+        fa.sample_marginals(tb, p, bufs, w.seed, fa.FA_CONF_PROB, st, write_q=True)
+    else:
+        fa.sample(tb, p, bufs, w.seed, st)
+        fa.marginals(tb, p, bufs, fa.FA_CONF_PROB, st, write_q=True)
+    torch.cuda.synchronize()
+    status = bufs.status.cpu().numpy()
+    states, tokens = bufs.states.cpu().numpy(), bufs.tokens.cpu().numpy()[:, :w.L]
+    q, conf = bufs.q.cpu().numpy(), bufs.conf.cpu().numpy()[:, :w.L]
+    logZ = bufs.logZ.cpu().numpy()
+    PT.log(f"[parity] underflow: status {status}")
+    assert status[1] == fa.FA_ROW_UNDERFLOW
+    assert (states[1] == -1).all() and (tokens[1] == -1).all()
+    assert (q[1] == 0).all() and (conf[1] == -np.inf).all()
+    assert logZ[1] == ref["logZ"][1]
+    for b in (0, 2):
+        assert status[b] == 0
+        for k, got in (("states", states), ("tokens", tokens), ("q", q), ("conf", conf), ("logZ", logZ)):
+            np.testing.assert_array_equal(got[b], ref[k][b], err_msg=f"{k} row {b}")
+
+
 def test_bad_probability_is_flagged():
     w = configs.make(2, B=2, L=8)
     w.p[0, 3, int(w.aut.label_tok[0])] = np.nan  # a token some label holds
