@@ -8,6 +8,8 @@
 
 #include "device_common.h"
 
+#include <type_traits>
+
 namespace fa {
 
 struct EmitSrc {
@@ -38,26 +40,44 @@ __device__ inline float pair_value(const DevTable &d, int q, size_t pos, const E
     // A single running fp32 sum over a long label drops terms that fall
     // below half an ulp of the total (a systematic loss when p decays along
     // the label); blocks keep each addition between similar magnitudes.
+    // Inside a block the terms are fetched in batches of up to eight (their
+    // indices, then their values: two rounds of independent loads instead of
+    // two dependent loads per term; the batch shrinks to what is left of the
+    // block, so a short label issues no extra loads) and added in label order.
     constexpr int kListBlock = 64;
     float acc = 0.f;
     const int k0 = d.list_off[q], k1 = d.list_off[q + 1];
+    const float *src = d.use_sel ? s.psel + pos * d.nsel : s.p + pos * d.V;
+    const int32_t *ids = d.use_sel ? d.list_sel : d.list_tok;
+    float blk = 0.f;
+    auto batch = [&](auto n, int k) {
+        constexpr int N = decltype(n)::value;
+        int id[N];
+        float x[N];
+#pragma unroll
+        for (int u = 0; u < N; ++u) id[u] = ids[k + u];
+#pragma unroll
+        for (int u = 0; u < N; ++u) x[u] = src[id[u]];
+#pragma unroll
+        for (int u = 0; u < N; ++u) {
+            if (!d.use_sel) bad |= !(x[u] >= 0.f);
+            blk += d.list_cnt ? x[u] * d.list_cnt[k + u] : x[u];
+        }
+    };
     for (int kb = k0; kb < k1; kb += kListBlock) {
         const int ke = min(k1, kb + kListBlock);
-        float blk = 0.f;
-        if (d.use_sel) {
-            const float *src = s.psel + pos * d.nsel;
-            if (d.list_cnt)
-                for (int k = kb; k < ke; ++k) blk += src[d.list_sel[k]] * d.list_cnt[k];
-            else
-                for (int k = kb; k < ke; ++k) blk += src[d.list_sel[k]];
-        } else {
-            const float *src = s.p + pos * d.V;
-            for (int k = kb; k < ke; ++k) {
-                const float x = src[d.list_tok[k]];
-                bad |= !(x >= 0.f);
-                blk += d.list_cnt ? x * d.list_cnt[k] : x;
-            }
+        blk = 0.f;
+        int k = kb;
+        for (; k + 8 <= ke; k += 8) batch(std::integral_constant<int, 8>(), k);
+        if (k + 4 <= ke) {
+            batch(std::integral_constant<int, 4>(), k);
+            k += 4;
         }
+        if (k + 2 <= ke) {
+            batch(std::integral_constant<int, 2>(), k);
+            k += 2;
+        }
+        if (k < ke) batch(std::integral_constant<int, 1>(), k);
         acc += blk;
     }
     return acc;
@@ -74,13 +94,20 @@ __device__ inline float pair_value_direct(const DevTable &d, int q, size_t pos, 
         const size_t cs = (size_t)s.BLpad * kDenseMax;  // chunk stride
         float acc = 0.f;
         int c = 0;
-        // eight partials loaded together, then added in chunk order
-        for (; c + 8 <= s.n_vchunks; c += 8) {
-            float t[8];
+        // sixteen partials loaded together, then added in chunk order
+        for (; c + 16 <= s.n_vchunks; c += 16) {
+            float t[16];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) t[u] = dp[(size_t)(c + u) * cs];
+            for (int u = 0; u < 16; ++u) t[u] = dp[(size_t)(c + u) * cs];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) acc += t[u];
+            for (int u = 0; u < 16; ++u) acc += t[u];
+        }
+        for (; c + 4 <= s.n_vchunks; c += 4) {
+            float t[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) t[u] = dp[(size_t)(c + u) * cs];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc += t[u];
         }
         for (; c < s.n_vchunks; ++c) acc += dp[(size_t)c * cs];
         return acc;
