@@ -312,12 +312,15 @@ def time_chain_vs_tree(torch, fa, tb, p, seed, steps, warmup):
     """The pages' central trade on this GPU: the sampling half of a step
     (emission reduce, then the draws and log Z) through the log-depth tree
     (fa_span_tree + fa_sample) and through the serial chain
-    (fa_chain_sample: L dependent forward launches, then backward sampling).
-    µs per step each; None when the table keeps no dense leaves."""
+    (fa_chain_sample: L dependent forward launches, then backward sampling);
+    then the whole step with q written both ways (fa_span_tree +
+    fa_sample_marginals against fa_chain_sample_marginals: L more dependent
+    launches for the backward messages).  µs per step each; None when the
+    table keeps no dense leaves."""
     if tb.info["leafless"]:
         return None
     B, L, _ = p.shape
-    bufs = fa.StepBuffers(tb, B, L, want_q=False, device=p.device)
+    bufs = fa.StepBuffers(tb, B, L, want_q=True, device=p.device)
     stream = torch.cuda.current_stream(p.device).cuda_stream
 
     def tree_step(s):
@@ -331,8 +334,20 @@ def time_chain_vs_tree(torch, fa, tb, p, seed, steps, warmup):
         fa.build_transitions(tb, p, bufs, stream)
         fa.chain_sample(tb, p, bufs, s, stream)
 
+    def tree_full(s):
+        bufs.status.zero_()
+        fa.build_transitions(tb, p, bufs, stream)
+        fa.span_tree(tb, bufs, stream)
+        fa.sample_marginals(tb, p, bufs, s, fa.FA_CONF_PROB, stream, write_q=True)
+
+    def chain_full(s):
+        bufs.status.zero_()
+        fa.build_transitions(tb, p, bufs, stream)
+        fa.chain_sample_marginals(tb, p, bufs, s, fa.FA_CONF_PROB, stream, write_q=True)
+
     out = {}
-    for name, fn in (("tree", tree_step), ("chain", chain_step)):
+    for name, fn in (("tree", tree_step), ("chain", chain_step), ("tree_full_step", tree_full),
+                     ("chain_full_step", chain_full)):
         for s in range(warmup):
             fn(seed + s)
         torch.cuda.synchronize()
@@ -345,8 +360,11 @@ def time_chain_vs_tree(torch, fa, tb, p, seed, steps, warmup):
         torch.cuda.synchronize()
         out[name + "_us"] = 1000.0 * a.elapsed_time(b) / steps
     out["chain_over_tree"] = out["chain_us"] / out["tree_us"]
+    out["chain_over_tree_full_step"] = out["chain_full_step_us"] / out["tree_full_step_us"]
     out["what"] = ("emission reduce + (span tree + top-down sampler) vs emission reduce + "
-                   "(serial forward filter, L launches, + backward sampler); both draw tokens")
+                   "(serial forward filter, L launches, + backward sampler); both draw tokens. "
+                   "full_step: the same plus q and the confidence (tree: message pass; chain: "
+                   "backward messages, L launches)")
     out["row_status"] = bufs.status.cpu().numpy().tolist()
     del bufs
     return out

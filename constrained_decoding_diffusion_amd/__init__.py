@@ -10,6 +10,6 @@ from ._fa import (  # noqa: F401
     FA_PROBE_COPY, FA_PROBE_READ,
     FA_PROF_EMISSION_DENSE, FA_PROF_MARG_Q, FA_PROF_NONE, FA_PROF_TREE_LEVEL1,
     FA_ROW_BADPROB, FA_ROW_INFEASIBLE, FA_ROW_UNDERFLOW, FaError, MapBuffers, StepBuffers, Table,
-    build_transitions, chain_sample, chain_step, commit, generate, lib, map_decode, marginals, probe_bandwidth, profile_kernel, sample, sample_marginals,
+    build_transitions, chain_sample, chain_sample_marginals, chain_step, commit, generate, lib, map_decode, marginals, probe_bandwidth, profile_kernel, sample, sample_marginals,
     span_tree, span_tree_noalloc, step,
 )

@@ -26,7 +26,7 @@ EXPORTS = ["fa_compile_table", "fa_table_upload", "fa_table_destroy", "fa_table_
            "fa_table_state_map", "fa_sizes", "fa_build_transitions", "fa_span_tree", "fa_sample",
            "fa_marginals", "fa_sample_marginals", "fa_commit", "fa_strerror", "fa_profile_kernel",
            "fa_span_tree_noalloc", "fa_probe_bandwidth", "fa_map_sizes", "fa_map_decode",
-           "fa_chain_sample"]
+           "fa_chain_sample", "fa_chain_sample_marginals"]
 FA_SPAN_TREE_NOALLOC_MAX_BYTES = 8 << 20
 
 
@@ -67,6 +67,7 @@ def lib():
     L.fa_probe_bandwidth.argtypes = [I32, P, P, SZ, I32, P]
     L.fa_map_sizes.argtypes = [P, I32, I32, P, P]
     L.fa_chain_sample.argtypes = [P, P, I32, I32, P, U64, P, P, P, P, SZ, P, P]
+    L.fa_chain_sample_marginals.argtypes = [P, P, I32, I32, P, U64, I32, P, P, P, P, P, P, SZ, P, P]
     L.fa_map_decode.argtypes = [P, P, I32, I32, P, P, SZ, P, P, P, P, P]
     L.fa_strerror.argtypes = [C.c_int]
     L.fa_strerror.restype = C.c_char_p
@@ -260,19 +261,34 @@ def chain_sample(table: Table, p, bufs: StepBuffers, seed: int, stream):
         C.c_void_p(stream)))
 
 
-def chain_step(table: Table, p, seed: int, bufs: StepBuffers = None):
+def chain_sample_marginals(table: Table, p, bufs: StepBuffers, seed: int, conf_mode: int, stream,
+                           write_q=True):
+    """fa_chain_sample_marginals: the chain sampler, backward messages and
+    the marginals from the two message chains (after build_transitions)."""
+    _check("fa_chain_sample_marginals", lib().fa_chain_sample_marginals(
+        table.handle, _ptr(p), bufs.B, bufs.L, _ptr(bufs.tree), C.c_uint64(seed), conf_mode,
+        _ptr(bufs.logZ), _ptr(bufs.states), _ptr(bufs.tokens), _ptr(bufs.q if write_q else None),
+        _ptr(bufs.conf), _ptr(bufs.ws), bufs.ws.numel(), _ptr(bufs.status), C.c_void_p(stream)))
+
+
+def chain_step(table: Table, p, seed: int, bufs: StepBuffers = None, marginals=False,
+               conf_mode: int = FA_CONF_PROB, write_q=True):
     """The emission reduce and the chain sampler on torch's current stream
-    (the serial baseline of step()'s sampling half)."""
+    (the serial baseline of step()'s sampling half); with marginals, the
+    whole serial forward-backward step (q and conf as well)."""
     import torch
     B, L, V = p.shape
     if table.buf is None:
         table.upload(p.device)
     if bufs is None:
-        bufs = StepBuffers(table, B, L, want_q=False, device=p.device)
+        bufs = StepBuffers(table, B, L, want_q=marginals and write_q, device=p.device)
     stream = torch.cuda.current_stream(p.device).cuda_stream
     bufs.status.zero_()
     build_transitions(table, p, bufs, stream)
-    chain_sample(table, p, bufs, seed, stream)
+    if marginals:
+        chain_sample_marginals(table, p, bufs, seed, conf_mode, stream, write_q=write_q)
+    else:
+        chain_sample(table, p, bufs, seed, stream)
     return bufs
 
 

@@ -293,6 +293,38 @@ extern "C" int fa_chain_sample(const fa_table *t, const float *p, int32_t B, int
     }));
 }
 
+extern "C" int fa_chain_sample_marginals(const fa_table *t, const float *p, int32_t B, int32_t L,
+                                         const float *tree, uint64_t seed, int32_t conf_mode,
+                                         double *logZ, int32_t *states, int32_t *tokens, float *q,
+                                         float *conf, void *ws, size_t ws_bytes,
+                                         int32_t *row_status, fa_stream_t stream)
+{
+    int rc = ready(t);
+    if (rc) return rc;
+    StepChunks ck;
+    if (int grc = plan_chunks(t->h, B, L, false, &ck)) return grc;
+    if (!conf_mode_ok(conf_mode)) return FA_EINVAL;
+    if (t->h.leafless && L > 1) return FA_EINVAL;
+    if (B == 0) return FA_OK;
+    if (!logZ || !states || !row_status || !ws || ws_bytes < ws_need(ck)) return FA_EINVAL;
+    if (L > 0 && (!p || !tree || !tokens || !conf)) return FA_EINVAL;
+    const DevTable d = t->h.device_view();
+    return hip_rc(each_chunk(t->h, B, L, ck, (uint8_t *)ws, [&](int32_t b0, const Geometry &g,
+                                                                 uint8_t *wsc) {
+        const float *pc = rows(p, (size_t)L * d.V, b0);
+        int32_t *tc = rows(tokens, (size_t)L, b0);
+        float *cc = rows(conf, (size_t)L, b0);
+        int32_t *sc = rows(row_status, 1, b0);
+        int r = launch_chain_sample_marginals(
+            d, g, pc, rows(tree, 2 * (size_t)g.Lpad * g.mat, b0), seed, base_mode(conf_mode),
+            rows(logZ, 1, b0), rows(states, (size_t)L + 1, b0), tc, rows(q, (size_t)L * d.V, b0), cc,
+            wsc, ws_layout(t->h, g), sc, stream);
+        if (!r && L > 0 && conf_mode == FA_CONF_UNCONSTRAINED)
+            r = launch_conf_unconstrained(d, g, pc, tc, sc, cc, stream);
+        return r;
+    }));
+}
+
 extern "C" int fa_map_sizes(const fa_table *t, int32_t B, int32_t L, size_t *tree_bytes,
                             size_t *ws_bytes)
 {

@@ -262,6 +262,13 @@ int tree_ksplit(const Geometry &g, int level);
 int launch_chain_sample(const DevTable &d, const Geometry &g, const float *p, const float *tree,
                         uint64_t seed, double *logZ, int32_t *states, int32_t *tokens,
                         uint8_t *ws, const WsLayout &w, int32_t *status, void *stream);
+// the chain sampler, then backward messages and the marginals from the two
+// message chains (conf_mode FA_CONF_PROB or FA_CONF_NEGENT)
+int launch_chain_sample_marginals(const DevTable &d, const Geometry &g, const float *p,
+                                  const float *tree, uint64_t seed, int32_t conf_mode,
+                                  double *logZ, int32_t *states, int32_t *tokens, float *q,
+                                  float *conf, uint8_t *ws, const WsLayout &w, int32_t *status,
+                                  void *stream);
 
 // MAP decoding (map.hip): workspace regions and the launcher
 struct MapWs {
@@ -316,6 +323,13 @@ bool marg_joint_ok(const DevTable &d, const Geometry &g, const float *p, const f
 int launch_marg_out(const DevTable &d, const Geometry &g, const float *p, const double *logZ,
                     const int32_t *tokens, int32_t conf_mode, float *q, float *conf, uint8_t *ws,
                     const WsLayout &w, int mode, int32_t *status, void *stream, int32_t *states);
+// The range weights per cut and the plain q writer (mode 0) from alpha/beta
+// already in ws at w.va/w.ea and w.vb/w.eb (each vector with its own
+// power-of-two exponent), as the chain's messages leave them.
+int launch_marg_from_messages(const DevTable &d, const Geometry &g, const float *p,
+                              const double *logZ, const int32_t *tokens, int32_t conf_mode,
+                              float *q, float *conf, uint8_t *ws, const WsLayout &w,
+                              int32_t *status, void *stream);
 
 // The remasking step (commit.hip).
 constexpr int kCommitMaxL = 8192;  // positions per row the selection holds in LDS

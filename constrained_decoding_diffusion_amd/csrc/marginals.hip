@@ -1233,6 +1233,42 @@ bool marg_joint_ok(const DevTable &d, const Geometry &g, const float *p, const f
            (q != nullptr || conf_mode == FA_CONF_NEGENT) && w.tcs_nch <= kTokChunksMax;
 }
 
+int launch_marg_from_messages(const DevTable &d, const Geometry &g, const float *p,
+                              const double *logZ, const int32_t *tokens, int32_t conf_mode,
+                              float *q, float *conf, uint8_t *ws, const WsLayout &w,
+                              int32_t *status, void *stream)
+{
+    hipStream_t st = (hipStream_t)stream;
+    StepView sv = step_view(g);
+    const float *va = (const float *)(ws + w.va), *vb = (const float *)(ws + w.vb);
+    hipError_t e;
+    if (d.ncut) {
+        float *rcut = (float *)(ws + w.rcut);
+        const int npos = g.B * g.L;
+        const size_t ab = (size_t)2 * g.Sp * sizeof(float);
+        const int ab_lds = ab <= 48 * 1024;
+        marg_rcut<<<npos, kRcutThreads, ab_lds ? ab : 0, st>>>(d, sv, va, vb, rcut, ab_lds);
+        e = hipGetLastError();
+        if (e != hipSuccess) return (int)e;
+    }
+    // the streaming writer's pair weights: on tables whose tree path forms
+    // them in the message pass's leaf level, the plain writer does not
+    if (q_streamed(d, p, q, w) && leaf_writes_pw(d, g, w)) {
+        const size_t plds = w.pw_nl ? ((size_t)std::min(d.n_tm, kPwChunk) + w.pw_nl) * 4 : 0;
+        if (plds > 48 * 1024) {
+            e = hipFuncSetAttribute(reinterpret_cast<const void *>(&marg_pairw),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)plds);
+            if (e != hipSuccess) return (int)e;
+        }
+        marg_pairw<<<g.B * g.L, kPwThreads, plds, st>>>(d, sv, va, vb, w.pw_nl, w.pw_ld,
+                                                         (float *)(ws + w.pw));
+        e = hipGetLastError();
+        if (e != hipSuccess) return (int)e;
+    }
+    return launch_marg_out(d, g, p, logZ, tokens, conf_mode, q, conf, ws, w, 0, status, stream,
+                           nullptr);
+}
+
 int launch_marg_out(const DevTable &d, const Geometry &g, const float *p, const double *logZ,
                     const int32_t *tokens, int32_t conf_mode, float *q, float *conf, uint8_t *ws,
                     const WsLayout &w, int mode, int32_t *status, void *stream, int32_t *states)

@@ -323,6 +323,30 @@ int fa_chain_sample(const fa_table *t, const float *p, int32_t B, int32_t L, con
                     size_t ws_bytes, int32_t *row_status, fa_stream_t stream);
 
 /*
+ * fa_chain_sample_marginals - the chain's full serial forward-backward
+ * pass: fa_chain_sample, then backward messages over the positions
+ * (L dependent steps, one launch each: b_L = 1_F, b_i = M_i (b_{i+1}
+ * 2^-e'_{i+1}) with e'_j the exponent of max b_j), and the marginals and
+ * confidence of fa_marginals from alpha_i = a_i 2^(e_0 + .. + e_{i-1}) and
+ * beta_i = b_i 2^(e'_{i+1} + .. + e'_L) instead of the span tree's messages.
+ * The same q and conf as the tree path up to rounding (the messages are
+ * products of up to L fp32 steps here, of log2 L levels there); the states
+ * and tokens of fa_chain_sample.
+ * Cite: paperfeed summary "The scan trick: log-depth exact sampling" (the
+ * serial forward-backward pass the tree replaces); papernotes 关键设计 3 (the
+ * constrained marginals as the remasking confidence).
+ *   arguments  as in fa_chain_sample, plus conf_mode, q (or NULL) and conf
+ *              as in fa_marginals; ws (>= fa_sizes) the workspace of this
+ *              step's fa_build_transitions
+ * Errors: FA_EINVAL (also for a table that keeps no dense leaves, L > 1),
+ * FA_ETOOBIG, FA_ESTATE, FA_EHIP.
+ */
+int fa_chain_sample_marginals(const fa_table *t, const float *p, int32_t B, int32_t L,
+                              const float *tree, uint64_t seed, int32_t conf_mode, double *logZ,
+                              int32_t *states, int32_t *tokens, float *q, float *conf, void *ws,
+                              size_t ws_bytes, int32_t *row_status, fa_stream_t stream);
+
+/*
  * fa_map_sizes - bytes of the fp64 tree and of the workspace fa_map_decode
  * needs for batch B and length L.  Errors: FA_EINVAL (also for a table with
  * range labels, which MAP decoding does not take), FA_ETOOBIG.
