@@ -247,13 +247,14 @@ def stage_fracs(work, stage_us, separate):
     return st
 
 
-def time_workload(torch, fa, configs, k, steps, warmup, dev, device_p=False):
+def time_workload(torch, fa, configs, k, steps, warmup, dev, device_p=False, live=False,
+                  chain=True):
     """µs per step of preset k (joint call form): `steps` steps bracketed by
     two events, then as many with events between the calls for the stage
-    split."""
+    split.  live: the table compiled with FA_LIVE_STATES."""
     t_prep = time.perf_counter()
     w = configs.make(k, device=dev if device_p else None)
-    tb = fa.Table.from_automaton(w.aut)
+    tb = fa.Table.from_automaton(w.aut, live_states=live)
     tb.upload(dev)
     p = w.p if device_p else torch.from_numpy(w.p).to(dev)
     bufs = fa.StepBuffers(tb, w.B, w.L, want_q=True, device=dev)
@@ -291,13 +292,13 @@ def time_workload(torch, fa, configs, k, steps, warmup, dev, device_p=False):
     work = algorithmic_work(tb, w.B, w.L)
     status = bufs.status.cpu().numpy().tolist()
     del bufs
-    chain = time_chain_vs_tree(torch, fa, tb, p, w.seed, min(steps, 5), 1)
+    chain = time_chain_vs_tree(torch, fa, tb, p, w.seed, min(steps, 5), 1) if chain else None
     out = dict(workload=w.describe(), B=w.B, L=w.L, S=tb.info["S"], Sp=tb.info["Sp"], V=w.aut.V,
                steps=steps, warmup=warmup, us_per_step=us, steps_per_s=1e6 / us,
                sequence_steps_per_s=w.B * 1e6 / us,
                first_level="sparse" if tb.info["first_sparse"] else "dense",
                second_level="sparse" if tb.info["second_sparse"] else "dense",
-               leafless=bool(tb.info["leafless"]),
+               leafless=bool(tb.info["leafless"]), live_states=bool(tb.info["live_states"]),
                p_drawn="on the device (same distribution, torch generator)" if device_p
                else "on the host (numpy PCG64)",
                stages=stage_fracs(work, stage_us, False), row_status=status,
@@ -812,6 +813,11 @@ def main():
             n = args.steps if k <= 3 else 5
             others[f"preset{k}"] = time_workload(torch, fa, configs, k, n, 3 if k > 3 else args.warmup,
                                                  dev, device_p=(k == 4))
+            if k == 4:
+                # its committed positions leave about a third of the states
+                # live per boundary: the same preset with FA_LIVE_STATES
+                others["preset4_live_states"] = time_workload(torch, fa, configs, k, n, 3, dev,
+                                                              device_p=True, live=True, chain=False)
         out["configs"] = others
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)

@@ -18,6 +18,7 @@ FA_OK, FA_EINVAL, FA_ENOTDET, FA_ETOOBIG, FA_EHIP, FA_ESTATE = range(6)
 FA_ROW_INFEASIBLE, FA_ROW_UNDERFLOW, FA_ROW_BADPROB = 1, 2, 4
 FA_DFA, FA_NFA, FA_LABEL_RANGES, FA_NO_TRIM = 1, 2, 4, 8
 FA_FIRST_LEVEL_SPARSE, FA_FIRST_LEVEL_DENSE, FA_SECOND_LEVEL_SPARSE = 16, 32, 64
+FA_LIVE_STATES = 128
 FA_CONF_PROB, FA_CONF_NEGENT, FA_CONF_UNCONSTRAINED = 0, 1, 2
 FA_PROF_NONE, FA_PROF_EMISSION_DENSE, FA_PROF_TREE_LEVEL1, FA_PROF_MARG_Q = range(4)
 FA_PROBE_READ, FA_PROBE_COPY = 0, 1
@@ -47,6 +48,9 @@ def lib():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
                           "(the sampler has no CPU path)")
+    # torch first: the HIP runtime torch ships is then the one libfa binds
+    # to, so device pointers and streams from torch are valid in the library
+    import torch  # noqa: F401
     L = C.CDLL(LIB_PATH)
     P, I32, I64, U32, U64, SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_uint32, C.c_uint64, C.c_size_t
     L.fa_compile_table.argtypes = [I32, I32, I32, P, I32, I64, P, P, P, P, U32, P, P]
@@ -90,7 +94,7 @@ def _np_ptr(a: np.ndarray):
 INFO_KEYS = ["S", "Sp", "start", "n_accept", "pairs", "list_pairs", "dense_pairs", "range_pairs",
              "list_entries", "segments", "cuts", "sel_tokens", "use_sel", "V", "S_orig",
              "first_sparse", "first_work", "second_sparse", "second_work", "pairs2", "leafless",
-             "leaf_msg_pairs"]
+             "leaf_msg_pairs", "live_states"]
 
 
 class Table:
@@ -119,12 +123,16 @@ class Table:
         self.orig = orig
 
     @classmethod
-    def from_automaton(cls, aut, flags=None, first_level="auto"):
+    def from_automaton(cls, aut, flags=None, first_level="auto", live_states=False):
         """first_level: "auto" (the library's choice), "sparse" (first span
         level from the pair values), "sparse2" (also the second level, from
-        the two-step pattern) or "dense" (dense matrix products)."""
+        the two-step pattern) or "dense" (dense matrix products).
+        live_states: FA_LIVE_STATES (span products over the states live at
+        their midpoint under each step's p)."""
         if flags is None:
             flags = (FA_DFA if aut.dfa else FA_NFA) | (FA_LABEL_RANGES if aut.ranges else 0)
+        if live_states:
+            flags |= FA_LIVE_STATES
         flags |= {"auto": 0, "sparse": FA_FIRST_LEVEL_SPARSE,
                   "dense": FA_FIRST_LEVEL_DENSE,
                   "sparse2": FA_FIRST_LEVEL_SPARSE | FA_SECOND_LEVEL_SPARSE}[first_level]

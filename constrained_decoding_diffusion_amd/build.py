@@ -15,7 +15,7 @@ ARCH = "gfx950"
 
 SOURCES = ["table.cpp", "api.cpp", "emission.hip", "tree.hip", "sample.hip", "marginals.hip",
            "commit.hip", "noalloc.hip", "probe.hip", "map.hip",
-           "chain.hip"]
+           "chain.hip", "live.hip"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", f"-I{CSRC}"]
 # packed fp32 instructions are kept out of every gfx950 code object

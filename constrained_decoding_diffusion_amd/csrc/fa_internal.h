@@ -118,6 +118,7 @@ struct DevTable {
     int32_t first_sparse;        // 1: the first span level is formed from the pair values
     int32_t leafless;            // 1: no dense leaves; every leaf reader takes the pair values
     int32_t second_sparse;       // 1: so is the second, from the two-step pattern
+    int32_t live_states;         // 1: dense products contract over the live states (live.hip)
     int32_t np2;                 // pairs of the two-step pattern
     int32_t nwin;                // win_cols-column windows of a row (0: one window)
     int32_t win_cols;            // kSpWin for Sp > kSpWin, kSpWin / 2 for Sp > kSpWin / 2
@@ -170,6 +171,7 @@ struct HostTable {
     std::vector<int32_t> col_a, p2_col_a;   // column walks' targets: a of each column-order entry
     bool second_sparse = false;
     int64_t second_work = 0;    // multiply-adds per second-level product
+    bool live_states = false;   // FA_LIVE_STATES: products over the live states of their midpoint
     // entry offsets of each state's row walk (_n) and column walk (_t) at
     // every window boundary, [S][nwin + 1]; only when Sp > kSpWin / 2
     std::vector<int32_t> w1_n, w1_t, w2_n, w2_t;
@@ -229,6 +231,7 @@ struct WsLayout {
     size_t zc = 0;                             // sampler: compact boundary states
     size_t tpair = 0, tdbit = 0;               // sampler: per position the drawn pair, its dense bit
     size_t kpart = 0;                          // span tree: split-K partial tiles
+    size_t lbits = 0, live = 0, nlive = 0;     // span tree: live-state bitsets, lists, counts
     size_t va = 0, ea = 0, vb = 0, eb = 0;     // marginals: messages
     size_t rcut = 0;                           // marginals: range weights per cut
     size_t ndval = 0;                          // emission: values of the indirect pairs (persist)
@@ -248,6 +251,9 @@ int launch_build_transitions(const DevTable &d, const Geometry &g, const float *
                              void *stream);
 int launch_span_tree(const DevTable &d, const Geometry &g, float *tree, int32_t *meta,
                      uint8_t *ws, const WsLayout &w, double *logZ, int32_t *status, void *stream);
+// the live states of every boundary (live.hip): lists at w.live, counts at w.nlive
+int launch_live_states(const DevTable &d, const Geometry &g, const float *tree, uint8_t *ws,
+                       const WsLayout &w, void *stream);
 
 // Measurement hook: records the caller's start (begin) or stop event on
 // `stream` when `which` is the kernel selected by fa_profile_kernel.

@@ -66,7 +66,10 @@ extern "C" int fa_span_tree_noalloc(const fa_table *t, int32_t B, int32_t L, flo
     // that bound should the rule change.  Row chunks run in turn on the
     // stream and reuse the array.
     uint8_t *ptr = nullptr;
-    const DevTable d = t->h.device_view();
+    // the live-state lists need workspace: this form runs the products over
+    // every state (the same results)
+    DevTable d = t->h.device_view();
+    d.live_states = 0;
     for (int32_t k = 0; k < ck.count; ++k) {
         const int32_t b0 = k * ck.rows;
         Geometry g;

@@ -146,6 +146,7 @@ DevTable HostTable::device_view() const
     nxt(d.p2_colpos); nxt(d.w1_n); nxt(d.w1_t); nxt(d.w2_n); nxt(d.w2_t);
     nxt(d.col_a); nxt(d.p2_col_a);
     d.second_sparse = second_sparse ? 1 : 0;
+    d.live_states = live_states ? 1 : 0;
     d.np2 = (int32_t)p2_a.size();
     d.nwin = nwin;
     d.win_cols = win_cols;
@@ -280,6 +281,10 @@ WsLayout ws_layout(const HostTable &t, const Geometry &g)
         if (s > 1) kp = std::max(kp, (size_t)g.B * (g.Lpad >> level) * s * g.mat);
     }
     w.kpart = o; o = al(o + kp * sizeof(float));
+    const size_t nbd = t.live_states ? (size_t)g.B * (g.Lpad + 1) : 0;  // boundaries
+    w.lbits = o; o = al(o + nbd * 2 * ((g.Sp + 31) / 32) * sizeof(uint32_t));
+    w.live = o; o = al(o + nbd * g.Sp * sizeof(int32_t));
+    w.nlive = o; o = al(o + nbd * sizeof(int32_t));
     size_t a2 = o;
     o = a0;  // marginals region
     size_t nv = (size_t)g.B * (g.Lpad + 1);
@@ -385,7 +390,7 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
     if ((n_accept > 0 && !accept) || (E > 0 && (!src || !dst || !label_off))) return FA_EINVAL;
     if ((flags & FA_DFA) && (flags & FA_NFA)) return FA_EINVAL;
     if (flags & ~uint32_t(FA_DFA | FA_NFA | FA_LABEL_RANGES | FA_NO_TRIM | FA_FIRST_LEVEL_SPARSE |
-                          FA_FIRST_LEVEL_DENSE | FA_SECOND_LEVEL_SPARSE))
+                          FA_FIRST_LEVEL_DENSE | FA_SECOND_LEVEL_SPARSE | FA_LIVE_STATES))
         return FA_EINVAL;
     if ((flags & FA_FIRST_LEVEL_SPARSE) && (flags & FA_FIRST_LEVEL_DENSE)) return FA_EINVAL;
     if (E > std::numeric_limits<int32_t>::max()) return FA_ETOOBIG;
@@ -782,6 +787,7 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
     int64_t w1 = 0;
     for (int32_t q = 0; q < np; ++q) w1 += t.row_ptr[t.pair_b[q] + 1] - t.row_ptr[t.pair_b[q]];
     t.first_work = w1;
+    t.live_states = (flags & FA_LIVE_STATES) != 0;
     if (flags & FA_FIRST_LEVEL_SPARSE) {
         if (t.Sp + t.S > kSparseMaxSpS || np >= kSparseMaxPairs) return FA_ETOOBIG;
         t.first_sparse = true;
@@ -882,13 +888,14 @@ extern "C" int fa_table_info(const fa_table *t, int64_t *info, int32_t n)
     const HostTable &h = t->h;
     int32_t nl = 0, nd = 0, nr = 0;
     for (int32_t c : h.pair_cls) (c == kList ? nl : c == kDense ? nd : nr)++;
-    constexpr int32_t kInfo = 22;
+    constexpr int32_t kInfo = 23;
     int64_t v[kInfo] = {h.S, h.Sp, h.start, (int64_t)h.acc.size(), h.npairs(), nl, nd, nr,
                         (int64_t)h.list_tok.size(), h.nseg(), h.ncut(), h.nsel(),
                         h.use_sel ? 1 : 0, h.V, h.S_orig, h.first_sparse ? 1 : 0, h.first_work,
                         h.second_sparse ? 1 : 0, h.second_work, (int64_t)h.p2_a.size(),
                         h.leafless ? 1 : 0,
-                        h.npairs() > 0 && leaf_level_from_pairs(h.npairs(), h.S, h.Sp) ? 1 : 0};
+                        h.npairs() > 0 && leaf_level_from_pairs(h.npairs(), h.S, h.Sp) ? 1 : 0,
+                        h.live_states ? 1 : 0};
     for (int32_t k = 0; k < n && k < kInfo; ++k) info[k] = v[k];
     return FA_OK;
 }

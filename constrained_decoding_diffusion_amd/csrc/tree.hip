@@ -491,12 +491,20 @@ constexpr int kHugeThreads = 512;
 struct HugeSrc {
     const float *F, *G;
     const int32_t *coF, *coG, *rfF, *rfG;
+    const int32_t *kidx;  // LIVE: the states live at the midpoint, padded with -1
     int tm, tn;
+    int nk;               // K steps of 32
 };
 
+// LIVE (tables compiled with FA_LIVE_STATES): the contraction runs over the
+// states live at the product's midpoint (lists and counts from
+// launch_live_states), each K step gathering 32 listed columns of both
+// operands; list entries of -1 load zero.
+template <bool LIVE>
 __global__ __launch_bounds__(kHugeThreads) void span_gemm256(StepView sv, float *__restrict__ tree,
                                                              int32_t *__restrict__ meta, int n0,
-                                                             int nn)
+                                                             int nn, const int32_t *__restrict__ live,
+                                                             const int32_t *__restrict__ nlive)
 {
     const int Sp = sv.Sp;
     const int tiles = Sp / kHuge;
@@ -527,6 +535,17 @@ __global__ __launch_bounds__(kHugeThreads) void span_gemm256(StepView sv, float 
         s.rfG = sv.meta_ptr((const int32_t *)meta, b, hG, 2);
         s.tm = tm;
         s.tn = tn;
+        s.kidx = nullptr;
+        s.nk = Sp / kBK2;
+        if constexpr (LIVE) {
+            // node n of level k: the level's nodes start at 2^(K-k) = Lpad / span
+            const int first = 1 << (31 - __clz(n));
+            const int span = sv.Lpad / first;
+            const int m = (n - first) * span + span / 2;  // midpoint boundary
+            const size_t bm = (size_t)b * (sv.Lpad + 1) + m;
+            s.kidx = live + bm * Sp;
+            s.nk = max(2, (nlive[bm] + 63) / 64 * 2);
+        }
         return s;
     };
 
@@ -539,7 +558,6 @@ __global__ __launch_bounds__(kHugeThreads) void span_gemm256(StepView sv, float 
     const size_t q_rows = (size_t)64 * Sp;
     const int wr = (wave >> 1) * 64, wc = (wave & 1) * 128;
     const int l32 = lane & 31, half = lane >> 5;
-    const int nk = Sp / kBK2;
 
     struct Stage {
         float4 f[4], g[4];
@@ -549,15 +567,39 @@ __global__ __launch_bounds__(kHugeThreads) void span_gemm256(StepView sv, float 
     // the rows' exponents come with block 0 of a tile and stay for its other blocks
     auto gload = [&](Stage &st, const HugeSrc &s, int ks, bool rows) {
         const int k0 = ks * kBK2;
-        const float *Fr = s.F + (size_t)(s.tm + lrow) * Sp + lk + k0;
-        const float *Gr = s.G + (size_t)(s.tn + lrow) * Sp + lk + k0;
+        if constexpr (LIVE) {
+            const int4 kk = *reinterpret_cast<const int4 *>(s.kidx + k0 + lk);
+            const int k[4] = {max(kk.x, 0), max(kk.y, 0), max(kk.z, 0), max(kk.w, 0)};
+            const bool ok[4] = {kk.x >= 0, kk.y >= 0, kk.z >= 0, kk.w >= 0};
+            const float *Fr = s.F + (size_t)(s.tm + lrow) * Sp;
+            const float *Gr = s.G + (size_t)(s.tn + lrow) * Sp;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            st.f[q] = *reinterpret_cast<const float4 *>(Fr + q * q_rows);
-            st.g[q] = *reinterpret_cast<const float4 *>(Gr + q * q_rows);
+            for (int q = 0; q < 4; ++q) {
+                const float *fr = Fr + q * q_rows, *gr = Gr + q * q_rows;
+                float fv[4], gv[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    fv[u] = fr[k[u]];
+                    gv[u] = gr[k[u]];
+                }
+                st.f[q] = make_float4(ok[0] ? fv[0] : 0.f, ok[1] ? fv[1] : 0.f, ok[2] ? fv[2] : 0.f,
+                                      ok[3] ? fv[3] : 0.f);
+                st.g[q] = make_float4(ok[0] ? gv[0] : 0.f, ok[1] ? gv[1] : 0.f, ok[2] ? gv[2] : 0.f,
+                                      ok[3] ? gv[3] : 0.f);
+            }
+            st.cf = make_int4(s.coF[k[0]], s.coF[k[1]], s.coF[k[2]], s.coF[k[3]]);
+            st.cg = make_int4(s.coG[k[0]], s.coG[k[1]], s.coG[k[2]], s.coG[k[3]]);
+        } else {
+            const float *Fr = s.F + (size_t)(s.tm + lrow) * Sp + lk + k0;
+            const float *Gr = s.G + (size_t)(s.tn + lrow) * Sp + lk + k0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                st.f[q] = *reinterpret_cast<const float4 *>(Fr + q * q_rows);
+                st.g[q] = *reinterpret_cast<const float4 *>(Gr + q * q_rows);
+            }
+            st.cf = *reinterpret_cast<const int4 *>(s.coF + k0 + lk);
+            st.cg = *reinterpret_cast<const int4 *>(s.coG + k0 + lk);
         }
-        st.cf = *reinterpret_cast<const int4 *>(s.coF + k0 + lk);
-        st.cg = *reinterpret_cast<const int4 *>(s.coG + k0 + lk);
         if (rows) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -616,17 +658,18 @@ __global__ __launch_bounds__(kHugeThreads) void span_gemm256(StepView sv, float 
         // step ks: issue the loads of K block ks+1 (of the next tile after
         // the last block), compute buffer ks & 1 (128 MFMAs per wave cover
         // the load latency), store that block into the other buffer.
-        // nk = Sp / 32 is even.  The scheduling barriers keep the compiler
-        // from moving the fold arithmetic of the stores (which waits for
-        // the loads) into the MFMAs.
-        for (int ks = 0; ks < nk; ks += 2) {
+        // A tile's K steps (Sp / 32, or its live list's length / 32) are
+        // even.  The scheduling barriers keep the compiler from moving the
+        // fold arithmetic of the stores (which waits for the loads) into
+        // the MFMAs.
+        for (int ks = 0; ks < cur.nk; ks += 2) {
             gload(st, cur, ks + 1, false);
             __builtin_amdgcn_sched_barrier(0);
             mfmas(0);
             __builtin_amdgcn_sched_barrier(0);
             lstore(st, 1);
             __syncthreads();
-            const bool last = ks + 2 == nk;
+            const bool last = ks + 2 == cur.nk;
             gload(st, last ? nxt : cur, last ? 0 : ks + 2, last);
             __builtin_amdgcn_sched_barrier(0);
             mfmas(1);
@@ -1138,7 +1181,8 @@ int device_cus()
 
 // one tree level as dense products over nodes n0 .. n0 + nn - 1 of every row
 int launch_dense_level(const Geometry &g, StepView sv, int k, int n0, int nn, float *tree,
-                       int32_t *meta, uint8_t *ws, const WsLayout &w, hipStream_t st)
+                       int32_t *meta, uint8_t *ws, const WsLayout &w, hipStream_t st,
+                       const int32_t *live, const int32_t *nlive)
 {
     if (nn <= 0) return 0;
     const int tiles = g.Sp / kTile;
@@ -1149,7 +1193,10 @@ int launch_dense_level(const Geometry &g, StepView sv, int k, int n0, int nn, fl
     const long long huge_wgs = (long long)g.B * nn * huge_tiles * huge_tiles;
     if (ks == 1 && g.Sp % kHuge == 0 && huge_wgs >= 256) {
         const unsigned grid = (unsigned)std::min<long long>(huge_wgs, device_cus());
-        span_gemm256<<<grid, kHugeThreads, 0, st>>>(sv, tree, meta, n0, nn);
+        if (live)
+            span_gemm256<true><<<grid, kHugeThreads, 0, st>>>(sv, tree, meta, n0, nn, live, nlive);
+        else
+            span_gemm256<false><<<grid, kHugeThreads, 0, st>>>(sv, tree, meta, n0, nn, nullptr, nullptr);
     } else if (ks == 1 && g.Sp % kBig == 0 && big_wgs >= 256) {
         span_gemm128<<<(unsigned)big_wgs, kBigThreads, 0, st>>>(sv, tree, meta, n0, nn);
     } else {
@@ -1191,6 +1238,15 @@ int launch_span_tree(const DevTable &d, const Geometry &g, float *tree, int32_t 
     // second level from the two-step pattern: its products whose four
     // leaves are all inside the sequence (the rest, if any, dense)
     const int nsp2 = d.second_sparse && d.np2 > 0 && sparse1 && g.K >= 2 ? g.L / 4 : 0;
+    // FA_LIVE_STATES: the states live at every boundary, for the products
+    // on 256x256 tiles
+    const int32_t *live = nullptr, *nlive = nullptr;
+    if (d.live_states) {
+        const int e = launch_live_states(d, g, tree, ws, w, stream);
+        if (e) return e;
+        live = (const int32_t *)(ws + w.live);
+        nlive = (const int32_t *)(ws + w.nlive);
+    }
     for (int k = 1; k <= g.K; ++k) {
         const int n0 = g.Lpad >> k, nn = n0;
         if (k == 1) {
@@ -1225,9 +1281,11 @@ int launch_span_tree(const DevTable &d, const Geometry &g, float *tree, int32_t 
             lv.n0 = n0;
             lv.nsp = nsp2;
             e = launch_sparse(d, g, sv, lv, tree, meta, st);
-            if (!e) e = launch_dense_level(g, sv, k, n0 + nsp2, nn - nsp2, tree, meta, ws, w, st);
+            if (!e)
+                e = launch_dense_level(g, sv, k, n0 + nsp2, nn - nsp2, tree, meta, ws, w, st, live,
+                                       nlive);
         } else {
-            e = launch_dense_level(g, sv, k, n0, nn, tree, meta, ws, w, st);
+            e = launch_dense_level(g, sv, k, n0, nn, tree, meta, ws, w, st, live, nlive);
         }
         if (e) return e;
         if (k == 1) {

@@ -83,8 +83,9 @@ enum {
     FA_NO_TRIM = 8,      /* keep states unreachable from s0 or unable to reach F */
     FA_FIRST_LEVEL_SPARSE = 16, /* first span level from the pair values (row combination) */
     FA_FIRST_LEVEL_DENSE = 32,  /* first span level as dense matrix products */
-    FA_SECOND_LEVEL_SPARSE = 64 /* also the second level from the two-step pattern (needs the
-                                   first level sparse) */
+    FA_SECOND_LEVEL_SPARSE = 64, /* also the second level from the two-step pattern (needs the
+                                    first level sparse) */
+    FA_LIVE_STATES = 128 /* span products over the states live at their midpoint (see fa_span_tree) */
 };
 
 enum { FA_CONF_PROB = 0, FA_CONF_NEGENT = 1, FA_CONF_UNCONSTRAINED = 2 };
@@ -109,7 +110,9 @@ enum { FA_CONF_PROB = 0, FA_CONF_NEGENT = 1, FA_CONF_UNCONSTRAINED = 2 };
  *                   FA_SECOND_LEVEL_SPARSE (the second level likewise, over
  *                   the pairs (a, c) joined through some k; default: when
  *                   the first is sparse and its own work is at most 1/256 of
- *                   S^3)
+ *                   S^3), and FA_LIVE_STATES (fa_span_tree restricts the
+ *                   256x256-tile products to the states live at their
+ *                   midpoint under the step's p)
  *   out             receives the handle (free with fa_table_destroy)
  *   device_bytes    receives the size of the device image
  * Dead states (unreachable from s0 or unable to reach F) are removed unless
@@ -146,8 +149,9 @@ void fa_table_destroy(fa_table *t);
  * two-step pattern it uses, [20] 1 if the step keeps no dense leaves (the
  * first level is sparse, and the message pass's leaf level and the leaf-level
  * midpoint draws read the pair values), [21] 1 if the message pass's leaf
- * level (L > 1) reads the pair values instead of the dense leaves.  Returns
- * FA_OK or FA_EINVAL.
+ * level (L > 1) reads the pair values instead of the dense leaves, [22] 1
+ * if the table was compiled with FA_LIVE_STATES.  Returns FA_OK or
+ * FA_EINVAL.
  */
 int fa_table_info(const fa_table *t, int64_t *info, int32_t n);
 
@@ -216,7 +220,14 @@ int fa_build_transitions(const fa_table *t, const float *p, int32_t B, int32_t L
  *               With FA_SECOND_LEVEL_SPARSE (or chosen likewise) the second
  *               level is formed the same way over the pairs (a, c) joined
  *               through some k, for its products whose four leaves lie
- *               inside the sequence.
+ *               inside the sequence.  With FA_LIVE_STATES the call first
+ *               finds, per row and boundary, the states reachable from s0
+ *               and able to reach F through transitions of positive value
+ *               (a forward and a backward pass over the positions), and
+ *               the products on 256x256 tiles sum only over the states
+ *               live at their midpoint: exact, since every path of the
+ *               posterior visits live states only, and cheaper where
+ *               committed positions (one-hot p) leave few of them.
  *   logZ        device double [B]; -inf for infeasible rows
  *   row_status  device int32 [B]; FA_ROW_INFEASIBLE when Z = 0
  * Errors: FA_EINVAL, FA_ESTATE, FA_EHIP.

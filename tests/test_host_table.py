@@ -66,7 +66,7 @@ def test_invalid_ranges_and_flags():
     assert _code(lambda: _compile(2, 10, 0, [1], [(0, 1, [0, 11])], R)) == _fa.FA_EINVAL
     assert _code(lambda: _compile(2, 10, 0, [1], [(0, 1, [0, 5, 3, 7])], R)) == _fa.FA_EINVAL
     assert _code(lambda: _compile(2, 10, 0, [1], [(0, 1, [1])], fa.FA_DFA | fa.FA_NFA)) == _fa.FA_EINVAL
-    assert _code(lambda: _compile(2, 10, 0, [1], [(0, 1, [1])], 128)) == _fa.FA_EINVAL
+    assert _code(lambda: _compile(2, 10, 0, [1], [(0, 1, [1])], 256)) == _fa.FA_EINVAL
     # the sparse second level needs the sparse first level
     assert _code(lambda: _compile(2, 10, 0, [1], [(0, 1, [1])], fa.FA_DFA | fa.FA_FIRST_LEVEL_DENSE
                                   | fa.FA_SECOND_LEVEL_SPARSE)) == _fa.FA_EINVAL
