@@ -299,6 +299,8 @@ def time_workload(torch, fa, configs, k, steps, warmup, dev, device_p=False, liv
                first_level="sparse" if tb.info["first_sparse"] else "dense",
                second_level="sparse" if tb.info["second_sparse"] else "dense",
                leafless=bool(tb.info["leafless"]), live_states=bool(tb.info["live_states"]),
+               flops_note=("the tree's flops count every product over all states (a dense-equivalent "
+                           "rate: the restricted products execute fewer)") if live else None,
                p_drawn="on the device (same distribution, torch generator)" if device_p
                else "on the host (numpy PCG64)",
                stages=stage_fracs(work, stage_us, False), row_status=status,
