@@ -294,13 +294,56 @@ __global__ __launch_bounds__(kGemmThreads) void span_reduce(StepView sv, float *
     if (tm == 0 && tid < kTile) coD[tn + tid] = add_exp(roG[tn + tid], rfG[tn + tid]);
 }
 
+// The 128- and 256-tile kernels run the fp32 products on the bf16 matrix
+// cores: every folded operand entry x is split, when it is staged, into
+// three bf16 pieces x = h + m + l (round to nearest at each step, so each
+// residual is exact and the pieces hold all 24 bits of x), and the product
+// x y takes the six partial products hh' + hm' + mh' + hl' + mm' + lh'.  The
+// three dropped ones are below 2^-23 |x y| together, and all entries are
+// non-negative, so every output entry keeps that relative bound on top of
+// the fp32 accumulation's rounding: the precision of the fp32 MFMA path at
+// 6/16 of its matrix-core time.  LDS stages hold the three pieces of K = 16
+// columns per stored row.
+constexpr int kBK3 = 16;        // K step per LDS stage
+constexpr int kLdb = kBK3 + 8;  // padded LDS row of one piece (bf16 entries)
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+
+// two fp32 values rounded to bf16 (to nearest even), packed low | high
+__device__ inline uint32_t bf16_pair(float a, float b)
+{
+    const f32x2v v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// the three bf16 pieces of four fp32 entries, two per word (h + m + l == x
+// exactly while x is a normal fp32 number of at least 2^-110)
+__device__ inline void split3(float4 x, uint2 &h, uint2 &m, uint2 &l)
+{
+    const float v[4] = {x.x, x.y, x.z, x.w};
+    uint32_t hw[2], mw[2], lw[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const float a = v[2 * u], b = v[2 * u + 1];
+        hw[u] = bf16_pair(a, b);
+        const float ra = a - __uint_as_float(hw[u] << 16), rb = b - __uint_as_float(hw[u] & 0xffff0000u);
+        mw[u] = bf16_pair(ra, rb);
+        const float sa = ra - __uint_as_float(mw[u] << 16), sb = rb - __uint_as_float(mw[u] & 0xffff0000u);
+        lw[u] = bf16_pair(sa, sb);
+    }
+    h = make_uint2(hw[0], hw[1]);
+    m = make_uint2(mw[0], mw[1]);
+    l = make_uint2(lw[0], lw[1]);
+}
+
+
 constexpr int kBig = 128;       // output tile of the large-level kernel
-constexpr int kBK2 = 32;        // K step per LDS stage
-constexpr int kLdk2 = kBK2 + 4; // padded LDS row (floats)
 constexpr int kBigThreads = 512;
 
-// 128x128 output tiles, eight wavefronts of 32x64 (1x2 MFMA 32x32x2 blocks),
-// double-buffered LDS stages of K = 32 (74 KB of LDS); the global data of
+// 128x128 output tiles, eight wavefronts of 32x64 (1x2 MFMA 32x32 blocks),
+// double-buffered LDS stages of K = 16 (74 KB of LDS); the global data of
 // stage s+1 is loaded while stage s runs.  Small per-wave state keeps four
 // wavefronts per SIMD resident.  grid.x enumerates (product, tile) so that
 // the tiles of one product land on one XCD.
@@ -333,17 +376,16 @@ __global__ __launch_bounds__(kBigThreads) void span_gemm128(StepView sv, float *
     int32_t *coD = sv.meta_ptr(meta, b, n, 1);
     int32_t *rfD = sv.meta_ptr(meta, b, n, 2);
 
-    __shared__ __align__(16) float Fs[2][kBig][kLdk2];
-    __shared__ __align__(16) float Gs[2][kBig][kLdk2];
+    // per buffer and operand: the pieces h, m, l of 128 stored rows
+    __shared__ __align__(16) __bf16 Fs[2][3][kBig][kLdb];
+    __shared__ __align__(16) __bf16 Gs[2][3][kBig][kLdb];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // loader: thread t stages float4 (t & 7) of rows t>>3 and 64 + (t>>3) of
-    // both operands, so eight lanes read one full 128-byte row segment
-    const int lrow = tid >> 3, lk = (tid & 7) * 4;
-    const int rfF0 = rfF[tm + lrow], rfF1 = rfF[tm + 64 + lrow];
-    const int rfG0 = rfG[tn + lrow], rfG1 = rfG[tn + 64 + lrow];
+    // loader: thread t stages float4 (t & 3) of row t >> 2 of both
+    // operands, so four lanes read one 64-byte row segment
+    const int lrow = tid >> 2, lk = (tid & 3) * 4;
+    const int rfF0 = rfF[tm + lrow], rfG0 = rfG[tn + lrow];
     const float *Frow = F + (size_t)(tm + lrow) * Sp + lk;
     const float *Grow = G + (size_t)(tn + lrow) * Sp + lk;
-    const size_t half_rows = (size_t)64 * Sp;
     const int wr = (wave >> 1) * 32, wc = (wave & 1) * 64;
     const int l32 = lane & 31, half = lane >> 5;
 
@@ -353,47 +395,51 @@ __global__ __launch_bounds__(kBigThreads) void span_gemm128(StepView sv, float *
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[y][r] = 0.f;
 
-    float4 fr[2], gr[2];
+    float4 fr, gr;
     int4 cf, cg;
     auto gload = [&](int k0) {
-        fr[0] = *reinterpret_cast<const float4 *>(Frow + k0);
-        fr[1] = *reinterpret_cast<const float4 *>(Frow + half_rows + k0);
-        gr[0] = *reinterpret_cast<const float4 *>(Grow + k0);
-        gr[1] = *reinterpret_cast<const float4 *>(Grow + half_rows + k0);
+        fr = *reinterpret_cast<const float4 *>(Frow + k0);
+        gr = *reinterpret_cast<const float4 *>(Grow + k0);
         cf = *reinterpret_cast<const int4 *>(coF + k0 + lk);
         cg = *reinterpret_cast<const int4 *>(coG + k0 + lk);
     };
-    auto lstore = [&](int buf) {
-        *reinterpret_cast<float4 *>(&Fs[buf][lrow][lk]) = fold4(fr[0], cf, rfF0);
-        *reinterpret_cast<float4 *>(&Fs[buf][64 + lrow][lk]) = fold4(fr[1], cf, rfF1);
-        *reinterpret_cast<float4 *>(&Gs[buf][lrow][lk]) = fold4(gr[0], cg, rfG0);
-        *reinterpret_cast<float4 *>(&Gs[buf][64 + lrow][lk]) = fold4(gr[1], cg, rfG1);
+    auto put = [&](__bf16 (*X)[kBig][kLdb], float4 x) {
+        uint2 h, m, l;
+        split3(x, h, m, l);
+        *reinterpret_cast<uint2 *>(&X[0][lrow][lk]) = h;
+        *reinterpret_cast<uint2 *>(&X[1][lrow][lk]) = m;
+        *reinterpret_cast<uint2 *>(&X[2][lrow][lk]) = l;
     };
-    const int nk = Sp / kBK2;
+    auto lstore = [&](int buf) {
+        put(Fs[buf], fold4(fr, cf, rfF0));
+        put(Gs[buf], fold4(gr, cg, rfG0));
+    };
+    const int nk = Sp / kBK3;
     gload(0);
     lstore(0);
     __syncthreads();
     for (int ks = 0; ks < nk; ++ks) {
         const int buf = ks & 1;
         // unconditional (the last step re-reads the final K block), and kept
-        // ahead of the MFMAs, with the fold arithmetic after them
-        gload(min(ks + 1, nk - 1) * kBK2);
+        // ahead of the MFMAs, with the split arithmetic after them
+        gload(min(ks + 1, nk - 1) * kBK3);
         __builtin_amdgcn_sched_barrier(0);
+        bf16x8 a[3], c[3][2];
 #pragma unroll
-        for (int t = 0; t < kBK2 / 2; t += 4) {
-            const float4 a = *reinterpret_cast<const float4 *>(&Fs[buf][wr + l32][half * (kBK2 / 2) + t]);
-            float4 c[2];
+        for (int pc = 0; pc < 3; ++pc) {
+            a[pc] = *reinterpret_cast<const bf16x8 *>(&Fs[buf][pc][wr + l32][half * 8]);
 #pragma unroll
             for (int y = 0; y < 2; ++y)
-                c[y] = *reinterpret_cast<const float4 *>(&Gs[buf][wc + 32 * y + l32][half * (kBK2 / 2) + t]);
-#pragma unroll
-            for (int y = 0; y < 2; ++y) {
-                acc[y] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, c[y].x, acc[y], 0, 0, 0);
-                acc[y] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, c[y].y, acc[y], 0, 0, 0);
-                acc[y] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, c[y].z, acc[y], 0, 0, 0);
-                acc[y] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, c[y].w, acc[y], 0, 0, 0);
-            }
+                c[pc][y] = *reinterpret_cast<const bf16x8 *>(&Gs[buf][pc][wc + 32 * y + l32][half * 8]);
         }
+        // the six partial products, grouped by the second operand's piece
+#pragma unroll
+        for (int pb = 0; pb < 3; ++pb)
+#pragma unroll
+            for (int pa = 0; pa < 3 - pb; ++pa)
+#pragma unroll
+                for (int y = 0; y < 2; ++y)
+                    acc[y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[pa], c[pb][y], acc[y], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         lstore(buf ^ 1);
         __syncthreads();
@@ -406,9 +452,9 @@ __global__ __launch_bounds__(kBigThreads) void span_gemm128(StepView sv, float *
         const int j = tn + wc + 32 * y + l32;
         coDj[y] = add_exp(roG[j], rfG[j]);
     }
-    int *E = reinterpret_cast<int *>(&Fs[0][0][0]);  // [kBig][2 * 32 + 4]
+    int *E = reinterpret_cast<int *>(&Fs[0][0][0][0]);  // [kBig][2 * 32 + 4]
     constexpr int ldE = 2 * 32 + 4;
-    static_assert(kBig * ldE <= 2 * kBig * kLdk2, "row-maximum exchange fits the operand buffers");
+    static_assert(kBig * ldE * sizeof(int) <= sizeof(Fs), "row-maximum exchange fits the operand buffers");
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int il = wr + (r >> 2) * 8 + half * 4 + (r & 3);
@@ -476,29 +522,28 @@ __global__ void tree_logz_empty(DevTable d, int B, double *__restrict__ logZ,
 
 // Large levels with 256x256 output tiles (one whole product when Sp = 256),
 // one persistent workgroup per CU walking tiles v = blockIdx.x + k gridDim.x:
-// 8 waves of 64 x 128 (2 x 4 MFMA tiles of 32x32), 128 MFMAs per wave per K
-// step of 32, double-buffered LDS (147 KB).  The
-// loads of block ks+1 are in flight while block ks computes; during the last
-// K step of a tile they fetch block 0 of the workgroup's next tile (or
-// re-read block 0 of the current one when there is none), so the next tile
-// starts from a filled buffer while the current one is stored.  Row
+// 8 waves of 64 x 128 (2 x 4 MFMA tiles of 32x32), double-buffered LDS
+// (147 KB) with K steps of 16 (the bf16 pieces above).  The loads of block
+// ks+1 are in flight while block ks computes (48 MFMAs per wave); during
+// the last K step of a tile they fetch block 0 of the workgroup's next tile
+// (or re-read block 0 of the current one when there is none), so the next
+// tile starts from a filled buffer while the current one is stored.  Row
 // exponents are reduced inside the workgroup through the free LDS buffer:
 // one store (full rows) or atomicMax (several column tiles) per row.
 constexpr int kHuge = 256;
 constexpr int kHugeThreads = 512;
-
 // the operand side of one 256x256 tile: stored rows tm.. of F, tn.. of G
 struct HugeSrc {
     const float *F, *G;
     const int32_t *coF, *coG, *rfF, *rfG;
     const int32_t *kidx;  // LIVE: the states live at the midpoint, padded with -1
     int tm, tn;
-    int nk;               // K steps of 32
+    int nk;               // K steps of 16
 };
 
 // LIVE (tables compiled with FA_LIVE_STATES): the contraction runs over the
 // states live at the product's midpoint (lists and counts from
-// launch_live_states), each K step gathering 32 listed columns of both
+// launch_live_states), each K step gathering 16 listed columns of both
 // operands; list entries of -1 load zero.
 template <bool LIVE>
 __global__ __launch_bounds__(kHugeThreads) void span_gemm256(StepView sv, float *__restrict__ tree,
@@ -536,7 +581,7 @@ __global__ __launch_bounds__(kHugeThreads) void span_gemm256(StepView sv, float 
         s.tm = tm;
         s.tn = tn;
         s.kidx = nullptr;
-        s.nk = Sp / kBK2;
+        s.nk = Sp / kBK3;
         if constexpr (LIVE) {
             // node n of level k: the level's nodes start at 2^(K-k) = Lpad / span
             const int first = 1 << (31 - __clz(n));
@@ -544,29 +589,30 @@ __global__ __launch_bounds__(kHugeThreads) void span_gemm256(StepView sv, float 
             const int m = (n - first) * span + span / 2;  // midpoint boundary
             const size_t bm = (size_t)b * (sv.Lpad + 1) + m;
             s.kidx = live + bm * Sp;
-            s.nk = max(2, (nlive[bm] + 63) / 64 * 2);
+            s.nk = max(4, (nlive[bm] + 63) / 64 * 4);
         }
         return s;
     };
 
-    __shared__ __align__(16) float Fs[2][kHuge][kLdk2];
-    __shared__ __align__(16) float Gs[2][kHuge][kLdk2];
+    // per buffer and operand: the pieces h, m, l of 256 stored rows
+    __shared__ __align__(16) __bf16 Fs[2][3][kHuge][kLdb];
+    __shared__ __align__(16) __bf16 Gs[2][3][kHuge][kLdb];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // loader: thread t stages float4 (t & 7) of rows (t >> 3) + 64 q, q < 4,
-    // of both operands: eight lanes read one 128-byte row segment
-    const int lrow = tid >> 3, lk = (tid & 7) * 4;
-    const size_t q_rows = (size_t)64 * Sp;
+    // loader: thread t stages float4 (t & 3) of rows (t >> 2) + 128 q, q < 2,
+    // of both operands: four lanes read one 64-byte row segment
+    const int lrow = tid >> 2, lk = (tid & 3) * 4;
+    const size_t q_rows = (size_t)128 * Sp;
     const int wr = (wave >> 1) * 64, wc = (wave & 1) * 128;
     const int l32 = lane & 31, half = lane >> 5;
 
     struct Stage {
-        float4 f[4], g[4];
+        float4 f[2], g[2];
         int4 cf, cg;
-        int rf[4], rg[4];
+        int rf[2], rg[2];
     };
     // the rows' exponents come with block 0 of a tile and stay for its other blocks
     auto gload = [&](Stage &st, const HugeSrc &s, int ks, bool rows) {
-        const int k0 = ks * kBK2;
+        const int k0 = ks * kBK3;
         if constexpr (LIVE) {
             const int4 kk = *reinterpret_cast<const int4 *>(s.kidx + k0 + lk);
             const int k[4] = {max(kk.x, 0), max(kk.y, 0), max(kk.z, 0), max(kk.w, 0)};
@@ -574,7 +620,7 @@ __global__ __launch_bounds__(kHugeThreads) void span_gemm256(StepView sv, float 
             const float *Fr = s.F + (size_t)(s.tm + lrow) * Sp;
             const float *Gr = s.G + (size_t)(s.tn + lrow) * Sp;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < 2; ++q) {
                 const float *fr = Fr + q * q_rows, *gr = Gr + q * q_rows;
                 float fv[4], gv[4];
 #pragma unroll
@@ -593,7 +639,7 @@ __global__ __launch_bounds__(kHugeThreads) void span_gemm256(StepView sv, float 
             const float *Fr = s.F + (size_t)(s.tm + lrow) * Sp + lk + k0;
             const float *Gr = s.G + (size_t)(s.tn + lrow) * Sp + lk + k0;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < 2; ++q) {
                 st.f[q] = *reinterpret_cast<const float4 *>(Fr + q * q_rows);
                 st.g[q] = *reinterpret_cast<const float4 *>(Gr + q * q_rows);
             }
@@ -602,39 +648,49 @@ __global__ __launch_bounds__(kHugeThreads) void span_gemm256(StepView sv, float 
         }
         if (rows) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                st.rf[q] = s.rfF[s.tm + lrow + 64 * q];
-                st.rg[q] = s.rfG[s.tn + lrow + 64 * q];
+            for (int q = 0; q < 2; ++q) {
+                st.rf[q] = s.rfF[s.tm + lrow + 128 * q];
+                st.rg[q] = s.rfG[s.tn + lrow + 128 * q];
             }
         }
     };
+    auto put = [&](__bf16 (*X)[kHuge][kLdb], int row, float4 x) {
+        uint2 h, m, l;
+        split3(x, h, m, l);
+        *reinterpret_cast<uint2 *>(&X[0][row][lk]) = h;
+        *reinterpret_cast<uint2 *>(&X[1][row][lk]) = m;
+        *reinterpret_cast<uint2 *>(&X[2][row][lk]) = l;
+    };
     auto lstore = [&](const Stage &st, int buf) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            *reinterpret_cast<float4 *>(&Fs[buf][lrow + 64 * q][lk]) = fold4(st.f[q], st.cf, st.rf[q]);
-            *reinterpret_cast<float4 *>(&Gs[buf][lrow + 64 * q][lk]) = fold4(st.g[q], st.cg, st.rg[q]);
+        for (int q = 0; q < 2; ++q) {
+            put(Fs[buf], lrow + 128 * q, fold4(st.f[q], st.cf, st.rf[q]));
+            put(Gs[buf], lrow + 128 * q, fold4(st.g[q], st.cg, st.rg[q]));
         }
     };
     f32x16 acc[2][4];
+    // the six partial products, grouped by the second operand's piece, each
+    // over the 8 output tiles in turn (no MFMA waits for the one before it)
     auto mfmas = [&](int buf) {
+        bf16x8 a[3][2], c[4];
 #pragma unroll
-        for (int t = 0; t < kBK2 / 2; t += 4) {
-            float4 a[2], c[4];
+        for (int pa = 0; pa < 3; ++pa)
 #pragma unroll
             for (int ry = 0; ry < 2; ++ry)
-                a[ry] = *reinterpret_cast<const float4 *>(&Fs[buf][wr + 32 * ry + l32][half * (kBK2 / 2) + t]);
+                a[pa][ry] = *reinterpret_cast<const bf16x8 *>(&Fs[buf][pa][wr + 32 * ry + l32][half * 8]);
+#pragma unroll
+        for (int pb = 0; pb < 3; ++pb) {
 #pragma unroll
             for (int cy = 0; cy < 4; ++cy)
-                c[cy] = *reinterpret_cast<const float4 *>(&Gs[buf][wc + 32 * cy + l32][half * (kBK2 / 2) + t]);
+                c[cy] = *reinterpret_cast<const bf16x8 *>(&Gs[buf][pb][wc + 32 * cy + l32][half * 8]);
 #pragma unroll
-            for (int ry = 0; ry < 2; ++ry)
+            for (int pa = 0; pa < 3 - pb; ++pa)
 #pragma unroll
-                for (int cy = 0; cy < 4; ++cy) {
-                    acc[ry][cy] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[ry].x, c[cy].x, acc[ry][cy], 0, 0, 0);
-                    acc[ry][cy] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[ry].y, c[cy].y, acc[ry][cy], 0, 0, 0);
-                    acc[ry][cy] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[ry].z, c[cy].z, acc[ry][cy], 0, 0, 0);
-                    acc[ry][cy] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[ry].w, c[cy].w, acc[ry][cy], 0, 0, 0);
-                }
+                for (int ry = 0; ry < 2; ++ry)
+#pragma unroll
+                    for (int cy = 0; cy < 4; ++cy)
+                        acc[ry][cy] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[pa][ry], c[cy], acc[ry][cy],
+                                                                              0, 0, 0);
         }
     };
 
@@ -656,9 +712,9 @@ __global__ __launch_bounds__(kHugeThreads) void span_gemm256(StepView sv, float 
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[ry][cy][r] = 0.f;
         // step ks: issue the loads of K block ks+1 (of the next tile after
-        // the last block), compute buffer ks & 1 (128 MFMAs per wave cover
+        // the last block), compute buffer ks & 1 (48 MFMAs per wave cover
         // the load latency), store that block into the other buffer.
-        // A tile's K steps (Sp / 32, or its live list's length / 32) are
+        // A tile's K steps (Sp / 16, or its live list's length / 16) are
         // even.  The scheduling barriers keep the compiler from moving the
         // fold arithmetic of the stores (which waits for the loads) into
         // the MFMAs.
@@ -715,8 +771,10 @@ __global__ __launch_bounds__(kHugeThreads) void span_gemm256(StepView sv, float 
                                                    tn + col0 + 32 * cy]);
         // per row the maximum over this lane's four columns, into buffer 1
         // (free until the next tile's first store into it): E[il][l32] of
-        // the wave's column half, rows padded to kLdk2 entries
-        int *E = reinterpret_cast<int *>(wc == 0 ? &Fs[1][0][0] : &Gs[1][0][0]);
+        // the wave's column half, rows padded to kLde entries
+        constexpr int kLde = 36;
+        static_assert(kHuge * kLde * sizeof(int) <= sizeof(Fs[1]), "row-maximum exchange fits one buffer");
+        int *E = reinterpret_cast<int *>(wc == 0 ? &Fs[1][0][0][0] : &Gs[1][0][0][0]);
 #pragma unroll
         for (int ry = 0; ry < 2; ++ry) {
 #pragma unroll
@@ -730,13 +788,13 @@ __global__ __launch_bounds__(kHugeThreads) void span_gemm256(StepView sv, float 
                     const bool ok = (x > 0.f) & (coDj[cy] > kNeg);
                     e = max(e, ok ? ex + coDj[cy] : kNeg);
                 }
-                E[(row0 + 32 * ry + (r >> 2) * 8 + (r & 3)) * kLdk2 + l32] = e;
+                E[(row0 + 32 * ry + (r >> 2) * 8 + (r & 3)) * kLde + l32] = e;
             }
         }
         __syncthreads();
         if (tid < kHuge) {
-            const int4 *e0 = reinterpret_cast<const int4 *>(&Fs[1][tid][0]);
-            const int4 *e1 = reinterpret_cast<const int4 *>(&Gs[1][tid][0]);
+            const int4 *e0 = reinterpret_cast<const int4 *>(reinterpret_cast<const int *>(&Fs[1][0][0][0]) + tid * kLde);
+            const int4 *e1 = reinterpret_cast<const int4 *>(reinterpret_cast<const int *>(&Gs[1][0][0][0]) + tid * kLde);
             int e = kNeg;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
