@@ -21,6 +21,10 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
+BF16_MFMA_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 matrix
+# the span products run on the bf16 matrix cores: each fp32 product is six
+# bf16 products of the operands' three-piece split
+SPLIT_PRODUCTS = 6
 # vector ALU issue: 256 CUs x 64 lanes x 2.4 GHz (fp64 and unpacked fp32 alike)
 VALU_FP64_LANE_OPS = 256 * 64 * 2.4e9
 METRIC = "constrained denoising steps/sec + per-step µs (L=256, V=151,936); HBM/MFMA % peak"
@@ -70,6 +74,7 @@ def algorithmic_work(tb, B, L):
     a4_leaves = pair_values if leaf_msg_pairs else dense_leaves
     internal = B * (Lpad - 1) * S * S * 4
     sparse1 = bool(tb.info["first_sparse"])
+    pairs1 = bool(tb.info["first_pairs"])
     sparse2 = sparse1 and bool(tb.info["second_sparse"]) and K >= 2
     npairs, w1 = tb.info["pairs"], tb.info["first_work"]
     npairs2, w2 = tb.info["pairs2"], tb.info["second_work"]
@@ -81,18 +86,52 @@ def algorithmic_work(tb, B, L):
     level2_flops = B * (nsp2 * 2.0 * w2 + (Lpad // 4 - nsp2) * 2.0 * S ** 3) if K >= 2 else 0.0
     upper_flops = 2.0 * S ** 3 * B * max(Lpad // 4 - 1, 0)
     out2 = npairs2 * 4 if sparse2 else 0
-    level1 = (dict(bound="hbm", work=B * (Lpad // 2) * (S * S * 4 + 2 * npairs * 4 + out2), unit="GB/s",
-                   per_unit="per product: the dense S*S output write + both leaves' pair values "
-                            "(2*pairs*4) + its values on the two-step pattern when the second "
-                            "level is sparse (pairs2*4), B*Lpad/2 products")
-              if sparse1 else
-              dict(bound="mfma", work=2.0 * S ** 3 * B * (Lpad // 2), unit="TFLOP/s",
-                   per_unit="2*S^3 per product (S trimmed states), B*Lpad/2 products"))
+
+    # the tree's roofline, level by level: a dense product reads its two
+    # operands and writes its output (3*S^2*4 bytes; a pair-staged first
+    # level reads both leaves' pair values instead) and executes 6*2*S^3
+    # bf16 flops; its ideal time is the larger of the two at peak.  A sparse
+    # level moves its bytes and does its multiply-adds on the vector ALUs.
+    def dense_product(in_bytes):
+        return dict(bytes=in_bytes + S * S * 4, mfma_flops=SPLIT_PRODUCTS * 2.0 * S ** 3)
+
+    levels = []
+    for k in range(1, K + 1):
+        nprod = B * (Lpad >> k)
+        if k == 1 and sparse1:
+            per = dict(bytes=S * S * 4 + 2 * npairs * 4 + out2, mfma_flops=0.0)
+        elif k == 1 and pairs1:
+            per = dense_product(2 * npairs * 4)
+        else:
+            per = dense_product(2 * S * S * 4)
+        n_dense = nprod - (nsp2 if k == 2 else 0)
+        lv = dict(level=k, products=nprod, bytes=nprod * per["bytes"], mfma_flops=n_dense * per["mfma_flops"])
+        if k == 2 and nsp2:
+            lv["bytes"] += nsp2 * (2 * npairs2 * 4 + S * S * 4 - per["bytes"])
+        lv["ideal_us"] = max(lv["bytes"] / (HBM_PEAK_GBS * 1e3), lv["mfma_flops"] / (BF16_MFMA_PEAK_TFLOPS * 1e6))
+        levels.append(lv)
+    l1 = levels[0] if levels else dict(bytes=0.0, mfma_flops=0.0)
+    if sparse1:
+        level1 = dict(bound="hbm", work=l1["bytes"], unit="GB/s",
+                      per_unit="per product: the dense S*S output write + both leaves' pair values "
+                               "(2*pairs*4) + its values on the two-step pattern when the second "
+                               "level is sparse (pairs2*4), B*Lpad/2 products")
+    elif l1["mfma_flops"] / (BF16_MFMA_PEAK_TFLOPS * 1e6) >= l1["bytes"] / (HBM_PEAK_GBS * 1e3):
+        level1 = dict(bound="mfma", work=l1["mfma_flops"], unit="TFLOP/s", peak=BF16_MFMA_PEAK_TFLOPS,
+                      per_unit="6*2*S^3 bf16 flops per product (six bf16 products of the three-piece "
+                               "split per fp32 product, S trimmed states), B*Lpad/2 products",
+                      fp32_equivalent_flops=l1["mfma_flops"] / SPLIT_PRODUCTS)
+    else:
+        level1 = dict(bound="hbm", work=l1["bytes"], unit="GB/s",
+                      per_unit=("per product: both leaves' pair values (2*pairs*4)" if pairs1 else
+                                "per product: both dense leaves (2*S*S*4)") +
+                               " + the dense S*S output write, B*Lpad/2 products")
     return dict(
         a1_bytes=p_bytes + table_bytes + a1_leaves,
         a1_basis=("p read + table + " + ("each leaf's pair values written (B*L*pairs*4)" if leafless
                                          else "dense leaves written (B*Lpad*S*S*4)")),
         a2_flops=level1_flops + level2_flops + upper_flops,
+        tree_levels=levels,
         a4_bytes=p_bytes + p_bytes + a4_leaves + internal + table_bytes,
         a4_basis=("p read + q write + internal nodes read + table + " +
                   ("leaf pair values read (B*L*pairs*4)" if leaf_msg_pairs
@@ -231,8 +270,12 @@ def stage_fracs(work, stage_us, separate):
         "build_transitions": dict(us=stage_us["build_transitions"], bound="hbm",
                                   algorithmic_bytes=work["a1_bytes"], basis=work["a1_basis"],
                                   gbs=work["a1_bytes"] / (stage_us["build_transitions"] * 1e3)),
-        "span_tree": dict(us=stage_us["span_tree"], bound="mfma", algorithmic_flops=work["a2_flops"],
-                          tflops=work["a2_flops"] / (stage_us["span_tree"] * 1e6)),
+        "span_tree": dict(us=stage_us["span_tree"], bound="mfma+hbm",
+                          ideal_us=sum(lv["ideal_us"] for lv in work["tree_levels"]),
+                          basis=("per level the larger of its HBM bytes at 8 TB/s and its bf16 "
+                                 "flops (six per fp32 product) at 2.5 PFLOP/s"),
+                          algorithmic_flops=work["a2_flops"],
+                          fp32_equivalent_tflops=work["a2_flops"] / (stage_us["span_tree"] * 1e6)),
     }
     if separate:
         st["sample"] = dict(us=stage_us["sample"], bound="latency")
@@ -243,7 +286,7 @@ def stage_fracs(work, stage_us, separate):
                     basis=work["a4_basis"], gbs=work["a4_bytes"] / (stage_us[last] * 1e3))
     for n in ("build_transitions", last):
         st[n]["frac"] = st[n]["gbs"] / HBM_PEAK_GBS
-    st["span_tree"]["frac"] = st["span_tree"]["tflops"] / FP32_MFMA_PEAK_TFLOPS
+    st["span_tree"]["frac"] = st["span_tree"]["ideal_us"] / st["span_tree"]["us"]
     return st
 
 
@@ -292,11 +335,11 @@ def time_workload(torch, fa, configs, k, steps, warmup, dev, device_p=False, liv
     work = algorithmic_work(tb, w.B, w.L)
     status = bufs.status.cpu().numpy().tolist()
     del bufs
-    chain = time_chain_vs_tree(torch, fa, tb, p, w.seed, min(steps, 5), 1) if chain else None
+    chain = time_chain_vs_tree(torch, fa, tb, p, w.seed, min(steps, 5), 1, w.aut) if chain else None
     out = dict(workload=w.describe(), B=w.B, L=w.L, S=tb.info["S"], Sp=tb.info["Sp"], V=w.aut.V,
                steps=steps, warmup=warmup, us_per_step=us, steps_per_s=1e6 / us,
                sequence_steps_per_s=w.B * 1e6 / us,
-               first_level="sparse" if tb.info["first_sparse"] else "dense",
+               first_level=first_level_name(tb),
                second_level="sparse" if tb.info["second_sparse"] else "dense",
                leafless=bool(tb.info["leafless"]), live_states=bool(tb.info["live_states"]),
                flops_note=("the tree's flops count every product over all states (a dense-equivalent "
@@ -311,17 +354,21 @@ def time_workload(torch, fa, configs, k, steps, warmup, dev, device_p=False, liv
     return out
 
 
-def time_chain_vs_tree(torch, fa, tb, p, seed, steps, warmup):
+def time_chain_vs_tree(torch, fa, tb, p, seed, steps, warmup, aut=None):
     """The pages' central trade on this GPU: the sampling half of a step
     (emission reduce, then the draws and log Z) through the log-depth tree
     (fa_span_tree + fa_sample) and through the serial chain
     (fa_chain_sample: L dependent forward launches, then backward sampling);
     then the whole step with q written both ways (fa_span_tree +
     fa_sample_marginals against fa_chain_sample_marginals: L more dependent
-    launches for the backward messages).  µs per step each; None when the
-    table keeps no dense leaves."""
+    launches for the backward messages).  µs per step each.  The chain reads
+    dense leaves: a table that keeps none is compiled again with them
+    (FA_FIRST_LEVEL_DENSE, from `aut`) for both sides; None without `aut`."""
     if tb.info["leafless"]:
-        return None
+        if aut is None:
+            return None
+        tb = fa.Table.from_automaton(aut, first_level="dense")
+        tb.upload(p.device)
     B, L, _ = p.shape
     bufs = fa.StepBuffers(tb, B, L, want_q=True, device=p.device)
     stream = torch.cuda.current_stream(p.device).cuda_stream
@@ -431,6 +478,13 @@ def generation_sweep(torch, fa, tb, p, seed, bufs, Ts):
 
 
 # --- rocprofv3 output -> committed summaries ------------------------------
+
+def first_level_name(tb):
+    """How the table forms the first span level."""
+    if tb.info["first_sparse"]:
+        return "sparse"
+    return "dense from pair values" if tb.info["first_pairs"] else "dense"
+
 
 def level1_name(tb):
     """The first tree level's kernel: sparse row combination or dense MFMA."""
@@ -602,7 +656,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", type=int, default=3, help="preset 1..5 (default 3)")
-    ap.add_argument("--first-level", choices=["auto", "sparse", "dense"], default="auto",
+    ap.add_argument("--first-level", choices=["auto", "sparse", "dense", "pairs"], default="auto",
                     help="form of the first span level (default: the library's choice)")
     ap.add_argument("--separate", action="store_true",
                     help="fa_sample then fa_marginals instead of fa_sample_marginals")
@@ -760,7 +814,7 @@ def main():
         if kw["bound"] == "hbm":
             achieved, peak = kw["work"] / (us * 1e3), HBM_PEAK_GBS
         else:
-            achieved, peak = kw["work"] / (us * 1e6), FP32_MFMA_PEAK_TFLOPS
+            achieved, peak = kw["work"] / (us * 1e6), kw.get("peak", FP32_MFMA_PEAK_TFLOPS)
         tr = traffic_record(name)
         kernels[name] = dict(bound=kw["bound"], achieved=achieved, peak=peak, unit=kw["unit"],
                              frac=achieved / peak, avg_launch_us=us, work_per_launch=kw["work"],
@@ -784,7 +838,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.describe(), "B": w.B, "L": w.L, "S": w.aut.S, "V": w.aut.V,
                    "calls": "separate" if args.separate else "joint",
-                   "first_level": "sparse" if tb.info["first_sparse"] else "dense",
+                   "first_level": first_level_name(tb),
                    "sequence_steps_per_s": w.B * 1000.0 / ms_per_step},
         "roofline": roof,
         "kernels": kernels,
@@ -802,7 +856,8 @@ def main():
         out["ceiling"] = ceilings(torch, fa, dev, p)
         if not tb.info["segments"]:
             out["map_decode"] = time_map(torch, fa, tb, p, args.steps, args.warmup)
-        out["chain_vs_tree"] = time_chain_vs_tree(torch, fa, tb, p, w.seed, args.steps, args.warmup)
+        out["chain_vs_tree"] = time_chain_vs_tree(torch, fa, tb, p, w.seed, args.steps, args.warmup,
+                                                  w.aut)
     del bufs, p
     torch.cuda.synchronize()
     torch.cuda.empty_cache()

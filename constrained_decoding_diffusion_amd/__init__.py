@@ -5,7 +5,7 @@ The C ABI (include/fa.h, libfa.so) does the work; this package marshals
 arguments.  See ``_fa.step`` for one whole step.
 """
 from ._fa import (  # noqa: F401
-    FA_CONF_NEGENT, FA_CONF_PROB, FA_CONF_UNCONSTRAINED, FA_DFA, FA_FIRST_LEVEL_DENSE, FA_FIRST_LEVEL_SPARSE, FA_SECOND_LEVEL_SPARSE, FA_LIVE_STATES,
+    FA_CONF_NEGENT, FA_CONF_PROB, FA_CONF_UNCONSTRAINED, FA_DFA, FA_FIRST_LEVEL_DENSE, FA_FIRST_LEVEL_PAIRS, FA_FIRST_LEVEL_SPARSE, FA_SECOND_LEVEL_SPARSE, FA_LIVE_STATES,
     FA_LABEL_RANGES, FA_NFA, FA_NO_TRIM,
     FA_PROBE_COPY, FA_PROBE_READ,
     FA_PROF_EMISSION_DENSE, FA_PROF_MARG_Q, FA_PROF_NONE, FA_PROF_TREE_LEVEL1,

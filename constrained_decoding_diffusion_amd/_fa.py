@@ -19,6 +19,7 @@ FA_ROW_INFEASIBLE, FA_ROW_UNDERFLOW, FA_ROW_BADPROB = 1, 2, 4
 FA_DFA, FA_NFA, FA_LABEL_RANGES, FA_NO_TRIM = 1, 2, 4, 8
 FA_FIRST_LEVEL_SPARSE, FA_FIRST_LEVEL_DENSE, FA_SECOND_LEVEL_SPARSE = 16, 32, 64
 FA_LIVE_STATES = 128
+FA_FIRST_LEVEL_PAIRS = 256
 FA_CONF_PROB, FA_CONF_NEGENT, FA_CONF_UNCONSTRAINED = 0, 1, 2
 FA_PROF_NONE, FA_PROF_EMISSION_DENSE, FA_PROF_TREE_LEVEL1, FA_PROF_MARG_Q = range(4)
 FA_PROBE_READ, FA_PROBE_COPY = 0, 1
@@ -94,7 +95,7 @@ def _np_ptr(a: np.ndarray):
 INFO_KEYS = ["S", "Sp", "start", "n_accept", "pairs", "list_pairs", "dense_pairs", "range_pairs",
              "list_entries", "segments", "cuts", "sel_tokens", "use_sel", "V", "S_orig",
              "first_sparse", "first_work", "second_sparse", "second_work", "pairs2", "leafless",
-             "leaf_msg_pairs", "live_states"]
+             "leaf_msg_pairs", "live_states", "first_pairs"]
 
 
 class Table:
@@ -126,7 +127,9 @@ class Table:
     def from_automaton(cls, aut, flags=None, first_level="auto", live_states=False):
         """first_level: "auto" (the library's choice), "sparse" (first span
         level from the pair values), "sparse2" (also the second level, from
-        the two-step pattern) or "dense" (dense matrix products).
+        the two-step pattern), "dense" (dense matrix products over dense
+        leaves) or "pairs" (dense matrix products whose operands are staged
+        from the pair values; no dense leaves).
         live_states: FA_LIVE_STATES (span products over the states live at
         their midpoint under each step's p)."""
         if flags is None:
@@ -134,7 +137,7 @@ class Table:
         if live_states:
             flags |= FA_LIVE_STATES
         flags |= {"auto": 0, "sparse": FA_FIRST_LEVEL_SPARSE,
-                  "dense": FA_FIRST_LEVEL_DENSE,
+                  "dense": FA_FIRST_LEVEL_DENSE, "pairs": FA_FIRST_LEVEL_PAIRS,
                   "sparse2": FA_FIRST_LEVEL_SPARSE | FA_SECOND_LEVEL_SPARSE}[first_level]
         return cls(aut.S, aut.V, aut.start, aut.accept, aut.src, aut.dst, aut.label_off,
                    aut.label_tok, flags)

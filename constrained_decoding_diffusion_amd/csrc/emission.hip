@@ -632,7 +632,7 @@ __global__ __launch_bounds__(kLeafThreads) void emission_leaves(DevTable d, Step
     __syncthreads();
     if (pv && real) {
         // the folded entries (value times 2^-rf of its stored row) in the
-        // leaf's stored entry order, for the sparse first span level
+        // leaf's stored entry order, for a first span level from the pairs
         float *pvrow = pv + pos * d.npairs + k0;
         for (int k = tid; k < ne; k += kLeafThreads) {
             const int rc = erc[k];
@@ -653,7 +653,98 @@ __global__ __launch_bounds__(kLeafThreads) void emission_leaves(DevTable d, Step
     }
 }
 
-// Folded entries of every leaf for the sparse first span level, on the path
+// Leaves of a table that keeps no dense leaves (L > 1): only the folded
+// pair values and the row exponents, no dense tile.  One workgroup per
+// leaf: every pair's value is evaluated in parallel in the leaf's stored
+// entry order into LDS, with its row's largest exponent taken by an LDS
+// atomicMax; then the values are written times 2^-rf of their row (what the
+// dense leaf's consumers fold them to) with coalesced stores, in stored
+// order, or with `walk` (the pair-staged first level) in the order that
+// level walks the leaf: column order for a row-major leaf (output o is
+// stored entry col_pairs[o]), pair order for a transposed one (output q is
+// stored entry pair_colpos[q]).  Identity leaves past the sequence end write
+// only their row exponents (those of a diagonal of ones).
+constexpr int kLpThreads = 1024;
+constexpr int kLpUnroll = 4;
+
+__global__ __launch_bounds__(kLpThreads) void emission_leaf_pairs(DevTable d, StepView sv, EmitSrc src,
+                                                                  int32_t *__restrict__ meta,
+                                                                  float *__restrict__ pv, int walk,
+                                                                  int32_t *__restrict__ status)
+{
+    extern __shared__ float lpv[];  // [npairs] values in stored order | [Sp] row exponents
+    const int np = d.npairs;
+    int *remax = reinterpret_cast<int *>(lpv + np);
+    const int tid = threadIdx.x;
+    const int b = blockIdx.x / sv.Lpad, i = blockIdx.x % sv.Lpad;
+    const int h = sv.Lpad + i;
+    const bool tr = stored_transposed(h);
+    const bool real = i < sv.L;
+    const size_t pos = (size_t)b * sv.L + i;
+    for (int r = tid; r < sv.Sp; r += kLpThreads) remax[r] = (!real && r < d.S) ? fexp(1.f) : kNeg;
+    __syncthreads();
+    if (real) {
+        const int32_t *erc = tr ? d.ent_t_rc : d.ent_n_rc;
+        const int32_t *esrc = tr ? d.ent_t_src : d.ent_n_src;
+        const float *direct = d.use_sel ? src.psel + pos * d.nsel : src.p + pos * d.V;
+        const float *indv = src.ndval + pos * d.n_ind;
+        int bad = 0;
+        // kLpUnroll entries per thread in flight: codes first (clamped), then values
+        for (int e0 = 0; e0 < np; e0 += kLpThreads * kLpUnroll) {
+            int code[kLpUnroll], row[kLpUnroll];
+#pragma unroll
+            for (int u = 0; u < kLpUnroll; ++u) {
+                const int e = min(e0 + u * kLpThreads + tid, np - 1);
+                code[u] = esrc[e];
+                row[u] = erc[e] >> 16;
+            }
+#pragma unroll
+            for (int u = 0; u < kLpUnroll; ++u) {
+                const int e = e0 + u * kLpThreads + tid;
+                const float xd = direct[max(code[u], 0)];
+                const float xi = indv[max(-1 - code[u], 0)];
+                const float v = code[u] >= 0 ? xd : xi;
+                if (e < np) {
+                    lpv[e] = v;
+                    if (code[u] >= 0 && !d.use_sel) bad |= !(v >= 0.f);
+                    if (v > 0.f) atomicMax(&remax[row[u]], fexp(v));
+                }
+            }
+        }
+        if (bad) atomicOr(&status[b], (int)FA_ROW_BADPROB);
+    }
+    __syncthreads();
+    if (real) {
+        // output o: stored entry e and its stored row (low half of the walk's codes)
+        const int32_t *perm = tr ? d.pair_colpos : d.col_pairs;
+        const int32_t *orc = walk ? (tr ? d.ent_n_rc : d.ent_t_rc) : nullptr;
+        const int32_t *erc = tr ? d.ent_t_rc : d.ent_n_rc;
+        float *out = pv + pos * np;
+        for (int o0 = 0; o0 < np; o0 += kLpThreads * kLpUnroll) {
+            int e[kLpUnroll], row[kLpUnroll];
+#pragma unroll
+            for (int u = 0; u < kLpUnroll; ++u) {
+                const int o = min(o0 + u * kLpThreads + tid, np - 1);
+                e[u] = walk ? perm[o] : o;
+                row[u] = walk ? (orc[o] & 0xffff) : (erc[o] >> 16);
+            }
+#pragma unroll
+            for (int u = 0; u < kLpUnroll; ++u) {
+                const int o = o0 + u * kLpThreads + tid;
+                if (o < np) out[o] = ldexpf(lpv[e[u]], 0 - remax[row[u]]);
+            }
+        }
+    }
+    int32_t *ro = sv.meta_ptr(meta, b, h, 0), *co = sv.meta_ptr(meta, b, h, 1);
+    int32_t *rf = sv.meta_ptr(meta, b, h, 2);
+    for (int r = tid; r < sv.Sp; r += kLpThreads) {
+        rf[r] = remax[r];
+        ro[r] = 0;
+        co[r] = 0;
+    }
+}
+
+// Folded entries of every leaf for a first span level from the pairs, on the path
 // whose leaves are densified from pair-order values: in the leaf's stored
 // entry order (pair order, or column order for a transposed leaf), each
 // value times 2^-rf of its stored row, as the dense kernels consume it.
@@ -734,9 +825,22 @@ int launch_build_transitions(const DevTable &d, const Geometry &g, const float *
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return (int)e;
         }
+        if (d.leafless && g.K >= 1) {
+            // the table keeps no dense leaves: pair values and row exponents only
+            const size_t lds = ((size_t)d.npairs + g.Sp) * 4;
+            if (lds > 48 * 1024) {
+                const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&emission_leaf_pairs),
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                         (int)lds);
+                if (e != hipSuccess) return (int)e;
+            }
+            emission_leaf_pairs<<<g.B * g.Lpad, kLpThreads, lds, st>>>(d, sv, src, meta, (float *)(ws + w.pvf),
+                                                                      d.first_pairs, status);
+            return (int)hipGetLastError();
+        }
         const int rg = kLeafTile / g.Sp;
         dim3 grid((g.Sp + rg - 1) / rg, g.B * g.Lpad);
-        float *pv = d.first_sparse ? (float *)(ws + w.pvf) : nullptr;
+        float *pv = d.first_sparse || d.first_pairs ? (float *)(ws + w.pvf) : nullptr;
         emission_leaves<<<grid, kLeafThreads, 0, st>>>(d, sv, rg, src, tree, meta, pv, status);
         return (int)hipGetLastError();
     }
@@ -754,7 +858,7 @@ int launch_build_transitions(const DevTable &d, const Geometry &g, const float *
         dim3 grid((g.Sp + 4 * kRowsPerWave - 1) / (4 * kRowsPerWave), g.B * g.Lpad);
         emission_densify<<<grid, kDensifyThreads, 0, st>>>(d, sv, val, tree, meta);
     }
-    if (d.first_sparse && d.npairs > 0 && npos > 0) {
+    if ((d.first_sparse || d.first_pairs) && d.npairs > 0 && npos > 0) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
         dim3 fgrid((d.npairs + 255) / 256, npos);

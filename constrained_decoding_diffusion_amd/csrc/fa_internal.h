@@ -116,6 +116,7 @@ struct DevTable {
     const int32_t *ind_pair;   // [n_ind] pairs whose value is computed (not one direct read)
     int32_t n_ind;
     int32_t first_sparse;        // 1: the first span level is formed from the pair values
+    int32_t first_pairs;         // 1: it is a dense product whose operands are staged from them
     int32_t leafless;            // 1: no dense leaves; every leaf reader takes the pair values
     int32_t second_sparse;       // 1: so is the second, from the two-step pattern
     int32_t live_states;         // 1: dense products contract over the live states (live.hip)
@@ -163,6 +164,7 @@ struct HostTable {
     bool use_sel = false;
     bool selbit = false;
     bool first_sparse = false;  // first span level by row combination over the pairs
+    bool first_pairs = false;   // first span level on the matrix cores, operands from the pairs
     bool leafless = false;      // dense leaves not written (every leaf reader takes pair values)
     int64_t first_work = 0;     // its multiply-adds per product: pairs (a, k) times pairs (k, c)
     // two-step pattern: pairs (a, c) joined by pairs (a, k), (k, c), sorted
@@ -222,7 +224,7 @@ int plan_chunks(const HostTable &t, int32_t B, int32_t L, bool map, StepChunks *
 // Workspace layout (bytes from the start of ws), sized for the largest user.
 struct WsLayout {
     size_t dpart = 0, dval = 0, psel = 0, cutp = 0, val = 0;  // emission reduce
-    size_t pvf = 0;                            // folded leaf pair values (sparse first level)
+    size_t pvf = 0;                            // folded leaf pair values (first level from the pairs)
     size_t pv2 = 0;                            // first-level nodes on the two-step pattern (second level)
     size_t pv2alt = 0;                         // the same values in each node's other walk order
     int32_t n_vchunks = 0;                     // dense-mask contraction: V split

@@ -53,7 +53,7 @@ extern "C" int fa_span_tree_noalloc(const fa_table *t, int32_t B, int32_t L, flo
     if (!t) return FA_EINVAL;
     // a first level formed from the pair values reads what this step's
     // fa_build_transitions left in the caller's workspace: fa_span_tree only
-    if (t->h.first_sparse) return FA_EINVAL;
+    if (t->h.first_sparse || t->h.first_pairs) return FA_EINVAL;
     if (!t->h.dev) return FA_ESTATE;
     StepChunks ck;
     if (int grc = plan_chunks(t->h, B, L, false, &ck)) return grc;

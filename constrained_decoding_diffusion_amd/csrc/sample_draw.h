@@ -117,7 +117,9 @@ __device__ inline void put_pair(const DevTable &d, int a, int c, int32_t *tpair,
 // a factor 2^-rf per leaf that is the same for every candidate) looked up in
 // map_n, or the identity past the sequence end.  The weights are formed as in
 // draw_mid from the same mantissas and exponent differences, so the draw is
-// the one the dense leaves give.
+// the one the dense leaves give.  The values are in each leaf's stored
+// order (pair order left, column order right), or, on a table whose first
+// level is staged from the pairs, in its walk order (the other one).
 __device__ int draw_mid_pairs(const DevTable &d, const StepView &sv, const int32_t *__restrict__ meta,
                               uint64_t seed, int b, int level, int idx, int n, int zl, int zr,
                               int lane, int32_t *__restrict__ status)
@@ -129,15 +131,16 @@ __device__ int draw_mid_pairs(const DevTable &d, const StepView &sv, const int32
     const int32_t *coL = sv.meta_ptr(meta, b, 2 * n, 1);
     const int32_t *coR = sv.meta_ptr(meta, b, 2 * n + 1, 1);
     const size_t Sp = sv.Sp;
+    const bool walk = d.first_pairs != 0;
     auto pl = [&](int k) -> float {
         if (!realL) return k == zl ? 1.f : 0.f;
         const int q = d.map_n[(size_t)zl * Sp + k];
-        return q >= 0 ? vL[q] : 0.f;
+        return q >= 0 ? vL[walk ? d.pair_colpos[q] : q] : 0.f;
     };
-    auto pr = [&](int k) -> float {   // the right leaf's values are in column order
+    auto pr = [&](int k) -> float {
         if (!realR) return k == zr ? 1.f : 0.f;
         const int q = d.map_n[(size_t)k * Sp + zr];
-        return q >= 0 ? vR[d.pair_colpos[q]] : 0.f;
+        return q >= 0 ? vR[walk ? q : d.pair_colpos[q]] : 0.f;
     };
     auto expo = [&](int k) {
         const float a = pl(k), c = pr(k);

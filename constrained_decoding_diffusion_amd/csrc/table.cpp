@@ -119,6 +119,7 @@ DevTable HostTable::device_view() const
     d.has_cnt = has_cnt ? 1 : 0;
     d.selbit = selbit ? 1 : 0;
     d.first_sparse = first_sparse ? 1 : 0;
+    d.first_pairs = first_pairs ? 1 : 0;
     d.leafless = leafless ? 1 : 0;
     const uint8_t *b = static_cast<const uint8_t *>(dev);
     size_t k = 0;
@@ -267,7 +268,7 @@ WsLayout ws_layout(const HostTable &t, const Geometry &g)
     w.ndval = o; o = al(o + (fused ? (BL * t.ind_pair.size() + 1) * sizeof(float) : 0));
     // the folded leaf pair values: read by the sparse first level, and on a
     // leafless table by the leaf-level draws too (so kept through the step)
-    w.pvf = o; o = al(o + (t.first_sparse ? BL * t.npairs() * sizeof(float) : 0));
+    w.pvf = o; o = al(o + (t.first_sparse || t.first_pairs ? BL * t.npairs() * sizeof(float) : 0));
     const size_t a0 = o;
     w.dpart = o; o = al(o + (size_t)w.n_vchunks * BLpad * kDenseMax * sizeof(float));
     w.dval = o; o = al(o + (t.ndense() && !fused ? BL * kDenseMax * sizeof(float) : 0));
@@ -390,9 +391,13 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
     if ((n_accept > 0 && !accept) || (E > 0 && (!src || !dst || !label_off))) return FA_EINVAL;
     if ((flags & FA_DFA) && (flags & FA_NFA)) return FA_EINVAL;
     if (flags & ~uint32_t(FA_DFA | FA_NFA | FA_LABEL_RANGES | FA_NO_TRIM | FA_FIRST_LEVEL_SPARSE |
-                          FA_FIRST_LEVEL_DENSE | FA_SECOND_LEVEL_SPARSE | FA_LIVE_STATES))
+                          FA_FIRST_LEVEL_DENSE | FA_SECOND_LEVEL_SPARSE | FA_LIVE_STATES |
+                          FA_FIRST_LEVEL_PAIRS))
         return FA_EINVAL;
-    if ((flags & FA_FIRST_LEVEL_SPARSE) && (flags & FA_FIRST_LEVEL_DENSE)) return FA_EINVAL;
+    {
+        const uint32_t first = flags & (FA_FIRST_LEVEL_SPARSE | FA_FIRST_LEVEL_DENSE | FA_FIRST_LEVEL_PAIRS);
+        if (first & (first - 1)) return FA_EINVAL;  // at most one first-level form
+    }
     if (E > std::numeric_limits<int32_t>::max()) return FA_ETOOBIG;
     if (E > 0 && label_off[0] != 0) return FA_EINVAL;
     for (int32_t k = 0; k < n_accept; ++k)
@@ -788,14 +793,25 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
     for (int32_t q = 0; q < np; ++q) w1 += t.row_ptr[t.pair_b[q] + 1] - t.row_ptr[t.pair_b[q]];
     t.first_work = w1;
     t.live_states = (flags & FA_LIVE_STATES) != 0;
+    // the dense first level from the pair values: 256x256 tiles, and every
+    // other leaf reader takes the pair values too (so no dense leaf is
+    // written); the live-state products read dense leaves
+    const bool pairs_ok = t.Sp % 256 == 0 && np > 0 && !t.live_states && !t.map_n.empty() &&
+                          leaf_level_from_pairs(np, t.S, t.Sp);
+    t.first_pairs = false;
     if (flags & FA_FIRST_LEVEL_SPARSE) {
         if (t.Sp + t.S > kSparseMaxSpS || np >= kSparseMaxPairs) return FA_ETOOBIG;
         t.first_sparse = true;
     } else if (flags & FA_FIRST_LEVEL_DENSE) {
         t.first_sparse = false;
+    } else if (flags & FA_FIRST_LEVEL_PAIRS) {
+        if (!pairs_ok) return t.live_states ? FA_EINVAL : FA_ETOOBIG;
+        t.first_sparse = false;
+        t.first_pairs = true;
     } else {
         t.first_sparse = t.Sp + t.S <= kSparseMaxSpS && np < kSparseMaxPairs &&
                          (double)kSparseFirstRatio * (double)w1 <= (double)t.Sp * t.Sp * t.Sp;
+        t.first_pairs = !t.first_sparse && pairs_ok;
     }
     t.p2_a.clear(); t.p2_b.clear(); t.p2_row_ptr.clear(); t.p2_col_ptr.clear();
     t.p2_col_pairs.clear(); t.p2_colpos.clear();
@@ -837,11 +853,13 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
     } else if (flags & FA_SECOND_LEVEL_SPARSE) {
         return FA_EINVAL;
     }
-    // no dense leaves when nothing reads them: the first level is sparse,
-    // the message pass's leaf level takes the pair values (LDS-resident
-    // pairs and vectors) and the leaf-level draws look pairs up in map_n
-    // (a one-leaf tree, whose root is the leaf, still writes it)
-    t.leafless = t.first_sparse && np > 0 && !t.map_n.empty() && leaf_level_from_pairs(np, t.S, t.Sp);
+    // no dense leaves when nothing reads them: the first level is sparse or
+    // staged from the pairs, the message pass's leaf level takes the pair
+    // values (LDS-resident pairs and vectors) and the leaf-level draws look
+    // pairs up in map_n (a one-leaf tree, whose root is the leaf, still
+    // writes it)
+    t.leafless = (t.first_sparse || t.first_pairs) && np > 0 && !t.map_n.empty() &&
+                 leaf_level_from_pairs(np, t.S, t.Sp);
     build_image(t);
     return FA_OK;
 }
@@ -888,14 +906,14 @@ extern "C" int fa_table_info(const fa_table *t, int64_t *info, int32_t n)
     const HostTable &h = t->h;
     int32_t nl = 0, nd = 0, nr = 0;
     for (int32_t c : h.pair_cls) (c == kList ? nl : c == kDense ? nd : nr)++;
-    constexpr int32_t kInfo = 23;
+    constexpr int32_t kInfo = 24;
     int64_t v[kInfo] = {h.S, h.Sp, h.start, (int64_t)h.acc.size(), h.npairs(), nl, nd, nr,
                         (int64_t)h.list_tok.size(), h.nseg(), h.ncut(), h.nsel(),
                         h.use_sel ? 1 : 0, h.V, h.S_orig, h.first_sparse ? 1 : 0, h.first_work,
                         h.second_sparse ? 1 : 0, h.second_work, (int64_t)h.p2_a.size(),
                         h.leafless ? 1 : 0,
                         h.npairs() > 0 && leaf_level_from_pairs(h.npairs(), h.S, h.Sp) ? 1 : 0,
-                        h.live_states ? 1 : 0};
+                        h.live_states ? 1 : 0, h.first_pairs ? 1 : 0};
     for (int32_t k = 0; k < n && k < kInfo; ++k) info[k] = v[k];
     return FA_OK;
 }

@@ -31,8 +31,8 @@ namespace {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kTile = 64;        // output tile (rows and columns)
-constexpr int kBK = 32;          // K step staged in LDS
-constexpr int kLdk = kBK + 4;    // padded LDS row (floats)
+constexpr int kBK = 32;          // K step staged in LDS (two MFMA K steps of 16)
+constexpr int kLdb2 = kBK + 8;   // padded LDS row of one bf16 piece
 constexpr int kGemmThreads = 256;
 
 __global__ void tree_init_rf(StepView sv, int32_t *__restrict__ meta)
@@ -95,6 +95,52 @@ __device__ inline int scaled_exp(float x, int c)
     return (x > 0.f) & (c > kNeg) ? ex + c : kNeg;
 }
 
+// The dense span kernels run the fp32 products on the bf16 matrix cores:
+// every folded operand entry x is split, when it is staged, into
+// three bf16 pieces x = h + m + l (round to nearest at each step, so each
+// residual is exact and the pieces hold all 24 bits of x), and the product
+// x y takes the six partial products hh' + hm' + mh' + hl' + mm' + lh'.  The
+// three dropped ones are below 2^-23 |x y| together, and all entries are
+// non-negative, so every output entry keeps that relative bound on top of
+// the fp32 accumulation's rounding: the precision of the fp32 MFMA path at
+// 6/16 of its matrix-core time.  Every kernel adds, per K step of 16, the
+// six products in the same order (by the second operand's piece, then the
+// first's), so a product does not depend on the kernel that forms it.
+constexpr int kBK3 = 16;        // K step per LDS stage of the 128- and 256-tile kernels
+constexpr int kLdb = kBK3 + 8;  // padded LDS row of one piece (bf16 entries)
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+
+// two fp32 values rounded to bf16 (to nearest even), packed low | high
+__device__ inline uint32_t bf16_pair(float a, float b)
+{
+    const f32x2v v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// the three bf16 pieces of four fp32 entries, two per word (h + m + l == x
+// exactly while x is a normal fp32 number of at least 2^-110)
+__device__ inline void split3(float4 x, uint2 &h, uint2 &m, uint2 &l)
+{
+    const float v[4] = {x.x, x.y, x.z, x.w};
+    uint32_t hw[2], mw[2], lw[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const float a = v[2 * u], b = v[2 * u + 1];
+        hw[u] = bf16_pair(a, b);
+        const float ra = a - __uint_as_float(hw[u] << 16), rb = b - __uint_as_float(hw[u] & 0xffff0000u);
+        mw[u] = bf16_pair(ra, rb);
+        const float sa = ra - __uint_as_float(mw[u] << 16), sb = rb - __uint_as_float(mw[u] & 0xffff0000u);
+        lw[u] = bf16_pair(sa, sb);
+    }
+    h = make_uint2(hw[0], hw[1]);
+    m = make_uint2(mw[0], mw[1]);
+    l = make_uint2(lw[0], lw[1]);
+}
+
+
 // One 64x64 output tile of D = X Y^T for node n of row b, over the K range
 // of split blockIdx.x / tiles^2.  With one split the tile is final; with
 // several it is a partial sum written to `part` and added by span_reduce.
@@ -135,8 +181,9 @@ __global__ __launch_bounds__(kGemmThreads) void span_gemm(StepView sv, float *__
     int32_t *coD = sv.meta_ptr(meta, b, n, 1);
     int32_t *rfD = sv.meta_ptr(meta, b, n, 2);
 
-    __shared__ __align__(16) float Fs[2][kTile][kLdk];
-    __shared__ __align__(16) float Gs[2][kTile][kLdk];
+    // per buffer and operand: the pieces h, m, l of 64 stored rows
+    __shared__ __align__(16) __bf16 Fs[2][3][kTile][kLdb2];
+    __shared__ __align__(16) __bf16 Gs[2][3][kTile][kLdb2];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // loader: thread t stages float4 (t & 7) of rows (t >> 3) and (t >> 3) + 32
     // of both operands (the four entries share their column exponents)
@@ -168,21 +215,34 @@ __global__ __launch_bounds__(kGemmThreads) void span_gemm(StepView sv, float *__
         x.cf = *reinterpret_cast<const int4 *>(coF + k_begin + k0 + lk);
         x.cg = *reinterpret_cast<const int4 *>(coG + k_begin + k0 + lk);
     };
-    auto ls = [&](const Blk &x, int buf) {
-        *reinterpret_cast<float4 *>(&Fs[buf][lrow][lk]) = fold4(x.f0, x.cf, rfF0);
-        *reinterpret_cast<float4 *>(&Fs[buf][lrow + 32][lk]) = fold4(x.f1, x.cf, rfF1);
-        *reinterpret_cast<float4 *>(&Gs[buf][lrow][lk]) = fold4(x.g0, x.cg, rfG0);
-        *reinterpret_cast<float4 *>(&Gs[buf][lrow + 32][lk]) = fold4(x.g1, x.cg, rfG1);
+    auto put = [&](__bf16 (*X)[kTile][kLdb2], int row, float4 x) {
+        uint2 h, m, l;
+        split3(x, h, m, l);
+        *reinterpret_cast<uint2 *>(&X[0][row][lk]) = h;
+        *reinterpret_cast<uint2 *>(&X[1][row][lk]) = m;
+        *reinterpret_cast<uint2 *>(&X[2][row][lk]) = l;
     };
+    auto ls = [&](const Blk &x, int buf) {
+        put(Fs[buf], lrow, fold4(x.f0, x.cf, rfF0));
+        put(Fs[buf], lrow + 32, fold4(x.f1, x.cf, rfF1));
+        put(Gs[buf], lrow, fold4(x.g0, x.cg, rfG0));
+        put(Gs[buf], lrow + 32, fold4(x.g1, x.cg, rfG1));
+    };
+    // the block's two K steps of 16, each the six partial products
     auto mm = [&](int buf) {
 #pragma unroll
-        for (int t = 0; t < kBK / 2; t += 4) {
-            const float4 a = *reinterpret_cast<const float4 *>(&Fs[buf][wr + l32][half * (kBK / 2) + t]);
-            const float4 c = *reinterpret_cast<const float4 *>(&Gs[buf][wc + l32][half * (kBK / 2) + t]);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, c.x, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, c.y, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, c.z, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, c.w, acc, 0, 0, 0);
+        for (int t = 0; t < kBK; t += kBK3) {
+            bf16x8 a[3], c[3];
+#pragma unroll
+            for (int pc = 0; pc < 3; ++pc) {
+                a[pc] = *reinterpret_cast<const bf16x8 *>(&Fs[buf][pc][wr + l32][t + half * 8]);
+                c[pc] = *reinterpret_cast<const bf16x8 *>(&Gs[buf][pc][wc + l32][t + half * 8]);
+            }
+#pragma unroll
+            for (int pb = 0; pb < 3; ++pb)
+#pragma unroll
+                for (int pa = 0; pa < 3 - pb; ++pa)
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[pa], c[pb], acc, 0, 0, 0);
         }
     };
     // block bi sits in ring[bi % DEPTH] until it is stored to LDS buffer
@@ -217,9 +277,9 @@ __global__ __launch_bounds__(kGemmThreads) void span_gemm(StepView sv, float *__
     // the operand buffers, free after the loop's last barrier), outer scales
     const int j = tn + wc + l32;
     const int coDj = add_exp(roG[j], rfG[j]);
-    int *E = reinterpret_cast<int *>(&Fs[0][0][0]);  // [kTile][2 * 32 + 4]
+    int *E = reinterpret_cast<int *>(&Fs[0][0][0][0]);  // [kTile][2 * 32 + 4]
     constexpr int ldE = 2 * 32 + 4;
-    static_assert(kTile * ldE <= 2 * kTile * kLdk, "row-maximum exchange fits the operand buffers");
+    static_assert(kTile * ldE * sizeof(int) <= sizeof(Fs), "row-maximum exchange fits the operand buffers");
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int il = wr + (r >> 2) * 8 + half * 4 + (r & 3);
@@ -293,51 +353,6 @@ __global__ __launch_bounds__(kGemmThreads) void span_reduce(StepView sv, float *
     if (tn == 0 && tid < kTile) roD[tm + tid] = add_exp(roF[tm + tid], rfF[tm + tid]);
     if (tm == 0 && tid < kTile) coD[tn + tid] = add_exp(roG[tn + tid], rfG[tn + tid]);
 }
-
-// The 128- and 256-tile kernels run the fp32 products on the bf16 matrix
-// cores: every folded operand entry x is split, when it is staged, into
-// three bf16 pieces x = h + m + l (round to nearest at each step, so each
-// residual is exact and the pieces hold all 24 bits of x), and the product
-// x y takes the six partial products hh' + hm' + mh' + hl' + mm' + lh'.  The
-// three dropped ones are below 2^-23 |x y| together, and all entries are
-// non-negative, so every output entry keeps that relative bound on top of
-// the fp32 accumulation's rounding: the precision of the fp32 MFMA path at
-// 6/16 of its matrix-core time.  LDS stages hold the three pieces of K = 16
-// columns per stored row.
-constexpr int kBK3 = 16;        // K step per LDS stage
-constexpr int kLdb = kBK3 + 8;  // padded LDS row of one piece (bf16 entries)
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x2v __attribute__((ext_vector_type(2)));
-
-// two fp32 values rounded to bf16 (to nearest even), packed low | high
-__device__ inline uint32_t bf16_pair(float a, float b)
-{
-    const f32x2v v = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-
-// the three bf16 pieces of four fp32 entries, two per word (h + m + l == x
-// exactly while x is a normal fp32 number of at least 2^-110)
-__device__ inline void split3(float4 x, uint2 &h, uint2 &m, uint2 &l)
-{
-    const float v[4] = {x.x, x.y, x.z, x.w};
-    uint32_t hw[2], mw[2], lw[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const float a = v[2 * u], b = v[2 * u + 1];
-        hw[u] = bf16_pair(a, b);
-        const float ra = a - __uint_as_float(hw[u] << 16), rb = b - __uint_as_float(hw[u] & 0xffff0000u);
-        mw[u] = bf16_pair(ra, rb);
-        const float sa = ra - __uint_as_float(mw[u] << 16), sb = rb - __uint_as_float(mw[u] & 0xffff0000u);
-        lw[u] = bf16_pair(sa, sb);
-    }
-    h = make_uint2(hw[0], hw[1]);
-    m = make_uint2(mw[0], mw[1]);
-    l = make_uint2(lw[0], lw[1]);
-}
-
 
 constexpr int kBig = 128;       // output tile of the large-level kernel
 constexpr int kBigThreads = 512;
@@ -520,6 +535,125 @@ __global__ void tree_logz_empty(DevTable d, int B, double *__restrict__ logZ,
     if (!ok) atomicOr(&status[b], (int)FA_ROW_INFEASIBLE);
 }
 
+constexpr int kHuge = 256;
+constexpr int kHugeThreads = 512;
+
+// The tiles of one 256x256-tile launch: products n0 .. n0+nn-1 of every
+// batch row, each of (Sp/256)^2 tiles.  With several tiles per product, the
+// tiles that run on one XCD (every eighth workgroup) are consecutive ones,
+// which share operand rows in L2.
+struct HugeWork {
+    int Sp, tiles, per_prod, nwork, full, n0, nn;
+    __device__ HugeWork(const StepView &sv, int n0_, int nn_)
+        : Sp(sv.Sp), tiles(sv.Sp / 256), per_prod((sv.Sp / 256) * (sv.Sp / 256)),
+          nwork(sv.B * nn_ * (sv.Sp / 256) * (sv.Sp / 256)), full(0), n0(n0_), nn(nn_)
+    {
+        full = nwork & ~7;
+    }
+    __device__ int work(int v) const
+    {
+        return (per_prod > 1 && v < full) ? (v & 7) * (full >> 3) + (v >> 3) : v;
+    }
+    // tile v: batch row, node, first output row and column
+    __device__ void node_of(int v, int &b, int &n, int &tm, int &tn) const
+    {
+        const int w = work(v);
+        const int prod = w / per_prod, tile = w % per_prod;
+        tm = (tile / tiles) * 256;
+        tn = (tile % tiles) * 256;
+        b = prod / nn;
+        n = n0 + prod % nn;
+    }
+};
+
+// Epilogue of a 256x256 output tile held by 8 waves of 64 x 128 (2 x 4
+// tiles of 32x32): D, and per row the largest e(D[i][j]) + coD[j], reduced
+// through E0 (the waves of columns 0..127) and E1 (128..255), two LDS
+// regions of 256 x kLde ints that are free until the caller's next barrier;
+// the first tile row / column also writes coD / roD.  All 512 threads call
+// it (it holds a barrier).
+constexpr int kLde = 36;
+
+__device__ __forceinline__ void huge_epilogue(const StepView &sv, float *__restrict__ tree,
+                                              int32_t *__restrict__ meta, f32x16 (&acc)[2][4],
+                                              int *E0, int *E1, int b, int n, int tm, int tn,
+                                              const int32_t *rfF, const int32_t *rfG)
+{
+    const int Sp = sv.Sp;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = (wave >> 1) * 64, wc = (wave & 1) * 128;
+    const int l32 = lane & 31, half = lane >> 5;
+    const bool tr = stored_transposed(n);
+    const int hF = tr ? 2 * n + 1 : 2 * n, hG = tr ? 2 * n : 2 * n + 1;
+    const int32_t *roF = sv.meta_ptr((const int32_t *)meta, b, hF, 0);
+    const int32_t *roG = sv.meta_ptr((const int32_t *)meta, b, hG, 0);
+    float *D = sv.mat_ptr(tree, b, n);
+    // this lane's first row and column in the tile; the empty asm keeps
+    // the addresses derived from them out of the tile loop (where they
+    // would stay live through the MFMAs)
+    int row0 = wr + half * 4, col0 = wc + l32;
+    asm volatile("" : "+v"(row0), "+v"(col0));
+    // every exponent the epilogue needs is loaded first, so that one
+    // load latency covers them all and the stores of D go out meanwhile
+    int coDj[4];
+#pragma unroll
+    for (int cy = 0; cy < 4; ++cy) {
+        const int j = tn + col0 + 32 * cy;
+        coDj[cy] = add_exp(roG[j], rfG[j]);
+    }
+    int outer = kNeg;  // roD[tm + tid] (tid < 256) or coD[tn + tid - 256]
+    if (tid < 256) {
+        if (tn == 0) outer = add_exp(roF[tm + tid], rfF[tm + tid]);
+    } else if (tm == 0) {
+        outer = add_exp(roG[tn + tid - 256], rfG[tn + tid - 256]);
+    }
+#pragma unroll
+    for (int ry = 0; ry < 2; ++ry)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+#pragma unroll
+            for (int cy = 0; cy < 4; ++cy)
+                __builtin_nontemporal_store(acc[ry][cy][r],
+                                            &D[(size_t)(tm + row0 + 32 * ry + (r >> 2) * 8 + (r & 3)) * Sp +
+                                               tn + col0 + 32 * cy]);
+    // per row the maximum over this lane's four columns: E[il][l32] of the
+    // wave's column half, rows padded to kLde entries
+    int *E = wc == 0 ? E0 : E1;
+#pragma unroll
+    for (int ry = 0; ry < 2; ++ry) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            int e = kNeg;
+#pragma unroll
+            for (int cy = 0; cy < 4; ++cy) {
+                const float x = acc[ry][cy][r];
+                int ex;
+                frexpf(x, &ex);
+                const bool ok = (x > 0.f) & (coDj[cy] > kNeg);
+                e = max(e, ok ? ex + coDj[cy] : kNeg);
+            }
+            E[(row0 + 32 * ry + (r >> 2) * 8 + (r & 3)) * kLde + l32] = e;
+        }
+    }
+    __syncthreads();
+    if (tid < 256) {
+        const int4 *e0 = reinterpret_cast<const int4 *>(E0 + tid * kLde);
+        const int4 *e1 = reinterpret_cast<const int4 *>(E1 + tid * kLde);
+        int e = kNeg;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int4 x = e0[k], y = e1[k];
+            e = max(e, max(max(max(x.x, x.y), max(x.z, x.w)), max(max(y.x, y.y), max(y.z, y.w))));
+        }
+        int32_t *rfD = sv.meta_ptr(meta, b, n, 2);
+        if (Sp == 256) rfD[tm + tid] = e;
+        else if (e > kNeg) atomicMax(&rfD[tm + tid], e);
+        if (tn == 0) sv.meta_ptr(meta, b, n, 0)[tm + tid] = outer;
+    } else if (tm == 0) {
+        sv.meta_ptr(meta, b, n, 1)[tn + tid - 256] = outer;
+    }
+}
+
 // Large levels with 256x256 output tiles (one whole product when Sp = 256),
 // one persistent workgroup per CU walking tiles v = blockIdx.x + k gridDim.x:
 // 8 waves of 64 x 128 (2 x 4 MFMA tiles of 32x32), double-buffered LDS
@@ -530,8 +664,6 @@ __global__ void tree_logz_empty(DevTable d, int B, double *__restrict__ logZ,
 // tile starts from a filled buffer while the current one is stored.  Row
 // exponents are reduced inside the workgroup through the free LDS buffer:
 // one store (full rows) or atomicMax (several column tiles) per row.
-constexpr int kHuge = 256;
-constexpr int kHugeThreads = 512;
 // the operand side of one 256x256 tile: stored rows tm.. of F, tn.. of G
 struct HugeSrc {
     const float *F, *G;
@@ -552,23 +684,11 @@ __global__ __launch_bounds__(kHugeThreads) void span_gemm256(StepView sv, float 
                                                              const int32_t *__restrict__ nlive)
 {
     const int Sp = sv.Sp;
-    const int tiles = Sp / kHuge;
-    const int per_prod = tiles * tiles;
-    const int nwork = sv.B * nn * per_prod;
-    const int full = nwork & ~7;
-    // with several tiles per product, the tiles that run on one XCD (every
-    // eighth workgroup) are consecutive ones, which share operand rows in L2
-    auto work = [&](int v) { return (per_prod > 1 && v < full) ? (v & 7) * (full >> 3) + (v >> 3) : v; };
-    auto node_of = [&](int w, int &b, int &n, int &tm, int &tn) {
-        const int prod = w / per_prod, tile = w % per_prod;
-        tm = (tile / tiles) * kHuge;
-        tn = (tile % tiles) * kHuge;
-        b = prod / nn;
-        n = n0 + prod % nn;
-    };
+    const HugeWork hw(sv, n0, nn);
+    const int nwork = hw.nwork;
     auto src_of = [&](int v) {
         int b, n, tm, tn;
-        node_of(work(v), b, n, tm, tn);
+        hw.node_of(v, b, n, tm, tn);
         const bool tr = stored_transposed(n);
         const int hF = tr ? 2 * n + 1 : 2 * n, hG = tr ? 2 * n : 2 * n + 1;
         HugeSrc s;
@@ -733,81 +853,13 @@ __global__ __launch_bounds__(kHugeThreads) void span_gemm256(StepView sv, float 
             lstore(st, 0);
             __syncthreads();
         }
-        // epilogue: D, and per row the largest e(D[i][j]) + coD[j]
+        // epilogue, the row maxima through buffer 1 (free until the next
+        // tile's first store into it)
         int b, n, tm, tn;
-        node_of(work(v), b, n, tm, tn);
-        const bool tr = stored_transposed(n);
-        const int hF = tr ? 2 * n + 1 : 2 * n, hG = tr ? 2 * n : 2 * n + 1;
-        const int32_t *roF = sv.meta_ptr((const int32_t *)meta, b, hF, 0);
-        const int32_t *roG = sv.meta_ptr((const int32_t *)meta, b, hG, 0);
-        float *D = sv.mat_ptr(tree, b, n);
-        // this lane's first row and column in the tile; the empty asm keeps
-        // the addresses derived from them out of the tile loop (where they
-        // would stay live through the MFMAs)
-        int row0 = wr + half * 4, col0 = wc + l32;
-        asm volatile("" : "+v"(row0), "+v"(col0));
-        // every exponent the epilogue needs is loaded first, so that one
-        // load latency covers them all and the stores of D go out meanwhile
-        int coDj[4];
-#pragma unroll
-        for (int cy = 0; cy < 4; ++cy) {
-            const int j = tn + col0 + 32 * cy;
-            coDj[cy] = add_exp(roG[j], cur.rfG[j]);
-        }
-        int outer = kNeg;  // roD[tm + tid] (tid < 256) or coD[tn + tid - 256]
-        if (tid < kHuge) {
-            if (tn == 0) outer = add_exp(roF[tm + tid], cur.rfF[tm + tid]);
-        } else if (tm == 0) {
-            outer = add_exp(roG[tn + tid - kHuge], cur.rfG[tn + tid - kHuge]);
-        }
-#pragma unroll
-        for (int ry = 0; ry < 2; ++ry)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-#pragma unroll
-                for (int cy = 0; cy < 4; ++cy)
-                    __builtin_nontemporal_store(acc[ry][cy][r],
-                                                &D[(size_t)(tm + row0 + 32 * ry + (r >> 2) * 8 + (r & 3)) * Sp +
-                                                   tn + col0 + 32 * cy]);
-        // per row the maximum over this lane's four columns, into buffer 1
-        // (free until the next tile's first store into it): E[il][l32] of
-        // the wave's column half, rows padded to kLde entries
-        constexpr int kLde = 36;
+        hw.node_of(v, b, n, tm, tn);
         static_assert(kHuge * kLde * sizeof(int) <= sizeof(Fs[1]), "row-maximum exchange fits one buffer");
-        int *E = reinterpret_cast<int *>(wc == 0 ? &Fs[1][0][0][0] : &Gs[1][0][0][0]);
-#pragma unroll
-        for (int ry = 0; ry < 2; ++ry) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                int e = kNeg;
-#pragma unroll
-                for (int cy = 0; cy < 4; ++cy) {
-                    const float x = acc[ry][cy][r];
-                    int ex;
-                    frexpf(x, &ex);
-                    const bool ok = (x > 0.f) & (coDj[cy] > kNeg);
-                    e = max(e, ok ? ex + coDj[cy] : kNeg);
-                }
-                E[(row0 + 32 * ry + (r >> 2) * 8 + (r & 3)) * kLde + l32] = e;
-            }
-        }
-        __syncthreads();
-        if (tid < kHuge) {
-            const int4 *e0 = reinterpret_cast<const int4 *>(reinterpret_cast<const int *>(&Fs[1][0][0][0]) + tid * kLde);
-            const int4 *e1 = reinterpret_cast<const int4 *>(reinterpret_cast<const int *>(&Gs[1][0][0][0]) + tid * kLde);
-            int e = kNeg;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int4 x = e0[k], y = e1[k];
-                e = max(e, max(max(max(x.x, x.y), max(x.z, x.w)), max(max(y.x, y.y), max(y.z, y.w))));
-            }
-            int32_t *rfD = sv.meta_ptr(meta, b, n, 2);
-            if (tiles == 1) rfD[tm + tid] = e;
-            else if (e > kNeg) atomicMax(&rfD[tm + tid], e);
-            if (tn == 0) sv.meta_ptr(meta, b, n, 0)[tm + tid] = outer;
-        } else if (tm == 0) {
-            sv.meta_ptr(meta, b, n, 1)[tn + tid - kHuge] = outer;
-        }
+        huge_epilogue(sv, tree, meta, acc, reinterpret_cast<int *>(&Fs[1][0][0][0]),
+                      reinterpret_cast<int *>(&Gs[1][0][0][0]), b, n, tm, tn, cur.rfF, cur.rfG);
         if (!more) break;
         __syncthreads();  // buffer 1 is read above and written by the next tile
         v = vn;
@@ -815,6 +867,211 @@ __global__ __launch_bounds__(kHugeThreads) void span_gemm256(StepView sv, float 
     }
 }
 
+
+// The first level as the dense product of 256x256 tiles, its operands
+// staged from the leaves' folded pair values (value times 2^-rf of its
+// stored row, as fa_build_transitions leaves them in the workspace) instead
+// of dense leaves: a K step of 16 stored columns holds the entries of the
+// pairs whose stored column lies in it, zeros elsewhere, which are the
+// values the dense kernel folds from a dense leaf (an identity leaf past the
+// sequence end: 2^-rf on its diagonal).  A row-major leaf is walked in
+// column order (col_ptr, ent_t_rc), a transposed one in pair order
+// (row_ptr, ent_n_rc), both giving (stored column << 16 | stored row); the
+// values are stored in that walk order, so entry e of a step and its value
+// are two independent loads.
+//
+// LDS: a ring of three slots of both operands' three bf16 pieces (rows of
+// 16 entries, 32 bytes, the two 16-byte halves swapped on rows with bit 3
+// set so that the fragment reads of 16 lanes hit distinct banks).  During K
+// step s the MFMAs read slot s % 3 while slot (s+2) % 3 is cleared and the
+// entries of step s+1 (loaded before the MFMAs) are written into slot
+// (s+1) % 3, cleared during step s-1: one barrier per step.  Each thread
+// holds kPvPer entries per operand and step; more are read when written.
+// The MFMAs, their order and the epilogue are those of span_gemm256, so the
+// products equal the dense-leaf ones bit for bit.
+constexpr int kPvSlots = 3;
+constexpr int kPvPer = 2;
+constexpr int kPvMaxSteps = kMapMaxSp / kBK3;  // Sp <= kMapMaxSp (the pair maps exist)
+
+struct PvOperand {
+    const int32_t *rc;   // walk order: stored (column << 16 | row)
+    const float *pv;     // walk order: the leaf's folded values; nullptr for an identity leaf
+    const int32_t *rf;   // the leaf's row exponents
+    const int *wofs;     // LDS: walk offset of each K step's first column, [steps + 1]
+    int t0;              // first stored row of the tile
+};
+
+// the held entries of one operand and K step
+struct PvHeld {
+    int rc[kPvPer];
+    float v[kPvPer];
+};
+
+__device__ inline int pv_swz(int row, int col) { return row * kBK3 + (col ^ (((row >> 3) & 1) << 3)); }
+
+__global__ __launch_bounds__(kHugeThreads) void span_pairs256(DevTable d, StepView sv,
+                                                              float *__restrict__ tree,
+                                                              int32_t *__restrict__ meta,
+                                                              const float *__restrict__ pvf, int n0,
+                                                              int nn)
+{
+    const int Sp = sv.Sp;
+    const HugeWork hw(sv, n0, nn);
+    const int nk = Sp / kBK3;
+    // [slot][operand][piece][row][16]
+    __shared__ __align__(16) __bf16 Ls[kPvSlots][2][3][kHuge * kBK3];
+    __shared__ int wofs_t[kPvMaxSteps + 1], wofs_n[kPvMaxSteps + 1];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = (wave >> 1) * 64, wc = (wave & 1) * 128;
+    const int l32 = lane & 31, half = lane >> 5;
+    for (int j = tid; j <= nk; j += kHugeThreads) {
+        const int c = min(j * kBK3, d.S);
+        wofs_t[j] = d.col_ptr[c];
+        wofs_n[j] = d.row_ptr[c];
+    }
+    int v = blockIdx.x;
+    if (v >= hw.nwork) return;
+
+    auto operand = [&](int b, int h, int t0) {
+        PvOperand o;
+        const int i = h - sv.Lpad;  // position of the leaf
+        const bool tr = stored_transposed(h);
+        o.rc = tr ? d.ent_n_rc : d.ent_t_rc;
+        o.pv = i < sv.L ? pvf + ((size_t)b * sv.L + i) * d.npairs : nullptr;
+        o.rf = sv.meta_ptr((const int32_t *)meta, b, h, 2);
+        o.wofs = tr ? wofs_n : wofs_t;
+        o.t0 = t0;
+        return o;
+    };
+    auto load = [&](const PvOperand &o, int ks, PvHeld &x) {
+        const int e0 = o.wofs[ks], e1 = o.wofs[ks + 1];
+#pragma unroll
+        for (int u = 0; u < kPvPer; ++u) {
+            const int e = e0 + tid + u * kHugeThreads;
+            const bool ok = o.pv != nullptr && e < e1;
+            const int ec = ok ? e : 0;
+            const int rc = o.rc[ec];
+            const float v = o.pv ? o.pv[ec] : 0.f;
+            x.rc[u] = ok ? rc : -1;
+            x.v[u] = v;
+        }
+    };
+    auto put1 = [&](__bf16 *X, int row, int col, float x) {
+        const __bf16 h = (__bf16)x;
+        const float r = x - (float)h;
+        const __bf16 m = (__bf16)r;
+        const int a = pv_swz(row, col);
+        X[a] = h;
+        X[kHuge * kBK3 + a] = m;
+        X[2 * kHuge * kBK3 + a] = (__bf16)(r - (float)m);
+    };
+    // the entries of K step ks into slot sl: the held ones, then any beyond
+    // kPvPer per thread, or the identity's diagonal
+    auto scatter = [&](const PvOperand &o, int opi, int sl, int ks, const PvHeld &x) {
+        __bf16 *X = &Ls[sl][opi][0][0];
+        const int k0 = ks * kBK3;
+        if (o.pv) {
+#pragma unroll
+            for (int u = 0; u < kPvPer; ++u) {
+                const int rc = x.rc[u];
+                const int row = (rc & 0xffff) - o.t0;
+                if (rc >= 0 && (unsigned)row < (unsigned)kHuge) put1(X, row, (rc >> 16) - k0, x.v[u]);
+            }
+            const int e1 = o.wofs[ks + 1];
+            for (int e = o.wofs[ks] + tid + kPvPer * kHugeThreads; e < e1; e += kHugeThreads) {
+                const int rc = o.rc[e];
+                const int row = (rc & 0xffff) - o.t0;
+                if ((unsigned)row < (unsigned)kHuge) put1(X, row, (rc >> 16) - k0, o.pv[e]);
+            }
+        } else if (tid < kBK3) {
+            const int k = k0 + tid, row = k - o.t0;
+            if (k < d.S && (unsigned)row < (unsigned)kHuge) put1(X, row, tid, ldexpf(1.f, 0 - o.rf[k]));
+        }
+    };
+    auto clear = [&](int sl) {
+        uint4 *z = reinterpret_cast<uint4 *>(&Ls[sl][0][0][0]);
+        constexpr int n16 = (int)(sizeof(Ls[0]) / sizeof(uint4));
+        static_assert(n16 % kHugeThreads == 0, "one slot clears in whole rounds");
+#pragma unroll
+        for (int k = 0; k < n16 / kHugeThreads; ++k) z[tid + k * kHugeThreads] = make_uint4(0u, 0u, 0u, 0u);
+    };
+    f32x16 acc[2][4];
+    auto mfmas = [&](int sl) {
+        const __bf16 *F = &Ls[sl][0][0][0], *G = &Ls[sl][1][0][0];
+        bf16x8 a[3][2], c[4];
+#pragma unroll
+        for (int pa = 0; pa < 3; ++pa)
+#pragma unroll
+            for (int ry = 0; ry < 2; ++ry) {
+                const int row = wr + 32 * ry + l32;
+                a[pa][ry] = *reinterpret_cast<const bf16x8 *>(F + pa * kHuge * kBK3 + pv_swz(row, half * 8));
+            }
+#pragma unroll
+        for (int pb = 0; pb < 3; ++pb) {
+#pragma unroll
+            for (int cy = 0; cy < 4; ++cy) {
+                const int row = wc + 32 * cy + l32;
+                c[cy] = *reinterpret_cast<const bf16x8 *>(G + pb * kHuge * kBK3 + pv_swz(row, half * 8));
+            }
+#pragma unroll
+            for (int pa = 0; pa < 3 - pb; ++pa)
+#pragma unroll
+                for (int ry = 0; ry < 2; ++ry)
+#pragma unroll
+                    for (int cy = 0; cy < 4; ++cy)
+                        acc[ry][cy] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[pa][ry], c[cy], acc[ry][cy],
+                                                                              0, 0, 0);
+        }
+    };
+
+    for (;;) {
+        int b, n, tm, tn;
+        hw.node_of(v, b, n, tm, tn);
+        const bool tr = stored_transposed(n);
+        const int hF = tr ? 2 * n + 1 : 2 * n, hG = tr ? 2 * n : 2 * n + 1;
+        const PvOperand oF = operand(b, hF, tm), oG = operand(b, hG, tn);
+#pragma unroll
+        for (int ry = 0; ry < 2; ++ry)
+#pragma unroll
+            for (int cy = 0; cy < 4; ++cy)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[ry][cy][r] = 0.f;
+        // prologue: slots 0 and 1 cleared, step 0 written into slot 0
+        PvHeld xF, xG;
+        clear(0);
+        clear(1);
+        __syncthreads();  // the window offsets, and the clears
+        load(oF, 0, xF);
+        load(oG, 0, xG);
+        scatter(oF, 0, 0, 0, xF);
+        scatter(oG, 1, 0, 0, xG);
+        __syncthreads();
+        for (int ks = 0; ks < nk; ++ks) {
+            const bool nxt = ks + 1 < nk;
+            if (nxt) {  // the entries of step ks+1, in flight during the MFMAs
+                load(oF, ks + 1, xF);
+                load(oG, ks + 1, xG);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(ks % 3);
+            __builtin_amdgcn_sched_barrier(0);
+            clear((ks + 2) % 3);
+            if (nxt) {
+                scatter(oF, 0, (ks + 1) % 3, ks + 1, xF);
+                scatter(oG, 1, (ks + 1) % 3, ks + 1, xG);
+            }
+            __syncthreads();
+        }
+        // epilogue, the row maxima through slots 0 and 1 (every slot is
+        // free after the last step's barrier)
+        static_assert(kHuge * kLde * sizeof(int) <= sizeof(Ls[0]), "row-maximum exchange fits one slot");
+        huge_epilogue(sv, tree, meta, acc, reinterpret_cast<int *>(&Ls[0][0][0][0]),
+                      reinterpret_cast<int *>(&Ls[1][0][0][0]), b, n, tm, tn, oF.rf, oG.rf);
+        v += (int)gridDim.x;
+        if (v >= hw.nwork) break;
+        __syncthreads();  // slots 0 and 1 are read above and cleared by the next tile
+    }
+}
 
 // Sparse levels.  A leaf holds one value per pair (a, b) of the automaton,
 // so a first-level product is a row combination: stored row s of node n is
@@ -1312,7 +1569,12 @@ int launch_span_tree(const DevTable &d, const Geometry &g, float *tree, int32_t 
             if (pe) return pe;
         }
         int e = 0;
-        if (k == 1 && sparse1) {
+        if (k == 1 && d.first_pairs && d.npairs > 0) {
+            const long long wgs = (long long)g.B * nn * (g.Sp / kHuge) * (g.Sp / kHuge);
+            const unsigned grid = (unsigned)std::min<long long>(wgs, device_cus());
+            span_pairs256<<<grid, kHugeThreads, 0, st>>>(d, sv, tree, meta, pvf, n0, nn);
+            e = (int)hipGetLastError();
+        } else if (k == 1 && sparse1) {
             SpLevel lv{};
             lv.in = pattern1(d);
             if (nsp2 > 0) lv.out = pattern2(d);

@@ -85,7 +85,9 @@ enum {
     FA_FIRST_LEVEL_DENSE = 32,  /* first span level as dense matrix products */
     FA_SECOND_LEVEL_SPARSE = 64, /* also the second level from the two-step pattern (needs the
                                     first level sparse) */
-    FA_LIVE_STATES = 128 /* span products over the states live at their midpoint (see fa_span_tree) */
+    FA_LIVE_STATES = 128, /* span products over the states live at their midpoint (see fa_span_tree) */
+    FA_FIRST_LEVEL_PAIRS = 256 /* first span level as dense matrix products whose operands are
+                                  staged from the pair values (no dense leaves) */
 };
 
 enum { FA_CONF_PROB = 0, FA_CONF_NEGENT = 1, FA_CONF_UNCONSTRAINED = 2 };
@@ -104,9 +106,15 @@ enum { FA_CONF_PROB = 0, FA_CONF_NEGENT = 1, FA_CONF_UNCONSTRAINED = 2 };
  *                   once), or with FA_LABEL_RANGES flat [lo, hi) pairs with
  *                   0 <= lo <= hi <= V, disjoint within one edge
  *   flags           FA_DFA | FA_NFA | FA_LABEL_RANGES | FA_NO_TRIM, and at
- *                   most one of FA_FIRST_LEVEL_SPARSE / FA_FIRST_LEVEL_DENSE
- *                   (how fa_span_tree forms the first level; default: the
- *                   sparse form when its work is at most 1/256 of S^3), and
+ *                   most one of FA_FIRST_LEVEL_SPARSE / FA_FIRST_LEVEL_DENSE /
+ *                   FA_FIRST_LEVEL_PAIRS (how fa_span_tree forms the first
+ *                   level; default: the sparse form when its work is at
+ *                   most 1/256 of S^3, else the pair-staged dense form when
+ *                   the table allows it (Sp a multiple of 256, Sp <= 2048,
+ *                   no FA_LIVE_STATES, the pairs fit the message pass's
+ *                   pair-value leaf level: FA_ETOOBIG when forced without
+ *                   that, FA_EINVAL with FA_LIVE_STATES), else dense
+ *                   products over dense leaves), and
  *                   FA_SECOND_LEVEL_SPARSE (the second level likewise, over
  *                   the pairs (a, c) joined through some k; default: when
  *                   the first is sparse and its own work is at most 1/256 of
@@ -147,11 +155,12 @@ void fa_table_destroy(fa_table *t);
  * number of pairs (a, k), (k, c) sharing k), [17] 1 if the second level is
  * formed likewise, [18] its multiply-adds per product, [19] the pairs of the
  * two-step pattern it uses, [20] 1 if the step keeps no dense leaves (the
- * first level is sparse, and the message pass's leaf level and the leaf-level
- * midpoint draws read the pair values), [21] 1 if the message pass's leaf
- * level (L > 1) reads the pair values instead of the dense leaves, [22] 1
- * if the table was compiled with FA_LIVE_STATES.  Returns FA_OK or
- * FA_EINVAL.
+ * first level is sparse or pair-staged, and the message pass's leaf level and
+ * the leaf-level midpoint draws read the pair values), [21] 1 if the message
+ * pass's leaf level (L > 1) reads the pair values instead of the dense
+ * leaves, [22] 1 if the table was compiled with FA_LIVE_STATES, [23] 1 if
+ * the first level is a dense product with operands staged from the pair
+ * values.  Returns FA_OK or FA_EINVAL.
  */
 int fa_table_info(const fa_table *t, int64_t *info, int32_t n);
 
@@ -186,7 +195,8 @@ int fa_sizes(const fa_table *t, int32_t B, int32_t L, size_t *tree_bytes, size_t
  *            negative entries that are read set FA_ROW_BADPROB)
  *   tree     device, fa_sizes bytes; leaves written, except on a table
  *            whose every leaf reader takes the pair values (fa_table_info
- *            [20]; the first span level then sparse) when L > 1
+ *            [20]; the first span level then sparse or pair-staged) when
+ *            L > 1
  *   meta     device, fa_sizes bytes; leaf exponents written
  *   ws       device workspace of ws_bytes >= fa_sizes; keeps, for the step's
  *            fa_marginals, the compact copy of p at token-list tokens and the
@@ -220,7 +230,12 @@ int fa_build_transitions(const fa_table *t, const float *p, int32_t B, int32_t L
  *               With FA_SECOND_LEVEL_SPARSE (or chosen likewise) the second
  *               level is formed the same way over the pairs (a, c) joined
  *               through some k, for its products whose four leaves lie
- *               inside the sequence.  With FA_LIVE_STATES the call first
+ *               inside the sequence.  With FA_FIRST_LEVEL_PAIRS (or
+ *               chosen likewise) the first level is the dense product,
+ *               each K step of its operands built in LDS from the leaves'
+ *               folded pair values in ws (zeros elsewhere): the same
+ *               operands as from dense leaves, and the same products bit
+ *               for bit.  With FA_LIVE_STATES the call first
  *               finds, per row and boundary, the states reachable from s0
  *               and able to reach F through transitions of positive value
  *               (a forward and a backward pass over the positions), and
@@ -441,8 +456,8 @@ int fa_commit(int32_t B, int32_t L, int32_t V, const float *conf, const int32_t 
  * on one GPU (different streams, or different threads) race and must not be
  * issued.  The array is fully written before it is read by each call.
  * Errors: FA_EINVAL (also for a table whose first span level is formed from
- * the pair values, fa_table_info [15] = 1: that level reads the workspace
- * fa_build_transitions wrote, so such tables take fa_span_tree),
+ * the pair values, fa_table_info [15] = 1 or [23] = 1: that level reads the
+ * workspace fa_build_transitions wrote, so such tables take fa_span_tree),
  * FA_ETOOBIG (the step's partial tiles exceed FA_SPAN_TREE_NOALLOC_MAX_BYTES,
  * or the grid limits of fa_span_tree), FA_ESTATE, FA_EHIP.
  */

@@ -66,7 +66,7 @@ def test_invalid_ranges_and_flags():
     assert _code(lambda: _compile(2, 10, 0, [1], [(0, 1, [0, 11])], R)) == _fa.FA_EINVAL
     assert _code(lambda: _compile(2, 10, 0, [1], [(0, 1, [0, 5, 3, 7])], R)) == _fa.FA_EINVAL
     assert _code(lambda: _compile(2, 10, 0, [1], [(0, 1, [1])], fa.FA_DFA | fa.FA_NFA)) == _fa.FA_EINVAL
-    assert _code(lambda: _compile(2, 10, 0, [1], [(0, 1, [1])], 256)) == _fa.FA_EINVAL
+    assert _code(lambda: _compile(2, 10, 0, [1], [(0, 1, [1])], 1 << 10)) == _fa.FA_EINVAL
     # the sparse second level needs the sparse first level
     assert _code(lambda: _compile(2, 10, 0, [1], [(0, 1, [1])], fa.FA_DFA | fa.FA_FIRST_LEVEL_DENSE
                                   | fa.FA_SECOND_LEVEL_SPARSE)) == _fa.FA_EINVAL
@@ -106,6 +106,33 @@ def test_first_level_flags_and_choice():
     assert _code(lambda: _compile(16401, 2, 0, [16400], big,
                                   fa.FA_DFA | fa.FA_FIRST_LEVEL_SPARSE)) == _fa.FA_ETOOBIG
     assert _compile(16401, 2, 0, [16400], big, fa.FA_DFA).info["first_sparse"] == 0
+
+
+def test_pair_staged_first_level():
+    """The dense first level staged from the pair values: chosen when the
+    sparse form's work is too large and the table allows it (Sp a multiple
+    of 256, the pairs fit the pair-value leaf level, no live states); such a
+    table keeps no dense leaves.  Forced where it cannot run: FA_ETOOBIG, or
+    FA_EINVAL with FA_LIVE_STATES or another first-level flag."""
+    S, fan = 200, 40
+    edges = [(s, (13 * s + 17 * j + 1) % S, [s * fan + j]) for s in range(S) for j in range(fan)]
+    mk = lambda f: _compile(S, S * fan, 0, [S - 1], edges, fa.FA_DFA | f)
+    t = mk(0)
+    assert t.info["Sp"] == 256 and t.info["first_work"] > 256 ** 3 // 256
+    assert t.info["first_pairs"] == 1 and t.info["first_sparse"] == 0 and t.info["leafless"] == 1
+    assert mk(fa.FA_FIRST_LEVEL_PAIRS).info["first_pairs"] == 1
+    dense = mk(fa.FA_FIRST_LEVEL_DENSE)
+    assert dense.info["first_pairs"] == 0 and dense.info["leafless"] == 0
+    assert mk(fa.FA_FIRST_LEVEL_SPARSE).info["first_pairs"] == 0
+    live = mk(fa.FA_LIVE_STATES)
+    assert live.info["first_pairs"] == 0 and live.info["leafless"] == 0
+    assert _code(lambda: mk(fa.FA_FIRST_LEVEL_PAIRS | fa.FA_LIVE_STATES)) == _fa.FA_EINVAL
+    assert _code(lambda: mk(fa.FA_FIRST_LEVEL_PAIRS | fa.FA_FIRST_LEVEL_DENSE)) == _fa.FA_EINVAL
+    # Sp = 64: no 256x256 tiles
+    chain = [(s, s + 1, [s % 7]) for s in range(39)]
+    assert _code(lambda: _compile(40, 10, 0, [39], chain, fa.FA_DFA | fa.FA_FIRST_LEVEL_PAIRS)) \
+        == _fa.FA_ETOOBIG
+    assert _compile(40, 10, 0, [39], chain, fa.FA_DFA).info["first_pairs"] == 0
 
 
 def test_determinism_check():
