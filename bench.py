@@ -487,8 +487,11 @@ def first_level_name(tb):
 
 
 def level1_name(tb):
-    """The first tree level's kernel: sparse row combination or dense MFMA."""
-    return "span_sparse1" if tb.info["first_sparse"] else "span_gemm_level1"
+    """The first tree level's kernel: sparse row combination, dense products
+    staged from the pair values, or dense products over dense leaves."""
+    if tb.info["first_sparse"]:
+        return "span_sparse1"
+    return "span_pairs_level1" if tb.info["first_pairs"] else "span_gemm_level1"
 
 
 # measured kernels: how to find their dispatches in rocprofv3 output
@@ -496,8 +499,10 @@ KERNEL_MATCH = {
     "emission_dense": lambda n: "emission_dense<" in n,
     "span_sparse1": lambda n: "span_sparse<" in n,    # first level: first launch after tree_init_rf
     "span_gemm_level1": lambda n: "span_gemm" in n,   # first of the family after tree_init_rf
+    "span_pairs_level1": lambda n: "span_pairs256" in n,
     "marg_q": lambda n: "marg_q" in n,
 }
+LEVEL1_KERNELS = ("span_gemm_level1", "span_sparse1", "span_pairs_level1")
 
 
 def _select(rows, name):
@@ -506,14 +511,16 @@ def _select(rows, name):
     tree_init_rf, dense or sparse)."""
     rows = sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
     match = KERNEL_MATCH[name]
-    if name not in ("span_gemm_level1", "span_sparse1"):
+    if name not in LEVEL1_KERNELS:
         return [r for r in rows if match(r["Kernel_Name"])]
     out, armed = [], False
     for r in rows:
-        if "tree_init_rf" in r["Kernel_Name"]:
+        n = r["Kernel_Name"]
+        if "tree_init_rf" in n:
             armed = True
-        elif armed and match(r["Kernel_Name"]):
-            out.append(r)
+        elif armed and any(KERNEL_MATCH[k](n) for k in LEVEL1_KERNELS):
+            if match(n):
+                out.append(r)
             armed = False
     return out
 
@@ -528,7 +535,7 @@ def tree_levels(rows):
         n = r["Kernel_Name"]
         if "tree_init_rf" in n:
             level = 0
-        elif level is not None and ("span_gemm" in n or "span_sparse<" in n):
+        elif level is not None and ("span_gemm" in n or "span_sparse<" in n or "span_pairs256" in n):
             level += 1
             out[r["Dispatch_Id"]] = f"L{level}"
         elif level is not None and "span_reduce" in n:
@@ -631,9 +638,11 @@ def summarize_mfma(pmc_dir, command, workload=3):
              "Command (from the repository root):", "", "```", command, "```", "",
              "MfmaUtil is rocprofv3's derived counter (summed SQ_VALU_MFMA_BUSY_CYCLES over "
              "GRBM_GUI_ACTIVE x SIMDs); the executed flops are SQ_INSTS_VALU_MFMA_MOPS_* x 512. "
-             "Durations are under the counter pass.", "",
+             "Durations are under the counter pass.  The span products run as six bf16 products per "
+             "fp32 product (the operands' three-piece split): their fp32-equivalent rate is the bf16 "
+             "rate / 6.", "",
              "| kernel | level | grid threads | launches | MfmaUtil % | fp32 MFMA GFLOP | bf16 MFMA GFLOP | avg us | "
-             "fp32 TFLOP/s |", "|---|---|---|---|---|---|---|---|---|"]
+             "bf16 TFLOP/s | fp32 TFLOP/s |", "|---|---|---|---|---|---|---|---|---|---|"]
     mean = lambda xs: sum(x[0] for x in xs) / len(xs) if xs else 0.0
     for (name, grid, level), c in sorted(agg.items(), key=lambda kv: -mean(kv[1].get(
             "SQ_INSTS_VALU_MFMA_MOPS_F32", [])) - mean(kv[1].get("SQ_INSTS_VALU_MFMA_MOPS_BF16", []))):
@@ -644,7 +653,7 @@ def summarize_mfma(pmc_dir, command, workload=3):
             continue
         us = sum(x[1] for x in mu) / len(mu)
         lines.append(f"| `{name}` | {level} | {grid} | {len(mu)} | {mean(mu):.1f} | {f32 / 1e9:.3f} | {bf / 1e9:.3f} | "
-                     f"{us:.1f} | {f32 / (us * 1e6):.1f} |")
+                     f"{us:.1f} | {bf / (us * 1e6):.1f} | {f32 / (us * 1e6):.1f} |")
     with open(os.path.join(ROOT, "profiles", f"mfma_{stem}.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
