@@ -906,10 +906,14 @@ __global__ __launch_bounds__(64) void marg_conf_tok(
 // term g[in] * v * 2^-rf[in] goes to LDS in output-grouped order (column
 // order for alpha through a row-major leaf, pair order for beta through a
 // transposed one); each output state then adds its own segment in order.
+// Leaf entries per thread: the smallest of 14, 24, 40 that holds the
+// table's pairs.  Fewer held entries take fewer registers, and more
+// workgroups fit on a CU at once (69 registers at 14: three per CU, against
+// two at 24), which matters because the launch has more workgroups than fit
+// (fewer than 14 entries take no fewer registers).
 constexpr int kLeafMsgThreads = 512;
-constexpr int kLeafMsgPer = 24;     // leaf entries per thread
-constexpr int kLeafMsgPerBig = 40;  // the same for tables with more pairs
-constexpr int kLeafMsgMax = kLeafMsgThreads * kLeafMsgPerBig;
+constexpr int kLeafMsgPerMax = 40;
+constexpr int kLeafMsgMax = kLeafMsgThreads * kLeafMsgPerMax;
 static_assert(kLeafMsgMax == kLeafMsgMaxPairs,
               "the table compiler's leafless decision assumes marg_leaf takes this many pairs");
 
@@ -1133,22 +1137,23 @@ int launch_marg_pass(const DevTable &d, const Geometry &g, const float *p, const
         if (level == g.K && sparse_leaf) {
             const bool wpw = leaf_writes_pw(d, g, w);
             const size_t llds = leaf_lds(d, g, w, wpw);
-            // entries per thread: the smaller register budget when it holds the table
-            const bool big = d.npairs > kLeafMsgThreads * kLeafMsgPer;
-            const void *fn = big ? reinterpret_cast<const void *>(&marg_leaf<kLeafMsgPerBig>)
-                                 : reinterpret_cast<const void *>(&marg_leaf<kLeafMsgPer>);
-            if (llds > 48 * 1024) {
-                e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)llds);
-                if (e != hipSuccess) return (int)e;
-            }
             float *pw = wpw ? (float *)(ws + w.pw) : nullptr;
-            if (big)
-                marg_leaf<kLeafMsgPerBig><<<products + md.nwg, kLeafMsgThreads, llds, st>>>(
-                    d, sv, emit_src(d, g, p, ws, w), meta, va, ea, vb, eb, pw, w.pw_nl, w.pw_ld, md);
-            else
-                marg_leaf<kLeafMsgPer><<<products + md.nwg, kLeafMsgThreads, llds, st>>>(
-                    d, sv, emit_src(d, g, p, ws, w), meta, va, ea, vb, eb, pw, w.pw_nl, w.pw_ld, md);
-            e = hipGetLastError();
+            const EmitSrc src = emit_src(d, g, p, ws, w);
+            auto leaf = [&](auto kernel) -> hipError_t {
+                if (llds > 48 * 1024) {
+                    const hipError_t a = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                             (int)llds);
+                    if (a != hipSuccess) return a;
+                }
+                kernel<<<products + md.nwg, kLeafMsgThreads, llds, st>>>(d, sv, src, meta, va, ea, vb, eb,
+                                                                       pw, w.pw_nl, w.pw_ld, md);
+                return hipGetLastError();
+            };
+            const int np = d.npairs;
+            if (np <= kLeafMsgThreads * 14) e = leaf(&marg_leaf<14>);
+            else if (np <= kLeafMsgThreads * 24) e = leaf(&marg_leaf<24>);
+            else e = leaf(&marg_leaf<kLeafMsgPerMax>);
             if (e != hipSuccess) return (int)e;
             continue;
         }
