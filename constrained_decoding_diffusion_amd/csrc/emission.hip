@@ -656,14 +656,15 @@ __global__ __launch_bounds__(kLeafThreads) void emission_leaves(DevTable d, Step
 // Leaves of a table that keeps no dense leaves (L > 1): only the folded
 // pair values and the row exponents, no dense tile.  One workgroup per
 // leaf: every pair's value is evaluated in parallel in the leaf's stored
-// entry order into LDS, with its row's largest exponent taken by an LDS
-// atomicMax; then the values are written times 2^-rf of their row (what the
-// dense leaf's consumers fold them to) with coalesced stores, in stored
-// order, or with `walk` (the pair-staged first level) in the order that
-// level walks the leaf: column order for a row-major leaf (output o is
-// stored entry col_pairs[o]), pair order for a transposed one (output q is
-// stored entry pair_colpos[q]).  Identity leaves past the sequence end write
-// only their row exponents (those of a diagonal of ones).
+// entry order into LDS, then each row's largest exponent is taken over the
+// row's contiguous entries, then the values are written times 2^-rf of
+// their row (what the dense leaf's consumers fold them to) with coalesced
+// stores, in stored order, or with `walk` (the pair-staged first level) in
+// the order that level walks the leaf: column order for a row-major leaf
+// (output o is stored entry col_pairs[o]), pair order for a transposed one
+// (output q is stored entry pair_colpos[q]).  Identity leaves past the
+// sequence end write only their row exponents (those of a diagonal of
+// ones).
 constexpr int kLpThreads = 1024;
 constexpr int kLpUnroll = 4;
 
@@ -707,11 +708,29 @@ __global__ __launch_bounds__(kLpThreads) void emission_leaf_pairs(DevTable d, St
                 if (e < np) {
                     lpv[e] = v;
                     if (code[u] >= 0 && !d.use_sel) bad |= !(v >= 0.f);
-                    if (v > 0.f) atomicMax(&remax[row[u]], fexp(v));
                 }
             }
         }
         if (bad) atomicOr(&status[b], (int)FA_ROW_BADPROB);
+        __syncthreads();
+        // each row's largest exponent: four threads per row over its
+        // contiguous stored entries, combined across the four lanes (LDS
+        // atomics on one row's word would serialize its lanes)
+        const int32_t *ptr = tr ? d.col_ptr : d.row_ptr;
+        for (int r0 = 0; r0 < sv.Sp; r0 += kLpThreads / 4) {
+            const int r = r0 + (tid >> 2), part = tid & 3;
+            int m = kNeg;
+            if (r < d.S) {
+                const int e1 = ptr[r + 1];
+                for (int e = ptr[r] + part; e < e1; e += 4) {
+                    const float v = lpv[e];
+                    if (v > 0.f) m = max(m, fexp(v));
+                }
+            }
+            m = max(m, __shfl_xor(m, 1));
+            m = max(m, __shfl_xor(m, 2));
+            if (part == 0 && r < sv.Sp) remax[r] = m;
+        }
     }
     __syncthreads();
     if (real) {
