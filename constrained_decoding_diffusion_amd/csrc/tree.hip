@@ -16,11 +16,10 @@
 // transposed by swapping the operands.  No entry is lost unless it is 2^-126
 // below the maximum of its own row.
 //
-// Products are stored with non-temporal stores: a level is read next by the
-// level above (a compute-bound kernel) and later by the sampler and the
-// message pass, after the streaming kernels in between have evicted it, so
-// writing it straight to HBM while the MFMAs run keeps that write-back out
-// of the streaming kernels.
+// Products are stored with plain (write-back) stores: a level is read next
+// by the level above and, in the joint call, by the message pass right after
+// the tree, so the last-level cache keeps much of it for them (measured
+// faster than writing it straight to HBM with non-temporal stores).
 #include "device_common.h"
 #include <algorithm>
 #include <atomic>
@@ -284,7 +283,7 @@ __global__ __launch_bounds__(kGemmThreads) void span_gemm(StepView sv, float *__
     for (int r = 0; r < 16; ++r) {
         const int il = wr + (r >> 2) * 8 + half * 4 + (r & 3);
         const float x = acc[r];
-        __builtin_nontemporal_store(x, &D[(size_t)(tm + il) * Sp + j]);
+        D[(size_t)(tm + il) * Sp + j] = x;
         E[il * ldE + (wc >> 5) * 32 + l32] = scaled_exp(x, coDj);
     }
     __syncthreads();
@@ -477,7 +476,7 @@ __global__ __launch_bounds__(kBigThreads) void span_gemm128(StepView sv, float *
 #pragma unroll
         for (int y = 0; y < 2; ++y) {
             const float v = acc[y][r];
-            __builtin_nontemporal_store(v, &D[(size_t)(tm + il) * Sp + tn + wc + 32 * y + l32]);
+            D[(size_t)(tm + il) * Sp + tn + wc + 32 * y + l32] = v;
             e = max(e, scaled_exp(v, coDj[y]));
         }
         E[il * ldE + (wc >> 6) * 32 + l32] = e;
@@ -613,9 +612,8 @@ __device__ __forceinline__ void huge_epilogue(const StepView &sv, float *__restr
         for (int r = 0; r < 16; ++r)
 #pragma unroll
             for (int cy = 0; cy < 4; ++cy)
-                __builtin_nontemporal_store(acc[ry][cy][r],
-                                            &D[(size_t)(tm + row0 + 32 * ry + (r >> 2) * 8 + (r & 3)) * Sp +
-                                               tn + col0 + 32 * cy]);
+                D[(size_t)(tm + row0 + 32 * ry + (r >> 2) * 8 + (r & 3)) * Sp + tn + col0 + 32 * cy] =
+                    acc[ry][cy][r];
     // per row the maximum over this lane's four columns: E[il][l32] of the
     // wave's column half, rows padded to kLde entries
     int *E = wc == 0 ? E0 : E1;
@@ -1364,7 +1362,7 @@ __global__ __launch_bounds__(kSpThreads) void span_sparse(DevTable d, StepView s
             for (int c = lane * 4; c < wn; c += 256) {
                 const f32x4 v = *reinterpret_cast<const f32x4 *>(&bufw[c]) +
                                 *reinterpret_cast<const f32x4 *>(&bufw[win + c]);
-                __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(&Drow[c]));
+                *reinterpret_cast<f32x4 *>(&Drow[c]) = v;
                 const int4 co = *reinterpret_cast<const int4 *>(&sco[w0 + c]);
                 const int cv[4] = {co.x, co.y, co.z, co.w};
 #pragma unroll
