@@ -50,14 +50,6 @@ __device__ inline int fexp(float x)
     return e;
 }
 
-// a float4 store that does not allocate in the caches (streaming output)
-__device__ inline void store_nt(float4 *dst, float4 v)
-{
-    typedef float f32x4n __attribute__((ext_vector_type(4)));
-    const f32x4n x = {v.x, v.y, v.z, v.w};
-    __builtin_nontemporal_store(x, reinterpret_cast<f32x4n *>(dst));
-}
-
 // a float4 load with the non-temporal hint: for streamed inputs read once
 // per kernel (p), which then do not displace cached tables; on gfx950 a plain
 // read of p ran at 5.9 TB/s, a non-temporal one at 6.8 TB/s
