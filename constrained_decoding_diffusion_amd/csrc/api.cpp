@@ -329,7 +329,8 @@ extern "C" int fa_map_sizes(const fa_table *t, int32_t B, int32_t L, size_t *tre
                             size_t *ws_bytes)
 {
     if (!t) return FA_EINVAL;
-    if (t->h.nseg() > 0) return FA_EINVAL;  // range labels: no range-maximum structure
+    // range labels: the per-position range-maximum structure must fit one workgroup's LDS
+    if (t->h.nseg() > 0 && map_range_lds(t->h.ncut()) > kMapRangeLdsMax) return FA_ETOOBIG;
     Geometry g;
     if (int grc = make_geometry(t->h, B, L, &g)) return grc;
     StepChunks ck;
@@ -344,7 +345,7 @@ extern "C" int fa_map_decode(const fa_table *t, const float *p, int32_t B, int32
                              int32_t *states, int32_t *tokens, int32_t *row_status,
                              fa_stream_t stream)
 {
-    if (t && t->h.nseg() > 0) return FA_EINVAL;
+    if (t && t->h.nseg() > 0 && map_range_lds(t->h.ncut()) > kMapRangeLdsMax) return FA_ETOOBIG;
     int rc = ready(t);
     if (rc) return rc;
     StepChunks ck;

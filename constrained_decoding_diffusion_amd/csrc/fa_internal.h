@@ -39,6 +39,25 @@ constexpr uint32_t kSelBit = 1u << 31;  // tokmask flag of LIST tokens (tables w
 constexpr int kRowChunk4 = 1024;   // float4 groups per chunk of a dense-pair token draw (4096 tokens)
 constexpr int kQParts = 4;         // workgroups per position of the streaming q writer
 constexpr int kTokChunksMax = 256;  // chunks per candidate list of one token draw
+// MAP decoding over range labels: per position, the maxima of p over the
+// ncut - 1 elementary intervals between cut points and a sparse table over
+// blocks of kMapRangeBlk of them, both in one workgroup's LDS; a table whose
+// structure exceeds kMapRangeLdsMax is refused
+constexpr int kMapRangeBlk = 64;
+constexpr size_t kMapRangeLdsMax = 160 * 1024;
+constexpr int map_range_blocks(int nint) { return (nint + kMapRangeBlk - 1) / kMapRangeBlk; }
+constexpr int map_range_levels(int nblk)   // floor(log2 nblk) + 1 levels
+{
+    int lg = 1;
+    while ((2LL << (lg - 1)) <= nblk) ++lg;
+    return lg;
+}
+constexpr size_t map_range_lds(int ncut)
+{
+    const int nint = ncut > 1 ? ncut - 1 : 0;
+    const int nblk = map_range_blocks(nint);
+    return ((size_t)nint + (size_t)nblk * map_range_levels(nblk)) * sizeof(uint32_t);
+}
 
 enum PairClass : int32_t { kList = 0, kDense = 1, kRange = 2 };
 

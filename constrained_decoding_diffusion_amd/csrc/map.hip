@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kMapThreads) void map_pairmax(DevTable d, const flo
     const int b = pos / L;
     const float *row = p + (size_t)pos * d.V;
     float *out = pmax + (size_t)pos * d.npairs;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x;
     int bad = 0;
     if constexpr (NG > 0) {
         // tokens grouped by their mask byte: T[g][y] is the largest p bit
@@ -114,6 +114,112 @@ __global__ __launch_bounds__(kMapThreads) void map_pairmax(DevTable d, const flo
             if (x > m) m = x;
         }
         out[q] = m;
+    }
+    if (bad) atomicOr(&status[b], (int)FA_ROW_BADPROB);
+}
+
+// ------------------------------------------------ range-label pair maxima
+// A range pair's maximum of p over its segments, from a range-maximum
+// structure built per position in LDS.  The sorted cut points split
+// [cuts[0], cuts[ncut-1]) into ncut-1 elementary intervals and every segment
+// is a run of them.  The workgroup first folds the row into the intervals'
+// maxima, as keys: the bit pattern of a p >= 0 (which orders as p does), all
+// ones for a NaN or negative p, so that a segment holding one reads as bad.
+// Then the maxima of blocks of kMapRangeBlk intervals, and a sparse table over
+// the blocks (level k at k * nblk: the maximum of 2^k blocks from each start).
+// A segment's maximum is at most two partial blocks of intervals and two
+// table entries.  One workgroup per position.
+constexpr int kMapRangeThreads = 1024;
+
+__device__ inline uint32_t range_key(float x)
+{
+    return x >= 0.f ? (__float_as_uint(x) & 0x7FFFFFFFu) : 0xFFFFFFFFu;
+}
+
+// maximum key over the intervals [lo, hi)
+__device__ inline uint32_t range_query(const uint32_t *rk, const uint32_t *tab, int nblk, int lo,
+                                       int hi)
+{
+    uint32_t m = 0u;
+    const int bl = (lo + kMapRangeBlk - 1) / kMapRangeBlk;  // first whole block
+    const int br = hi / kMapRangeBlk - 1;                   // last whole block
+    if (bl > br) {
+        for (int c = lo; c < hi; ++c) m = max(m, rk[c]);
+        return m;
+    }
+    for (int c = lo; c < bl * kMapRangeBlk; ++c) m = max(m, rk[c]);
+    for (int c = (br + 1) * kMapRangeBlk; c < hi; ++c) m = max(m, rk[c]);
+    const int k = 31 - __clz(br - bl + 1);
+    return max(m, max(tab[k * nblk + bl], tab[k * nblk + br - (1 << k) + 1]));
+}
+
+// VEC4: V % 4 == 0 and p and tok2cut 16-byte aligned
+template <bool VEC4>
+__global__ __launch_bounds__(kMapRangeThreads) void map_rangemax(DevTable d,
+                                                                 const float *__restrict__ p,
+                                                                 int L, float *__restrict__ pmax,
+                                                                 int32_t *__restrict__ status)
+{
+    extern __shared__ uint32_t rk[];  // [nint] interval maxima, then the block table
+    const int pos = blockIdx.x;
+    const int b = pos / L;
+    const float *row = p + (size_t)pos * d.V;
+    float *out = pmax + (size_t)pos * d.npairs;
+    const int tid = threadIdx.x;
+    const int nint = d.ncut - 1;
+    const int nblk = map_range_blocks(nint);
+    const int lg = map_range_levels(nblk);
+    uint32_t *tab = rk + nint;
+    for (int c = tid; c < nint; c += kMapRangeThreads) rk[c] = 0u;
+    __syncthreads();
+    // a thread's tokens ascend, so equal intervals come in runs: one LDS
+    // maximum per run
+    int rc = -1;
+    uint32_t rkey = 0u;
+    auto put = [&](int c, float x) {
+        const uint32_t k = range_key(x);
+        if (c != rc) {
+            if (rc >= 0 && rc < nint && rkey) atomicMax(&rk[rc], rkey);
+            rc = c;
+            rkey = 0u;
+        }
+        rkey = max(rkey, k);
+    };
+    if (VEC4) {
+        const int n4 = d.V >> 2;
+        for (int g = tid; g < n4; g += kMapRangeThreads) {
+            const float4 x4 = load_nt(row + 4 * (size_t)g);
+            const int4 c4 = reinterpret_cast<const int4 *>(d.tok2cut)[g];
+            put(c4.x, x4.x);
+            put(c4.y, x4.y);
+            put(c4.z, x4.z);
+            put(c4.w, x4.w);
+        }
+    } else {
+        for (int v = tid; v < d.V; v += kMapRangeThreads) put(d.tok2cut[v], row[v]);
+    }
+    put(-1, 0.f);
+    __syncthreads();
+    for (int j = tid; j < nblk; j += kMapRangeThreads) {
+        uint32_t m = 0u;
+        for (int c = j * kMapRangeBlk; c < min(nint, (j + 1) * kMapRangeBlk); ++c) m = max(m, rk[c]);
+        tab[j] = m;
+    }
+    __syncthreads();
+    for (int k = 1; k < lg; ++k) {
+        const int h = 1 << (k - 1);
+        for (int j = tid; j + 2 * h <= nblk; j += kMapRangeThreads)
+            tab[k * nblk + j] = max(tab[(k - 1) * nblk + j], tab[(k - 1) * nblk + j + h]);
+        __syncthreads();
+    }
+    int bad = 0;
+    for (int q = tid; q < d.npairs; q += kMapRangeThreads) {
+        if (d.pair_cls[q] != kRange) continue;
+        uint32_t m = 0u;
+        for (int s = d.seg_off[q]; s < d.seg_off[q + 1]; ++s)
+            m = max(m, range_query(rk, tab, nblk, d.seg_lo_cut[s], d.seg_hi_cut[s]));
+        bad |= m == 0xFFFFFFFFu;
+        out[q] = m == 0xFFFFFFFFu ? 0.f : __uint_as_float(m);
     }
     if (bad) atomicOr(&status[b], (int)FA_ROW_BADPROB);
 }
@@ -319,7 +425,7 @@ __global__ __launch_bounds__(64) void map_mid(DevTable d, int Lpad, int lev,
 }
 
 // The most probable token of each position's edge (z_i, z_{i+1}): over the
-// pair's token list, or over the row with the dense pair's bit array;
+// pair's token list, its segments, or the row with the dense pair's bit array;
 // smallest token among equal probabilities.  One workgroup per position.
 __global__ __launch_bounds__(kMapThreads) void map_tokens(DevTable d, int L, int Lpad,
                                                           const float *__restrict__ p,
@@ -366,6 +472,12 @@ __global__ __launch_bounds__(kMapThreads) void map_tokens(DevTable d, int L, int
                         if (x > 0.f) better(v, k, (double)x, t);
                     }
             }
+        } else if (d.pair_cls[q] == kRange) {
+            for (int s = d.seg_off[q]; s < d.seg_off[q + 1]; ++s)
+                for (int t = d.seg_lo[s] + tid; t < d.seg_hi[s]; t += kMapThreads) {
+                    const float x = row[t];
+                    if (x > 0.f) better(v, k, (double)x, t);
+                }
         } else {
             for (int e = d.list_off[q] + tid; e < d.list_off[q + 1]; e += kMapThreads) {
                 const int t = d.list_tok[e];
@@ -481,6 +593,23 @@ int launch_map_decode(const DevTable &d, const Geometry &g, const float *p, doub
 #undef FA_MAP_PM
     e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
+    if (d.nseg > 0) {
+        // the entry points refuse tables whose structure exceeds kMapRangeLdsMax
+        const size_t rlds = map_range_lds(d.ncut);
+        const bool rv4 = vec4 && ((uintptr_t)d.tok2cut & 15) == 0;
+        const void *fn = rv4 ? reinterpret_cast<const void *>(&map_rangemax<true>)
+                             : reinterpret_cast<const void *>(&map_rangemax<false>);
+        if (rlds > 48 * 1024) {
+            e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)rlds);
+            if (e != hipSuccess) return (int)e;
+        }
+        if (rv4)
+            map_rangemax<true><<<npos, kMapRangeThreads, rlds, st>>>(d, p, g.L, pmax, status);
+        else
+            map_rangemax<false><<<npos, kMapRangeThreads, rlds, st>>>(d, p, g.L, pmax, status);
+        e = hipGetLastError();
+        if (e != hipSuccess) return (int)e;
+    }
     const size_t llds = (size_t)g.Sp * sizeof(double);
     if (llds > 48 * 1024) {
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(&map_leaves),

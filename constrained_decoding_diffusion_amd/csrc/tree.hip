@@ -49,12 +49,6 @@ __global__ void tree_init_rf(StepView sv, int32_t *__restrict__ meta)
     }
 }
 
-__device__ inline void load8(const float *src, float4 &a, float4 &b)
-{
-    a = *reinterpret_cast<const float4 *>(src);
-    b = *reinterpret_cast<const float4 *>(src + 4);
-}
-
 // exact power-of-two rescale of four consumed entries; zero stays zero and
 // values more than 2^126 below the row maximum flush to zero
 __device__ inline float4 fold4(float4 x, int4 c, int rfrow)
@@ -91,7 +85,7 @@ __device__ inline int scaled_exp(float x, int c)
 {
     int ex;
     frexpf(x, &ex);
-    return (x > 0.f) & (c > kNeg) ? ex + c : kNeg;
+    return ((x > 0.f) & (c > kNeg)) ? ex + c : kNeg;
 }
 
 // The dense span kernels run the fp32 products on the bf16 matrix cores:

@@ -374,8 +374,10 @@ int fa_chain_sample_marginals(const fa_table *t, const float *p, int32_t B, int3
 
 /*
  * fa_map_sizes - bytes of the fp64 tree and of the workspace fa_map_decode
- * needs for batch B and length L.  Errors: FA_EINVAL (also for a table with
- * range labels, which MAP decoding does not take), FA_ETOOBIG.
+ * needs for batch B and length L.  Errors: FA_EINVAL, FA_ETOOBIG (also for a
+ * table with range labels whose per-position range-maximum structure, 4 bytes
+ * per elementary interval between cut points plus a sparse table over blocks
+ * of 64 of them, exceeds 160 KB: about 34,000 distinct cut points).
  */
 int fa_map_sizes(const fa_table *t, int32_t B, int32_t L, size_t *tree_bytes, size_t *ws_bytes);
 
@@ -390,7 +392,10 @@ int fa_map_sizes(const fa_table *t, int32_t B, int32_t L, size_t *tree_bytes, si
  * over an automaton by dynamic programming); the tree of "The scan trick:
  * log-depth exact sampling" with max in place of sum.
  * Method: per position the max-times transition matrix
- * Mmax_i[a][b] = max over v with c(a, v, b) > 0 of p[b][i][v]; 2^k-span
+ * Mmax_i[a][b] = max over v with c(a, v, b) > 0 of p[b][i][v] (range labels:
+ * per position the maxima of p over the elementary intervals between cut
+ * points, a sparse table over blocks of them, and each segment's maximum
+ * from at most two partial blocks and two table entries); 2^k-span
  * max-times products level by level in fp64 logs; the final boundary state
  * maximizing root[s0][f] over f in F; top-down, every midpoint z_m
  * maximizing P[l,m)[z_l][z_m] + P[m,r)[z_m][z_r]; every token the most
@@ -406,8 +411,8 @@ int fa_map_sizes(const fa_table *t, int32_t B, int32_t L, size_t *tree_bytes, si
  *   states   device int32 [B][L+1] original ids; tokens device int32 [B][L]
  *            (-1 on flagged rows)
  *   row_status device int32 [B], OR-ed
- * Errors: FA_EINVAL (also for tables with range labels), FA_ETOOBIG,
- * FA_ESTATE, FA_EHIP.
+ * Errors: FA_EINVAL, FA_ETOOBIG (also range labels beyond fa_map_sizes'
+ * bound), FA_ESTATE, FA_EHIP.
  */
 int fa_map_decode(const fa_table *t, const float *p, int32_t B, int32_t L, double *tree,
                   void *ws, size_t ws_bytes, double *logmax, int32_t *states, int32_t *tokens,

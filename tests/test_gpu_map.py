@@ -55,7 +55,7 @@ def check_map_row(w, g, b, orc):
     return rep
 
 
-MAP_CASES = [n for n in CASES if n != "range-small"]
+MAP_CASES = list(CASES)
 
 
 @pytest.mark.parametrize("name", MAP_CASES)
@@ -140,13 +140,71 @@ def test_map_flagged_rows_and_empty():
     fa.map_decode(tb, torch.zeros((0, 6, 12), dtype=torch.float32, device="cuda"))
 
 
-def test_map_refuses_range_labels():
+def _hand_range_nfa():
+    """Three states over 50 tokens with range labels: pair (0, 1) holds two
+    parallel edges whose ranges overlap (segments of counts 1 and 2), pair
+    (0, 2) overlaps pair (0, 1), and tokens 38, 39 and 46-49 lie in no
+    segment (38 and 39 inside an elementary interval between cut points)."""
+    edges = [(0, 1, np.array([5, 10, 20, 30])), (0, 2, np.array([8, 15])),
+             (0, 1, np.array([25, 35])), (1, 1, np.array([0, 38])), (1, 2, np.array([44, 46])),
+             (2, 0, np.array([40, 45])), (2, 2, np.array([1, 3]))]
+    return A._pack(3, 50, 0, [1, 2], edges, ranges=True, dfa=False, name="hand range NFA")
+
+
+def test_map_range_labels_by_hand():
+    """Range labels through the per-position range-maximum structure: rows
+    of a hand-built range NFA decode like the oracle; a NaN at a token in no
+    segment leaves its row unflagged, one inside a segment flags it."""
+    aut = _hand_range_nfa()
+    rng = np.random.default_rng(77)
+    B, L = 4, 13
+    p = rng.normal(0, 2, (B, L, aut.V))
+    p = np.exp(p - p.max(-1, keepdims=True))
+    p = (p / p.sum(-1, keepdims=True)).astype(np.float32)
+    p[0, 2, 39] = np.nan      # in no segment
+    p[1, 3, 7] = np.nan       # in pair (0, 1)'s first segment
+    w = configs.Workload(aut.name, aut, p, B, L, 1, [])
+    g = run_map(w)
+    orc = oracle.Oracle(aut)
+    for b in (0, 2, 3):
+        check_map_row(w, g, b, orc)
+    assert g["status"][1] & 4 and g["logmax"][1] == -np.inf
+    assert (g["states"][1] == -1).all() and (g["tokens"][1] == -1).all()
+
+
+def test_map_range_universal_and_ties():
+    """The universal automaton as one range [0, V): the decoded tokens are the
+    per-position argmax of p, the smaller id on an exact tie."""
+    V, L = 3000, 21
+    rng = np.random.default_rng(78)
+    p = rng.normal(0, 2, (2, L, V))
+    p = np.exp(p - p.max(-1, keepdims=True))
+    p = (p / p.sum(-1, keepdims=True)).astype(np.float32)
+    p[0, 5, 1234] = p[0, 5, 2345] = p[0, 5].max() + np.float32(0.05)
+    aut = A._pack(1, V, 0, [0], [(0, 0, np.array([0, V]))], ranges=True, name="universal range")
+    w = configs.Workload(aut.name, aut, p, 2, L, 1, [])
+    g = run_map(w)
+    np.testing.assert_array_equal(g["tokens"], np.argmax(p, -1))
+    assert g["tokens"][0, 5] == 1234
+    expect = np.log(p.max(-1).astype(np.float64)).sum(-1)
+    np.testing.assert_allclose(g["logmax"], expect, rtol=LOGMAX_RTOL)
+
+
+def test_map_range_dfa_full_vocabulary():
+    """The range DFA of S = 1024 over V = 151,936 (16 ranges per state: about
+    29,500 cut points, every level of the block table in use) at a short
+    length, row for row against the oracle."""
     import constrained_decoding_diffusion_amd as fa
-    w = CASES["range-small"]()
+    aut = configs._draw(lambda r: A.range_dfa(r, S=1024, V=151936), 7801, 12)
+    w = configs.from_automaton(aut, 2, 12, "normal4_zipf", 0, 7802, "range DFA S 1024, L 12")
     tb = fa.Table.from_automaton(w.aut)
-    with pytest.raises(fa.FaError) as ei:
-        fa.MapBuffers(tb, w.B, w.L)
-    assert ei.value.code == 1
+    PT.log(f"[map] {w.describe()}, cuts {tb.info['cuts']}")
+    assert tb.info["cuts"] > 20000
+    g = run_map(w, table=tb)
+    orc = oracle.Oracle(w.aut)
+    for b in range(w.B):
+        rep = check_map_row(w, g, b, orc)
+        PT.log(f"[map] range DFA row {b}: ok ({rep})")
 
 
 def test_map_determinism_and_repeat():

@@ -186,6 +186,25 @@ def test_range_pairs_merge_parallel_edges():
     assert t.info["cuts"] == 5  # 0, 4, 6, 9, 10
 
 
+def test_map_range_structure_limit():
+    """MAP decoding over range labels keeps one position's interval maxima and
+    their block table in 160 KB of LDS: 35,420 cut points fit, 35,422 do not
+    (FA_ETOOBIG from the sizes and from the decode call, before any launch)."""
+    R = fa.FA_DFA | fa.FA_LABEL_RANGES
+    lib = _fa.lib()
+    for k, ok in ((17710, True), (17711, False)):
+        lab = np.stack([2 * np.arange(k), 2 * np.arange(k) + 1], 1).ravel()
+        t = _compile(1, 40000, 0, [0], [(0, 0, lab)], R)
+        assert t.info["cuts"] == 2 * k
+        tb, wb = C.c_size_t(), C.c_size_t()
+        rc = lib.fa_map_sizes(t.handle, 1, 8, C.byref(tb), C.byref(wb))
+        assert rc == (_fa.FA_OK if ok else _fa.FA_ETOOBIG)
+        if not ok:
+            rc = lib.fa_map_decode(t.handle, None, 1, 8, None, None, 0, None, None, None, None,
+                                   None)
+            assert rc == _fa.FA_ETOOBIG
+
+
 def test_sizes_and_limits():
     t = fa.Table.from_automaton(A.real_number_dfa())
     Sp = t.info["Sp"]
