@@ -258,7 +258,7 @@ def ceilings(torch, fa, dev, p, reps=7):
     best = min((med(lambda g=g: fa.probe_bandwidth(fa.FA_PROBE_COPY, src, dst, 1 << 30, g, stream)), g)
                for g in grids)
     out["copy_1GiB"] = rec(best[0], 2 << 30, f"plain copy kernel, 1 GiB each way, streaming stores, "
-                                             f"{best[1]} workgroups")
+                                             f"{best[1]} workgroups of 1024 threads")
     out["torch_copy_1GiB"] = rec(med(lambda: dst.copy_(src)), 2 << 30, "torch copy_ of 1 GiB")
     del src, dst, part
     return out

@@ -491,9 +491,10 @@ int fa_profile_kernel(int32_t which, void *start_event, void *stop_event);
 
 /* Measurement hook; not part of the method.
  * fa_probe_bandwidth - one plain streaming kernel on `stream`, whose rate is
- *   an achievable HBM ceiling for the step's kernels: `blocks` workgroups
- *   of 256 threads, each over its own contiguous chunk, eight non-temporal
- *   float4 loads in flight per thread (non-temporal stores for the copy).
+ *   an achievable HBM ceiling for the step's kernels: `blocks` workgroups,
+ *   each over its own contiguous chunk, with non-temporal float4 loads: 256
+ *   threads and eight loads in flight per thread for the read, 1024 threads
+ *   and four for the copy (with non-temporal stores).
  *     FA_PROBE_READ  every byte of src read once; dst receives one float per
  *                    workgroup (at least blocks * 4 bytes)
  *     FA_PROBE_COPY  dst = src (bytes each), streaming stores
