@@ -95,7 +95,7 @@ def _np_ptr(a: np.ndarray):
 INFO_KEYS = ["S", "Sp", "start", "n_accept", "pairs", "list_pairs", "dense_pairs", "range_pairs",
              "list_entries", "segments", "cuts", "sel_tokens", "use_sel", "V", "S_orig",
              "first_sparse", "first_work", "second_sparse", "second_work", "pairs2", "leafless",
-             "leaf_msg_pairs", "live_states", "first_pairs"]
+             "leaf_msg_pairs", "live_states", "first_pairs", "map_first_sparse"]
 
 
 class Table:

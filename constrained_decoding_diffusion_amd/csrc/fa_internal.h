@@ -35,6 +35,10 @@ constexpr int kDenseSelLds = 64;    // token-list tokens per V chunk that its LD
 constexpr int kDenseTile = 32;     // positions per workgroup of the dense-mask contraction
 constexpr int kSelMax = 8192;      // LIST tokens gathered through a compact copy of p
 constexpr int kMapMaxSp = 2048;   // dense (row, column) -> pair maps up to this Sp
+// greedy decoding forms its first max-plus level from the pairs when their
+// terms, each costing about as much as this many dense terms (a chain of
+// dependent gathers against a streamed tile), fall below S^3
+constexpr int kMapSparseCost = 256;
 constexpr uint32_t kSelBit = 1u << 31;  // tokmask flag of LIST tokens (tables with < 32 dense pairs)
 constexpr int kRowChunk4 = 1024;   // float4 groups per chunk of a dense-pair token draw (4096 tokens)
 constexpr int kQParts = 4;         // workgroups per position of the streaming q writer
@@ -136,6 +140,7 @@ struct DevTable {
     int32_t n_ind;
     int32_t first_sparse;        // 1: the first span level is formed from the pair values
     int32_t first_pairs;         // 1: it is a dense product whose operands are staged from them
+    int32_t map_first_sparse;    // 1: greedy decoding forms its first max-plus level from the pairs
     int32_t leafless;            // 1: no dense leaves; every leaf reader takes the pair values
     int32_t second_sparse;       // 1: so is the second, from the two-step pattern
     int32_t live_states;         // 1: dense products contract over the live states (live.hip)
@@ -184,6 +189,7 @@ struct HostTable {
     bool selbit = false;
     bool first_sparse = false;  // first span level by row combination over the pairs
     bool first_pairs = false;   // first span level on the matrix cores, operands from the pairs
+    bool map_first_sparse = false;  // greedy decoding's first max-plus level over the pairs
     bool leafless = false;      // dense leaves not written (every leaf reader takes pair values)
     int64_t first_work = 0;     // its multiply-adds per product: pairs (a, k) times pairs (k, c)
     // two-step pattern: pairs (a, c) joined by pairs (a, k), (k, c), sorted

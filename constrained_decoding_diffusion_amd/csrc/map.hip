@@ -262,6 +262,82 @@ __global__ __launch_bounds__(kMapThreads) void map_leaves(DevTable d, int L, int
     }
 }
 
+// ---------------------------------------- first max-plus level from pairs
+// Level-1 products (two leaves each) over the pair structure: D[a][c] is the
+// largest sum of the log weights of a pair (a, k) of the left leaf and a
+// pair (k, c) of the right one, -inf where there is none; the weights are
+// read from the dense log leaves at the pairs' entries.  A node stored as is
+// builds its rows a from the left leaf's rows and the right leaf's rows; one
+// stored transposed builds its rows c from the right leaf's columns and the
+// left leaf's columns.  Each term is the same fp64 add as map_gemm's and the
+// maximum does not depend on the order, so the nodes are map_gemm's, bit for
+// bit.  A right leaf past the sequence end is the identity (D = the left
+// leaf), and so are both when the left one is.  One workgroup per (node,
+// `rows` stored rows, held in LDS); each wavefront takes a stored row at a
+// time, its lanes over one inner pair list at a time, whose columns are
+// distinct, so no two lanes update one entry at once.
+__global__ __launch_bounds__(kMapThreads) void map_sparse1(DevTable d, int L, int Lpad, int rows,
+                                                           double *__restrict__ tree)
+{
+    extern __shared__ double accs[];  // [rows][Sp]
+    const int Sp = d.Sp;
+    const int half = Lpad >> 1;
+    const int b = blockIdx.y / half, n = half + blockIdx.y % half;
+    const bool tr = stored_transposed(n);
+    const int il = 2 * n - Lpad;
+    const bool id_l = il >= L, id_r = il + 1 >= L;  // identity leaves past the sequence end
+    const double *Xl = node_ptr(tree, Sp, Lpad, b, 2 * n);      // stored as is: Xl[a][k]
+    const double *Xr = node_ptr(tree, Sp, Lpad, b, 2 * n + 1);  // transposed: Xr[c][k]
+    double *D = node_ptr(tree, Sp, Lpad, b, n);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r0 = blockIdx.x * rows, nr = min(rows, Sp - r0);
+    for (int e = tid; e < nr * Sp; e += kMapThreads) accs[e] = -INFINITY;
+    __syncthreads();
+    for (int rr = wave; rr < nr; rr += kMapThreads / 64) {
+        const int x = r0 + rr;  // stored row: a (as is) or c (transposed)
+        double *acc = accs + (size_t)rr * Sp;
+        if (x >= d.S) continue;
+        if (id_l) {
+            if (lane == 0) acc[x] = 0.0;
+        } else if (id_r) {
+            // D = the left leaf (each entry plus the identity's 0): its row
+            // x, or its column x for a transposed node
+            const int q0 = tr ? d.col_ptr[x] : d.row_ptr[x], q1 = tr ? d.col_ptr[x + 1] : d.row_ptr[x + 1];
+            for (int q = q0 + lane; q < q1; q += 64) {
+                if (tr) {
+                    const int a = d.pair_a[d.col_pairs[q]];
+                    acc[a] = Xl[(size_t)a * Sp + x] + 0.0;
+                } else {
+                    const int c = d.pair_b[q];
+                    acc[c] = Xl[(size_t)x * Sp + c] + 0.0;
+                }
+            }
+        } else if (!tr) {
+            for (int kl = d.row_ptr[x]; kl < d.row_ptr[x + 1]; ++kl) {
+                const int k = d.pair_b[kl];
+                const double wl = Xl[(size_t)x * Sp + k];
+                for (int q = d.row_ptr[k] + lane; q < d.row_ptr[k + 1]; q += 64) {
+                    const int c = d.pair_b[q];
+                    acc[c] = fmax(acc[c], wl + Xr[(size_t)c * Sp + k]);
+                }
+            }
+        } else {
+            // stored row c of D^T: over the right leaf's pairs (k, c) and the
+            // left leaf's pairs (a, k)
+            for (int kr = d.col_ptr[x]; kr < d.col_ptr[x + 1]; ++kr) {
+                const int k = d.pair_a[d.col_pairs[kr]];
+                const double wr = Xr[(size_t)x * Sp + k];
+                for (int q = d.col_ptr[k] + lane; q < d.col_ptr[k + 1]; q += 64) {
+                    const int a = d.pair_a[d.col_pairs[q]];
+                    acc[a] = fmax(acc[a], Xl[(size_t)a * Sp + k] + wr);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < nr * Sp; e += kMapThreads) D[(size_t)r0 * Sp + e] = accs[e];
+}
+
 // ------------------------------------------------------ max-plus products
 // One wavefront per 64 x 64 output tile of D = X (max,+) Y^T over one K
 // range (a split); each lane owns an 8 x 8 block of the tile.  Operand tiles
@@ -623,6 +699,21 @@ int launch_map_decode(const DevTable &d, const Geometry &g, const float *p, doub
     const int tiles = g.Sp / kMT;
     for (int k = 1; k <= g.K; ++k) {
         const int n0 = g.Lpad >> k, nn = n0;
+        if (k == 1 && d.map_first_sparse) {
+            // rows per workgroup: at most 64 KB of LDS
+            const int rows = std::max(1, std::min(16, (int)(65536 / ((size_t)g.Sp * sizeof(double)))));
+            const size_t slds = (size_t)rows * g.Sp * sizeof(double);
+            if (slds > 48 * 1024) {
+                e = hipFuncSetAttribute(reinterpret_cast<const void *>(&map_sparse1),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)slds);
+                if (e != hipSuccess) return (int)e;
+            }
+            map_sparse1<<<dim3((g.Sp + rows - 1) / rows, g.B * nn), kMapThreads, slds, st>>>(
+                d, g.L, g.Lpad, rows, tree);
+            e = hipGetLastError();
+            if (e != hipSuccess) return (int)e;
+            continue;
+        }
         const int ks = map_ksplit(g, k);
         map_gemm<<<dim3(tiles * tiles * ks, g.B * nn), 64, 0, st>>>(g.Sp, g.Lpad, tree, n0, nn, ks,
                                                                       part);

@@ -120,6 +120,7 @@ DevTable HostTable::device_view() const
     d.selbit = selbit ? 1 : 0;
     d.first_sparse = first_sparse ? 1 : 0;
     d.first_pairs = first_pairs ? 1 : 0;
+    d.map_first_sparse = map_first_sparse ? 1 : 0;
     d.leafless = leafless ? 1 : 0;
     const uint8_t *b = static_cast<const uint8_t *>(dev);
     size_t k = 0;
@@ -813,6 +814,11 @@ static int compile(int32_t S, int32_t V, int32_t start, const int32_t *accept, i
                          (double)kSparseFirstRatio * (double)w1 <= (double)t.Sp * t.Sp * t.Sp;
         t.first_pairs = !t.first_sparse && pairs_ok;
     }
+    // greedy decoding's first level: the same forcing flags, else by its
+    // own cost rule (a max-plus term over the pairs against a dense one)
+    if (flags & FA_FIRST_LEVEL_SPARSE) t.map_first_sparse = true;
+    else if (flags & FA_FIRST_LEVEL_DENSE) t.map_first_sparse = false;
+    else t.map_first_sparse = (double)kMapSparseCost * (double)w1 <= (double)t.S * t.S * t.S;
     t.p2_a.clear(); t.p2_b.clear(); t.p2_row_ptr.clear(); t.p2_col_ptr.clear();
     t.p2_col_pairs.clear(); t.p2_colpos.clear();
     t.w1_n.clear(); t.w1_t.clear(); t.w2_n.clear(); t.w2_t.clear();
@@ -906,14 +912,15 @@ extern "C" int fa_table_info(const fa_table *t, int64_t *info, int32_t n)
     const HostTable &h = t->h;
     int32_t nl = 0, nd = 0, nr = 0;
     for (int32_t c : h.pair_cls) (c == kList ? nl : c == kDense ? nd : nr)++;
-    constexpr int32_t kInfo = 24;
+    constexpr int32_t kInfo = 25;
     int64_t v[kInfo] = {h.S, h.Sp, h.start, (int64_t)h.acc.size(), h.npairs(), nl, nd, nr,
                         (int64_t)h.list_tok.size(), h.nseg(), h.ncut(), h.nsel(),
                         h.use_sel ? 1 : 0, h.V, h.S_orig, h.first_sparse ? 1 : 0, h.first_work,
                         h.second_sparse ? 1 : 0, h.second_work, (int64_t)h.p2_a.size(),
                         h.leafless ? 1 : 0,
                         h.npairs() > 0 && leaf_level_from_pairs(h.npairs(), h.S, h.Sp) ? 1 : 0,
-                        h.live_states ? 1 : 0, h.first_pairs ? 1 : 0};
+                        h.live_states ? 1 : 0, h.first_pairs ? 1 : 0,
+                        h.map_first_sparse ? 1 : 0};
     for (int32_t k = 0; k < n && k < kInfo; ++k) info[k] = v[k];
     return FA_OK;
 }

@@ -160,7 +160,9 @@ void fa_table_destroy(fa_table *t);
  * pass's leaf level (L > 1) reads the pair values instead of the dense
  * leaves, [22] 1 if the table was compiled with FA_LIVE_STATES, [23] 1 if
  * the first level is a dense product with operands staged from the pair
- * values.  Returns FA_OK or FA_EINVAL.
+ * values, [24] 1 if fa_map_decode forms its first max-plus level from the
+ * pairs (FA_FIRST_LEVEL_SPARSE forces it and FA_FIRST_LEVEL_DENSE keeps it
+ * dense; else when 256 [16] <= S^3).  Returns FA_OK or FA_EINVAL.
  */
 int fa_table_info(const fa_table *t, int64_t *info, int32_t n);
 

@@ -207,6 +207,44 @@ def test_map_range_dfa_full_vocabulary():
         PT.log(f"[map] range DFA row {b}: ok ({rep})")
 
 
+def _map_tree(fa, torch, w, first_level):
+    tb = fa.Table.from_automaton(w.aut, first_level=first_level)
+    p = torch.from_numpy(w.p).cuda()
+    bufs = fa.map_decode(tb, p)
+    torch.cuda.synchronize()
+    Lpad = 1 << max(0, (w.L - 1).bit_length())
+    Sp = tb.info["Sp"]
+    tree = bufs.tree[: w.B * 2 * Lpad * Sp * Sp].view(w.B, 2 * Lpad, Sp, Sp)
+    return tb, [tree[:, 1:Lpad].cpu().numpy(), bufs.logmax.cpu().numpy(), bufs.states.cpu().numpy(),
+                bufs.tokens.cpu().numpy(), bufs.status.cpu().numpy()]
+
+
+@pytest.mark.parametrize("name", ["json-small", "random-dfa", "range-small", "nfa-small",
+                                  "hand-range", "odd-length"])
+def test_map_sparse_first_level_equals_dense(name):
+    """The first max-plus level formed over the pairs (map_sparse1) against
+    the dense products: every internal node of the tree, the log-max, the
+    states and the tokens equal bit for bit (each term is the same fp64 add,
+    and the maximum does not depend on the order)."""
+    import torch
+    import constrained_decoding_diffusion_amd as fa
+    if name == "hand-range":
+        aut = _hand_range_nfa()
+        rng = np.random.default_rng(79)
+        p = rng.dirichlet(np.ones(aut.V), (3, 11)).astype(np.float32)
+        w = configs.Workload(aut.name, aut, p, 3, 11, 1, [])
+    elif name == "odd-length":
+        w = configs.make(2, B=2, L=13)   # identity leaves past the sequence end
+    else:
+        w = CASES[name]()
+    ts, rs = _map_tree(fa, torch, w, "sparse")
+    td, rd = _map_tree(fa, torch, w, "dense")
+    assert ts.info["map_first_sparse"] == 1 and td.info["map_first_sparse"] == 0
+    PT.log(f"[map] {name}: sparse first level against dense, {w.describe()}")
+    for a, b_, what in zip(rs, rd, ("internal nodes", "log-max", "states", "tokens", "status")):
+        np.testing.assert_array_equal(a, b_, err_msg=what)
+
+
 def test_map_determinism_and_repeat():
     w = CASES["json-small"]()
     g1 = run_map(w)
