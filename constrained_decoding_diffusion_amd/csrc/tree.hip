@@ -1,5 +1,6 @@
 // Span tree: bottom-up 2^k-span transition products, level by level, as
-// batched fp32 MFMA matrix products (paperfeed "The scan trick: log-depth
+// batched matrix products in fp32 precision on the bf16 matrix cores (the
+// three-piece operand split below; paperfeed "The scan trick: log-depth
 // exact sampling": 2^k-step transitions from two 2^(k-1)-step ones in log L
 // rounds of batched matrix multiplication; papernotes 关键设计 2).
 //
@@ -34,10 +35,11 @@ constexpr int kBK = 32;          // K step staged in LDS (two MFMA K steps of 16
 constexpr int kLdb2 = kBK + 8;   // padded LDS row of one bf16 piece
 constexpr int kGemmThreads = 256;
 
-__global__ void tree_init_rf(StepView sv, int32_t *__restrict__ meta)
+// rf of the internal nodes 1 .. hend-1 of every row: kNeg (the levels whose
+// tiles split rows fill it by atomicMax), over the whole grid
+__device__ inline void init_rf_nodes(const StepView &sv, int32_t *__restrict__ meta, int hend)
 {
-    // rf of every internal node of every row: kNeg (filled by atomicMax)
-    const size_t per_row = (size_t)(sv.Lpad - 1) * sv.Sp;
+    const size_t per_row = (size_t)(hend - 1) * sv.Sp;
     const size_t total = per_row * sv.B;
     for (size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x; k < total;
          k += (size_t)gridDim.x * blockDim.x) {
@@ -47,6 +49,11 @@ __global__ void tree_init_rf(StepView sv, int32_t *__restrict__ meta)
         const int r = (int)(rem % sv.Sp);
         sv.meta_ptr(meta, b, h, 2)[r] = kNeg;
     }
+}
+
+__global__ void tree_init_rf(StepView sv, int32_t *__restrict__ meta)
+{
+    init_rf_nodes(sv, meta, sv.Lpad);
 }
 
 // exact power-of-two rescale of four consumed entries; zero stays zero and
@@ -905,11 +912,15 @@ __global__ __launch_bounds__(kHugeThreads) void span_pairs256(DevTable d, StepVi
                                                               float *__restrict__ tree,
                                                               int32_t *__restrict__ meta,
                                                               const float *__restrict__ pvf, int n0,
-                                                              int nn)
+                                                              int nn, int init_upper)
 {
     const int Sp = sv.Sp;
     const HugeWork hw(sv, n0, nn);
     const int nk = Sp / kBK3;
+    // with one tile per product (rows stored whole), the first level needs no
+    // rf initialized and clears that of the levels above it instead of a
+    // launch of its own (they run after this launch)
+    if (init_upper) init_rf_nodes(sv, meta, sv.Lpad >> 1);
     // [slot][operand][piece][row][16]
     __shared__ __align__(16) __bf16 Ls[kPvSlots][2][3][kHuge * kBK3];
     __shared__ int wofs_t[kPvMaxSteps + 1], wofs_n[kPvMaxSteps + 1];
@@ -1531,7 +1542,9 @@ int launch_span_tree(const DevTable &d, const Geometry &g, float *tree, int32_t 
         return (int)hipGetLastError();
     }
     StepView sv = step_view(g);
-    if (g.Lpad > 1) {
+    // the pair-staged first level at Sp = 256 clears the upper levels' rf itself
+    const bool pairs_init = d.first_pairs && d.npairs > 0 && g.Sp == kHuge && g.K >= 1;
+    if (g.Lpad > 1 && !pairs_init) {
         const size_t total = (size_t)g.B * (g.Lpad - 1) * g.Sp;
         const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
         tree_init_rf<<<blocks, 256, 0, st>>>(sv, meta);
@@ -1564,7 +1577,8 @@ int launch_span_tree(const DevTable &d, const Geometry &g, float *tree, int32_t 
         if (k == 1 && d.first_pairs && d.npairs > 0) {
             const long long wgs = (long long)g.B * nn * (g.Sp / kHuge) * (g.Sp / kHuge);
             const unsigned grid = (unsigned)std::min<long long>(wgs, device_cus());
-            span_pairs256<<<grid, kHugeThreads, 0, st>>>(d, sv, tree, meta, pvf, n0, nn);
+            span_pairs256<<<grid, kHugeThreads, 0, st>>>(d, sv, tree, meta, pvf, n0, nn,
+                                                         pairs_init ? 1 : 0);
             e = (int)hipGetLastError();
         } else if (k == 1 && sparse1) {
             SpLevel lv{};
