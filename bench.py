@@ -501,52 +501,57 @@ def level1_name(tb):
 # measured kernels: how to find their dispatches in rocprofv3 output
 KERNEL_MATCH = {
     "emission_dense": lambda n: "emission_dense<" in n,
-    "span_sparse1": lambda n: "span_sparse<" in n,    # first level: first launch after tree_init_rf
-    "span_gemm_level1": lambda n: "span_gemm" in n,   # first of the family after tree_init_rf
+    "span_sparse1": lambda n: "span_sparse<" in n,    # first level only (tree_levels)
+    "span_gemm_level1": lambda n: "span_gemm" in n,
     "span_pairs_level1": lambda n: "span_pairs256" in n,
     "marg_q": lambda n: "marg_q" in n,
 }
 LEVEL1_KERNELS = ("span_gemm_level1", "span_sparse1", "span_pairs_level1")
 
 
-def _select(rows, name):
-    """Dispatches of one measured kernel, in dispatch order; for the tree
-    products only the first level (the first product launch after each
-    tree_init_rf, dense or sparse)."""
-    rows = sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
-    match = KERNEL_MATCH[name]
-    if name not in LEVEL1_KERNELS:
-        return [r for r in rows if match(r["Kernel_Name"])]
-    out, armed = [], False
-    for r in rows:
-        n = r["Kernel_Name"]
-        if "tree_init_rf" in n:
-            armed = True
-        elif armed and any(KERNEL_MATCH[k](n) for k in LEVEL1_KERNELS):
-            if match(n):
-                out.append(r)
-            armed = False
-    return out
+def _tree_product(n):
+    return "span_gemm" in n or "span_sparse<" in n or "span_pairs256" in n
+
+
+def _tree_launch(n):
+    return (_tree_product(n) or "span_reduce" in n or "tree_init_rf" in n or "live_reach" in n
+            or "live_lists" in n)
 
 
 def tree_levels(rows):
     """Dispatch id -> "L<k>" for the span tree's launches (level k of the
-    step: the k-th product launch after tree_init_rf; a split-K reduce
-    takes its product's level), so that levels of one launch shape stay
-    apart in the summaries."""
+    step: the k-th product launch of one span tree, which starts with its
+    first launch (the row-exponent initialization, the live-state lists or
+    the first product) and ends at log Z; a split-K reduce takes its
+    product's level), so that levels of one launch shape stay apart in the
+    summaries."""
     out, level = {}, None
     for r in sorted(rows, key=lambda r: int(r["Dispatch_Id"])):
         n = r["Kernel_Name"]
-        if "tree_init_rf" in n:
+        if "tree_logz" in n:
+            level = None
+            continue
+        if level is None and _tree_launch(n):
             level = 0
-        elif level is not None and ("span_gemm" in n or "span_sparse<" in n or "span_pairs256" in n):
+        if level is None:
+            continue
+        if _tree_product(n):
             level += 1
             out[r["Dispatch_Id"]] = f"L{level}"
-        elif level is not None and "span_reduce" in n:
+        elif "span_reduce" in n and level:
             out[r["Dispatch_Id"]] = f"L{level}"
-        elif "tree_logz" in n:
-            level = None
     return out
+
+
+def _select(rows, name):
+    """Dispatches of one measured kernel, in dispatch order; for the tree
+    products only the first level's launches."""
+    rows = sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
+    match = KERNEL_MATCH[name]
+    if name not in LEVEL1_KERNELS:
+        return [r for r in rows if match(r["Kernel_Name"])]
+    lv = tree_levels(rows)
+    return [r for r in rows if lv.get(r["Dispatch_Id"]) == "L1" and match(r["Kernel_Name"])]
 
 
 def summarize_counters(fetch_dir, write_dir, command):
