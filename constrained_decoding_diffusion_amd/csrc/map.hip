@@ -273,13 +273,26 @@ __global__ __launch_bounds__(kMapThreads) void map_leaves(DevTable d, int L, int
 // maximum does not depend on the order, so the nodes are map_gemm's, bit for
 // bit.  A right leaf past the sequence end is the identity (D = the left
 // leaf), and so are both when the left one is.  One workgroup per (node,
-// `rows` stored rows, held in LDS); each wavefront takes a stored row at a
-// time, its lanes over one inner pair list at a time, whose columns are
-// distinct, so no two lanes update one entry at once.
-__global__ __launch_bounds__(kMapThreads) void map_sparse1(DevTable d, int L, int Lpad, int rows,
-                                                           double *__restrict__ tree)
+// `rows` stored rows, held in LDS as order-preserving integer keys); each
+// wavefront takes a stored row at a time, each lane one outer pair and its
+// inner pair list, four terms in flight, combined by LDS atomic maxima.
+constexpr int kMapSpThreads = 1024;
+
+// fp64 -> uint64 key with the same order (no NaN here), and back
+__device__ inline unsigned long long dkey(double x)
 {
-    extern __shared__ double accs[];  // [rows][Sp]
+    const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+    return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+__device__ inline double dval(unsigned long long k)
+{
+    return __longlong_as_double((long long)((k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k));
+}
+
+__global__ __launch_bounds__(kMapSpThreads) void map_sparse1(DevTable d, int L, int Lpad, int rows,
+                                                             double *__restrict__ tree)
+{
+    extern __shared__ unsigned long long accs[];  // [rows][Sp] keys
     const int Sp = d.Sp;
     const int half = Lpad >> 1;
     const int b = blockIdx.y / half, n = half + blockIdx.y % half;
@@ -291,51 +304,54 @@ __global__ __launch_bounds__(kMapThreads) void map_sparse1(DevTable d, int L, in
     double *D = node_ptr(tree, Sp, Lpad, b, n);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r0 = blockIdx.x * rows, nr = min(rows, Sp - r0);
-    for (int e = tid; e < nr * Sp; e += kMapThreads) accs[e] = -INFINITY;
+    const unsigned long long kinf = dkey(-INFINITY);
+    for (int e = tid; e < nr * Sp; e += kMapSpThreads) accs[e] = kinf;
     __syncthreads();
-    for (int rr = wave; rr < nr; rr += kMapThreads / 64) {
-        const int x = r0 + rr;  // stored row: a (as is) or c (transposed)
-        double *acc = accs + (size_t)rr * Sp;
+    // the outer pairs of stored row x: the left leaf's row x (as is) or the
+    // right leaf's column x (transposed); for each, the inner pairs through k
+    const int32_t *optr = tr ? d.col_ptr : d.row_ptr;
+    for (int rr = wave; rr < nr; rr += kMapSpThreads / 64) {
+        const int x = r0 + rr;
+        unsigned long long *acc = accs + (size_t)rr * Sp;
         if (x >= d.S) continue;
         if (id_l) {
-            if (lane == 0) acc[x] = 0.0;
-        } else if (id_r) {
-            // D = the left leaf (each entry plus the identity's 0): its row
-            // x, or its column x for a transposed node
-            const int q0 = tr ? d.col_ptr[x] : d.row_ptr[x], q1 = tr ? d.col_ptr[x + 1] : d.row_ptr[x + 1];
-            for (int q = q0 + lane; q < q1; q += 64) {
+            if (lane == 0) acc[x] = dkey(0.0);
+            continue;
+        }
+        for (int o = optr[x] + lane; o < optr[x + 1]; o += 64) {
+            if (id_r) {
+                // D = the left leaf: its row x, or its column x when transposed
                 if (tr) {
-                    const int a = d.pair_a[d.col_pairs[q]];
-                    acc[a] = Xl[(size_t)a * Sp + x] + 0.0;
+                    const int a = d.pair_a[d.col_pairs[o]];
+                    acc[a] = dkey(Xl[(size_t)a * Sp + x] + 0.0);
                 } else {
-                    const int c = d.pair_b[q];
-                    acc[c] = Xl[(size_t)x * Sp + c] + 0.0;
+                    const int c = d.pair_b[o];
+                    acc[c] = dkey(Xl[(size_t)x * Sp + c] + 0.0);
                 }
+                continue;
             }
-        } else if (!tr) {
-            for (int kl = d.row_ptr[x]; kl < d.row_ptr[x + 1]; ++kl) {
-                const int k = d.pair_b[kl];
-                const double wl = Xl[(size_t)x * Sp + k];
-                for (int q = d.row_ptr[k] + lane; q < d.row_ptr[k + 1]; q += 64) {
-                    const int c = d.pair_b[q];
-                    acc[c] = fmax(acc[c], wl + Xr[(size_t)c * Sp + k]);
+            const int k = tr ? d.pair_a[d.col_pairs[o]] : d.pair_b[o];
+            const double wo = tr ? Xr[(size_t)x * Sp + k] : Xl[(size_t)x * Sp + k];
+            const int q0 = optr[k], q1 = optr[k + 1];
+            for (int q = q0; q < q1; q += 4) {
+                int t[4];
+                double w[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int qq = min(q + u, q1 - 1);
+                    t[u] = tr ? d.pair_a[d.col_pairs[qq]] : d.pair_b[qq];
                 }
-            }
-        } else {
-            // stored row c of D^T: over the right leaf's pairs (k, c) and the
-            // left leaf's pairs (a, k)
-            for (int kr = d.col_ptr[x]; kr < d.col_ptr[x + 1]; ++kr) {
-                const int k = d.pair_a[d.col_pairs[kr]];
-                const double wr = Xr[(size_t)x * Sp + k];
-                for (int q = d.col_ptr[k] + lane; q < d.col_ptr[k + 1]; q += 64) {
-                    const int a = d.pair_a[d.col_pairs[q]];
-                    acc[a] = fmax(acc[a], Xl[(size_t)a * Sp + k] + wr);
-                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    w[u] = tr ? Xl[(size_t)t[u] * Sp + k] : Xr[(size_t)t[u] * Sp + k];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (q + u < q1) atomicMax(&acc[t[u]], dkey(tr ? w[u] + wo : wo + w[u]));
             }
         }
     }
     __syncthreads();
-    for (int e = tid; e < nr * Sp; e += kMapThreads) D[(size_t)r0 * Sp + e] = accs[e];
+    for (int e = tid; e < nr * Sp; e += kMapSpThreads) D[(size_t)r0 * Sp + e] = dval(accs[e]);
 }
 
 // ------------------------------------------------------ max-plus products
@@ -700,15 +716,16 @@ int launch_map_decode(const DevTable &d, const Geometry &g, const float *p, doub
     for (int k = 1; k <= g.K; ++k) {
         const int n0 = g.Lpad >> k, nn = n0;
         if (k == 1 && d.map_first_sparse) {
-            // rows per workgroup: at most 64 KB of LDS
-            const int rows = std::max(1, std::min(16, (int)(65536 / ((size_t)g.Sp * sizeof(double)))));
+            // rows per workgroup: one per wavefront, at most 64 KB of LDS
+            const int rows = std::max(1, std::min(kMapSpThreads / 64,
+                                                  (int)(65536 / ((size_t)g.Sp * sizeof(double)))));
             const size_t slds = (size_t)rows * g.Sp * sizeof(double);
             if (slds > 48 * 1024) {
                 e = hipFuncSetAttribute(reinterpret_cast<const void *>(&map_sparse1),
                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)slds);
                 if (e != hipSuccess) return (int)e;
             }
-            map_sparse1<<<dim3((g.Sp + rows - 1) / rows, g.B * nn), kMapThreads, slds, st>>>(
+            map_sparse1<<<dim3((g.Sp + rows - 1) / rows, g.B * nn), kMapSpThreads, slds, st>>>(
                 d, g.L, g.Lpad, rows, tree);
             e = hipGetLastError();
             if (e != hipSuccess) return (int)e;
